@@ -1,0 +1,202 @@
+"""CPU oracle for the ensemble ODE record / replay / discrete-adjoint path.
+
+TEST INFRASTRUCTURE ONLY.  Imported by ``tests/``, by ``__graft_entry__.smoke``
+and by the CPU-baseline leg of ``bench.py``; the GPU library never imports,
+links or calls anything here, and this package imports nothing from it.
+
+The arithmetic lives in ``oracle.cpp`` (binary64 C++, ``-ffp-contract=off``):
+
+* adaptive Tsit5 / Rosenbrock23 solve with a record of accepted steps
+  (arXiv 2609.02876, Sec. 2.1 and Sec. 3.1, Fig. 2);
+* the fixed-step replay of a recorded mesh (Sec. 3.1, Eq. 4);
+* the reverse-mode derivative of that replay, computed with a scalar tape
+  (Sec. 3.1: exact gradient of the chain with the mesh held fixed);
+* a complex-step replay for directional derivatives.
+
+Array layouts match the library boundary: parameters ``[p][n]`` (shared MLP
+weights ``[4740]``), states ``[d][n]``, record rows ``[n][s_cap]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "oracle.cpp")
+
+SYSTEMS = {"decay": 0, "lotka_volterra": 1, "lorenz63": 2, "mlp": 3, "robertson": 4, "loghalo": 5}
+METHODS = {"tsit5": 0, "rosenbrock23": 1}
+STATUS = {0: "ok", 1: "max_steps", 2: "nonfinite", 3: "dt_underflow", 4: "capacity"}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with g++ (binary64, no FP contraction)."""
+    if force or not os.path.exists(_SO):
+        cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+               "-shared", "-pthread", _SRC, "-o", _SO + ".tmp"]
+        subprocess.run(cmd, check=True)
+        os.replace(_SO + ".tmp", _SO)
+    return _SO
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_SO)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        D = ctypes.c_double
+        I = ctypes.c_int
+        L.oracle_dims.argtypes = [I, P, P, P]
+        L.oracle_tsit5_table.argtypes = [P, P, P]
+        L.oracle_ros23_consts.argtypes = [P, P]
+        for name in ("oracle_solve_f64", "oracle_solve_f32"):
+            getattr(L, name).argtypes = [I, I, I64, P, P, D, D, D, D, D, I64, I64, P, P, P, P, P, P, I]
+        L.oracle_replay_f64.argtypes = [I, I, I64, P, P, P, P, I64, P, I]
+        L.oracle_replay_cs.argtypes = [I, I, I64, P, P, P, P, D, P, P, I64, P, P]
+        L.oracle_grad_f64.argtypes = [I, I, I64, P, P, P, P, I64, P, P, P, P, I]
+        L.oracle_step_f64.argtypes = [I, I, P, P, D, P, P]
+        L.oracle_rhs_f64.argtypes = [I, P, P, P]
+        L.oracle_jac_f64.argtypes = [I, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def dims(system: str):
+    d, p, s = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    rc = lib().oracle_dims(SYSTEMS[system], ctypes.byref(d), ctypes.byref(p), ctypes.byref(s))
+    assert rc == 0
+    return d.value, p.value, bool(s.value)
+
+
+def tsit5_table():
+    c = np.zeros(7)
+    A = np.zeros((7, 7))
+    bt = np.zeros(7)
+    lib().oracle_tsit5_table(_p(c), _p(A), _p(bt))
+    return c, A, A[6].copy(), bt
+
+
+def ros23_consts():
+    d, e = ctypes.c_double(), ctypes.c_double()
+    lib().oracle_ros23_consts(ctypes.byref(d), ctypes.byref(e))
+    return d.value, e.value
+
+
+def solve(system, method, theta, y0, t0, t1, rtol, atol, dt0=0.0, max_steps=100000, s_cap=4096,
+          dtype="f64", nthreads=1, record=True):
+    """Adaptive solve with record.  Returns a dict of numpy arrays."""
+    d, p, shared = dims(system)
+    np_t = np.float64 if dtype == "f64" else np.float32
+    theta = np.ascontiguousarray(theta, dtype=np_t)
+    y0 = np.ascontiguousarray(y0, dtype=np_t)
+    n = y0.shape[-1] if y0.ndim == 2 else 0
+    assert y0.shape == (d, n)
+    assert theta.shape == ((p,) if shared else (p, n))
+    y1 = np.zeros((d, n), np_t)
+    count = np.zeros(n, np.int32)
+    nrej = np.zeros(n, np.int32)
+    status = np.zeros(n, np.int32)
+    t_rec = np.zeros((n, s_cap), np_t) if record else None
+    h_rec = np.zeros((n, s_cap), np_t) if record else None
+    fn = lib().oracle_solve_f64 if dtype == "f64" else lib().oracle_solve_f32
+    rc = fn(SYSTEMS[system], METHODS[method], n, _p(theta), _p(y0), float(t0), float(t1),
+            float(rtol), float(atol), float(dt0), int(max_steps), int(s_cap), _p(y1), _p(count),
+            _p(nrej), _p(status), _p(t_rec), _p(h_rec), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_solve: invalid argument")
+    return dict(y1=y1, count=count, nrej=nrej, status=status, t=t_rec, h=h_rec)
+
+
+def replay(system, method, theta, y0, count, h, nthreads=1):
+    d, p, shared = dims(system)
+    theta = np.ascontiguousarray(theta, dtype=np.float64)
+    y0 = np.ascontiguousarray(y0, dtype=np.float64)
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    count = np.ascontiguousarray(count, dtype=np.int32)
+    n = y0.shape[1]
+    yS = np.zeros((d, n))
+    rc = lib().oracle_replay_f64(SYSTEMS[system], METHODS[method], n, _p(theta), _p(y0), _p(count),
+                                 _p(h), h.shape[1], _p(yS), int(nthreads))
+    assert rc == 0
+    return yS
+
+
+def replay_cs(system, method, theta, y0, dtheta, dy0, count, h, eps=1e-30):
+    """Complex-step directional derivative of the replayed final state."""
+    d, p, shared = dims(system)
+    theta = np.ascontiguousarray(theta, dtype=np.float64)
+    y0 = np.ascontiguousarray(y0, dtype=np.float64)
+    dtheta = np.ascontiguousarray(dtheta, dtype=np.float64)
+    dy0 = np.ascontiguousarray(dy0, dtype=np.float64)
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    count = np.ascontiguousarray(count, dtype=np.int32)
+    n = y0.shape[1]
+    yS = np.zeros((d, n))
+    dyS = np.zeros((d, n))
+    rc = lib().oracle_replay_cs(SYSTEMS[system], METHODS[method], n, _p(theta), _p(y0), _p(dtheta),
+                                _p(dy0), float(eps), _p(count), _p(h), h.shape[1], _p(yS), _p(dyS))
+    assert rc == 0
+    return yS, dyS
+
+
+def grad(system, method, theta, y0, count, h, dLdy, nthreads=1):
+    """Reverse-mode gradient of L on the mesh (count, h).  Returns (dtheta, dy0, yS)."""
+    d, p, shared = dims(system)
+    theta = np.ascontiguousarray(theta, dtype=np.float64)
+    y0 = np.ascontiguousarray(y0, dtype=np.float64)
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    count = np.ascontiguousarray(count, dtype=np.int32)
+    dLdy = np.ascontiguousarray(dLdy, dtype=np.float64)
+    n = y0.shape[1]
+    dtheta = np.zeros((p,) if shared else (p, n))
+    dy0 = np.zeros((d, n))
+    yS = np.zeros((d, n))
+    rc = lib().oracle_grad_f64(SYSTEMS[system], METHODS[method], n, _p(theta), _p(y0), _p(count),
+                               _p(h), h.shape[1], _p(dLdy), _p(dtheta), _p(dy0), _p(yS),
+                               int(nthreads))
+    assert rc == 0
+    return dtheta, dy0, yS
+
+
+def step(system, method, theta, y, h):
+    """One attempted step from y (no acceptance decision): (y_new, error estimate)."""
+    d, p, _ = dims(system)
+    theta = np.ascontiguousarray(theta, dtype=np.float64)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    ynew = np.zeros(d)
+    err = np.zeros(d)
+    rc = lib().oracle_step_f64(SYSTEMS[system], METHODS[method], _p(theta), _p(y), float(h),
+                               _p(ynew), _p(err))
+    assert rc == 0
+    return ynew, err
+
+
+def rhs(system, theta, y):
+    d, p, _ = dims(system)
+    theta = np.ascontiguousarray(theta, dtype=np.float64)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    dy = np.zeros(d)
+    assert lib().oracle_rhs_f64(SYSTEMS[system], _p(theta), _p(y), _p(dy)) == 0
+    return dy
+
+
+def jac(system, theta, y):
+    d, p, _ = dims(system)
+    theta = np.ascontiguousarray(theta, dtype=np.float64)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    J = np.zeros((d, d))
+    assert lib().oracle_jac_f64(SYSTEMS[system], _p(theta), _p(y), _p(J)) == 0
+    return J

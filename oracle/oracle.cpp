@@ -1,0 +1,802 @@
+// ============================================================================
+// Ensemble ODE oracle: adaptive record, fixed-step replay, discrete adjoint.
+//
+// TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, CPU reference that
+// the GPU library is checked against.  Only the test suite, the smoke check and
+// the benchmark's CPU-baseline leg may load it.  It shares no code, header,
+// table or helper with the GPU library (differentiable_adaptive_ode_amd/csrc).
+//
+// What it follows (arXiv 2609.02876, "gradsolve: fast exact gradients for ODE
+// ensembles on GPUs"):
+//   * Section 2.1: explicit Runge-Kutta stages and step (Eqs. 1-2), the
+//     embedded error estimate e = y_new - yhat_new, the RMS acceptance test
+//     with tau_abs + tau_rel * max(|y|, |y_new|), retry from the same (t, y)
+//     with a smaller h after a failed test, FSAL reuse of the last stage.
+//   * Section 3.1 (Fig. 2, Eq. 4): the record keeps only accepted step sizes;
+//     the replay is the chain y_{i+1} = Phi_i(y_i; h_i, theta) with the
+//     recorded h_i held fixed; the gradient is the exact reverse-mode
+//     derivative of that chain (stop-gradient on the mesh).
+//   * Section 3.2: the Rosenbrock-Wanner one-step map with matrix I - gamma h J.
+//
+// How the gradient is computed here: the replay is run once on a reverse-mode
+// tape scalar (every +, -, *, /, fma, tanh is recorded with its local partial
+// derivatives) and the tape is swept backward from dL/dy_S.  That is reverse
+// mode of the replay chain by definition; no hand-derived vector-Jacobian
+// product appears in this file.  The same templated replay also runs on
+// std::complex<double> for complex-step derivatives (an independent pin).
+//
+// Readings where the pages are silent (also listed in the design doc):
+//   * Tsit5 coefficients: Tsitouras, Comput. Math. Appl. 62 (2011) 770-775,
+//     Table 1 (the pages cite the pair but do not print it).
+//   * Rosenbrock23: Shampine & Reichelt, SIAM J. Sci. Comput. 18 (1997) 1-22
+//     (the ode23s triple, autonomous form).
+//   * Controller: integral controller fac = 0.9 * err^(-1/(q+1)) with
+//     q+1 = 5 (Tsit5) or 3 (Rosenbrock23), clamped to [0.2, 10], no growth on
+//     the step after a rejection; the factor is truncated to 16 explicit
+//     mantissa bits (8 in binary32) so that the mesh does not depend on the
+//     last-ulp behaviour of pow() in a given math library.
+//   * Initial step: Hairer-Norsett-Wanner, Solving ODEs I, Sec. II.4, with
+//     exponent 1/order, truncated like the controller factor.
+//   * The last step is clipped to land exactly on t1.
+//   * Arithmetic contract: fused multiply-adds appear exactly where fma3() is
+//     written below; build with -ffp-contract=off.
+// ============================================================================
+#include <algorithm>
+#include <cmath>
+#include <complex>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace {
+
+// ----------------------------------------------------------------------------
+// Scalar types.  double / float for the adaptive solve; double, complex<double>
+// and Rev for the replay.
+// ----------------------------------------------------------------------------
+typedef std::complex<double> cplx;
+
+inline double fma3(double a, double b, double c) { return std::fma(a, b, c); }
+inline float fma3(float a, float b, float c) { return std::fma(a, b, c); }
+// For the complex-step replay the derivative of a*b+c is what matters; the
+// rounding of the real part is irrelevant to the imaginary part's accuracy.
+inline cplx fma3(cplx a, cplx b, cplx c) { return a * b + c; }
+inline double tanh_(double a) { return std::tanh(a); }
+inline float tanh_(float a) { return std::tanh(a); }
+inline cplx tanh_(cplx a) { return std::tanh(a); }
+inline double rv(double a) { return a; }
+inline double rv(float a) { return a; }
+inline double rv(cplx a) { return a.real(); }
+
+// Reverse-mode tape.  Each node stores up to three parents and the partial
+// derivative of the node's value with respect to each.
+struct Node {
+  int64_t p[3];
+  double d[3];
+};
+struct Tape {
+  std::vector<Node> nodes;
+};
+thread_local Tape* g_tape = nullptr;
+
+struct Rev {
+  double v;
+  int64_t id;  // < 0: a constant, carries no derivative
+  Rev() : v(0.0), id(-1) {}
+  Rev(double x) : v(x), id(-1) {}  // NOLINT: constants promote implicitly
+};
+
+inline Rev rnode(double v, int64_t a, double da, int64_t b = -1, double db = 0.0,
+                 int64_t c = -1, double dc = 0.0) {
+  Rev r;
+  r.v = v;
+  if (a < 0 && b < 0 && c < 0) return r;
+  Node n;
+  n.p[0] = a; n.d[0] = da;
+  n.p[1] = b; n.d[1] = db;
+  n.p[2] = c; n.d[2] = dc;
+  g_tape->nodes.push_back(n);
+  r.id = (int64_t)g_tape->nodes.size() - 1;
+  return r;
+}
+inline Rev rleaf(double v) {
+  Node n;
+  n.p[0] = n.p[1] = n.p[2] = -1;
+  n.d[0] = n.d[1] = n.d[2] = 0.0;
+  g_tape->nodes.push_back(n);
+  Rev r;
+  r.v = v;
+  r.id = (int64_t)g_tape->nodes.size() - 1;
+  return r;
+}
+inline Rev operator+(Rev a, Rev b) { return rnode(a.v + b.v, a.id, 1.0, b.id, 1.0); }
+inline Rev operator-(Rev a, Rev b) { return rnode(a.v - b.v, a.id, 1.0, b.id, -1.0); }
+inline Rev operator*(Rev a, Rev b) { return rnode(a.v * b.v, a.id, b.v, b.id, a.v); }
+inline Rev operator/(Rev a, Rev b) {
+  double q = a.v / b.v;
+  return rnode(q, a.id, 1.0 / b.v, b.id, -q / b.v);
+}
+inline Rev operator-(Rev a) { return rnode(-a.v, a.id, -1.0); }
+inline Rev fma3(Rev a, Rev b, Rev c) {
+  return rnode(std::fma(a.v, b.v, c.v), a.id, b.v, b.id, a.v, c.id, 1.0);
+}
+inline Rev tanh_(Rev a) {
+  double t = std::tanh(a.v);
+  return rnode(t, a.id, 1.0 - t * t);
+}
+inline double rv(Rev a) { return a.v; }
+
+// ----------------------------------------------------------------------------
+// Tsit5 pair (Tsitouras 2011, Table 1).  b equals the last row of A (FSAL:
+// the seventh stage is evaluated at y_new), b_7 = 0.  BT = b - bhat, the
+// error weights; the seventh entry is 1/66.
+// ----------------------------------------------------------------------------
+const double TS_C[7] = {0.0, 0.161, 0.327, 0.9, 0.9800255409045097, 1.0, 1.0};
+const double TS_A[7][7] = {
+    {0, 0, 0, 0, 0, 0, 0},
+    {0.161, 0, 0, 0, 0, 0, 0},
+    {-0.008480655492356989, 0.335480655492357, 0, 0, 0, 0, 0},
+    {2.897153057105493, -6.359448489975075, 4.3622954328695815, 0, 0, 0, 0},
+    {5.325864828439257, -11.748883564062828, 7.4955393428898365, -0.09249506636175525, 0, 0, 0},
+    {5.86145544294642, -12.92096931784711, 8.159367898576159, -0.071584973281401,
+     -0.028269050394068383, 0, 0},
+    {0.09646076681806523, 0.01, 0.4798896504144996, 1.379008574103742, -3.290069515436081,
+     2.324710524099774, 0}};
+const double TS_BT[7] = {-0.00178001105222577714, -0.0008164344596567469, 0.007880878010261995,
+                         -0.1447110071732629,     0.5823571654525552,     -0.45808210592918697,
+                         0.015151515151515152};
+
+// Rosenbrock23 (Shampine & Reichelt 1997): gamma = d = 1/(2+sqrt 2),
+// e32 = 6 + sqrt 2.
+const double R23_D = 1.0 / (2.0 + 1.4142135623730951);
+const double R23_E32 = 6.0 + 1.4142135623730951;
+
+// ----------------------------------------------------------------------------
+// Systems.  Each is templated on the scalar T; theta is the trajectory's own
+// parameter vector (or, for the MLP, the shared weight vector).
+// ----------------------------------------------------------------------------
+enum { SYS_DECAY = 0, SYS_LV = 1, SYS_LORENZ = 2, SYS_MLP = 3, SYS_ROBERTSON = 4, SYS_LOGHALO = 5,
+       SYS_COUNT = 6 };
+enum { M_TSIT5 = 0, M_ROS23 = 1 };
+enum { ST_OK = 0, ST_MAXSTEPS = 1, ST_NONFINITE = 2, ST_DTMIN = 3, ST_CAPACITY = 4 };
+
+const int SYS_D[SYS_COUNT] = {1, 2, 3, 4, 3, 6};
+const int SYS_P[SYS_COUNT] = {1, 4, 3, 4740, 3, 3};
+const int MAXD = 6;
+
+// y' = -theta y  (the linear test system; exact solution y0 exp(-theta t)).
+template <class T>
+void f_decay(const T* th, const T* y, T* dy) {
+  dy[0] = -(th[0] * y[0]);
+}
+template <class T>
+void j_decay(const T* th, const T* y, T* J) {
+  (void)y;
+  J[0] = -th[0];
+}
+
+// Lotka-Volterra, theta = (a, b, g, d):
+//   y1' = a y1 - b y1 y2 = y1 (a - b y2),  y2' = d y1 y2 - g y2 = y2 (d y1 - g).
+template <class T>
+void f_lv(const T* th, const T* y, T* dy) {
+  dy[0] = y[0] * fma3(-th[1], y[1], th[0]);
+  dy[1] = y[1] * fma3(th[3], y[0], -th[2]);
+}
+template <class T>
+void j_lv(const T* th, const T* y, T* J) {
+  J[0] = fma3(-th[1], y[1], th[0]);
+  J[1] = -(th[1] * y[0]);
+  J[2] = th[3] * y[1];
+  J[3] = fma3(th[3], y[0], -th[2]);
+}
+
+// Lorenz-63, theta = (sigma, rho, beta).
+template <class T>
+void f_lorenz(const T* th, const T* y, T* dy) {
+  dy[0] = th[0] * (y[1] - y[0]);
+  dy[1] = fma3(y[0], th[1] - y[2], -y[1]);
+  dy[2] = fma3(y[0], y[1], -(th[2] * y[2]));
+}
+template <class T>
+void j_lorenz(const T* th, const T* y, T* J) {
+  J[0] = -th[0]; J[1] = th[0]; J[2] = T(0.0);
+  J[3] = th[1] - y[2]; J[4] = T(-1.0); J[5] = -y[0];
+  J[6] = y[1]; J[7] = y[0]; J[8] = -th[2];
+}
+
+// Robertson kinetics, theta = (k1, k2, k3):
+//   y1' = -k1 y1 + k3 y2 y3,  y2' = k1 y1 - k2 y2^2 - k3 y2 y3,  y3' = k2 y2^2.
+template <class T>
+void f_rober(const T* th, const T* y, T* dy) {
+  T a = th[0] * y[0];
+  T b = th[1] * (y[1] * y[1]);
+  T c = th[2] * (y[1] * y[2]);
+  dy[0] = c - a;
+  dy[1] = (a - b) - c;
+  dy[2] = b;
+}
+template <class T>
+void j_rober(const T* th, const T* y, T* J) {
+  T j12 = th[2] * y[2];
+  T j13 = th[2] * y[1];
+  T t = (T(2.0) * th[1]) * y[1];
+  J[0] = -th[0]; J[1] = j12;        J[2] = j13;
+  J[3] = th[0];  J[4] = -(t + j12); J[5] = -j13;
+  J[6] = T(0.0); J[7] = t;          J[8] = T(0.0);
+}
+
+// Star in a flattened logarithmic halo, Phi = 1/2 v0^2 ln(Rc^2 + x^2 + y^2 + z^2/q^2),
+// state (x, y, z, vx, vy, vz), theta = (v0, Rc, q).  Acceleration -grad Phi.
+template <class T>
+void f_halo(const T* th, const T* y, T* dy) {
+  T v2 = th[0] * th[0];
+  T r2 = th[1] * th[1];
+  T iq2 = T(1.0) / (th[2] * th[2]);
+  T zq = y[2] * iq2;
+  T D = fma3(y[0], y[0], fma3(y[1], y[1], fma3(y[2], zq, r2)));
+  T A = v2 / D;
+  dy[0] = y[3];
+  dy[1] = y[4];
+  dy[2] = y[5];
+  dy[3] = -(A * y[0]);
+  dy[4] = -(A * y[1]);
+  dy[5] = -(A * zq);
+}
+template <class T>
+void j_halo(const T* th, const T* y, T* J) {
+  // d/d(x,y,z) of a = -A g, g = (x, y, z/q^2), A = v0^2 / D.
+  T v2 = th[0] * th[0];
+  T r2 = th[1] * th[1];
+  T iq2 = T(1.0) / (th[2] * th[2]);
+  T zq = y[2] * iq2;
+  T D = fma3(y[0], y[0], fma3(y[1], y[1], fma3(y[2], zq, r2)));
+  T A = v2 / D;
+  T g[3] = {y[0], y[1], zq};
+  T dD[3] = {T(2.0) * y[0], T(2.0) * y[1], T(2.0) * zq};
+  for (int i = 0; i < 36; ++i) J[i] = T(0.0);
+  for (int i = 0; i < 3; ++i) J[i * 6 + 3 + i] = T(1.0);
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 3; ++j) {
+      T dg = (i == j) ? ((i == 2) ? iq2 : T(1.0)) : T(0.0);
+      // d(-A g_i)/dy_j = -A dg_ij + A g_i dD_j / D
+      J[(3 + i) * 6 + j] = (A * g[i]) * dD[j] / D - A * dg;
+    }
+}
+
+// Neural field y' = W3 tanh(W2 tanh(W1 y + b1) + b2) + b3, sizes 4-64-64-4,
+// weights packed [W1 (64x4, row-major), b1 (64), W2 (64x64), b2 (64),
+// W3 (4x64), b3 (4)] = 4740 values shared by every trajectory.
+const int MLP_H = 64, MLP_I = 4;
+const int MLP_OW1 = 0, MLP_OB1 = 256, MLP_OW2 = 320, MLP_OB2 = 4416, MLP_OW3 = 4480, MLP_OB3 = 4736;
+template <class T>
+void f_mlp(const T* th, const T* y, T* dy) {
+  T h1[MLP_H], h2[MLP_H];
+  for (int j = 0; j < MLP_H; ++j) {
+    T acc = th[MLP_OB1 + j];
+    for (int i = 0; i < MLP_I; ++i) acc = fma3(th[MLP_OW1 + j * MLP_I + i], y[i], acc);
+    h1[j] = tanh_(acc);
+  }
+  for (int j = 0; j < MLP_H; ++j) {
+    T acc = th[MLP_OB2 + j];
+    for (int i = 0; i < MLP_H; ++i) acc = fma3(th[MLP_OW2 + j * MLP_H + i], h1[i], acc);
+    h2[j] = tanh_(acc);
+  }
+  for (int j = 0; j < MLP_I; ++j) {
+    T acc = th[MLP_OB3 + j];
+    for (int i = 0; i < MLP_H; ++i) acc = fma3(th[MLP_OW3 + j * MLP_H + i], h2[i], acc);
+    dy[j] = acc;
+  }
+}
+
+template <class T>
+void rhs(int sys, const T* th, const T* y, T* dy) {
+  switch (sys) {
+    case SYS_DECAY: f_decay(th, y, dy); break;
+    case SYS_LV: f_lv(th, y, dy); break;
+    case SYS_LORENZ: f_lorenz(th, y, dy); break;
+    case SYS_MLP: f_mlp(th, y, dy); break;
+    case SYS_ROBERTSON: f_rober(th, y, dy); break;
+    case SYS_LOGHALO: f_halo(th, y, dy); break;
+  }
+}
+template <class T>
+bool jac(int sys, const T* th, const T* y, T* J) {
+  switch (sys) {
+    case SYS_DECAY: j_decay(th, y, J); return true;
+    case SYS_LV: j_lv(th, y, J); return true;
+    case SYS_LORENZ: j_lorenz(th, y, J); return true;
+    case SYS_ROBERTSON: j_rober(th, y, J); return true;
+    case SYS_LOGHALO: j_halo(th, y, J); return true;
+    default: return false;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// One Tsit5 step (Section 2.1, Eqs. 1-2).  k[0] holds f(y) on entry.  Fills
+// k[1..6], ynew (= the seventh stage state) and, if err != nullptr, the
+// embedded error e = h * sum_j BT_j k_j (needs k[6] = f(ynew)).
+// ----------------------------------------------------------------------------
+template <class T>
+void tsit5_step(int sys, const T* th, int d, const T* y, T h, T k[7][MAXD], T* ynew, T* err) {
+  T Y[MAXD];
+  for (int i = 1; i < 7; ++i) {
+    for (int c = 0; c < d; ++c) {
+      T acc = T(TS_A[i][0]) * k[0][c];
+      for (int j = 1; j < i; ++j) acc = fma3(T(TS_A[i][j]), k[j][c], acc);
+      Y[c] = fma3(h, acc, y[c]);
+    }
+    if (i == 6) {
+      for (int c = 0; c < d; ++c) ynew[c] = Y[c];
+      if (err == nullptr) return;  // the replay needs no seventh evaluation
+    }
+    rhs(sys, th, Y, k[i]);
+  }
+  for (int c = 0; c < d; ++c) {
+    T acc = T(TS_BT[0]) * k[0][c];
+    for (int j = 1; j < 7; ++j) acc = fma3(T(TS_BT[j]), k[j][c], acc);
+    err[c] = h * acc;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Dense LU with partial pivoting (first row of largest magnitude) and the
+// solve with its factors.  Used for the Rosenbrock matrix W = I - h d J.
+// ----------------------------------------------------------------------------
+template <class T>
+void lu_factor(int d, T* A, int* piv) {
+  for (int k = 0; k < d; ++k) {
+    int p = k;
+    double best = std::fabs(rv(A[k * d + k]));
+    for (int i = k + 1; i < d; ++i) {
+      double v = std::fabs(rv(A[i * d + k]));
+      if (v > best) { best = v; p = i; }
+    }
+    piv[k] = p;
+    if (p != k)
+      for (int j = 0; j < d; ++j) std::swap(A[k * d + j], A[p * d + j]);
+    for (int i = k + 1; i < d; ++i) {
+      T l = A[i * d + k] / A[k * d + k];
+      A[i * d + k] = l;
+      for (int j = k + 1; j < d; ++j) A[i * d + j] = fma3(-l, A[k * d + j], A[i * d + j]);
+    }
+  }
+}
+template <class T>
+void lu_solve(int d, const T* LU, const int* piv, const T* b, T* x) {
+  T z[MAXD];
+  for (int i = 0; i < d; ++i) z[i] = b[i];
+  for (int k = 0; k < d; ++k)
+    if (piv[k] != k) std::swap(z[k], z[piv[k]]);
+  for (int i = 1; i < d; ++i)
+    for (int j = 0; j < i; ++j) z[i] = fma3(-LU[i * d + j], z[j], z[i]);
+  for (int i = d - 1; i >= 0; --i) {
+    T acc = z[i];
+    for (int j = i + 1; j < d; ++j) acc = fma3(-LU[i * d + j], x[j], acc);
+    x[i] = acc / LU[i * d + i];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// One Rosenbrock23 step (Section 3.2; Shampine-Reichelt form, autonomous).
+// F0 = f(y) on entry.  Returns ynew; if err != nullptr also evaluates
+// F2 = f(ynew) (returned for reuse as the next F0) and the error estimate.
+// ----------------------------------------------------------------------------
+template <class T>
+void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* ynew, T* F2, T* err) {
+  T J[MAXD * MAXD], W[MAXD * MAXD];
+  int piv[MAXD];
+  jac(sys, th, y, J);
+  T hd = h * T(R23_D);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) W[i * d + j] = fma3(-hd, J[i * d + j], T(i == j ? 1.0 : 0.0));
+  lu_factor(d, W, piv);
+  T k1[MAXD], k2[MAXD], Y1[MAXD], F1[MAXD], r[MAXD], u[MAXD];
+  lu_solve(d, W, piv, F0, k1);
+  T hh = T(0.5) * h;
+  for (int c = 0; c < d; ++c) Y1[c] = fma3(hh, k1[c], y[c]);
+  rhs(sys, th, Y1, F1);
+  for (int c = 0; c < d; ++c) r[c] = F1[c] - k1[c];
+  lu_solve(d, W, piv, r, u);
+  for (int c = 0; c < d; ++c) k2[c] = u[c] + k1[c];
+  for (int c = 0; c < d; ++c) ynew[c] = fma3(h, k2[c], y[c]);
+  if (err == nullptr) return;
+  rhs(sys, th, ynew, F2);
+  T k3[MAXD];
+  for (int c = 0; c < d; ++c) {
+    T t2 = fma3(T(-R23_E32), k2[c] - F1[c], F2[c]);
+    r[c] = fma3(T(-2.0), k1[c] - F0[c], t2);
+  }
+  lu_solve(d, W, piv, r, k3);
+  T h6 = h / T(6.0);
+  for (int c = 0; c < d; ++c) err[c] = h6 * (fma3(T(-2.0), k2[c], k1[c]) + k3[c]);
+}
+
+// ----------------------------------------------------------------------------
+// Step-size helpers.
+// ----------------------------------------------------------------------------
+inline double trunc_bits(double x) {  // keep 16 explicit mantissa bits
+  uint64_t u;
+  std::memcpy(&u, &x, 8);
+  u &= ~((uint64_t(1) << 36) - 1);
+  std::memcpy(&x, &u, 8);
+  return x;
+}
+inline float trunc_bits(float x) {  // keep 8 explicit mantissa bits
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  u &= ~((uint32_t(1) << 15) - 1);
+  std::memcpy(&x, &u, 4);
+  return x;
+}
+
+// Mean of squares of the scaled components, sum order c = 0..d-1.
+template <class T>
+T mean_sq(int d, const T* e, const T* sc) {
+  T r = e[0] / sc[0];
+  T acc = r * r;
+  for (int c = 1; c < d; ++c) {
+    r = e[c] / sc[c];
+    acc = fma3(r, r, acc);
+  }
+  return acc / T(d);
+}
+
+// Starting step (Hairer, Norsett & Wanner, Solving ODEs I, Sec. II.4).
+template <class T>
+T initial_step(int sys, const T* th, int d, const T* y0, const T* f0, T span, T rtol, T atol,
+               int order) {
+  T sc[MAXD], y1[MAXD], f1[MAXD], df[MAXD];
+  for (int c = 0; c < d; ++c) sc[c] = fma3(rtol, std::fabs(y0[c]), atol);
+  T d0 = std::sqrt(mean_sq(d, y0, sc));
+  T d1 = std::sqrt(mean_sq(d, f0, sc));
+  T h0 = (d0 < T(1e-5) || d1 < T(1e-5)) ? T(1e-6) : T(0.01) * (d0 / d1);
+  h0 = std::min(h0, span);
+  for (int c = 0; c < d; ++c) y1[c] = fma3(h0, f0[c], y0[c]);
+  rhs(sys, th, y1, f1);
+  for (int c = 0; c < d; ++c) df[c] = f1[c] - f0[c];
+  T d2 = std::sqrt(mean_sq(d, df, sc)) / h0;
+  T m = std::max(d1, d2);
+  T h1 = (m <= T(1e-15)) ? std::max(T(1e-6), h0 * T(1e-3))
+                         : T(std::pow(T(0.01) / m, T(1.0) / T(order)));
+  return trunc_bits(std::min(T(100.0) * h0, h1));
+}
+
+// ----------------------------------------------------------------------------
+// Adaptive solve of one trajectory with record (Section 2.1 loop, Section 3.1
+// record).  Writes t_rec[n], h_rec[n] for accepted steps n < s_cap.
+// ----------------------------------------------------------------------------
+template <class T>
+struct SolveOut {
+  int32_t count, nrej, status;
+};
+
+template <class T>
+SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1, T rtol, T atol,
+                      T dt0, int64_t max_steps, int64_t s_cap, T* y1, T* t_rec, T* h_rec) {
+  const int d = SYS_D[sys];
+  const int order = (method == M_TSIT5) ? 5 : 2;
+  const T expo = (method == M_TSIT5) ? T(-0.1) : T(-1.0 / 6.0);  // applied to the mean square
+  SolveOut<T> out = {0, 0, ST_OK};
+  T y[MAXD], ynew[MAXD], e[MAXD], sc[MAXD], k[7][MAXD], F2[MAXD];
+  for (int c = 0; c < d; ++c) y[c] = y0[c];
+  T t = t0;
+  if (t1 > t0) {
+    rhs(sys, th, y, k[0]);  // k1, or F0 for the Rosenbrock step
+    T h = (dt0 > T(0)) ? dt0 : initial_step(sys, th, d, y, k[0], t1 - t0, rtol, atol, order);
+    int64_t attempts = 0;
+    bool prev_rejected = false;
+    int64_t n = 0;
+    while (t < t1) {
+      if (attempts >= max_steps) { out.status = ST_MAXSTEPS; break; }
+      ++attempts;
+      bool last = (t + h >= t1);
+      T hs = last ? (t1 - t) : h;
+      if (!std::isfinite(hs)) { out.status = ST_NONFINITE; break; }
+      if (!(t + hs > t)) { out.status = ST_DTMIN; break; }
+      if (method == M_TSIT5) {
+        tsit5_step(sys, th, d, y, hs, k, ynew, e);
+      } else {
+        ros23_step(sys, th, d, y, hs, k[0], ynew, F2, e);
+      }
+      for (int c = 0; c < d; ++c)
+        sc[c] = fma3(rtol, std::max(std::fabs(y[c]), std::fabs(ynew[c])), atol);
+      T msq = mean_sq(d, e, sc);
+      if (!std::isfinite(msq)) { out.status = ST_NONFINITE; break; }
+      if (msq <= T(1.0)) {
+        if (n >= s_cap) { out.status = ST_CAPACITY; break; }
+        if (t_rec) t_rec[n] = t;
+        if (h_rec) h_rec[n] = hs;
+        ++n;
+        t = last ? t1 : t + hs;
+        for (int c = 0; c < d; ++c) y[c] = ynew[c];
+        if (method == M_TSIT5)
+          for (int c = 0; c < d; ++c) k[0][c] = k[6][c];
+        else
+          for (int c = 0; c < d; ++c) k[0][c] = F2[c];
+        T fac = (msq == T(0)) ? T(10.0) : trunc_bits(T(0.9) * T(std::pow(msq, expo)));
+        fac = std::min(T(10.0), std::max(T(0.2), fac));
+        if (prev_rejected) fac = std::min(fac, T(1.0));
+        h = hs * fac;
+        prev_rejected = false;
+      } else {
+        ++out.nrej;
+        T fac = std::max(T(0.2), trunc_bits(T(0.9) * T(std::pow(msq, expo))));
+        h = hs * fac;
+        prev_rejected = true;
+      }
+    }
+    out.count = (int32_t)n;
+  }
+  for (int c = 0; c < d; ++c) y1[c] = (out.status == ST_OK) ? y[c] : T(NAN);
+  return out;
+}
+
+// ----------------------------------------------------------------------------
+// Replay (Section 3.1, Eq. 4): y_{i+1} = Phi(y_i; h_i, theta) for i < count.
+// ----------------------------------------------------------------------------
+template <class T>
+void replay_one(int sys, int method, const T* th, const T* y0, int32_t count, const double* h_rec,
+                T* yS) {
+  const int d = SYS_D[sys];
+  T y[MAXD], ynew[MAXD], k[7][MAXD];
+  for (int c = 0; c < d; ++c) y[c] = y0[c];
+  for (int32_t n = 0; n < count; ++n) {
+    T h = T(h_rec[n]);
+    rhs(sys, th, y, k[0]);
+    if (method == M_TSIT5)
+      tsit5_step<T>(sys, th, d, y, h, k, ynew, nullptr);
+    else
+      ros23_step<T>(sys, th, d, y, h, k[0], ynew, nullptr, nullptr);
+    for (int c = 0; c < d; ++c) y[c] = ynew[c];
+  }
+  for (int c = 0; c < d; ++c) yS[c] = y[c];
+}
+
+// Gradient of L through the replay of one trajectory: build the tape, seed
+// dL/dy_S, sweep backward.  th_bar (length p) and y0_bar (length d) receive
+// dL/dtheta and dL/dy0; yS receives the replayed final state.
+void grad_one(int sys, int method, const double* th, const double* y0, int32_t count,
+              const double* h_rec, const double* dLdy, double* th_bar, double* y0_bar,
+              double* yS) {
+  const int d = SYS_D[sys], p = SYS_P[sys];
+  Tape tape;
+  g_tape = &tape;
+  std::vector<Rev> rth(p);
+  Rev ry0[MAXD], ryS[MAXD];
+  for (int i = 0; i < p; ++i) rth[i] = rleaf(th[i]);
+  for (int c = 0; c < d; ++c) ry0[c] = rleaf(y0[c]);
+  replay_one<Rev>(sys, method, rth.data(), ry0, count, h_rec, ryS);
+  std::vector<double> adj(tape.nodes.size(), 0.0);
+  for (int c = 0; c < d; ++c) {
+    yS[c] = ryS[c].v;
+    if (ryS[c].id >= 0) adj[ryS[c].id] += dLdy[c];
+  }
+  for (int64_t i = (int64_t)tape.nodes.size() - 1; i >= 0; --i) {
+    double a = adj[i];
+    if (a == 0.0) continue;
+    const Node& nd = tape.nodes[i];
+    for (int j = 0; j < 3; ++j)
+      if (nd.p[j] >= 0) adj[nd.p[j]] += nd.d[j] * a;
+  }
+  for (int i = 0; i < p; ++i) th_bar[i] = adj[rth[i].id];
+  for (int c = 0; c < d; ++c) {
+    // An output equal to an input leaf (count = 0) also carries dLdy.
+    y0_bar[c] = adj[ry0[c].id];
+  }
+  g_tape = nullptr;
+}
+
+// ----------------------------------------------------------------------------
+// Threading over trajectories (static contiguous blocks).
+// ----------------------------------------------------------------------------
+template <class F>
+void parallel_for(int64_t n, int nthreads, F fn) {
+  if (nthreads <= 1 || n < 2) {
+    fn(0, (int64_t)0, n);
+    return;
+  }
+  nthreads = (int)std::min<int64_t>(nthreads, n);
+  std::vector<std::thread> pool;
+  for (int t = 0; t < nthreads; ++t) {
+    int64_t lo = n * t / nthreads, hi = n * (t + 1) / nthreads;
+    pool.emplace_back([=] { fn(t, lo, hi); });
+  }
+  for (auto& th : pool) th.join();
+}
+
+bool valid_sys(int sys, int method) {
+  if (sys < 0 || sys >= SYS_COUNT) return false;
+  if (method != M_TSIT5 && method != M_ROS23) return false;
+  if (method == M_ROS23 && sys == SYS_MLP) return false;
+  return true;
+}
+
+template <class T>
+int solve_impl(int sys, int method, int64_t n, const T* theta, const T* y0, double t0, double t1,
+               double rtol, double atol, double dt0, int64_t max_steps, int64_t s_cap, T* y1,
+               int32_t* count, int32_t* nrej, int32_t* status, T* t_rec, T* h_rec, int nthreads) {
+  if (!valid_sys(sys, method) || n < 0 || !(t1 >= t0) || !(rtol > 0) || !(atol > 0) ||
+      max_steps < 1 || s_cap < 0)
+    return 1;
+  const int d = SYS_D[sys], p = SYS_P[sys];
+  const bool shared = (sys == SYS_MLP);
+  parallel_for(n, nthreads, [&](int, int64_t lo, int64_t hi) {
+    std::vector<T> th(p);
+    T yy0[MAXD], yy1[MAXD];
+    for (int64_t k = lo; k < hi; ++k) {
+      for (int i = 0; i < p; ++i) th[i] = shared ? theta[i] : theta[i * n + k];
+      for (int c = 0; c < d; ++c) yy0[c] = y0[c * n + k];
+      SolveOut<T> o = solve_one<T>(sys, method, th.data(), yy0, T(t0), T(t1), T(rtol), T(atol),
+                                   T(dt0), max_steps, s_cap, yy1, t_rec ? t_rec + k * s_cap : nullptr,
+                                   h_rec ? h_rec + k * s_cap : nullptr);
+      for (int c = 0; c < d; ++c) y1[c * n + k] = yy1[c];
+      count[k] = o.count;
+      nrej[k] = o.nrej;
+      status[k] = o.status;
+    }
+  });
+  return 0;
+}
+
+}  // namespace
+
+// ============================================================================
+// C entry points (loaded with ctypes by oracle/__init__.py).
+// Layouts: theta [p][n] (shared MLP weights: [4740]); y0, y1, dLdy [d][n];
+// record rows t_rec, h_rec [n][s_cap]; count, nrej, status [n].
+// Return value 0 = success, 1 = invalid argument.
+// ============================================================================
+extern "C" {
+
+int oracle_dims(int sys, int* d, int* p, int* shared) {
+  if (sys < 0 || sys >= SYS_COUNT) return 1;
+  *d = SYS_D[sys];
+  *p = SYS_P[sys];
+  *shared = (sys == SYS_MLP);
+  return 0;
+}
+
+void oracle_tsit5_table(double* c, double* A, double* bt) {
+  for (int i = 0; i < 7; ++i) {
+    c[i] = TS_C[i];
+    bt[i] = TS_BT[i];
+    for (int j = 0; j < 7; ++j) A[i * 7 + j] = TS_A[i][j];
+  }
+}
+
+void oracle_ros23_consts(double* d, double* e32) {
+  *d = R23_D;
+  *e32 = R23_E32;
+}
+
+int oracle_solve_f64(int sys, int method, int64_t n, const double* theta, const double* y0,
+                     double t0, double t1, double rtol, double atol, double dt0, int64_t max_steps,
+                     int64_t s_cap, double* y1, int32_t* count, int32_t* nrej, int32_t* status,
+                     double* t_rec, double* h_rec, int nthreads) {
+  return solve_impl<double>(sys, method, n, theta, y0, t0, t1, rtol, atol, dt0, max_steps, s_cap,
+                            y1, count, nrej, status, t_rec, h_rec, nthreads);
+}
+
+int oracle_solve_f32(int sys, int method, int64_t n, const float* theta, const float* y0,
+                     double t0, double t1, double rtol, double atol, double dt0, int64_t max_steps,
+                     int64_t s_cap, float* y1, int32_t* count, int32_t* nrej, int32_t* status,
+                     float* t_rec, float* h_rec, int nthreads) {
+  return solve_impl<float>(sys, method, n, theta, y0, t0, t1, rtol, atol, dt0, max_steps, s_cap,
+                           y1, count, nrej, status, t_rec, h_rec, nthreads);
+}
+
+// Replay in binary64 on a given mesh (h_rec [n][s_cap], count [n]).
+int oracle_replay_f64(int sys, int method, int64_t n, const double* theta, const double* y0,
+                      const int32_t* count, const double* h_rec, int64_t s_cap, double* yS,
+                      int nthreads) {
+  if (!valid_sys(sys, method) || n < 0) return 1;
+  const int d = SYS_D[sys], p = SYS_P[sys];
+  const bool shared = (sys == SYS_MLP);
+  parallel_for(n, nthreads, [&](int, int64_t lo, int64_t hi) {
+    std::vector<double> th(p);
+    double a0[MAXD], a1[MAXD];
+    for (int64_t k = lo; k < hi; ++k) {
+      for (int i = 0; i < p; ++i) th[i] = shared ? theta[i] : theta[i * n + k];
+      for (int c = 0; c < d; ++c) a0[c] = y0[c * n + k];
+      replay_one<double>(sys, method, th.data(), a0, count[k], h_rec + k * s_cap, a1);
+      for (int c = 0; c < d; ++c) yS[c * n + k] = a1[c];
+    }
+  });
+  return 0;
+}
+
+// Complex-step replay: theta + i*eps*dtheta, y0 + i*eps*dy0.  Returns the real
+// part and Im/eps (the directional derivative of y_S) per component.
+int oracle_replay_cs(int sys, int method, int64_t n, const double* theta, const double* y0,
+                     const double* dtheta, const double* dy0, double eps, const int32_t* count,
+                     const double* h_rec, int64_t s_cap, double* yS, double* dyS) {
+  if (!valid_sys(sys, method) || n < 0) return 1;
+  const int d = SYS_D[sys], p = SYS_P[sys];
+  const bool shared = (sys == SYS_MLP);
+  std::vector<cplx> th(p);
+  cplx a0[MAXD], a1[MAXD];
+  for (int64_t k = 0; k < n; ++k) {
+    for (int i = 0; i < p; ++i) {
+      int64_t idx = shared ? i : i * n + k;
+      th[i] = cplx(theta[idx], eps * dtheta[idx]);
+    }
+    for (int c = 0; c < d; ++c) a0[c] = cplx(y0[c * n + k], eps * dy0[c * n + k]);
+    replay_one<cplx>(sys, method, th.data(), a0, count[k], h_rec + k * s_cap, a1);
+    for (int c = 0; c < d; ++c) {
+      yS[c * n + k] = a1[c].real();
+      dyS[c * n + k] = a1[c].imag() / eps;
+    }
+  }
+  return 0;
+}
+
+// Reverse-mode gradient of L through the replay.  dtheta is [p][n], or [4740]
+// summed over the ensemble for the shared MLP weights; dy0 [d][n]; yS [d][n]
+// receives the replayed final state.
+int oracle_grad_f64(int sys, int method, int64_t n, const double* theta, const double* y0,
+                    const int32_t* count, const double* h_rec, int64_t s_cap, const double* dLdy,
+                    double* dtheta, double* dy0, double* yS, int nthreads) {
+  if (!valid_sys(sys, method) || n < 0) return 1;
+  const int d = SYS_D[sys], p = SYS_P[sys];
+  const bool shared = (sys == SYS_MLP);
+  if (nthreads < 1) nthreads = 1;
+  int nt = (int)std::max<int64_t>(1, std::min<int64_t>(nthreads, n));
+  std::vector<std::vector<double>> partial(shared ? nt : 0, std::vector<double>(p, 0.0));
+  parallel_for(n, nt, [&](int tid, int64_t lo, int64_t hi) {
+    std::vector<double> th(p), thb(p);
+    double a0[MAXD], ab[MAXD], aS[MAXD], g[MAXD];
+    for (int64_t k = lo; k < hi; ++k) {
+      for (int i = 0; i < p; ++i) th[i] = shared ? theta[i] : theta[i * n + k];
+      for (int c = 0; c < d; ++c) {
+        a0[c] = y0[c * n + k];
+        g[c] = dLdy[c * n + k];
+      }
+      grad_one(sys, method, th.data(), a0, count[k], h_rec + k * s_cap, g, thb.data(), ab, aS);
+      if (shared)
+        for (int i = 0; i < p; ++i) partial[tid][i] += thb[i];
+      else
+        for (int i = 0; i < p; ++i) dtheta[i * n + k] = thb[i];
+      for (int c = 0; c < d; ++c) {
+        dy0[c * n + k] = ab[c];
+        yS[c * n + k] = aS[c];
+      }
+    }
+  });
+  if (shared) {
+    for (int i = 0; i < p; ++i) {
+      double s = 0.0;
+      for (int t = 0; t < nt; ++t) s += partial[t][i];
+      dtheta[i] = s;
+    }
+  }
+  return 0;
+}
+
+// One attempted step from y with step h (no acceptance decision): returns the
+// new state and the embedded error estimate.  For tests of the pairs.
+int oracle_step_f64(int sys, int method, const double* th, const double* y, double h,
+                    double* ynew, double* err) {
+  if (!valid_sys(sys, method)) return 1;
+  const int d = SYS_D[sys];
+  double k[7][MAXD], F2[MAXD];
+  rhs(sys, th, y, k[0]);
+  if (method == M_TSIT5)
+    tsit5_step(sys, th, d, y, h, k, ynew, err);
+  else
+    ros23_step(sys, th, d, y, h, k[0], ynew, F2, err);
+  return 0;
+}
+
+// Right-hand side and Jacobian at single points (for tests of the fields).
+int oracle_rhs_f64(int sys, const double* th, const double* y, double* dy) {
+  if (sys < 0 || sys >= SYS_COUNT) return 1;
+  rhs(sys, th, y, dy);
+  return 0;
+}
+int oracle_jac_f64(int sys, const double* th, const double* y, double* J) {
+  if (sys < 0 || sys >= SYS_COUNT) return 1;
+  return jac(sys, th, y, J) ? 0 : 1;
+}
+
+}  // extern "C"

@@ -1,0 +1,166 @@
+"""Pins of the oracle's Runge-Kutta and Rosenbrock coefficients.
+
+The pages (arXiv 2609.02876, Sec. 2.1 and Sec. 3.1) name the Tsit5 pair -- a
+fifth-order explicit pair with s = 7 stages whose last stage is reused (FSAL)
+-- and the Rosenbrock23 method, but print neither table.  The oracle takes the
+values from the primary sources; these tests pin them to what the mathematics
+fixes: Butcher's order conditions (enumerated here over rooted trees, with no
+code from the oracle), the FSAL structure, the null-space structure of the
+error weights, and the Rosenbrock23 stability function.
+"""
+import itertools
+from functools import lru_cache
+
+import numpy as np
+import pytest
+
+
+# --- rooted trees and elementary weights (Butcher) ---------------------------
+@lru_cache(None)
+def trees(order):
+    """All rooted trees with `order` vertices, as sorted tuples of child trees."""
+    if order == 1:
+        return ((),)
+    out = set()
+
+    def forests(rem, min_key):
+        if rem == 0:
+            yield ()
+            return
+        for m in range(1, rem + 1):
+            for t in trees(m):
+                key = (m, t)
+                if min_key is not None and key < min_key:
+                    continue
+                for rest in forests(rem - m, key):
+                    yield ((m, t),) + rest
+
+    for f in forests(order - 1, None):
+        out.add(tuple(sorted(t for _, t in f)))
+    return tuple(sorted(out))
+
+
+def tree_order(t):
+    return 1 + sum(tree_order(s) for s in t)
+
+
+def density(t):
+    g = tree_order(t)
+    for s in t:
+        g *= density(s)
+    return g
+
+
+def stage_weights(A, t):
+    v = np.ones(A.shape[0])
+    for s in t:
+        v = v * (A @ stage_weights(A, s))
+    return v
+
+
+def residuals(A, b, max_order):
+    res = []
+    for p in range(1, max_order + 1):
+        for t in trees(p):
+            res.append(b @ stage_weights(A, t) - 1.0 / density(t))
+    return np.array(res)
+
+
+def test_tree_counts():
+    # Number of rooted trees of order 1..5 is 1, 1, 2, 4, 9 (OEIS A000081).
+    assert [len(trees(p)) for p in range(1, 6)] == [1, 1, 2, 4, 9]
+
+
+def test_tsit5_row_sums_and_fsal(orc):
+    c, A, b, bt = orc.tsit5_table()
+    assert np.max(np.abs(A.sum(axis=1) - c)) < 1e-15
+    assert np.all(np.triu(A) == 0.0)  # explicit
+    assert b[6] == 0.0 and c[6] == 1.0  # the 7th stage sits at y_new (FSAL)
+    assert np.array_equal(A[6], b)
+    assert c[5] == 1.0
+
+
+def test_tsit5_fifth_order(orc):
+    c, A, b, bt = orc.tsit5_table()
+    r = residuals(A, b, 5)
+    assert r.size == 17
+    assert np.max(np.abs(r)) < 5e-14
+
+
+def test_tsit5_embedded_fourth_order(orc):
+    c, A, b, bt = orc.tsit5_table()
+    bhat = b - bt
+    assert np.max(np.abs(residuals(A, bhat, 4))) < 5e-14
+    # ... and genuinely not fifth order, so e = y_new - yhat_new is O(h^5)
+    assert np.max(np.abs(residuals(A, bhat, 5)[8:])) > 1e-4
+
+
+def test_tsit5_error_weights_span_the_null_space(orc):
+    # b - bhat annihilates every order <= 4 condition; that null space is 1-D,
+    # so the error weights are fixed up to one scale (bt_7 = 1/66 is the
+    # primary source's normalisation: parity unpinned by the pages).
+    c, A, b, bt = orc.tsit5_table()
+    M = np.array([stage_weights(A, t) for p in range(1, 5) for t in trees(p)])
+    s = np.linalg.svd(M, compute_uv=False)
+    assert s[-1] < 1e-14 * s[0] and s[-2] > 1e-3
+    assert np.max(np.abs(M @ bt)) < 1e-15 * 1e2
+    assert bt[6] == pytest.approx(1.0 / 66.0, rel=1e-15)
+
+
+def test_order_conditions_catch_a_wrong_coefficient(orc):
+    # Planted mistakes (in a copy of the table, on the CPU): any single
+    # coefficient off in its 8th significant digit, or with its sign flipped,
+    # must break a fifth-order condition or a row sum.
+    c, A, b, bt = orc.tsit5_table()
+    for i, j in itertools.product(range(1, 7), range(6)):
+        if j >= i:
+            continue
+        for bad in (A[i, j] * (1 + 1e-8), -A[i, j]):
+            A2 = A.copy()
+            A2[i, j] = bad
+            b2 = A2[6].copy()
+            row = np.max(np.abs(A2.sum(axis=1) - c))
+            cond = np.max(np.abs(residuals(A2, b2, 5)))
+            assert max(row, cond) > 1e-12, (i, j)
+
+
+def test_ros23_l_stability_root(orc):
+    # One Rosenbrock23 step on y' = lambda y gives
+    #   R(z) = 1 + z w (2 - w + z w / 2),  w = 1 / (1 - d z),
+    # whose limit at z -> -inf is 1 - 2/d + 1/(2 d^2); L-stability makes it 0,
+    # i.e. d is the smaller root 1 - sqrt(2)/2 = 1/(2 + sqrt 2).
+    d, e32 = orc.ros23_consts()
+    assert abs(1 - 2 / d + 1 / (2 * d * d)) < 1e-14
+    assert d == pytest.approx(1 - np.sqrt(2) / 2, rel=1e-15)
+    assert e32 == pytest.approx(6 + np.sqrt(2), rel=1e-15)
+
+
+def test_ros23_stability_function(orc):
+    d, _ = orc.ros23_consts()
+    for z in (-1e-3, -0.1, -1.0, -7.0, -1e3, -1e8, 0.05):
+        w = 1.0 / (1.0 - d * z)
+        R = 1.0 + z * w * (2.0 - w + 0.5 * z * w)
+        ynew, _ = orc.step("decay", "rosenbrock23", [-z], [1.0], 1.0)  # h=1, theta=-z
+        assert ynew[0] == pytest.approx(R, rel=1e-13, abs=1e-15)
+    big, _ = orc.step("decay", "rosenbrock23", [1e12], [1.0], 1.0)
+    assert abs(big[0]) < 1e-11  # L-stable: R(-inf) = 0
+    # order 2: R(z) - exp(z) = O(z^3)
+    for z in (-1e-2, -5e-3):
+        ynew, _ = orc.step("decay", "rosenbrock23", [-z], [1.0], 1.0)
+        assert abs(ynew[0] - np.exp(z)) < 0.2 * abs(z) ** 3
+
+
+def _tsit5_R(orc, z):
+    c, A, b, bt = orc.tsit5_table()
+    return 1.0 + z * b @ np.linalg.solve(np.eye(7) - z * A, np.ones(7))
+
+
+def test_tsit5_stability_function_from_table(orc):
+    # The replay of y' = -theta y is y_{n+1} = R(-theta h) y_n exactly (up to
+    # rounding), with R the stability polynomial of the table.
+    for z in (-0.01, -0.3, -1.0, -2.5):
+        ynew, _ = orc.step("decay", "tsit5", [-z], [1.0], 1.0)
+        assert ynew[0] == pytest.approx(_tsit5_R(orc, z), rel=2e-15)
+        # fifth order: R(z) - exp(z) = O(z^6)
+    for z in (-0.05, -0.1):
+        assert abs(_tsit5_R(orc, z) - np.exp(z)) < 1e-2 * abs(z) ** 6
