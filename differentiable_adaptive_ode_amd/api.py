@@ -1,0 +1,182 @@
+"""Torch-facing helpers over the C ABI: device buffers come from PyTorch's
+caching allocator and the stream is torch's current stream; all compute is in
+libdao's kernels.
+
+    rec, y1 = solve("lorenz63", "tsit5", theta, y0, 0.0, 2.0, rtol=1e-8, atol=1e-10)
+    g = cotangent(y1, target)                  # dL/dy1 of 1/2 |y1 - target|^2
+    dtheta, dy0 = grad(rec, g)                 # discrete adjoint on the recorded mesh
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+_TORCH_DTYPE = {"f64": torch.float64, "f32": torch.float32}
+
+
+def _dtype_name(t: torch.Tensor) -> str:
+    if t.dtype == torch.float64:
+        return "f64"
+    if t.dtype == torch.float32:
+        return "f32"
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("all arrays must be device (cuda) tensors")
+            if not t.is_contiguous():
+                raise ValueError("all arrays must be contiguous")
+
+
+@dataclass
+class Record:
+    """Step record of one ensemble solve (caller-owned device tensors).
+
+    h, t: [n, s_cap] accepted step sizes / start times (rows past count unused)
+    count, nrej, status: [n] int32
+    The solve's inputs are kept so that grad() can replay the mesh.
+    """
+
+    system: str
+    method: str
+    dtype: str
+    theta: torch.Tensor
+    y0: torch.Tensor
+    t0: float
+    t1: float
+    h: torch.Tensor
+    t: torch.Tensor | None
+    count: torch.Tensor
+    nrej: torch.Tensor
+    status: torch.Tensor
+
+    @property
+    def n(self):
+        return self.count.shape[0]
+
+    @property
+    def s_cap(self):
+        return self.h.shape[1]
+
+    def c_struct(self):
+        return _lib.dao_record(self.s_cap, _ptr(self.t), _ptr(self.h), _ptr(self.count),
+                               _ptr(self.nrej), _ptr(self.status))
+
+
+class Workspace:
+    """Grow-only device scratch shared by calls on one stream."""
+
+    def __init__(self, device=None):
+        self.buf = None
+        self.device = device
+
+    def get(self, nbytes: int, device) -> torch.Tensor:
+        nbytes = max(int(nbytes), 256)
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws: dict = {}
+
+
+def _ws(device, ws=None):
+    if ws is not None:
+        return ws
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace()
+    return _default_ws[key]
+
+
+def alloc_record(n: int, s_cap: int, dtype: str, device, with_t: bool = True) -> dict:
+    td = _TORCH_DTYPE[dtype]
+    return dict(h=torch.empty((n, s_cap), dtype=td, device=device),
+                t=torch.empty((n, s_cap), dtype=td, device=device) if with_t else None,
+                count=torch.empty(n, dtype=torch.int32, device=device),
+                nrej=torch.empty(n, dtype=torch.int32, device=device),
+                status=torch.empty(n, dtype=torch.int32, device=device))
+
+
+def solve(system: str, method: str, theta: torch.Tensor, y0: torch.Tensor, t0: float, t1: float,
+          rtol: float, atol: float, dt0: float = 0.0, max_steps: int = 100000, s_cap: int = 4096,
+          record_t: bool = True, out=None, rec_buffers=None, workspace=None, stream=None):
+    """Adaptive solve with record.  Returns (Record, y1)."""
+    _check_dev(theta, y0)
+    dtype = _dtype_name(y0)
+    if theta.dtype != y0.dtype:
+        raise TypeError("theta and y0 must share a dtype")
+    d, p, shared = _lib.dao_system_dims(_lib.SYSTEMS[system])
+    n = y0.shape[1] if y0.dim() == 2 else 0
+    if y0.shape != (d, n):
+        raise ValueError(f"y0 must be [{d}, n]")
+    if tuple(theta.shape) != ((p,) if shared else (p, n)):
+        raise ValueError("theta has the wrong shape")
+    dev = y0.device
+    y1 = torch.empty_like(y0) if out is None else out
+    bufs = rec_buffers if rec_buffers is not None else alloc_record(n, s_cap, dtype, dev, record_t)
+    rec = Record(system, method, dtype, theta, y0, float(t0), float(t1), bufs["h"], bufs.get("t"),
+                 bufs["count"], bufs["nrej"], bufs["status"])
+    ws = _ws(dev, workspace)
+    sysid, mid, did = _lib.SYSTEMS[system], _lib.METHODS[method], _lib.DTYPES[dtype]
+    nb = _lib.dao_solve_workspace_size(sysid, mid, did, n)
+    buf = ws.get(nb, dev)
+    tol = _lib.dao_tol(float(rtol), float(atol), float(dt0), int(max_steps))
+    crec = rec.c_struct()
+    _lib.check(_lib.dao_solve(sysid, mid, did, n, _ptr(theta), _ptr(y0), float(t0), float(t1),
+                              tol, _ptr(y1), crec, _ptr(buf), buf.numel(), _stream(stream)))
+    return rec, y1
+
+
+def grad(rec: Record, dLdy1: torch.Tensor, theta: torch.Tensor | None = None, s_max: int | None = None,
+         out_theta=None, out_y0=None, workspace=None, stream=None):
+    """dL/dtheta and dL/dy0 by the discrete adjoint on rec's mesh.
+
+    theta: parameters to differentiate at (default: the solve's theta).
+    s_max: an upper bound on rec.count (default: read back from the device).
+    """
+    _check_dev(dLdy1)
+    th = rec.theta if theta is None else theta
+    _check_dev(th)
+    n = rec.n
+    if s_max is None:
+        s_max = int(rec.count.max().item()) if n > 0 else 0
+    s_max = min(int(s_max), rec.s_cap)
+    sysid, mid, did = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
+    dev = dLdy1.device
+    dth = torch.empty_like(th) if out_theta is None else out_theta
+    dy0 = torch.empty_like(rec.y0) if out_y0 is None else out_y0
+    ws = _ws(dev, workspace)
+    nb = _lib.dao_grad_workspace_size(sysid, mid, did, n, s_max)
+    buf = ws.get(nb, dev)
+    crec = rec.c_struct()
+    _lib.check(_lib.dao_grad(sysid, mid, did, n, _ptr(th), _ptr(rec.y0), crec, s_max, _ptr(dLdy1),
+                             _ptr(dth), _ptr(dy0), _ptr(buf), buf.numel(), _stream(stream)))
+    return dth, dy0
+
+
+def cotangent(y1: torch.Tensor, target: torch.Tensor, scale: float = 1.0, d_used: int | None = None,
+              out=None, stream=None):
+    """dL/dy1 = scale * (y1 - target) on the first d_used components, 0 elsewhere."""
+    _check_dev(y1, target)
+    d, n = y1.shape
+    d_used = d if d_used is None else d_used
+    o = torch.empty_like(y1) if out is None else out
+    _lib.check(_lib.dao_sqerr_cotangent(_lib.DTYPES[_dtype_name(y1)], n, d, d_used, _ptr(y1),
+                                        _ptr(target), float(scale), _ptr(o), _stream(stream)))
+    return o

@@ -1,0 +1,433 @@
+// C ABI of the ensemble ODE library (declared in include/dao.h): argument
+// checks, workspace carving, kernel dispatch.  No device memory is allocated
+// here; every buffer is the caller's.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/dao.h"
+#include "kernels.hpp"
+
+namespace dao {
+
+// ------------------------------------------------------------- small kernels
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// bucket = (s_max + 1) - min(count, s_max + 1): larger counts come first.
+__device__ __forceinline__ int64_t bucket_of(int32_t c, int64_t s_max) {
+  int64_t cc = c < 0 ? 0 : (int64_t)c;
+  if (cc > s_max + 1) cc = s_max + 1;
+  return (s_max + 1) - cc;
+}
+
+__global__ void count_hist_kernel(const int32_t* count, int64_t n, int64_t s_max, uint32_t* hist) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) atomicAdd(&hist[bucket_of(count[i], s_max)], 1u);
+}
+
+// In-place exclusive scan of hist[0..nb) by one 1024-thread workgroup.
+__global__ void __launch_bounds__(1024) scan_buckets_kernel(uint32_t* hist, int64_t nb) {
+  __shared__ uint32_t part[1024];
+  const int tid = threadIdx.x;
+  const int64_t chunk = (nb + 1023) / 1024;
+  const int64_t lo = tid * chunk;
+  const int64_t hi = (lo + chunk < nb) ? lo + chunk : nb;
+  uint32_t s = 0;
+  for (int64_t i = lo; i < hi; ++i) s += hist[i];
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const uint32_t v = (tid >= off) ? part[tid - off] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  uint32_t run = part[tid] - s;  // exclusive prefix of this thread's chunk
+  for (int64_t i = lo; i < hi; ++i) {
+    const uint32_t v = hist[i];
+    hist[i] = run;
+    run += v;
+  }
+}
+
+__global__ void scatter_perm_kernel(const int32_t* count, int64_t n, int64_t s_max, uint32_t* off,
+                                    int32_t* perm) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) perm[atomicAdd(&off[bucket_of(count[i], s_max)], 1u)] = (int32_t)i;
+}
+
+template <class R>
+__global__ void sqerr_cotangent_kernel(int64_t n, int d, int d_used, const R* y1, const R* tgt,
+                                       R scale, R* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n * d) return;
+  const int c = (int)(i / n);
+  out[i] = (c < d_used) ? scale * (y1[i] - tgt[i]) : R(0);
+}
+
+}  // namespace dao
+
+using namespace dao;
+
+// ------------------------------------------------------------- error state
+namespace {
+
+thread_local char g_err[512] = "";
+
+dao_status fail(dao_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dao_status check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DAO_OK;
+  return fail(DAO_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+const int SYS_D[6] = {1, 2, 3, 4, 3, 6};
+const int SYS_P[6] = {1, 4, 3, 4740, 3, 3};
+
+bool sys_ok(int sys) { return sys >= 0 && sys <= 5; }
+
+struct DevInfo {
+  int cus = 0;
+};
+
+DevInfo dev_info() {
+  static std::mutex mu;
+  static std::vector<DevInfo> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DevInfo{256};
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1);
+  if (cache[dev].cus == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev].cus = v;
+  }
+  return cache[dev];
+}
+
+constexpr int BLOCK = 256;
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Resident workgroups for a kernel at BLOCK threads.
+template <class K>
+int64_t resident_blocks(K kernel) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, BLOCK, 0) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
+  return (int64_t)per_cu * dev_info().cus;
+}
+
+// --------------------------------------------------------- typed launchers
+template <class R, class Sys, int M>
+dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0, double t1,
+                        const dao_tol* tol, void* y1, const dao_record* rec, void* ws,
+                        hipStream_t stream) {
+  SolveArgs<R> a;
+  a.n = n;
+  a.theta = (const R*)theta;
+  a.y0 = (const R*)y0;
+  a.t0 = R(t0);
+  a.t1 = R(t1);
+  a.rtol = R(tol->rtol);
+  a.atol = R(tol->atol);
+  a.dt0 = R(tol->dt0);
+  a.max_steps = tol->max_steps;
+  a.y1 = (R*)y1;
+  a.s_cap = rec->s_cap;
+  a.t_rec = (R*)rec->t;
+  a.h_rec = (R*)rec->h;
+  a.count = rec->count;
+  a.nrej = rec->nrej;
+  a.status = rec->status;
+  a.queue = (unsigned long long*)ws;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)ws, (int64_t)2, 0u);
+  auto kern = solve_kernel<R, Sys, M>;
+  int64_t blocks = (n + BLOCK - 1) / BLOCK;
+  const int64_t res = resident_blocks(kern);
+  if (blocks > res) blocks = res;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), 0, stream, a);
+  return check_hip(hipGetLastError(), "solve kernel launch");
+}
+
+template <class R, int D>
+size_t grad_slot_bytes(int64_t s_max) {
+  return (size_t)(s_max > 0 ? s_max : 1) * D * WAVE * sizeof(R);
+}
+
+size_t grad_header_bytes(int64_t n, int64_t s_max) {
+  return align_up(16) + align_up((size_t)(s_max + 2) * 4) + align_up((size_t)(n > 0 ? n : 1) * 4);
+}
+
+template <class R, class Sys, int M>
+dao_status launch_grad(int64_t n, const void* theta, const void* y0, const dao_record* rec,
+                       int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  constexpr int D = Sys::D;
+  char* base = (char*)ws;
+  unsigned long long* groups = (unsigned long long*)base;
+  uint32_t* hist = (uint32_t*)(base + align_up(16));
+  int32_t* perm = (int32_t*)(base + align_up(16) + align_up((size_t)(s_max + 2) * 4));
+  const size_t hdr = grad_header_bytes(n, s_max);
+  R* scratch = (R*)(base + hdr);
+  const size_t slot = grad_slot_bytes<R, D>(s_max);
+  int64_t slots = (int64_t)((ws_bytes - hdr) / slot);
+
+  auto kern = grad_kernel<R, Sys, M>;
+  const int64_t ngroups = (n + WAVE - 1) / WAVE;
+  const int64_t waves_per_block = BLOCK / WAVE;
+  int64_t blocks = (ngroups + waves_per_block - 1) / waves_per_block;
+  const int64_t res = resident_blocks(kern);
+  if (blocks > res) blocks = res;
+  if (blocks > slots / waves_per_block) blocks = slots / waves_per_block;
+  if (blocks < 1) return fail(DAO_EWORKSPACE, "dao_grad: workspace too small");
+
+  const int64_t nb = s_max + 2;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream,
+                     hist, nb, 0u);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)groups, (int64_t)2, 0u);
+  const unsigned nblk = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(count_hist_kernel, dim3(nblk), dim3(256), 0, stream, rec->count, n, s_max, hist);
+  hipLaunchKernelGGL(scan_buckets_kernel, dim3(1), dim3(1024), 0, stream, hist, nb);
+  hipLaunchKernelGGL(scatter_perm_kernel, dim3(nblk), dim3(256), 0, stream, rec->count, n, s_max,
+                     hist, perm);
+
+  GradArgs<R> a;
+  a.n = n;
+  a.theta = (const R*)theta;
+  a.y0 = (const R*)y0;
+  a.s_cap = rec->s_cap;
+  a.h_rec = (const R*)rec->h;
+  a.count = rec->count;
+  a.status = rec->status;
+  a.s_max = s_max;
+  a.dLdy1 = (const R*)dLdy1;
+  a.dLdtheta = (R*)dLdtheta;
+  a.dLdy0 = (R*)dLdy0;
+  a.scratch = scratch;
+  a.perm = perm;
+  a.groups = groups;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), 0, stream, a);
+  return check_hip(hipGetLastError(), "grad kernel launch");
+}
+
+// Dispatch table over (system, method, dtype).
+template <class R, template <class> class S, int M>
+struct Entry {
+  static dao_status solve(int64_t n, const void* th, const void* y0, double t0, double t1,
+                          const dao_tol* tol, void* y1, const dao_record* rec, void* ws,
+                          hipStream_t st) {
+    return launch_solve<R, S<R>, M>(n, th, y0, t0, t1, tol, y1, rec, ws, st);
+  }
+  static dao_status grad(int64_t n, const void* th, const void* y0, const dao_record* rec,
+                         int64_t s_max, const void* g, void* dth, void* dy0, void* ws,
+                         size_t wsb, hipStream_t st) {
+    return launch_grad<R, S<R>, M>(n, th, y0, rec, s_max, g, dth, dy0, ws, wsb, st);
+  }
+  static size_t slot_bytes(int64_t s_max) { return grad_slot_bytes<R, S<R>::D>(s_max); }
+  static int64_t resident_waves() {
+    return resident_blocks(grad_kernel<R, S<R>, M>) * (BLOCK / WAVE);
+  }
+};
+
+typedef dao_status (*solve_fn)(int64_t, const void*, const void*, double, double, const dao_tol*,
+                               void*, const dao_record*, void*, hipStream_t);
+typedef dao_status (*grad_fn)(int64_t, const void*, const void*, const dao_record*, int64_t,
+                              const void*, void*, void*, void*, size_t, hipStream_t);
+typedef size_t (*slot_fn)(int64_t);
+typedef int64_t (*res_fn)();
+
+struct Impl {
+  solve_fn solve;
+  grad_fn grad;
+  slot_fn slot;
+  res_fn resident;
+};
+
+template <class R, template <class> class S, int M>
+Impl make_impl() {
+  return Impl{&Entry<R, S, M>::solve, &Entry<R, S, M>::grad, &Entry<R, S, M>::slot_bytes,
+              &Entry<R, S, M>::resident_waves};
+}
+
+const Impl* find_impl(int sys, int method, int dtype) {
+  static Impl table[6][2][2];
+  static bool init = false;
+  static std::mutex mu;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!init) {
+    std::memset(table, 0, sizeof(table));
+    table[DAO_SYS_DECAY][M_TSIT5][DAO_F64] = make_impl<double, Decay, M_TSIT5>();
+    table[DAO_SYS_DECAY][M_TSIT5][DAO_F32] = make_impl<float, Decay, M_TSIT5>();
+    table[DAO_SYS_DECAY][M_ROS23][DAO_F64] = make_impl<double, Decay, M_ROS23>();
+    table[DAO_SYS_DECAY][M_ROS23][DAO_F32] = make_impl<float, Decay, M_ROS23>();
+    table[DAO_SYS_LOTKA_VOLTERRA][M_TSIT5][DAO_F64] = make_impl<double, LotkaVolterra, M_TSIT5>();
+    table[DAO_SYS_LOTKA_VOLTERRA][M_TSIT5][DAO_F32] = make_impl<float, LotkaVolterra, M_TSIT5>();
+    table[DAO_SYS_LOTKA_VOLTERRA][M_ROS23][DAO_F64] = make_impl<double, LotkaVolterra, M_ROS23>();
+    table[DAO_SYS_LOTKA_VOLTERRA][M_ROS23][DAO_F32] = make_impl<float, LotkaVolterra, M_ROS23>();
+    table[DAO_SYS_LORENZ63][M_TSIT5][DAO_F64] = make_impl<double, Lorenz63, M_TSIT5>();
+    table[DAO_SYS_LORENZ63][M_TSIT5][DAO_F32] = make_impl<float, Lorenz63, M_TSIT5>();
+    table[DAO_SYS_LORENZ63][M_ROS23][DAO_F64] = make_impl<double, Lorenz63, M_ROS23>();
+    table[DAO_SYS_LORENZ63][M_ROS23][DAO_F32] = make_impl<float, Lorenz63, M_ROS23>();
+    table[DAO_SYS_ROBERTSON][M_TSIT5][DAO_F64] = make_impl<double, Robertson, M_TSIT5>();
+    table[DAO_SYS_ROBERTSON][M_TSIT5][DAO_F32] = make_impl<float, Robertson, M_TSIT5>();
+    table[DAO_SYS_ROBERTSON][M_ROS23][DAO_F64] = make_impl<double, Robertson, M_ROS23>();
+    table[DAO_SYS_ROBERTSON][M_ROS23][DAO_F32] = make_impl<float, Robertson, M_ROS23>();
+    table[DAO_SYS_LOGHALO][M_TSIT5][DAO_F64] = make_impl<double, LogHalo, M_TSIT5>();
+    table[DAO_SYS_LOGHALO][M_TSIT5][DAO_F32] = make_impl<float, LogHalo, M_TSIT5>();
+    init = true;
+  }
+  if (!sys_ok(sys) || method < 0 || method > 1 || dtype < 0 || dtype > 1) return nullptr;
+  const Impl* im = &table[sys][method][dtype];
+  return im->solve ? im : nullptr;
+}
+
+bool is_fin(double x) { return std::isfinite(x); }
+
+}  // namespace
+
+// ================================================================== C ABI
+extern "C" {
+
+const char* dao_last_error(void) { return g_err; }
+
+const char* dao_version(void) { return "0.1.0 gfx950"; }
+
+dao_status dao_system_dims(dao_system sys, int* d, int* p, int* shared) {
+  if (!sys_ok(sys)) return fail(DAO_EINVAL, "dao_system_dims: unknown system %d", (int)sys);
+  if (d) *d = SYS_D[sys];
+  if (p) *p = SYS_P[sys];
+  if (shared) *shared = (sys == DAO_SYS_MLP);
+  return DAO_OK;
+}
+
+size_t dao_solve_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n) {
+  (void)sys; (void)method; (void)dtype; (void)n;
+  return ALIGN;
+}
+
+dao_status dao_solve(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                     const void* theta, const void* y0, double t0, double t1, const dao_tol* tol,
+                     void* y1, const dao_record* rec, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  g_err[0] = 0;
+  if (!sys_ok(sys)) return fail(DAO_EINVAL, "dao_solve: unknown system %d", (int)sys);
+  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
+    return fail(DAO_EINVAL, "dao_solve: unknown method %d", (int)method);
+  if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "dao_solve: unknown dtype %d", (int)dtype);
+  if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "dao_solve: n = %lld out of range", (long long)n);
+  if (!tol) return fail(DAO_EINVAL, "dao_solve: tol is NULL");
+  if (!(is_fin(t0) && is_fin(t1))) return fail(DAO_EINVAL, "dao_solve: t0/t1 not finite");
+  if (!(t1 >= t0)) return fail(DAO_EINVAL, "dao_solve: t1 < t0");
+  if (!(tol->rtol > 0) || !is_fin(tol->rtol)) return fail(DAO_EINVAL, "dao_solve: rtol must be > 0");
+  if (!(tol->atol > 0) || !is_fin(tol->atol)) return fail(DAO_EINVAL, "dao_solve: atol must be > 0");
+  if (!is_fin(tol->dt0)) return fail(DAO_EINVAL, "dao_solve: dt0 not finite");
+  if (tol->max_steps < 1) return fail(DAO_EINVAL, "dao_solve: max_steps must be >= 1");
+  const Impl* im = find_impl(sys, method, dtype);
+  if (!im) return fail(DAO_EUNSUPPORTED, "dao_solve: system %d with method %d dtype %d is not provided",
+                       (int)sys, (int)method, (int)dtype);
+  if (n == 0) return DAO_OK;
+  if (!theta) return fail(DAO_EINVAL, "dao_solve: theta is NULL");
+  if (!y0) return fail(DAO_EINVAL, "dao_solve: y0 is NULL");
+  if (!y1) return fail(DAO_EINVAL, "dao_solve: y1 is NULL");
+  dao_record none;
+  std::memset(&none, 0, sizeof(none));
+  if (rec) {
+    if (rec->s_cap < 0) return fail(DAO_EINVAL, "dao_solve: rec->s_cap < 0");
+    if (!rec->count) return fail(DAO_EINVAL, "dao_solve: rec->count is NULL");
+    if (!rec->status) return fail(DAO_EINVAL, "dao_solve: rec->status is NULL");
+    if (rec->s_cap > 0 && !rec->h) return fail(DAO_EINVAL, "dao_solve: rec->h is NULL");
+  } else {
+    return fail(DAO_EINVAL, "dao_solve: rec is NULL (count and status are written there)");
+  }
+  if (!workspace || workspace_bytes < dao_solve_workspace_size(sys, method, dtype, n))
+    return fail(DAO_EWORKSPACE, "dao_solve: workspace needs %zu bytes",
+                dao_solve_workspace_size(sys, method, dtype, n));
+  return im->solve(n, theta, y0, t0, t1, tol, y1, rec, workspace, (hipStream_t)stream);
+}
+
+size_t dao_grad_workspace_min(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                              int64_t s_max) {
+  const Impl* im = find_impl(sys, method, dtype);
+  if (!im || n < 0 || s_max < 0) return 0;
+  return grad_header_bytes(n, s_max) + (size_t)(BLOCK / WAVE) * im->slot(s_max);
+}
+
+size_t dao_grad_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                               int64_t s_max) {
+  const Impl* im = find_impl(sys, method, dtype);
+  if (!im || n < 0 || s_max < 0) return 0;
+  int64_t waves = (n + WAVE - 1) / WAVE;
+  waves = (waves + BLOCK / WAVE - 1) / (BLOCK / WAVE) * (BLOCK / WAVE);
+  const int64_t res = im->resident();
+  if (waves > res) waves = res;
+  if (waves < BLOCK / WAVE) waves = BLOCK / WAVE;
+  return grad_header_bytes(n, s_max) + (size_t)waves * im->slot(s_max);
+}
+
+dao_status dao_grad(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                    const void* theta, const void* y0, const dao_record* rec, int64_t s_max,
+                    const void* dLdy1, void* dLdtheta, void* dLdy0, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!sys_ok(sys)) return fail(DAO_EINVAL, "dao_grad: unknown system %d", (int)sys);
+  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
+    return fail(DAO_EINVAL, "dao_grad: unknown method %d", (int)method);
+  if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "dao_grad: unknown dtype %d", (int)dtype);
+  if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "dao_grad: n = %lld out of range", (long long)n);
+  if (!rec) return fail(DAO_EINVAL, "dao_grad: rec is NULL");
+  if (rec->s_cap < 0) return fail(DAO_EINVAL, "dao_grad: rec->s_cap < 0");
+  if (s_max < 0 || s_max > rec->s_cap) return fail(DAO_EINVAL, "dao_grad: s_max must be in [0, rec->s_cap]");
+  const Impl* im = find_impl(sys, method, dtype);
+  if (!im) return fail(DAO_EUNSUPPORTED, "dao_grad: system %d with method %d dtype %d is not provided",
+                       (int)sys, (int)method, (int)dtype);
+  if (n == 0) return DAO_OK;
+  if (!theta) return fail(DAO_EINVAL, "dao_grad: theta is NULL");
+  if (!y0) return fail(DAO_EINVAL, "dao_grad: y0 is NULL");
+  if (!rec->count) return fail(DAO_EINVAL, "dao_grad: rec->count is NULL");
+  if (s_max > 0 && !rec->h) return fail(DAO_EINVAL, "dao_grad: rec->h is NULL");
+  if (!dLdy1) return fail(DAO_EINVAL, "dao_grad: dLdy1 is NULL");
+  const size_t need = dao_grad_workspace_min(sys, method, dtype, n, s_max);
+  if (!workspace || workspace_bytes < need)
+    return fail(DAO_EWORKSPACE, "dao_grad: workspace needs at least %zu bytes", need);
+  return im->grad(n, theta, y0, rec, s_max, dLdy1, dLdtheta, dLdy0, workspace, workspace_bytes,
+                  (hipStream_t)stream);
+}
+
+dao_status dao_sqerr_cotangent(dao_dtype dtype, int64_t n, int d, int d_used, const void* y1,
+                               const void* target, double scale, void* out, void* stream) {
+  g_err[0] = 0;
+  if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "dao_sqerr_cotangent: unknown dtype");
+  if (n < 0 || d < 1 || d_used < 0 || d_used > d)
+    return fail(DAO_EINVAL, "dao_sqerr_cotangent: bad sizes");
+  if (!is_fin(scale)) return fail(DAO_EINVAL, "dao_sqerr_cotangent: scale not finite");
+  if (n == 0) return DAO_OK;
+  if (!y1 || !target || !out) return fail(DAO_EINVAL, "dao_sqerr_cotangent: NULL array");
+  const int64_t tot = n * d;
+  const unsigned blocks = (unsigned)((tot + 255) / 256);
+  if (dtype == DAO_F64)
+    hipLaunchKernelGGL(sqerr_cotangent_kernel<double>, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       n, d, d_used, (const double*)y1, (const double*)target, scale, (double*)out);
+  else
+    hipLaunchKernelGGL(sqerr_cotangent_kernel<float>, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       n, d, d_used, (const float*)y1, (const float*)target, (float)scale, (float*)out);
+  return check_hip(hipGetLastError(), "cotangent kernel launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,331 @@
+// Solve and gradient kernels: one trajectory per lane.
+//
+// Solve (arXiv 2609.02876 Sec. 2.1 loop, Sec. 3.1 record): a persistent grid
+// of wavefronts pulls trajectories from a global work queue.  Whenever lanes
+// of a wavefront finish their trajectory, the wavefront ballots the idle
+// lanes, claims that many new trajectory indices with ONE atomic add, and
+// hands them out by rank among the idle lanes (mbcnt).  So a wavefront never
+// waits for its slowest trajectory while work remains.  Each accepted step
+// appends (t_n, h_n) to the lane's own record row.
+//
+// Gradient (Sec. 3.1 replay chain, reverse sweep): trajectories are visited in
+// order of decreasing step count, 64 at a time (one wavefront); the 64 lanes
+// replay their meshes in lockstep, store every state y_j in a per-wavefront
+// scratch tile laid out [step][component][lane] (each store and load is one
+// contiguous 512-byte row), then sweep backward, recomputing each step's
+// stages from y_j.
+#pragma once
+
+#include "common.hpp"
+#include "ros23.hpp"
+#include "systems.hpp"
+#include "tsit5.hpp"
+
+namespace dao {
+
+enum Method : int { M_TSIT5 = 0, M_ROS23 = 1 };
+
+template <class R>
+struct SolveArgs {
+  int64_t n;
+  const R* theta;
+  const R* y0;
+  R t0, t1, rtol, atol, dt0;
+  int64_t max_steps;
+  R* y1;
+  int64_t s_cap;
+  R* t_rec;
+  R* h_rec;
+  int32_t* count;
+  int32_t* nrej;
+  int32_t* status;
+  unsigned long long* queue;
+};
+
+template <class R>
+struct GradArgs {
+  int64_t n;
+  const R* theta;
+  const R* y0;
+  int64_t s_cap;
+  const R* h_rec;
+  const int32_t* count;
+  const int32_t* status;
+  int64_t s_max;
+  const R* dLdy1;
+  R* dLdtheta;
+  R* dLdy0;
+  R* scratch;
+  const int32_t* perm;
+  unsigned long long* groups;
+};
+
+template <class R, int D>
+__device__ __forceinline__ R mean_sq(const R (&e)[D], const R (&sc)[D]) {
+  R r = e[0] / sc[0];
+  R acc = r * r;
+#pragma unroll
+  for (int c = 1; c < D; ++c) {
+    r = e[c] / sc[c];
+    acc = fmaR(r, r, acc);
+  }
+  return acc / R(D);
+}
+
+// Starting step: Hairer, Norsett & Wanner, Solving ODEs I, Sec. II.4, with
+// exponent 1/order; truncated like the controller factors.
+template <class R, class Sys>
+__device__ R initial_step(const Sys& sys, const R (&y0)[Sys::D], const R (&f0)[Sys::D], R span,
+                          R rtol, R atol, int order) {
+  constexpr int D = Sys::D;
+  R sc[D], y1[D], f1[D], df[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) sc[c] = fmaR(rtol, absR(y0[c]), atol);
+  R d0 = sqrtR(mean_sq<R, D>(y0, sc));
+  R d1 = sqrtR(mean_sq<R, D>(f0, sc));
+  R h0 = (d0 < R(1e-5) || d1 < R(1e-5)) ? R(1e-6) : R(0.01) * (d0 / d1);
+  h0 = (span < h0) ? span : h0;
+#pragma unroll
+  for (int c = 0; c < D; ++c) y1[c] = fmaR(h0, f0[c], y0[c]);
+  sys.f(y1, f1);
+#pragma unroll
+  for (int c = 0; c < D; ++c) df[c] = f1[c] - f0[c];
+  R d2 = sqrtR(mean_sq<R, D>(df, sc)) / h0;
+  R m = (d1 < d2) ? d2 : d1;
+  R h1;
+  if (m <= R(1e-15)) {
+    R t = h0 * R(1e-3);
+    h1 = (R(1e-6) < t) ? t : R(1e-6);
+  } else {
+    h1 = powR(R(0.01) / m, R(1) / R(order));
+  }
+  R h100 = R(100) * h0;
+  return truncBits((h1 < h100) ? h1 : h100);
+}
+
+template <class R, class Sys, int METHOD>
+__global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
+  constexpr int D = Sys::D;
+  constexpr int ORDER = (METHOD == M_TSIT5) ? 5 : 2;
+  const R expo = (METHOD == M_TSIT5) ? R(-0.1) : R(-1.0 / 6.0);
+  const int lane = laneId();
+
+  Sys sys;
+  R y[D];
+  R k[7][D];  // Tsit5: stages, k[0] = f(y) (FSAL); Rosenbrock23: k[0] = F0 = f(y)
+  R t = R(0), h = R(0);
+  int32_t nacc = 0, nrej = 0;
+  int64_t attempts = 0;
+  bool prev_rej = false;
+  int64_t traj = -1;
+  bool live = true;
+
+  auto finish = [&](int32_t st) {
+#pragma unroll
+    for (int c = 0; c < D; ++c) a.y1[c * a.n + traj] = (st == TRAJ_OK) ? y[c] : nanR(R(0));
+    a.count[traj] = nacc;
+    if (a.nrej) a.nrej[traj] = nrej;
+    a.status[traj] = st;
+    traj = -1;
+  };
+
+  for (;;) {
+    // ---- refill idle lanes from the work queue: one atomic per wavefront
+    const bool need = live && traj < 0;
+    const unsigned long long m = __ballot(need);
+    if (m) {
+      const int leader = __ffsll((unsigned long long)m) - 1;
+      unsigned long long base = 0;
+      if (lane == leader) base = atomicAdd(a.queue, (unsigned long long)__popcll(m));
+      base = __shfl(base, leader);
+      if (need) {
+        const unsigned long long kk = base + (unsigned long long)__popcll(m & ((1ull << lane) - 1ull));
+        if (kk < (unsigned long long)a.n) {
+          traj = (int64_t)kk;
+          sys.load(a.theta, a.n, traj);
+#pragma unroll
+          for (int c = 0; c < D; ++c) y[c] = a.y0[c * a.n + traj];
+          t = a.t0;
+          nacc = 0;
+          nrej = 0;
+          attempts = 0;
+          prev_rej = false;
+          if (!(a.t1 > a.t0)) {
+            finish(TRAJ_OK);
+          } else {
+            sys.f(y, k[0]);
+            h = (a.dt0 > R(0)) ? a.dt0 : initial_step<R, Sys>(sys, y, k[0], a.t1 - a.t0, a.rtol, a.atol, ORDER);
+          }
+        } else {
+          live = false;
+        }
+      }
+    }
+    if (__ballot(live) == 0ull) break;
+    if (traj < 0) continue;
+
+    // ---- one attempted step
+    if (attempts >= a.max_steps) {
+      finish(TRAJ_MAX_STEPS);
+      continue;
+    }
+    ++attempts;
+    const bool last = (t + h >= a.t1);
+    const R hs = last ? (a.t1 - t) : h;
+    if (!finiteR(hs)) {
+      finish(TRAJ_NONFINITE);
+      continue;
+    }
+    if (!(t + hs > t)) {
+      finish(TRAJ_DT_UNDERFLOW);
+      continue;
+    }
+    R ynew[D], err[D], F2[D];
+    if constexpr (METHOD == M_TSIT5) {
+      tsit5::trial<R, Sys>(sys, y, hs, k, ynew, err);
+    } else {
+      ros23::trial<R, Sys>(sys, y, hs, k[0], ynew, F2, err);
+    }
+    R sc[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      const R ay = absR(y[c]), an = absR(ynew[c]);
+      sc[c] = fmaR(a.rtol, (ay < an) ? an : ay, a.atol);
+    }
+    const R msq = mean_sq<R, D>(err, sc);
+    if (!finiteR(msq)) {
+      finish(TRAJ_NONFINITE);
+      continue;
+    }
+    if (msq <= R(1)) {
+      if (nacc >= a.s_cap) {
+        finish(TRAJ_CAPACITY);
+        continue;
+      }
+      const int64_t row = traj * a.s_cap + nacc;
+      if (a.t_rec) a.t_rec[row] = t;
+      if (a.h_rec) a.h_rec[row] = hs;
+      ++nacc;
+      t = last ? a.t1 : t + hs;
+#pragma unroll
+      for (int c = 0; c < D; ++c) y[c] = ynew[c];
+      if constexpr (METHOD == M_TSIT5) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) k[0][c] = k[6][c];
+      } else {
+#pragma unroll
+        for (int c = 0; c < D; ++c) k[0][c] = F2[c];
+      }
+      R fac = (msq == R(0)) ? R(10) : truncBits(R(0.9) * powR(msq, expo));
+      fac = (R(0.2) < fac) ? fac : R(0.2);
+      fac = (fac < R(10)) ? fac : R(10);
+      if (prev_rej) fac = (fac < R(1)) ? fac : R(1);
+      h = hs * fac;
+      prev_rej = false;
+      if (!(t < a.t1)) finish(TRAJ_OK);
+    } else {
+      ++nrej;
+      const R fq = truncBits(R(0.9) * powR(msq, expo));
+      h = hs * ((R(0.2) < fq) ? fq : R(0.2));
+      prev_rej = true;
+    }
+  }
+}
+
+template <class R, class Sys, int METHOD>
+__global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
+  constexpr int D = Sys::D, P = Sys::P;
+  const int lane = laneId();
+  const int64_t slot = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
+  R* scr = a.scratch + slot * (a.s_max * D * WAVE) + lane;
+  const unsigned long long ngroups = (unsigned long long)((a.n + WAVE - 1) / WAVE);
+
+  for (;;) {
+    unsigned long long g = 0;
+    if (lane == 0) g = atomicAdd(a.groups, 1ull);
+    g = __shfl(g, 0);
+    if (g >= ngroups) break;
+    const int64_t idx = (int64_t)g * WAVE + lane;
+    int64_t k = -1;
+    int cnt = 0;
+    bool ok = false;
+    if (idx < a.n) {
+      k = a.perm ? (int64_t)a.perm[idx] : idx;
+      cnt = a.count[k];
+      ok = cnt >= 0 && cnt <= a.s_max && (a.status == nullptr || a.status[k] == TRAJ_OK);
+      if (!ok) cnt = 0;
+    }
+    int mx = cnt;
+#pragma unroll
+    for (int off = WAVE / 2; off > 0; off >>= 1) {
+      const int o = __shfl_xor(mx, off);
+      mx = (o > mx) ? o : mx;
+    }
+
+    Sys sys;
+    R y[D], lam[D], pb[P];
+    const R* hrow = a.h_rec;
+    if (k >= 0) {
+      sys.load(a.theta, a.n, k);
+#pragma unroll
+      for (int c = 0; c < D; ++c) {
+        y[c] = a.y0[c * a.n + k];
+        lam[c] = a.dLdy1[c * a.n + k];
+      }
+      hrow = a.h_rec + k * a.s_cap;
+    }
+#pragma unroll
+    for (int j = 0; j < P; ++j) pb[j] = R(0);
+
+    // forward replay, storing y_j before step j
+    for (int i = 0; i < mx; ++i) {
+      if (i < cnt) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) scr[((int64_t)i * D + c) * WAVE] = y[c];
+        const R hj = hrow[i];
+        if constexpr (METHOD == M_TSIT5)
+          tsit5::replay<R, Sys>(sys, y, hj);
+        else
+          ros23::replay<R, Sys>(sys, y, hj);
+      }
+    }
+    // reverse sweep
+    for (int i = mx - 1; i >= 0; --i) {
+      if (i < cnt) {
+        R yj[D];
+#pragma unroll
+        for (int c = 0; c < D; ++c) yj[c] = scr[((int64_t)i * D + c) * WAVE];
+        const R hj = hrow[i];
+        if constexpr (METHOD == M_TSIT5)
+          tsit5::reverse<R, Sys>(sys, yj, hj, lam, pb);
+        else
+          ros23::reverse<R, Sys>(sys, yj, hj, lam, pb);
+      }
+    }
+    if (k >= 0) {
+      if (!ok) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) lam[c] = nanR(R(0));
+#pragma unroll
+        for (int j = 0; j < P; ++j) pb[j] = nanR(R(0));
+      }
+      if (a.dLdtheta) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) a.dLdtheta[j * a.n + k] = pb[j];
+      }
+      if (a.dLdy0) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) a.dLdy0[c * a.n + k] = lam[c];
+      }
+    }
+  }
+}
+
+// ---- trajectory ordering by step count (counting sort, decreasing count)
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v);
+__global__ void count_hist_kernel(const int32_t* count, int64_t n, int64_t s_max, uint32_t* hist);
+__global__ void scan_buckets_kernel(uint32_t* hist, int64_t nb);
+__global__ void scatter_perm_kernel(const int32_t* count, int64_t n, int64_t s_max, uint32_t* off,
+                                    int32_t* perm);
+
+}  // namespace dao

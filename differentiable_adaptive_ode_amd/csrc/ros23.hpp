@@ -1,0 +1,252 @@
+// Rosenbrock23: the second-order linearly implicit Rosenbrock-Wanner method
+// of Shampine & Reichelt (the ode23s triple), autonomous form.  arXiv
+// 2609.02876 Sec. 3.1 names it as the stiff default of the fused kernels and
+// Sec. 3.2 gives the structure: each stage solves with W = I - gamma h J,
+// and the backward sweep needs one more solve per stage, against W^T.
+//
+//   F0 = f(y), W = I - h d J(y), d = 1/(2 + sqrt 2)
+//   k1 = W^-1 F0
+//   F1 = f(y + h/2 k1)
+//   k2 = W^-1 (F1 - k1) + k1
+//   y_new = y + h k2
+//   F2 = f(y_new)                                   (reused as the next F0)
+//   k3 = W^-1 (F2 - e32 (k2 - F1) - 2 (k1 - F0)),   e32 = 6 + sqrt 2
+//   err = h/6 (k1 - 2 k2 + k3)
+//
+// W is factored per lane as P W = L U with partial pivoting (first row of
+// largest magnitude).  The pivot index is data dependent, so rows are
+// exchanged with selects on compile-time indices to keep every value in a
+// register.
+#pragma once
+
+#include "common.hpp"
+
+namespace dao {
+namespace ros23 {
+
+__device__ constexpr double GAMMA = 0.29289321881345248;  // 1 / (2 + sqrt 2)
+__device__ constexpr double E32 = 7.4142135623730951;     // 6 + sqrt 2
+
+template <class R, int D>
+struct LU {
+  R m[D][D];   // unit-lower L below the diagonal, U on and above
+  int piv[D];  // row exchanged with row k at elimination step k
+};
+
+template <class R, int D>
+__device__ __forceinline__ void factor(LU<R, D>& f) {
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    int p = k;
+    R best = absR(f.m[k][k]);
+#pragma unroll
+    for (int i = k + 1; i < D; ++i) {
+      R v = absR(f.m[i][k]);
+      if (v > best) { best = v; p = i; }
+    }
+    f.piv[k] = p;
+#pragma unroll
+    for (int i = k + 1; i < D; ++i) {
+      const bool sw = (p == i);
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        R rk = f.m[k][j], ri = f.m[i][j];
+        f.m[k][j] = sw ? ri : rk;
+        f.m[i][j] = sw ? rk : ri;
+      }
+    }
+#pragma unroll
+    for (int i = k + 1; i < D; ++i) {
+      R l = f.m[i][k] / f.m[k][k];
+      f.m[i][k] = l;
+#pragma unroll
+      for (int j = k + 1; j < D; ++j) f.m[i][j] = fmaR(-l, f.m[k][j], f.m[i][j]);
+    }
+  }
+}
+
+// x = W^-1 b
+template <class R, int D>
+__device__ __forceinline__ void solve(const LU<R, D>& f, const R (&b)[D], R (&x)[D]) {
+  R z[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) z[i] = b[i];
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+#pragma unroll
+    for (int i = k + 1; i < D; ++i) {
+      const bool sw = (f.piv[k] == i);
+      R zk = z[k], zi = z[i];
+      z[k] = sw ? zi : zk;
+      z[i] = sw ? zk : zi;
+    }
+  }
+#pragma unroll
+  for (int i = 1; i < D; ++i)
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j < i) z[i] = fmaR(-f.m[i][j], z[j], z[i]);
+#pragma unroll
+  for (int i = D - 1; i >= 0; --i) {
+    R acc = z[i];
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j > i) acc = fmaR(-f.m[i][j], x[j], acc);
+    x[i] = acc / f.m[i][i];
+  }
+}
+
+// x = W^-T b, with W = P^T L U:  U^T z = b,  L^T w = z,  x = P^T w.
+template <class R, int D>
+__device__ __forceinline__ void solve_t(const LU<R, D>& f, const R (&b)[D], R (&x)[D]) {
+  R z[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    R acc = b[i];
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j < i) acc = fmaR(-f.m[j][i], z[j], acc);
+    z[i] = acc / f.m[i][i];
+  }
+#pragma unroll
+  for (int i = D - 1; i >= 0; --i) {
+    R acc = z[i];
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j > i) acc = fmaR(-f.m[j][i], x[j], acc);
+    x[i] = acc;
+  }
+#pragma unroll
+  for (int k = D - 1; k >= 0; --k) {
+#pragma unroll
+    for (int i = k + 1; i < D; ++i) {
+      const bool sw = (f.piv[k] == i);
+      R xk = x[k], xi = x[i];
+      x[k] = sw ? xi : xk;
+      x[i] = sw ? xk : xi;
+    }
+  }
+}
+
+template <class R, class Sys>
+__device__ __forceinline__ void build_w(const Sys& sys, const R (&y)[Sys::D], R h,
+                                        LU<R, Sys::D>& w) {
+  constexpr int D = Sys::D;
+  R J[D][D];
+  sys.jac(y, J);
+  R hd = h * R(GAMMA);
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+#pragma unroll
+    for (int j = 0; j < D; ++j) w.m[i][j] = fmaR(-hd, J[i][j], R(i == j ? 1 : 0));
+  factor<R, D>(w);
+}
+
+// Trial step: F0 = f(y) on entry; returns ynew, F2 = f(ynew) and err.
+template <class R, class Sys>
+__device__ __forceinline__ void trial(const Sys& sys, const R (&y)[Sys::D], R h,
+                                      const R (&F0)[Sys::D], R (&ynew)[Sys::D], R (&F2)[Sys::D],
+                                      R (&err)[Sys::D]) {
+  constexpr int D = Sys::D;
+  LU<R, D> w;
+  build_w(sys, y, h, w);
+  R k1[D], k2[D], Y1[D], F1[D], r[D], u[D], k3[D];
+  solve<R, D>(w, F0, k1);
+  R hh = R(0.5) * h;
+#pragma unroll
+  for (int c = 0; c < D; ++c) Y1[c] = fmaR(hh, k1[c], y[c]);
+  sys.f(Y1, F1);
+#pragma unroll
+  for (int c = 0; c < D; ++c) r[c] = F1[c] - k1[c];
+  solve<R, D>(w, r, u);
+#pragma unroll
+  for (int c = 0; c < D; ++c) k2[c] = u[c] + k1[c];
+#pragma unroll
+  for (int c = 0; c < D; ++c) ynew[c] = fmaR(h, k2[c], y[c]);
+  sys.f(ynew, F2);
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    R t2 = fmaR(R(-E32), k2[c] - F1[c], F2[c]);
+    r[c] = fmaR(R(-2), k1[c] - F0[c], t2);
+  }
+  solve<R, D>(w, r, k3);
+  R h6 = h / R(6);
+#pragma unroll
+  for (int c = 0; c < D; ++c) err[c] = h6 * (fmaR(R(-2), k2[c], k1[c]) + k3[c]);
+}
+
+// Replay step y <- Phi(y; h) (no k3, no error estimate).
+template <class R, class Sys>
+__device__ __forceinline__ void replay(const Sys& sys, R (&y)[Sys::D], R h) {
+  constexpr int D = Sys::D;
+  LU<R, D> w;
+  build_w(sys, y, h, w);
+  R F0[D], k1[D], Y1[D], F1[D], r[D], u[D];
+  sys.f(y, F0);
+  solve<R, D>(w, F0, k1);
+  R hh = R(0.5) * h;
+#pragma unroll
+  for (int c = 0; c < D; ++c) Y1[c] = fmaR(hh, k1[c], y[c]);
+  sys.f(Y1, F1);
+#pragma unroll
+  for (int c = 0; c < D; ++c) r[c] = F1[c] - k1[c];
+  solve<R, D>(w, r, u);
+#pragma unroll
+  for (int c = 0; c < D; ++c) y[c] = fmaR(h, u[c] + k1[c], y[c]);
+}
+
+// Reverse of one replay step: lam = dL/dy_{j+1} in, dL/dy_j out; pb += dL/dtheta.
+template <class R, class Sys>
+__device__ __forceinline__ void reverse(const Sys& sys, const R (&y)[Sys::D], R h,
+                                        R (&lam)[Sys::D], R (&pb)[Sys::P]) {
+  constexpr int D = Sys::D;
+  LU<R, D> w;
+  build_w(sys, y, h, w);
+  R F0[D], k1[D], Y1[D], F1[D], r[D], u[D];
+  sys.f(y, F0);
+  solve<R, D>(w, F0, k1);
+  R hh = R(0.5) * h;
+#pragma unroll
+  for (int c = 0; c < D; ++c) Y1[c] = fmaR(hh, k1[c], y[c]);
+  sys.f(Y1, F1);
+#pragma unroll
+  for (int c = 0; c < D; ++c) r[c] = F1[c] - k1[c];
+  solve<R, D>(w, r, u);
+
+  // y_new = y + h (u + k1)
+  R ub[D], k1b[D], rb[D], tmp[D], F0b[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    ub[c] = h * lam[c];
+    k1b[c] = ub[c];
+  }
+  // u = W^-1 r:  rb = W^-T ub,  Wb = -rb u^T
+  solve_t<R, D>(w, ub, rb);
+  // r = F1 - k1
+#pragma unroll
+  for (int c = 0; c < D; ++c) k1b[c] -= rb[c];
+  // F1 = f(Y1), Y1 = y + h/2 k1
+  sys.vjp(Y1, rb, tmp, pb);
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    lam[c] += tmp[c];
+    k1b[c] = fmaR(hh, tmp[c], k1b[c]);
+  }
+  // k1 = W^-1 F0:  F0b = W^-T k1b,  Wb -= F0b k1^T
+  solve_t<R, D>(w, k1b, F0b);
+  // F0 = f(y)
+  sys.vjp(y, F0b, tmp, pb);
+#pragma unroll
+  for (int c = 0; c < D; ++c) lam[c] += tmp[c];
+  // W = I - h d J(y, theta):  Jb = -h d Wb = h d (rb u^T + F0b k1^T)
+  R hd = h * R(GAMMA);
+  R Jb[D][D];
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+#pragma unroll
+    for (int j = 0; j < D; ++j) Jb[i][j] = hd * fmaR(rb[i], u[j], F0b[i] * k1[j]);
+  sys.jac_vjp(y, Jb, lam, pb);
+}
+
+}  // namespace ros23
+}  // namespace dao

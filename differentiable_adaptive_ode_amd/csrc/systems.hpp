@@ -1,0 +1,236 @@
+// Built-in right-hand sides for the per-lane kernels.
+//
+// Every system exposes, for one trajectory held in one lane's registers:
+//   load(theta, n, k)      gather the trajectory's parameters from SoA theta[p][n]
+//                          and precompute per-trajectory constants
+//   f(y, dy)               the field, with the rounding contract of the solve
+//   vjp(y, v, yb, pb)      yb = (df/dy)^T v ;  pb += (df/dtheta)^T v
+//   jac(y, J)              J = df/dy (Rosenbrock stages)
+//   jac_vjp(y, Jb, yb, pb) yb += d/dy <Jb, J(y,theta)> ; pb += d/dtheta <Jb, J>
+//                          (the Jacobian's own dependence, needed by the
+//                          Rosenbrock adjoint; arXiv 2609.02876 Sec. 3.2 notes
+//                          the backward sweep differentiates through J)
+// The vector-Jacobian products are derived by hand from the formulas below.
+#pragma once
+
+#include "common.hpp"
+
+namespace dao {
+
+// y' = -theta y.
+template <class R>
+struct Decay {
+  static constexpr int D = 1, P = 1;
+  R th;
+  __device__ void load(const R* theta, int64_t n, int64_t k) { (void)n; th = theta[k]; }
+  __device__ void f(const R (&y)[D], R (&dy)[D]) const { dy[0] = -(th * y[0]); }
+  __device__ void vjp(const R (&y)[D], const R (&v)[D], R (&yb)[D], R (&pb)[P]) const {
+    yb[0] = -th * v[0];
+    pb[0] = fmaR(-y[0], v[0], pb[0]);
+  }
+  __device__ void jac(const R (&y)[D], R (&J)[D][D]) const { (void)y; J[0][0] = -th; }
+  __device__ void jac_vjp(const R (&y)[D], const R (&Jb)[D][D], R (&yb)[D], R (&pb)[P]) const {
+    (void)y; (void)yb;
+    pb[0] -= Jb[0][0];
+  }
+};
+
+// Lotka-Volterra, theta = (a, b, g, d): y1' = y1 (a - b y2), y2' = y2 (d y1 - g).
+template <class R>
+struct LotkaVolterra {
+  static constexpr int D = 2, P = 4;
+  R a, b, g, d;
+  __device__ void load(const R* theta, int64_t n, int64_t k) {
+    a = theta[k]; b = theta[n + k]; g = theta[2 * n + k]; d = theta[3 * n + k];
+  }
+  __device__ void f(const R (&y)[D], R (&dy)[D]) const {
+    dy[0] = y[0] * fmaR(-b, y[1], a);
+    dy[1] = y[1] * fmaR(d, y[0], -g);
+  }
+  __device__ void vjp(const R (&y)[D], const R (&v)[D], R (&yb)[D], R (&pb)[P]) const {
+    R j11 = fmaR(-b, y[1], a), j22 = fmaR(d, y[0], -g);
+    yb[0] = fmaR(j11, v[0], (d * y[1]) * v[1]);
+    yb[1] = fmaR(j22, v[1], -(b * y[0]) * v[0]);
+    R y12 = y[0] * y[1];
+    pb[0] = fmaR(y[0], v[0], pb[0]);
+    pb[1] = fmaR(-y12, v[0], pb[1]);
+    pb[2] = fmaR(-y[1], v[1], pb[2]);
+    pb[3] = fmaR(y12, v[1], pb[3]);
+  }
+  __device__ void jac(const R (&y)[D], R (&J)[D][D]) const {
+    J[0][0] = fmaR(-b, y[1], a);
+    J[0][1] = -(b * y[0]);
+    J[1][0] = d * y[1];
+    J[1][1] = fmaR(d, y[0], -g);
+  }
+  __device__ void jac_vjp(const R (&y)[D], const R (&Jb)[D][D], R (&yb)[D], R (&pb)[P]) const {
+    yb[0] += fmaR(d, Jb[1][1], -b * Jb[0][1]);
+    yb[1] += fmaR(d, Jb[1][0], -b * Jb[0][0]);
+    pb[0] += Jb[0][0];
+    pb[1] -= fmaR(y[1], Jb[0][0], y[0] * Jb[0][1]);
+    pb[2] -= Jb[1][1];
+    pb[3] += fmaR(y[1], Jb[1][0], y[0] * Jb[1][1]);
+  }
+};
+
+// Lorenz-63, theta = (sigma, rho, beta).
+template <class R>
+struct Lorenz63 {
+  static constexpr int D = 3, P = 3;
+  R s, r, b;
+  __device__ void load(const R* theta, int64_t n, int64_t k) {
+    s = theta[k]; r = theta[n + k]; b = theta[2 * n + k];
+  }
+  __device__ void f(const R (&y)[D], R (&dy)[D]) const {
+    dy[0] = s * (y[1] - y[0]);
+    dy[1] = fmaR(y[0], r - y[2], -y[1]);
+    dy[2] = fmaR(y[0], y[1], -(b * y[2]));
+  }
+  __device__ void vjp(const R (&y)[D], const R (&v)[D], R (&yb)[D], R (&pb)[P]) const {
+    R sv = s * v[0];
+    yb[0] = fmaR(r - y[2], v[1], fmaR(y[1], v[2], -sv));
+    yb[1] = fmaR(y[0], v[2], sv - v[1]);
+    yb[2] = -fmaR(y[0], v[1], b * v[2]);
+    pb[0] = fmaR(y[1] - y[0], v[0], pb[0]);
+    pb[1] = fmaR(y[0], v[1], pb[1]);
+    pb[2] = fmaR(-y[2], v[2], pb[2]);
+  }
+  __device__ void jac(const R (&y)[D], R (&J)[D][D]) const {
+    J[0][0] = -s; J[0][1] = s; J[0][2] = R(0);
+    J[1][0] = r - y[2]; J[1][1] = R(-1); J[1][2] = -y[0];
+    J[2][0] = y[1]; J[2][1] = y[0]; J[2][2] = -b;
+  }
+  __device__ void jac_vjp(const R (&y)[D], const R (&Jb)[D][D], R (&yb)[D], R (&pb)[P]) const {
+    (void)y;
+    yb[0] += Jb[2][1] - Jb[1][2];
+    yb[1] += Jb[2][0];
+    yb[2] -= Jb[1][0];
+    pb[0] += Jb[0][1] - Jb[0][0];
+    pb[1] += Jb[1][0];
+    pb[2] -= Jb[2][2];
+  }
+};
+
+// Robertson kinetics, theta = (k1, k2, k3):
+//   y1' = -k1 y1 + k3 y2 y3,  y2' = k1 y1 - k2 y2^2 - k3 y2 y3,  y3' = k2 y2^2.
+template <class R>
+struct Robertson {
+  static constexpr int D = 3, P = 3;
+  R k1, k2, k3;
+  __device__ void load(const R* theta, int64_t n, int64_t k) {
+    k1 = theta[k]; k2 = theta[n + k]; k3 = theta[2 * n + k];
+  }
+  __device__ void f(const R (&y)[D], R (&dy)[D]) const {
+    R a = k1 * y[0];
+    R b = k2 * (y[1] * y[1]);
+    R c = k3 * (y[1] * y[2]);
+    dy[0] = c - a;
+    dy[1] = (a - b) - c;
+    dy[2] = b;
+  }
+  __device__ void vjp(const R (&y)[D], const R (&v)[D], R (&yb)[D], R (&pb)[P]) const {
+    R v21 = v[1] - v[0], v12 = v[0] - v[1], v32 = v[2] - v[1];
+    R t2 = (R(2) * k2) * y[1];
+    yb[0] = k1 * v21;
+    yb[1] = fmaR(k3 * y[2], v12, t2 * v32);
+    yb[2] = (k3 * y[1]) * v12;
+    pb[0] = fmaR(y[0], v21, pb[0]);
+    pb[1] = fmaR(y[1] * y[1], v32, pb[1]);
+    pb[2] = fmaR(y[1] * y[2], v12, pb[2]);
+  }
+  __device__ void jac(const R (&y)[D], R (&J)[D][D]) const {
+    R j12 = k3 * y[2];
+    R j13 = k3 * y[1];
+    R t = (R(2) * k2) * y[1];
+    J[0][0] = -k1; J[0][1] = j12;        J[0][2] = j13;
+    J[1][0] = k1;  J[1][1] = -(t + j12); J[1][2] = -j13;
+    J[2][0] = R(0); J[2][1] = t;         J[2][2] = R(0);
+  }
+  __device__ void jac_vjp(const R (&y)[D], const R (&Jb)[D][D], R (&yb)[D], R (&pb)[P]) const {
+    // <Jb, J> = -k1 Jb00 + k3 y3 Jb01 + k3 y2 Jb02 + k1 Jb10 - (2 k2 y2 + k3 y3) Jb11
+    //           - k3 y2 Jb12 + 2 k2 y2 Jb21
+    R w21 = Jb[2][1] - Jb[1][1];
+    R w02 = Jb[0][2] - Jb[1][2];
+    R w01 = Jb[0][1] - Jb[1][1];
+    yb[1] += fmaR(k3, w02, (R(2) * k2) * w21);
+    yb[2] += k3 * w01;
+    pb[0] += Jb[1][0] - Jb[0][0];
+    pb[1] += (R(2) * y[1]) * w21;
+    pb[2] += fmaR(y[2], w01, y[1] * w02);
+  }
+};
+
+// Star in a flattened logarithmic halo, Phi = 1/2 v0^2 ln(Rc^2 + x^2 + y^2 + z^2/q^2).
+// State (x, y, z, vx, vy, vz), theta = (v0, Rc, q).
+template <class R>
+struct LogHalo {
+  static constexpr int D = 6, P = 3;
+  R v0, rc, q, v2, r2, iq2;
+  __device__ void load(const R* theta, int64_t n, int64_t k) {
+    v0 = theta[k]; rc = theta[n + k]; q = theta[2 * n + k];
+    v2 = v0 * v0;
+    r2 = rc * rc;
+    iq2 = R(1) / (q * q);
+  }
+  __device__ void f(const R (&y)[D], R (&dy)[D]) const {
+    R zq = y[2] * iq2;
+    R Dn = fmaR(y[0], y[0], fmaR(y[1], y[1], fmaR(y[2], zq, r2)));
+    R A = v2 / Dn;
+    dy[0] = y[3];
+    dy[1] = y[4];
+    dy[2] = y[5];
+    dy[3] = -(A * y[0]);
+    dy[4] = -(A * y[1]);
+    dy[5] = -(A * zq);
+  }
+  // a = -A g with g = (x, y, z/q^2), A = v0^2 / Dn.  With s = <w, g> for the
+  // acceleration cotangent w and u = s A / Dn:
+  //   d/dx = -A w_x + 2 x u, d/dy = -A w_y + 2 y u, d/dz = -A w_z / q^2 + 2 (z/q^2) u,
+  //   d/dv0 = -2 s v0 / Dn, d/dRc = 2 Rc u, d/dq = (u z^2 - A w_z z) (-2 / (q^3)).
+  __device__ void vjp(const R (&y)[D], const R (&v)[D], R (&yb)[D], R (&pb)[P]) const {
+    R zq = y[2] * iq2;
+    R Dn = fmaR(y[0], y[0], fmaR(y[1], y[1], fmaR(y[2], zq, r2)));
+    R iD = R(1) / Dn;
+    R A = v2 * iD;
+    R s = fmaR(v[3], y[0], fmaR(v[4], y[1], v[5] * zq));
+    R u = (s * A) * iD;
+    R u2 = u + u;
+    yb[0] = fmaR(u2, y[0], -A * v[3]);
+    yb[1] = fmaR(u2, y[1], -A * v[4]);
+    yb[2] = fmaR(u2, zq, -(A * iq2) * v[5]);
+    yb[3] = v[0];
+    yb[4] = v[1];
+    yb[5] = v[2];
+    pb[0] = fmaR(-(s + s) * v0, iD, pb[0]);
+    pb[1] = fmaR(u2, rc, pb[1]);
+    R dq = (R(-2) * iq2) / q;
+    pb[2] = fmaR(fmaR(u, y[2], -A * v[5]) * y[2], dq, pb[2]);
+  }
+  __device__ void jac(const R (&y)[D], R (&J)[D][D]) const {
+    R zq = y[2] * iq2;
+    R Dn = fmaR(y[0], y[0], fmaR(y[1], y[1], fmaR(y[2], zq, r2)));
+    R iD = R(1) / Dn;
+    R A = v2 * iD;
+    R g[3] = {y[0], y[1], zq};
+    R dD[3] = {R(2) * y[0], R(2) * y[1], R(2) * zq};
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+#pragma unroll
+      for (int j = 0; j < 6; ++j) J[i][j] = R(0);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) J[i][3 + i] = R(1);
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        R dg = (i == j) ? ((i == 2) ? iq2 : R(1)) : R(0);
+        J[3 + i][j] = (A * g[i]) * dD[j] * iD - A * dg;
+      }
+  }
+  __device__ void jac_vjp(const R (&y)[D], const R (&Jb)[D][D], R (&yb)[D], R (&pb)[P]) const {
+    // Not used: the halo has no Rosenbrock path (dao_solve/dao_grad refuse it).
+    (void)y; (void)Jb; (void)yb; (void)pb;
+  }
+};
+
+}  // namespace dao

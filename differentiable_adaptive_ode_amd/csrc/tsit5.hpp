@@ -1,0 +1,147 @@
+// Tsit5: the Tsitouras 5(4) explicit pair with 7 stages and FSAL
+// (arXiv 2609.02876 Sec. 2.1 names it as the default non-stiff method; the
+// coefficients are the published ones, Tsitouras 2011, Table 1).
+//
+// Per lane, all stage values live in registers.  Stage i (0-based) is
+//   Y_i = y + h * (a_i0 k_0 + sum_{j=1}^{i-1} a_ij k_j)        (fma chain, j ascending)
+//   k_i = f(Y_i)
+// and y_new = Y_6 (the weights b equal the last row of A).  The error estimate
+// is e = h * (bt_0 k_0 + sum_{j=1}^{6} bt_j k_j) with bt = b - bhat.
+#pragma once
+
+#include "common.hpp"
+
+namespace dao {
+namespace tsit5 {
+
+__device__ constexpr double A10 = 0.161;
+__device__ constexpr double A20 = -0.008480655492356989, A21 = 0.335480655492357;
+__device__ constexpr double A30 = 2.897153057105493, A31 = -6.359448489975075,
+                            A32 = 4.3622954328695815;
+__device__ constexpr double A40 = 5.325864828439257, A41 = -11.748883564062828,
+                            A42 = 7.4955393428898365, A43 = -0.09249506636175525;
+__device__ constexpr double A50 = 5.86145544294642, A51 = -12.92096931784711,
+                            A52 = 8.159367898576159, A53 = -0.071584973281401,
+                            A54 = -0.028269050394068383;
+__device__ constexpr double A60 = 0.09646076681806523, A61 = 0.01, A62 = 0.4798896504144996,
+                            A63 = 1.379008574103742, A64 = -3.290069515436081,
+                            A65 = 2.324710524099774;
+__device__ constexpr double E0 = -0.00178001105222577714, E1 = -0.0008164344596567469,
+                            E2 = 0.007880878010261995, E3 = -0.1447110071732629,
+                            E4 = 0.5823571654525552, E5 = -0.45808210592918697,
+                            E6 = 0.015151515151515152;
+
+// Coefficient lookup with compile-time indices (the stage loops below are
+// fully unrolled, so every access resolves to a literal).
+template <class R>
+__device__ __forceinline__ constexpr R a(int i, int j) {
+  return R(i == 1 ? A10
+         : i == 2 ? (j == 0 ? A20 : A21)
+         : i == 3 ? (j == 0 ? A30 : j == 1 ? A31 : A32)
+         : i == 4 ? (j == 0 ? A40 : j == 1 ? A41 : j == 2 ? A42 : A43)
+         : i == 5 ? (j == 0 ? A50 : j == 1 ? A51 : j == 2 ? A52 : j == 3 ? A53 : A54)
+                  : (j == 0 ? A60 : j == 1 ? A61 : j == 2 ? A62 : j == 3 ? A63 : j == 4 ? A64 : A65));
+}
+template <class R>
+__device__ __forceinline__ constexpr R e(int j) {
+  return R(j == 0 ? E0 : j == 1 ? E1 : j == 2 ? E2 : j == 3 ? E3 : j == 4 ? E4 : j == 5 ? E5 : E6);
+}
+
+// Stage state Y_i from y and k_0..k_{i-1}.
+template <class R, int D>
+__device__ __forceinline__ void stage_state(int i, const R (&y)[D], R h, const R (&k)[7][D],
+                                            R (&Y)[D]) {
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    R acc = a<R>(i, 0) * k[0][c];
+#pragma unroll
+    for (int j = 1; j < 6; ++j)
+      if (j < i) acc = fmaR(a<R>(i, j), k[j][c], acc);
+    Y[c] = fmaR(h, acc, y[c]);
+  }
+}
+
+// One trial step: k[0] = f(y) on entry; fills k[1..6], ynew and err.
+template <class R, class Sys>
+__device__ __forceinline__ void trial(const Sys& sys, const R (&y)[Sys::D], R h,
+                                      R (&k)[7][Sys::D], R (&ynew)[Sys::D], R (&err)[Sys::D]) {
+  constexpr int D = Sys::D;
+  R Y[D];
+#pragma unroll
+  for (int i = 1; i < 7; ++i) {
+    stage_state<R, D>(i, y, h, k, Y);
+    sys.f(Y, k[i]);
+  }
+#pragma unroll
+  for (int c = 0; c < D; ++c) ynew[c] = Y[c];
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    R acc = e<R>(0) * k[0][c];
+#pragma unroll
+    for (int j = 1; j < 7; ++j) acc = fmaR(e<R>(j), k[j][c], acc);
+    err[c] = h * acc;
+  }
+}
+
+// One replay step y <- Phi(y; h): six evaluations, no error estimate.
+template <class R, class Sys>
+__device__ __forceinline__ void replay(const Sys& sys, R (&y)[Sys::D], R h) {
+  constexpr int D = Sys::D;
+  R k[7][D];
+  R Y[D];
+  sys.f(y, k[0]);
+#pragma unroll
+  for (int i = 1; i < 6; ++i) {
+    stage_state<R, D>(i, y, h, k, Y);
+    sys.f(Y, k[i]);
+  }
+  stage_state<R, D>(6, y, h, k, Y);
+#pragma unroll
+  for (int c = 0; c < D; ++c) y[c] = Y[c];
+}
+
+// Reverse of one replay step.  On entry lam = dL/dy_{j+1}; on exit
+// lam = dL/dy_j and pb has accumulated dL/dtheta from this step.
+// The stage states are recomputed from y_j (store-the-state, recompute-the-
+// stages, as the in-kernel adjoint of Sec. 3.3 does).
+template <class R, class Sys>
+__device__ __forceinline__ void reverse(const Sys& sys, const R (&y)[Sys::D], R h,
+                                        R (&lam)[Sys::D], R (&pb)[Sys::P]) {
+  constexpr int D = Sys::D;
+  R k[7][D];
+  R Y[6][D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) Y[0][c] = y[c];
+  sys.f(Y[0], k[0]);
+#pragma unroll
+  for (int i = 1; i < 6; ++i) {
+    stage_state<R, D>(i, y, h, k, Y[i]);
+    sys.f(Y[i], k[i]);
+  }
+  // y_new = y + h * sum_j b_j k_j with b_j = a(6, j):  kb_j = h b_j lam.
+  R kb[6][D];
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    R hb = h * a<R>(6, j);
+#pragma unroll
+    for (int c = 0; c < D; ++c) kb[j][c] = hb * lam[c];
+  }
+  R yb[D];
+#pragma unroll
+  for (int i = 5; i >= 0; --i) {
+    sys.vjp(Y[i], kb[i], yb, pb);
+#pragma unroll
+    for (int c = 0; c < D; ++c) lam[c] += yb[c];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      if (j < i) {
+        R ha = h * a<R>(i, j);
+#pragma unroll
+        for (int c = 0; c < D; ++c) kb[j][c] = fmaR(ha, yb[c], kb[j][c]);
+      }
+    }
+  }
+}
+
+}  // namespace tsit5
+}  // namespace dao

@@ -1,0 +1,175 @@
+/*
+ * dao.h -- C ABI of the MI355X ensemble ODE library: adaptive solve with a
+ * step record, and the discrete-adjoint gradient on the recorded mesh.
+ *
+ * Method (arXiv 2609.02876, "gradsolve: fast exact gradients for ODE
+ * ensembles on GPUs"):
+ *   - Section 2.1: each trajectory is integrated by an embedded explicit
+ *     Runge-Kutta pair (Tsit5) or a linearly implicit Rosenbrock-Wanner step
+ *     (Rosenbrock23), accepting a trial step when the RMS of
+ *     e / (atol + rtol * max(|y|, |y_new|)) is at most one.
+ *   - Section 3.1 (Fig. 2, Eq. 4): the record keeps the accepted step sizes;
+ *     the gradient is the exact reverse-mode derivative of the fixed-step
+ *     replay of that mesh, with the step sizes held constant.
+ *   - Section 3.2: the Rosenbrock stage solves with I - gamma h J, and its
+ *     adjoint solves with the transpose.
+ *
+ * Conventions shared by every entry point:
+ *   - "real" is double for DAO_F64 and float for DAO_F32.
+ *   - All array pointers are DEVICE pointers unless stated otherwise; the
+ *     caller allocates and owns them, the library never frees them and never
+ *     allocates device memory itself.
+ *   - Layouts are structure-of-arrays: parameters theta[p][n] (index
+ *     i*n + k), states y[d][n]; the shared MLP weights are one vector
+ *     theta[4740].  Record rows are trajectory-major: h[k*s_cap + j] is the
+ *     j-th accepted step of trajectory k.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns; results are ready when the stream
+ *     is.  Argument checks happen before anything is enqueued; a call that
+ *     fails them returns DAO_EINVAL (or DAO_EUNSUPPORTED / DAO_EWORKSPACE)
+ *     and enqueues nothing.  dao_last_error() then names the argument.
+ *   - Per-trajectory failures are not call failures: they are written to
+ *     record.status, and that trajectory's outputs are NaN.
+ *   - Calls on one stream are ordered; calls that share a workspace must
+ *     not overlap in time.
+ */
+#ifndef DAO_H
+#define DAO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DAO_OK = 0,
+  DAO_EINVAL = 1,       /* an argument is invalid; dao_last_error() names it       */
+  DAO_EDEVICE = 2,      /* a HIP runtime call or kernel launch failed              */
+  DAO_EWORKSPACE = 3,   /* the workspace is smaller than the call needs            */
+  DAO_EUNSUPPORTED = 4  /* system / method / dtype combination is not provided     */
+} dao_status;
+
+/* Built-in right-hand sides (d = state size, p = parameters per trajectory). */
+typedef enum {
+  DAO_SYS_DECAY = 0,          /* y' = -theta y; d=1, p=1                                     */
+  DAO_SYS_LOTKA_VOLTERRA = 1, /* theta=(a,b,g,d): y1'=y1(a-b y2), y2'=y2(d y1-g); d=2, p=4    */
+  DAO_SYS_LORENZ63 = 2,       /* theta=(sigma,rho,beta); d=3, p=3                            */
+  DAO_SYS_MLP = 3,            /* y'=W3 tanh(W2 tanh(W1 y+b1)+b2)+b3, 4-64-64-4, shared
+                                 theta[4740] = [W1(64x4) b1 W2(64x64) b2 W3(4x64) b3]; d=4   */
+  DAO_SYS_ROBERTSON = 4,      /* theta=(k1,k2,k3): Robertson kinetics; d=3, p=3              */
+  DAO_SYS_LOGHALO = 5         /* theta=(v0,Rc,q), y=(x,y,z,vx,vy,vz), potential
+                                 1/2 v0^2 ln(Rc^2+x^2+y^2+z^2/q^2); d=6, p=3                 */
+} dao_system;
+
+typedef enum {
+  DAO_TSIT5 = 0,        /* Tsitouras 5(4) pair, 7 stages, FSAL (Sec. 2.1)                  */
+  DAO_ROSENBROCK23 = 1  /* Shampine-Reichelt second-order Rosenbrock, autonomous (Sec. 3.2) */
+} dao_method;
+
+typedef enum { DAO_F64 = 0, DAO_F32 = 1 } dao_dtype;
+
+/* Per-trajectory status codes (record.status). */
+enum {
+  DAO_TRAJ_OK = 0,
+  DAO_TRAJ_MAX_STEPS = 1,    /* more than tol.max_steps attempts                          */
+  DAO_TRAJ_NONFINITE = 2,    /* error estimate or step size not finite                    */
+  DAO_TRAJ_DT_UNDERFLOW = 3, /* t + h == t                                                */
+  DAO_TRAJ_CAPACITY = 4      /* more accepted steps than record.s_cap (or the grad's s_max) */
+};
+
+/* Tolerances and step controls (host struct, read during the call). */
+typedef struct {
+  double rtol;       /* relative tolerance, > 0                                         */
+  double atol;       /* absolute tolerance, > 0                                         */
+  double dt0;        /* > 0: first trial step; <= 0: automatic starting step           */
+  int64_t max_steps; /* cap on attempted steps per trajectory, >= 1                     */
+} dao_tol;
+
+/* Step record (Sec. 3.1, Fig. 2): host struct of caller-owned device arrays.
+ * Rows past count[k] are never read.                                       */
+typedef struct {
+  int64_t s_cap;   /* rows per trajectory (capacity), >= 0                       */
+  void* t;         /* real[n][s_cap]: start time of each accepted step; may be NULL */
+  void* h;         /* real[n][s_cap]: accepted step sizes                          */
+  int32_t* count;  /* int32[n]: accepted steps                                     */
+  int32_t* nrej;   /* int32[n]: rejected attempts; may be NULL                     */
+  int32_t* status; /* int32[n]: DAO_TRAJ_* code                                    */
+} dao_record;
+
+/* State size d, parameter count p, and whether theta is shared (MLP).
+ * Returns DAO_EINVAL for an unknown system.                                 */
+dao_status dao_system_dims(dao_system sys, int* d, int* p, int* shared);
+
+/* Workspace (device bytes) dao_solve needs for n trajectories. */
+size_t dao_solve_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n);
+
+/*
+ * dao_solve -- adaptive solve of n independent trajectories on [t0, t1]
+ * (Sec. 2.1): per trajectory, FSAL Tsit5 or Rosenbrock23 trial steps, RMS
+ * acceptance test, integral step-size controller, last step clipped to t1.
+ * Writes y1[d][n] (NaN where status != DAO_TRAJ_OK) and, when rec != NULL,
+ * the record of accepted steps (Sec. 3.1).  rec == NULL runs the same solve
+ * without writing a record.
+ *   theta    real[p][n] (or real[4740] for DAO_SYS_MLP), y0 real[d][n]
+ *   t0 <= t1, both finite; tol as above
+ *   workspace >= dao_solve_workspace_size() device bytes (work-queue counter)
+ * Errors: DAO_EINVAL (NULL array with n > 0, t1 < t0, bad tolerances,
+ * rec->s_cap < 0), DAO_EUNSUPPORTED, DAO_EWORKSPACE, DAO_EDEVICE.
+ */
+dao_status dao_solve(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                     const void* theta, const void* y0, double t0, double t1,
+                     const dao_tol* tol, void* y1, const dao_record* rec,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace (device bytes) dao_grad needs for n trajectories whose records
+ * hold at most s_max accepted steps.  Less is accepted (down to
+ * dao_grad_workspace_min) and runs fewer trajectories at once.               */
+size_t dao_grad_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                               int64_t s_max);
+size_t dao_grad_workspace_min(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                              int64_t s_max);
+
+/*
+ * dao_grad -- discrete-adjoint gradient on the recorded mesh (Sec. 3.1):
+ * replays y_{j+1} = Phi(y_j; h_j, theta) for j < count[k] from y0 with the
+ * recorded h_j as constants, then sweeps backward from dL/dy1 through every
+ * stage (Tsit5), or through both stage solves with the transposed LU factors
+ * and the Jacobian's own dependence on y and theta (Rosenbrock23, Sec. 3.2).
+ * theta may differ from the theta of the solve that wrote the record: the
+ * derivative is then taken at theta on the old mesh (Sec. 3.1, 4.8).
+ *   theta, y0 as in dao_solve; rec->h and rec->count are read
+ *   s_max    >= max_k count[k] and <= rec->s_cap (trajectories with more
+ *            steps get NaN outputs)
+ *   dLdy1    real[d][n], the cotangent of the final state
+ *   dLdtheta real[p][n], or real[4740] summed over the ensemble (MLP);
+ *            may be NULL
+ *   dLdy0    real[d][n]; may be NULL
+ * Errors: DAO_EINVAL, DAO_EUNSUPPORTED, DAO_EWORKSPACE, DAO_EDEVICE.
+ */
+dao_status dao_grad(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                    const void* theta, const void* y0, const dao_record* rec, int64_t s_max,
+                    const void* dLdy1, void* dLdtheta, void* dLdy0,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dao_sqerr_cotangent -- cotangent of a squared-error loss (the misfit
+ * l(y(t1)) of Sec. 2.2's calibration loss), out[c][k] = scale *
+ * (y1[c][k] - target[c][k]) for components c < d_used, 0 for the rest.
+ *   y1, target, out real[d][n]; 0 <= d_used <= d
+ */
+dao_status dao_sqerr_cotangent(dao_dtype dtype, int64_t n, int d, int d_used, const void* y1,
+                               const void* target, double scale, void* out, void* stream);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* dao_last_error(void);
+
+/* Library version string, e.g. "0.1.0 gfx950". */
+const char* dao_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DAO_H */

@@ -1,0 +1,109 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/dao.h declares, and rejects invalid arguments before
+enqueuing any work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.abspath(os.path.join(os.path.dirname(__file__), ".."))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "dao.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(dao_[a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from differentiable_adaptive_ode_amd import _lib
+
+    return _lib
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("dao_solve", "dao_grad", "dao_solve_workspace_size", "dao_grad_workspace_size",
+              "dao_grad_workspace_min", "dao_system_dims", "dao_sqerr_cotangent",
+              "dao_last_error", "dao_version"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = ctypes.CDLL(L.SO_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_system_dims(L):
+    assert L.dao_system_dims(L.SYSTEMS["lorenz63"]) == (3, 3, False)
+    assert L.dao_system_dims(L.SYSTEMS["mlp"]) == (4, 4740, True)
+    assert L.dao_system_dims(L.SYSTEMS["loghalo"]) == (6, 3, False)
+    with pytest.raises(L.DaoError):
+        L.dao_system_dims(17)
+
+
+def _solve(L, **over):
+    args = dict(system=2, method=0, dtype=0, n=10, theta=1, y0=1, t0=0.0, t1=1.0,
+                tol=L.dao_tol(1e-6, 1e-8, 0.0, 1000), y1=1,
+                rec=L.dao_record(16, 1, 1, 1, 1, 1), ws=1, wsb=256, stream=None)
+    args.update(over)
+    return L.dao_solve(args["system"], args["method"], args["dtype"], args["n"], args["theta"],
+                       args["y0"], args["t0"], args["t1"], args["tol"], args["y1"], args["rec"],
+                       args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(t1=-1.0), 1), (dict(t0=float("nan")), 1), (dict(n=-3), 1),
+    (dict(system=9), 1), (dict(method=5), 1), (dict(dtype=7), 1),
+    (dict(theta=None), 1), (dict(y0=None), 1), (dict(y1=None), 1), (dict(rec=None), 1),
+    (dict(ws=None), 3), (dict(wsb=8), 3), (dict(system=5, method=1), 4), (dict(system=3), 4),
+])
+def test_solve_argument_errors(L, over, code):
+    if "tol" not in over:
+        pass
+    assert _solve(L, **over) == code
+    assert L.dao_last_error() != ""
+
+
+@pytest.mark.parametrize("field,val", [("rtol", 0.0), ("atol", -1.0), ("max_steps", 0),
+                                       ("dt0", float("inf"))])
+def test_solve_tolerance_errors(L, field, val):
+    tol = L.dao_tol(1e-6, 1e-8, 0.0, 1000)
+    setattr(tol, field, val)
+    assert _solve(L, tol=tol) == 1
+
+
+def test_empty_ensemble_is_a_no_op(L):
+    assert _solve(L, n=0, theta=None, y0=None, y1=None) == 0
+
+
+def test_grad_argument_errors(L):
+    rec = L.dao_record(16, None, 1, 1, None, 1)
+    ok = dict(system=2, method=0, dtype=0, n=4, theta=1, y0=1, rec=rec, s_max=8, g=1, dth=1,
+              dy0=1, ws=1, wsb=1 << 30, st=None)
+
+    def call(**o):
+        a = dict(ok)
+        a.update(o)
+        return L.dao_grad(a["system"], a["method"], a["dtype"], a["n"], a["theta"], a["y0"],
+                          a["rec"], a["s_max"], a["g"], a["dth"], a["dy0"], a["ws"], a["wsb"],
+                          a["st"])
+
+    assert call(s_max=17) == 1          # s_max > s_cap
+    assert call(s_max=-1) == 1
+    assert call(rec=None) == 1
+    assert call(g=None) == 1
+    assert call(theta=None) == 1
+    assert call(system=5, method=1) == 4
+    assert call(n=0) == 0
+
+
+def test_cotangent_argument_errors(L):
+    assert L.dao_sqerr_cotangent(0, 4, 3, 4, 1, 1, 1.0, 1, None) == 1
+    assert L.dao_sqerr_cotangent(0, 4, 0, 0, 1, 1, 1.0, 1, None) == 1
+    assert L.dao_sqerr_cotangent(0, 4, 3, 3, None, 1, 1.0, 1, None) == 1
+    assert L.dao_sqerr_cotangent(0, 0, 3, 3, None, None, 1.0, None, None) == 0

@@ -1,0 +1,223 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle on
+identical seeded inputs.
+
+Bars (per trajectory, relative 2-norm, R14 reading):
+* forward: accepted-step counts equal, final states within 1e-9 (fp64);
+* gradient: with both sides on the oracle's recorded mesh, dL/dtheta and
+  dL/dy0 within 1e-9 (fp64).  Robertson rate gradients are compared as
+  log-sensitivities theta * dL/dtheta (the rates span 0.04 ... 3e7).
+"""
+import numpy as np
+import pytest
+import torch
+
+import dao_inputs as di
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-9
+
+
+@pytest.fixture(scope="module")
+def dao():
+    import differentiable_adaptive_ode_amd as m
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+DEV = "cuda:0"
+
+
+def rel_err(a, b, axis=0):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.maximum(np.linalg.norm(b, axis=axis), 1e-300)
+    return np.linalg.norm(a - b, axis=axis) / den
+
+
+def gpu_solve(dao, w, s_cap, **kw):
+    th = torch.tensor(w.theta, device=DEV)
+    y0 = torch.tensor(w.y0, device=DEV)
+    rec, y1 = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=s_cap, **kw)
+    torch.cuda.synchronize()
+    return rec, y1
+
+
+def oracle_solve(w, s_cap, **kw):
+    return oracle.solve(w.system, w.method, w.theta, w.y0, w.t0, w.t1, w.rtol, w.atol,
+                        s_cap=s_cap, dtype=w.dtype, nthreads=8, **kw)
+
+
+def import_mesh(dao, w, ref, s_cap):
+    """A device record holding the oracle's mesh (what the gradient replays)."""
+    from differentiable_adaptive_ode_amd.api import Record
+
+    n = w.n
+    h = torch.zeros((n, s_cap), dtype=torch.float64, device=DEV)
+    h[:, :ref["h"].shape[1]] = torch.tensor(ref["h"], device=DEV)
+    return Record(w.system, w.method, w.dtype, torch.tensor(w.theta, device=DEV),
+                  torch.tensor(w.y0, device=DEV), w.t0, w.t1, h, None,
+                  torch.tensor(ref["count"], device=DEV), torch.tensor(ref["nrej"], device=DEV),
+                  torch.tensor(ref["status"], device=DEV))
+
+
+CASES = [("decay", 300, 256), ("lotka_volterra", 300, 256), ("lorenz63", 300, 1024),
+         ("loghalo", 200, 4096), ("robertson", 200, 2048)]
+
+
+@pytest.mark.parametrize("name,n,s_cap", CASES)
+def test_forward_parity(dao, name, n, s_cap):
+    w = di.make(name, n)
+    print(f"[forward parity] {name} n={n}", flush=True)
+    ref = oracle_solve(w, s_cap)
+    rec, y1 = gpu_solve(dao, w, s_cap)
+    cnt = rec.count.cpu().numpy()
+    assert np.array_equal(rec.status.cpu().numpy(), ref["status"])
+    assert np.array_equal(cnt, ref["count"]), np.flatnonzero(cnt != ref["count"])[:10]
+    assert np.array_equal(rec.nrej.cpu().numpy(), ref["nrej"])
+    err = rel_err(y1.cpu().numpy(), ref["y1"])
+    assert err.max() <= TOL, err.max()
+    h = rec.h.cpu().numpy()
+    t = rec.t.cpu().numpy()
+    mask = np.arange(s_cap)[None, :] < cnt[:, None]
+    assert np.array_equal(h[mask], ref["h"][mask])  # same arithmetic, same mesh bits
+    assert np.array_equal(t[mask], ref["t"][mask])
+
+
+@pytest.mark.parametrize("name,n,s_cap", CASES)
+def test_gradient_parity_on_oracle_mesh(dao, name, n, s_cap):
+    w = di.make(name, n)
+    print(f"[gradient parity] {name} n={n}", flush=True)
+    ref = oracle_solve(w, s_cap)
+    lam = di.cotangent(w, ref["y1"])
+    dth_o, dy0_o, _ = oracle.grad(w.system, w.method, w.theta, w.y0, ref["count"], ref["h"], lam,
+                                  nthreads=8)
+    rec = import_mesh(dao, w, ref, s_cap)
+    dth, dy0 = dao.grad(rec, torch.tensor(lam, device=DEV))
+    torch.cuda.synchronize()
+    dth = dth.cpu().numpy()
+    if name == "robertson":
+        e = rel_err(dth * w.theta, dth_o * w.theta)
+    else:
+        e = rel_err(dth, dth_o)
+    assert e.max() <= TOL, e.max()
+    e0 = rel_err(dy0.cpu().numpy(), dy0_o)
+    assert e0.max() <= TOL, e0.max()
+
+
+@pytest.mark.parametrize("name,n,s_cap", CASES[:3])
+def test_gradient_on_own_mesh_at_moved_theta(dao, name, n, s_cap):
+    # Reusing a record while theta moves (Sec. 3.1): the derivative is taken at
+    # the new theta on the old mesh.
+    w = di.make(name, n)
+    rec, y1 = gpu_solve(dao, w, s_cap)
+    ref = oracle_solve(w, s_cap)
+    th2 = w.theta * 1.001
+    lam = np.random.default_rng(2).normal(size=w.y0.shape)
+    dth_o, dy0_o, _ = oracle.grad(w.system, w.method, th2, w.y0, ref["count"], ref["h"], lam)
+    dth, dy0 = dao.grad(rec, torch.tensor(lam, device=DEV), theta=torch.tensor(th2, device=DEV))
+    torch.cuda.synchronize()
+    assert rel_err(dth.cpu().numpy(), dth_o).max() <= TOL
+    assert rel_err(dy0.cpu().numpy(), dy0_o).max() <= TOL
+
+
+def test_lorenz_full_size_sampled(dao):
+    # The benchmark's ensemble (65,536 Lorenz trajectories) in the benchmark's
+    # launch configuration; a seeded sample is checked against the oracle.
+    w = di.make("lorenz63")
+    print(f"[full size] lorenz63 n={w.n}", flush=True)
+    s_cap = 1024
+    rec, y1 = gpu_solve(dao, w, s_cap)
+    lam_all = torch.tensor(di.cotangent(w, y1.cpu().numpy()), device=DEV)
+    dth, dy0 = dao.grad(rec, lam_all)
+    torch.cuda.synchronize()
+    cnt = rec.count.cpu().numpy()
+    rng = np.random.default_rng(0)
+    idx = np.unique(np.concatenate([rng.choice(w.n, 96, replace=False), [0, w.n - 1],
+                                    [np.argmax(cnt), np.argmin(cnt)]]))
+    ws = di.subset(w, idx)
+    ref = oracle_solve(ws, s_cap)
+    assert np.array_equal(cnt[idx], ref["count"])
+    assert rel_err(y1.cpu().numpy()[:, idx], ref["y1"]).max() <= TOL
+    lam = lam_all.cpu().numpy()[:, idx]
+    dth_o, dy0_o, _ = oracle.grad(ws.system, ws.method, ws.theta, ws.y0, ref["count"], ref["h"],
+                                  lam, nthreads=8)
+    assert rel_err(dth.cpu().numpy()[:, idx], dth_o).max() <= TOL
+    assert rel_err(dy0.cpu().numpy()[:, idx], dy0_o).max() <= TOL
+    assert np.all(rec.status.cpu().numpy() == 0)
+
+
+# ------------------------------------------------------------------ edge cases
+def test_empty_ensemble(dao):
+    th = torch.empty((3, 0), dtype=torch.float64, device=DEV)
+    y0 = torch.empty((3, 0), dtype=torch.float64, device=DEV)
+    rec, y1 = dao.solve("lorenz63", "tsit5", th, y0, 0.0, 1.0, 1e-6, 1e-8, s_cap=8)
+    dth, dy0 = dao.grad(rec, torch.empty_like(y0), s_max=0)
+    torch.cuda.synchronize()
+    assert y1.shape == (3, 0) and dth.shape == (3, 0)
+
+
+def test_single_trajectory_and_zero_span(dao):
+    w = di.make("lorenz63", 1)
+    rec, y1 = gpu_solve(dao, w, 1024)
+    ref = oracle_solve(w, 1024)
+    assert rec.count.item() == ref["count"][0]
+    w0 = di.make("lorenz63", 70)
+    w0.t1 = w0.t0
+    rec, y1 = gpu_solve(dao, w0, 8)
+    assert np.all(rec.count.cpu().numpy() == 0)
+    assert np.array_equal(y1.cpu().numpy(), w0.y0)
+    lam = np.random.default_rng(1).normal(size=w0.y0.shape)
+    dth, dy0 = dao.grad(rec, torch.tensor(lam, device=DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(dy0.cpu().numpy(), lam) and np.all(dth.cpu().numpy() == 0)
+
+
+def test_failure_statuses(dao):
+    w = di.make("lorenz63", 130)
+    rec, y1 = gpu_solve(dao, w, 1024, max_steps=10)
+    assert np.all(rec.status.cpu().numpy() == 1) and torch.isnan(y1).all()
+    rec, y1 = gpu_solve(dao, w, 5)
+    ref = oracle_solve(w, 5)
+    assert np.array_equal(rec.status.cpu().numpy(), ref["status"])
+    assert np.all(rec.count.cpu().numpy() == 5)
+    th = w.theta.copy()
+    th[1, 7] = np.nan
+    w2 = di.Workload(**{**w.__dict__, "theta": th})
+    rec, y1 = gpu_solve(dao, w2, 1024)
+    st = rec.status.cpu().numpy()
+    assert st[7] == 2 and np.all(np.delete(st, 7) == 0)
+    # gradient of a failed trajectory is NaN; the rest are unaffected
+    lam = torch.ones_like(y1)
+    dth, dy0 = dao.grad(rec, lam)
+    torch.cuda.synchronize()
+    assert torch.isnan(dth[:, 7]).all() and torch.isfinite(dth[:, :7]).all()
+
+
+def test_s_max_bound_gives_nan_not_overrun(dao):
+    w = di.make("lorenz63", 100)
+    rec, y1 = gpu_solve(dao, w, 1024)
+    cnt = rec.count.cpu().numpy()
+    s_max = int(np.median(cnt))
+    dth, dy0 = dao.grad(rec, torch.ones_like(y1), s_max=s_max)
+    torch.cuda.synchronize()
+    bad = cnt > s_max
+    assert torch.isnan(dy0[:, torch.tensor(bad, device=DEV)]).all()
+    assert torch.isfinite(dy0[:, torch.tensor(~bad, device=DEV)]).all()
+
+
+def test_invalid_arguments_enqueue_nothing(dao):
+    from differentiable_adaptive_ode_amd import DaoError
+
+    w = di.make("lorenz63", 10)
+    th = torch.tensor(w.theta, device=DEV)
+    y0 = torch.tensor(w.y0, device=DEV)
+    with pytest.raises(DaoError):
+        dao.solve("lorenz63", "tsit5", th, y0, 1.0, 0.0, 1e-6, 1e-8)
+    with pytest.raises(DaoError):
+        dao.solve("lorenz63", "tsit5", th, y0, 0.0, 1.0, -1.0, 1e-8)
+    with pytest.raises(DaoError):
+        dao.solve("loghalo", "rosenbrock23", torch.zeros((3, 10), dtype=torch.float64, device=DEV),
+                  torch.zeros((6, 10), dtype=torch.float64, device=DEV), 0.0, 1.0, 1e-6, 1e-8)
