@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--workload", default="lorenz63")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=65536)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the steps, copy one buffer of MIB MiB once (a plain copy "
+                         "kernel of known size, the reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -106,6 +109,14 @@ def main():
 
     def events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 8, dtype=torch.float64, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         rec = step(events())

@@ -53,6 +53,67 @@ __device__ __forceinline__ float truncBits(float x) {
   return __uint_as_float(u);
 }
 
+// Step-size controller power x^(-1/Q) (Q = 10 for Tsit5, 6 for Rosenbrock23;
+// x is the mean square of the scaled error, so this is err^(-1/(order+1))).
+// A libm pow costs about a thousand cycles of dependent FP64 work per call on
+// one wavefront; this rule costs two short Horner chains:
+//   clamp x to [lo, hi] (beyond it 0.9 x^(-1/Q) is outside the controller's
+//   limits [0.2, 10] anyway), write x = m 2^e with m in [1, 2) and
+//   e = Q a + b (0 <= b < Q), then
+//   x^(-1/Q) = P(2m - 3) * E(2 b / Q - 1) * 2^(-a)
+// with P ~ m^(-1/Q) on [1, 2] and E ~ 2^(-f) on f in [0, 1] (Chebyshev
+// interpolants in monomial form; relative error below 1e-7).  Every step is
+// IEEE-exact or an explicit fused multiply-add, so the result does not depend
+// on any math library.
+template <int Q>
+struct CtrlRoot;
+template <>
+struct CtrlRoot<10> {
+  static constexpr double lo = 1e-12, hi = 1e8;
+  static constexpr double c[8] = {0.9602644780153649,     -0.03200878522189435,
+                                  0.005869002336249675,   -0.0013696795740665145,
+                                  0.0003502086621236076,  -9.523230976561381e-05,
+                                  3.278285231379161e-05,  -9.803433032024717e-06};
+};
+template <>
+struct CtrlRoot<6> {
+  static constexpr double lo = 1e-8, hi = 1e5;
+  static constexpr double c[8] = {0.9346552216460542,     -0.05192523185937651,
+                                  0.010097959271667333,   -0.0024314560515976726,
+                                  0.0006347021852295785,  -0.0001753744494318341,
+                                  6.143024330877807e-05,  -1.8571447204984547e-05};
+};
+__device__ constexpr double EXP2_NEG[7] = {0.7071067811579441,    -0.24506454511279616,
+                                           0.042466448938030865,  -0.004905842513716687,
+                                           0.00042506069534188184, -2.9611051419632863e-05,
+                                           1.7091800607644192e-06};
+
+__device__ __forceinline__ double frexpR(double x, int* e) { return __builtin_frexp(x, e); }
+__device__ __forceinline__ float frexpR(float x, int* e) { return __builtin_frexpf(x, e); }
+__device__ __forceinline__ double ldexpR(double x, int e) { return __builtin_ldexp(x, e); }
+__device__ __forceinline__ float ldexpR(float x, int e) { return __builtin_ldexpf(x, e); }
+
+template <class R, int Q>
+__device__ __forceinline__ R ctrl_root(R x) {
+  using K = CtrlRoot<Q>;
+  x = x > R(K::lo) ? x : R(K::lo);
+  x = x < R(K::hi) ? x : R(K::hi);
+  int e = 0;
+  const R m = frexpR(x, &e) * R(2);  // x = m 2^(e-1)
+  e -= 1;
+  const int a = (e + 64 * Q) / Q - 64;  // floor(e / Q); e > -64 Q after the clamp
+  const int b = e - Q * a;
+  const R s = m * R(2) - R(3);
+  R p = R(K::c[7]);
+#pragma unroll
+  for (int i = 6; i >= 0; --i) p = fmaR(p, s, R(K::c[i]));
+  const R s2 = fmaR(R(b), R(2.0 / Q), R(-1));
+  R q = R(EXP2_NEG[6]);
+#pragma unroll
+  for (int i = 5; i >= 0; --i) q = fmaR(q, s2, R(EXP2_NEG[i]));
+  return ldexpR(p * q, -a);
+}
+
 // Lane index within the 64-wide wavefront and cross-lane helpers.
 __device__ __forceinline__ int laneId() { return __lane_id(); }
 

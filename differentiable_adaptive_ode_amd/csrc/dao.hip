@@ -21,16 +21,32 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
   if (i < n) p[i] = v;
 }
 
-// bucket = (s_max + 1) - min(count, s_max + 1): larger counts come first.
-__device__ __forceinline__ int64_t bucket_of(int32_t c, int64_t s_max) {
+// Trajectory ordering for the gradient: a counting sort by decreasing
+// accepted-step count, so that the 64 lanes of a wavefront replay meshes of
+// similar length.  Counts are binned as
+//   bucket = ((s_max + 1) - min(count, s_max + 1)) >> shift
+// with shift chosen so that at most ORDER_BINS bins exist; the order within a
+// bin is arbitrary (each lane's result does not depend on its neighbours).
+// Both passes histogram in LDS first, so global atomics are one per non-empty
+// bin per workgroup rather than one per trajectory.
+__device__ __forceinline__ int bucket_of(int32_t c, int64_t s_max, int shift) {
   int64_t cc = c < 0 ? 0 : (int64_t)c;
   if (cc > s_max + 1) cc = s_max + 1;
-  return (s_max + 1) - cc;
+  return (int)(((s_max + 1) - cc) >> shift);
 }
 
-__global__ void count_hist_kernel(const int32_t* count, int64_t n, int64_t s_max, uint32_t* hist) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) atomicAdd(&hist[bucket_of(count[i], s_max)], 1u);
+__global__ void __launch_bounds__(256) order_hist_kernel(const int32_t* count, int64_t n,
+                                                         int64_t s_max, int shift, int nb,
+                                                         uint32_t* hist) {
+  __shared__ uint32_t lh[ORDER_BINS];
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) lh[b] = 0u;
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    atomicAdd(&lh[bucket_of(count[i], s_max, shift)], 1u);
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += blockDim.x)
+    if (lh[b]) atomicAdd(&hist[b], lh[b]);
 }
 
 // In-place exclusive scan of hist[0..nb) by one 1024-thread workgroup.
@@ -58,10 +74,26 @@ __global__ void __launch_bounds__(1024) scan_buckets_kernel(uint32_t* hist, int6
   }
 }
 
-__global__ void scatter_perm_kernel(const int32_t* count, int64_t n, int64_t s_max, uint32_t* off,
-                                    int32_t* perm) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) perm[atomicAdd(&off[bucket_of(count[i], s_max)], 1u)] = (int32_t)i;
+// Each workgroup owns the contiguous slice [lo, hi) of trajectories: it counts
+// its slice per bin in LDS, reserves each bin's range in the global offsets
+// with one atomic, then places its trajectories with LDS atomics.
+__global__ void __launch_bounds__(256) order_scatter_kernel(const int32_t* count, int64_t n,
+                                                            int64_t s_max, int shift, int nb,
+                                                            uint32_t* off, int32_t* perm) {
+  __shared__ uint32_t lh[ORDER_BINS];
+  const int64_t chunk = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int64_t hi = (lo + chunk < n) ? lo + chunk : n;
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) lh[b] = 0u;
+  __syncthreads();
+  for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x)
+    atomicAdd(&lh[bucket_of(count[i], s_max, shift)], 1u);
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += blockDim.x)
+    if (lh[b]) lh[b] = atomicAdd(&off[b], lh[b]);
+  __syncthreads();
+  for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x)
+    perm[atomicAdd(&lh[bucket_of(count[i], s_max, shift)], 1u)] = (int32_t)i;
 }
 
 template <class R>
@@ -157,6 +189,7 @@ dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0,
   a.nrej = rec->nrej;
   a.status = rec->status;
   a.queue = (unsigned long long*)ws;
+  a.trash = (R*)((char*)ws + ALIGN);
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)ws, (int64_t)2, 0u);
   auto kern = solve_kernel<R, Sys, M>;
   int64_t blocks = (n + BLOCK - 1) / BLOCK;
@@ -172,7 +205,8 @@ size_t grad_slot_bytes(int64_t s_max) {
 }
 
 size_t grad_header_bytes(int64_t n, int64_t s_max) {
-  return align_up(16) + align_up((size_t)(s_max + 2) * 4) + align_up((size_t)(n > 0 ? n : 1) * 4);
+  (void)s_max;
+  return align_up(16) + align_up((size_t)ORDER_BINS * 4) + align_up((size_t)(n > 0 ? n : 1) * 4);
 }
 
 template <class R, class Sys, int M>
@@ -183,7 +217,7 @@ dao_status launch_grad(int64_t n, const void* theta, const void* y0, const dao_r
   char* base = (char*)ws;
   unsigned long long* groups = (unsigned long long*)base;
   uint32_t* hist = (uint32_t*)(base + align_up(16));
-  int32_t* perm = (int32_t*)(base + align_up(16) + align_up((size_t)(s_max + 2) * 4));
+  int32_t* perm = (int32_t*)(base + align_up(16) + align_up((size_t)ORDER_BINS * 4));
   const size_t hdr = grad_header_bytes(n, s_max);
   R* scratch = (R*)(base + hdr);
   const size_t slot = grad_slot_bytes<R, D>(s_max);
@@ -198,15 +232,19 @@ dao_status launch_grad(int64_t n, const void* theta, const void* y0, const dao_r
   if (blocks > slots / waves_per_block) blocks = slots / waves_per_block;
   if (blocks < 1) return fail(DAO_EWORKSPACE, "dao_grad: workspace too small");
 
-  const int64_t nb = s_max + 2;
+  int shift = 0;
+  while (((s_max + 1) >> shift) + 1 > ORDER_BINS) ++shift;
+  const int nb = (int)(((s_max + 1) >> shift) + 1);
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream,
-                     hist, nb, 0u);
+                     hist, (int64_t)nb, 0u);
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)groups, (int64_t)2, 0u);
-  const unsigned nblk = (unsigned)((n + 255) / 256);
-  hipLaunchKernelGGL(count_hist_kernel, dim3(nblk), dim3(256), 0, stream, rec->count, n, s_max, hist);
-  hipLaunchKernelGGL(scan_buckets_kernel, dim3(1), dim3(1024), 0, stream, hist, nb);
-  hipLaunchKernelGGL(scatter_perm_kernel, dim3(nblk), dim3(256), 0, stream, rec->count, n, s_max,
-                     hist, perm);
+  int64_t oblk = (n + 255) / 256;
+  if (oblk > 1024) oblk = 1024;
+  hipLaunchKernelGGL(order_hist_kernel, dim3((unsigned)oblk), dim3(256), 0, stream, rec->count, n,
+                     s_max, shift, nb, hist);
+  hipLaunchKernelGGL(scan_buckets_kernel, dim3(1), dim3(1024), 0, stream, hist, (int64_t)nb);
+  hipLaunchKernelGGL(order_scatter_kernel, dim3((unsigned)oblk), dim3(256), 0, stream, rec->count,
+                     n, s_max, shift, nb, hist, perm);
 
   GradArgs<R> a;
   a.n = n;
@@ -319,7 +357,7 @@ dao_status dao_system_dims(dao_system sys, int* d, int* p, int* shared) {
 
 size_t dao_solve_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n) {
   (void)sys; (void)method; (void)dtype; (void)n;
-  return ALIGN;
+  return ALIGN + align_up((size_t)WAVE * 2 * sizeof(double));  // queue counter + trash slots
 }
 
 dao_status dao_solve(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,

@@ -40,6 +40,7 @@ struct SolveArgs {
   int32_t* nrej;
   int32_t* status;
   unsigned long long* queue;
+  R* trash;  // [64][2] scratch target of record stores that have no row
 };
 
 template <class R>
@@ -60,6 +61,8 @@ struct GradArgs {
   unsigned long long* groups;
 };
 
+// Mean of squares of the scaled error: (1/D) sum_c (e_c / sc_c)^2, summed in
+// component order, the mean taken as a product with the constant 1/D.
 template <class R, int D>
 __device__ __forceinline__ R mean_sq(const R (&e)[D], const R (&sc)[D]) {
   R r = e[0] / sc[0];
@@ -69,7 +72,7 @@ __device__ __forceinline__ R mean_sq(const R (&e)[D], const R (&sc)[D]) {
     r = e[c] / sc[c];
     acc = fmaR(r, r, acc);
   }
-  return acc / R(D);
+  return acc * R(1.0 / D);
 }
 
 // Starting step: Hairer, Norsett & Wanner, Solving ODEs I, Sec. II.4, with
@@ -107,8 +110,10 @@ template <class R, class Sys, int METHOD>
 __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   constexpr int D = Sys::D;
   constexpr int ORDER = (METHOD == M_TSIT5) ? 5 : 2;
-  const R expo = (METHOD == M_TSIT5) ? R(-0.1) : R(-1.0 / 6.0);
+  constexpr int CTRL_Q = (METHOD == M_TSIT5) ? 10 : 6;  // msq^(-1/Q) = err^(-1/(ORDER+1))
+  constexpr int32_t RUNNING = -1;
   const int lane = laneId();
+  R* const trash = a.trash + 2 * lane;
 
   Sys sys;
   R y[D];
@@ -119,6 +124,8 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   bool prev_rej = false;
   int64_t traj = -1;
   bool live = true;
+  R* hrow = nullptr;
+  R* trow = nullptr;
 
   auto finish = [&](int32_t st) {
 #pragma unroll
@@ -129,15 +136,22 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     traj = -1;
   };
 
+  // Once a claim comes back past the end of the ensemble, the queue is empty
+  // for good: the wavefront stops claiming (a device-scope atomic is a round
+  // trip to the coherence point, and every wavefront hitting one counter
+  // serialises there).
+  bool drained = false;
   for (;;) {
     // ---- refill idle lanes from the work queue: one atomic per wavefront
     const bool need = live && traj < 0;
-    const unsigned long long m = __ballot(need);
+    if (drained && need) live = false;
+    const unsigned long long m = drained ? 0ull : __ballot(need);
     if (m) {
       const int leader = __ffsll((unsigned long long)m) - 1;
       unsigned long long base = 0;
       if (lane == leader) base = atomicAdd(a.queue, (unsigned long long)__popcll(m));
       base = __shfl(base, leader);
+      if (base + (unsigned long long)__popcll(m) >= (unsigned long long)a.n) drained = true;
       if (need) {
         const unsigned long long kk = base + (unsigned long long)__popcll(m & ((1ull << lane) - 1ull));
         if (kk < (unsigned long long)a.n) {
@@ -145,6 +159,13 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
           sys.load(a.theta, a.n, traj);
 #pragma unroll
           for (int c = 0; c < D; ++c) y[c] = a.y0[c * a.n + traj];
+          // Loads and stores share one in-order counter (vmcnt).  Waiting
+          // here, once per trajectory, keeps the attempt loop below free of
+          // waits that would otherwise also drain the record stores of the
+          // previous attempt.
+          __builtin_amdgcn_s_waitcnt(0);
+          hrow = a.h_rec + traj * a.s_cap;
+          trow = a.t_rec ? a.t_rec + traj * a.s_cap : nullptr;
           t = a.t0;
           nacc = 0;
           nrej = 0;
@@ -164,22 +185,11 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     if (__ballot(live) == 0ull) break;
     if (traj < 0) continue;
 
-    // ---- one attempted step
-    if (attempts >= a.max_steps) {
-      finish(TRAJ_MAX_STEPS);
-      continue;
-    }
+    // ---- one attempted step.  Both outcomes are applied by selects; the
+    // only branch is the (rare) exit of a finished or failed trajectory.
     ++attempts;
     const bool last = (t + h >= a.t1);
     const R hs = last ? (a.t1 - t) : h;
-    if (!finiteR(hs)) {
-      finish(TRAJ_NONFINITE);
-      continue;
-    }
-    if (!(t + hs > t)) {
-      finish(TRAJ_DT_UNDERFLOW);
-      continue;
-    }
     R ynew[D], err[D], F2[D];
     if constexpr (METHOD == M_TSIT5) {
       tsit5::trial<R, Sys>(sys, y, hs, k, ynew, err);
@@ -193,42 +203,49 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
       sc[c] = fmaR(a.rtol, (ay < an) ? an : ay, a.atol);
     }
     const R msq = mean_sq<R, D>(err, sc);
-    if (!finiteR(msq)) {
-      finish(TRAJ_NONFINITE);
-      continue;
-    }
-    if (msq <= R(1)) {
-      if (nacc >= a.s_cap) {
-        finish(TRAJ_CAPACITY);
-        continue;
-      }
-      const int64_t row = traj * a.s_cap + nacc;
-      if (a.t_rec) a.t_rec[row] = t;
-      if (a.h_rec) a.h_rec[row] = hs;
-      ++nacc;
-      t = last ? a.t1 : t + hs;
+    const bool acc = msq <= R(1);
+    // One controller evaluation serves both outcomes.
+    const R root = ctrl_root<R, CTRL_Q>(msq);
+    const R fq = (msq == R(0)) ? R(10) : truncBits(R(0.9) * root);
+    const R fmin = (R(0.2) < fq) ? fq : R(0.2);
+
+    // Failure checks in the solve's order of precedence, as selects (the
+    // lowest-precedence check is applied first and overridden).
+    int32_t st = (acc && nacc >= a.s_cap) ? TRAJ_CAPACITY : RUNNING;
+    st = finiteR(msq) ? st : TRAJ_NONFINITE;
+    st = (t + hs > t) ? st : TRAJ_DT_UNDERFLOW;
+    st = finiteR(hs) ? st : TRAJ_NONFINITE;
+
+    // Record row nacc: an accepted step keeps it, a rejected one is
+    // overwritten by the next accepted step (rows past count are unused).
+    // With the record full, the store goes to the lane's trash slot.
+    const bool room = nacc < a.s_cap;
+    *(room ? hrow + nacc : trash) = hs;
+    if (a.t_rec) *(room ? trow + nacc : trash + 1) = t;
+
+    const bool take = (st == RUNNING) && acc;
+    const R tn = last ? a.t1 : t + hs;
 #pragma unroll
-      for (int c = 0; c < D; ++c) y[c] = ynew[c];
-      if constexpr (METHOD == M_TSIT5) {
+    for (int c = 0; c < D; ++c) y[c] = take ? ynew[c] : y[c];
+    if constexpr (METHOD == M_TSIT5) {
 #pragma unroll
-        for (int c = 0; c < D; ++c) k[0][c] = k[6][c];
-      } else {
-#pragma unroll
-        for (int c = 0; c < D; ++c) k[0][c] = F2[c];
-      }
-      R fac = (msq == R(0)) ? R(10) : truncBits(R(0.9) * powR(msq, expo));
-      fac = (R(0.2) < fac) ? fac : R(0.2);
-      fac = (fac < R(10)) ? fac : R(10);
-      if (prev_rej) fac = (fac < R(1)) ? fac : R(1);
-      h = hs * fac;
-      prev_rej = false;
-      if (!(t < a.t1)) finish(TRAJ_OK);
+      for (int c = 0; c < D; ++c) k[0][c] = take ? k[6][c] : k[0][c];
     } else {
-      ++nrej;
-      const R fq = truncBits(R(0.9) * powR(msq, expo));
-      h = hs * ((R(0.2) < fq) ? fq : R(0.2));
-      prev_rej = true;
+#pragma unroll
+      for (int c = 0; c < D; ++c) k[0][c] = take ? F2[c] : k[0][c];
     }
+    t = take ? tn : t;
+    nacc += take ? 1 : 0;
+    nrej += (st == RUNNING && !acc) ? 1 : 0;
+    R fa = (fmin < R(10)) ? fmin : R(10);
+    fa = (prev_rej && fa > R(1)) ? R(1) : fa;
+    h = hs * (acc ? fa : fmin);
+    prev_rej = !acc;
+    if (st == RUNNING) {
+      if (take && !(tn < a.t1)) st = TRAJ_OK;
+      else if (attempts >= a.max_steps) st = TRAJ_MAX_STEPS;
+    }
+    if (st != RUNNING) finish(st);
   }
 }
 
@@ -262,11 +279,19 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
       mx = (o > mx) ? o : mx;
     }
 
+    // Lanes past the end of the ensemble (k < 0, count 0) run the loops below
+    // on trajectory 0's parameters with a zero state; nothing of theirs is
+    // written.
     Sys sys;
     R y[D], lam[D], pb[P];
+    sys.load(a.theta, a.n, k >= 0 ? k : 0);
     const R* hrow = a.h_rec;
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      y[c] = R(0);
+      lam[c] = R(0);
+    }
     if (k >= 0) {
-      sys.load(a.theta, a.n, k);
 #pragma unroll
       for (int c = 0; c < D; ++c) {
         y[c] = a.y0[c * a.n + k];
@@ -277,30 +302,54 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
 #pragma unroll
     for (int j = 0; j < P; ++j) pb[j] = R(0);
 
-    // forward replay, storing y_j before step j
+    // The group's lanes step in lockstep for mx steps.  A lane past its own
+    // count takes steps of size zero: for a finite state, a zero step leaves y
+    // unchanged, and its reverse leaves lam and the parameter cotangent
+    // unchanged (every update is a multiple of h), so those steps are exact
+    // no-ops and the loops need no per-lane branches.  Rows i < mx <= s_max
+    // <= s_cap of a record are in bounds whatever their contents; rows past a
+    // lane's count are loaded but not used.
+    //
+    // Forward replay, storing y_j before step j.  Each step's h is loaded one
+    // step ahead: loads and stores retire in order (one vmcnt counter), so a
+    // load issued before this step's stores is ready by the next step without
+    // waiting for those stores.
+    R h_nx = (mx > 0) ? hrow[0] : R(0);
     for (int i = 0; i < mx; ++i) {
-      if (i < cnt) {
+      const R hj = (i < cnt) ? h_nx : R(0);
+      if (i + 1 < mx) h_nx = hrow[i + 1];
 #pragma unroll
-        for (int c = 0; c < D; ++c) scr[((int64_t)i * D + c) * WAVE] = y[c];
-        const R hj = hrow[i];
-        if constexpr (METHOD == M_TSIT5)
-          tsit5::replay<R, Sys>(sys, y, hj);
-        else
-          ros23::replay<R, Sys>(sys, y, hj);
-      }
+      for (int c = 0; c < D; ++c) scr[((int64_t)i * D + c) * WAVE] = y[c];
+      if constexpr (METHOD == M_TSIT5)
+        tsit5::replay<R, Sys>(sys, y, hj);
+      else
+        ros23::replay<R, Sys>(sys, y, hj);
     }
-    // reverse sweep
-    for (int i = mx - 1; i >= 0; --i) {
-      if (i < cnt) {
-        R yj[D];
+    // Reverse sweep, with y_j and h_j of the next step (j - 1) prefetched the
+    // same way.
+    R y_nx[D];
 #pragma unroll
-        for (int c = 0; c < D; ++c) yj[c] = scr[((int64_t)i * D + c) * WAVE];
-        const R hj = hrow[i];
-        if constexpr (METHOD == M_TSIT5)
-          tsit5::reverse<R, Sys>(sys, yj, hj, lam, pb);
-        else
-          ros23::reverse<R, Sys>(sys, yj, hj, lam, pb);
+    for (int c = 0; c < D; ++c) y_nx[c] = R(0);
+    h_nx = R(0);
+    if (mx > 0) {
+#pragma unroll
+      for (int c = 0; c < D; ++c) y_nx[c] = scr[((int64_t)(mx - 1) * D + c) * WAVE];
+      h_nx = hrow[mx - 1];
+    }
+    for (int i = mx - 1; i >= 0; --i) {
+      R yj[D];
+      const R hj = (i < cnt) ? h_nx : R(0);
+#pragma unroll
+      for (int c = 0; c < D; ++c) yj[c] = y_nx[c];
+      if (i >= 1) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) y_nx[c] = scr[((int64_t)(i - 1) * D + c) * WAVE];
+        h_nx = hrow[i - 1];
       }
+      if constexpr (METHOD == M_TSIT5)
+        tsit5::reverse<R, Sys>(sys, yj, hj, lam, pb);
+      else
+        ros23::reverse<R, Sys>(sys, yj, hj, lam, pb);
     }
     if (k >= 0) {
       if (!ok) {
@@ -322,10 +371,12 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
 }
 
 // ---- trajectory ordering by step count (counting sort, decreasing count)
+constexpr int ORDER_BINS = 4096;
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v);
-__global__ void count_hist_kernel(const int32_t* count, int64_t n, int64_t s_max, uint32_t* hist);
+__global__ void order_hist_kernel(const int32_t* count, int64_t n, int64_t s_max, int shift, int nb,
+                                  uint32_t* hist);
 __global__ void scan_buckets_kernel(uint32_t* hist, int64_t nb);
-__global__ void scatter_perm_kernel(const int32_t* count, int64_t n, int64_t s_max, uint32_t* off,
-                                    int32_t* perm);
+__global__ void order_scatter_kernel(const int32_t* count, int64_t n, int64_t s_max, int shift,
+                                     int nb, uint32_t* off, int32_t* perm);
 
 }  // namespace dao

@@ -66,6 +66,10 @@ def lib():
         L.oracle_step_f64.argtypes = [I, I, P, P, D, P, P]
         L.oracle_rhs_f64.argtypes = [I, P, P, P]
         L.oracle_jac_f64.argtypes = [I, P, P, P]
+        L.oracle_ctrl_root_f64.argtypes = [D, I]
+        L.oracle_ctrl_root_f64.restype = D
+        L.oracle_ctrl_root_f32.argtypes = [ctypes.c_float, I]
+        L.oracle_ctrl_root_f32.restype = ctypes.c_float
         _lib = L
     return _lib
 
@@ -182,6 +186,12 @@ def step(system, method, theta, y, h):
                                _p(ynew), _p(err))
     assert rc == 0
     return ynew, err
+
+
+def ctrl_root(x, q, dtype="f64"):
+    """The solve's controller power x^(-1/q) (q = 10 or 6), as the oracle evaluates it."""
+    fn = lib().oracle_ctrl_root_f64 if dtype == "f64" else lib().oracle_ctrl_root_f32
+    return np.array([fn(float(v), int(q)) for v in np.atleast_1d(x)])
 
 
 def rhs(system, theta, y):

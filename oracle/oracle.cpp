@@ -32,9 +32,12 @@
 //     (the ode23s triple, autonomous form).
 //   * Controller: integral controller fac = 0.9 * err^(-1/(q+1)) with
 //     q+1 = 5 (Tsit5) or 3 (Rosenbrock23), clamped to [0.2, 10], no growth on
-//     the step after a rejection; the factor is truncated to 16 explicit
-//     mantissa bits (8 in binary32) so that the mesh does not depend on the
-//     last-ulp behaviour of pow() in a given math library.
+//     the step after a rejection.  The test works on the mean square
+//     msq = err^2, so the power is msq^(-1/10) or msq^(-1/6); it is evaluated
+//     by the fixed rule of ctrl_root() below (relative error under 1e-7, only
+//     IEEE-exact steps and explicit fused multiply-adds), so every
+//     implementation that takes the same steps gets the same bits.  The
+//     factor is then truncated to 16 explicit mantissa bits (8 in binary32).
 //   * Initial step: Hairer-Norsett-Wanner, Solving ODEs I, Sec. II.4, with
 //     exponent 1/order, truncated like the controller factor.
 //   * The last step is clipped to land exactly on t1.
@@ -430,7 +433,47 @@ inline float trunc_bits(float x) {  // keep 8 explicit mantissa bits
   return x;
 }
 
-// Mean of squares of the scaled components, sum order c = 0..d-1.
+// Controller power x^(-1/q), q = 10 (Tsit5) or 6 (Rosenbrock23), for x > 0.
+// x is first clamped to a range outside which 0.9 x^(-1/q) lies beyond the
+// controller's limits [0.2, 10] anyway.  With x = m 2^e (m in [1, 2)) and
+// e = q a + b (0 <= b < q):
+//   x^(-1/q) = m^(-1/q) * 2^(-b/q) * 2^(-a),
+// where m^(-1/q) and 2^(-f) (f = b/q in [0, 1)) are polynomials in
+// s in [-1, 1] (Chebyshev interpolants of those functions on 400 nodes,
+// rewritten in monomial form, evaluated by Horner's rule with fused
+// multiply-adds) and the power of two is exact.
+const double ROOT10_C[8] = {0.9602644780153649,     -0.03200878522189435,  0.005869002336249675,
+                            -0.0013696795740665145, 0.0003502086621236076, -9.523230976561381e-05,
+                            3.278285231379161e-05,  -9.803433032024717e-06};
+const double ROOT6_C[8] = {0.9346552216460542,     -0.05192523185937651,    0.010097959271667333,
+                           -0.0024314560515976726, 0.0006347021852295785,   -0.0001753744494318341,
+                           6.143024330877807e-05,  -1.8571447204984547e-05};
+const double EXP2N_C[7] = {0.7071067811579441,     -0.24506454511279616,  0.042466448938030865,
+                           -0.004905842513716687,  0.00042506069534188184, -2.9611051419632863e-05,
+                           1.7091800607644192e-06};
+
+template <class T>
+T ctrl_root(T x, int q) {
+  const double* rc = (q == 10) ? ROOT10_C : ROOT6_C;
+  const T lo = (q == 10) ? T(1e-12) : T(1e-8);
+  const T hi = (q == 10) ? T(1e8) : T(1e5);
+  x = std::min(std::max(x, lo), hi);
+  int e = 0;
+  T m = std::frexp(x, &e) * T(2.0);  // x = m 2^(e-1), m in [1, 2)
+  e -= 1;
+  const int a = (e >= 0) ? e / q : -((q - 1 - e) / q);  // floor(e / q)
+  const int b = e - q * a;
+  const T s = m * T(2.0) - T(3.0);  // exact
+  T p = T(rc[7]);
+  for (int i = 6; i >= 0; --i) p = fma3(p, s, T(rc[i]));
+  const T s2 = fma3(T(b), T(2.0 / q), T(-1.0));
+  T c = T(EXP2N_C[6]);
+  for (int i = 5; i >= 0; --i) c = fma3(c, s2, T(EXP2N_C[i]));
+  return std::ldexp(p * c, -a);
+}
+
+// Mean of squares of the scaled components, sum order c = 0..d-1; the mean
+// is the sum times the constant 1/d.
 template <class T>
 T mean_sq(int d, const T* e, const T* sc) {
   T r = e[0] / sc[0];
@@ -439,7 +482,7 @@ T mean_sq(int d, const T* e, const T* sc) {
     r = e[c] / sc[c];
     acc = fma3(r, r, acc);
   }
-  return acc / T(d);
+  return acc * T(1.0 / d);
 }
 
 // Starting step (Hairer, Norsett & Wanner, Solving ODEs I, Sec. II.4).
@@ -476,7 +519,7 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
                       T dt0, int64_t max_steps, int64_t s_cap, T* y1, T* t_rec, T* h_rec) {
   const int d = SYS_D[sys];
   const int order = (method == M_TSIT5) ? 5 : 2;
-  const T expo = (method == M_TSIT5) ? T(-0.1) : T(-1.0 / 6.0);  // applied to the mean square
+  const int q = (method == M_TSIT5) ? 10 : 6;  // msq^(-1/q) = err^(-1/(order+1))
   SolveOut<T> out = {0, 0, ST_OK};
   T y[MAXD], ynew[MAXD], e[MAXD], sc[MAXD], k[7][MAXD], F2[MAXD];
   for (int c = 0; c < d; ++c) y[c] = y0[c];
@@ -514,14 +557,14 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
           for (int c = 0; c < d; ++c) k[0][c] = k[6][c];
         else
           for (int c = 0; c < d; ++c) k[0][c] = F2[c];
-        T fac = (msq == T(0)) ? T(10.0) : trunc_bits(T(0.9) * T(std::pow(msq, expo)));
+        T fac = (msq == T(0)) ? T(10.0) : trunc_bits(T(0.9) * ctrl_root(msq, q));
         fac = std::min(T(10.0), std::max(T(0.2), fac));
         if (prev_rejected) fac = std::min(fac, T(1.0));
         h = hs * fac;
         prev_rejected = false;
       } else {
         ++out.nrej;
-        T fac = std::max(T(0.2), trunc_bits(T(0.9) * T(std::pow(msq, expo))));
+        T fac = std::max(T(0.2), trunc_bits(T(0.9) * ctrl_root(msq, q)));
         h = hs * fac;
         prev_rejected = true;
       }
@@ -787,6 +830,10 @@ int oracle_step_f64(int sys, int method, const double* th, const double* y, doub
     ros23_step(sys, th, d, y, h, k[0], ynew, F2, err);
   return 0;
 }
+
+// The controller power x^(-1/q) of the solve (for tests of its accuracy).
+double oracle_ctrl_root_f64(double x, int q) { return ctrl_root<double>(x, q); }
+float oracle_ctrl_root_f32(float x, int q) { return ctrl_root<float>(x, q); }
 
 // Right-hand side and Jacobian at single points (for tests of the fields).
 int oracle_rhs_f64(int sys, const double* th, const double* y, double* dy) {

@@ -164,3 +164,26 @@ def test_tsit5_stability_function_from_table(orc):
         # fifth order: R(z) - exp(z) = O(z^6)
     for z in (-0.05, -0.1):
         assert abs(_tsit5_R(orc, z) - np.exp(z)) < 1e-2 * abs(z) ** 6
+
+
+@pytest.mark.parametrize("q", [10, 6])
+def test_controller_power_matches_exact_power(orc, q):
+    # The controller factor 0.9 * msq^(-1/q), clamped to [0.2, 10], is the
+    # integral controller err^(-1/(order+1)) on the mean square msq = err^2.
+    # The oracle evaluates the power by a polynomial rule; pin it to the exact
+    # power inside its range, and check that the clamped range only cuts where
+    # the clamped factor saturates anyway.
+    lo, hi = (1e-12, 1e8) if q == 10 else (1e-8, 1e5)
+    x = np.logspace(np.log10(lo), np.log10(hi), 4001)
+    x = np.concatenate([x, x * (1 + 1e-9), np.nextafter(x, 0)])
+    x = x[(x >= lo) & (x <= hi)]
+    got = orc.ctrl_root(x, q)
+    exact = x ** (-1.0 / q)
+    assert np.max(np.abs(got / exact - 1)) < 1e-7
+    got32 = orc.ctrl_root(x.astype(np.float32), q, dtype="f32")
+    exact32 = x.astype(np.float32).astype(np.float64) ** (-1.0 / q)
+    assert np.max(np.abs(got32 / exact32 - 1)) < 2e-6
+    assert 0.9 * lo ** (-1.0 / q) >= 10 and 0.9 * hi ** (-1.0 / q) <= 0.2
+    out = orc.ctrl_root(np.array([lo * 1e-3, hi * 1e3]), q)
+    assert out[0] == orc.ctrl_root(np.array([lo]), q)[0]
+    assert out[1] == orc.ctrl_root(np.array([hi]), q)[0]
