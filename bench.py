@@ -145,6 +145,14 @@ def main():
     fl_grad = steps_total * f_step
     dom = "grad" if tg >= ts else "solve"
     ach = (fl_grad / tg) if dom == "grad" else (fl_solve / ts)
+    # Measured HBM bytes per launch of the dominant kernel (rocprofv3 FETCH_SIZE +
+    # WRITE_SIZE, copy-calibrated), only if taken on the current kernel sources.
+    from differentiable_adaptive_ode_amd.profiling import load_traffic
+
+    tr = load_traffic(w.name)
+    traffic = None
+    if tr is not None and f"{dom}_kernel" in tr["kernels"]:
+        traffic = tr["kernels"][f"{dom}_kernel"]["hbm_bytes"]
     out = {
         "metric": "gradient trajectories/s (replay adjoint) + solves/s at 1 GPU; % of roofline",
         "value": w.n / (wall / args.steps),
@@ -171,7 +179,10 @@ def main():
         "grad_fp64_tflops": fl_grad / tg * 1e-12,
         "roofline": {"bound": "alu", "kernel": f"{dom}_kernel", "achieved": ach * 1e-12,
                      "peak": PEAK_FP64_VALU * 1e-12, "unit": "TFLOP/s",
-                     "frac": ach / PEAK_FP64_VALU, "traffic": None},
+                     "frac": ach / PEAK_FP64_VALU, "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch"},
+        "roofline_solve_frac": fl_solve / ts / PEAK_FP64_VALU,
+        "roofline_grad_frac": fl_grad / tg / PEAK_FP64_VALU,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)

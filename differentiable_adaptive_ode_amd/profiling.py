@@ -1,0 +1,189 @@
+"""Profile bookkeeping for the benchmark: kernel-source digests and summaries of
+rocprofv3 CSV output.
+
+    python -m differentiable_adaptive_ode_amd.profiling summarize \\
+        --workload lorenz63 --n 65536 --trace DIR --fetch DIR --write DIR \\
+        [--sq DIR] --copy-mib 256 --cmd-trace "..." --cmd-fetch "..." \\
+        --cmd-write "..." [--cmd-sq "..."] --out profiles
+
+`summarize` reads the kernel_stats / counter_collection CSVs that
+`rocprofv3 -f csv` wrote, and writes
+
+* profiles/<workload>_n<N>_kernels.md  -- per-kernel average durations, HBM
+  bytes per launch and (with --sq) instruction counts, with the commands;
+* profiles/traffic_<workload>.json     -- HBM bytes per launch of the solve and
+  gradient kernels, tagged with the digest of the kernel sources they were
+  measured on.
+
+HBM bytes: rocprofv3's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled
+by what the same counters read for a plain device-to-device copy of a known
+size in the same run (bench.py --copy-calibration MiB): factor = copied bytes /
+counted bytes, separately for reads and writes.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources (file names and contents, sorted)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload: str, root: str | None = None) -> str:
+    root = root or os.path.join(os.path.dirname(HERE), "profiles")
+    return os.path.join(root, f"traffic_{workload}.json")
+
+
+def load_traffic(workload: str):
+    """Measured HBM bytes per launch for the current kernel sources, or None."""
+    p = traffic_path(workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return d
+
+
+def _short(name: str) -> str:
+    if "solve_kernel" in name:
+        return "solve_kernel"
+    if "grad_kernel" in name:
+        return "grad_kernel"
+    if "mlp" in name.lower():
+        return name.split("(")[0].replace("void ", "")
+    return name.split("(")[0].replace("void ", "")
+
+
+def _find(d: str, suffix: str) -> str:
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def read_stats(trace_dir: str):
+    rows = list(csv.DictReader(open(_find(trace_dir, "kernel_stats.csv"))))
+    return [(r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["Percentage"])) for r in rows]
+
+
+def read_counters(d: str):
+    """{(kernel name, counter): [values per dispatch]} and {name: grid sizes}."""
+    vals = defaultdict(list)
+    grids = defaultdict(set)
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        vals[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+        grids[r["Kernel_Name"]].add(int(r["Grid_Size"]))
+    return vals, grids
+
+
+def _copy_counter(vals, counter: str, copy_bytes: int) -> float:
+    """Largest per-dispatch value of `counter` over copy kernels (the calibration copy)."""
+    best = 0.0
+    for (name, c), v in vals.items():
+        if c == counter and "copyBuffer" in name:
+            best = max(best, max(v))
+    if best <= 0:
+        raise RuntimeError(f"no copy kernel with {counter} in the counter run")
+    return copy_bytes / (best * 1024.0)
+
+
+def summarize(args) -> None:
+    stats = read_stats(args.trace)
+    fetch, _ = read_counters(args.fetch)
+    write, _ = read_counters(args.write)
+    copy_bytes = args.copy_mib << 20
+    f_fac = _copy_counter(fetch, "FETCH_SIZE", copy_bytes)
+    w_fac = _copy_counter(write, "WRITE_SIZE", copy_bytes)
+
+    def per_launch(vals, counter, fac, key):
+        xs = [v for (name, c), vv in vals.items() if c == counter and _short(name) == key for v in vv]
+        return (sum(xs) / len(xs)) * 1024.0 * fac if xs else None
+
+    traffic = {"workload": args.workload, "n": args.n, "kernel_source_sha256": kernel_source_digest(),
+               "fetch_factor": f_fac, "write_factor": w_fac, "kernels": {}}
+    for key in ("solve_kernel", "grad_kernel"):
+        fb = per_launch(fetch, "FETCH_SIZE", f_fac, key)
+        wb = per_launch(write, "WRITE_SIZE", w_fac, key)
+        if fb is not None and wb is not None:
+            traffic["kernels"][key] = {"read_bytes": fb, "write_bytes": wb, "hbm_bytes": fb + wb}
+    os.makedirs(args.out, exist_ok=True)
+    with open(traffic_path(args.workload, args.out), "w") as f:
+        json.dump(traffic, f, indent=1)
+
+    sq = None
+    if args.sq:
+        sq, _ = read_counters(args.sq)
+    lines = [f"# {args.workload}, n = {args.n}: kernel durations and HBM traffic", "",
+             "Kernel trace (rocprofv3 --kernel-trace --stats):", "", "    " + args.cmd_trace, "",
+             "| kernel | calls | average us | share of GPU time |", "|---|---|---|---|"]
+    for name, calls, avg, pct in stats:
+        lines.append(f"| {_short(name)} | {calls} | {avg / 1e3:.2f} | {pct:.1f} % |")
+    lines += ["", "HBM bytes per launch (FETCH_SIZE, WRITE_SIZE in KiB per dispatch, scaled by the "
+              "calibration copy of the same run):", "", "    " + args.cmd_fetch, "    " + args.cmd_write, "",
+              f"Calibration: a device-to-device copy of {args.copy_mib} MiB reads "
+              f"{copy_bytes / f_fac / 1024:.0f} KiB of FETCH_SIZE and {copy_bytes / w_fac / 1024:.0f} KiB of "
+              f"WRITE_SIZE, so read bytes = {f_fac:.3f} x FETCH_SIZE x 1024 and write bytes = "
+              f"{w_fac:.3f} x WRITE_SIZE x 1024.", "",
+              "| kernel | read MB / launch | write MB / launch |", "|---|---|---|"]
+    for key, t in traffic["kernels"].items():
+        lines.append(f"| {key} | {t['read_bytes'] / 1e6:.1f} | {t['write_bytes'] / 1e6:.1f} |")
+    if sq:
+        lines += ["", "Instruction counters (per launch, summed over the device):", "",
+                  "    " + args.cmd_sq, ""]
+        counters = sorted({c for (_, c) in sq})
+        lines.append("| kernel | " + " | ".join(counters) + " |")
+        lines.append("|---|" + "---|" * len(counters))
+        for key in ("solve_kernel", "grad_kernel"):
+            row = []
+            for c in counters:
+                xs = [v for (name, cc), vv in sq.items() if cc == c and _short(name) == key for v in vv]
+                row.append(f"{sum(xs) / len(xs):.4g}" if xs else "-")
+            lines.append(f"| {key} | " + " | ".join(row) + " |")
+    lines += ["", f"Kernel sources sha256: `{traffic['kernel_source_sha256']}`", ""]
+    path = os.path.join(args.out, f"{args.workload}_n{args.n}_kernels.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    print(path)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("summarize")
+    s.add_argument("--workload", required=True)
+    s.add_argument("--n", type=int, required=True)
+    s.add_argument("--trace", required=True)
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--sq", default=None)
+    s.add_argument("--copy-mib", type=int, default=256)
+    s.add_argument("--cmd-trace", default="")
+    s.add_argument("--cmd-fetch", default="")
+    s.add_argument("--cmd-write", default="")
+    s.add_argument("--cmd-sq", default="")
+    s.add_argument("--out", default=os.path.join(os.path.dirname(HERE), "profiles"))
+    a = ap.parse_args(argv)
+    if a.cmd == "summarize":
+        summarize(a)
+
+
+if __name__ == "__main__":
+    main()

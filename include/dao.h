@@ -87,8 +87,9 @@ typedef struct {
   int64_t max_steps; /* cap on attempted steps per trajectory, >= 1                     */
 } dao_tol;
 
-/* Step record (Sec. 3.1, Fig. 2): host struct of caller-owned device arrays.
- * Rows past count[k] are never read.                                       */
+/* Step record (Sec. 3, Fig. 2): host struct of caller-owned device arrays.
+ * Rows past count[k] are never read, and after dao_solve they hold
+ * unspecified values (a rejected attempt may write the next row).           */
 typedef struct {
   int64_t s_cap;   /* rows per trajectory (capacity), >= 0                       */
   void* t;         /* real[n][s_cap]: start time of each accepted step; may be NULL */
@@ -109,14 +110,16 @@ size_t dao_solve_workspace_size(dao_system sys, dao_method method, dao_dtype dty
  * dao_solve -- adaptive solve of n independent trajectories on [t0, t1]
  * (Sec. 2.1): per trajectory, FSAL Tsit5 or Rosenbrock23 trial steps, RMS
  * acceptance test, integral step-size controller, last step clipped to t1.
- * Writes y1[d][n] (NaN where status != DAO_TRAJ_OK) and, when rec != NULL,
- * the record of accepted steps (Sec. 3.1).  rec == NULL runs the same solve
- * without writing a record.
+ * Writes y1[d][n] (NaN where status != DAO_TRAJ_OK) and the record of
+ * accepted steps (Sec. 3, Fig. 2): rec->h (and rec->t if not NULL) rows,
+ * rec->count, rec->nrej (if not NULL) and rec->status.
  *   theta    real[p][n] (or real[4740] for DAO_SYS_MLP), y0 real[d][n]
  *   t0 <= t1, both finite; tol as above
- *   workspace >= dao_solve_workspace_size() device bytes (work-queue counter)
+ *   rec      required; rec->h may be NULL only when rec->s_cap == 0
+ *   workspace >= dao_solve_workspace_size() device bytes (work-queue
+ *            counter and trash slots); its contents need no initialisation
  * Errors: DAO_EINVAL (NULL array with n > 0, t1 < t0, bad tolerances,
- * rec->s_cap < 0), DAO_EUNSUPPORTED, DAO_EWORKSPACE, DAO_EDEVICE.
+ * rec NULL, rec->s_cap < 0), DAO_EUNSUPPORTED, DAO_EWORKSPACE, DAO_EDEVICE.
  */
 dao_status dao_solve(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
                      const void* theta, const void* y0, double t0, double t1,
