@@ -209,6 +209,25 @@ size_t grad_header_bytes(int64_t n, int64_t s_max) {
   return align_up(16) + align_up((size_t)ORDER_BINS * 4) + align_up((size_t)(n > 0 ? n : 1) * 4);
 }
 
+// Orders trajectories by decreasing step count into perm and clears the
+// group counter of the gradient's work queue.
+void launch_order(const int32_t* count, int64_t n, int64_t s_max, uint32_t* hist, int32_t* perm,
+                  unsigned long long* groups, hipStream_t stream) {
+  int shift = 0;
+  while (((s_max + 1) >> shift) + 1 > ORDER_BINS) ++shift;
+  const int nb = (int)(((s_max + 1) >> shift) + 1);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream,
+                     hist, (int64_t)nb, 0u);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)groups, (int64_t)2, 0u);
+  int64_t oblk = (n + 255) / 256;
+  if (oblk > 1024) oblk = 1024;
+  hipLaunchKernelGGL(order_hist_kernel, dim3((unsigned)oblk), dim3(256), 0, stream, count, n,
+                     s_max, shift, nb, hist);
+  hipLaunchKernelGGL(scan_buckets_kernel, dim3(1), dim3(1024), 0, stream, hist, (int64_t)nb);
+  hipLaunchKernelGGL(order_scatter_kernel, dim3((unsigned)oblk), dim3(256), 0, stream, count, n,
+                     s_max, shift, nb, hist, perm);
+}
+
 template <class R, class Sys, int M>
 dao_status launch_grad(int64_t n, const void* theta, const void* y0, const dao_record* rec,
                        int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0, void* ws,
@@ -232,19 +251,7 @@ dao_status launch_grad(int64_t n, const void* theta, const void* y0, const dao_r
   if (blocks > slots / waves_per_block) blocks = slots / waves_per_block;
   if (blocks < 1) return fail(DAO_EWORKSPACE, "dao_grad: workspace too small");
 
-  int shift = 0;
-  while (((s_max + 1) >> shift) + 1 > ORDER_BINS) ++shift;
-  const int nb = (int)(((s_max + 1) >> shift) + 1);
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream,
-                     hist, (int64_t)nb, 0u);
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)groups, (int64_t)2, 0u);
-  int64_t oblk = (n + 255) / 256;
-  if (oblk > 1024) oblk = 1024;
-  hipLaunchKernelGGL(order_hist_kernel, dim3((unsigned)oblk), dim3(256), 0, stream, rec->count, n,
-                     s_max, shift, nb, hist);
-  hipLaunchKernelGGL(scan_buckets_kernel, dim3(1), dim3(1024), 0, stream, hist, (int64_t)nb);
-  hipLaunchKernelGGL(order_scatter_kernel, dim3((unsigned)oblk), dim3(256), 0, stream, rec->count,
-                     n, s_max, shift, nb, hist, perm);
+  launch_order(rec->count, n, s_max, hist, perm, groups, stream);
 
   GradArgs<R> a;
   a.n = n;
@@ -263,6 +270,95 @@ dao_status launch_grad(int64_t n, const void* theta, const void* y0, const dao_r
   a.groups = groups;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), 0, stream, a);
   return check_hip(hipGetLastError(), "grad kernel launch");
+}
+
+// ------------------------------------------------- neural right-hand side
+dao_status launch_mlp_solve(int64_t n, const void* theta, const void* y0, double t0, double t1,
+                            const dao_tol* tol, void* y1, const dao_record* rec, void* ws,
+                            hipStream_t stream) {
+  mlp::SolveArgs a;
+  a.n = n;
+  a.theta = (const float*)theta;
+  a.y0 = (const float*)y0;
+  a.t0 = (float)t0;
+  a.t1 = (float)t1;
+  a.rtol = (float)tol->rtol;
+  a.atol = (float)tol->atol;
+  a.dt0 = (float)tol->dt0;
+  a.max_steps = tol->max_steps;
+  a.y1 = (float*)y1;
+  a.s_cap = rec->s_cap;
+  a.t_rec = (float*)rec->t;
+  a.h_rec = (float*)rec->h;
+  a.count = rec->count;
+  a.nrej = rec->nrej;
+  a.status = rec->status;
+  a.queue = (unsigned long long*)ws;
+  a.trash = (float*)((char*)ws + ALIGN);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)ws, (int64_t)2, 0u);
+  const int64_t groups = (n + mlp::SLOTS - 1) / mlp::SLOTS;
+  int64_t blocks = (groups + BLOCK / WAVE - 1) / (BLOCK / WAVE);
+  const int64_t res = resident_blocks(mlp::solve_kernel);
+  if (blocks > res) blocks = res;
+  hipLaunchKernelGGL(mlp::solve_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, stream, a);
+  return check_hip(hipGetLastError(), "mlp solve kernel launch");
+}
+
+// Per-wavefront workspace of the neural gradient: the state tile
+// [s_max][64] and the partial weight gradient [4740], both float.
+size_t mlp_slot_bytes(int64_t s_max) {
+  return align_up((size_t)(s_max > 0 ? s_max : 1) * WAVE * sizeof(float)) +
+         align_up((size_t)mlp::NP * sizeof(float));
+}
+
+dao_status launch_mlp_grad(int64_t n, const void* theta, const void* y0, const dao_record* rec,
+                           int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  char* base = (char*)ws;
+  unsigned long long* groups = (unsigned long long*)base;
+  uint32_t* hist = (uint32_t*)(base + align_up(16));
+  int32_t* perm = (int32_t*)(base + align_up(16) + align_up((size_t)ORDER_BINS * 4));
+  const size_t hdr = grad_header_bytes(n, s_max);
+  const size_t slot = mlp_slot_bytes(s_max);
+  const int64_t slots = (int64_t)((ws_bytes - hdr) / slot);
+  const int64_t ngroups = (n + mlp::SLOTS - 1) / mlp::SLOTS;
+  const int64_t waves_per_block = BLOCK / WAVE;
+  int64_t blocks = (ngroups + waves_per_block - 1) / waves_per_block;
+  const int64_t res = resident_blocks(mlp::grad_kernel);
+  if (blocks > res) blocks = res;
+  if (blocks > slots / waves_per_block) blocks = slots / waves_per_block;
+  if (blocks < 1) return fail(DAO_EWORKSPACE, "dao_grad: workspace too small");
+  const int64_t nw = blocks * waves_per_block;
+  float* scratch = (float*)(base + hdr);
+  float* partial = (float*)(base + hdr + (size_t)nw * align_up((size_t)(s_max > 0 ? s_max : 1) *
+                                                                WAVE * sizeof(float)));
+
+  launch_order(rec->count, n, s_max, hist, perm, groups, stream);
+
+  mlp::GradArgs a;
+  a.n = n;
+  a.theta = (const float*)theta;
+  a.y0 = (const float*)y0;
+  a.s_cap = rec->s_cap;
+  a.h_rec = (const float*)rec->h;
+  a.count = rec->count;
+  a.status = rec->status;
+  a.s_max = s_max;
+  a.dLdy1 = (const float*)dLdy1;
+  a.dLdy0 = (float*)dLdy0;
+  a.scratch = scratch;
+  a.partial = partial;
+  a.perm = perm;
+  a.groups = groups;
+  hipLaunchKernelGGL(mlp::grad_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, stream, a);
+  dao_status st = check_hip(hipGetLastError(), "mlp grad kernel launch");
+  if (st != DAO_OK) return st;
+  if (dLdtheta) {
+    hipLaunchKernelGGL(mlp::reduce_kernel, dim3((mlp::NP + 255) / 256), dim3(256), 0, stream,
+                       (const float*)partial, nw, (float*)dLdtheta);
+    st = check_hip(hipGetLastError(), "mlp reduce kernel launch");
+  }
+  return st;
 }
 
 // Dispatch table over (system, method, dtype).
@@ -296,12 +392,15 @@ struct Impl {
   grad_fn grad;
   slot_fn slot;
   res_fn resident;
+  int group;  // trajectories per wavefront in the gradient
 };
+
+int64_t mlp_resident_waves() { return resident_blocks(mlp::grad_kernel) * (BLOCK / WAVE); }
 
 template <class R, template <class> class S, int M>
 Impl make_impl() {
   return Impl{&Entry<R, S, M>::solve, &Entry<R, S, M>::grad, &Entry<R, S, M>::slot_bytes,
-              &Entry<R, S, M>::resident_waves};
+              &Entry<R, S, M>::resident_waves, WAVE};
 }
 
 const Impl* find_impl(int sys, int method, int dtype) {
@@ -329,6 +428,8 @@ const Impl* find_impl(int sys, int method, int dtype) {
     table[DAO_SYS_ROBERTSON][M_ROS23][DAO_F32] = make_impl<float, Robertson, M_ROS23>();
     table[DAO_SYS_LOGHALO][M_TSIT5][DAO_F64] = make_impl<double, LogHalo, M_TSIT5>();
     table[DAO_SYS_LOGHALO][M_TSIT5][DAO_F32] = make_impl<float, LogHalo, M_TSIT5>();
+    table[DAO_SYS_MLP][M_TSIT5][DAO_F32] =
+        Impl{&launch_mlp_solve, &launch_mlp_grad, &mlp_slot_bytes, &mlp_resident_waves, mlp::SLOTS};
     init = true;
   }
   if (!sys_ok(sys) || method < 0 || method > 1 || dtype < 0 || dtype > 1) return nullptr;
@@ -411,7 +512,7 @@ size_t dao_grad_workspace_size(dao_system sys, dao_method method, dao_dtype dtyp
                                int64_t s_max) {
   const Impl* im = find_impl(sys, method, dtype);
   if (!im || n < 0 || s_max < 0) return 0;
-  int64_t waves = (n + WAVE - 1) / WAVE;
+  int64_t waves = (n + im->group - 1) / im->group;
   waves = (waves + BLOCK / WAVE - 1) / (BLOCK / WAVE) * (BLOCK / WAVE);
   const int64_t res = im->resident();
   if (waves > res) waves = res;

@@ -17,6 +17,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "mlp.hpp"
 #include "ros23.hpp"
 #include "systems.hpp"
 #include "tsit5.hpp"
