@@ -23,14 +23,41 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# Algorithmic fp64 flops (fma = 2, add/mul/div/sqrt/pow = 1, compare/abs/neg = 0)
-#   per attempted Tsit5 step and per replayed+reversed gradient step.  Derived
-#   operation by operation in DESIGN.md ("Algorithmic work").
-FLOPS = {
-    # system: (flops per solve attempt, flops per gradient step)
-    "lorenz63": (255, 606),
+# Algorithmic work (flop convention: fma = 2; add, sub, mul, div, sqrt, tanh and
+# the controller power = 1; compare, abs, negate, select = 0).
+#   init  : f(y0) and the starting step, once per trajectory
+#   att   : one attempted step (trial stages, error estimate, test, controller);
+#           an accepted step adds one flop (the time update)
+#   replay: one replay step (no error estimate), as the gradient's forward pass
+# These three are the operation tallies of the oracle's counting scalar on the
+# same arithmetic (pinned by tests/test_flop_counts.py).
+#   grad  : one accepted step of the gradient = forward replay + recomputed
+#           stages + reverse sweep.  Tsit5 (d states, six stage VJPs of V flops
+#           each): replay + (replay - 13 d) + 21 + 42 d + 6 V.  Rosenbrock23:
+#           replay + (replay - 3 d) + 144 (two transposed solves, two field
+#           VJPs, the Jacobian cotangent and its second-derivative pull-back).
+#   V per field VJP: Lotka-Volterra 21, Lorenz 19, log halo 41; neural field
+#   18954 (W3^T v, W2^T dz2, W1^T dz1, the three weight outer products and the
+#   bias sums, tanh derivatives).
+def _tsit5_grad(replay, d, v):
+    return replay + (replay - 13 * d) + 21 + 42 * d + 6 * v
+
+
+WORKLOADS = {
+    # name: s_cap, keep t record, flops dict, peak (flop/s), bound, cpu sample size
+    "lotka_volterra": dict(s_cap=256, with_t=True, init=50, att=175, replay=132,
+                           grad=_tsit5_grad(132, 2, 21), peak=78.6e12, bound="alu", cpu_n=256),
+    "lorenz63": dict(s_cap=1024, with_t=True, init=68, att=254, replay=192,
+                     grad=_tsit5_grad(192, 3, 19), peak=78.6e12, bound="alu", cpu_n=65536),
+    "mlp": dict(s_cap=64, with_t=True, init=18754, att=56337, replay=56256,
+                grad=_tsit5_grad(56256, 4, 18954), peak=157.3e12, bound="mfma", cpu_n=1024),
+    "robertson": dict(s_cap=1024, with_t=True, init=68, att=168, replay=102,
+                      grad=102 + (102 - 9) + 144, peak=78.6e12, bound="alu", cpu_n=8192),
+    "loghalo": dict(s_cap=8192, with_t=False, init=124, att=497, replay=378,
+                    grad=_tsit5_grad(378, 6, 41), peak=78.6e12, bound="alu", cpu_n=2048),
 }
-PEAK_FP64_VALU = 78.6e12  # 256 CU x 4 SIMD x 16 lanes x 2 flop (fma) x 2.4 GHz
+# MI355X published peaks: FP64 vector 78.6 TFLOP/s (256 CU x 4 SIMD x 16 lanes x
+# 2 flop x 2.4 GHz); FP32 matrix (MFMA) 157.3 TFLOP/s.
 
 
 def parse():
@@ -40,14 +67,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lorenz63")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=65536)
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="trajectories in the CPU-baseline sample (default per workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, copy one buffer of MIB MiB once (a plain copy "
                          "kernel of known size, the reference for HBM byte counters)")
     return ap.parse_args()
 
 
-def cpu_baseline(w, sample):
+def cpu_baseline(w, sample, s_cap):
     """The oracle, as is, on the host cores: solve + gradient of a sample."""
     import numpy as np
 
@@ -58,21 +86,24 @@ def cpu_baseline(w, sample):
     ws = di.subset(w, np.arange(min(sample, w.n)))
     t0 = time.perf_counter()
     r = oracle.solve(ws.system, ws.method, ws.theta, ws.y0, ws.t0, ws.t1, ws.rtol, ws.atol,
-                     s_cap=2048, nthreads=nthreads)
+                     s_cap=s_cap, dtype=ws.dtype, nthreads=nthreads)
     lam = di.cotangent(ws, r["y1"])
-    oracle.grad(ws.system, ws.method, ws.theta, ws.y0, r["count"], r["h"], lam, nthreads=nthreads)
+    oracle.grad(ws.system, ws.method, ws.theta.astype(np.float64), ws.y0.astype(np.float64),
+                r["count"], r["h"].astype(np.float64), lam, nthreads=nthreads)
     dt = time.perf_counter() - t0
     return {"value": ws.n / dt, "unit": "trajectories/s (solve + gradient)", "cores": nthreads,
             "kind": "oracle",
             "sample": f"first {ws.n} of the {w.n} {w.name} trajectories, full solve + tape "
-                      f"reverse-mode gradient, {dt:.2f} s wall on {nthreads} threads"}
+                      f"reverse-mode gradient ({ws.dtype} solve, f64 gradient), {dt:.2f} s wall "
+                      f"on {nthreads} threads"}
 
 
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; the ensemble would shard by "
-              "trajectory index across GPUs with no exchange (see DESIGN.md). Use --gpus 1.",
+              "trajectory index across GPUs, with no exchange for per-trajectory parameters "
+              "and one all-reduce of the shared weights otherwise. Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -85,25 +116,32 @@ def main():
 
     dev = torch.device("cuda:0")
     w = di.make(args.workload)
-    s_cap = {"lorenz63": 1024}[w.name]
+    cfg = WORKLOADS[w.name]
+    s_cap = cfg["s_cap"]
     th = torch.tensor(w.theta, device=dev)
     y0 = torch.tensor(w.y0, device=dev)
     tgt = torch.tensor(w.target, device=dev)
-    bufs = api.alloc_record(w.n, s_cap, w.dtype, dev, with_t=True)
+    bufs = api.alloc_record(w.n, s_cap, w.dtype, dev, with_t=cfg["with_t"])
+    # cotangent of the workload's loss: 1/2 |y - target|^2 (positions only for
+    # the orbits), or the mean square over the n x d entries (neural field)
+    d_used = 3 if w.loss == "half_sq_pos" else w.d
+    scale = 2.0 / (w.n * w.d) if w.loss == "mse" else 1.0
     y1 = torch.empty_like(y0)
     lam = torch.empty_like(y0)
     dth = torch.empty_like(th)
     dy0 = torch.empty_like(y0)
     wsp = api.Workspace()
 
+    s_max = [s_cap]
+
     def step(ev):
         ev[0].record()
         rec, _ = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=s_cap,
                            out=y1, rec_buffers=bufs, workspace=wsp)
         ev[1].record()
-        dao.cotangent(y1, tgt, 1.0, out=lam)
+        dao.cotangent(y1, tgt, scale, d_used=d_used, out=lam)
         ev[2].record()
-        dao.grad(rec, lam, s_max=s_cap, out_theta=dth, out_y0=dy0, workspace=wsp)
+        dao.grad(rec, lam, s_max=s_max[0], out_theta=dth, out_y0=dy0, workspace=wsp)
         ev[3].record()
         return rec
 
@@ -118,7 +156,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
+    # The record's longest row sizes the gradient's checkpoint scratch.  Every
+    # step solves the same inputs, so it is read once, after the first solve.
+    rec = step(events())
+    torch.cuda.synchronize()
+    s_max[0] = int(rec.count.max().item())
+    for _ in range(max(args.warmup - 1, 0)):
         rec = step(events())
     torch.cuda.synchronize()
 
@@ -135,14 +178,16 @@ def main():
     cnt = rec.count.cpu().numpy().astype(np.int64)
     nrej = rec.nrej.cpu().numpy().astype(np.int64)
     status = rec.status.cpu().numpy()
-    assert np.all(status == 0), "some trajectories failed"
+    if not np.all(status == 0):
+        bad = np.bincount(status, minlength=5)
+        raise SystemExit(f"bench: some trajectories failed (status counts {bad.tolist()})")
     attempts = int((cnt + nrej).sum())
     steps_total = int(cnt.sum())
     ms = wall / args.steps * 1e3
     ts, tg = float(np.mean(t_solve)), float(np.mean(t_grad))
-    f_att, f_step = FLOPS[w.name]
-    fl_solve = attempts * f_att
-    fl_grad = steps_total * f_step
+    fl_solve = w.n * cfg["init"] + attempts * cfg["att"] + steps_total
+    fl_grad = steps_total * cfg["grad"]
+    peak = cfg["peak"]
     dom = "grad" if tg >= ts else "solve"
     ach = (fl_grad / tg) if dom == "grad" else (fl_solve / ts)
     # Measured HBM bytes per launch of the dominant kernel (rocprofv3 FETCH_SIZE +
@@ -153,6 +198,7 @@ def main():
     traffic = None
     if tr is not None and f"{dom}_kernel" in tr["kernels"]:
         traffic = tr["kernels"][f"{dom}_kernel"]["hbm_bytes"]
+    dtype_name = {"f64": "f64", "f32": "f32"}[w.dtype]
     out = {
         "metric": "gradient trajectories/s (replay adjoint) + solves/s at 1 GPU; % of roofline",
         "value": w.n / (wall / args.steps),
@@ -164,7 +210,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64",
+        "dtype": dtype_name,
         "data": "synthetic",
         "config": {"workload": f"{w.name} ensemble", "n_trajectories": w.n, "method": w.method,
                    "t_span": [w.t0, w.t1], "rtol": w.rtol, "atol": w.atol, "s_cap": s_cap},
@@ -175,17 +221,16 @@ def main():
         "accepted_steps_mean": float(cnt.mean()),
         "accepted_steps_max": int(cnt.max()),
         "attempts_total": attempts,
-        "solve_fp64_tflops": fl_solve / ts * 1e-12,
-        "grad_fp64_tflops": fl_grad / tg * 1e-12,
-        "roofline": {"bound": "alu", "kernel": f"{dom}_kernel", "achieved": ach * 1e-12,
-                     "peak": PEAK_FP64_VALU * 1e-12, "unit": "TFLOP/s",
-                     "frac": ach / PEAK_FP64_VALU, "traffic": traffic,
-                     "traffic_unit": "HBM bytes per launch"},
-        "roofline_solve_frac": fl_solve / ts / PEAK_FP64_VALU,
-        "roofline_grad_frac": fl_grad / tg / PEAK_FP64_VALU,
+        "solve_tflops": fl_solve / ts * 1e-12,
+        "grad_tflops": fl_grad / tg * 1e-12,
+        "roofline": {"bound": cfg["bound"], "kernel": f"{dom}_kernel", "achieved": ach * 1e-12,
+                     "peak": peak * 1e-12, "unit": "TFLOP/s", "frac": ach / peak,
+                     "traffic": traffic, "traffic_unit": "HBM bytes per launch"},
+        "roofline_solve_frac": fl_solve / ts / peak,
+        "roofline_grad_frac": fl_grad / tg / peak,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample or cfg["cpu_n"], s_cap)
     print(json.dumps(out), flush=True)
 
 

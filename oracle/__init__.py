@@ -66,6 +66,9 @@ def lib():
         L.oracle_step_f64.argtypes = [I, I, P, P, D, P, P]
         L.oracle_rhs_f64.argtypes = [I, P, P, P]
         L.oracle_jac_f64.argtypes = [I, P, P, P]
+        L.oracle_count_solve.argtypes = [I, I, P, P, D, D, D, D, I64, P]
+        L.oracle_count_replay_step.argtypes = [I, I, P, P, D]
+        L.oracle_count_replay_step.restype = I64
         L.oracle_ctrl_root_f64.argtypes = [D, I]
         L.oracle_ctrl_root_f64.restype = D
         L.oracle_ctrl_root_f32.argtypes = [ctypes.c_float, I]
@@ -186,6 +189,25 @@ def step(system, method, theta, y, h):
                                _p(ynew), _p(err))
     assert rc == 0
     return ynew, err
+
+
+def count_solve(system, method, theta, y0, t0, t1, rtol, atol, s_cap=100000):
+    """Operation tally of one trajectory's solve: dict(total, init, attempts, accepted)."""
+    theta = np.ascontiguousarray(theta, dtype=np.float64)
+    y0 = np.ascontiguousarray(y0, dtype=np.float64)
+    out = np.zeros(4, np.int64)
+    rc = lib().oracle_count_solve(SYSTEMS[system], METHODS[method], _p(theta), _p(y0), float(t0),
+                                  float(t1), float(rtol), float(atol), int(s_cap), _p(out))
+    assert rc == 0, rc
+    return dict(total=int(out[0]), init=int(out[1]), attempts=int(out[2]), accepted=int(out[3]))
+
+
+def count_replay_step(system, method, theta, y, h):
+    """Operation tally of one replay step from y with step h."""
+    theta = np.ascontiguousarray(theta, dtype=np.float64)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    return int(lib().oracle_count_replay_step(SYSTEMS[system], METHODS[method], _p(theta), _p(y),
+                                              float(h)))
 
 
 def ctrl_root(x, q, dtype="f64"):

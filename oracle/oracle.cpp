@@ -130,6 +130,45 @@ inline Rev tanh_(Rev a) {
 }
 inline double rv(Rev a) { return a.v; }
 
+// Operation-counting scalar, used only to tally the arithmetic of a solve:
+// every +, -, *, / adds 1 to the thread's count, a fused multiply-add adds 2,
+// sqrt, tanh, pow and the controller power add 1; negation, abs, comparisons,
+// min/max and selects add 0.  Values are carried in binary64.
+thread_local int64_t g_flops = 0;
+struct Cnt {
+  double v;
+  Cnt() : v(0.0) {}
+  Cnt(double x) : v(x) {}  // NOLINT: constants promote implicitly
+};
+inline Cnt operator+(Cnt a, Cnt b) { ++g_flops; return Cnt(a.v + b.v); }
+inline Cnt operator-(Cnt a, Cnt b) { ++g_flops; return Cnt(a.v - b.v); }
+inline Cnt operator*(Cnt a, Cnt b) { ++g_flops; return Cnt(a.v * b.v); }
+inline Cnt operator/(Cnt a, Cnt b) { ++g_flops; return Cnt(a.v / b.v); }
+inline Cnt operator-(Cnt a) { return Cnt(-a.v); }
+inline bool operator<(Cnt a, Cnt b) { return a.v < b.v; }
+inline bool operator>(Cnt a, Cnt b) { return a.v > b.v; }
+inline bool operator<=(Cnt a, Cnt b) { return a.v <= b.v; }
+inline bool operator>=(Cnt a, Cnt b) { return a.v >= b.v; }
+inline bool operator==(Cnt a, Cnt b) { return a.v == b.v; }
+inline bool operator!=(Cnt a, Cnt b) { return a.v != b.v; }
+inline Cnt fma3(Cnt a, Cnt b, Cnt c) { g_flops += 2; return Cnt(std::fma(a.v, b.v, c.v)); }
+inline Cnt tanh_(Cnt a) { ++g_flops; return Cnt(std::tanh(a.v)); }
+inline double rv(Cnt a) { return a.v; }
+
+// Elementary functions with the scalar types of the solve.
+inline double abs_(double a) { return std::fabs(a); }
+inline float abs_(float a) { return std::fabs(a); }
+inline Cnt abs_(Cnt a) { return Cnt(std::fabs(a.v)); }
+inline double sqrt_(double a) { return std::sqrt(a); }
+inline float sqrt_(float a) { return std::sqrt(a); }
+inline Cnt sqrt_(Cnt a) { ++g_flops; return Cnt(std::sqrt(a.v)); }
+inline double pow_(double a, double b) { return std::pow(a, b); }
+inline float pow_(float a, float b) { return std::pow(a, b); }
+inline Cnt pow_(Cnt a, Cnt b) { ++g_flops; return Cnt(std::pow(a.v, b.v)); }
+inline bool finite_(double a) { return std::isfinite(a); }
+inline bool finite_(float a) { return std::isfinite(a); }
+inline bool finite_(Cnt a) { return std::isfinite(a.v); }
+
 // ----------------------------------------------------------------------------
 // Tsit5 pair (Tsitouras 2011, Table 1).  b equals the last row of A (FSAL:
 // the seventh stage is evaluated at y_new), b_7 = 0.  BT = b - bhat, the
@@ -433,6 +472,8 @@ inline float trunc_bits(float x) {  // keep 8 explicit mantissa bits
   return x;
 }
 
+inline Cnt trunc_bits(Cnt x) { return Cnt(trunc_bits(x.v)); }
+
 // Controller power x^(-1/q), q = 10 (Tsit5) or 6 (Rosenbrock23), for x > 0.
 // x is first clamped to a range outside which 0.9 x^(-1/q) lies beyond the
 // controller's limits [0.2, 10] anyway.  With x = m 2^e (m in [1, 2)) and
@@ -472,6 +513,12 @@ T ctrl_root(T x, int q) {
   return std::ldexp(p * c, -a);
 }
 
+// The controller power counts as one operation in the tally.
+inline Cnt ctrl_root(Cnt x, int q) {
+  ++g_flops;
+  return Cnt(ctrl_root<double>(x.v, q));
+}
+
 // Mean of squares of the scaled components, sum order c = 0..d-1; the mean
 // is the sum times the constant 1/d.
 template <class T>
@@ -490,18 +537,18 @@ template <class T>
 T initial_step(int sys, const T* th, int d, const T* y0, const T* f0, T span, T rtol, T atol,
                int order) {
   T sc[MAXD], y1[MAXD], f1[MAXD], df[MAXD];
-  for (int c = 0; c < d; ++c) sc[c] = fma3(rtol, std::fabs(y0[c]), atol);
-  T d0 = std::sqrt(mean_sq(d, y0, sc));
-  T d1 = std::sqrt(mean_sq(d, f0, sc));
+  for (int c = 0; c < d; ++c) sc[c] = fma3(rtol, abs_(y0[c]), atol);
+  T d0 = sqrt_(mean_sq(d, y0, sc));
+  T d1 = sqrt_(mean_sq(d, f0, sc));
   T h0 = (d0 < T(1e-5) || d1 < T(1e-5)) ? T(1e-6) : T(0.01) * (d0 / d1);
   h0 = std::min(h0, span);
   for (int c = 0; c < d; ++c) y1[c] = fma3(h0, f0[c], y0[c]);
   rhs(sys, th, y1, f1);
   for (int c = 0; c < d; ++c) df[c] = f1[c] - f0[c];
-  T d2 = std::sqrt(mean_sq(d, df, sc)) / h0;
+  T d2 = sqrt_(mean_sq(d, df, sc)) / h0;
   T m = std::max(d1, d2);
   T h1 = (m <= T(1e-15)) ? std::max(T(1e-6), h0 * T(1e-3))
-                         : T(std::pow(T(0.01) / m, T(1.0) / T(order)));
+                         : T(pow_(T(0.01) / m, T(1.0) / T(order)));
   return trunc_bits(std::min(T(100.0) * h0, h1));
 }
 
@@ -535,7 +582,7 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
       ++attempts;
       bool last = (t + h >= t1);
       T hs = last ? (t1 - t) : h;
-      if (!std::isfinite(hs)) { out.status = ST_NONFINITE; break; }
+      if (!finite_(hs)) { out.status = ST_NONFINITE; break; }
       if (!(t + hs > t)) { out.status = ST_DTMIN; break; }
       if (method == M_TSIT5) {
         tsit5_step(sys, th, d, y, hs, k, ynew, e);
@@ -543,9 +590,9 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
         ros23_step(sys, th, d, y, hs, k[0], ynew, F2, e);
       }
       for (int c = 0; c < d; ++c)
-        sc[c] = fma3(rtol, std::max(std::fabs(y[c]), std::fabs(ynew[c])), atol);
+        sc[c] = fma3(rtol, std::max(abs_(y[c]), abs_(ynew[c])), atol);
       T msq = mean_sq(d, e, sc);
-      if (!std::isfinite(msq)) { out.status = ST_NONFINITE; break; }
+      if (!finite_(msq)) { out.status = ST_NONFINITE; break; }
       if (msq <= T(1.0)) {
         if (n >= s_cap) { out.status = ST_CAPACITY; break; }
         if (t_rec) t_rec[n] = t;
@@ -829,6 +876,47 @@ int oracle_step_f64(int sys, int method, const double* th, const double* y, doub
   else
     ros23_step(sys, th, d, y, h, k[0], ynew, F2, err);
   return 0;
+}
+
+// Tally of the arithmetic of one trajectory's solve (counting scalar):
+// out[0] = total operations, out[1] = operations before the first attempt
+// (f(y0) and the starting step), out[2] = attempts, out[3] = accepted steps.
+int oracle_count_solve(int sys, int method, const double* theta, const double* y0, double t0,
+                       double t1, double rtol, double atol, int64_t s_cap, int64_t* out) {
+  if (!valid_sys(sys, method) || !(t1 > t0)) return 1;
+  const int d = SYS_D[sys], p = SYS_P[sys];
+  std::vector<Cnt> th(p), hr(s_cap), tr(s_cap);
+  Cnt y[MAXD], f0[MAXD], y1[MAXD];
+  for (int i = 0; i < p; ++i) th[i] = Cnt(theta[i]);
+  for (int c = 0; c < d; ++c) y[c] = Cnt(y0[c]);
+  g_flops = 0;
+  rhs(sys, th.data(), y, f0);
+  initial_step(sys, th.data(), d, y, f0, Cnt(t1 - t0), Cnt(rtol), Cnt(atol),
+               method == M_TSIT5 ? 5 : 2);
+  out[1] = g_flops;
+  g_flops = 0;
+  SolveOut<Cnt> o = solve_one<Cnt>(sys, method, th.data(), y, Cnt(t0), Cnt(t1), Cnt(rtol),
+                                   Cnt(atol), Cnt(0.0), 100000, s_cap, y1, tr.data(), hr.data());
+  out[0] = g_flops;
+  out[2] = (int64_t)o.count + o.nrej;
+  out[3] = o.count;
+  return o.status == ST_OK ? 0 : 2;
+}
+
+// Tally of one replay step (Tsit5: six field evaluations and the stage sums;
+// Rosenbrock23: Jacobian, factorisation, two solves, two field evaluations).
+int64_t oracle_count_replay_step(int sys, int method, const double* theta, const double* y0,
+                                 double h) {
+  if (!valid_sys(sys, method)) return -1;
+  const int d = SYS_D[sys], p = SYS_P[sys];
+  std::vector<Cnt> th(p);
+  Cnt y[MAXD], yS[MAXD];
+  for (int i = 0; i < p; ++i) th[i] = Cnt(theta[i]);
+  for (int c = 0; c < d; ++c) y[c] = Cnt(y0[c]);
+  const double hh[1] = {h};
+  g_flops = 0;
+  replay_one<Cnt>(sys, method, th.data(), y, 1, hh, yS);
+  return g_flops;
 }
 
 // The controller power x^(-1/q) of the solve (for tests of its accuracy).
