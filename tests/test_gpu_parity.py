@@ -346,3 +346,39 @@ def test_mlp_empty_and_single(dao):
     ref = oracle.solve(w.system, w.method, w.theta.astype(np.float64), w.y0.astype(np.float64),
                        w.t0, w.t1, w.rtol, w.atol, s_cap=256, dtype="f64")
     assert rel_err(y1.cpu().numpy(), ref["y1"]).max() <= TOL32_Y
+
+
+@pytest.mark.parametrize("name,s_cap,record_t", [("robertson", 1024, True), ("loghalo", 8192, False)])
+def test_full_size_sampled(dao, name, s_cap, record_t):
+    # The benchmark ensembles at full size (262,144 stiff Robertson
+    # trajectories; 1,048,576 orbits) in the benchmark's launch configuration;
+    # a seeded sample, plus the longest and shortest records, against the
+    # oracle: equal accepted-step counts, final states and gradients within
+    # the fp64 bar.
+    w = di.make(name)
+    print(f"[full size] {name} n={w.n}", flush=True)
+    rec, y1 = gpu_solve(dao, w, s_cap, record_t=record_t)
+    st = rec.status.cpu().numpy()
+    assert np.all(st == 0), np.bincount(st)
+    cnt = rec.count.cpu().numpy()
+    y1n = y1.cpu().numpy()
+    lam_all = torch.tensor(di.cotangent(w, y1n), device=DEV)
+    dth, dy0 = dao.grad(rec, lam_all, s_max=int(cnt.max()))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    idx = np.unique(np.concatenate([rng.choice(w.n, 96, replace=False), [0, w.n - 1],
+                                    [np.argmax(cnt), np.argmin(cnt)]]))
+    ws = di.subset(w, idx)
+    ref = oracle_solve(ws, s_cap)
+    assert np.array_equal(cnt[idx], ref["count"])
+    assert rel_err(y1n[:, idx], ref["y1"]).max() <= TOL
+    lam = lam_all.cpu().numpy()[:, idx]
+    dth_o, dy0_o, _ = oracle.grad(ws.system, ws.method, ws.theta, ws.y0, ref["count"], ref["h"],
+                                  lam, nthreads=8)
+    g = dth.cpu().numpy()[:, idx]
+    if name == "robertson":
+        e = rel_err(g * ws.theta, dth_o * ws.theta)
+    else:
+        e = rel_err(g, dth_o)
+    assert e.max() <= TOL, e.max()
+    assert rel_err(dy0.cpu().numpy()[:, idx], dy0_o).max() <= TOL
