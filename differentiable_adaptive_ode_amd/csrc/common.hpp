@@ -21,6 +21,7 @@ enum : int32_t {
 };
 
 constexpr int WAVE = 64;
+constexpr int BLOCK_WAVES = 4;  // wavefronts per workgroup of the per-lane kernels
 
 __device__ __forceinline__ double fmaR(double a, double b, double c) { return __builtin_fma(a, b, c); }
 __device__ __forceinline__ float fmaR(float a, float b, float c) { return __builtin_fmaf(a, b, c); }

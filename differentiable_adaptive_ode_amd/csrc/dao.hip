@@ -152,7 +152,7 @@ DevInfo dev_info() {
   return cache[dev];
 }
 
-constexpr int BLOCK = 256;
+constexpr int BLOCK = BLOCK_WAVES * WAVE;
 constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 

@@ -128,12 +128,34 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   R* hrow = nullptr;
   R* trow = nullptr;
 
+  // Record staging.  A lane keeps its last STAGE (t, h) entries in an LDS
+  // ring (slot-major, lane-minor) and writes them out as one aligned
+  // 64-byte chunk per array whenever its count reaches a multiple of STAGE,
+  // so the record reaches memory in whole chunks instead of 8-byte pieces
+  // scattered over 64 rows.  A trajectory's last partial chunk is written
+  // entry by entry when it finishes.  Records whose capacity is not a
+  // multiple of STAGE are written directly.
+  constexpr int STAGE = 8;
+  __shared__ R ring[BLOCK_WAVES][2][STAGE][WAVE];
+  R(*const hring)[WAVE] = ring[threadIdx.x / WAVE][0];
+  R(*const tring)[WAVE] = ring[threadIdx.x / WAVE][1];
+  const bool staged = (a.s_cap % STAGE) == 0 && ((uintptr_t)a.h_rec % 16) == 0 &&
+                      ((uintptr_t)a.t_rec % 16) == 0;
+  const bool with_t = a.t_rec != nullptr;
+
   auto finish = [&](int32_t st) {
 #pragma unroll
     for (int c = 0; c < D; ++c) a.y1[c * a.n + traj] = (st == TRAJ_OK) ? y[c] : nanR(R(0));
     a.count[traj] = nacc;
     if (a.nrej) a.nrej[traj] = nrej;
     a.status[traj] = st;
+    if (staged) {
+      const int32_t lo = nacc & ~(STAGE - 1);
+      for (int32_t r = lo; r < nacc; ++r) {
+        hrow[r] = hring[r & (STAGE - 1)][lane];
+        if (with_t) trow[r] = tring[r & (STAGE - 1)][lane];
+      }
+    }
     traj = -1;
   };
 
@@ -219,10 +241,15 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
 
     // Record row nacc: an accepted step keeps it, a rejected one is
     // overwritten by the next accepted step (rows past count are unused).
-    // With the record full, the store goes to the lane's trash slot.
-    const bool room = nacc < a.s_cap;
-    *(room ? hrow + nacc : trash) = hs;
-    if (a.t_rec) *(room ? trow + nacc : trash + 1) = t;
+    if (staged) {
+      hring[nacc & (STAGE - 1)][lane] = hs;
+      if (with_t) tring[nacc & (STAGE - 1)][lane] = t;
+    } else {
+      // With the record full, the store goes to the lane's trash slot.
+      const bool room = nacc < a.s_cap;
+      *(room ? hrow + nacc : trash) = hs;
+      if (with_t) *(room ? trow + nacc : trash + 1) = t;
+    }
 
     const bool take = (st == RUNNING) && acc;
     const R tn = last ? a.t1 : t + hs;
@@ -238,6 +265,16 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     t = take ? tn : t;
     nacc += take ? 1 : 0;
     nrej += (st == RUNNING && !acc) ? 1 : 0;
+    if (staged && take && (nacc & (STAGE - 1)) == 0) {
+      // A full chunk: rows [nacc - STAGE, nacc), 64-byte aligned.
+      const int32_t lo = nacc - STAGE;
+#pragma unroll
+      for (int r = 0; r < STAGE; r += 2) {
+        typedef R R2 __attribute__((ext_vector_type(2)));
+        *(R2*)(hrow + lo + r) = R2{hring[r][lane], hring[r + 1][lane]};
+        if (with_t) *(R2*)(trow + lo + r) = R2{tring[r][lane], tring[r + 1][lane]};
+      }
+    }
     R fa = (fmin < R(10)) ? fmin : R(10);
     fa = (prev_rej && fa > R(1)) ? R(1) : fa;
     h = hs * (acc ? fa : fmin);
