@@ -51,8 +51,8 @@ WORKLOADS = {
                      grad=_tsit5_grad(192, 3, 19), peak=78.6e12, bound="alu", cpu_n=65536),
     "mlp": dict(s_cap=64, with_t=True, init=18754, att=56337, replay=56256,
                 grad=_tsit5_grad(56256, 4, 18954), peak=157.3e12, bound="mfma", cpu_n=1024),
-    "robertson": dict(s_cap=1024, with_t=True, init=68, att=168, replay=102,
-                      grad=102 + (102 - 9) + 144, peak=78.6e12, bound="alu", cpu_n=8192),
+    "robertson": dict(s_cap=1024, with_t=True, init=68, att=171, replay=105,
+                      grad=105 + (105 - 9) + 144, peak=78.6e12, bound="alu", cpu_n=8192),
     "loghalo": dict(s_cap=8192, with_t=False, init=124, att=497, replay=378,
                     grad=_tsit5_grad(378, 6, 41), peak=78.6e12, bound="alu", cpu_n=2048),
 }

@@ -14,9 +14,10 @@
 //   err = h/6 (k1 - 2 k2 + k3)
 //
 // W is factored per lane as P W = L U with partial pivoting (first row of
-// largest magnitude).  The pivot index is data dependent, so rows are
-// exchanged with selects on compile-time indices to keep every value in a
-// register.
+// largest magnitude); the reciprocal pivots are formed once per
+// factorisation and the elimination and every solve multiply by them.  The
+// pivot index is data dependent, so rows are exchanged with selects on
+// compile-time indices to keep every value in a register.
 #pragma once
 
 #include "common.hpp"
@@ -30,6 +31,7 @@ __device__ constexpr double E32 = 7.4142135623730951;     // 6 + sqrt 2
 template <class R, int D>
 struct LU {
   R m[D][D];   // unit-lower L below the diagonal, U on and above
+  R rp[D];     // reciprocal pivots 1 / u_kk (elimination and solves multiply by them)
   int piv[D];  // row exchanged with row k at elimination step k
 };
 
@@ -55,9 +57,10 @@ __device__ __forceinline__ void factor(LU<R, D>& f) {
         f.m[i][j] = sw ? rk : ri;
       }
     }
+    f.rp[k] = R(1) / f.m[k][k];
 #pragma unroll
     for (int i = k + 1; i < D; ++i) {
-      R l = f.m[i][k] / f.m[k][k];
+      R l = f.m[i][k] * f.rp[k];
       f.m[i][k] = l;
 #pragma unroll
       for (int j = k + 1; j < D; ++j) f.m[i][j] = fmaR(-l, f.m[k][j], f.m[i][j]);
@@ -92,7 +95,7 @@ __device__ __forceinline__ void solve(const LU<R, D>& f, const R (&b)[D], R (&x)
 #pragma unroll
     for (int j = 0; j < D; ++j)
       if (j > i) acc = fmaR(-f.m[i][j], x[j], acc);
-    x[i] = acc / f.m[i][i];
+    x[i] = acc * f.rp[i];
   }
 }
 
@@ -106,7 +109,7 @@ __device__ __forceinline__ void solve_t(const LU<R, D>& f, const R (&b)[D], R (&
 #pragma unroll
     for (int j = 0; j < D; ++j)
       if (j < i) acc = fmaR(-f.m[j][i], z[j], acc);
-    z[i] = acc / f.m[i][i];
+    z[i] = acc * f.rp[i];
   }
 #pragma unroll
   for (int i = D - 1; i >= 0; --i) {

@@ -384,9 +384,11 @@ void tsit5_step(int sys, const T* th, int d, const T* y, T h, T k[7][MAXD], T* y
 // ----------------------------------------------------------------------------
 // Dense LU with partial pivoting (first row of largest magnitude) and the
 // solve with its factors.  Used for the Rosenbrock matrix W = I - h d J.
+// The reciprocal of each pivot is formed once (rp[k] = 1 / u_kk) and the
+// elimination and the solves multiply by it.
 // ----------------------------------------------------------------------------
 template <class T>
-void lu_factor(int d, T* A, int* piv) {
+void lu_factor(int d, T* A, int* piv, T* rp) {
   for (int k = 0; k < d; ++k) {
     int p = k;
     double best = std::fabs(rv(A[k * d + k]));
@@ -397,15 +399,16 @@ void lu_factor(int d, T* A, int* piv) {
     piv[k] = p;
     if (p != k)
       for (int j = 0; j < d; ++j) std::swap(A[k * d + j], A[p * d + j]);
+    rp[k] = T(1.0) / A[k * d + k];
     for (int i = k + 1; i < d; ++i) {
-      T l = A[i * d + k] / A[k * d + k];
+      T l = A[i * d + k] * rp[k];
       A[i * d + k] = l;
       for (int j = k + 1; j < d; ++j) A[i * d + j] = fma3(-l, A[k * d + j], A[i * d + j]);
     }
   }
 }
 template <class T>
-void lu_solve(int d, const T* LU, const int* piv, const T* b, T* x) {
+void lu_solve(int d, const T* LU, const int* piv, const T* rp, const T* b, T* x) {
   T z[MAXD];
   for (int i = 0; i < d; ++i) z[i] = b[i];
   for (int k = 0; k < d; ++k)
@@ -415,7 +418,7 @@ void lu_solve(int d, const T* LU, const int* piv, const T* b, T* x) {
   for (int i = d - 1; i >= 0; --i) {
     T acc = z[i];
     for (int j = i + 1; j < d; ++j) acc = fma3(-LU[i * d + j], x[j], acc);
-    x[i] = acc / LU[i * d + i];
+    x[i] = acc * rp[i];
   }
 }
 
@@ -426,20 +429,20 @@ void lu_solve(int d, const T* LU, const int* piv, const T* b, T* x) {
 // ----------------------------------------------------------------------------
 template <class T>
 void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* ynew, T* F2, T* err) {
-  T J[MAXD * MAXD], W[MAXD * MAXD];
+  T J[MAXD * MAXD], W[MAXD * MAXD], rp[MAXD];
   int piv[MAXD];
   jac(sys, th, y, J);
   T hd = h * T(R23_D);
   for (int i = 0; i < d; ++i)
     for (int j = 0; j < d; ++j) W[i * d + j] = fma3(-hd, J[i * d + j], T(i == j ? 1.0 : 0.0));
-  lu_factor(d, W, piv);
+  lu_factor(d, W, piv, rp);
   T k1[MAXD], k2[MAXD], Y1[MAXD], F1[MAXD], r[MAXD], u[MAXD];
-  lu_solve(d, W, piv, F0, k1);
+  lu_solve(d, W, piv, rp, F0, k1);
   T hh = T(0.5) * h;
   for (int c = 0; c < d; ++c) Y1[c] = fma3(hh, k1[c], y[c]);
   rhs(sys, th, Y1, F1);
   for (int c = 0; c < d; ++c) r[c] = F1[c] - k1[c];
-  lu_solve(d, W, piv, r, u);
+  lu_solve(d, W, piv, rp, r, u);
   for (int c = 0; c < d; ++c) k2[c] = u[c] + k1[c];
   for (int c = 0; c < d; ++c) ynew[c] = fma3(h, k2[c], y[c]);
   if (err == nullptr) return;
@@ -449,7 +452,7 @@ void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* yn
     T t2 = fma3(T(-R23_E32), k2[c] - F1[c], F2[c]);
     r[c] = fma3(T(-2.0), k1[c] - F0[c], t2);
   }
-  lu_solve(d, W, piv, r, k3);
+  lu_solve(d, W, piv, rp, r, k3);
   T h6 = h / T(6.0);
   for (int c = 0; c < d; ++c) err[c] = h6 * (fma3(T(-2.0), k2[c], k1[c]) + k3[c]);
 }
