@@ -354,6 +354,9 @@ dao_status launch_mlp_grad(int64_t n, const void* theta, const void* y0, const d
   dao_status st = check_hip(hipGetLastError(), "mlp grad kernel launch");
   if (st != DAO_OK) return st;
   if (dLdtheta) {
+    const int64_t nchunks = (nw + mlp::REDUCE_CHUNK - 1) / mlp::REDUCE_CHUNK;
+    hipLaunchKernelGGL(mlp::reduce_chunks_kernel, dim3((mlp::NP + 255) / 256, (unsigned)nchunks),
+                       dim3(256), 0, stream, partial, nw);
     hipLaunchKernelGGL(mlp::reduce_kernel, dim3((mlp::NP + 255) / 256), dim3(256), 0, stream,
                        (const float*)partial, nw, (float*)dLdtheta);
     st = check_hip(hipGetLastError(), "mlp reduce kernel launch");

@@ -98,7 +98,21 @@ struct Bwd {
   }
 };
 
-__device__ __forceinline__ float tanh_(float x) { return tanhf(x); }
+// tanh in binary32: for |x| < 1/4 the odd Taylor polynomial to x^9 (relative
+// truncation error below 4e-8 there), otherwise 1 - 2 / (exp(2|x|) + 1) with
+// the hardware base-2 exponential and reciprocal (absolute error ~2e-7);
+// sign restored at the end.  Large |x| saturate to +-1.
+__device__ __forceinline__ float tanh_(float x) {
+  const float ax = __builtin_fabsf(x);
+  const float x2 = ax * ax;
+  float p = fmaR(x2, 62.0f / 2835.0f, -17.0f / 315.0f);
+  p = fmaR(p, x2, 2.0f / 15.0f);
+  p = fmaR(p, x2, -1.0f / 3.0f);
+  p = fmaR(p * x2, ax, ax);
+  const float e = __builtin_amdgcn_exp2f(ax * 2.8853900817779268f);  // exp(2|x|)
+  const float q = fmaR(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
+  return __builtin_copysignf(ax < 0.25f ? p : q, x);
+}
 
 // W2 kept once in LDS for the gradient kernel, row u2 = 64 floats, column u1
 // stored at u1 ^ swz(u2).  swz sends bits (0, 1, 3, 2) of u2 mod 16 to bits
@@ -133,7 +147,7 @@ struct W2Lds {
 // Forward pass for the 16 slots: y in the state layout; returns f in the
 // state layout and the hidden activations as D tiles (unit 16T + 4g + r of
 // slot j in h[T][r]).
-template <class W2>
+template <class W2, bool OUT = true>
 __device__ __forceinline__ float forward(const Fwd& P, const W2& w2, int g, int j, float y,
                                          f4 (&h1)[4], f4 (&h2)[4]) {
 #pragma unroll
@@ -152,6 +166,7 @@ __device__ __forceinline__ float forward(const Fwd& P, const W2& w2, int g, int 
 #pragma unroll
     for (int r = 0; r < 4; ++r) h2[T2][r] = tanh_(acc[r]);
   }
+  if constexpr (!OUT) return 0.f;
   f4 out = P.b3;
 #pragma unroll
   for (int T = 0; T < 4; ++T)
@@ -436,7 +451,7 @@ struct GradAcc {
 __device__ __forceinline__ float vjp(const Fwd& P, const Bwd& Q, const float* w2s, float* buf,
                                      float Y, float v, GradAcc& G, int g, int j) {
   f4 h1[4], h2[4];
-  (void)forward(P, W2Lds{w2s}, g, j, Y, h1, h2);
+  (void)forward<W2Lds, false>(P, W2Lds{w2s}, g, j, Y, h1, h2);
   // dh2 = W3^T v, dz2 = dh2 (1 - h2^2)
   f4 dz2[4];
 #pragma unroll
@@ -670,12 +685,26 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   if (j == 0) out[OB3 + g] = s3;
 }
 
-// dL/dtheta[p] = sum over wavefronts w of partial[w][p], in wavefront order.
+// dL/dtheta[p] = sum over wavefronts w of partial[w][p], deterministically:
+// pass 1 sums each chunk of REDUCE_CHUNK consecutive rows into the chunk's
+// first row (block (x, c): columns 256x .. 256x + 255 of chunk c, so every
+// row read is coalesced and a column of a chunk belongs to one thread);
+// pass 2 sums those rows in chunk order.
+constexpr int REDUCE_CHUNK = 64;
+__global__ void __launch_bounds__(256) reduce_chunks_kernel(float* partial, int64_t nw) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= NP) return;
+  const int64_t w0 = (int64_t)blockIdx.y * REDUCE_CHUNK;
+  const int64_t w1 = (w0 + REDUCE_CHUNK < nw) ? w0 + REDUCE_CHUNK : nw;
+  float s = 0.f;
+  for (int64_t w = w0; w < w1; ++w) s += partial[w * NP + p];
+  partial[w0 * NP + p] = s;
+}
 __global__ void __launch_bounds__(256) reduce_kernel(const float* partial, int64_t nw, float* out) {
   const int p = blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= NP) return;
   float s = 0.f;
-  for (int64_t w = 0; w < nw; ++w) s += partial[w * NP + p];
+  for (int64_t w = 0; w < nw; w += REDUCE_CHUNK) s += partial[w * NP + p];
   out[p] = s;
 }
 
