@@ -115,6 +115,11 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   constexpr int32_t RUNNING = -1;
   const int lane = laneId();
   R* const trash = a.trash + 2 * lane;
+  // Tsit5 coefficients pinned to registers where the state is small enough
+  // that the extra 56 registers cost no occupancy (larger states keep the
+  // literals: more resident wavefronts matter more there).
+  tsit5::Coef<R> C5;
+  if constexpr (METHOD == M_TSIT5) C5 = (Sys::D <= 4) ? tsit5::Coef<R>::pinned() : tsit5::Coef<R>::literal();
 
   Sys sys;
   R y[D];
@@ -215,7 +220,7 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     const R hs = last ? (a.t1 - t) : h;
     R ynew[D], err[D], F2[D];
     if constexpr (METHOD == M_TSIT5) {
-      tsit5::trial<R, Sys>(sys, y, hs, k, ynew, err);
+      tsit5::trial<R, Sys>(C5, sys, y, hs, k, ynew, err);
     } else {
       ros23::trial<R, Sys>(sys, y, hs, k[0], ynew, F2, err);
     }
@@ -291,6 +296,11 @@ template <class R, class Sys, int METHOD>
 __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
   constexpr int D = Sys::D, P = Sys::P;
   const int lane = laneId();
+  // Tsit5 coefficients pinned to registers where the state is small enough
+  // that the extra 56 registers cost no occupancy (larger states keep the
+  // literals: more resident wavefronts matter more there).
+  tsit5::Coef<R> C5;
+  if constexpr (METHOD == M_TSIT5) C5 = (Sys::D <= 4) ? tsit5::Coef<R>::pinned() : tsit5::Coef<R>::literal();
   const int64_t slot = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
   R* scr = a.scratch + slot * (a.s_max * D * WAVE) + lane;
   const unsigned long long ngroups = (unsigned long long)((a.n + WAVE - 1) / WAVE);
@@ -359,7 +369,7 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
 #pragma unroll
       for (int c = 0; c < D; ++c) scr[((int64_t)i * D + c) * WAVE] = y[c];
       if constexpr (METHOD == M_TSIT5)
-        tsit5::replay<R, Sys>(sys, y, hj);
+        tsit5::replay<R, Sys>(C5, sys, y, hj);
       else
         ros23::replay<R, Sys>(sys, y, hj);
     }
@@ -385,7 +395,7 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
         h_nx = hrow[i - 1];
       }
       if constexpr (METHOD == M_TSIT5)
-        tsit5::reverse<R, Sys>(sys, yj, hj, lam, pb);
+        tsit5::reverse<R, Sys>(C5, sys, yj, hj, lam, pb);
       else
         ros23::reverse<R, Sys>(sys, yj, hj, lam, pb);
     }

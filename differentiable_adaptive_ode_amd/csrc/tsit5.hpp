@@ -47,55 +47,94 @@ __device__ __forceinline__ constexpr R e(int j) {
   return R(j == 0 ? E0 : j == 1 ? E1 : j == 2 ? E2 : j == 3 ? E3 : j == 4 ? E4 : j == 5 ? E5 : E6);
 }
 
+// The coefficients as values held in registers for a whole kernel.  As plain
+// literals every binary64 coefficient is rebuilt from two scalar moves at each
+// use; pinning them to vector registers once (an empty asm that claims to
+// modify the value keeps the compiler from re-materialising the literal)
+// removes those moves from the step loops.
+template <class R>
+__device__ __forceinline__ R pin(R v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+template <class R>
+struct Coef {
+  R a[7][6];  // a[i][j], j < i
+  R e[7];     // error weights b - bhat
+  __device__ __forceinline__ static Coef pinned() {
+    Coef C;
+#pragma unroll
+    for (int i = 1; i < 7; ++i)
+#pragma unroll
+      for (int j = 0; j < 6; ++j)
+        if (j < i) C.a[i][j] = pin(tsit5::a<R>(i, j));
+#pragma unroll
+    for (int j = 0; j < 7; ++j) C.e[j] = pin(tsit5::e<R>(j));
+    return C;
+  }
+  __device__ __forceinline__ static Coef literal() {
+    Coef C;
+#pragma unroll
+    for (int i = 1; i < 7; ++i)
+#pragma unroll
+      for (int j = 0; j < 6; ++j)
+        if (j < i) C.a[i][j] = tsit5::a<R>(i, j);
+#pragma unroll
+    for (int j = 0; j < 7; ++j) C.e[j] = tsit5::e<R>(j);
+    return C;
+  }
+};
+
 // Stage state Y_i from y and k_0..k_{i-1}.
 template <class R, int D>
-__device__ __forceinline__ void stage_state(int i, const R (&y)[D], R h, const R (&k)[7][D],
-                                            R (&Y)[D]) {
+__device__ __forceinline__ void stage_state(const Coef<R>& C, int i, const R (&y)[D], R h,
+                                            const R (&k)[7][D], R (&Y)[D]) {
 #pragma unroll
   for (int c = 0; c < D; ++c) {
-    R acc = a<R>(i, 0) * k[0][c];
+    R acc = C.a[i][0] * k[0][c];
 #pragma unroll
     for (int j = 1; j < 6; ++j)
-      if (j < i) acc = fmaR(a<R>(i, j), k[j][c], acc);
+      if (j < i) acc = fmaR(C.a[i][j], k[j][c], acc);
     Y[c] = fmaR(h, acc, y[c]);
   }
 }
 
 // One trial step: k[0] = f(y) on entry; fills k[1..6], ynew and err.
 template <class R, class Sys>
-__device__ __forceinline__ void trial(const Sys& sys, const R (&y)[Sys::D], R h,
+__device__ __forceinline__ void trial(const Coef<R>& C, const Sys& sys, const R (&y)[Sys::D], R h,
                                       R (&k)[7][Sys::D], R (&ynew)[Sys::D], R (&err)[Sys::D]) {
   constexpr int D = Sys::D;
   R Y[D];
 #pragma unroll
   for (int i = 1; i < 7; ++i) {
-    stage_state<R, D>(i, y, h, k, Y);
+    stage_state<R, D>(C, i, y, h, k, Y);
     sys.f(Y, k[i]);
   }
 #pragma unroll
   for (int c = 0; c < D; ++c) ynew[c] = Y[c];
 #pragma unroll
   for (int c = 0; c < D; ++c) {
-    R acc = e<R>(0) * k[0][c];
+    R acc = C.e[0] * k[0][c];
 #pragma unroll
-    for (int j = 1; j < 7; ++j) acc = fmaR(e<R>(j), k[j][c], acc);
+    for (int j = 1; j < 7; ++j) acc = fmaR(C.e[j], k[j][c], acc);
     err[c] = h * acc;
   }
 }
 
 // One replay step y <- Phi(y; h): six evaluations, no error estimate.
 template <class R, class Sys>
-__device__ __forceinline__ void replay(const Sys& sys, R (&y)[Sys::D], R h) {
+__device__ __forceinline__ void replay(const Coef<R>& C, const Sys& sys, R (&y)[Sys::D], R h) {
   constexpr int D = Sys::D;
   R k[7][D];
   R Y[D];
   sys.f(y, k[0]);
 #pragma unroll
   for (int i = 1; i < 6; ++i) {
-    stage_state<R, D>(i, y, h, k, Y);
+    stage_state<R, D>(C, i, y, h, k, Y);
     sys.f(Y, k[i]);
   }
-  stage_state<R, D>(6, y, h, k, Y);
+  stage_state<R, D>(C, 6, y, h, k, Y);
 #pragma unroll
   for (int c = 0; c < D; ++c) y[c] = Y[c];
 }
@@ -105,7 +144,7 @@ __device__ __forceinline__ void replay(const Sys& sys, R (&y)[Sys::D], R h) {
 // The stage states are recomputed from y_j (store-the-state, recompute-the-
 // stages, as the in-kernel adjoint of Sec. 3.3 does).
 template <class R, class Sys>
-__device__ __forceinline__ void reverse(const Sys& sys, const R (&y)[Sys::D], R h,
+__device__ __forceinline__ void reverse(const Coef<R>& C, const Sys& sys, const R (&y)[Sys::D], R h,
                                         R (&lam)[Sys::D], R (&pb)[Sys::P]) {
   constexpr int D = Sys::D;
   R k[7][D];
@@ -115,14 +154,14 @@ __device__ __forceinline__ void reverse(const Sys& sys, const R (&y)[Sys::D], R 
   sys.f(Y[0], k[0]);
 #pragma unroll
   for (int i = 1; i < 6; ++i) {
-    stage_state<R, D>(i, y, h, k, Y[i]);
+    stage_state<R, D>(C, i, y, h, k, Y[i]);
     sys.f(Y[i], k[i]);
   }
   // y_new = y + h * sum_j b_j k_j with b_j = a(6, j):  kb_j = h b_j lam.
   R kb[6][D];
 #pragma unroll
   for (int j = 0; j < 6; ++j) {
-    R hb = h * a<R>(6, j);
+    R hb = h * C.a[6][j];
 #pragma unroll
     for (int c = 0; c < D; ++c) kb[j][c] = hb * lam[c];
   }
@@ -135,7 +174,7 @@ __device__ __forceinline__ void reverse(const Sys& sys, const R (&y)[Sys::D], R 
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
       if (j < i) {
-        R ha = h * a<R>(i, j);
+        R ha = h * C.a[i][j];
 #pragma unroll
         for (int c = 0; c < D; ++c) kb[j][c] = fmaR(ha, yb[c], kb[j][c]);
       }
