@@ -44,16 +44,19 @@ def _tsit5_grad(replay, d, v):
 
 
 WORKLOADS = {
-    # name: s_cap, keep t record, flops dict, peak (flop/s), bound, cpu sample size
-    "lotka_volterra": dict(s_cap=256, with_t=True, init=50, att=175, replay=132,
+    # name: s_cap, keep t record, keep the states (the gradient then skips the
+    # replay's forward pass; measured slower end to end on every workload here:
+    # the solve's extra state writes cost what the replay saves, so off), flops,
+    # peak (flop/s), bound, cpu sample size
+    "lotka_volterra": dict(s_cap=256, with_t=True, states=False, init=50, att=175, replay=132,
                            grad=_tsit5_grad(132, 2, 21), peak=78.6e12, bound="alu", cpu_n=256),
-    "lorenz63": dict(s_cap=1024, with_t=True, init=68, att=254, replay=192,
+    "lorenz63": dict(s_cap=1024, with_t=True, states=False, init=68, att=254, replay=192,
                      grad=_tsit5_grad(192, 3, 19), peak=78.6e12, bound="alu", cpu_n=65536),
-    "mlp": dict(s_cap=64, with_t=True, init=18754, att=56337, replay=56256,
+    "mlp": dict(s_cap=64, with_t=True, states=False, init=18754, att=56337, replay=56256,
                 grad=_tsit5_grad(56256, 4, 18954), peak=157.3e12, bound="mfma", cpu_n=1024),
-    "robertson": dict(s_cap=1024, with_t=True, init=68, att=171, replay=105,
+    "robertson": dict(s_cap=1024, with_t=True, states=False, init=68, att=171, replay=105,
                       grad=105 + (105 - 9) + 144, peak=78.6e12, bound="alu", cpu_n=8192),
-    "loghalo": dict(s_cap=8192, with_t=False, init=124, att=497, replay=378,
+    "loghalo": dict(s_cap=8192, with_t=False, states=False, init=124, att=497, replay=378,
                     grad=_tsit5_grad(378, 6, 41), peak=78.6e12, bound="alu", cpu_n=2048),
 }
 # MI355X published peaks: FP64 vector 78.6 TFLOP/s (256 CU x 4 SIMD x 16 lanes x
@@ -67,6 +70,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lorenz63")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--states", action="store_true",
+                    help="record states in the solve; the gradient skips the forward replay")
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="trajectories in the CPU-baseline sample (default per workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -121,7 +126,9 @@ def main():
     th = torch.tensor(w.theta, device=dev)
     y0 = torch.tensor(w.y0, device=dev)
     tgt = torch.tensor(w.target, device=dev)
-    bufs = api.alloc_record(w.n, s_cap, w.dtype, dev, with_t=cfg["with_t"])
+    states = cfg["states"] or args.states
+    bufs = api.alloc_record(w.n, s_cap, w.dtype, dev, with_t=cfg["with_t"],
+                            states_dim=w.d if states else 0)
     # cotangent of the workload's loss: 1/2 |y - target|^2 (positions only for
     # the orbits), or the mean square over the n x d entries (neural field)
     d_used = 3 if w.loss == "half_sq_pos" else w.d
@@ -186,7 +193,8 @@ def main():
     ms = wall / args.steps * 1e3
     ts, tg = float(np.mean(t_solve)), float(np.mean(t_grad))
     fl_solve = w.n * cfg["init"] + attempts * cfg["att"] + steps_total
-    fl_grad = steps_total * cfg["grad"]
+    # with recorded states the gradient does no forward replay
+    fl_grad = steps_total * (cfg["grad"] - (cfg["replay"] if states else 0))
     peak = cfg["peak"]
     dom = "grad" if tg >= ts else "solve"
     ach = (fl_grad / tg) if dom == "grad" else (fl_solve / ts)
@@ -213,7 +221,8 @@ def main():
         "dtype": dtype_name,
         "data": "synthetic",
         "config": {"workload": f"{w.name} ensemble", "n_trajectories": w.n, "method": w.method,
-                   "t_span": [w.t0, w.t1], "rtol": w.rtol, "atol": w.atol, "s_cap": s_cap},
+                   "t_span": [w.t0, w.t1], "rtol": w.rtol, "atol": w.atol, "s_cap": s_cap,
+                   "recorded_states": states},
         "solves_per_s": w.n / ts,
         "grad_trajectories_per_s": w.n / tg,
         "solve_ms": ts * 1e3,

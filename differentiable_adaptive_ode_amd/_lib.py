@@ -30,7 +30,7 @@ class dao_tol(ctypes.Structure):
 class dao_record(ctypes.Structure):
     _fields_ = [("s_cap", ctypes.c_int64), ("t", ctypes.c_void_p), ("h", ctypes.c_void_p),
                 ("count", ctypes.c_void_p), ("nrej", ctypes.c_void_p),
-                ("status", ctypes.c_void_p)]
+                ("status", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 class DaoError(RuntimeError):

@@ -64,6 +64,7 @@ class Record:
     count: torch.Tensor
     nrej: torch.Tensor
     status: torch.Tensor
+    y: torch.Tensor | None = None  # [n, s_cap, d] recorded states, or None
 
     @property
     def n(self):
@@ -73,9 +74,10 @@ class Record:
     def s_cap(self):
         return self.h.shape[1]
 
-    def c_struct(self):
+    def c_struct(self, states: bool = True):
         return _lib.dao_record(self.s_cap, _ptr(self.t), _ptr(self.h), _ptr(self.count),
-                               _ptr(self.nrej), _ptr(self.status))
+                               _ptr(self.nrej), _ptr(self.status),
+                               _ptr(self.y) if states else None)
 
 
 class Workspace:
@@ -104,19 +106,28 @@ def _ws(device, ws=None):
     return _default_ws[key]
 
 
-def alloc_record(n: int, s_cap: int, dtype: str, device, with_t: bool = True) -> dict:
+def alloc_record(n: int, s_cap: int, dtype: str, device, with_t: bool = True,
+                 states_dim: int = 0) -> dict:
+    """Record buffers; states_dim > 0 also allocates the recorded states [n, s_cap, d]."""
     td = _TORCH_DTYPE[dtype]
     return dict(h=torch.empty((n, s_cap), dtype=td, device=device),
                 t=torch.empty((n, s_cap), dtype=td, device=device) if with_t else None,
                 count=torch.empty(n, dtype=torch.int32, device=device),
                 nrej=torch.empty(n, dtype=torch.int32, device=device),
-                status=torch.empty(n, dtype=torch.int32, device=device))
+                status=torch.empty(n, dtype=torch.int32, device=device),
+                y=(torch.empty((n, s_cap, states_dim), dtype=td, device=device)
+                   if states_dim > 0 else None))
 
 
 def solve(system: str, method: str, theta: torch.Tensor, y0: torch.Tensor, t0: float, t1: float,
           rtol: float, atol: float, dt0: float = 0.0, max_steps: int = 100000, s_cap: int = 4096,
-          record_t: bool = True, out=None, rec_buffers=None, workspace=None, stream=None):
-    """Adaptive solve with record.  Returns (Record, y1)."""
+          record_t: bool = True, record_states: bool = False, out=None, rec_buffers=None,
+          workspace=None, stream=None):
+    """Adaptive solve with record.  Returns (Record, y1).
+
+    record_states: also keep the state at the start of every accepted step, so
+    that grad() at the solve's theta skips the replay's forward pass.
+    """
     _check_dev(theta, y0)
     dtype = _dtype_name(y0)
     if theta.dtype != y0.dtype:
@@ -129,9 +140,10 @@ def solve(system: str, method: str, theta: torch.Tensor, y0: torch.Tensor, t0: f
         raise ValueError("theta has the wrong shape")
     dev = y0.device
     y1 = torch.empty_like(y0) if out is None else out
-    bufs = rec_buffers if rec_buffers is not None else alloc_record(n, s_cap, dtype, dev, record_t)
+    bufs = rec_buffers if rec_buffers is not None else alloc_record(
+        n, s_cap, dtype, dev, record_t, d if record_states else 0)
     rec = Record(system, method, dtype, theta, y0, float(t0), float(t1), bufs["h"], bufs.get("t"),
-                 bufs["count"], bufs["nrej"], bufs["status"])
+                 bufs["count"], bufs["nrej"], bufs["status"], bufs.get("y"))
     ws = _ws(dev, workspace)
     sysid, mid, did = _lib.SYSTEMS[system], _lib.METHODS[method], _lib.DTYPES[dtype]
     nb = _lib.dao_solve_workspace_size(sysid, mid, did, n)
@@ -147,7 +159,8 @@ def grad(rec: Record, dLdy1: torch.Tensor, theta: torch.Tensor | None = None, s_
          out_theta=None, out_y0=None, workspace=None, stream=None):
     """dL/dtheta and dL/dy0 by the discrete adjoint on rec's mesh.
 
-    theta: parameters to differentiate at (default: the solve's theta).
+    theta: parameters to differentiate at (default: the solve's theta).  At a
+           theta other than the solve's, recorded states are not used.
     s_max: an upper bound on rec.count (default: read back from the device).
     """
     _check_dev(dLdy1)
@@ -164,7 +177,7 @@ def grad(rec: Record, dLdy1: torch.Tensor, theta: torch.Tensor | None = None, s_
     ws = _ws(dev, workspace)
     nb = _lib.dao_grad_workspace_size(sysid, mid, did, n, s_max)
     buf = ws.get(nb, dev)
-    crec = rec.c_struct()
+    crec = rec.c_struct(states=theta is None)
     _lib.check(_lib.dao_grad(sysid, mid, did, n, _ptr(th), _ptr(rec.y0), crec, s_max, _ptr(dLdy1),
                              _ptr(dth), _ptr(dy0), _ptr(buf), buf.numel(), _stream(stream)))
     return dth, dy0

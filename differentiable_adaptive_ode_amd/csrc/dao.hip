@@ -156,11 +156,12 @@ constexpr int BLOCK = BLOCK_WAVES * WAVE;
 constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
-// Resident workgroups for a kernel at BLOCK threads.
+// Resident workgroups for a kernel at BLOCK threads and `lds` bytes of
+// dynamic LDS.
 template <class K>
-int64_t resident_blocks(K kernel) {
+int64_t resident_blocks(K kernel, size_t lds = 0) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, BLOCK, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, BLOCK, lds) != hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
   return (int64_t)per_cu * dev_info().cus;
@@ -188,14 +189,17 @@ dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0,
   a.count = rec->count;
   a.nrej = rec->nrej;
   a.status = rec->status;
+  a.y_rec = (R*)rec->y;
   a.queue = (unsigned long long*)ws;
   a.trash = (R*)((char*)ws + ALIGN);
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)ws, (int64_t)2, 0u);
   auto kern = solve_kernel<R, Sys, M>;
+  // record staging ring: (t, h [, y]) x 8 slots x 64 lanes per wavefront
+  const size_t lds = (size_t)BLOCK_WAVES * (rec->y ? 2 + Sys::D : 2) * 8 * WAVE * sizeof(R);
   int64_t blocks = (n + BLOCK - 1) / BLOCK;
-  const int64_t res = resident_blocks(kern);
+  const int64_t res = resident_blocks(kern, lds);
   if (blocks > res) blocks = res;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), 0, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), lds, stream, a);
   return check_hip(hipGetLastError(), "solve kernel launch");
 }
 
@@ -266,6 +270,7 @@ dao_status launch_grad(int64_t n, const void* theta, const void* y0, const dao_r
   a.dLdtheta = (R*)dLdtheta;
   a.dLdy0 = (R*)dLdy0;
   a.scratch = scratch;
+  a.y_rec = (const R*)rec->y;
   a.perm = perm;
   a.groups = groups;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), 0, stream, a);
@@ -498,6 +503,8 @@ dao_status dao_solve(dao_system sys, dao_method method, dao_dtype dtype, int64_t
   } else {
     return fail(DAO_EINVAL, "dao_solve: rec is NULL (count and status are written there)");
   }
+  if (rec->y && sys == DAO_SYS_MLP)
+    return fail(DAO_EUNSUPPORTED, "dao_solve: recorded states (rec->y) are not provided for the neural field");
   if (!workspace || workspace_bytes < dao_solve_workspace_size(sys, method, dtype, n))
     return fail(DAO_EWORKSPACE, "dao_solve: workspace needs %zu bytes",
                 dao_solve_workspace_size(sys, method, dtype, n));
@@ -545,6 +552,8 @@ dao_status dao_grad(dao_system sys, dao_method method, dao_dtype dtype, int64_t 
   if (!rec->count) return fail(DAO_EINVAL, "dao_grad: rec->count is NULL");
   if (s_max > 0 && !rec->h) return fail(DAO_EINVAL, "dao_grad: rec->h is NULL");
   if (!dLdy1) return fail(DAO_EINVAL, "dao_grad: dLdy1 is NULL");
+  if (rec->y && sys == DAO_SYS_MLP)
+    return fail(DAO_EUNSUPPORTED, "dao_grad: recorded states (rec->y) are not provided for the neural field");
   const size_t need = dao_grad_workspace_min(sys, method, dtype, n, s_max);
   if (!workspace || workspace_bytes < need)
     return fail(DAO_EWORKSPACE, "dao_grad: workspace needs at least %zu bytes", need);

@@ -40,6 +40,7 @@ struct SolveArgs {
   int32_t* count;
   int32_t* nrej;
   int32_t* status;
+  R* y_rec;  // optional [n][s_cap][D]: the state at the start of each accepted step
   unsigned long long* queue;
   R* trash;  // [64][2] scratch target of record stores that have no row
 };
@@ -58,6 +59,7 @@ struct GradArgs {
   R* dLdtheta;
   R* dLdy0;
   R* scratch;
+  const R* y_rec;  // optional recorded states [n][s_cap][D] (skip the forward replay)
   const int32_t* perm;
   unsigned long long* groups;
 };
@@ -132,21 +134,27 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   bool live = true;
   R* hrow = nullptr;
   R* trow = nullptr;
+  R* yrow = nullptr;
 
-  // Record staging.  A lane keeps its last STAGE (t, h) entries in an LDS
-  // ring (slot-major, lane-minor) and writes them out as one aligned
-  // 64-byte chunk per array whenever its count reaches a multiple of STAGE,
-  // so the record reaches memory in whole chunks instead of 8-byte pieces
-  // scattered over 64 rows.  A trajectory's last partial chunk is written
-  // entry by entry when it finishes.  Records whose capacity is not a
-  // multiple of STAGE are written directly.
+  // Record staging.  A lane keeps its last STAGE entries (t, h and, when
+  // states are recorded, y) in an LDS ring (slot-major, lane-minor) and
+  // writes them out as one aligned chunk per array whenever its count
+  // reaches a multiple of STAGE, so the record reaches memory in whole
+  // chunks instead of 8-byte pieces scattered over 64 rows.  A trajectory's
+  // last partial chunk is written entry by entry when it finishes.  Records
+  // whose capacity is not a multiple of STAGE are written directly.  The
+  // ring is dynamic LDS: ring_arrays(with states) x STAGE x 64 values per
+  // wavefront.
   constexpr int STAGE = 8;
-  __shared__ R ring[BLOCK_WAVES][2][STAGE][WAVE];
-  R(*const hring)[WAVE] = ring[threadIdx.x / WAVE][0];
-  R(*const tring)[WAVE] = ring[threadIdx.x / WAVE][1];
-  const bool staged = (a.s_cap % STAGE) == 0 && ((uintptr_t)a.h_rec % 16) == 0 &&
-                      ((uintptr_t)a.t_rec % 16) == 0;
   const bool with_t = a.t_rec != nullptr;
+  const bool with_y = a.y_rec != nullptr;
+  HIP_DYNAMIC_SHARED(unsigned char, dyn_lds)
+  R* const wring = (R*)dyn_lds + (threadIdx.x / WAVE) * ((with_y ? 2 + D : 2) * STAGE * WAVE);
+  R(*const hring)[WAVE] = (R(*)[WAVE])wring;
+  R(*const tring)[WAVE] = (R(*)[WAVE])(wring + STAGE * WAVE);
+  auto yring = [&](int c, int slot) -> R& { return wring[((2 + c) * STAGE + slot) * WAVE + lane]; };
+  const bool staged = (a.s_cap % STAGE) == 0 && ((uintptr_t)a.h_rec % 16) == 0 &&
+                      ((uintptr_t)a.t_rec % 16) == 0 && ((uintptr_t)a.y_rec % 16) == 0;
 
   auto finish = [&](int32_t st) {
 #pragma unroll
@@ -159,6 +167,10 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
       for (int32_t r = lo; r < nacc; ++r) {
         hrow[r] = hring[r & (STAGE - 1)][lane];
         if (with_t) trow[r] = tring[r & (STAGE - 1)][lane];
+        if (with_y) {
+#pragma unroll
+          for (int c = 0; c < D; ++c) yrow[r * D + c] = yring(c, r & (STAGE - 1));
+        }
       }
     }
     traj = -1;
@@ -194,6 +206,7 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
           __builtin_amdgcn_s_waitcnt(0);
           hrow = a.h_rec + traj * a.s_cap;
           trow = a.t_rec ? a.t_rec + traj * a.s_cap : nullptr;
+          yrow = a.y_rec ? a.y_rec + traj * a.s_cap * D : nullptr;
           t = a.t0;
           nacc = 0;
           nrej = 0;
@@ -249,11 +262,19 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     if (staged) {
       hring[nacc & (STAGE - 1)][lane] = hs;
       if (with_t) tring[nacc & (STAGE - 1)][lane] = t;
+      if (with_y) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) yring(c, nacc & (STAGE - 1)) = y[c];
+      }
     } else {
       // With the record full, the store goes to the lane's trash slot.
       const bool room = nacc < a.s_cap;
       *(room ? hrow + nacc : trash) = hs;
       if (with_t) *(room ? trow + nacc : trash + 1) = t;
+      if (with_y && room) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) yrow[nacc * D + c] = y[c];
+      }
     }
 
     const bool take = (st == RUNNING) && acc;
@@ -273,11 +294,18 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     if (staged && take && (nacc & (STAGE - 1)) == 0) {
       // A full chunk: rows [nacc - STAGE, nacc), 64-byte aligned.
       const int32_t lo = nacc - STAGE;
+      typedef R R2 __attribute__((ext_vector_type(2)));
 #pragma unroll
       for (int r = 0; r < STAGE; r += 2) {
-        typedef R R2 __attribute__((ext_vector_type(2)));
         *(R2*)(hrow + lo + r) = R2{hring[r][lane], hring[r + 1][lane]};
         if (with_t) *(R2*)(trow + lo + r) = R2{tring[r][lane], tring[r + 1][lane]};
+      }
+      if (with_y) {
+        // rows lo .. lo + STAGE - 1 of D values each: STAGE * D contiguous values
+#pragma unroll
+        for (int e = 0; e < STAGE * D; e += 2)
+          *(R2*)(yrow + lo * D + e) =
+              R2{yring(e % D, e / D), yring((e + 1) % D, (e + 1) / D)};
       }
     }
     R fa = (fmin < R(10)) ? fmin : R(10);
@@ -362,36 +390,44 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
     // step ahead: loads and stores retire in order (one vmcnt counter), so a
     // load issued before this step's stores is ready by the next step without
     // waiting for those stores.
+    // With states recorded by the solve (valid at the theta it ran with) the
+    // forward replay is skipped and y_j is read from the record, row j.
+    const bool rec_y = a.y_rec != nullptr;
+    const R* ysrc = rec_y ? a.y_rec + (k >= 0 ? k : 0) * a.s_cap * D : scr;
+    const int64_t istr = rec_y ? D : (int64_t)D * WAVE, cstr = rec_y ? 1 : WAVE;
     R h_nx = (mx > 0) ? hrow[0] : R(0);
-    for (int i = 0; i < mx; ++i) {
-      const R hj = (i < cnt) ? h_nx : R(0);
-      if (i + 1 < mx) h_nx = hrow[i + 1];
+    if (!rec_y) {
+      for (int i = 0; i < mx; ++i) {
+        const R hj = (i < cnt) ? h_nx : R(0);
+        if (i + 1 < mx) h_nx = hrow[i + 1];
 #pragma unroll
-      for (int c = 0; c < D; ++c) scr[((int64_t)i * D + c) * WAVE] = y[c];
-      if constexpr (METHOD == M_TSIT5)
-        tsit5::replay<R, Sys>(C5, sys, y, hj);
-      else
-        ros23::replay<R, Sys>(sys, y, hj);
+        for (int c = 0; c < D; ++c) scr[((int64_t)i * D + c) * WAVE] = y[c];
+        if constexpr (METHOD == M_TSIT5)
+          tsit5::replay<R, Sys>(C5, sys, y, hj);
+        else
+          ros23::replay<R, Sys>(sys, y, hj);
+      }
     }
     // Reverse sweep, with y_j and h_j of the next step (j - 1) prefetched the
-    // same way.
+    // same way.  Past a lane's count the state is taken as zero (recorded rows
+    // there are unspecified), which keeps the zero-size steps exact no-ops.
     R y_nx[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) y_nx[c] = R(0);
     h_nx = R(0);
     if (mx > 0) {
 #pragma unroll
-      for (int c = 0; c < D; ++c) y_nx[c] = scr[((int64_t)(mx - 1) * D + c) * WAVE];
+      for (int c = 0; c < D; ++c) y_nx[c] = ysrc[(int64_t)(mx - 1) * istr + c * cstr];
       h_nx = hrow[mx - 1];
     }
     for (int i = mx - 1; i >= 0; --i) {
       R yj[D];
       const R hj = (i < cnt) ? h_nx : R(0);
 #pragma unroll
-      for (int c = 0; c < D; ++c) yj[c] = y_nx[c];
+      for (int c = 0; c < D; ++c) yj[c] = (i < cnt) ? y_nx[c] : R(0);
       if (i >= 1) {
 #pragma unroll
-        for (int c = 0; c < D; ++c) y_nx[c] = scr[((int64_t)(i - 1) * D + c) * WAVE];
+        for (int c = 0; c < D; ++c) y_nx[c] = ysrc[(int64_t)(i - 1) * istr + c * cstr];
         h_nx = hrow[i - 1];
       }
       if constexpr (METHOD == M_TSIT5)

@@ -97,6 +97,10 @@ typedef struct {
   int32_t* count;  /* int32[n]: accepted steps                                     */
   int32_t* nrej;   /* int32[n]: rejected attempts; may be NULL                     */
   int32_t* status; /* int32[n]: DAO_TRAJ_* code                                    */
+  void* y;         /* optional real[n][s_cap][d]: the state at the start of each
+                      accepted step (the accepted states the in-kernel adjoint of
+                      Sec. 3.3 keeps); NULL = not recorded.  Not provided for
+                      DAO_SYS_MLP.                                                */
 } dao_record;
 
 /* State size d, parameter count p, and whether theta is shared (MLP).
@@ -142,6 +146,10 @@ size_t dao_grad_workspace_min(dao_system sys, dao_method method, dao_dtype dtype
  * and the Jacobian's own dependence on y and theta (Rosenbrock23, Sec. 3.2).
  * theta may differ from the theta of the solve that wrote the record: the
  * derivative is then taken at theta on the old mesh (Sec. 3.1, 4.8).
+ * When rec->y is not NULL the forward pass of the replay is skipped and the
+ * recorded states are used instead; they are the replay's states only at the
+ * theta (and y0) the solve ran with, so a call at another theta must pass a
+ * record whose y is NULL.
  *   theta, y0 as in dao_solve; rec->h and rec->count are read
  *   s_max    >= max_k count[k] and <= rec->s_cap (trajectories with more
  *            steps get NaN outputs)

@@ -383,3 +383,37 @@ def test_full_size_sampled(dao, name, s_cap, record_t):
         e = rel_err(g, dth_o)
     assert e.max() <= TOL, e.max()
     assert rel_err(dy0.cpu().numpy()[:, idx], dy0_o).max() <= TOL
+
+
+@pytest.mark.parametrize("name,n,s_cap", [("lotka_volterra", 300, 256), ("lorenz63", 300, 1024),
+                                          ("robertson", 200, 2048), ("loghalo", 130, 4096)])
+def test_recorded_states(dao, name, n, s_cap):
+    # The solve can keep the state at the start of every accepted step; the
+    # gradient then skips the replay's forward pass.  Those states are the
+    # replay's states bit for bit, so both gradients agree exactly; at a moved
+    # theta the states are not used.
+    w = di.make(name, n)
+    print(f"[recorded states] {name} n={n}", flush=True)
+    rec0, y1a = gpu_solve(dao, w, s_cap)
+    rec1, y1b = gpu_solve(dao, w, s_cap, record_states=True)
+    assert torch.equal(rec0.count, rec1.count) and torch.equal(y1a, y1b)
+    cnt = rec1.count.cpu().numpy()
+    ys = rec1.y.cpu().numpy()
+    assert np.array_equal(ys[:, 0, :], w.y0.T)
+    lam = torch.tensor(di.cotangent(w, y1a.cpu().numpy()), device=DEV)
+    ga = dao.grad(rec0, lam)
+    gb = dao.grad(rec1, lam)
+    torch.cuda.synchronize()
+    assert torch.equal(ga[0], gb[0]) and torch.equal(ga[1], gb[1])
+    th2 = w.theta * 1.002
+    gm = dao.grad(rec1, lam, theta=torch.tensor(th2, device=DEV))
+    torch.cuda.synchronize()
+    ref = oracle_solve(w, s_cap)
+    dth_o, dy0_o, _ = oracle.grad(w.system, w.method, th2, w.y0, ref["count"], ref["h"],
+                                  lam.cpu().numpy(), nthreads=8)
+    if name == "robertson":
+        e = rel_err(gm[0].cpu().numpy() * th2, dth_o * th2)
+    else:
+        e = rel_err(gm[0].cpu().numpy(), dth_o)
+    assert e.max() <= TOL
+    assert rel_err(gm[1].cpu().numpy(), dy0_o).max() <= TOL
