@@ -59,6 +59,11 @@ def _load():
     L.dao_grad_workspace_min.restype = SZ
     L.dao_grad.argtypes = [I, I, I, I64, P, P, ctypes.POINTER(dao_record), I64, P, P, P, P, SZ, P]
     L.dao_grad.restype = I
+    L.dao_grad_order.argtypes = [I, I, I, I64, ctypes.POINTER(dao_record), I64, P, SZ, P]
+    L.dao_grad_order.restype = I
+    L.dao_grad_ordered.argtypes = [I, I, I, I64, P, P, ctypes.POINTER(dao_record), I64, P, P, P,
+                                   P, SZ, P]
+    L.dao_grad_ordered.restype = I
     L.dao_sqerr_cotangent.argtypes = [I, I64, I, I, P, P, D, P, P]
     L.dao_sqerr_cotangent.restype = I
     L.dao_last_error.argtypes = []
@@ -107,6 +112,19 @@ def dao_grad(system, method, dtype, n, theta, y0, rec, s_max, dLdy1, dLdtheta, d
     return lib.dao_grad(system, method, dtype, n, theta, y0,
                         ctypes.byref(rec) if rec is not None else None, s_max, dLdy1, dLdtheta,
                         dLdy0, workspace, ws_bytes, stream)
+
+
+def dao_grad_order(system, method, dtype, n, rec, s_max, workspace, ws_bytes, stream):
+    return lib.dao_grad_order(system, method, dtype, n,
+                              ctypes.byref(rec) if rec is not None else None, s_max, workspace,
+                              ws_bytes, stream)
+
+
+def dao_grad_ordered(system, method, dtype, n, theta, y0, rec, s_max, dLdy1, dLdtheta, dLdy0,
+                     workspace, ws_bytes, stream):
+    return lib.dao_grad_ordered(system, method, dtype, n, theta, y0,
+                                ctypes.byref(rec) if rec is not None else None, s_max, dLdy1,
+                                dLdtheta, dLdy0, workspace, ws_bytes, stream)
 
 
 def dao_sqerr_cotangent(dtype, n, d, d_used, y1, target, scale, out, stream):

@@ -155,31 +155,48 @@ def solve(system: str, method: str, theta: torch.Tensor, y0: torch.Tensor, t0: f
     return rec, y1
 
 
-def grad(rec: Record, dLdy1: torch.Tensor, theta: torch.Tensor | None = None, s_max: int | None = None,
-         out_theta=None, out_y0=None, workspace=None, stream=None):
-    """dL/dtheta and dL/dy0 by the discrete adjoint on rec's mesh.
-
-    theta: parameters to differentiate at (default: the solve's theta).  At a
-           theta other than the solve's, recorded states are not used.
-    s_max: an upper bound on rec.count (default: read back from the device).
-    """
-    _check_dev(dLdy1)
-    th = rec.theta if theta is None else theta
-    _check_dev(th)
+def _grad_setup(rec: Record, s_max, workspace, device):
     n = rec.n
     if s_max is None:
         s_max = int(rec.count.max().item()) if n > 0 else 0
     s_max = min(int(s_max), rec.s_cap)
-    sysid, mid, did = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
+    ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
+    nb = _lib.dao_grad_workspace_size(*ids, n, s_max)
+    buf = _ws(device, workspace).get(nb, device)
+    return ids, n, s_max, buf
+
+
+def grad_order(rec: Record, s_max: int | None = None, workspace=None, stream=None) -> int:
+    """Sort rec's trajectories by step count into the workspace, for later
+    grad(..., ordered=True) calls on the same record and workspace.  Returns
+    the s_max it used (pass the same value to those calls)."""
+    ids, n, s_max, buf = _grad_setup(rec, s_max, workspace, rec.count.device)
+    _lib.check(_lib.dao_grad_order(*ids, n, rec.c_struct(), s_max, _ptr(buf), buf.numel(),
+                                   _stream(stream)))
+    return s_max
+
+
+def grad(rec: Record, dLdy1: torch.Tensor, theta: torch.Tensor | None = None, s_max: int | None = None,
+         out_theta=None, out_y0=None, workspace=None, stream=None, ordered: bool = False):
+    """dL/dtheta and dL/dy0 by the discrete adjoint on rec's mesh.
+
+    theta:   parameters to differentiate at (default: the solve's theta).  At a
+             theta other than the solve's, recorded states are not used.
+    s_max:   an upper bound on rec.count (default: read back from the device).
+    ordered: the workspace already holds this record's order (grad_order with
+             the same workspace and s_max); skips the sort.
+    """
+    _check_dev(dLdy1)
+    th = rec.theta if theta is None else theta
+    _check_dev(th)
     dev = dLdy1.device
+    ids, n, s_max, buf = _grad_setup(rec, s_max, workspace, dev)
     dth = torch.empty_like(th) if out_theta is None else out_theta
     dy0 = torch.empty_like(rec.y0) if out_y0 is None else out_y0
-    ws = _ws(dev, workspace)
-    nb = _lib.dao_grad_workspace_size(sysid, mid, did, n, s_max)
-    buf = ws.get(nb, dev)
     crec = rec.c_struct(states=theta is None)
-    _lib.check(_lib.dao_grad(sysid, mid, did, n, _ptr(th), _ptr(rec.y0), crec, s_max, _ptr(dLdy1),
-                             _ptr(dth), _ptr(dy0), _ptr(buf), buf.numel(), _stream(stream)))
+    fn = _lib.dao_grad_ordered if ordered else _lib.dao_grad
+    _lib.check(fn(*ids, n, _ptr(th), _ptr(rec.y0), crec, s_max, _ptr(dLdy1), _ptr(dth), _ptr(dy0),
+                  _ptr(buf), buf.numel(), _stream(stream)))
     return dth, dy0
 
 

@@ -213,16 +213,14 @@ size_t grad_header_bytes(int64_t n, int64_t s_max) {
   return align_up(16) + align_up((size_t)ORDER_BINS * 4) + align_up((size_t)(n > 0 ? n : 1) * 4);
 }
 
-// Orders trajectories by decreasing step count into perm and clears the
-// group counter of the gradient's work queue.
+// Orders trajectories by decreasing step count into perm.
 void launch_order(const int32_t* count, int64_t n, int64_t s_max, uint32_t* hist, int32_t* perm,
-                  unsigned long long* groups, hipStream_t stream) {
+                  hipStream_t stream) {
   int shift = 0;
   while (((s_max + 1) >> shift) + 1 > ORDER_BINS) ++shift;
   const int nb = (int)(((s_max + 1) >> shift) + 1);
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream,
                      hist, (int64_t)nb, 0u);
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)groups, (int64_t)2, 0u);
   int64_t oblk = (n + 255) / 256;
   if (oblk > 1024) oblk = 1024;
   hipLaunchKernelGGL(order_hist_kernel, dim3((unsigned)oblk), dim3(256), 0, stream, count, n,
@@ -232,8 +230,12 @@ void launch_order(const int32_t* count, int64_t n, int64_t s_max, uint32_t* hist
                      s_max, shift, nb, hist, perm);
 }
 
+// What a gradient call does: order the trajectories by step count into the
+// workspace, run the gradient with the order the workspace holds, or both.
+enum { GRAD_ORDER = 1, GRAD_RUN = 2 };
+
 template <class R, class Sys, int M>
-dao_status launch_grad(int64_t n, const void* theta, const void* y0, const dao_record* rec,
+dao_status launch_grad(int mode, int64_t n, const void* theta, const void* y0, const dao_record* rec,
                        int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
   constexpr int D = Sys::D;
@@ -255,7 +257,9 @@ dao_status launch_grad(int64_t n, const void* theta, const void* y0, const dao_r
   if (blocks > slots / waves_per_block) blocks = slots / waves_per_block;
   if (blocks < 1) return fail(DAO_EWORKSPACE, "dao_grad: workspace too small");
 
-  launch_order(rec->count, n, s_max, hist, perm, groups, stream);
+  if (mode & GRAD_ORDER) launch_order(rec->count, n, s_max, hist, perm, stream);
+  if (!(mode & GRAD_RUN)) return check_hip(hipGetLastError(), "order kernel launch");
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)groups, (int64_t)2, 0u);
 
   GradArgs<R> a;
   a.n = n;
@@ -316,7 +320,7 @@ size_t mlp_slot_bytes(int64_t s_max) {
          align_up((size_t)mlp::NP * sizeof(float));
 }
 
-dao_status launch_mlp_grad(int64_t n, const void* theta, const void* y0, const dao_record* rec,
+dao_status launch_mlp_grad(int mode, int64_t n, const void* theta, const void* y0, const dao_record* rec,
                            int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0, void* ws,
                            size_t ws_bytes, hipStream_t stream) {
   char* base = (char*)ws;
@@ -338,7 +342,9 @@ dao_status launch_mlp_grad(int64_t n, const void* theta, const void* y0, const d
   float* partial = (float*)(base + hdr + (size_t)nw * align_up((size_t)(s_max > 0 ? s_max : 1) *
                                                                 WAVE * sizeof(float)));
 
-  launch_order(rec->count, n, s_max, hist, perm, groups, stream);
+  if (mode & GRAD_ORDER) launch_order(rec->count, n, s_max, hist, perm, stream);
+  if (!(mode & GRAD_RUN)) return check_hip(hipGetLastError(), "order kernel launch");
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)groups, (int64_t)2, 0u);
 
   mlp::GradArgs a;
   a.n = n;
@@ -377,10 +383,10 @@ struct Entry {
                           hipStream_t st) {
     return launch_solve<R, S<R>, M>(n, th, y0, t0, t1, tol, y1, rec, ws, st);
   }
-  static dao_status grad(int64_t n, const void* th, const void* y0, const dao_record* rec,
+  static dao_status grad(int mode, int64_t n, const void* th, const void* y0, const dao_record* rec,
                          int64_t s_max, const void* g, void* dth, void* dy0, void* ws,
                          size_t wsb, hipStream_t st) {
-    return launch_grad<R, S<R>, M>(n, th, y0, rec, s_max, g, dth, dy0, ws, wsb, st);
+    return launch_grad<R, S<R>, M>(mode, n, th, y0, rec, s_max, g, dth, dy0, ws, wsb, st);
   }
   static size_t slot_bytes(int64_t s_max) { return grad_slot_bytes<R, S<R>::D>(s_max); }
   static int64_t resident_waves() {
@@ -390,7 +396,7 @@ struct Entry {
 
 typedef dao_status (*solve_fn)(int64_t, const void*, const void*, double, double, const dao_tol*,
                                void*, const dao_record*, void*, hipStream_t);
-typedef dao_status (*grad_fn)(int64_t, const void*, const void*, const dao_record*, int64_t,
+typedef dao_status (*grad_fn)(int, int64_t, const void*, const void*, const dao_record*, int64_t,
                               const void*, void*, void*, void*, size_t, hipStream_t);
 typedef size_t (*slot_fn)(int64_t);
 typedef int64_t (*res_fn)();
@@ -530,35 +536,71 @@ size_t dao_grad_workspace_size(dao_system sys, dao_method method, dao_dtype dtyp
   return grad_header_bytes(n, s_max) + (size_t)waves * im->slot(s_max);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the gradient's entry points; `fn` names the entry
+// point in the message.  The order step reads only rec->count (and status), so
+// theta, y0 and dLdy1 are checked only when the gradient itself runs.
+dao_status grad_call(const char* fn, int mode, dao_system sys, dao_method method, dao_dtype dtype,
+                     int64_t n, const void* theta, const void* y0, const dao_record* rec,
+                     int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!sys_ok(sys)) return fail(DAO_EINVAL, "%s: unknown system %d", fn, (int)sys);
+  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
+    return fail(DAO_EINVAL, "%s: unknown method %d", fn, (int)method);
+  if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+  if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "%s: n = %lld out of range", fn, (long long)n);
+  if (!rec) return fail(DAO_EINVAL, "%s: rec is NULL", fn);
+  if (rec->s_cap < 0) return fail(DAO_EINVAL, "%s: rec->s_cap < 0", fn);
+  if (s_max < 0 || s_max > rec->s_cap) return fail(DAO_EINVAL, "%s: s_max must be in [0, rec->s_cap]", fn);
+  const Impl* im = find_impl(sys, method, dtype);
+  if (!im) return fail(DAO_EUNSUPPORTED, "%s: system %d with method %d dtype %d is not provided",
+                       fn, (int)sys, (int)method, (int)dtype);
+  if (n == 0) return DAO_OK;
+  if (!rec->count) return fail(DAO_EINVAL, "%s: rec->count is NULL", fn);
+  if (mode & GRAD_RUN) {
+    if (!theta) return fail(DAO_EINVAL, "%s: theta is NULL", fn);
+    if (!y0) return fail(DAO_EINVAL, "%s: y0 is NULL", fn);
+    if (s_max > 0 && !rec->h) return fail(DAO_EINVAL, "%s: rec->h is NULL", fn);
+    if (!dLdy1) return fail(DAO_EINVAL, "%s: dLdy1 is NULL", fn);
+    if (rec->y && sys == DAO_SYS_MLP)
+      return fail(DAO_EUNSUPPORTED, "%s: recorded states (rec->y) are not provided for the neural field", fn);
+  }
+  const size_t need = dao_grad_workspace_min(sys, method, dtype, n, s_max);
+  if (!workspace || workspace_bytes < need)
+    return fail(DAO_EWORKSPACE, "%s: workspace needs at least %zu bytes", fn, need);
+  return im->grad(mode, n, theta, y0, rec, s_max, dLdy1, dLdtheta, dLdy0, workspace,
+                  workspace_bytes, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
 dao_status dao_grad(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
                     const void* theta, const void* y0, const dao_record* rec, int64_t s_max,
                     const void* dLdy1, void* dLdtheta, void* dLdy0, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
-  if (!sys_ok(sys)) return fail(DAO_EINVAL, "dao_grad: unknown system %d", (int)sys);
-  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
-    return fail(DAO_EINVAL, "dao_grad: unknown method %d", (int)method);
-  if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "dao_grad: unknown dtype %d", (int)dtype);
-  if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "dao_grad: n = %lld out of range", (long long)n);
-  if (!rec) return fail(DAO_EINVAL, "dao_grad: rec is NULL");
-  if (rec->s_cap < 0) return fail(DAO_EINVAL, "dao_grad: rec->s_cap < 0");
-  if (s_max < 0 || s_max > rec->s_cap) return fail(DAO_EINVAL, "dao_grad: s_max must be in [0, rec->s_cap]");
-  const Impl* im = find_impl(sys, method, dtype);
-  if (!im) return fail(DAO_EUNSUPPORTED, "dao_grad: system %d with method %d dtype %d is not provided",
-                       (int)sys, (int)method, (int)dtype);
-  if (n == 0) return DAO_OK;
-  if (!theta) return fail(DAO_EINVAL, "dao_grad: theta is NULL");
-  if (!y0) return fail(DAO_EINVAL, "dao_grad: y0 is NULL");
-  if (!rec->count) return fail(DAO_EINVAL, "dao_grad: rec->count is NULL");
-  if (s_max > 0 && !rec->h) return fail(DAO_EINVAL, "dao_grad: rec->h is NULL");
-  if (!dLdy1) return fail(DAO_EINVAL, "dao_grad: dLdy1 is NULL");
-  if (rec->y && sys == DAO_SYS_MLP)
-    return fail(DAO_EUNSUPPORTED, "dao_grad: recorded states (rec->y) are not provided for the neural field");
-  const size_t need = dao_grad_workspace_min(sys, method, dtype, n, s_max);
-  if (!workspace || workspace_bytes < need)
-    return fail(DAO_EWORKSPACE, "dao_grad: workspace needs at least %zu bytes", need);
-  return im->grad(n, theta, y0, rec, s_max, dLdy1, dLdtheta, dLdy0, workspace, workspace_bytes,
-                  (hipStream_t)stream);
+  return grad_call("dao_grad", GRAD_ORDER | GRAD_RUN, sys, method, dtype, n, theta, y0, rec, s_max,
+                   dLdy1, dLdtheta, dLdy0, workspace, workspace_bytes, stream);
+}
+
+dao_status dao_grad_order(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                          const dao_record* rec, int64_t s_max, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return grad_call("dao_grad_order", GRAD_ORDER, sys, method, dtype, n, nullptr, nullptr, rec,
+                   s_max, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+dao_status dao_grad_ordered(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                            const void* theta, const void* y0, const dao_record* rec,
+                            int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return grad_call("dao_grad_ordered", GRAD_RUN, sys, method, dtype, n, theta, y0, rec, s_max,
+                   dLdy1, dLdtheta, dLdy0, workspace, workspace_bytes, stream);
 }
 
 dao_status dao_sqerr_cotangent(dao_dtype dtype, int64_t n, int d, int d_used, const void* y1,

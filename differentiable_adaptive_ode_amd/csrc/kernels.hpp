@@ -344,9 +344,13 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
     bool ok = false;
     if (idx < a.n) {
       k = a.perm ? (int64_t)a.perm[idx] : idx;
-      cnt = a.count[k];
-      ok = cnt >= 0 && cnt <= a.s_max && (a.status == nullptr || a.status[k] == TRAJ_OK);
-      if (!ok) cnt = 0;
+      if (k < 0 || k >= a.n) {
+        k = -1;  // an order that is not this record's: nothing is read or written
+      } else {
+        cnt = a.count[k];
+        ok = cnt >= 0 && cnt <= a.s_max && (a.status == nullptr || a.status[k] == TRAJ_OK);
+        if (!ok) cnt = 0;
+      }
     }
     int mx = cnt;
 #pragma unroll

@@ -165,6 +165,29 @@ dao_status dao_grad(dao_system sys, dao_method method, dao_dtype dtype, int64_t 
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dao_grad in two parts.  The gradient runs trajectories in groups of similar
+ * step count; dao_grad_order sorts the record's trajectories by count[k] into
+ * the workspace, and dao_grad_ordered runs the gradient with the order the
+ * workspace holds.  dao_grad does both.  One order serves any number of
+ * dao_grad_ordered calls on the same record counts, n and s_max (Sec. 3.1
+ * and 4.8 reuse one record while theta moves: theta, y0 and dLdy1 may change
+ * between them), provided nothing else writes the workspace in between (a
+ * dao_grad call with it, or its use as a dao_solve workspace, does).
+ * dao_grad_order reads rec->count and rec->s_cap only; theta, y0 and dLdy1
+ * are not touched.  Arguments, errors and results otherwise as dao_grad; with
+ * a workspace that holds no order for this record, dao_grad_ordered's
+ * results are unspecified (every access stays within the workspace and the
+ * record).
+ */
+dao_status dao_grad_order(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                          const dao_record* rec, int64_t s_max, void* workspace,
+                          size_t workspace_bytes, void* stream);
+dao_status dao_grad_ordered(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                            const void* theta, const void* y0, const dao_record* rec,
+                            int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * dao_sqerr_cotangent -- cotangent of a squared-error loss (the misfit
  * l(y(t1)) of Sec. 2.2's calibration loss), out[c][k] = scale *
  * (y1[c][k] - target[c][k]) for components c < d_used, 0 for the rest.

@@ -26,7 +26,8 @@ def L():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("dao_solve", "dao_grad", "dao_solve_workspace_size", "dao_grad_workspace_size",
+    for n in ("dao_solve", "dao_grad", "dao_grad_order", "dao_grad_ordered",
+              "dao_solve_workspace_size", "dao_grad_workspace_size",
               "dao_grad_workspace_min", "dao_system_dims", "dao_sqerr_cotangent",
               "dao_last_error", "dao_version"):
         assert n in names, n
@@ -100,6 +101,30 @@ def test_grad_argument_errors(L):
     assert call(theta=None) == 1
     assert call(system=5, method=1) == 4
     assert call(n=0) == 0
+
+
+def test_grad_order_and_ordered_argument_errors(L):
+    rec = L.dao_record(16, None, 1, 1, None, 1)
+    # the order step reads only the record's counts: no theta, y0 or cotangent
+    assert L.dao_grad_order(2, 0, 0, 4, None, 8, 1, 1 << 30, None) == 1   # rec NULL
+    assert L.dao_grad_order(2, 0, 0, 4, rec, 17, 1, 1 << 30, None) == 1   # s_max > s_cap
+    assert L.dao_grad_order(2, 0, 0, 4, rec, 8, None, 1 << 30, None) == 3  # no workspace
+    assert L.dao_grad_order(5, 1, 0, 4, rec, 8, 1, 1 << 30, None) == 4    # not provided
+    assert L.dao_grad_order(2, 0, 0, 0, rec, 8, None, 0, None) == 0       # empty ensemble
+    assert "dao_grad_order" in L.dao_last_error() or L.dao_last_error() == ""
+
+    def ordered(**o):
+        a = dict(theta=1, y0=1, g=1, ws=1, wsb=1 << 30, s_max=8)
+        a.update(o)
+        return L.dao_grad_ordered(2, 0, 0, 4, a["theta"], a["y0"], rec, a["s_max"], a["g"], 1, 1,
+                                  a["ws"], a["wsb"], None)
+
+    assert ordered(g=None) == 1
+    assert "dao_grad_ordered" in L.dao_last_error()
+    assert ordered(theta=None) == 1
+    assert ordered(y0=None) == 1
+    assert ordered(s_max=-1) == 1
+    assert ordered(wsb=16) == 3
 
 
 def test_cotangent_argument_errors(L):

@@ -417,3 +417,30 @@ def test_recorded_states(dao, name, n, s_cap):
         e = rel_err(gm[0].cpu().numpy(), dth_o)
     assert e.max() <= TOL
     assert rel_err(gm[1].cpu().numpy(), dy0_o).max() <= TOL
+
+
+@pytest.mark.parametrize("name,n,s_cap", [("lorenz63", 300, 1024), ("robertson", 200, 2048)])
+def test_one_order_many_gradients(dao, name, n, s_cap):
+    # dao_grad_order sorts a record's trajectories once; dao_grad_ordered then
+    # serves several gradients at moved theta (Sec. 3.1 reuses one record
+    # while theta moves).  Each equals dao_grad bit for bit and the oracle.
+    from differentiable_adaptive_ode_amd import api
+
+    w = di.make(name, n)
+    print(f"[order once] {name} n={n}", flush=True)
+    rec, y1 = gpu_solve(dao, w, s_cap)
+    ref = oracle_solve(w, s_cap)
+    ws = api.Workspace()
+    s_max = dao.grad_order(rec, workspace=ws)
+    lam = torch.tensor(np.random.default_rng(5).normal(size=w.y0.shape), device=DEV)
+    for f in (1.0, 1.001, 0.999):
+        th = torch.tensor(w.theta * f, device=DEV)
+        go = dao.grad(rec, lam, theta=th, s_max=s_max, workspace=ws, ordered=True)
+        gd = dao.grad(rec, lam, theta=th, s_max=s_max)  # its own workspace, sorted again
+        torch.cuda.synchronize()
+        assert torch.equal(go[0], gd[0]) and torch.equal(go[1], gd[1])
+        dth_o, dy0_o, _ = oracle.grad(w.system, w.method, w.theta * f, w.y0, ref["count"],
+                                      ref["h"], lam.cpu().numpy(), nthreads=8)
+        scale = w.theta * f if name == "robertson" else 1.0
+        assert rel_err(go[0].cpu().numpy() * scale, dth_o * scale).max() <= TOL
+        assert rel_err(go[1].cpu().numpy(), dy0_o).max() <= TOL
