@@ -396,6 +396,10 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
     // waiting for those stores.
     // With states recorded by the solve (valid at the theta it ran with) the
     // forward replay is skipped and y_j is read from the record, row j.
+    // The states are written once and read once, long after (a wavefront's
+    // tile is s_max x d x 512 bytes): they stream through the L2 as
+    // nontemporal accesses, which leaves the lines of the h rows, each read
+    // eight bytes per step, resident between their steps.
     const bool rec_y = a.y_rec != nullptr;
     const R* ysrc = rec_y ? a.y_rec + (k >= 0 ? k : 0) * a.s_cap * D : scr;
     const int64_t istr = rec_y ? D : (int64_t)D * WAVE, cstr = rec_y ? 1 : WAVE;
@@ -405,7 +409,8 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
         const R hj = (i < cnt) ? h_nx : R(0);
         if (i + 1 < mx) h_nx = hrow[i + 1];
 #pragma unroll
-        for (int c = 0; c < D; ++c) scr[((int64_t)i * D + c) * WAVE] = y[c];
+        for (int c = 0; c < D; ++c)
+          __builtin_nontemporal_store(y[c], &scr[((int64_t)i * D + c) * WAVE]);
         if constexpr (METHOD == M_TSIT5)
           tsit5::replay<R, Sys>(C5, sys, y, hj);
         else
@@ -415,13 +420,16 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
     // Reverse sweep, with y_j and h_j of the next step (j - 1) prefetched the
     // same way.  Past a lane's count the state is taken as zero (recorded rows
     // there are unspecified), which keeps the zero-size steps exact no-ops.
+    // (Recomputing step j - 1's stages during step j's sweep, for two
+    // independent chains per iteration, measured no faster on any workload.)
     R y_nx[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) y_nx[c] = R(0);
     h_nx = R(0);
     if (mx > 0) {
 #pragma unroll
-      for (int c = 0; c < D; ++c) y_nx[c] = ysrc[(int64_t)(mx - 1) * istr + c * cstr];
+      for (int c = 0; c < D; ++c)
+        y_nx[c] = __builtin_nontemporal_load(&ysrc[(int64_t)(mx - 1) * istr + c * cstr]);
       h_nx = hrow[mx - 1];
     }
     for (int i = mx - 1; i >= 0; --i) {
@@ -431,13 +439,19 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
       for (int c = 0; c < D; ++c) yj[c] = (i < cnt) ? y_nx[c] : R(0);
       if (i >= 1) {
 #pragma unroll
-        for (int c = 0; c < D; ++c) y_nx[c] = ysrc[(int64_t)(i - 1) * istr + c * cstr];
+        for (int c = 0; c < D; ++c)
+          y_nx[c] = __builtin_nontemporal_load(&ysrc[(int64_t)(i - 1) * istr + c * cstr]);
         h_nx = hrow[i - 1];
       }
-      if constexpr (METHOD == M_TSIT5)
-        tsit5::reverse<R, Sys>(C5, sys, yj, hj, lam, pb);
-      else
-        ros23::reverse<R, Sys>(sys, yj, hj, lam, pb);
+      if constexpr (METHOD == M_TSIT5) {
+        tsit5::Stages<R, D> S;
+        tsit5::stages<R, Sys>(C5, sys, yj, hj, S);
+        tsit5::sweep<R, Sys>(C5, sys, S, hj, lam, pb);
+      } else {
+        ros23::Stages<R, D> S;
+        ros23::stages<R, Sys>(sys, yj, hj, S);
+        ros23::sweep<R, Sys>(sys, S, hj, lam, pb);
+      }
     }
     if (k >= 0) {
       if (!ok) {

@@ -198,24 +198,42 @@ __device__ __forceinline__ void replay(const Sys& sys, R (&y)[Sys::D], R h) {
   for (int c = 0; c < D; ++c) y[c] = fmaR(h, u[c] + k1[c], y[c]);
 }
 
-// Reverse of one replay step: lam = dL/dy_{j+1} in, dL/dy_j out; pb += dL/dtheta.
+// Reverse of one replay step, in two parts: the forward quantities of the
+// step (they depend only on y_j and h_j), then the sweep that takes
+// lam = dL/dy_{j+1} to dL/dy_j and accumulates dL/dtheta into pb.
+template <class R, int D>
+struct Stages {
+  LU<R, D> w;   // factors of W = I - h d J(y)
+  R y[D];       // y_j
+  R k1[D];      // W^-1 F0
+  R Y1[D];      // y + h/2 k1
+  R u[D];       // W^-1 (F1 - k1)
+};
+
 template <class R, class Sys>
-__device__ __forceinline__ void reverse(const Sys& sys, const R (&y)[Sys::D], R h,
-                                        R (&lam)[Sys::D], R (&pb)[Sys::P]) {
+__device__ __forceinline__ void stages(const Sys& sys, const R (&y)[Sys::D], R h,
+                                       Stages<R, Sys::D>& S) {
   constexpr int D = Sys::D;
-  LU<R, D> w;
-  build_w(sys, y, h, w);
-  R F0[D], k1[D], Y1[D], F1[D], r[D], u[D];
+  build_w(sys, y, h, S.w);
+  R F0[D], F1[D], r[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) S.y[c] = y[c];
   sys.f(y, F0);
-  solve<R, D>(w, F0, k1);
+  solve<R, D>(S.w, F0, S.k1);
   R hh = R(0.5) * h;
 #pragma unroll
-  for (int c = 0; c < D; ++c) Y1[c] = fmaR(hh, k1[c], y[c]);
-  sys.f(Y1, F1);
+  for (int c = 0; c < D; ++c) S.Y1[c] = fmaR(hh, S.k1[c], y[c]);
+  sys.f(S.Y1, F1);
 #pragma unroll
-  for (int c = 0; c < D; ++c) r[c] = F1[c] - k1[c];
-  solve<R, D>(w, r, u);
+  for (int c = 0; c < D; ++c) r[c] = F1[c] - S.k1[c];
+  solve<R, D>(S.w, r, S.u);
+}
 
+template <class R, class Sys>
+__device__ __forceinline__ void sweep(const Sys& sys, const Stages<R, Sys::D>& S, R h,
+                                      R (&lam)[Sys::D], R (&pb)[Sys::P]) {
+  constexpr int D = Sys::D;
+  const R hh = R(0.5) * h;
   // y_new = y + h (u + k1)
   R ub[D], k1b[D], rb[D], tmp[D], F0b[D];
 #pragma unroll
@@ -224,21 +242,21 @@ __device__ __forceinline__ void reverse(const Sys& sys, const R (&y)[Sys::D], R 
     k1b[c] = ub[c];
   }
   // u = W^-1 r:  rb = W^-T ub,  Wb = -rb u^T
-  solve_t<R, D>(w, ub, rb);
+  solve_t<R, D>(S.w, ub, rb);
   // r = F1 - k1
 #pragma unroll
   for (int c = 0; c < D; ++c) k1b[c] -= rb[c];
   // F1 = f(Y1), Y1 = y + h/2 k1
-  sys.vjp(Y1, rb, tmp, pb);
+  sys.vjp(S.Y1, rb, tmp, pb);
 #pragma unroll
   for (int c = 0; c < D; ++c) {
     lam[c] += tmp[c];
     k1b[c] = fmaR(hh, tmp[c], k1b[c]);
   }
   // k1 = W^-1 F0:  F0b = W^-T k1b,  Wb -= F0b k1^T
-  solve_t<R, D>(w, k1b, F0b);
+  solve_t<R, D>(S.w, k1b, F0b);
   // F0 = f(y)
-  sys.vjp(y, F0b, tmp, pb);
+  sys.vjp(S.y, F0b, tmp, pb);
 #pragma unroll
   for (int c = 0; c < D; ++c) lam[c] += tmp[c];
   // W = I - h d J(y, theta):  Jb = -h d Wb = h d (rb u^T + F0b k1^T)
@@ -247,8 +265,8 @@ __device__ __forceinline__ void reverse(const Sys& sys, const R (&y)[Sys::D], R 
 #pragma unroll
   for (int i = 0; i < D; ++i)
 #pragma unroll
-    for (int j = 0; j < D; ++j) Jb[i][j] = hd * fmaR(rb[i], u[j], F0b[i] * k1[j]);
-  sys.jac_vjp(y, Jb, lam, pb);
+    for (int j = 0; j < D; ++j) Jb[i][j] = hd * fmaR(rb[i], S.u[j], F0b[i] * S.k1[j]);
+  sys.jac_vjp(S.y, Jb, lam, pb);
 }
 
 }  // namespace ros23

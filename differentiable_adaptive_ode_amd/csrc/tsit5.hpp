@@ -139,24 +139,35 @@ __device__ __forceinline__ void replay(const Coef<R>& C, const Sys& sys, R (&y)[
   for (int c = 0; c < D; ++c) y[c] = Y[c];
 }
 
-// Reverse of one replay step.  On entry lam = dL/dy_{j+1}; on exit
-// lam = dL/dy_j and pb has accumulated dL/dtheta from this step.
-// The stage states are recomputed from y_j (store-the-state, recompute-the-
-// stages, as the in-kernel adjoint of Sec. 3.3 does).
+// Reverse of one replay step, in two parts.  The stage states depend only
+// on y_j and h_j (store-the-state, recompute-the-stages, as the in-kernel
+// adjoint of Sec. 3.3 does); the sweep takes lam = dL/dy_{j+1} to
+// lam = dL/dy_j and accumulates dL/dtheta into pb.  Keeping them apart lets a
+// caller recompute one step's stages while it sweeps back through another.
+template <class R, int D>
+struct Stages {
+  R Y[6][D];  // stage states Y_1 .. Y_6 (Y_1 = y_j)
+};
+
 template <class R, class Sys>
-__device__ __forceinline__ void reverse(const Coef<R>& C, const Sys& sys, const R (&y)[Sys::D], R h,
-                                        R (&lam)[Sys::D], R (&pb)[Sys::P]) {
+__device__ __forceinline__ void stages(const Coef<R>& C, const Sys& sys, const R (&y)[Sys::D], R h,
+                                       Stages<R, Sys::D>& S) {
   constexpr int D = Sys::D;
   R k[7][D];
-  R Y[6][D];
 #pragma unroll
-  for (int c = 0; c < D; ++c) Y[0][c] = y[c];
-  sys.f(Y[0], k[0]);
+  for (int c = 0; c < D; ++c) S.Y[0][c] = y[c];
+  sys.f(S.Y[0], k[0]);
 #pragma unroll
   for (int i = 1; i < 6; ++i) {
-    stage_state<R, D>(C, i, y, h, k, Y[i]);
-    sys.f(Y[i], k[i]);
+    stage_state<R, D>(C, i, y, h, k, S.Y[i]);
+    sys.f(S.Y[i], k[i]);
   }
+}
+
+template <class R, class Sys>
+__device__ __forceinline__ void sweep(const Coef<R>& C, const Sys& sys, const Stages<R, Sys::D>& S,
+                                      R h, R (&lam)[Sys::D], R (&pb)[Sys::P]) {
+  constexpr int D = Sys::D;
   // y_new = y + h * sum_j b_j k_j with b_j = a(6, j):  kb_j = h b_j lam.
   R kb[6][D];
 #pragma unroll
@@ -168,7 +179,7 @@ __device__ __forceinline__ void reverse(const Coef<R>& C, const Sys& sys, const 
   R yb[D];
 #pragma unroll
   for (int i = 5; i >= 0; --i) {
-    sys.vjp(Y[i], kb[i], yb, pb);
+    sys.vjp(S.Y[i], kb[i], yb, pb);
 #pragma unroll
     for (int c = 0; c < D; ++c) lam[c] += yb[c];
 #pragma unroll
