@@ -11,7 +11,9 @@ The arithmetic lives in ``oracle.cpp`` (binary64 C++, ``-ffp-contract=off``):
 * the fixed-step replay of a recorded mesh (Sec. 3.1, Eq. 4);
 * the reverse-mode derivative of that replay, computed with a scalar tape
   (Sec. 3.1: exact gradient of the chain with the mesh held fixed);
-* a complex-step replay for directional derivatives.
+* a complex-step replay for directional derivatives;
+* the forward-mode sensitivities of the replayed final state (dual numbers
+  carrying one derivative per parameter and initial-state component).
 
 Array layouts match the library boundary: parameters ``[p][n]`` (shared MLP
 weights ``[4740]``), states ``[d][n]``, record rows ``[n][s_cap]``.
@@ -63,6 +65,7 @@ def lib():
         L.oracle_replay_f64.argtypes = [I, I, I64, P, P, P, P, I64, P, I]
         L.oracle_replay_cs.argtypes = [I, I, I64, P, P, P, P, D, P, P, I64, P, P]
         L.oracle_grad_f64.argtypes = [I, I, I64, P, P, P, P, I64, P, P, P, P, I]
+        L.oracle_sens_f64.argtypes = [I, I, I64, P, P, P, P, I64, P, P, P, I]
         L.oracle_step_f64.argtypes = [I, I, P, P, D, P, P]
         L.oracle_rhs_f64.argtypes = [I, P, P, P]
         L.oracle_jac_f64.argtypes = [I, P, P, P]
@@ -176,6 +179,26 @@ def grad(system, method, theta, y0, count, h, dLdy, nthreads=1):
                                int(nthreads))
     assert rc == 0
     return dtheta, dy0, yS
+
+
+def sens(system, method, theta, y0, count, h, with_y0=True, nthreads=1):
+    """Forward-mode sensitivities of the replayed final state on the mesh
+    (count, h): S_theta [d][p][n] = dy_S/dtheta and S_y0 [d][d][n] = dy_S/dy0
+    (None unless with_y0).  Returns (S_theta, S_y0, yS)."""
+    d, p, shared = dims(system)
+    assert not shared
+    theta = np.ascontiguousarray(theta, dtype=np.float64)
+    y0 = np.ascontiguousarray(y0, dtype=np.float64)
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    count = np.ascontiguousarray(count, dtype=np.int32)
+    n = y0.shape[1]
+    S_th = np.zeros((d, p, n))
+    S_y0 = np.zeros((d, d, n)) if with_y0 else None
+    yS = np.zeros((d, n))
+    rc = lib().oracle_sens_f64(SYSTEMS[system], METHODS[method], n, _p(theta), _p(y0), _p(count),
+                               _p(h), h.shape[1], _p(S_th), _p(S_y0), _p(yS), int(nthreads))
+    assert rc == 0
+    return S_th, S_y0, yS
 
 
 def step(system, method, theta, y, h):

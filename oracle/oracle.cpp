@@ -25,7 +25,7 @@
 // product appears in this file.  The same templated replay also runs on
 // std::complex<double> for complex-step derivatives (an independent pin).
 //
-// Readings where the pages are silent (also listed in the design doc):
+// Readings where the pages are silent:
 //   * Tsit5 coefficients: Tsitouras, Comput. Math. Appl. 62 (2011) 770-775,
 //     Table 1 (the pages cite the pair but do not print it).
 //   * Rosenbrock23: Shampine & Reichelt, SIAM J. Sci. Comput. 18 (1997) 1-22
@@ -129,6 +129,62 @@ inline Rev tanh_(Rev a) {
   return rnode(t, a.id, 1.0 - t * t);
 }
 inline double rv(Rev a) { return a.v; }
+
+// Forward-mode dual number: a value and its derivatives along up to MAXDIR
+// directions (the parameters, then the initial state), each propagated by
+// the chain rule through every operation.  Run through the replay it gives
+// the Jacobian of the final state, column by column, in one pass.
+const int MAXDIR = 9;
+thread_local int g_ndir = 0;  // directions in use
+struct Fwd {
+  double v;
+  double t[MAXDIR];
+  Fwd() : v(0.0) {
+    for (int i = 0; i < MAXDIR; ++i) t[i] = 0.0;
+  }
+  Fwd(double x) : v(x) {  // NOLINT: constants promote implicitly
+    for (int i = 0; i < MAXDIR; ++i) t[i] = 0.0;
+  }
+};
+inline Fwd operator+(const Fwd& a, const Fwd& b) {
+  Fwd r(a.v + b.v);
+  for (int i = 0; i < g_ndir; ++i) r.t[i] = a.t[i] + b.t[i];
+  return r;
+}
+inline Fwd operator-(const Fwd& a, const Fwd& b) {
+  Fwd r(a.v - b.v);
+  for (int i = 0; i < g_ndir; ++i) r.t[i] = a.t[i] - b.t[i];
+  return r;
+}
+inline Fwd operator*(const Fwd& a, const Fwd& b) {
+  Fwd r(a.v * b.v);
+  for (int i = 0; i < g_ndir; ++i) r.t[i] = a.t[i] * b.v + a.v * b.t[i];
+  return r;
+}
+inline Fwd operator/(const Fwd& a, const Fwd& b) {
+  Fwd r(a.v / b.v);
+  for (int i = 0; i < g_ndir; ++i) r.t[i] = (a.t[i] - r.v * b.t[i]) / b.v;
+  return r;
+}
+inline Fwd operator-(const Fwd& a) {
+  Fwd r(-a.v);
+  for (int i = 0; i < g_ndir; ++i) r.t[i] = -a.t[i];
+  return r;
+}
+inline Fwd fma3(const Fwd& a, const Fwd& b, const Fwd& c) {
+  Fwd r(std::fma(a.v, b.v, c.v));
+  for (int i = 0; i < g_ndir; ++i) r.t[i] = a.t[i] * b.v + a.v * b.t[i] + c.t[i];
+  return r;
+}
+inline Fwd tanh_(const Fwd& a) {
+  Fwd r(std::tanh(a.v));
+  for (int i = 0; i < g_ndir; ++i) r.t[i] = (1.0 - r.v * r.v) * a.t[i];
+  return r;
+}
+inline double rv(const Fwd& a) { return a.v; }
+inline Fwd abs_(const Fwd& a) { return a.v < 0.0 ? -a : a; }
+inline bool operator<(const Fwd& a, const Fwd& b) { return a.v < b.v; }
+inline bool operator>(const Fwd& a, const Fwd& b) { return a.v > b.v; }
 
 // Operation-counting scalar, used only to tally the arithmetic of a solve:
 // every +, -, *, / adds 1 to the thread's count, a fused multiply-add adds 2,
@@ -821,6 +877,40 @@ int oracle_replay_cs(int sys, int method, int64_t n, const double* theta, const 
       dyS[c * n + k] = a1[c].imag() / eps;
     }
   }
+  return 0;
+}
+
+// Forward-mode sensitivities of the replayed final state: S_theta[c][j][k] =
+// d y_S,c / d theta_j and (if not NULL) S_y0[c][j][k] = d y_S,c / d y0_j for
+// trajectory k, by the dual numbers above.  Per-trajectory parameters only.
+int oracle_sens_f64(int sys, int method, int64_t n, const double* theta, const double* y0,
+                    const int32_t* count, const double* h_rec, int64_t s_cap, double* S_theta,
+                    double* S_y0, double* yS, int nthreads) {
+  if (!valid_sys(sys, method) || n < 0 || sys == SYS_MLP) return 1;
+  const int d = SYS_D[sys], p = SYS_P[sys];
+  const int ndir = p + (S_y0 ? d : 0);
+  if (ndir > MAXDIR) return 1;
+  parallel_for(n, nthreads, [&](int, int64_t lo, int64_t hi) {
+    g_ndir = ndir;
+    Fwd th[MAXDIR], a0[MAXD], a1[MAXD];
+    for (int64_t k = lo; k < hi; ++k) {
+      for (int i = 0; i < p; ++i) {
+        th[i] = Fwd(theta[i * n + k]);
+        th[i].t[i] = 1.0;
+      }
+      for (int c = 0; c < d; ++c) {
+        a0[c] = Fwd(y0[c * n + k]);
+        if (S_y0) a0[c].t[p + c] = 1.0;
+      }
+      replay_one<Fwd>(sys, method, th, a0, count[k], h_rec + k * s_cap, a1);
+      for (int c = 0; c < d; ++c) {
+        if (yS) yS[c * n + k] = a1[c].v;
+        for (int j = 0; j < p; ++j) S_theta[(c * p + j) * n + k] = a1[c].t[j];
+        if (S_y0)
+          for (int j = 0; j < d; ++j) S_y0[(c * d + j) * n + k] = a1[c].t[p + j];
+      }
+    }
+  });
   return 0;
 }
 
