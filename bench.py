@@ -59,6 +59,18 @@ WORKLOADS = {
     "loghalo": dict(s_cap=8192, with_t=False, states=False, init=124, att=497, replay=378,
                     grad=_tsit5_grad(378, 6, 41), peak=78.6e12, bound="alu", cpu_n=2048),
 }
+# Forward sensitivities (solve_sens, Tsit5): per accepted step and parameter
+# direction, the stage tangents and the tangent update take 48 d flops, plus
+# six field JVPs; JVP_SUM is one JVP's flops summed over the p parameter
+# directions (decay 2, Lotka-Volterra 4 x 15, Lorenz 15 + 14 + 13, Robertson
+# 14 + 15 + 15, log halo 34 + 36 + 35).
+JVP_SUM = {"decay": 2, "lotka_volterra": 60, "lorenz63": 42, "robertson": 44, "loghalo": 105}
+
+
+def _sens_step_flops(d, p, name):
+    return 48 * d * p + 6 * JVP_SUM[name]
+
+
 # MI355X published peaks: FP64 vector 78.6 TFLOP/s (256 CU x 4 SIMD x 16 lanes x
 # 2 flop x 2.4 GHz); FP32 matrix (MFMA) 157.3 TFLOP/s.
 
@@ -74,6 +86,10 @@ def parse():
                          "Lotka-Volterra system at n = 1048576, where its 256-trajectory "
                          "ensemble cannot fill the chip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("gradient", "sens"), default="gradient",
+                    help="gradient: solve with record + replay-adjoint gradient (default); "
+                         "sens: solve with the forward sensitivities dy1/dtheta in the same "
+                         "kernel")
     ap.add_argument("--states", action="store_true",
                     help="record states in the solve; the gradient skips the forward replay")
     ap.add_argument("--cpu-sample", type=int, default=None,
@@ -125,6 +141,8 @@ def main():
 
     dev = torch.device("cuda:0")
     w = di.make(args.workload, args.n)
+    if args.mode == "sens":
+        return bench_sens(args, w)
     cfg = WORKLOADS[w.name]
     s_cap = cfg["s_cap"]
     th = torch.tensor(w.theta, device=dev)
@@ -257,6 +275,107 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample or cfg["cpu_n"], s_cap)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_sens(w, sample, s_cap):
+    """The oracle, as is: solve + dual-number forward sensitivities of a sample."""
+    import numpy as np
+
+    import dao_inputs as di
+    import oracle
+
+    nthreads = min(os.cpu_count() or 1, 16)
+    ws = di.subset(w, np.arange(min(sample, w.n)))
+    t0 = time.perf_counter()
+    r = oracle.solve(ws.system, ws.method, ws.theta, ws.y0, ws.t0, ws.t1, ws.rtol, ws.atol,
+                     s_cap=s_cap, dtype=ws.dtype, nthreads=nthreads)
+    oracle.sens(ws.system, ws.method, ws.theta, ws.y0, r["count"], r["h"], with_y0=False,
+                nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": ws.n / dt, "unit": "trajectories/s (solve + forward sensitivities)",
+            "cores": nthreads, "kind": "oracle",
+            "sample": f"first {ws.n} of the {w.n} {w.name} trajectories, full solve + dual-number "
+                      f"forward sensitivities on its mesh, {dt:.2f} s wall on {nthreads} threads"}
+
+
+def bench_sens(args, w):
+    """One step = dao_solve_sens: the adaptive solve with record and the forward
+    sensitivities S = dy1/dtheta integrated in the same kernel (application
+    paper arXiv 2609.28458 Sec. 2.3, Sec. 3)."""
+    import numpy as np
+    import torch
+
+    import differentiable_adaptive_ode_amd as dao
+    from differentiable_adaptive_ode_amd import api
+
+    dev = torch.device("cuda:0")
+    cfg = WORKLOADS[w.name]
+    s_cap = cfg["s_cap"]
+    th = torch.tensor(w.theta, device=dev)
+    y0 = torch.tensor(w.y0, device=dev)
+    bufs = api.alloc_record(w.n, s_cap, w.dtype, dev, with_t=cfg["with_t"])
+    y1 = torch.empty_like(y0)
+    S = torch.empty((w.d, w.theta.shape[0], w.n), dtype=y0.dtype, device=dev)
+    wsp = api.Workspace()
+
+    def run(ev, sens):
+        ev[0].record()
+        if sens:
+            dao.solve_sens(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=s_cap,
+                           out=y1, rec_buffers=bufs, workspace=wsp, out_sens=S)
+        else:
+            dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=s_cap,
+                      out=y1, rec_buffers=bufs, workspace=wsp)
+        ev[1].record()
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    for _ in range(max(args.warmup, 1)):
+        run(events(), True)
+        run(events(), False)
+    torch.cuda.synchronize()
+    plain = [events() for _ in range(args.steps)]
+    for e in plain:
+        run(e, False)
+    evs = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        run(e, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tk = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    tp = float(np.mean([e[0].elapsed_time(e[1]) for e in plain])) * 1e-3
+    cnt = bufs["count"].cpu().numpy().astype(np.int64)
+    nrej = bufs["nrej"].cpu().numpy().astype(np.int64)
+    if not np.all(bufs["status"].cpu().numpy() == 0):
+        raise SystemExit("bench: some trajectories failed")
+    attempts, steps_total = int((cnt + nrej).sum()), int(cnt.sum())
+    fl_solve = w.n * cfg["init"] + attempts * cfg["att"] + steps_total
+    fl_sens = steps_total * _sens_step_flops(w.d, w.theta.shape[0], w.name)
+    ach = (fl_solve + fl_sens) / tk
+    out = {
+        "metric": "forward-sensitivity trajectories/s (solve + dy1/dtheta in one kernel) at 1 GPU",
+        "value": w.n / (wall / args.steps),
+        "unit": "trajectories/s (solve with record + forward sensitivities)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name} ensemble, forward sensitivities", "n_trajectories": w.n,
+                   "method": w.method, "t_span": [w.t0, w.t1], "rtol": w.rtol, "atol": w.atol,
+                   "s_cap": s_cap, "directions": int(w.theta.shape[0])},
+        "solve_sens_ms": tk * 1e3, "solve_ms": tp * 1e3,
+        "accepted_steps_mean": float(cnt.mean()), "attempts_total": attempts,
+        "roofline": {"bound": cfg["bound"], "kernel": "solve_kernel (with sensitivities)",
+                     "launch_ms": tk * 1e3, "achieved": ach * 1e-12, "peak": cfg["peak"] * 1e-12,
+                     "unit": "TFLOP/s", "frac": ach / cfg["peak"], "traffic": None,
+                     "traffic_unit": "HBM bytes per launch"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_sens(w, args.cpu_sample or min(cfg["cpu_n"], 4096),
+                                                s_cap)
     print(json.dumps(out), flush=True)
 
 

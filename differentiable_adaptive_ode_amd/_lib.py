@@ -64,6 +64,13 @@ def _load():
     L.dao_grad_ordered.argtypes = [I, I, I, I64, P, P, ctypes.POINTER(dao_record), I64, P, P, P,
                                    P, SZ, P]
     L.dao_grad_ordered.restype = I
+    L.dao_solve_sens.argtypes = [I, I, I, I64, P, P, D, D, ctypes.POINTER(dao_tol), P,
+                                 ctypes.POINTER(dao_record), P, P, SZ, P]
+    L.dao_solve_sens.restype = I
+    L.dao_sens_workspace_size.argtypes = [I, I, I, I64, I64]
+    L.dao_sens_workspace_size.restype = SZ
+    L.dao_sens.argtypes = [I, I, I, I64, P, P, ctypes.POINTER(dao_record), I64, P, P, P, SZ, P]
+    L.dao_sens.restype = I
     L.dao_sqerr_cotangent.argtypes = [I, I64, I, I, P, P, D, P, P]
     L.dao_sqerr_cotangent.restype = I
     L.dao_last_error.argtypes = []
@@ -97,6 +104,25 @@ def dao_solve(system, method, dtype, n, theta, y0, t0, t1, tol, y1, rec, workspa
                          ctypes.byref(tol) if tol is not None else None, y1,
                          ctypes.byref(rec) if rec is not None else None, workspace, ws_bytes,
                          stream)
+
+
+def dao_solve_sens(system, method, dtype, n, theta, y0, t0, t1, tol, y1, rec, S_theta, workspace,
+                   ws_bytes, stream):
+    return lib.dao_solve_sens(system, method, dtype, n, theta, y0, t0, t1,
+                              ctypes.byref(tol) if tol is not None else None, y1,
+                              ctypes.byref(rec) if rec is not None else None, S_theta, workspace,
+                              ws_bytes, stream)
+
+
+def dao_sens_workspace_size(system, method, dtype, n, s_max):
+    return lib.dao_sens_workspace_size(system, method, dtype, n, s_max)
+
+
+def dao_sens(system, method, dtype, n, theta, y0, rec, s_max, S_theta, S_y0, workspace, ws_bytes,
+             stream):
+    return lib.dao_sens(system, method, dtype, n, theta, y0,
+                        ctypes.byref(rec) if rec is not None else None, s_max, S_theta, S_y0,
+                        workspace, ws_bytes, stream)
 
 
 def dao_grad_workspace_size(system, method, dtype, n, s_max):

@@ -122,7 +122,7 @@ def alloc_record(n: int, s_cap: int, dtype: str, device, with_t: bool = True,
 def solve(system: str, method: str, theta: torch.Tensor, y0: torch.Tensor, t0: float, t1: float,
           rtol: float, atol: float, dt0: float = 0.0, max_steps: int = 100000, s_cap: int = 4096,
           record_t: bool = True, record_states: bool = False, out=None, rec_buffers=None,
-          workspace=None, stream=None):
+          workspace=None, stream=None, out_sens=None, _sens=False):
     """Adaptive solve with record.  Returns (Record, y1).
 
     record_states: also keep the state at the start of every accepted step, so
@@ -150,9 +150,45 @@ def solve(system: str, method: str, theta: torch.Tensor, y0: torch.Tensor, t0: f
     buf = ws.get(nb, dev)
     tol = _lib.dao_tol(float(rtol), float(atol), float(dt0), int(max_steps))
     crec = rec.c_struct()
+    if _sens:
+        S = torch.empty((d, p, n), dtype=y0.dtype, device=dev) if out_sens is None else out_sens
+        _lib.check(_lib.dao_solve_sens(sysid, mid, did, n, _ptr(theta), _ptr(y0), float(t0),
+                                       float(t1), tol, _ptr(y1), crec, _ptr(S), _ptr(buf),
+                                       buf.numel(), _stream(stream)))
+        return rec, y1, S
     _lib.check(_lib.dao_solve(sysid, mid, did, n, _ptr(theta), _ptr(y0), float(t0), float(t1),
                               tol, _ptr(y1), crec, _ptr(buf), buf.numel(), _stream(stream)))
     return rec, y1
+
+
+def solve_sens(system: str, method: str, theta: torch.Tensor, y0: torch.Tensor, t0: float,
+               t1: float, rtol: float, atol: float, out_sens=None, **kw):
+    """solve() that also integrates the forward sensitivities S = dy1/dtheta
+    beside the state (steps chosen on the state alone).  Returns
+    (Record, y1, S) with S[d][p][n]; Tsit5, per-trajectory theta only."""
+    return solve(system, method, theta, y0, t0, t1, rtol, atol, out_sens=out_sens, _sens=True, **kw)
+
+
+def sens(rec: Record, theta: torch.Tensor | None = None, with_theta: bool = True,
+         with_y0: bool = False, s_max: int | None = None, workspace=None, stream=None):
+    """Forward sensitivities of y1 through the replay of rec's mesh:
+    (S_theta [d][p][n] or None, S_y0 [d][d][n] or None)."""
+    th = rec.theta if theta is None else theta
+    _check_dev(th)
+    n = rec.n
+    d, p, _ = _lib.dao_system_dims(_lib.SYSTEMS[rec.system])
+    if s_max is None:
+        s_max = int(rec.count.max().item()) if n > 0 else 0
+    s_max = min(int(s_max), rec.s_cap)
+    ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
+    dev = rec.count.device
+    S_th = torch.empty((d, p, n), dtype=rec.y0.dtype, device=dev) if with_theta else None
+    S_y0 = torch.empty((d, d, n), dtype=rec.y0.dtype, device=dev) if with_y0 else None
+    nb = _lib.dao_sens_workspace_size(*ids, n, s_max)
+    buf = _ws(dev, workspace).get(nb, dev)
+    _lib.check(_lib.dao_sens(*ids, n, _ptr(th), _ptr(rec.y0), rec.c_struct(states=False), s_max,
+                             _ptr(S_th), _ptr(S_y0), _ptr(buf), buf.numel(), _stream(stream)))
+    return S_th, S_y0
 
 
 def _grad_setup(rec: Record, s_max, workspace, device):

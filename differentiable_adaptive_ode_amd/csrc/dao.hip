@@ -168,11 +168,12 @@ int64_t resident_blocks(K kernel, size_t lds = 0) {
 }
 
 // --------------------------------------------------------- typed launchers
-template <class R, class Sys, int M>
+template <class R, class Sys, int M, bool SENS = false>
 dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0, double t1,
                         const dao_tol* tol, void* y1, const dao_record* rec, void* ws,
-                        hipStream_t stream) {
+                        hipStream_t stream, void* S_theta = nullptr) {
   SolveArgs<R> a;
+  a.S_theta = (R*)S_theta;
   a.n = n;
   a.theta = (const R*)theta;
   a.y0 = (const R*)y0;
@@ -193,7 +194,7 @@ dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0,
   a.queue = (unsigned long long*)ws;
   a.trash = (R*)((char*)ws + ALIGN);
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)ws, (int64_t)2, 0u);
-  auto kern = solve_kernel<R, Sys, M>;
+  auto kern = solve_kernel<R, Sys, M, SENS>;
   // record staging ring: (t, h [, y]) x 8 slots x 64 lanes per wavefront
   const size_t lds = (size_t)BLOCK_WAVES * (rec->y ? 2 + Sys::D : 2) * 8 * WAVE * sizeof(R);
   int64_t blocks = (n + BLOCK - 1) / BLOCK;
@@ -279,6 +280,45 @@ dao_status launch_grad(int mode, int64_t n, const void* theta, const void* y0, c
   a.groups = groups;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), 0, stream, a);
   return check_hip(hipGetLastError(), "grad kernel launch");
+}
+
+// Forward sensitivities through the replay: the record's trajectories are
+// sorted once, then one pass of sens_kernel per P directions (the
+// parameters, then the initial-state components).
+template <class R, class Sys>
+dao_status launch_sens(int64_t n, const void* theta, const void* y0, const dao_record* rec,
+                       int64_t s_max, void* S_theta, void* S_y0, void* ws, hipStream_t stream) {
+  constexpr int D = Sys::D, P = Sys::P;
+  char* base = (char*)ws;
+  unsigned long long* groups = (unsigned long long*)base;
+  uint32_t* hist = (uint32_t*)(base + align_up(16));
+  int32_t* perm = (int32_t*)(base + align_up(16) + align_up((size_t)ORDER_BINS * 4));
+  auto kern = sens_kernel<R, Sys, P>;
+  const int64_t ngroups = (n + WAVE - 1) / WAVE;
+  int64_t blocks = (ngroups + BLOCK / WAVE - 1) / (BLOCK / WAVE);
+  const int64_t res = resident_blocks(kern);
+  if (blocks > res) blocks = res;
+  launch_order(rec->count, n, s_max, hist, perm, stream);
+  SensArgs<R> a;
+  a.n = n;
+  a.theta = (const R*)theta;
+  a.y0 = (const R*)y0;
+  a.s_cap = rec->s_cap;
+  a.h_rec = (const R*)rec->h;
+  a.count = rec->count;
+  a.status = rec->status;
+  a.s_max = s_max;
+  a.S_theta = (R*)S_theta;
+  a.S_y0 = (R*)S_y0;
+  a.perm = perm;
+  a.groups = groups;
+  const int first = S_theta ? 0 : P, last = S_y0 ? P + D : P;
+  for (int d0 = first; d0 < last; d0 += P) {
+    a.dir0 = d0;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)groups, (int64_t)2, 0u);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), 0, stream, a);
+  }
+  return check_hip(hipGetLastError(), "sensitivity kernel launch");
 }
 
 // ------------------------------------------------- neural right-hand side
@@ -388,6 +428,21 @@ struct Entry {
                          size_t wsb, hipStream_t st) {
     return launch_grad<R, S<R>, M>(mode, n, th, y0, rec, s_max, g, dth, dy0, ws, wsb, st);
   }
+  static dao_status solve_sens(int64_t n, const void* th, const void* y0, double t0, double t1,
+                               const dao_tol* tol, void* y1, const dao_record* rec, void* ws,
+                               hipStream_t st, void* S_theta) {
+    if constexpr (M == M_TSIT5)
+      return launch_solve<R, S<R>, M, true>(n, th, y0, t0, t1, tol, y1, rec, ws, st, S_theta);
+    else
+      return DAO_EUNSUPPORTED;
+  }
+  static dao_status sens(int64_t n, const void* th, const void* y0, const dao_record* rec,
+                         int64_t s_max, void* S_theta, void* S_y0, void* ws, hipStream_t st) {
+    if constexpr (M == M_TSIT5)
+      return launch_sens<R, S<R>>(n, th, y0, rec, s_max, S_theta, S_y0, ws, st);
+    else
+      return DAO_EUNSUPPORTED;
+  }
   static size_t slot_bytes(int64_t s_max) { return grad_slot_bytes<R, S<R>::D>(s_max); }
   static int64_t resident_waves() {
     return resident_blocks(grad_kernel<R, S<R>, M>) * (BLOCK / WAVE);
@@ -398,6 +453,11 @@ typedef dao_status (*solve_fn)(int64_t, const void*, const void*, double, double
                                void*, const dao_record*, void*, hipStream_t);
 typedef dao_status (*grad_fn)(int, int64_t, const void*, const void*, const dao_record*, int64_t,
                               const void*, void*, void*, void*, size_t, hipStream_t);
+typedef dao_status (*solve_sens_fn)(int64_t, const void*, const void*, double, double,
+                                    const dao_tol*, void*, const dao_record*, void*, hipStream_t,
+                                    void*);
+typedef dao_status (*sens_fn)(int64_t, const void*, const void*, const dao_record*, int64_t, void*,
+                              void*, void*, hipStream_t);
 typedef size_t (*slot_fn)(int64_t);
 typedef int64_t (*res_fn)();
 
@@ -407,14 +467,18 @@ struct Impl {
   slot_fn slot;
   res_fn resident;
   int group;  // trajectories per wavefront in the gradient
+  solve_sens_fn solve_sens;  // forward sensitivities (Tsit5, per-trajectory theta), else null
+  sens_fn sens;
 };
 
 int64_t mlp_resident_waves() { return resident_blocks(mlp::grad_kernel) * (BLOCK / WAVE); }
 
 template <class R, template <class> class S, int M>
 Impl make_impl() {
+  const bool fwd = (M == M_TSIT5);
   return Impl{&Entry<R, S, M>::solve, &Entry<R, S, M>::grad, &Entry<R, S, M>::slot_bytes,
-              &Entry<R, S, M>::resident_waves, WAVE};
+              &Entry<R, S, M>::resident_waves, WAVE,
+              fwd ? &Entry<R, S, M>::solve_sens : nullptr, fwd ? &Entry<R, S, M>::sens : nullptr};
 }
 
 const Impl* find_impl(int sys, int method, int dtype) {
@@ -443,7 +507,8 @@ const Impl* find_impl(int sys, int method, int dtype) {
     table[DAO_SYS_LOGHALO][M_TSIT5][DAO_F64] = make_impl<double, LogHalo, M_TSIT5>();
     table[DAO_SYS_LOGHALO][M_TSIT5][DAO_F32] = make_impl<float, LogHalo, M_TSIT5>();
     table[DAO_SYS_MLP][M_TSIT5][DAO_F32] =
-        Impl{&launch_mlp_solve, &launch_mlp_grad, &mlp_slot_bytes, &mlp_resident_waves, mlp::SLOTS};
+        Impl{&launch_mlp_solve, &launch_mlp_grad, &mlp_slot_bytes, &mlp_resident_waves, mlp::SLOTS,
+             nullptr, nullptr};
     init = true;
   }
   if (!sys_ok(sys) || method < 0 || method > 1 || dtype < 0 || dtype > 1) return nullptr;
@@ -475,46 +540,109 @@ size_t dao_solve_workspace_size(dao_system sys, dao_method method, dao_dtype dty
   return ALIGN + align_up((size_t)WAVE * 2 * sizeof(double));  // queue counter + trash slots
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the solve's entry points; S_theta (the forward
+// sensitivities) is non-null only for dao_solve_sens, whose name `fn` then is.
+dao_status solve_call(const char* fn, dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                      const void* theta, const void* y0, double t0, double t1, const dao_tol* tol,
+                      void* y1, const dao_record* rec, void* S_theta, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  const bool sens = std::strcmp(fn, "dao_solve_sens") == 0;
+  g_err[0] = 0;
+  if (!sys_ok(sys)) return fail(DAO_EINVAL, "%s: unknown system %d", fn, (int)sys);
+  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
+    return fail(DAO_EINVAL, "%s: unknown method %d", fn, (int)method);
+  if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+  if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "%s: n = %lld out of range", fn, (long long)n);
+  if (!tol) return fail(DAO_EINVAL, "%s: tol is NULL", fn);
+  if (!(is_fin(t0) && is_fin(t1))) return fail(DAO_EINVAL, "%s: t0/t1 not finite", fn);
+  if (!(t1 >= t0)) return fail(DAO_EINVAL, "%s: t1 < t0", fn);
+  if (!(tol->rtol > 0) || !is_fin(tol->rtol)) return fail(DAO_EINVAL, "%s: rtol must be > 0", fn);
+  if (!(tol->atol > 0) || !is_fin(tol->atol)) return fail(DAO_EINVAL, "%s: atol must be > 0", fn);
+  if (!is_fin(tol->dt0)) return fail(DAO_EINVAL, "%s: dt0 not finite", fn);
+  if (tol->max_steps < 1) return fail(DAO_EINVAL, "%s: max_steps must be >= 1", fn);
+  const Impl* im = find_impl(sys, method, dtype);
+  if (!im || (sens && !im->solve_sens))
+    return fail(DAO_EUNSUPPORTED, "%s: system %d with method %d dtype %d is not provided", fn,
+                (int)sys, (int)method, (int)dtype);
+  if (n == 0) return DAO_OK;
+  if (!theta) return fail(DAO_EINVAL, "%s: theta is NULL", fn);
+  if (!y0) return fail(DAO_EINVAL, "%s: y0 is NULL", fn);
+  if (!y1) return fail(DAO_EINVAL, "%s: y1 is NULL", fn);
+  if (sens && !S_theta) return fail(DAO_EINVAL, "%s: S_theta is NULL", fn);
+  if (!rec) return fail(DAO_EINVAL, "%s: rec is NULL (count and status are written there)", fn);
+  if (rec->s_cap < 0) return fail(DAO_EINVAL, "%s: rec->s_cap < 0", fn);
+  if (!rec->count) return fail(DAO_EINVAL, "%s: rec->count is NULL", fn);
+  if (!rec->status) return fail(DAO_EINVAL, "%s: rec->status is NULL", fn);
+  if (rec->s_cap > 0 && !rec->h) return fail(DAO_EINVAL, "%s: rec->h is NULL", fn);
+  if (rec->y && sys == DAO_SYS_MLP)
+    return fail(DAO_EUNSUPPORTED, "%s: recorded states (rec->y) are not provided for the neural field", fn);
+  if (!workspace || workspace_bytes < dao_solve_workspace_size(sys, method, dtype, n))
+    return fail(DAO_EWORKSPACE, "%s: workspace needs %zu bytes", fn,
+                dao_solve_workspace_size(sys, method, dtype, n));
+  if (sens)
+    return im->solve_sens(n, theta, y0, t0, t1, tol, y1, rec, workspace, (hipStream_t)stream, S_theta);
+  return im->solve(n, theta, y0, t0, t1, tol, y1, rec, workspace, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
 dao_status dao_solve(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
                      const void* theta, const void* y0, double t0, double t1, const dao_tol* tol,
                      void* y1, const dao_record* rec, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  g_err[0] = 0;
-  if (!sys_ok(sys)) return fail(DAO_EINVAL, "dao_solve: unknown system %d", (int)sys);
-  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
-    return fail(DAO_EINVAL, "dao_solve: unknown method %d", (int)method);
-  if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "dao_solve: unknown dtype %d", (int)dtype);
-  if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "dao_solve: n = %lld out of range", (long long)n);
-  if (!tol) return fail(DAO_EINVAL, "dao_solve: tol is NULL");
-  if (!(is_fin(t0) && is_fin(t1))) return fail(DAO_EINVAL, "dao_solve: t0/t1 not finite");
-  if (!(t1 >= t0)) return fail(DAO_EINVAL, "dao_solve: t1 < t0");
-  if (!(tol->rtol > 0) || !is_fin(tol->rtol)) return fail(DAO_EINVAL, "dao_solve: rtol must be > 0");
-  if (!(tol->atol > 0) || !is_fin(tol->atol)) return fail(DAO_EINVAL, "dao_solve: atol must be > 0");
-  if (!is_fin(tol->dt0)) return fail(DAO_EINVAL, "dao_solve: dt0 not finite");
-  if (tol->max_steps < 1) return fail(DAO_EINVAL, "dao_solve: max_steps must be >= 1");
+  return solve_call("dao_solve", sys, method, dtype, n, theta, y0, t0, t1, tol, y1, rec, nullptr,
+                    workspace, workspace_bytes, stream);
+}
+
+dao_status dao_solve_sens(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                          const void* theta, const void* y0, double t0, double t1,
+                          const dao_tol* tol, void* y1, const dao_record* rec, void* S_theta,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return solve_call("dao_solve_sens", sys, method, dtype, n, theta, y0, t0, t1, tol, y1, rec,
+                    S_theta, workspace, workspace_bytes, stream);
+}
+
+size_t dao_sens_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                               int64_t s_max) {
   const Impl* im = find_impl(sys, method, dtype);
-  if (!im) return fail(DAO_EUNSUPPORTED, "dao_solve: system %d with method %d dtype %d is not provided",
-                       (int)sys, (int)method, (int)dtype);
+  if (!im || !im->sens || n < 0 || s_max < 0) return 0;
+  return grad_header_bytes(n, s_max);
+}
+
+dao_status dao_sens(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                    const void* theta, const void* y0, const dao_record* rec, int64_t s_max,
+                    void* S_theta, void* S_y0, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  const char* fn = "dao_sens";
+  g_err[0] = 0;
+  if (!sys_ok(sys)) return fail(DAO_EINVAL, "%s: unknown system %d", fn, (int)sys);
+  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
+    return fail(DAO_EINVAL, "%s: unknown method %d", fn, (int)method);
+  if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+  if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "%s: n = %lld out of range", fn, (long long)n);
+  if (!rec) return fail(DAO_EINVAL, "%s: rec is NULL", fn);
+  if (rec->s_cap < 0) return fail(DAO_EINVAL, "%s: rec->s_cap < 0", fn);
+  if (s_max < 0 || s_max > rec->s_cap) return fail(DAO_EINVAL, "%s: s_max must be in [0, rec->s_cap]", fn);
+  const Impl* im = find_impl(sys, method, dtype);
+  if (!im || !im->sens)
+    return fail(DAO_EUNSUPPORTED, "%s: system %d with method %d dtype %d is not provided", fn,
+                (int)sys, (int)method, (int)dtype);
   if (n == 0) return DAO_OK;
-  if (!theta) return fail(DAO_EINVAL, "dao_solve: theta is NULL");
-  if (!y0) return fail(DAO_EINVAL, "dao_solve: y0 is NULL");
-  if (!y1) return fail(DAO_EINVAL, "dao_solve: y1 is NULL");
-  dao_record none;
-  std::memset(&none, 0, sizeof(none));
-  if (rec) {
-    if (rec->s_cap < 0) return fail(DAO_EINVAL, "dao_solve: rec->s_cap < 0");
-    if (!rec->count) return fail(DAO_EINVAL, "dao_solve: rec->count is NULL");
-    if (!rec->status) return fail(DAO_EINVAL, "dao_solve: rec->status is NULL");
-    if (rec->s_cap > 0 && !rec->h) return fail(DAO_EINVAL, "dao_solve: rec->h is NULL");
-  } else {
-    return fail(DAO_EINVAL, "dao_solve: rec is NULL (count and status are written there)");
-  }
-  if (rec->y && sys == DAO_SYS_MLP)
-    return fail(DAO_EUNSUPPORTED, "dao_solve: recorded states (rec->y) are not provided for the neural field");
-  if (!workspace || workspace_bytes < dao_solve_workspace_size(sys, method, dtype, n))
-    return fail(DAO_EWORKSPACE, "dao_solve: workspace needs %zu bytes",
-                dao_solve_workspace_size(sys, method, dtype, n));
-  return im->solve(n, theta, y0, t0, t1, tol, y1, rec, workspace, (hipStream_t)stream);
+  if (!S_theta && !S_y0) return fail(DAO_EINVAL, "%s: S_theta and S_y0 are both NULL", fn);
+  if (!theta) return fail(DAO_EINVAL, "%s: theta is NULL", fn);
+  if (!y0) return fail(DAO_EINVAL, "%s: y0 is NULL", fn);
+  if (!rec->count) return fail(DAO_EINVAL, "%s: rec->count is NULL", fn);
+  if (s_max > 0 && !rec->h) return fail(DAO_EINVAL, "%s: rec->h is NULL", fn);
+  const size_t need = dao_sens_workspace_size(sys, method, dtype, n, s_max);
+  if (!workspace || workspace_bytes < need)
+    return fail(DAO_EWORKSPACE, "%s: workspace needs at least %zu bytes", fn, need);
+  return im->sens(n, theta, y0, rec, s_max, S_theta, S_y0, workspace, (hipStream_t)stream);
 }
 
 size_t dao_grad_workspace_min(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,

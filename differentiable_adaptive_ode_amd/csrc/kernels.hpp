@@ -43,6 +43,7 @@ struct SolveArgs {
   R* y_rec;  // optional [n][s_cap][D]: the state at the start of each accepted step
   unsigned long long* queue;
   R* trash;  // [64][2] scratch target of record stores that have no row
+  R* S_theta;  // forward sensitivities dy1/dtheta [D][P][n] (solve_kernel<..., true>)
 };
 
 template <class R>
@@ -109,9 +110,19 @@ __device__ R initial_step(const Sys& sys, const R (&y0)[Sys::D], const R (&f0)[S
   return truncBits((h1 < h100) ? h1 : h100);
 }
 
-template <class R, class Sys, int METHOD>
+// SENS: also integrate the forward sensitivities S = dy/dtheta beside the
+// state, with the steps chosen on the state alone (arXiv 2609.28458 Sec. 2.3
+// and Sec. 3; Tsit5 only).  S starts at zero, takes the tangent of every
+// accepted step and is written to S_theta when the trajectory finishes.
+template <class R, class Sys, int METHOD, bool SENS = false>
 __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   constexpr int D = Sys::D;
+  static_assert(!SENS || METHOD == M_TSIT5, "forward sensitivities are Tsit5 only");
+  constexpr int NS = SENS ? Sys::P : 1;
+  R Sv[D][NS];
+  int sdir[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) sdir[j] = j;
   constexpr int ORDER = (METHOD == M_TSIT5) ? 5 : 2;
   constexpr int CTRL_Q = (METHOD == M_TSIT5) ? 10 : 6;  // msq^(-1/Q) = err^(-1/(ORDER+1))
   constexpr int32_t RUNNING = -1;
@@ -162,6 +173,13 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     a.count[traj] = nacc;
     if (a.nrej) a.nrej[traj] = nrej;
     a.status[traj] = st;
+    if constexpr (SENS) {
+#pragma unroll
+      for (int c = 0; c < D; ++c)
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+          a.S_theta[(c * NS + j) * a.n + traj] = (st == TRAJ_OK) ? Sv[c][j] : nanR(R(0));
+    }
     if (staged) {
       const int32_t lo = nacc & ~(STAGE - 1);
       for (int32_t r = lo; r < nacc; ++r) {
@@ -210,6 +228,12 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
           t = a.t0;
           nacc = 0;
           nrej = 0;
+          if constexpr (SENS) {
+#pragma unroll
+            for (int c = 0; c < D; ++c)
+#pragma unroll
+              for (int j = 0; j < NS; ++j) Sv[c][j] = R(0);
+          }
           attempts = 0;
           prev_rej = false;
           if (!(a.t1 > a.t0)) {
@@ -279,6 +303,9 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
 
     const bool take = (st == RUNNING) && acc;
     const R tn = last ? a.t1 : t + hs;
+    if constexpr (SENS) {
+      if (take) tsit5::tangent<R, Sys, NS>(C5, sys, y, hs, k, sdir, Sv);
+    }
 #pragma unroll
     for (int c = 0; c < D; ++c) y[c] = take ? ynew[c] : y[c];
     if constexpr (METHOD == M_TSIT5) {
@@ -467,6 +494,114 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
       if (a.dLdy0) {
 #pragma unroll
         for (int c = 0; c < D; ++c) a.dLdy0[c * a.n + k] = lam[c];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Forward sensitivities through the replay of a record (arXiv 2609.28458
+// Sec. 2.3; arXiv 2609.02876 Sec. 3.1 replays the recorded steps): per
+// trajectory, the tangent of y_{j+1} = Phi(y_j; h_j, theta) along NT
+// directions dir0 .. dir0 + NT - 1 of (theta_0 .. theta_{P-1}, y0_0 ..
+// y0_{D-1}); directions past the last are carried as zero columns and not
+// written.  Trajectories are visited in the gradient's sorted groups of 64.
+template <class R>
+struct SensArgs {
+  int64_t n;
+  const R* theta;
+  const R* y0;
+  int64_t s_cap;
+  const R* h_rec;
+  const int32_t* count;
+  const int32_t* status;
+  int64_t s_max;
+  R* S_theta;  // [D][P][n] or null
+  R* S_y0;     // [D][D][n] or null
+  int dir0;    // first direction of this pass
+  const int32_t* perm;
+  unsigned long long* groups;
+};
+
+template <class R, class Sys, int NT>
+__global__ void __launch_bounds__(256) sens_kernel(SensArgs<R> a) {
+  constexpr int D = Sys::D, P = Sys::P;
+  const int lane = laneId();
+  const tsit5::Coef<R> C5 = tsit5::Coef<R>::literal();
+  int dir[NT], pdir[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    dir[t] = a.dir0 + t;
+    pdir[t] = dir[t] < P ? dir[t] : -1;  // parameter index, or none
+  }
+  const unsigned long long ngroups = (unsigned long long)((a.n + WAVE - 1) / WAVE);
+  for (;;) {
+    unsigned long long g = 0;
+    if (lane == 0) g = atomicAdd(a.groups, 1ull);
+    g = __shfl(g, 0);
+    if (g >= ngroups) break;
+    const int64_t idx = (int64_t)g * WAVE + lane;
+    int64_t k = -1;
+    int cnt = 0;
+    bool ok = false;
+    if (idx < a.n) {
+      k = a.perm ? (int64_t)a.perm[idx] : idx;
+      if (k < 0 || k >= a.n) {
+        k = -1;
+      } else {
+        cnt = a.count[k];
+        ok = cnt >= 0 && cnt <= a.s_max && (a.status == nullptr || a.status[k] == TRAJ_OK);
+        if (!ok) cnt = 0;
+      }
+    }
+    int mx = cnt;
+#pragma unroll
+    for (int off = WAVE / 2; off > 0; off >>= 1) {
+      const int o = __shfl_xor(mx, off);
+      mx = (o > mx) ? o : mx;
+    }
+    Sys sys;
+    sys.load(a.theta, a.n, k >= 0 ? k : 0);
+    R y[D], S[D][NT];
+    const R* hrow = a.h_rec;
+#pragma unroll
+    for (int c = 0; c < D; ++c) y[c] = (k >= 0) ? a.y0[c * a.n + k] : R(0);
+    if (k >= 0) hrow = a.h_rec + k * a.s_cap;
+#pragma unroll
+    for (int c = 0; c < D; ++c)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) S[c][t] = (dir[t] - P == c) ? R(1) : R(0);
+    // Lockstep steps; past a lane's count h = 0, which leaves y and S
+    // unchanged.  h is loaded one step ahead.
+    R h_nx = (mx > 0) ? hrow[0] : R(0);
+    for (int i = 0; i < mx; ++i) {
+      const R hj = (i < cnt) ? h_nx : R(0);
+      if (i + 1 < mx) h_nx = hrow[i + 1];
+      R kk[7][D], Y[D];
+      sys.f(y, kk[0]);
+#pragma unroll
+      for (int st = 1; st < 6; ++st) {
+        tsit5::stage_state<R, D>(C5, st, y, hj, kk, Y);
+        sys.f(Y, kk[st]);
+      }
+      tsit5::tangent<R, Sys, NT>(C5, sys, y, hj, kk, pdir, S);
+      tsit5::stage_state<R, D>(C5, 6, y, hj, kk, Y);
+#pragma unroll
+      for (int c = 0; c < D; ++c) y[c] = Y[c];
+    }
+    if (k >= 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int d = dir[t];
+#pragma unroll
+        for (int c = 0; c < D; ++c) {
+          const R v = ok ? S[c][t] : nanR(R(0));
+          if (d < P) {
+            if (a.S_theta) a.S_theta[(c * P + d) * a.n + k] = v;
+          } else if (d < P + D) {
+            if (a.S_y0) a.S_y0[(c * D + (d - P)) * a.n + k] = v;
+          }
+        }
       }
     }
   }

@@ -10,6 +10,10 @@
 //                          (the Jacobian's own dependence, needed by the
 //                          Rosenbrock adjoint; arXiv 2609.02876 Sec. 3.2 notes
 //                          the backward sweep differentiates through J)
+//   jvp(y, yd, j, fd)      fd = (df/dy) yd + df/dtheta_j (no parameter term for
+//                          j outside [0, P)): one column of the sensitivity
+//                          equations S' = (df/dy) S + df/dtheta (arXiv
+//                          2609.28458 Sec. 2.3)
 // The vector-Jacobian products are derived by hand from the formulas below.
 #pragma once
 
@@ -32,6 +36,9 @@ struct Decay {
   __device__ void jac_vjp(const R (&y)[D], const R (&Jb)[D][D], R (&yb)[D], R (&pb)[P]) const {
     (void)y; (void)yb;
     pb[0] -= Jb[0][0];
+  }
+  __device__ void jvp(const R (&y)[D], const R (&yd)[D], int j, R (&fd)[D]) const {
+    fd[0] = (j == 0) ? -fmaR(th, yd[0], y[0]) : -(th * yd[0]);
   }
 };
 
@@ -71,6 +78,13 @@ struct LotkaVolterra {
     pb[2] -= Jb[1][1];
     pb[3] += fmaR(y[1], Jb[1][0], y[0] * Jb[1][1]);
   }
+  __device__ void jvp(const R (&y)[D], const R (&yd)[D], int j, R (&fd)[D]) const {
+    const R y12 = y[0] * y[1];
+    R p0 = (j == 0) ? y[0] : (j == 1) ? -y12 : R(0);
+    R p1 = (j == 2) ? -y[1] : (j == 3) ? y12 : R(0);
+    fd[0] = fmaR(fmaR(-b, y[1], a), yd[0], fmaR(-(b * y[0]), yd[1], p0));
+    fd[1] = fmaR(d * y[1], yd[0], fmaR(fmaR(d, y[0], -g), yd[1], p1));
+  }
 };
 
 // Lorenz-63, theta = (sigma, rho, beta).
@@ -108,6 +122,12 @@ struct Lorenz63 {
     pb[0] += Jb[0][1] - Jb[0][0];
     pb[1] += Jb[1][0];
     pb[2] -= Jb[2][2];
+  }
+  __device__ void jvp(const R (&y)[D], const R (&yd)[D], int j, R (&fd)[D]) const {
+    const R d10 = yd[1] - yd[0];
+    fd[0] = (j == 0) ? fmaR(s, d10, y[1] - y[0]) : s * d10;
+    fd[1] = fmaR(r - y[2], yd[0], fmaR(-y[0], yd[2], (j == 1) ? y[0] - yd[1] : -yd[1]));
+    fd[2] = fmaR(y[1], yd[0], fmaR(y[0], yd[1], -fmaR(b, yd[2], (j == 2) ? y[2] : R(0))));
   }
 };
 
@@ -157,6 +177,15 @@ struct Robertson {
     pb[0] += Jb[1][0] - Jb[0][0];
     pb[1] += (R(2) * y[1]) * w21;
     pb[2] += fmaR(y[2], w01, y[1] * w02);
+  }
+  __device__ void jvp(const R (&y)[D], const R (&yd)[D], int j, R (&fd)[D]) const {
+    // tangents of a = k1 y1, b = k2 y2^2, c = k3 y2 y3
+    const R ad = fmaR(k1, yd[0], (j == 0) ? y[0] : R(0));
+    const R bd = fmaR((R(2) * k2) * y[1], yd[1], (j == 1) ? y[1] * y[1] : R(0));
+    const R cd = fmaR(k3, fmaR(y[2], yd[1], y[1] * yd[2]), (j == 2) ? y[1] * y[2] : R(0));
+    fd[0] = cd - ad;
+    fd[1] = (ad - bd) - cd;
+    fd[2] = bd;
   }
 };
 
@@ -230,6 +259,25 @@ struct LogHalo {
   __device__ void jac_vjp(const R (&y)[D], const R (&Jb)[D][D], R (&yb)[D], R (&pb)[P]) const {
     // Not used: the halo has no Rosenbrock path (dao_solve/dao_grad refuse it).
     (void)y; (void)Jb; (void)yb; (void)pb;
+  }
+  // a = -A g: ad = -(Ad g + A gd) with Dnd = 2 <g, (xd, yd, zd)> + dRc^2 + z^2 d(1/q^2),
+  // Ad = d(v0^2) / Dn - A Dnd / Dn, gd = (xd, yd, zd / q^2 + z d(1/q^2)).
+  __device__ void jvp(const R (&y)[D], const R (&yd)[D], int j, R (&fd)[D]) const {
+    const R zq = y[2] * iq2;
+    const R Dn = fmaR(y[0], y[0], fmaR(y[1], y[1], fmaR(y[2], zq, r2)));
+    const R iD = R(1) / Dn;
+    const R A = v2 * iD;
+    const R diq2 = (j == 2) ? (R(-2) * iq2) / q : R(0);  // d(1/q^2)/dq
+    const R gzd = fmaR(yd[2], iq2, y[2] * diq2);
+    R Dnd = R(2) * fmaR(y[0], yd[0], fmaR(y[1], yd[1], zq * yd[2]));
+    Dnd = fmaR(y[2] * y[2], diq2, (j == 1) ? fmaR(R(2) * rc, R(1), Dnd) : Dnd);
+    const R Ad = fmaR(-A, Dnd, (j == 0) ? R(2) * v0 : R(0)) * iD;
+    fd[0] = yd[3];
+    fd[1] = yd[4];
+    fd[2] = yd[5];
+    fd[3] = -fmaR(Ad, y[0], A * yd[0]);
+    fd[4] = -fmaR(Ad, y[1], A * yd[1]);
+    fd[5] = -fmaR(Ad, zq, A * gzd);
   }
 };
 

@@ -139,6 +139,58 @@ __device__ __forceinline__ void replay(const Coef<R>& C, const Sys& sys, R (&y)[
   for (int c = 0; c < D; ++c) y[c] = Y[c];
 }
 
+// Forward sensitivities through one step (arXiv 2609.28458 Sec. 2.3: the
+// sensitivity equations integrated beside the state with the state's own
+// steps; with the steps held fixed this is the exact tangent of the step).
+// On entry S[c][t] = dy_c/dp_t for NT directions, direction t being the
+// parameter dir[t] (or none, for an initial-state direction: dir[t] < 0 or
+// >= P); k[0..5] are the step's stage derivatives at (y, h).  On exit S holds
+// the tangent of y_new.  Stage tangents: Yd_i = S + h sum_j a_ij K_j,
+// K_i = (df/dy)(Y_i) Yd_i + df/dtheta_dir(Y_i).
+template <class R, class Sys, int NT>
+__device__ __forceinline__ void tangent(const Coef<R>& C, const Sys& sys, const R (&y)[Sys::D],
+                                        R h, const R (&k)[7][Sys::D], const int (&dir)[NT],
+                                        R (&S)[Sys::D][NT]) {
+  constexpr int D = Sys::D;
+  R K[6][NT][D];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    R Y[D];
+    if (i == 0) {
+#pragma unroll
+      for (int c = 0; c < D; ++c) Y[c] = y[c];
+    } else {
+      stage_state<R, D>(C, i, y, h, k, Y);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      R Yd[D];
+#pragma unroll
+      for (int c = 0; c < D; ++c) {
+        if (i == 0) {
+          Yd[c] = S[c][t];
+        } else {
+          R acc = C.a[i][0] * K[0][t][c];
+#pragma unroll
+          for (int j = 1; j < 5; ++j)
+            if (j < i) acc = fmaR(C.a[i][j], K[j][t][c], acc);
+          Yd[c] = fmaR(h, acc, S[c][t]);
+        }
+      }
+      sys.jvp(Y, Yd, dir[t], K[i][t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      R acc = C.a[6][0] * K[0][t][c];
+#pragma unroll
+      for (int j = 1; j < 6; ++j) acc = fmaR(C.a[6][j], K[j][t][c], acc);
+      S[c][t] = fmaR(h, acc, S[c][t]);
+    }
+}
+
 // Reverse of one replay step, in two parts.  The stage states depend only
 // on y_j and h_j (store-the-state, recompute-the-stages, as the in-kernel
 // adjoint of Sec. 3.3 does); the sweep takes lam = dL/dy_{j+1} to

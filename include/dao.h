@@ -188,6 +188,47 @@ dao_status dao_grad_ordered(dao_system sys, dao_method method, dao_dtype dtype, 
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward sensitivities of the final state, S = dy1/dtheta (and dy1/dy0):
+ * the derivatives the application paper (arXiv 2609.28458, "Differentiable
+ * astrophysics at scale") obtains in the same kernel as the solve by
+ * integrating the sensitivity equations S' = (df/dy) S + df/dtheta beside the
+ * state, with the step size chosen on the state alone (its Sec. 2.3 and
+ * Sec. 3; eq. 2).  With the steps held fixed that is the exact derivative of
+ * the discrete solution on the recorded mesh, the same quantity the forward
+ * mode through the replay of the record gives (gradsolve Sec. 3.1).  Tsit5
+ * with per-trajectory parameters only: DAO_EUNSUPPORTED for Rosenbrock23
+ * and for the neural field (whose 4740 shared weights are a reverse-mode
+ * case).  Layouts: S_theta real[d][p][n] with S_theta[(c p + j) n + k] =
+ * dy1_c/dtheta_j of trajectory k; S_y0 real[d][d][n] likewise.  Failed
+ * trajectories get NaN.
+ *
+ * dao_solve_sens -- dao_solve (same arguments, record and results, the same
+ * steps bit for bit) plus S_theta (required).
+ */
+dao_status dao_solve_sens(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                          const void* theta, const void* y0, double t0, double t1,
+                          const dao_tol* tol, void* y1, const dao_record* rec, void* S_theta,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace (device bytes) dao_sens needs; 0 for an unsupported combination. */
+size_t dao_sens_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                               int64_t s_max);
+
+/*
+ * dao_sens -- the same sensitivities by forward mode through the replay of a
+ * record (rec->h, rec->count, rec->status read), at theta (which may differ
+ * from the solve's) and y0.  S_theta or S_y0 may be NULL, not both.  With
+ * the record of a dao_solve_sens call at the same theta, S_theta equals that
+ * call's bit for bit.  s_max as in dao_grad.  The workspace holds the sorted
+ * order of the record (its contents need no initialisation).
+ * Errors: DAO_EINVAL, DAO_EUNSUPPORTED, DAO_EWORKSPACE, DAO_EDEVICE.
+ */
+dao_status dao_sens(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                    const void* theta, const void* y0, const dao_record* rec, int64_t s_max,
+                    void* S_theta, void* S_y0, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
  * dao_sqerr_cotangent -- cotangent of a squared-error loss (the misfit
  * l(y(t1)) of Sec. 2.2's calibration loss), out[c][k] = scale *
  * (y1[c][k] - target[c][k]) for components c < d_used, 0 for the rest.

@@ -26,7 +26,8 @@ def L():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("dao_solve", "dao_grad", "dao_grad_order", "dao_grad_ordered",
+    for n in ("dao_solve", "dao_grad", "dao_grad_order", "dao_grad_ordered", "dao_solve_sens",
+              "dao_sens", "dao_sens_workspace_size",
               "dao_solve_workspace_size", "dao_grad_workspace_size",
               "dao_grad_workspace_min", "dao_system_dims", "dao_sqerr_cotangent",
               "dao_last_error", "dao_version"):
@@ -125,6 +126,39 @@ def test_grad_order_and_ordered_argument_errors(L):
     assert ordered(y0=None) == 1
     assert ordered(s_max=-1) == 1
     assert ordered(wsb=16) == 3
+
+
+def test_sensitivity_argument_errors(L):
+    tol = L.dao_tol(1e-6, 1e-8, 0.0, 1000)
+    rec = L.dao_record(16, 1, 1, 1, 1, 1)
+
+    def solve_sens(**o):
+        a = dict(system=2, method=0, dtype=0, n=10, S=1, ws=1, wsb=256)
+        a.update(o)
+        return L.dao_solve_sens(a["system"], a["method"], a["dtype"], a["n"], 1, 1, 0.0, 1.0, tol,
+                                1, rec, a["S"], a["ws"], a["wsb"], None)
+
+    assert solve_sens(S=None) == 1
+    assert "dao_solve_sens" in L.dao_last_error()
+    assert solve_sens(system=4, method=1) == 4      # Rosenbrock23: no forward sensitivities
+    assert solve_sens(system=3, dtype=1) == 4       # neural field: shared weights
+    assert solve_sens(ws=None) == 3
+    assert solve_sens(n=0) == 0                     # empty ensemble: nothing to do
+
+    def sens(**o):
+        a = dict(system=2, method=0, n=4, s_max=8, St=1, Sy=None, ws=1, wsb=1 << 20, theta=1)
+        a.update(o)
+        return L.dao_sens(a["system"], a["method"], 0, a["n"], a["theta"], 1, rec, a["s_max"],
+                          a["St"], a["Sy"], a["ws"], a["wsb"], None)
+
+    assert sens(St=None, Sy=None) == 1
+    assert sens(s_max=17) == 1
+    assert sens(theta=None) == 1
+    assert sens(ws=None) == 3
+    assert sens(system=4, method=1) == 4
+    assert sens(n=0) == 0
+    assert L.dao_sens_workspace_size(2, 0, 0, 100, 50) > 0
+    assert L.dao_sens_workspace_size(4, 1, 0, 100, 50) == 0   # not provided
 
 
 def test_cotangent_argument_errors(L):
