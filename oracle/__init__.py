@@ -13,7 +13,9 @@ The arithmetic lives in ``oracle.cpp`` (binary64 C++, ``-ffp-contract=off``):
   (Sec. 3.1: exact gradient of the chain with the mesh held fixed);
 * a complex-step replay for directional derivatives;
 * the forward-mode sensitivities of the replayed final state (dual numbers
-  carrying one derivative per parameter and initial-state component).
+  carrying one derivative per parameter and initial-state component);
+* states at requested times on a recorded mesh (a shortened step from the
+  start of the step that holds each time).
 
 Array layouts match the library boundary: parameters ``[p][n]`` (shared MLP
 weights ``[4740]``), states ``[d][n]``, record rows ``[n][s_cap]``.
@@ -66,6 +68,7 @@ def lib():
         L.oracle_replay_cs.argtypes = [I, I, I64, P, P, P, P, D, P, P, I64, P, P]
         L.oracle_grad_f64.argtypes = [I, I, I64, P, P, P, P, I64, P, P, P, P, I]
         L.oracle_sens_f64.argtypes = [I, I, I64, P, P, P, P, I64, P, P, P, I]
+        L.oracle_states_at_f64.argtypes = [I, I, I64, P, P, D, D, P, P, I64, I64, P, P, I]
         L.oracle_step_f64.argtypes = [I, I, P, P, D, P, P]
         L.oracle_rhs_f64.argtypes = [I, P, P, P]
         L.oracle_jac_f64.argtypes = [I, P, P, P]
@@ -199,6 +202,24 @@ def sens(system, method, theta, y0, count, h, with_y0=True, nthreads=1):
                                _p(h), h.shape[1], _p(S_th), _p(S_y0), _p(yS), int(nthreads))
     assert rc == 0
     return S_th, S_y0, yS
+
+
+def states_at(system, method, theta, y0, t0, t1, count, h, tq, nthreads=1):
+    """States at the requested times tq (ascending, in [t0, t1]) on the mesh
+    (count, h): [m][d][n]."""
+    d, p, shared = dims(system)
+    theta = np.ascontiguousarray(theta, dtype=np.float64)
+    y0 = np.ascontiguousarray(y0, dtype=np.float64)
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    count = np.ascontiguousarray(count, dtype=np.int32)
+    tq = np.ascontiguousarray(tq, dtype=np.float64)
+    n, m = y0.shape[1], tq.shape[0]
+    yq = np.zeros((m, d, n))
+    rc = lib().oracle_states_at_f64(SYSTEMS[system], METHODS[method], n, _p(theta), _p(y0),
+                                    float(t0), float(t1), _p(count), _p(h), h.shape[1], m, _p(tq),
+                                    _p(yq), int(nthreads))
+    assert rc == 0
+    return yq
 
 
 def step(system, method, theta, y, h):

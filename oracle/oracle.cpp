@@ -880,6 +880,66 @@ int oracle_replay_cs(int sys, int method, int64_t n, const double* theta, const 
   return 0;
 }
 
+// States at requested times on a recorded mesh (application paper Sec. 2.3
+// and its Appendix A: the state between steps is a shortened step from the
+// start of the accepted step; the library paper's replay engines integrate
+// one extra step to each requested time).  Step j spans [t_j, t_j + h_j]
+// with t_0 = t0 and t_{j+1} = t_j + h_j (the solve's own time update); the
+// state at tau in step j is Phi(y_j; tau - t_j); tau = t1 gives the final
+// state.  tq ascending in [t0, t1]; a time outside it, or below its
+// predecessor, gives NaN.
+int oracle_states_at_f64(int sys, int method, int64_t n, const double* theta, const double* y0,
+                         double t0, double t1, const int32_t* count, const double* h_rec,
+                         int64_t s_cap, int64_t m, const double* tq, double* yq, int nthreads) {
+  if (!valid_sys(sys, method) || n < 0 || m < 0) return 1;
+  const int d = SYS_D[sys], p = SYS_P[sys];
+  const bool shared = (sys == SYS_MLP);
+  parallel_for(n, nthreads, [&](int, int64_t lo, int64_t hi) {
+    std::vector<double> th(p);
+    double y[MAXD], ys[MAXD], k[7][MAXD], ynew[MAXD];
+    auto step = [&](const double* from, double h, double* to) {
+      rhs(sys, th.data(), from, k[0]);
+      if (method == M_TSIT5)
+        tsit5_step<double>(sys, th.data(), d, from, h, k, to, nullptr);
+      else
+        ros23_step<double>(sys, th.data(), d, from, h, k[0], to, nullptr, nullptr);
+    };
+    for (int64_t kk = lo; kk < hi; ++kk) {
+      for (int i = 0; i < p; ++i) th[i] = shared ? theta[i] : theta[i * n + kk];
+      for (int c = 0; c < d; ++c) y[c] = y0[c * n + kk];
+      const double* h = h_rec + kk * s_cap;
+      const int32_t S = count[kk];
+      double t = t0;
+      int32_t j = 0;
+      double prev = t0;
+      for (int64_t q = 0; q < m; ++q) {
+        const double tau = tq[q];
+        double* out = yq + q * d * n;
+        const bool bad = !(tau >= t0 && tau <= t1) || tau < prev;
+        if (bad) {
+          for (int c = 0; c < d; ++c) out[c * n + kk] = NAN;
+          continue;
+        }
+        prev = tau;
+        // advance to the step that holds tau (the last step holds up to t1)
+        while (j < S - 1 && tau >= t + h[j]) {
+          step(y, h[j], ynew);
+          for (int c = 0; c < d; ++c) y[c] = ynew[c];
+          t = t + h[j];
+          ++j;
+        }
+        if (S == 0) {
+          for (int c = 0; c < d; ++c) out[c * n + kk] = y[c];
+        } else {
+          step(y, tau - t, ys);
+          for (int c = 0; c < d; ++c) out[c * n + kk] = ys[c];
+        }
+      }
+    }
+  });
+  return 0;
+}
+
 // Forward-mode sensitivities of the replayed final state: S_theta[c][j][k] =
 // d y_S,c / d theta_j and (if not NULL) S_y0[c][j][k] = d y_S,c / d y0_j for
 // trajectory k, by the dual numbers above.  Per-trajectory parameters only.
