@@ -100,6 +100,19 @@ def parse():
     return ap.parse_args()
 
 
+def copy_calibration(mib, dev):
+    """One device-to-device copy of a known size: the reference that scales the
+    HBM byte counters of a profiled run."""
+    import torch
+
+    if mib > 0:
+        src = torch.ones((mib << 20) // 8, dtype=torch.float64, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+
 def cpu_baseline(w, sample, s_cap):
     """The oracle, as is, on the host cores: solve + gradient of a sample."""
     import numpy as np
@@ -182,13 +195,7 @@ def main():
     def events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
 
-    if args.copy_calibration > 0:
-        nbytes = args.copy_calibration << 20
-        src = torch.ones(nbytes // 8, dtype=torch.float64, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args.copy_calibration, dev)
 
     # The record's longest row sizes the gradient's checkpoint scratch.  Every
     # step solves the same inputs, so it is read once, after the first solve.
@@ -332,6 +339,7 @@ def bench_sens(args, w):
     def events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(2)]
 
+    copy_calibration(args.copy_calibration, dev)
     for _ in range(max(args.warmup, 1)):
         run(events(), True)
         run(events(), False)
@@ -356,6 +364,11 @@ def bench_sens(args, w):
     fl_solve = w.n * cfg["init"] + attempts * cfg["att"] + steps_total
     fl_sens = steps_total * _sens_step_flops(w.d, w.theta.shape[0], w.name)
     ach = (fl_solve + fl_sens) / tk
+    from differentiable_adaptive_ode_amd.profiling import load_traffic
+
+    tr = load_traffic(f"{w.name}_sens")
+    kern = "solve_sens_kernel"
+    traffic = tr["kernels"][kern]["hbm_bytes"] if tr and kern in tr["kernels"] else None
     out = {
         "metric": "forward-sensitivity trajectories/s (solve + dy1/dtheta in one kernel) at 1 GPU",
         "value": w.n / (wall / args.steps),
@@ -368,9 +381,9 @@ def bench_sens(args, w):
                    "s_cap": s_cap, "directions": int(w.theta.shape[0])},
         "solve_sens_ms": tk * 1e3, "solve_ms": tp * 1e3,
         "accepted_steps_mean": float(cnt.mean()), "attempts_total": attempts,
-        "roofline": {"bound": cfg["bound"], "kernel": "solve_kernel (with sensitivities)",
+        "roofline": {"bound": cfg["bound"], "kernel": "solve_sens_kernel",
                      "launch_ms": tk * 1e3, "achieved": ach * 1e-12, "peak": cfg["peak"] * 1e-12,
-                     "unit": "TFLOP/s", "frac": ach / cfg["peak"], "traffic": None,
+                     "unit": "TFLOP/s", "frac": ach / cfg["peak"], "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch"},
     }
     if not args.no_cpu_baseline:

@@ -71,6 +71,11 @@ def _load():
     L.dao_sens_workspace_size.restype = SZ
     L.dao_sens.argtypes = [I, I, I, I64, P, P, ctypes.POINTER(dao_record), I64, P, P, P, SZ, P]
     L.dao_sens.restype = I
+    L.dao_states_workspace_size.argtypes = [I, I, I, I64, I64]
+    L.dao_states_workspace_size.restype = SZ
+    L.dao_states_at.argtypes = [I, I, I, I64, P, P, D, D, ctypes.POINTER(dao_record), I64, I64,
+                                P, P, P, SZ, P]
+    L.dao_states_at.restype = I
     L.dao_sqerr_cotangent.argtypes = [I, I64, I, I, P, P, D, P, P]
     L.dao_sqerr_cotangent.restype = I
     L.dao_last_error.argtypes = []
@@ -123,6 +128,17 @@ def dao_sens(system, method, dtype, n, theta, y0, rec, s_max, S_theta, S_y0, wor
     return lib.dao_sens(system, method, dtype, n, theta, y0,
                         ctypes.byref(rec) if rec is not None else None, s_max, S_theta, S_y0,
                         workspace, ws_bytes, stream)
+
+
+def dao_states_workspace_size(system, method, dtype, n, s_max):
+    return lib.dao_states_workspace_size(system, method, dtype, n, s_max)
+
+
+def dao_states_at(system, method, dtype, n, theta, y0, t0, t1, rec, s_max, m, tq, yq, workspace,
+                  ws_bytes, stream):
+    return lib.dao_states_at(system, method, dtype, n, theta, y0, t0, t1,
+                             ctypes.byref(rec) if rec is not None else None, s_max, m, tq, yq,
+                             workspace, ws_bytes, stream)
 
 
 def dao_grad_workspace_size(system, method, dtype, n, s_max):

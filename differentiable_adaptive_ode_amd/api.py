@@ -236,6 +236,31 @@ def grad(rec: Record, dLdy1: torch.Tensor, theta: torch.Tensor | None = None, s_
     return dth, dy0
 
 
+def states_at(rec: Record, tq: torch.Tensor, theta: torch.Tensor | None = None,
+              s_max: int | None = None, out=None, workspace=None, stream=None):
+    """States at the requested times tq (device [m], ascending in [t0, t1]) on
+    rec's mesh, by a shortened step from the start of the step that holds
+    each time: [m][d][n]."""
+    th = rec.theta if theta is None else theta
+    _check_dev(th, tq)
+    n, m = rec.n, int(tq.numel())
+    d, _, _ = _lib.dao_system_dims(_lib.SYSTEMS[rec.system])
+    if tq.dtype != rec.y0.dtype:
+        raise TypeError("tq must have the record's dtype")
+    if s_max is None:
+        s_max = int(rec.count.max().item()) if n > 0 else 0
+    s_max = min(int(s_max), rec.s_cap)
+    ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
+    dev = rec.count.device
+    yq = torch.empty((m, d, n), dtype=rec.y0.dtype, device=dev) if out is None else out
+    nb = _lib.dao_states_workspace_size(*ids, n, s_max)
+    buf = _ws(dev, workspace).get(nb, dev)
+    _lib.check(_lib.dao_states_at(*ids, n, _ptr(th), _ptr(rec.y0), rec.t0, rec.t1,
+                                  rec.c_struct(states=False), s_max, m, _ptr(tq.contiguous()),
+                                  _ptr(yq), _ptr(buf), buf.numel(), _stream(stream)))
+    return yq
+
+
 def cotangent(y1: torch.Tensor, target: torch.Tensor, scale: float = 1.0, d_used: int | None = None,
               out=None, stream=None):
     """dL/dy1 = scale * (y1 - target) on the first d_used components, 0 elsewhere."""

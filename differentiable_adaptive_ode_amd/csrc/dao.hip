@@ -321,6 +321,43 @@ dao_status launch_sens(int64_t n, const void* theta, const void* y0, const dao_r
   return check_hip(hipGetLastError(), "sensitivity kernel launch");
 }
 
+// States at requested times: the record's trajectories sorted once, then one
+// states_kernel launch.
+template <class R, class Sys, int M>
+dao_status launch_states(int64_t n, const void* theta, const void* y0, double t0, double t1,
+                         const dao_record* rec, int64_t s_max, int64_t m, const void* tq, void* yq,
+                         void* ws, hipStream_t stream) {
+  char* base = (char*)ws;
+  unsigned long long* groups = (unsigned long long*)base;
+  uint32_t* hist = (uint32_t*)(base + align_up(16));
+  int32_t* perm = (int32_t*)(base + align_up(16) + align_up((size_t)ORDER_BINS * 4));
+  auto kern = states_kernel<R, Sys, M>;
+  const int64_t ngroups = (n + WAVE - 1) / WAVE;
+  int64_t blocks = (ngroups + BLOCK / WAVE - 1) / (BLOCK / WAVE);
+  const int64_t res = resident_blocks(kern);
+  if (blocks > res) blocks = res;
+  launch_order(rec->count, n, s_max, hist, perm, stream);
+  StatesArgs<R> a;
+  a.n = n;
+  a.theta = (const R*)theta;
+  a.y0 = (const R*)y0;
+  a.t0 = R(t0);
+  a.t1 = R(t1);
+  a.s_cap = rec->s_cap;
+  a.h_rec = (const R*)rec->h;
+  a.count = rec->count;
+  a.status = rec->status;
+  a.s_max = s_max;
+  a.m = m;
+  a.tq = (const R*)tq;
+  a.yq = (R*)yq;
+  a.perm = perm;
+  a.groups = groups;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)groups, (int64_t)2, 0u);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), 0, stream, a);
+  return check_hip(hipGetLastError(), "states kernel launch");
+}
+
 // ------------------------------------------------- neural right-hand side
 dao_status launch_mlp_solve(int64_t n, const void* theta, const void* y0, double t0, double t1,
                             const dao_tol* tol, void* y1, const dao_record* rec, void* ws,
@@ -443,6 +480,11 @@ struct Entry {
     else
       return DAO_EUNSUPPORTED;
   }
+  static dao_status states(int64_t n, const void* th, const void* y0, double t0, double t1,
+                           const dao_record* rec, int64_t s_max, int64_t m, const void* tq,
+                           void* yq, void* ws, hipStream_t st) {
+    return launch_states<R, S<R>, M>(n, th, y0, t0, t1, rec, s_max, m, tq, yq, ws, st);
+  }
   static size_t slot_bytes(int64_t s_max) { return grad_slot_bytes<R, S<R>::D>(s_max); }
   static int64_t resident_waves() {
     return resident_blocks(grad_kernel<R, S<R>, M>) * (BLOCK / WAVE);
@@ -458,6 +500,9 @@ typedef dao_status (*solve_sens_fn)(int64_t, const void*, const void*, double, d
                                     void*);
 typedef dao_status (*sens_fn)(int64_t, const void*, const void*, const dao_record*, int64_t, void*,
                               void*, void*, hipStream_t);
+typedef dao_status (*states_fn)(int64_t, const void*, const void*, double, double,
+                                const dao_record*, int64_t, int64_t, const void*, void*, void*,
+                                hipStream_t);
 typedef size_t (*slot_fn)(int64_t);
 typedef int64_t (*res_fn)();
 
@@ -469,6 +514,7 @@ struct Impl {
   int group;  // trajectories per wavefront in the gradient
   solve_sens_fn solve_sens;  // forward sensitivities (Tsit5, per-trajectory theta), else null
   sens_fn sens;
+  states_fn states;  // states at requested times (per-lane systems), else null
 };
 
 int64_t mlp_resident_waves() { return resident_blocks(mlp::grad_kernel) * (BLOCK / WAVE); }
@@ -478,7 +524,8 @@ Impl make_impl() {
   const bool fwd = (M == M_TSIT5);
   return Impl{&Entry<R, S, M>::solve, &Entry<R, S, M>::grad, &Entry<R, S, M>::slot_bytes,
               &Entry<R, S, M>::resident_waves, WAVE,
-              fwd ? &Entry<R, S, M>::solve_sens : nullptr, fwd ? &Entry<R, S, M>::sens : nullptr};
+              fwd ? &Entry<R, S, M>::solve_sens : nullptr, fwd ? &Entry<R, S, M>::sens : nullptr,
+              &Entry<R, S, M>::states};
 }
 
 const Impl* find_impl(int sys, int method, int dtype) {
@@ -508,7 +555,7 @@ const Impl* find_impl(int sys, int method, int dtype) {
     table[DAO_SYS_LOGHALO][M_TSIT5][DAO_F32] = make_impl<float, LogHalo, M_TSIT5>();
     table[DAO_SYS_MLP][M_TSIT5][DAO_F32] =
         Impl{&launch_mlp_solve, &launch_mlp_grad, &mlp_slot_bytes, &mlp_resident_waves, mlp::SLOTS,
-             nullptr, nullptr};
+             nullptr, nullptr, nullptr};
     init = true;
   }
   if (!sys_ok(sys) || method < 0 || method > 1 || dtype < 0 || dtype > 1) return nullptr;
@@ -613,6 +660,47 @@ size_t dao_sens_workspace_size(dao_system sys, dao_method method, dao_dtype dtyp
   const Impl* im = find_impl(sys, method, dtype);
   if (!im || !im->sens || n < 0 || s_max < 0) return 0;
   return grad_header_bytes(n, s_max);
+}
+
+size_t dao_states_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                                 int64_t s_max) {
+  const Impl* im = find_impl(sys, method, dtype);
+  if (!im || !im->states || n < 0 || s_max < 0) return 0;
+  return grad_header_bytes(n, s_max);
+}
+
+dao_status dao_states_at(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                         const void* theta, const void* y0, double t0, double t1,
+                         const dao_record* rec, int64_t s_max, int64_t m, const void* tq,
+                         void* yq, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "dao_states_at";
+  g_err[0] = 0;
+  if (!sys_ok(sys)) return fail(DAO_EINVAL, "%s: unknown system %d", fn, (int)sys);
+  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
+    return fail(DAO_EINVAL, "%s: unknown method %d", fn, (int)method);
+  if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+  if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "%s: n = %lld out of range", fn, (long long)n);
+  if (m < 0) return fail(DAO_EINVAL, "%s: m < 0", fn);
+  if (!(is_fin(t0) && is_fin(t1))) return fail(DAO_EINVAL, "%s: t0/t1 not finite", fn);
+  if (!(t1 >= t0)) return fail(DAO_EINVAL, "%s: t1 < t0", fn);
+  if (!rec) return fail(DAO_EINVAL, "%s: rec is NULL", fn);
+  if (rec->s_cap < 0) return fail(DAO_EINVAL, "%s: rec->s_cap < 0", fn);
+  if (s_max < 0 || s_max > rec->s_cap) return fail(DAO_EINVAL, "%s: s_max must be in [0, rec->s_cap]", fn);
+  const Impl* im = find_impl(sys, method, dtype);
+  if (!im || !im->states)
+    return fail(DAO_EUNSUPPORTED, "%s: system %d with method %d dtype %d is not provided", fn,
+                (int)sys, (int)method, (int)dtype);
+  if (n == 0 || m == 0) return DAO_OK;
+  if (!theta) return fail(DAO_EINVAL, "%s: theta is NULL", fn);
+  if (!y0) return fail(DAO_EINVAL, "%s: y0 is NULL", fn);
+  if (!tq) return fail(DAO_EINVAL, "%s: tq is NULL", fn);
+  if (!yq) return fail(DAO_EINVAL, "%s: yq is NULL", fn);
+  if (!rec->count) return fail(DAO_EINVAL, "%s: rec->count is NULL", fn);
+  if (s_max > 0 && !rec->h) return fail(DAO_EINVAL, "%s: rec->h is NULL", fn);
+  const size_t need = dao_states_workspace_size(sys, method, dtype, n, s_max);
+  if (!workspace || workspace_bytes < need)
+    return fail(DAO_EWORKSPACE, "%s: workspace needs at least %zu bytes", fn, need);
+  return im->states(n, theta, y0, t0, t1, rec, s_max, m, tq, yq, workspace, (hipStream_t)stream);
 }
 
 dao_status dao_sens(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,

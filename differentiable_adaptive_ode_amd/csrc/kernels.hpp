@@ -607,6 +607,107 @@ __global__ void __launch_bounds__(256) sens_kernel(SensArgs<R> a) {
   }
 }
 
+// ------------------------------------------------------------------------
+// States at requested times on a recorded mesh (arXiv 2609.28458 Sec. 2.3
+// and Appendix A: a shortened step from the start of the accepted step that
+// holds the time; arXiv 2609.02876: the replay engines integrate one extra
+// step to each requested time).  Step j spans [t_j, t_j + h_j], t_0 = t0,
+// t_{j+1} = t_j + h_j (the solve's own time update); the last step holds up
+// to t1.  Each lane walks its trajectory's steps and the shared, ascending
+// requested times together; every iteration takes exactly one step of the
+// method per lane, either the next recorded step (advance) or the shortened
+// step to the next requested time (write), so the lockstep loop is
+// branch-free.  A requested time outside [t0, t1], not a number, or below its
+// predecessor gives NaN; a failed trajectory gives NaN throughout.
+template <class R>
+struct StatesArgs {
+  int64_t n;
+  const R* theta;
+  const R* y0;
+  R t0, t1;
+  int64_t s_cap;
+  const R* h_rec;
+  const int32_t* count;
+  const int32_t* status;
+  int64_t s_max;
+  int64_t m;
+  const R* tq;  // [m]
+  R* yq;        // [m][D][n]
+  const int32_t* perm;
+  unsigned long long* groups;
+};
+
+template <class R, class Sys, int METHOD>
+__global__ void __launch_bounds__(256) states_kernel(StatesArgs<R> a) {
+  constexpr int D = Sys::D;
+  const int lane = laneId();
+  tsit5::Coef<R> C5;
+  if constexpr (METHOD == M_TSIT5) C5 = tsit5::Coef<R>::literal();
+  const unsigned long long ngroups = (unsigned long long)((a.n + WAVE - 1) / WAVE);
+  for (;;) {
+    unsigned long long g = 0;
+    if (lane == 0) g = atomicAdd(a.groups, 1ull);
+    g = __shfl(g, 0);
+    if (g >= ngroups) break;
+    const int64_t idx = (int64_t)g * WAVE + lane;
+    int64_t k = -1;
+    int cnt = 0;
+    bool ok = false;
+    if (idx < a.n) {
+      k = a.perm ? (int64_t)a.perm[idx] : idx;
+      if (k < 0 || k >= a.n) {
+        k = -1;
+      } else {
+        cnt = a.count[k];
+        ok = cnt >= 0 && cnt <= a.s_max && (a.status == nullptr || a.status[k] == TRAJ_OK);
+        if (!ok) cnt = 0;
+      }
+    }
+    Sys sys;
+    sys.load(a.theta, a.n, k >= 0 ? k : 0);
+    R y[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) y[c] = (k >= 0) ? a.y0[c * a.n + k] : R(0);
+    const R* hrow = (k >= 0) ? a.h_rec + k * a.s_cap : a.h_rec;
+    R t = a.t0, prev = a.t0;
+    int j = 0;
+    int64_t q = (k >= 0) ? 0 : a.m;  // lanes without a trajectory are done
+    R hc = (cnt > 0) ? hrow[0] : R(0);
+    R hn = (cnt > 1) ? hrow[1] : R(0);
+    R tau = (q < a.m) ? a.tq[q] : R(0);
+    while (__ballot(q < a.m)) {
+      const bool live = q < a.m;
+      const bool bad = !(tau >= a.t0 && tau <= a.t1) || tau < prev || !ok;
+      const bool adv = live && !bad && (j < cnt - 1) && (tau >= t + hc);
+      const bool put = live && !adv;
+      // one step of the method: the recorded step, or the shortened step to tau
+      R hs = adv ? hc : ((put && !bad && cnt > 0) ? tau - t : R(0));
+      R ys[D];
+#pragma unroll
+      for (int c = 0; c < D; ++c) ys[c] = y[c];
+      if constexpr (METHOD == M_TSIT5)
+        tsit5::replay<R, Sys>(C5, sys, ys, hs);
+      else
+        ros23::replay<R, Sys>(sys, ys, hs);
+      if (adv) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) y[c] = ys[c];
+        t = t + hc;
+        ++j;
+        hc = hn;
+        if (j + 1 < cnt) hn = hrow[j + 1];
+      }
+      if (put) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) a.yq[(q * D + c) * a.n + k] = bad ? nanR(R(0)) : ys[c];
+        if (!bad) prev = tau;
+        ++q;
+        if (q < a.m) tau = a.tq[q];
+      }
+    }
+  }
+}
+
 // ---- trajectory ordering by step count (counting sort, decreasing count)
 constexpr int ORDER_BINS = 4096;
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v);

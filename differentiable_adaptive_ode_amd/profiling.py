@@ -63,9 +63,12 @@ def load_traffic(workload: str):
 
 def _short(name: str) -> str:
     if "solve_kernel" in name:
-        return "solve_kernel"
+        # the variant that integrates the forward sensitivities (template flag true)
+        return "solve_sens_kernel" if ", true>" in name else "solve_kernel"
     if "grad_kernel" in name:
         return "grad_kernel"
+    if "sens_kernel" in name:
+        return "sens_kernel"
     if "mlp" in name.lower():
         return name.split("(")[0].replace("void ", "")
     return name.split("(")[0].replace("void ", "")
@@ -119,7 +122,7 @@ def summarize(args) -> None:
 
     traffic = {"workload": args.workload, "n": args.n, "kernel_source_sha256": kernel_source_digest(),
                "fetch_factor": f_fac, "write_factor": w_fac, "kernels": {}}
-    for key in ("solve_kernel", "grad_kernel"):
+    for key in ("solve_kernel", "solve_sens_kernel", "grad_kernel", "sens_kernel"):
         fb = per_launch(fetch, "FETCH_SIZE", f_fac, key)
         wb = per_launch(write, "WRITE_SIZE", w_fac, key)
         if fb is not None and wb is not None:
@@ -151,7 +154,7 @@ def summarize(args) -> None:
         counters = sorted({c for (_, c) in sq})
         lines.append("| kernel | " + " | ".join(counters) + " |")
         lines.append("|---|" + "---|" * len(counters))
-        for key in ("solve_kernel", "grad_kernel"):
+        for key in traffic["kernels"]:
             row = []
             for c in counters:
                 xs = [v for (name, cc), vv in sq.items() if cc == c and _short(name) == key for v in vv]

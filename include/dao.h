@@ -228,6 +228,36 @@ dao_status dao_sens(dao_system sys, dao_method method, dao_dtype dtype, int64_t 
                     void* S_theta, void* S_y0, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Workspace (device bytes) dao_states_at needs; 0 for an unsupported combination. */
+size_t dao_states_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                                 int64_t s_max);
+
+/*
+ * dao_states_at -- the state of every trajectory at m requested times on its
+ * recorded mesh: a shortened step of the method from the start of the
+ * accepted step that holds the time (application paper arXiv 2609.28458,
+ * Sec. 2.3 and Appendix A; gradsolve's replay engines integrate one extra
+ * step to each requested time).  Step j spans [t_j, t_j + h_j] with t_0 = t0
+ * and t_{j+1} = t_j + h_j, the solve's own time update, so a time on a step
+ * boundary returns the replay's state there bit for bit and t1 the final
+ * state.  The record's mesh is not changed.
+ *   theta, y0  as in dao_solve (the theta may differ from the solve's)
+ *   t0, t1     the span of the solve that wrote the record
+ *   rec        rec->h, rec->count and rec->status are read
+ *   s_max      as in dao_grad
+ *   tq         real[m], shared by all trajectories, ascending in [t0, t1];
+ *              a time outside that range, not a number, or below its
+ *              predecessor gives NaN (so do failed trajectories)
+ *   yq         real[m][d][n]: yq[(q d + c) n + k] = component c of
+ *              trajectory k at tq[q]
+ * Not provided for DAO_SYS_MLP.  Errors: DAO_EINVAL, DAO_EUNSUPPORTED,
+ * DAO_EWORKSPACE, DAO_EDEVICE.
+ */
+dao_status dao_states_at(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                         const void* theta, const void* y0, double t0, double t1,
+                         const dao_record* rec, int64_t s_max, int64_t m, const void* tq,
+                         void* yq, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * dao_sqerr_cotangent -- cotangent of a squared-error loss (the misfit
  * l(y(t1)) of Sec. 2.2's calibration loss), out[c][k] = scale *

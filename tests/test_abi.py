@@ -27,7 +27,7 @@ def L():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dao_solve", "dao_grad", "dao_grad_order", "dao_grad_ordered", "dao_solve_sens",
-              "dao_sens", "dao_sens_workspace_size",
+              "dao_sens", "dao_sens_workspace_size", "dao_states_at", "dao_states_workspace_size",
               "dao_solve_workspace_size", "dao_grad_workspace_size",
               "dao_grad_workspace_min", "dao_system_dims", "dao_sqerr_cotangent",
               "dao_last_error", "dao_version"):
@@ -159,6 +159,29 @@ def test_sensitivity_argument_errors(L):
     assert sens(n=0) == 0
     assert L.dao_sens_workspace_size(2, 0, 0, 100, 50) > 0
     assert L.dao_sens_workspace_size(4, 1, 0, 100, 50) == 0   # not provided
+
+
+def test_states_at_argument_errors(L):
+    rec = L.dao_record(16, None, 1, 1, None, 1)
+
+    def call(**o):
+        a = dict(system=2, method=0, n=4, t0=0.0, t1=1.0, s_max=8, m=3, tq=1, yq=1, ws=1,
+                 wsb=1 << 20, theta=1)
+        a.update(o)
+        return L.dao_states_at(a["system"], a["method"], 0, a["n"], a["theta"], 1, a["t0"], a["t1"],
+                               rec, a["s_max"], a["m"], a["tq"], a["yq"], a["ws"], a["wsb"], None)
+
+    assert call(tq=None) == 1
+    assert "dao_states_at" in L.dao_last_error()
+    assert call(yq=None) == 1
+    assert call(m=-1) == 1
+    assert call(t1=-1.0) == 1
+    assert call(t0=float("inf")) == 1
+    assert call(s_max=17) == 1
+    assert call(ws=None) == 3
+    assert call(system=3, method=0) == 4       # the neural field: not provided
+    assert call(m=0, tq=None, yq=None) == 0    # nothing requested
+    assert call(n=0) == 0
 
 
 def test_cotangent_argument_errors(L):
