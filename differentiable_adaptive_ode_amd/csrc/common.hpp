@@ -57,7 +57,7 @@ __device__ __forceinline__ float truncBits(float x) {
 // Step-size controller power x^(-1/Q) (Q = 10 for Tsit5, 6 for Rosenbrock23;
 // x is the mean square of the scaled error, so this is err^(-1/(order+1))).
 // A libm pow costs about a thousand cycles of dependent FP64 work per call on
-// one wavefront; this rule costs two short Horner chains:
+// one wavefront; this rule costs two short polynomial evaluations:
 //   clamp x to [lo, hi] (beyond it 0.9 x^(-1/Q) is outside the controller's
 //   limits [0.2, 10] anyway), write x = m 2^e with m in [1, 2) and
 //   e = Q a + b (0 <= b < Q), then
@@ -94,24 +94,49 @@ __device__ __forceinline__ float frexpR(float x, int* e) { return __builtin_frex
 __device__ __forceinline__ double ldexpR(double x, int e) { return __builtin_ldexp(x, e); }
 __device__ __forceinline__ float ldexpR(float x, int e) { return __builtin_ldexpf(x, e); }
 
+// The rule's coefficients as values: literals, or pinned to vector registers
+// once per kernel where scalar registers are the scarce resource (an empty
+// asm that claims to modify the value keeps the compiler from rebuilding the
+// literal from scalar moves at each use).
 template <class R, int Q>
-__device__ __forceinline__ R ctrl_root(R x) {
-  using K = CtrlRoot<Q>;
-  x = x > R(K::lo) ? x : R(K::lo);
-  x = x < R(K::hi) ? x : R(K::hi);
+struct CtrlCoef {
+  R c[8], e[7];
+  __device__ __forceinline__ static R pin_(R v) {
+    asm volatile("" : "+v"(v));
+    return v;
+  }
+  __device__ __forceinline__ static CtrlCoef make(bool pinned) {
+    CtrlCoef K;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) K.c[i] = pinned ? pin_(R(CtrlRoot<Q>::c[i])) : R(CtrlRoot<Q>::c[i]);
+#pragma unroll
+    for (int i = 0; i < 7; ++i) K.e[i] = pinned ? pin_(R(EXP2_NEG[i])) : R(EXP2_NEG[i]);
+    return K;
+  }
+};
+
+template <class R, int Q>
+__device__ __forceinline__ R ctrl_root(R x, const CtrlCoef<R, Q>& K) {
+  using L = CtrlRoot<Q>;
+  x = x > R(L::lo) ? x : R(L::lo);
+  x = x < R(L::hi) ? x : R(L::hi);
   int e = 0;
-  const R m = frexpR(x, &e) * R(2);  // x = m 2^(e-1)
+  const R mh = frexpR(x, &e);  // x = mh 2^e, mh in [1/2, 1): m = 2 mh
   e -= 1;
   const int a = (e + 64 * Q) / Q - 64;  // floor(e / Q); e > -64 Q after the clamp
   const int b = e - Q * a;
-  const R s = m * R(2) - R(3);
-  R p = R(K::c[7]);
-#pragma unroll
-  for (int i = 6; i >= 0; --i) p = fmaR(p, s, R(K::c[i]));
-  const R s2 = fmaR(R(b), R(2.0 / Q), R(-1));
-  R q = R(EXP2_NEG[6]);
-#pragma unroll
-  for (int i = 5; i >= 0; --i) q = fmaR(q, s2, R(EXP2_NEG[i]));
+  const R s = fmaR(mh, R(4), R(-3));  // 2 m - 3, exact
+  // P(s), degree 7, and E(t), degree 6, by Estrin's scheme (pairs of
+  // coefficients, then pairs of pairs): three dependent steps, not seven.
+  const R s2 = s * s, s4 = s2 * s2;
+  const R p01 = fmaR(K.c[1], s, K.c[0]), p23 = fmaR(K.c[3], s, K.c[2]);
+  const R p45 = fmaR(K.c[5], s, K.c[4]), p67 = fmaR(K.c[7], s, K.c[6]);
+  const R p = fmaR(fmaR(p67, s2, p45), s4, fmaR(p23, s2, p01));
+  const R t = fmaR(R(b), R(2.0 / Q), R(-1));
+  const R t2 = t * t, t4 = t2 * t2;
+  const R q01 = fmaR(K.e[1], t, K.e[0]), q23 = fmaR(K.e[3], t, K.e[2]);
+  const R q45 = fmaR(K.e[5], t, K.e[4]);
+  const R q = fmaR(fmaR(K.e[6], t2, q45), t4, fmaR(q23, t2, q01));
   return ldexpR(p * q, -a);
 }
 

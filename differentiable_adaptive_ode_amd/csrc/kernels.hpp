@@ -133,6 +133,9 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   // literals: more resident wavefronts matter more there).
   tsit5::Coef<R> C5;
   if constexpr (METHOD == M_TSIT5) C5 = (Sys::D <= 4) ? tsit5::Coef<R>::pinned() : tsit5::Coef<R>::literal();
+  // the controller's coefficients likewise (with the Tsit5 table pinned the
+  // scalar registers would otherwise overflow)
+  const CtrlCoef<R, CTRL_Q> KC = CtrlCoef<R, CTRL_Q>::make(METHOD == M_TSIT5 && Sys::D <= 4);
 
   Sys sys;
   R y[D];
@@ -270,7 +273,7 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     const R msq = mean_sq<R, D>(err, sc);
     const bool acc = msq <= R(1);
     // One controller evaluation serves both outcomes.
-    const R root = ctrl_root<R, CTRL_Q>(msq);
+    const R root = ctrl_root<R, CTRL_Q>(msq, KC);
     const R fq = (msq == R(0)) ? R(10) : truncBits(R(0.9) * root);
     const R fmin = (R(0.2) < fq) ? fq : R(0.2);
 

@@ -257,6 +257,7 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs a) {
   Fwd P;
   P.load(a.theta, g, j);
   float* const trash = a.trash + 2 * lane;
+  const CtrlCoef<float, 10> KC = CtrlCoef<float, 10>::make(false);
 
   float y = 0.f, k[7];
 #pragma unroll
@@ -348,7 +349,7 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs a) {
     const float sc = fmaR(a.rtol, (ay < an) ? an : ay, a.atol);
     const float msq = slot_mean_sq(err, sc, j);
     const bool acc = msq <= 1.f;
-    const float root = ctrl_root<float, 10>(msq);
+    const float root = ctrl_root<float, 10>(msq, KC);
     const float fq = (msq == 0.f) ? 10.f : truncBits(0.9f * root);
     const float fmin = (0.2f < fq) ? fq : 0.2f;
     int32_t st = (acc && nacc >= a.s_cap) ? TRAJ_CAPACITY : RUNNING;

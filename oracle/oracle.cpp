@@ -540,7 +540,7 @@ inline Cnt trunc_bits(Cnt x) { return Cnt(trunc_bits(x.v)); }
 //   x^(-1/q) = m^(-1/q) * 2^(-b/q) * 2^(-a),
 // where m^(-1/q) and 2^(-f) (f = b/q in [0, 1)) are polynomials in
 // s in [-1, 1] (Chebyshev interpolants of those functions on 400 nodes,
-// rewritten in monomial form, evaluated by Horner's rule with fused
+// rewritten in monomial form, evaluated by Estrin's scheme with fused
 // multiply-adds) and the power of two is exact.
 const double ROOT10_C[8] = {0.9602644780153649,     -0.03200878522189435,  0.005869002336249675,
                             -0.0013696795740665145, 0.0003502086621236076, -9.523230976561381e-05,
@@ -559,16 +559,21 @@ T ctrl_root(T x, int q) {
   const T hi = (q == 10) ? T(1e8) : T(1e5);
   x = std::min(std::max(x, lo), hi);
   int e = 0;
-  T m = std::frexp(x, &e) * T(2.0);  // x = m 2^(e-1), m in [1, 2)
-  e -= 1;
+  const T mh = std::frexp(x, &e);  // x = mh 2^e, mh in [1/2, 1): m = 2 mh in [1, 2)
+  e -= 1;                          // x = m 2^e
   const int a = (e >= 0) ? e / q : -((q - 1 - e) / q);  // floor(e / q)
   const int b = e - q * a;
-  const T s = m * T(2.0) - T(3.0);  // exact
-  T p = T(rc[7]);
-  for (int i = 6; i >= 0; --i) p = fma3(p, s, T(rc[i]));
-  const T s2 = fma3(T(b), T(2.0 / q), T(-1.0));
-  T c = T(EXP2N_C[6]);
-  for (int i = 5; i >= 0; --i) c = fma3(c, s2, T(EXP2N_C[i]));
+  const T s = fma3(mh, T(4.0), T(-3.0));  // 2 m - 3, exact
+  // Estrin's scheme: coefficient pairs, then pairs of pairs.
+  const T s2 = s * s, s4 = s2 * s2;
+  const T p01 = fma3(T(rc[1]), s, T(rc[0])), p23 = fma3(T(rc[3]), s, T(rc[2]));
+  const T p45 = fma3(T(rc[5]), s, T(rc[4])), p67 = fma3(T(rc[7]), s, T(rc[6]));
+  const T p = fma3(fma3(p67, s2, p45), s4, fma3(p23, s2, p01));
+  const T f = fma3(T(b), T(2.0 / q), T(-1.0));
+  const T f2 = f * f, f4 = f2 * f2;
+  const T c01 = fma3(T(EXP2N_C[1]), f, T(EXP2N_C[0])), c23 = fma3(T(EXP2N_C[3]), f, T(EXP2N_C[2]));
+  const T c45 = fma3(T(EXP2N_C[5]), f, T(EXP2N_C[4]));
+  const T c = fma3(fma3(T(EXP2N_C[6]), f2, c45), f4, fma3(c23, f2, c01));
   return std::ldexp(p * c, -a);
 }
 
