@@ -444,3 +444,43 @@ def test_one_order_many_gradients(dao, name, n, s_cap):
         scale = w.theta * f if name == "robertson" else 1.0
         assert rel_err(go[0].cpu().numpy() * scale, dth_o * scale).max() <= TOL
         assert rel_err(go[1].cpu().numpy(), dy0_o).max() <= TOL
+
+
+@pytest.mark.parametrize("name,n,s_cap", [("lorenz63", 1000, 1024), ("mlp", 500, 64)])
+def test_gradient_with_the_minimum_workspace(dao, name, n, s_cap):
+    # A workspace of dao_grad_workspace_min bytes holds the scratch of one
+    # workgroup only: the gradient then runs its groups one workgroup at a
+    # time.  Per-trajectory results are the same bit for bit; the shared
+    # weights of the neural field are summed over other partials (1e-5).
+    from differentiable_adaptive_ode_amd import _lib
+
+    w = di.make(name, n)
+    print(f"[min workspace] {name} n={n}", flush=True)
+    th = torch.tensor(w.theta, device=DEV)
+    y0 = torch.tensor(w.y0, device=DEV)
+    rec, y1 = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=s_cap)
+    lam = torch.tensor(di.cotangent(w, y1.cpu().numpy()).astype(w.y0.dtype), device=DEV)
+    s_max = int(rec.count.max().item())
+    g_full = dao.grad(rec, lam, s_max=s_max)
+    ids = _lib.SYSTEMS[w.system], _lib.METHODS[w.method], _lib.DTYPES[w.dtype]
+    nmin = _lib.dao_grad_workspace_min(*ids, n, s_max)
+    assert 0 < nmin < _lib.dao_grad_workspace_size(*ids, n, s_max)
+    buf = torch.empty(nmin, dtype=torch.uint8, device=DEV)
+    dth = torch.empty_like(g_full[0])
+    dy0 = torch.empty_like(g_full[1])
+    stream = torch.cuda.current_stream().cuda_stream
+    _lib.check(_lib.dao_grad(*ids, n, th.data_ptr(), y0.data_ptr(), rec.c_struct(), s_max,
+                             lam.data_ptr(), dth.data_ptr(), dy0.data_ptr(), buf.data_ptr(),
+                             nmin, stream))
+    torch.cuda.synchronize()
+    assert torch.equal(dy0, g_full[1])
+    if name == "mlp":
+        e = (dth - g_full[0]).norm() / g_full[0].norm()
+        assert e.item() <= 1e-5, e.item()
+    else:
+        assert torch.equal(dth, g_full[0])
+    # one byte less is refused before anything runs
+    with pytest.raises(_lib.DaoError, match="workspace"):
+        _lib.check(_lib.dao_grad(*ids, n, th.data_ptr(), y0.data_ptr(), rec.c_struct(), s_max,
+                                 lam.data_ptr(), dth.data_ptr(), dy0.data_ptr(), buf.data_ptr(),
+                                 nmin - 1, stream))
