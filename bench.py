@@ -65,9 +65,17 @@ WORKLOADS = {
 # directions (decay 2, Lotka-Volterra 4 x 15, Lorenz 15 + 14 + 13, Robertson
 # 14 + 15 + 15, log halo 34 + 36 + 35).
 JVP_SUM = {"decay": 2, "lotka_volterra": 60, "lorenz63": 42, "robertson": 44, "loghalo": 105}
+# Rosenbrock23's tangent per direction: two Jacobian-tangent products with the
+# stages (2 d^2 + 2 d, 2 d^2 + 3 d), two solves with the step's LU factors
+# (2 d^2 - d each), 5 d vector updates = 8 d^2 + 8 d; plus two field JVPs and
+# one Jacobian JVP (JJVP_SUM over the p directions: decay 0, Lotka-Volterra
+# 4 x 14, Lorenz 3 x 1, Robertson 3 x 11).
+JJVP_SUM = {"decay": 0, "lotka_volterra": 56, "lorenz63": 3, "robertson": 33}
 
 
-def _sens_step_flops(d, p, name):
+def _sens_step_flops(d, p, name, method):
+    if method == "rosenbrock23":
+        return p * (8 * d * d + 8 * d) + 2 * JVP_SUM[name] + JJVP_SUM[name]
     return 48 * d * p + 6 * JVP_SUM[name]
 
 
@@ -362,7 +370,7 @@ def bench_sens(args, w):
         raise SystemExit("bench: some trajectories failed")
     attempts, steps_total = int((cnt + nrej).sum()), int(cnt.sum())
     fl_solve = w.n * cfg["init"] + attempts * cfg["att"] + steps_total
-    fl_sens = steps_total * _sens_step_flops(w.d, w.theta.shape[0], w.name)
+    fl_sens = steps_total * _sens_step_flops(w.d, w.theta.shape[0], w.name, w.method)
     ach = (fl_solve + fl_sens) / tk
     from differentiable_adaptive_ode_amd.profiling import load_traffic
 

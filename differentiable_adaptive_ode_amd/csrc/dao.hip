@@ -285,7 +285,7 @@ dao_status launch_grad(int mode, int64_t n, const void* theta, const void* y0, c
 // Forward sensitivities through the replay: the record's trajectories are
 // sorted once, then one pass of sens_kernel per P directions (the
 // parameters, then the initial-state components).
-template <class R, class Sys>
+template <class R, class Sys, int M>
 dao_status launch_sens(int64_t n, const void* theta, const void* y0, const dao_record* rec,
                        int64_t s_max, void* S_theta, void* S_y0, void* ws, hipStream_t stream) {
   constexpr int D = Sys::D, P = Sys::P;
@@ -293,7 +293,7 @@ dao_status launch_sens(int64_t n, const void* theta, const void* y0, const dao_r
   unsigned long long* groups = (unsigned long long*)base;
   uint32_t* hist = (uint32_t*)(base + align_up(16));
   int32_t* perm = (int32_t*)(base + align_up(16) + align_up((size_t)ORDER_BINS * 4));
-  auto kern = sens_kernel<R, Sys, P>;
+  auto kern = sens_kernel<R, Sys, M, P>;
   const int64_t ngroups = (n + WAVE - 1) / WAVE;
   int64_t blocks = (ngroups + BLOCK / WAVE - 1) / (BLOCK / WAVE);
   const int64_t res = resident_blocks(kern);
@@ -468,17 +468,11 @@ struct Entry {
   static dao_status solve_sens(int64_t n, const void* th, const void* y0, double t0, double t1,
                                const dao_tol* tol, void* y1, const dao_record* rec, void* ws,
                                hipStream_t st, void* S_theta) {
-    if constexpr (M == M_TSIT5)
-      return launch_solve<R, S<R>, M, true>(n, th, y0, t0, t1, tol, y1, rec, ws, st, S_theta);
-    else
-      return DAO_EUNSUPPORTED;
+    return launch_solve<R, S<R>, M, true>(n, th, y0, t0, t1, tol, y1, rec, ws, st, S_theta);
   }
   static dao_status sens(int64_t n, const void* th, const void* y0, const dao_record* rec,
                          int64_t s_max, void* S_theta, void* S_y0, void* ws, hipStream_t st) {
-    if constexpr (M == M_TSIT5)
-      return launch_sens<R, S<R>>(n, th, y0, rec, s_max, S_theta, S_y0, ws, st);
-    else
-      return DAO_EUNSUPPORTED;
+    return launch_sens<R, S<R>, M>(n, th, y0, rec, s_max, S_theta, S_y0, ws, st);
   }
   static dao_status states(int64_t n, const void* th, const void* y0, double t0, double t1,
                            const dao_record* rec, int64_t s_max, int64_t m, const void* tq,
@@ -512,7 +506,7 @@ struct Impl {
   slot_fn slot;
   res_fn resident;
   int group;  // trajectories per wavefront in the gradient
-  solve_sens_fn solve_sens;  // forward sensitivities (Tsit5, per-trajectory theta), else null
+  solve_sens_fn solve_sens;  // forward sensitivities (per-trajectory theta), else null
   sens_fn sens;
   states_fn states;  // states at requested times (per-lane systems), else null
 };
@@ -521,11 +515,9 @@ int64_t mlp_resident_waves() { return resident_blocks(mlp::grad_kernel) * (BLOCK
 
 template <class R, template <class> class S, int M>
 Impl make_impl() {
-  const bool fwd = (M == M_TSIT5);
   return Impl{&Entry<R, S, M>::solve, &Entry<R, S, M>::grad, &Entry<R, S, M>::slot_bytes,
-              &Entry<R, S, M>::resident_waves, WAVE,
-              fwd ? &Entry<R, S, M>::solve_sens : nullptr, fwd ? &Entry<R, S, M>::sens : nullptr,
-              &Entry<R, S, M>::states};
+              &Entry<R, S, M>::resident_waves, WAVE, &Entry<R, S, M>::solve_sens,
+              &Entry<R, S, M>::sens, &Entry<R, S, M>::states};
 }
 
 const Impl* find_impl(int sys, int method, int dtype) {

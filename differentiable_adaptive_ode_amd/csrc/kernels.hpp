@@ -112,12 +112,11 @@ __device__ R initial_step(const Sys& sys, const R (&y0)[Sys::D], const R (&f0)[S
 
 // SENS: also integrate the forward sensitivities S = dy/dtheta beside the
 // state, with the steps chosen on the state alone (arXiv 2609.28458 Sec. 2.3
-// and Sec. 3; Tsit5 only).  S starts at zero, takes the tangent of every
-// accepted step and is written to S_theta when the trajectory finishes.
+// and Sec. 3).  S starts at zero, takes the tangent of every accepted step
+// and is written to S_theta when the trajectory finishes.
 template <class R, class Sys, int METHOD, bool SENS = false>
 __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   constexpr int D = Sys::D;
-  static_assert(!SENS || METHOD == M_TSIT5, "forward sensitivities are Tsit5 only");
   constexpr int NS = SENS ? Sys::P : 1;
   R Sv[D][NS];
   int sdir[NS];
@@ -307,7 +306,15 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     const bool take = (st == RUNNING) && acc;
     const R tn = last ? a.t1 : t + hs;
     if constexpr (SENS) {
-      if (take) tsit5::tangent<R, Sys, NS>(C5, sys, y, hs, k, sdir, Sv);
+      if (take) {
+        if constexpr (METHOD == M_TSIT5) {
+          tsit5::tangent<R, Sys, NS>(C5, sys, y, hs, k, sdir, Sv);
+        } else {
+          ros23::Stages<R, D> St;  // the step's factors and stages, recomputed
+          ros23::stages<R, Sys>(sys, y, hs, St);
+          ros23::tangent<R, Sys, NS>(sys, St, hs, sdir, Sv);
+        }
+      }
     }
 #pragma unroll
     for (int c = 0; c < D; ++c) y[c] = take ? ynew[c] : y[c];
@@ -526,7 +533,7 @@ struct SensArgs {
   unsigned long long* groups;
 };
 
-template <class R, class Sys, int NT>
+template <class R, class Sys, int METHOD, int NT>
 __global__ void __launch_bounds__(256) sens_kernel(SensArgs<R> a) {
   constexpr int D = Sys::D, P = Sys::P;
   const int lane = laneId();
@@ -580,17 +587,25 @@ __global__ void __launch_bounds__(256) sens_kernel(SensArgs<R> a) {
     for (int i = 0; i < mx; ++i) {
       const R hj = (i < cnt) ? h_nx : R(0);
       if (i + 1 < mx) h_nx = hrow[i + 1];
-      R kk[7][D], Y[D];
-      sys.f(y, kk[0]);
+      if constexpr (METHOD == M_TSIT5) {
+        R kk[7][D], Y[D];
+        sys.f(y, kk[0]);
 #pragma unroll
-      for (int st = 1; st < 6; ++st) {
-        tsit5::stage_state<R, D>(C5, st, y, hj, kk, Y);
-        sys.f(Y, kk[st]);
+        for (int st = 1; st < 6; ++st) {
+          tsit5::stage_state<R, D>(C5, st, y, hj, kk, Y);
+          sys.f(Y, kk[st]);
+        }
+        tsit5::tangent<R, Sys, NT>(C5, sys, y, hj, kk, pdir, S);
+        tsit5::stage_state<R, D>(C5, 6, y, hj, kk, Y);
+#pragma unroll
+        for (int c = 0; c < D; ++c) y[c] = Y[c];
+      } else {
+        ros23::Stages<R, D> St;
+        ros23::stages<R, Sys>(sys, y, hj, St);
+        ros23::tangent<R, Sys, NT>(sys, St, hj, pdir, S);
+#pragma unroll
+        for (int c = 0; c < D; ++c) y[c] = fmaR(hj, St.u[c] + St.k1[c], y[c]);  // as ros23::replay
       }
-      tsit5::tangent<R, Sys, NT>(C5, sys, y, hj, kk, pdir, S);
-      tsit5::stage_state<R, D>(C5, 6, y, hj, kk, Y);
-#pragma unroll
-      for (int c = 0; c < D; ++c) y[c] = Y[c];
     }
     if (k >= 0) {
 #pragma unroll

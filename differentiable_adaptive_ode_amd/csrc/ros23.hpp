@@ -269,5 +269,52 @@ __device__ __forceinline__ void sweep(const Sys& sys, const Stages<R, Sys::D>& S
   sys.jac_vjp(S.y, Jb, lam, pb);
 }
 
+// Tangent of one replay step along NT directions (arXiv 2609.28458 Sec. 2.3:
+// the sensitivity equations with the steps held fixed), from the step's
+// forward quantities St (stages() at the same y and h).  Direction t is the
+// parameter dir[t] (none for dir[t] < 0 or >= P).  On entry S[c][t] = dy_c/dp_t,
+// on exit the tangent of y_new = y + h (u + k1):
+//   Wd = -h d Jd,  k1d = W^-1 (F0d - Wd k1),  Y1d = yd + h/2 k1d,
+//   ud = W^-1 (F1d - k1d - Wd u),  y_new d = yd + h (ud + k1d),
+// with F0d, F1d the field's tangents at y and Y1 and Jd the Jacobian's.
+template <class R, class Sys, int NT>
+__device__ __forceinline__ void tangent(const Sys& sys, const Stages<R, Sys::D>& St, R h,
+                                        const int (&dir)[NT], R (&S)[Sys::D][NT]) {
+  constexpr int D = Sys::D;
+  const R hh = R(0.5) * h, hd = h * R(GAMMA);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    R yd[D], F0d[D], F1d[D], k1d[D], Y1d[D], ud[D], r[D];
+    R Jd[D][D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) yd[c] = S[c][t];
+    sys.jvp(St.y, yd, dir[t], F0d);
+    sys.jac_jvp(St.y, yd, dir[t], Jd);
+    // F0d - Wd k1 = F0d + h d Jd k1
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      R acc = R(0);
+#pragma unroll
+      for (int j = 0; j < D; ++j) acc = fmaR(Jd[i][j], St.k1[j], acc);
+      r[i] = fmaR(hd, acc, F0d[i]);
+    }
+    solve<R, D>(St.w, r, k1d);
+#pragma unroll
+    for (int c = 0; c < D; ++c) Y1d[c] = fmaR(hh, k1d[c], yd[c]);
+    sys.jvp(St.Y1, Y1d, dir[t], F1d);
+    // F1d - k1d - Wd u = F1d - k1d + h d Jd u
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      R acc = R(0);
+#pragma unroll
+      for (int j = 0; j < D; ++j) acc = fmaR(Jd[i][j], St.u[j], acc);
+      r[i] = fmaR(hd, acc, F1d[i] - k1d[i]);
+    }
+    solve<R, D>(St.w, r, ud);
+#pragma unroll
+    for (int c = 0; c < D; ++c) S[c][t] = fmaR(h, ud[c] + k1d[c], yd[c]);
+  }
+}
+
 }  // namespace ros23
 }  // namespace dao

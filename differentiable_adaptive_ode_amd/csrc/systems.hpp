@@ -14,6 +14,9 @@
 //                          j outside [0, P)): one column of the sensitivity
 //                          equations S' = (df/dy) S + df/dtheta (arXiv
 //                          2609.28458 Sec. 2.3)
+//   jac_jvp(y, yd, j, Jd)  Jd = d/de J(y + e yd, theta + e e_j) at e = 0: the
+//                          tangent of the Jacobian, which the tangent of a
+//                          Rosenbrock step needs (W = I - gamma h J moves too)
 // The vector-Jacobian products are derived by hand from the formulas below.
 #pragma once
 
@@ -39,6 +42,10 @@ struct Decay {
   }
   __device__ void jvp(const R (&y)[D], const R (&yd)[D], int j, R (&fd)[D]) const {
     fd[0] = (j == 0) ? -fmaR(th, yd[0], y[0]) : -(th * yd[0]);
+  }
+  __device__ void jac_jvp(const R (&y)[D], const R (&yd)[D], int j, R (&Jd)[D][D]) const {
+    (void)y; (void)yd;
+    Jd[0][0] = (j == 0) ? R(-1) : R(0);
   }
 };
 
@@ -85,6 +92,14 @@ struct LotkaVolterra {
     fd[0] = fmaR(fmaR(-b, y[1], a), yd[0], fmaR(-(b * y[0]), yd[1], p0));
     fd[1] = fmaR(d * y[1], yd[0], fmaR(fmaR(d, y[0], -g), yd[1], p1));
   }
+  __device__ void jac_jvp(const R (&y)[D], const R (&yd)[D], int j, R (&Jd)[D][D]) const {
+    const R ad = (j == 0) ? R(1) : R(0), bd = (j == 1) ? R(1) : R(0);
+    const R gd = (j == 2) ? R(1) : R(0), dd = (j == 3) ? R(1) : R(0);
+    Jd[0][0] = ad - fmaR(bd, y[1], b * yd[1]);
+    Jd[0][1] = -fmaR(bd, y[0], b * yd[0]);
+    Jd[1][0] = fmaR(dd, y[1], d * yd[1]);
+    Jd[1][1] = fmaR(dd, y[0], d * yd[0]) - gd;
+  }
 };
 
 // Lorenz-63, theta = (sigma, rho, beta).
@@ -128,6 +143,13 @@ struct Lorenz63 {
     fd[0] = (j == 0) ? fmaR(s, d10, y[1] - y[0]) : s * d10;
     fd[1] = fmaR(r - y[2], yd[0], fmaR(-y[0], yd[2], (j == 1) ? y[0] - yd[1] : -yd[1]));
     fd[2] = fmaR(y[1], yd[0], fmaR(y[0], yd[1], -fmaR(b, yd[2], (j == 2) ? y[2] : R(0))));
+  }
+  __device__ void jac_jvp(const R (&y)[D], const R (&yd)[D], int j, R (&Jd)[D][D]) const {
+    (void)y;
+    const R sd = (j == 0) ? R(1) : R(0), rd = (j == 1) ? R(1) : R(0), bd = (j == 2) ? R(1) : R(0);
+    Jd[0][0] = -sd; Jd[0][1] = sd; Jd[0][2] = R(0);
+    Jd[1][0] = rd - yd[2]; Jd[1][1] = R(0); Jd[1][2] = -yd[0];
+    Jd[2][0] = yd[1]; Jd[2][1] = yd[0]; Jd[2][2] = -bd;
   }
 };
 
@@ -186,6 +208,15 @@ struct Robertson {
     fd[0] = cd - ad;
     fd[1] = (ad - bd) - cd;
     fd[2] = bd;
+  }
+  __device__ void jac_jvp(const R (&y)[D], const R (&yd)[D], int j, R (&Jd)[D][D]) const {
+    const R k1d = (j == 0) ? R(1) : R(0), k2d = (j == 1) ? R(1) : R(0), k3d = (j == 2) ? R(1) : R(0);
+    const R j12 = fmaR(k3d, y[2], k3 * yd[2]);                        // (k3 y3)'
+    const R j13 = fmaR(k3d, y[1], k3 * yd[1]);                        // (k3 y2)'
+    const R t = R(2) * fmaR(k2d, y[1], k2 * yd[1]);                   // (2 k2 y2)'
+    Jd[0][0] = -k1d; Jd[0][1] = j12;        Jd[0][2] = j13;
+    Jd[1][0] = k1d;  Jd[1][1] = -(t + j12); Jd[1][2] = -j13;
+    Jd[2][0] = R(0); Jd[2][1] = t;          Jd[2][2] = R(0);
   }
 };
 
@@ -259,6 +290,14 @@ struct LogHalo {
   __device__ void jac_vjp(const R (&y)[D], const R (&Jb)[D][D], R (&yb)[D], R (&pb)[P]) const {
     // Not used: the halo has no Rosenbrock path (dao_solve/dao_grad refuse it).
     (void)y; (void)Jb; (void)yb; (void)pb;
+  }
+  __device__ void jac_jvp(const R (&y)[D], const R (&yd)[D], int j, R (&Jd)[D][D]) const {
+    // Not used: the halo has no Rosenbrock path.
+    (void)y; (void)yd; (void)j;
+#pragma unroll
+    for (int a = 0; a < D; ++a)
+#pragma unroll
+      for (int c = 0; c < D; ++c) Jd[a][c] = R(0);
   }
   // a = -A g: ad = -(Ad g + A gd) with Dnd = 2 <g, (xd, yd, zd)> + dRc^2 + z^2 d(1/q^2),
   // Ad = d(v0^2) / Dn - A Dnd / Dn, gd = (xd, yd, zd / q^2 + z d(1/q^2)).

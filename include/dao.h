@@ -195,10 +195,10 @@ dao_status dao_grad_ordered(dao_system sys, dao_method method, dao_dtype dtype, 
  * state, with the step size chosen on the state alone (its Sec. 2.3 and
  * Sec. 3; eq. 2).  With the steps held fixed that is the exact derivative of
  * the discrete solution on the recorded mesh, the same quantity the forward
- * mode through the replay of the record gives (gradsolve Sec. 3.1).  Tsit5
- * with per-trajectory parameters only: DAO_EUNSUPPORTED for Rosenbrock23
- * and for the neural field (whose 4740 shared weights are a reverse-mode
- * case).  Layouts: S_theta real[d][p][n] with S_theta[(c p + j) n + k] =
+ * mode through the replay of the record gives (gradsolve Sec. 3.1).  Both
+ * methods; for Rosenbrock23 the tangent of W = I - gamma h J is included.
+ * Per-trajectory parameters only: DAO_EUNSUPPORTED for the neural field
+ * (whose 4740 shared weights are a reverse-mode case).  Layouts: S_theta real[d][p][n] with S_theta[(c p + j) n + k] =
  * dy1_c/dtheta_j of trajectory k; S_y0 real[d][d][n] likewise.  Failed
  * trajectories get NaN.
  *

@@ -140,7 +140,6 @@ def test_sensitivity_argument_errors(L):
 
     assert solve_sens(S=None) == 1
     assert "dao_solve_sens" in L.dao_last_error()
-    assert solve_sens(system=4, method=1) == 4      # Rosenbrock23: no forward sensitivities
     assert solve_sens(system=3, dtype=1) == 4       # neural field: shared weights
     assert solve_sens(ws=None) == 3
     assert solve_sens(n=0) == 0                     # empty ensemble: nothing to do
@@ -155,10 +154,10 @@ def test_sensitivity_argument_errors(L):
     assert sens(s_max=17) == 1
     assert sens(theta=None) == 1
     assert sens(ws=None) == 3
-    assert sens(system=4, method=1) == 4
+    assert sens(system=3) == 4                      # the neural field: reverse mode only
     assert sens(n=0) == 0
     assert L.dao_sens_workspace_size(2, 0, 0, 100, 50) > 0
-    assert L.dao_sens_workspace_size(4, 1, 0, 100, 50) == 0   # not provided
+    assert L.dao_sens_workspace_size(3, 0, 1, 100, 50) == 0   # not provided
 
 
 def test_states_at_argument_errors(L):
