@@ -204,9 +204,11 @@ dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0,
   return check_hip(hipGetLastError(), "solve kernel launch");
 }
 
+// Per-wavefront scratch tile of the gradient: per step the D state
+// components and h, 64 lanes each.
 template <class R, int D>
 size_t grad_slot_bytes(int64_t s_max) {
-  return (size_t)(s_max > 0 ? s_max : 1) * D * WAVE * sizeof(R);
+  return (size_t)(s_max > 0 ? s_max : 1) * (D + 1) * WAVE * sizeof(R);
 }
 
 size_t grad_header_bytes(int64_t n, int64_t s_max) {

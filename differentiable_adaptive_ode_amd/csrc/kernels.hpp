@@ -41,7 +41,7 @@ struct SolveArgs {
   int32_t* nrej;
   int32_t* status;
   R* y_rec;  // optional [n][s_cap][D]: the state at the start of each accepted step
-  unsigned long long* queue;
+  unsigned long long* queue;  // trajectories handed out so far (zero at launch)
   R* trash;  // [64][2] scratch target of record stores that have no row
   R* S_theta;  // forward sensitivities dy1/dtheta [D][P][n] (solve_kernel<..., true>)
 };
@@ -196,56 +196,71 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     traj = -1;
   };
 
-  // Once a claim comes back past the end of the ensemble, the queue is empty
-  // for good: the wavefront stops claiming (a device-scope atomic is a round
-  // trip to the coherence point, and every wavefront hitting one counter
-  // serialises there).
-  bool drained = false;
+  // Work distribution.  The queue hands out batches of 64 consecutive
+  // trajectories, one device-scope atomic per batch; within its batch a
+  // wavefront gives the next index to whichever lane asks first (a
+  // wave-uniform cursor).  Batches keep the atomic rate low when trajectories
+  // are short and many per lane (one queue hit per finished trajectory
+  // serialises every wavefront on one counter), while the ensemble stays
+  // balanced across wavefronts.
+  constexpr int64_t BATCH = WAVE;
+  int64_t cursor = 0, bend = 0;  // the wavefront's current batch [cursor, bend)
+  bool drained = false;          // the queue has nothing left
   for (;;) {
-    // ---- refill idle lanes from the work queue: one atomic per wavefront
     const bool need = live && traj < 0;
-    if (drained && need) live = false;
-    const unsigned long long m = drained ? 0ull : __ballot(need);
+    const unsigned long long m = __ballot(need);
     if (m) {
-      const int leader = __ffsll((unsigned long long)m) - 1;
-      unsigned long long base = 0;
-      if (lane == leader) base = atomicAdd(a.queue, (unsigned long long)__popcll(m));
-      base = __shfl(base, leader);
-      if (base + (unsigned long long)__popcll(m) >= (unsigned long long)a.n) drained = true;
-      if (need) {
-        const unsigned long long kk = base + (unsigned long long)__popcll(m & ((1ull << lane) - 1ull));
-        if (kk < (unsigned long long)a.n) {
-          traj = (int64_t)kk;
-          sys.load(a.theta, a.n, traj);
+      const int64_t cnt_w = (int64_t)__popcll(m);
+      const int64_t rank = (int64_t)__popcll(m & ((1ull << lane) - 1ull));
+      const int64_t left = bend - cursor;           // indices left in the batch
+      const bool more = cnt_w > left && !drained;  // take a new batch (one atomic)
+      int64_t base = a.n;
+      if (more) {
+        unsigned long long b = 0;
+        if (lane == 0) b = atomicAdd(a.queue, (unsigned long long)BATCH);
+        base = (int64_t)__shfl(b, 0);
+        if (base + BATCH >= a.n) drained = true;
+      }
+      // ranks below `left` take the rest of the batch, the others the start
+      // of the new one (rank - left < 64, as at most 64 lanes ask at once)
+      const int64_t kk = (rank < left) ? cursor + rank : (more ? base + (rank - left) : a.n);
+      if (more) {
+        bend = (base + BATCH < a.n) ? base + BATCH : a.n;
+        cursor = base + (cnt_w - left);
+        if (cursor > bend) cursor = bend;
+      } else {
+        cursor = (cursor + cnt_w < bend) ? cursor + cnt_w : bend;
+      }
+      if (need && kk >= a.n) live = false;  // nothing left for this lane
+      if (need && kk < a.n) {
+        traj = kk;
+        sys.load(a.theta, a.n, traj);
 #pragma unroll
-          for (int c = 0; c < D; ++c) y[c] = a.y0[c * a.n + traj];
-          // Loads and stores share one in-order counter (vmcnt).  Waiting
-          // here, once per trajectory, keeps the attempt loop below free of
-          // waits that would otherwise also drain the record stores of the
-          // previous attempt.
-          __builtin_amdgcn_s_waitcnt(0);
-          hrow = a.h_rec + traj * a.s_cap;
-          trow = a.t_rec ? a.t_rec + traj * a.s_cap : nullptr;
-          yrow = a.y_rec ? a.y_rec + traj * a.s_cap * D : nullptr;
-          t = a.t0;
-          nacc = 0;
-          nrej = 0;
-          if constexpr (SENS) {
+        for (int c = 0; c < D; ++c) y[c] = a.y0[c * a.n + traj];
+        // Loads and stores share one in-order counter (vmcnt).  Waiting here,
+        // once per trajectory, keeps the attempt loop free of waits on these
+        // loads, which would otherwise also drain the record stores of every
+        // previous attempt.
+        __builtin_amdgcn_s_waitcnt(0);
+        hrow = a.h_rec + traj * a.s_cap;
+        trow = a.t_rec ? a.t_rec + traj * a.s_cap : nullptr;
+        yrow = a.y_rec ? a.y_rec + traj * a.s_cap * D : nullptr;
+        t = a.t0;
+        nacc = 0;
+        nrej = 0;
+        if constexpr (SENS) {
 #pragma unroll
-            for (int c = 0; c < D; ++c)
+          for (int c = 0; c < D; ++c)
 #pragma unroll
-              for (int j = 0; j < NS; ++j) Sv[c][j] = R(0);
-          }
-          attempts = 0;
-          prev_rej = false;
-          if (!(a.t1 > a.t0)) {
-            finish(TRAJ_OK);
-          } else {
-            sys.f(y, k[0]);
-            h = (a.dt0 > R(0)) ? a.dt0 : initial_step<R, Sys>(sys, y, k[0], a.t1 - a.t0, a.rtol, a.atol, ORDER);
-          }
+            for (int j = 0; j < NS; ++j) Sv[c][j] = R(0);
+        }
+        attempts = 0;
+        prev_rej = false;
+        if (!(a.t1 > a.t0)) {
+          finish(TRAJ_OK);
         } else {
-          live = false;
+          sys.f(y, k[0]);
+          h = (a.dt0 > R(0)) ? a.dt0 : initial_step<R, Sys>(sys, y, k[0], a.t1 - a.t0, a.rtol, a.atol, ORDER);
         }
       }
     }
@@ -367,7 +382,7 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
   tsit5::Coef<R> C5;
   if constexpr (METHOD == M_TSIT5) C5 = (Sys::D <= 4) ? tsit5::Coef<R>::pinned() : tsit5::Coef<R>::literal();
   const int64_t slot = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
-  R* scr = a.scratch + slot * (a.s_max * D * WAVE) + lane;
+  R* scr = a.scratch + slot * (a.s_max * (D + 1) * WAVE) + lane;  // tile [s_max][D + 1][64]
   const unsigned long long ngroups = (unsigned long long)((a.n + WAVE - 1) / WAVE);
 
   for (;;) {
@@ -437,9 +452,13 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
     // tile is s_max x d x 512 bytes): they stream through the L2 as
     // nontemporal accesses, which leaves the lines of the h rows, each read
     // eight bytes per step, resident between their steps.
+    // The scratch tile holds, per step, the D state components and the
+    // step's h (zero past the lane's count), so that the reverse sweep reads
+    // both as whole 512-byte rows instead of h again from 64 record rows.
     const bool rec_y = a.y_rec != nullptr;
+    constexpr int SD = D + 1;
     const R* ysrc = rec_y ? a.y_rec + (k >= 0 ? k : 0) * a.s_cap * D : scr;
-    const int64_t istr = rec_y ? D : (int64_t)D * WAVE, cstr = rec_y ? 1 : WAVE;
+    const int64_t istr = rec_y ? D : (int64_t)SD * WAVE, cstr = rec_y ? 1 : WAVE;
     R h_nx = (mx > 0) ? hrow[0] : R(0);
     if (!rec_y) {
       for (int i = 0; i < mx; ++i) {
@@ -447,7 +466,8 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
         if (i + 1 < mx) h_nx = hrow[i + 1];
 #pragma unroll
         for (int c = 0; c < D; ++c)
-          __builtin_nontemporal_store(y[c], &scr[((int64_t)i * D + c) * WAVE]);
+          __builtin_nontemporal_store(y[c], &scr[((int64_t)i * SD + c) * WAVE]);
+        __builtin_nontemporal_store(hj, &scr[((int64_t)i * SD + D) * WAVE]);
         if constexpr (METHOD == M_TSIT5)
           tsit5::replay<R, Sys>(C5, sys, y, hj);
         else
@@ -463,11 +483,15 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
 #pragma unroll
     for (int c = 0; c < D; ++c) y_nx[c] = R(0);
     h_nx = R(0);
+    // h of row i: from the tile (zero past the count already), or the record
+    auto h_at = [&](int i) -> R {
+      return rec_y ? hrow[i] : __builtin_nontemporal_load(&scr[((int64_t)i * SD + D) * WAVE]);
+    };
     if (mx > 0) {
 #pragma unroll
       for (int c = 0; c < D; ++c)
         y_nx[c] = __builtin_nontemporal_load(&ysrc[(int64_t)(mx - 1) * istr + c * cstr]);
-      h_nx = hrow[mx - 1];
+      h_nx = h_at(mx - 1);
     }
     for (int i = mx - 1; i >= 0; --i) {
       R yj[D];
@@ -478,7 +502,7 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
 #pragma unroll
         for (int c = 0; c < D; ++c)
           y_nx[c] = __builtin_nontemporal_load(&ysrc[(int64_t)(i - 1) * istr + c * cstr]);
-        h_nx = hrow[i - 1];
+        h_nx = h_at(i - 1);
       }
       if constexpr (METHOD == M_TSIT5) {
         tsit5::Stages<R, D> S;
