@@ -249,7 +249,7 @@ def main():
     # WRITE_SIZE, copy-calibrated), only if taken on the current kernel sources.
     from differentiable_adaptive_ode_amd.profiling import load_traffic
 
-    tr = load_traffic(w.name)
+    tr = load_traffic(w.name, w.n)
     traffic = None
     if tr is not None and f"{dom}_kernel" in tr["kernels"]:
         traffic = tr["kernels"][f"{dom}_kernel"]["hbm_bytes"]
@@ -374,7 +374,7 @@ def bench_sens(args, w):
     ach = (fl_solve + fl_sens) / tk
     from differentiable_adaptive_ode_amd.profiling import load_traffic
 
-    tr = load_traffic(f"{w.name}_sens")
+    tr = load_traffic(f"{w.name}_sens", w.n)
     kern = "solve_sens_kernel"
     traffic = tr["kernels"][kern]["hbm_bytes"] if tr and kern in tr["kernels"] else None
     out = {

@@ -49,14 +49,15 @@ def traffic_path(workload: str, root: str | None = None) -> str:
     return os.path.join(root, f"traffic_{workload}.json")
 
 
-def load_traffic(workload: str):
-    """Measured HBM bytes per launch for the current kernel sources, or None."""
+def load_traffic(workload: str, n: int):
+    """Measured HBM bytes per launch for the current kernel sources at ensemble
+    size n, or None (no profile, other sources, or another size)."""
     p = traffic_path(workload)
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha256") != kernel_source_digest():
+    if d.get("kernel_source_sha256") != kernel_source_digest() or d.get("n") != n:
         return None
     return d
 
