@@ -17,7 +17,10 @@
 // largest magnitude); the reciprocal pivots are formed once per
 // factorisation and the elimination and every solve multiply by them.  The
 // pivot index is data dependent, so rows are exchanged with selects on
-// compile-time indices to keep every value in a register.
+// compile-time indices to keep every value in a register.  When no lane of
+// the wavefront exchanges rows at a step (the usual case: for Robertson's W
+// the diagonal always pivots), the selects of that step are skipped on a
+// wavefront-uniform branch; they would leave every value as it is.
 #pragma once
 
 #include "common.hpp"
@@ -33,6 +36,7 @@ struct LU {
   R m[D][D];   // unit-lower L below the diagonal, U on and above
   R rp[D];     // reciprocal pivots 1 / u_kk (elimination and solves multiply by them)
   int piv[D];  // row exchanged with row k at elimination step k
+  bool swaps;  // some lane of the wavefront exchanges rows (wavefront-uniform)
 };
 
 template <class R, int D>
@@ -47,14 +51,19 @@ __device__ __forceinline__ void factor(LU<R, D>& f) {
       if (v > best) { best = v; p = i; }
     }
     f.piv[k] = p;
+    const bool any = (k + 1 < D) && __ballot(p != k) != 0ull;
+    if (k == 0) f.swaps = any;
+    else f.swaps = f.swaps || any;
+    if (any) {
 #pragma unroll
-    for (int i = k + 1; i < D; ++i) {
-      const bool sw = (p == i);
+      for (int i = k + 1; i < D; ++i) {
+        const bool sw = (p == i);
 #pragma unroll
-      for (int j = 0; j < D; ++j) {
-        R rk = f.m[k][j], ri = f.m[i][j];
-        f.m[k][j] = sw ? ri : rk;
-        f.m[i][j] = sw ? rk : ri;
+        for (int j = 0; j < D; ++j) {
+          R rk = f.m[k][j], ri = f.m[i][j];
+          f.m[k][j] = sw ? ri : rk;
+          f.m[i][j] = sw ? rk : ri;
+        }
       }
     }
     f.rp[k] = R(1) / f.m[k][k];
@@ -74,14 +83,16 @@ __device__ __forceinline__ void solve(const LU<R, D>& f, const R (&b)[D], R (&x)
   R z[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) z[i] = b[i];
+  if (f.swaps) {
 #pragma unroll
-  for (int k = 0; k < D; ++k) {
+    for (int k = 0; k < D; ++k) {
 #pragma unroll
-    for (int i = k + 1; i < D; ++i) {
-      const bool sw = (f.piv[k] == i);
-      R zk = z[k], zi = z[i];
-      z[k] = sw ? zi : zk;
-      z[i] = sw ? zk : zi;
+      for (int i = k + 1; i < D; ++i) {
+        const bool sw = (f.piv[k] == i);
+        R zk = z[k], zi = z[i];
+        z[k] = sw ? zi : zk;
+        z[i] = sw ? zk : zi;
+      }
     }
   }
 #pragma unroll
@@ -119,14 +130,16 @@ __device__ __forceinline__ void solve_t(const LU<R, D>& f, const R (&b)[D], R (&
       if (j > i) acc = fmaR(-f.m[j][i], x[j], acc);
     x[i] = acc;
   }
+  if (f.swaps) {
 #pragma unroll
-  for (int k = D - 1; k >= 0; --k) {
+    for (int k = D - 1; k >= 0; --k) {
 #pragma unroll
-    for (int i = k + 1; i < D; ++i) {
-      const bool sw = (f.piv[k] == i);
-      R xk = x[k], xi = x[i];
-      x[k] = sw ? xi : xk;
-      x[i] = sw ? xk : xi;
+      for (int i = k + 1; i < D; ++i) {
+        const bool sw = (f.piv[k] == i);
+        R xk = x[k], xi = x[i];
+        x[k] = sw ? xi : xk;
+        x[i] = sw ? xk : xi;
+      }
     }
   }
 }
