@@ -373,7 +373,9 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
 }
 
 template <class R, class Sys, int METHOD>
-__global__ void __launch_bounds__(256) grad_kernel(GradArgs<R> a) {
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu((METHOD == M_ROS23 && Sys::D <= 3) ? 4 : 1)))
+grad_kernel(GradArgs<R> a) {
   constexpr int D = Sys::D, P = Sys::P;
   const int lane = laneId();
   // Tsit5 coefficients pinned to registers where the state is small enough

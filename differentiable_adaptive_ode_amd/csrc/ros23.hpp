@@ -31,6 +31,10 @@ namespace ros23 {
 __device__ constexpr double GAMMA = 0.29289321881345248;  // 1 / (2 + sqrt 2)
 __device__ constexpr double E32 = 7.4142135623730951;     // 6 + sqrt 2
 
+// Keeps the compiler from turning a skippable block into selects executed
+// every time (an empty asm statement cannot be speculated).
+__device__ __forceinline__ void skip_point() { asm volatile("" ::: "memory"); }
+
 template <class R, int D>
 struct LU {
   R m[D][D];   // unit-lower L below the diagonal, U on and above
@@ -55,6 +59,7 @@ __device__ __forceinline__ void factor(LU<R, D>& f) {
     if (k == 0) f.swaps = any;
     else f.swaps = f.swaps || any;
     if (any) {
+      skip_point();
 #pragma unroll
       for (int i = k + 1; i < D; ++i) {
         const bool sw = (p == i);
@@ -84,6 +89,7 @@ __device__ __forceinline__ void solve(const LU<R, D>& f, const R (&b)[D], R (&x)
 #pragma unroll
   for (int i = 0; i < D; ++i) z[i] = b[i];
   if (f.swaps) {
+    skip_point();
 #pragma unroll
     for (int k = 0; k < D; ++k) {
 #pragma unroll
@@ -131,6 +137,7 @@ __device__ __forceinline__ void solve_t(const LU<R, D>& f, const R (&b)[D], R (&
     x[i] = acc;
   }
   if (f.swaps) {
+    skip_point();
 #pragma unroll
     for (int k = D - 1; k >= 0; --k) {
 #pragma unroll
