@@ -168,10 +168,56 @@ int64_t resident_blocks(K kernel, size_t lds = 0) {
 }
 
 // --------------------------------------------------------- typed launchers
+void launch_order(const int32_t* count, int64_t n, int64_t s_max, uint32_t* hist, int32_t* perm,
+                  hipStream_t stream);
+
+// Two-phase solve of large ensembles.  When the ensemble is several times
+// the solve's resident lanes, the order in which trajectories are handed out
+// decides how long the last ones run alone: phase 1 takes the first
+// SOLVE_PROBE attempts of every trajectory and predicts each one's remaining
+// attempts from the time those covered; the suspended trajectories are
+// sorted by that prediction and phase 2 resumes them longest first.  Every
+// trajectory takes the same attempts as in one phase, bit for bit.
+constexpr int32_t SOLVE_PROBE = 16;
+
+size_t solve_base_bytes() { return ALIGN + align_up((size_t)WAVE * 2 * sizeof(double)); }
+
+template <class R, int D>
+size_t solve_phase_bytes(int64_t n) {  // save, save_i, key, perm, histogram
+  return align_up((size_t)(2 * D + 2) * n * sizeof(R)) + align_up((size_t)2 * n * 4) +
+         2 * align_up((size_t)n * 4) + align_up((size_t)ORDER_BINS * 4);
+}
+
+// Whether a solve of n trajectories takes two phases: n at least four times
+// the resident lanes and a record capacity of at least 64 probes' worth of
+// steps (DAO_SOLVE_PHASES=1 or 2 forces one or two).  The capacity is the
+// caller's bound on a trajectory's length: resuming a trajectory costs its
+// wavefront a few memory round trips, which short trajectories (tens of
+// steps) do not repay, while long ones are where a late start runs alone.
+// s_cap < 0 asks whether two phases are possible at all (workspace sizing).
+template <class R, class Sys, int M>
+bool solve_two_phase(int64_t n, int64_t s_cap) {
+  if (n <= 0) return false;
+  if (const char* e = getenv("DAO_SOLVE_PHASES")) {
+    if (e[0] == '1') return false;
+    if (e[0] == '2') return true;
+  }
+  if (s_cap >= 0 && s_cap < 64 * SOLVE_PROBE) return false;
+  auto kern = solve_kernel<R, Sys, M, false, true>;
+  const size_t lds = (size_t)BLOCK_WAVES * 2 * 8 * WAVE * sizeof(R);
+  return n >= 4 * resident_blocks(kern, lds) * BLOCK;
+}
+
+template <class R, class Sys, int M>
+size_t solve_ws_bytes(int64_t n) {
+  return solve_base_bytes() +
+         (solve_two_phase<R, Sys, M>(n, -1) ? solve_phase_bytes<R, Sys::D>(n) : 0);
+}
+
 template <class R, class Sys, int M, bool SENS = false>
 dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0, double t1,
                         const dao_tol* tol, void* y1, const dao_record* rec, void* ws,
-                        hipStream_t stream, void* S_theta = nullptr) {
+                        size_t ws_bytes, hipStream_t stream, void* S_theta = nullptr) {
   SolveArgs<R> a;
   a.S_theta = (R*)S_theta;
   a.n = n;
@@ -193,10 +239,46 @@ dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0,
   a.y_rec = (R*)rec->y;
   a.queue = (unsigned long long*)ws;
   a.trash = (R*)((char*)ws + ALIGN);
+  a.phase = 0;
+  a.probe = 0;
+  a.save = nullptr;
+  a.save_i = nullptr;
+  a.key = nullptr;
+  a.order = nullptr;
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)ws, (int64_t)2, 0u);
-  auto kern = solve_kernel<R, Sys, M, SENS>;
   // record staging ring: (t, h [, y]) x 8 slots x 64 lanes per wavefront
   const size_t lds = (size_t)BLOCK_WAVES * (rec->y ? 2 + Sys::D : 2) * 8 * WAVE * sizeof(R);
+  if constexpr (!SENS) {
+    if (solve_two_phase<R, Sys, M>(n, rec->s_cap) &&
+        ws_bytes >= solve_base_bytes() + solve_phase_bytes<R, Sys::D>(n)) {
+      constexpr int D = Sys::D;
+      char* p = (char*)ws + solve_base_bytes();
+      a.save = (R*)p;
+      p += align_up((size_t)(2 * D + 2) * n * sizeof(R));
+      a.save_i = (int32_t*)p;
+      p += align_up((size_t)2 * n * 4);
+      a.key = (int32_t*)p;
+      p += align_up((size_t)n * 4);
+      int32_t* perm = (int32_t*)p;
+      p += align_up((size_t)n * 4);
+      uint32_t* hist = (uint32_t*)p;
+      auto kern = solve_kernel<R, Sys, M, false, true>;
+      int64_t blocks = (n + BLOCK - 1) / BLOCK;
+      const int64_t res = resident_blocks(kern, lds);
+      if (blocks > res) blocks = res;
+      a.phase = 1;
+      a.probe = SOLVE_PROBE;
+      hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), lds, stream, a);
+      launch_order(a.key, n, ORDER_KEY_MAX, hist, perm, stream);
+      hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)ws, (int64_t)2,
+                         0u);
+      a.phase = 2;
+      a.order = perm;
+      hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), lds, stream, a);
+      return check_hip(hipGetLastError(), "solve kernel launch");
+    }
+  }
+  auto kern = solve_kernel<R, Sys, M, SENS>;
   int64_t blocks = (n + BLOCK - 1) / BLOCK;
   const int64_t res = resident_blocks(kern, lds);
   if (blocks > res) blocks = res;
@@ -363,7 +445,8 @@ dao_status launch_states(int64_t n, const void* theta, const void* y0, double t0
 // ------------------------------------------------- neural right-hand side
 dao_status launch_mlp_solve(int64_t n, const void* theta, const void* y0, double t0, double t1,
                             const dao_tol* tol, void* y1, const dao_record* rec, void* ws,
-                            hipStream_t stream) {
+                            size_t ws_bytes, hipStream_t stream) {
+  (void)ws_bytes;
   mlp::SolveArgs a;
   a.n = n;
   a.theta = (const float*)theta;
@@ -459,9 +542,10 @@ template <class R, template <class> class S, int M>
 struct Entry {
   static dao_status solve(int64_t n, const void* th, const void* y0, double t0, double t1,
                           const dao_tol* tol, void* y1, const dao_record* rec, void* ws,
-                          hipStream_t st) {
-    return launch_solve<R, S<R>, M>(n, th, y0, t0, t1, tol, y1, rec, ws, st);
+                          size_t wsb, hipStream_t st) {
+    return launch_solve<R, S<R>, M>(n, th, y0, t0, t1, tol, y1, rec, ws, wsb, st);
   }
+  static size_t solve_ws(int64_t n) { return solve_ws_bytes<R, S<R>, M>(n); }
   static dao_status grad(int mode, int64_t n, const void* th, const void* y0, const dao_record* rec,
                          int64_t s_max, const void* g, void* dth, void* dy0, void* ws,
                          size_t wsb, hipStream_t st) {
@@ -470,7 +554,8 @@ struct Entry {
   static dao_status solve_sens(int64_t n, const void* th, const void* y0, double t0, double t1,
                                const dao_tol* tol, void* y1, const dao_record* rec, void* ws,
                                hipStream_t st, void* S_theta) {
-    return launch_solve<R, S<R>, M, true>(n, th, y0, t0, t1, tol, y1, rec, ws, st, S_theta);
+    return launch_solve<R, S<R>, M, true>(n, th, y0, t0, t1, tol, y1, rec, ws, solve_base_bytes(),
+                                          st, S_theta);
   }
   static dao_status sens(int64_t n, const void* th, const void* y0, const dao_record* rec,
                          int64_t s_max, void* S_theta, void* S_y0, void* ws, hipStream_t st) {
@@ -488,7 +573,8 @@ struct Entry {
 };
 
 typedef dao_status (*solve_fn)(int64_t, const void*, const void*, double, double, const dao_tol*,
-                               void*, const dao_record*, void*, hipStream_t);
+                               void*, const dao_record*, void*, size_t, hipStream_t);
+typedef size_t (*solve_ws_fn)(int64_t);
 typedef dao_status (*grad_fn)(int, int64_t, const void*, const void*, const dao_record*, int64_t,
                               const void*, void*, void*, void*, size_t, hipStream_t);
 typedef dao_status (*solve_sens_fn)(int64_t, const void*, const void*, double, double,
@@ -511,15 +597,17 @@ struct Impl {
   solve_sens_fn solve_sens;  // forward sensitivities (per-trajectory theta), else null
   sens_fn sens;
   states_fn states;  // states at requested times (per-lane systems), else null
+  solve_ws_fn solve_ws;  // workspace of dao_solve for n trajectories
 };
 
 int64_t mlp_resident_waves() { return resident_blocks(mlp::grad_kernel) * (BLOCK / WAVE); }
+size_t mlp_solve_ws(int64_t) { return solve_base_bytes(); }
 
 template <class R, template <class> class S, int M>
 Impl make_impl() {
   return Impl{&Entry<R, S, M>::solve, &Entry<R, S, M>::grad, &Entry<R, S, M>::slot_bytes,
               &Entry<R, S, M>::resident_waves, WAVE, &Entry<R, S, M>::solve_sens,
-              &Entry<R, S, M>::sens, &Entry<R, S, M>::states};
+              &Entry<R, S, M>::sens, &Entry<R, S, M>::states, &Entry<R, S, M>::solve_ws};
 }
 
 const Impl* find_impl(int sys, int method, int dtype) {
@@ -549,7 +637,7 @@ const Impl* find_impl(int sys, int method, int dtype) {
     table[DAO_SYS_LOGHALO][M_TSIT5][DAO_F32] = make_impl<float, LogHalo, M_TSIT5>();
     table[DAO_SYS_MLP][M_TSIT5][DAO_F32] =
         Impl{&launch_mlp_solve, &launch_mlp_grad, &mlp_slot_bytes, &mlp_resident_waves, mlp::SLOTS,
-             nullptr, nullptr, nullptr};
+             nullptr, nullptr, nullptr, &mlp_solve_ws};
     init = true;
   }
   if (!sys_ok(sys) || method < 0 || method > 1 || dtype < 0 || dtype > 1) return nullptr;
@@ -577,8 +665,11 @@ dao_status dao_system_dims(dao_system sys, int* d, int* p, int* shared) {
 }
 
 size_t dao_solve_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n) {
-  (void)sys; (void)method; (void)dtype; (void)n;
-  return ALIGN + align_up((size_t)WAVE * 2 * sizeof(double));  // queue counter + trash slots
+  // queue counter and trash slots; for large ensembles also the two-phase
+  // solve's saved states, ordering keys and order
+  const Impl* im = find_impl(sys, method, dtype);
+  if (!im || n < 0) return solve_base_bytes();
+  return im->solve_ws(n);
 }
 
 }  // extern "C"
@@ -621,12 +712,13 @@ dao_status solve_call(const char* fn, dao_system sys, dao_method method, dao_dty
   if (rec->s_cap > 0 && !rec->h) return fail(DAO_EINVAL, "%s: rec->h is NULL", fn);
   if (rec->y && sys == DAO_SYS_MLP)
     return fail(DAO_EUNSUPPORTED, "%s: recorded states (rec->y) are not provided for the neural field", fn);
-  if (!workspace || workspace_bytes < dao_solve_workspace_size(sys, method, dtype, n))
+  if (!workspace || workspace_bytes < solve_base_bytes())
     return fail(DAO_EWORKSPACE, "%s: workspace needs %zu bytes", fn,
                 dao_solve_workspace_size(sys, method, dtype, n));
   if (sens)
     return im->solve_sens(n, theta, y0, t0, t1, tol, y1, rec, workspace, (hipStream_t)stream, S_theta);
-  return im->solve(n, theta, y0, t0, t1, tol, y1, rec, workspace, (hipStream_t)stream);
+  return im->solve(n, theta, y0, t0, t1, tol, y1, rec, workspace, workspace_bytes,
+                   (hipStream_t)stream);
 }
 
 }  // namespace

@@ -44,7 +44,22 @@ struct SolveArgs {
   unsigned long long* queue;  // trajectories handed out so far (zero at launch)
   R* trash;  // [64][2] scratch target of record stores that have no row
   R* S_theta;  // forward sensitivities dy1/dtheta [D][P][n] (solve_kernel<..., true>)
+  // Two-phase solve (solve_kernel<..., PHASED>): phase 1 runs the first
+  // `probe` attempts of every trajectory and suspends the unfinished ones
+  // (state into `save`, an ordering key into `key`); phase 2 resumes them in
+  // the queue order `order`.
+  int phase;              // 1 or 2
+  int32_t probe;          // attempts per trajectory in phase 1
+  R* save;                // [2D + 2][n]: y, f(y), t, h of a suspended trajectory
+  int32_t* save_i;        // [2][n]: accepted count; rejected count * 2 + last-rejected flag
+  int32_t* key;           // [n] phase 1: predicted remaining attempts, log scale
+  const int32_t* order;   // [n] phase 2: queue position -> trajectory
 };
+
+// Ordering key of a suspended trajectory: its remaining attempts predicted
+// from the time the probe attempts covered, 200 log2(1 + r) capped at
+// ORDER_KEY_MAX (the sort's bins).
+constexpr int ORDER_KEY_MAX = 4095;
 
 template <class R>
 struct GradArgs {
@@ -114,8 +129,9 @@ __device__ R initial_step(const Sys& sys, const R (&y0)[Sys::D], const R (&f0)[S
 // state, with the steps chosen on the state alone (arXiv 2609.28458 Sec. 2.3
 // and Sec. 3).  S starts at zero, takes the tangent of every accepted step
 // and is written to S_theta when the trajectory finishes.
-template <class R, class Sys, int METHOD, bool SENS = false>
+template <class R, class Sys, int METHOD, bool SENS = false, bool PHASED = false>
 __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
+  static_assert(!(SENS && PHASED), "the two-phase solve carries no sensitivities");
   constexpr int D = Sys::D;
   constexpr int NS = SENS ? Sys::P : 1;
   R Sv[D][NS];
@@ -175,6 +191,9 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     a.count[traj] = nacc;
     if (a.nrej) a.nrej[traj] = nrej;
     a.status[traj] = st;
+    if constexpr (PHASED) {
+      if (a.phase == 1) a.key[traj] = 0;  // done: nothing left to order
+    }
     if constexpr (SENS) {
 #pragma unroll
       for (int c = 0; c < D; ++c)
@@ -185,6 +204,37 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     if (staged) {
       const int32_t lo = nacc & ~(STAGE - 1);
       for (int32_t r = lo; r < nacc; ++r) {
+        hrow[r] = hring[r & (STAGE - 1)][lane];
+        if (with_t) trow[r] = tring[r & (STAGE - 1)][lane];
+        if (with_y) {
+#pragma unroll
+          for (int c = 0; c < D; ++c) yrow[r * D + c] = yring(c, r & (STAGE - 1));
+        }
+      }
+    }
+    traj = -1;
+  };
+
+  // Phase 1 of a two-phase solve: park an unfinished trajectory.  Its state
+  // for the next attempt goes to a.save, its unwritten record rows to memory
+  // (phase 2 reloads them into the ring), and status stays RUNNING.
+  auto suspend = [&]() {
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      a.save[c * a.n + traj] = y[c];
+      a.save[(D + c) * a.n + traj] = k[0][c];
+    }
+    a.save[(2 * D) * a.n + traj] = t;
+    a.save[(2 * D + 1) * a.n + traj] = h;
+    a.save_i[traj] = nacc;
+    a.save_i[a.n + traj] = nrej * 2 + (prev_rej ? 1 : 0);
+    a.status[traj] = RUNNING;
+    const double done = (double)(t - a.t0), left = (double)(a.t1 - t);
+    const double rem = (done > 0.0) ? (double)attempts * left / done : 1e30;
+    const double kf = 200.0 * log2(1.0 + (rem < 1e30 ? rem : 1e30));
+    a.key[traj] = (kf < (double)ORDER_KEY_MAX) ? (int32_t)kf : ORDER_KEY_MAX;
+    if (staged) {
+      for (int32_t r = nacc & ~(STAGE - 1); r < nacc; ++r) {
         hrow[r] = hring[r & (STAGE - 1)][lane];
         if (with_t) trow[r] = tring[r & (STAGE - 1)][lane];
         if (with_y) {
@@ -232,8 +282,47 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
         cursor = (cursor + cnt_w < bend) ? cursor + cnt_w : bend;
       }
       if (need && kk >= a.n) live = false;  // nothing left for this lane
-      if (need && kk < a.n) {
-        traj = kk;
+      // Phase 2 takes trajectories in the given order and resumes only the
+      // suspended ones (a lane that drew a finished one claims again).
+      int64_t tk = kk;
+      bool go = need && kk < a.n;
+      if (PHASED && a.phase == 2 && go) {
+        tk = a.order[kk];
+        go = a.status[tk] == RUNNING;
+      }
+      if (PHASED && a.phase == 2 && go) {
+        traj = tk;
+        sys.load(a.theta, a.n, traj);
+#pragma unroll
+        for (int c = 0; c < D; ++c) {
+          y[c] = a.save[c * a.n + traj];
+          k[0][c] = a.save[(D + c) * a.n + traj];
+        }
+        t = a.save[(2 * D) * a.n + traj];
+        h = a.save[(2 * D + 1) * a.n + traj];
+        nacc = a.save_i[traj];
+        const int32_t rj = a.save_i[a.n + traj];
+        __builtin_amdgcn_s_waitcnt(0);
+        nrej = rj >> 1;
+        prev_rej = (rj & 1) != 0;
+        attempts = a.probe;
+        hrow = a.h_rec + traj * a.s_cap;
+        trow = a.t_rec ? a.t_rec + traj * a.s_cap : nullptr;
+        yrow = a.y_rec ? a.y_rec + traj * a.s_cap * D : nullptr;
+        if (staged) {
+          // the rows of the current chunk that phase 1 wrote, back into the ring
+          for (int32_t r = nacc & ~(STAGE - 1); r < nacc; ++r) {
+            hring[r & (STAGE - 1)][lane] = hrow[r];
+            if (with_t) tring[r & (STAGE - 1)][lane] = trow[r];
+            if (with_y) {
+#pragma unroll
+              for (int c = 0; c < D; ++c) yring(c, r & (STAGE - 1)) = yrow[r * D + c];
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(0);
+        }
+      } else if (go) {
+        traj = tk;
         sys.load(a.theta, a.n, traj);
 #pragma unroll
         for (int c = 0; c < D; ++c) y[c] = a.y0[c * a.n + traj];
@@ -369,6 +458,7 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
       else if (attempts >= a.max_steps) st = TRAJ_MAX_STEPS;
     }
     if (st != RUNNING) finish(st);
+    else if (PHASED && a.phase == 1 && attempts >= a.probe) suspend();
   }
 }
 

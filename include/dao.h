@@ -107,7 +107,11 @@ typedef struct {
  * Returns DAO_EINVAL for an unknown system.                                 */
 dao_status dao_system_dims(dao_system sys, int* d, int* p, int* shared);
 
-/* Workspace (device bytes) dao_solve needs for n trajectories. */
+/* Workspace (device bytes) dao_solve needs for n trajectories.  For an
+ * ensemble of at least four times the lanes the solve keeps resident (per
+ * GPU; dao_solve_sens and the neural field excepted) this includes the
+ * two-phase solve's saved states, ordering keys and order, about
+ * (2d + 5) x 8 bytes per trajectory in binary64.                             */
 size_t dao_solve_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n);
 
 /*
@@ -121,7 +125,17 @@ size_t dao_solve_workspace_size(dao_system sys, dao_method method, dao_dtype dty
  *   t0 <= t1, both finite; tol as above
  *   rec      required; rec->h may be NULL only when rec->s_cap == 0
  *   workspace >= dao_solve_workspace_size() device bytes (work-queue
- *            counter and trash slots); its contents need no initialisation
+ *            counter and trash slots); its contents need no initialisation.
+ *            Large ensembles (see dao_solve_workspace_size) with
+ *            rec->s_cap >= 1024 are solved in two phases when the workspace
+ *            holds the extra: the first 16 attempts of every trajectory,
+ *            then the unfinished ones resumed longest-predicted first (the
+ *            remaining attempts extrapolated from the time the first ones
+ *            covered), so that long trajectories do not run alone at the
+ *            end.  Every trajectory takes the same attempts either way: the
+ *            outputs are identical bit for bit.  A workspace of at least the
+ *            size for one trajectory runs one phase.  The environment
+ *            variable DAO_SOLVE_PHASES=1 or 2 forces one or two phases.
  * Errors: DAO_EINVAL (NULL array with n > 0, t1 < t0, bad tolerances,
  * rec NULL, rec->s_cap < 0), DAO_EUNSUPPORTED, DAO_EWORKSPACE, DAO_EDEVICE.
  */

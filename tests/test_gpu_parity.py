@@ -484,3 +484,51 @@ def test_gradient_with_the_minimum_workspace(dao, name, n, s_cap):
         _lib.check(_lib.dao_grad(*ids, n, th.data_ptr(), y0.data_ptr(), rec.c_struct(), s_max,
                                  lam.data_ptr(), dth.data_ptr(), dy0.data_ptr(), buf.data_ptr(),
                                  nmin - 1, stream))
+
+
+@pytest.mark.parametrize("name,n,s_cap,record_t,states,max_steps",
+                         [("decay", 300, 256, True, False, 100000),
+                          ("lotka_volterra", 64 * 9 + 13, 256, True, False, 100000),
+                          ("lorenz63", 1000, 1024, False, False, 100000),
+                          ("lorenz63", 300, 1024, True, True, 100000),
+                          ("loghalo", 400, 4096, True, False, 100000),
+                          ("robertson", 300, 1024, True, False, 100000),
+                          ("lorenz63", 200, 64, True, False, 100000),
+                          ("lorenz63", 200, 1024, True, False, 40),
+                          ("lorenz63", 200, 1024, True, False, 12)])
+def test_two_phase_solve_equals_one_phase(dao, name, n, s_cap, record_t, states, max_steps,
+                                          monkeypatch):
+    # Large ensembles are solved in two phases (16 probe attempts per
+    # trajectory, then the unfinished ones longest-predicted first);
+    # DAO_SOLVE_PHASES forces either.  Every trajectory takes the same
+    # attempts: record, counts, statuses and final states equal bit for bit,
+    # also when the record fills (s_cap 64), when the attempt cap ends
+    # trajectories in phase 2 (40) or in phase 1 (12), and with recorded
+    # states.
+    w = di.make(name, n)
+    print(f"[two-phase solve] {name} n={n} s_cap={s_cap} max_steps={max_steps}", flush=True)
+    th = torch.tensor(w.theta, device=DEV)
+    y0 = torch.tensor(w.y0, device=DEV)
+    out = {}
+    for mode in ("1", "2"):
+        monkeypatch.setenv("DAO_SOLVE_PHASES", mode)
+        rec, y1 = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=s_cap,
+                            record_t=record_t, record_states=states, max_steps=max_steps)
+        torch.cuda.synchronize()
+        out[mode] = (rec, y1)
+    (r1, y1a), (r2, y1b) = out["1"], out["2"]
+    assert torch.equal(r1.count, r2.count) and torch.equal(r1.status, r2.status)
+    assert torch.equal(r1.nrej, r2.nrej)
+    assert torch.equal(torch.nan_to_num(y1a, nan=7.0), torch.nan_to_num(y1b, nan=7.0))
+    cnt = r1.count.cpu().numpy()
+    mask = torch.tensor(np.arange(s_cap)[None, :] < cnt[:, None], device=DEV)
+    assert torch.equal(r1.h[mask], r2.h[mask])
+    if record_t:
+        assert torch.equal(r1.t[mask], r2.t[mask])
+    if states:
+        assert torch.equal(r1.y[mask], r2.y[mask])
+    st = r1.status.cpu().numpy()
+    if (name, s_cap) == ("lorenz63", 64) or max_steps < 100000:
+        assert np.any(st != 0)  # the failure paths are exercised
+    else:
+        assert np.all(st == 0)
