@@ -175,10 +175,12 @@ void launch_order(const int32_t* count, int64_t n, int64_t s_max, uint32_t* hist
 // the solve's resident lanes, the order in which trajectories are handed out
 // decides how long the last ones run alone: phase 1 takes the first
 // SOLVE_PROBE attempts of every trajectory and predicts each one's remaining
-// attempts from the time those covered; the suspended trajectories are
-// sorted by that prediction and phase 2 resumes them longest first.  Every
+// attempts from the time those covered (64 attempts, about a tenth of a
+// log-halo orbit trajectory on average, rank them well enough); the
+// suspended trajectories are sorted by that prediction and phase 2 resumes
+// them longest first.  Every
 // trajectory takes the same attempts as in one phase, bit for bit.
-constexpr int32_t SOLVE_PROBE = 16;
+constexpr int32_t SOLVE_PROBE = 64;
 
 size_t solve_base_bytes() { return ALIGN + align_up((size_t)WAVE * 2 * sizeof(double)); }
 
@@ -189,11 +191,11 @@ size_t solve_phase_bytes(int64_t n) {  // save, save_i, key, perm, histogram
 }
 
 // Whether a solve of n trajectories takes two phases: n at least four times
-// the resident lanes and a record capacity of at least 64 probes' worth of
-// steps (DAO_SOLVE_PHASES=1 or 2 forces one or two).  The capacity is the
-// caller's bound on a trajectory's length: resuming a trajectory costs its
-// wavefront a few memory round trips, which short trajectories (tens of
-// steps) do not repay, while long ones are where a late start runs alone.
+// the resident lanes and a record capacity of at least 1024 steps
+// (DAO_SOLVE_PHASES=1 or 2 forces one or two).  The capacity is the caller's
+// bound on a trajectory's length: resuming a trajectory costs its wavefront
+// a few memory round trips, which short trajectories (tens of steps) do not
+// repay, while long ones are where a late start runs alone.
 // s_cap < 0 asks whether two phases are possible at all (workspace sizing).
 template <class R, class Sys, int M>
 bool solve_two_phase(int64_t n, int64_t s_cap) {
@@ -202,7 +204,7 @@ bool solve_two_phase(int64_t n, int64_t s_cap) {
     if (e[0] == '1') return false;
     if (e[0] == '2') return true;
   }
-  if (s_cap >= 0 && s_cap < 64 * SOLVE_PROBE) return false;
+  if (s_cap >= 0 && s_cap < 1024) return false;
   auto kern = solve_kernel<R, Sys, M, false, true>;
   const size_t lds = (size_t)BLOCK_WAVES * 2 * 8 * WAVE * sizeof(R);
   return n >= 4 * resident_blocks(kern, lds) * BLOCK;

@@ -128,7 +128,7 @@ size_t dao_solve_workspace_size(dao_system sys, dao_method method, dao_dtype dty
  *            counter and trash slots); its contents need no initialisation.
  *            Large ensembles (see dao_solve_workspace_size) with
  *            rec->s_cap >= 1024 are solved in two phases when the workspace
- *            holds the extra: the first 16 attempts of every trajectory,
+ *            holds the extra: the first 64 attempts of every trajectory,
  *            then the unfinished ones resumed longest-predicted first (the
  *            remaining attempts extrapolated from the time the first ones
  *            covered), so that long trajectories do not run alone at the

@@ -494,16 +494,16 @@ def test_gradient_with_the_minimum_workspace(dao, name, n, s_cap):
                           ("loghalo", 400, 4096, True, False, 100000),
                           ("robertson", 300, 1024, True, False, 100000),
                           ("lorenz63", 200, 64, True, False, 100000),
-                          ("lorenz63", 200, 1024, True, False, 40),
-                          ("lorenz63", 200, 1024, True, False, 12)])
+                          ("lorenz63", 200, 1024, True, False, 150),
+                          ("lorenz63", 200, 1024, True, False, 40)])
 def test_two_phase_solve_equals_one_phase(dao, name, n, s_cap, record_t, states, max_steps,
                                           monkeypatch):
-    # Large ensembles are solved in two phases (16 probe attempts per
+    # Large ensembles are solved in two phases (64 probe attempts per
     # trajectory, then the unfinished ones longest-predicted first);
     # DAO_SOLVE_PHASES forces either.  Every trajectory takes the same
     # attempts: record, counts, statuses and final states equal bit for bit,
     # also when the record fills (s_cap 64), when the attempt cap ends
-    # trajectories in phase 2 (40) or in phase 1 (12), and with recorded
+    # trajectories in phase 2 (150) or in phase 1 (40), and with recorded
     # states.
     w = di.make(name, n)
     print(f"[two-phase solve] {name} n={n} s_cap={s_cap} max_steps={max_steps}", flush=True)
