@@ -27,6 +27,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,9 +64,18 @@ def load_traffic(workload: str, n: int):
 
 
 def _short(name: str) -> str:
+    if "solve_kernel" in name and "mlp" not in name:
+        # solve_kernel<R, Sys, method, SENS, PHASED>: the variant that integrates
+        # the forward sensitivities, the two-phase variant (two launches per
+        # solve), or the plain solve
+        m = re.search(r", (true|false), (true|false)>\(", name)
+        if m and m.group(1) == "true":
+            return "solve_sens_kernel"
+        if m and m.group(2) == "true":
+            return "solve_phased_kernel"
+        return "solve_kernel"
     if "solve_kernel" in name:
-        # the variant that integrates the forward sensitivities (template flag true)
-        return "solve_sens_kernel" if ", true>" in name else "solve_kernel"
+        return "solve_kernel"
     if "grad_kernel" in name:
         return "grad_kernel"
     if "sens_kernel" in name:
@@ -123,7 +133,9 @@ def summarize(args) -> None:
 
     traffic = {"workload": args.workload, "n": args.n, "kernel_source_sha256": kernel_source_digest(),
                "fetch_factor": f_fac, "write_factor": w_fac, "kernels": {}}
-    for key in ("solve_kernel", "solve_sens_kernel", "grad_kernel", "sens_kernel"):
+    # (solve_phased_kernel: averaged over its two launches per solve)
+    for key in ("solve_kernel", "solve_phased_kernel", "solve_sens_kernel", "grad_kernel",
+                "sens_kernel"):
         fb = per_launch(fetch, "FETCH_SIZE", f_fac, key)
         wb = per_launch(write, "WRITE_SIZE", w_fac, key)
         if fb is not None and wb is not None:
