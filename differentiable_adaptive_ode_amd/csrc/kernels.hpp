@@ -365,7 +365,7 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     if constexpr (METHOD == M_TSIT5) {
       tsit5::trial<R, Sys>(C5, sys, y, hs, k, ynew, err);
     } else {
-      ros23::trial<R, Sys>(sys, y, hs, k[0], ynew, F2, err);
+      ros23::trial<R, Sys, !SENS>(sys, y, hs, k[0], ynew, F2, err);
     }
     R sc[D];
 #pragma unroll
@@ -415,8 +415,8 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
           tsit5::tangent<R, Sys, NS>(C5, sys, y, hs, k, sdir, Sv);
         } else {
           ros23::Stages<R, D> St;  // the step's factors and stages, recomputed
-          ros23::stages<R, Sys>(sys, y, hs, St);
-          ros23::tangent<R, Sys, NS>(sys, St, hs, sdir, Sv);
+          ros23::stages<R, Sys, false>(sys, y, hs, St);
+          ros23::tangent<R, Sys, NS, false>(sys, St, hs, sdir, Sv);
         }
       }
     }
@@ -717,8 +717,8 @@ __global__ void __launch_bounds__(256) sens_kernel(SensArgs<R> a) {
         for (int c = 0; c < D; ++c) y[c] = Y[c];
       } else {
         ros23::Stages<R, D> St;
-        ros23::stages<R, Sys>(sys, y, hj, St);
-        ros23::tangent<R, Sys, NT>(sys, St, hj, pdir, S);
+        ros23::stages<R, Sys, false>(sys, y, hj, St);
+        ros23::tangent<R, Sys, NT, false>(sys, St, hj, pdir, S);
 #pragma unroll
         for (int c = 0; c < D; ++c) y[c] = fmaR(hj, St.u[c] + St.k1[c], y[c]);  // as ros23::replay
       }

@@ -43,7 +43,13 @@ struct LU {
   bool swaps;  // some lane of the wavefront exchanges rows (wavefront-uniform)
 };
 
-template <class R, int D>
+// SKIP (here and below): test, once per elimination step and per solve,
+// whether any lane of the wavefront exchanges rows, and skip the exchange on
+// a real branch when none does.  Without it the exchanges are selects in
+// straight-line code, which suits kernels that run many independent solves
+// per step (the sensitivity tangents), where branches would keep the
+// compiler from interleaving them.
+template <class R, int D, bool SKIP = true>
 __device__ __forceinline__ void factor(LU<R, D>& f) {
 #pragma unroll
   for (int k = 0; k < D; ++k) {
@@ -55,11 +61,11 @@ __device__ __forceinline__ void factor(LU<R, D>& f) {
       if (v > best) { best = v; p = i; }
     }
     f.piv[k] = p;
-    const bool any = (k + 1 < D) && __ballot(p != k) != 0ull;
+    const bool any = !SKIP || ((k + 1 < D) && __ballot(p != k) != 0ull);
     if (k == 0) f.swaps = any;
     else f.swaps = f.swaps || any;
     if (any) {
-      skip_point();
+      if (SKIP) skip_point();
 #pragma unroll
       for (int i = k + 1; i < D; ++i) {
         const bool sw = (p == i);
@@ -83,13 +89,13 @@ __device__ __forceinline__ void factor(LU<R, D>& f) {
 }
 
 // x = W^-1 b
-template <class R, int D>
+template <class R, int D, bool SKIP = true>
 __device__ __forceinline__ void solve(const LU<R, D>& f, const R (&b)[D], R (&x)[D]) {
   R z[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) z[i] = b[i];
-  if (f.swaps) {
-    skip_point();
+  if (!SKIP || f.swaps) {
+    if (SKIP) skip_point();
 #pragma unroll
     for (int k = 0; k < D; ++k) {
 #pragma unroll
@@ -117,7 +123,7 @@ __device__ __forceinline__ void solve(const LU<R, D>& f, const R (&b)[D], R (&x)
 }
 
 // x = W^-T b, with W = P^T L U:  U^T z = b,  L^T w = z,  x = P^T w.
-template <class R, int D>
+template <class R, int D, bool SKIP = true>
 __device__ __forceinline__ void solve_t(const LU<R, D>& f, const R (&b)[D], R (&x)[D]) {
   R z[D];
 #pragma unroll
@@ -136,8 +142,8 @@ __device__ __forceinline__ void solve_t(const LU<R, D>& f, const R (&b)[D], R (&
       if (j > i) acc = fmaR(-f.m[j][i], x[j], acc);
     x[i] = acc;
   }
-  if (f.swaps) {
-    skip_point();
+  if (!SKIP || f.swaps) {
+    if (SKIP) skip_point();
 #pragma unroll
     for (int k = D - 1; k >= 0; --k) {
 #pragma unroll
@@ -151,7 +157,7 @@ __device__ __forceinline__ void solve_t(const LU<R, D>& f, const R (&b)[D], R (&
   }
 }
 
-template <class R, class Sys>
+template <class R, class Sys, bool SKIP = true>
 __device__ __forceinline__ void build_w(const Sys& sys, const R (&y)[Sys::D], R h,
                                         LU<R, Sys::D>& w) {
   constexpr int D = Sys::D;
@@ -162,26 +168,26 @@ __device__ __forceinline__ void build_w(const Sys& sys, const R (&y)[Sys::D], R 
   for (int i = 0; i < D; ++i)
 #pragma unroll
     for (int j = 0; j < D; ++j) w.m[i][j] = fmaR(-hd, J[i][j], R(i == j ? 1 : 0));
-  factor<R, D>(w);
+  factor<R, D, SKIP>(w);
 }
 
 // Trial step: F0 = f(y) on entry; returns ynew, F2 = f(ynew) and err.
-template <class R, class Sys>
+template <class R, class Sys, bool SKIP = true>
 __device__ __forceinline__ void trial(const Sys& sys, const R (&y)[Sys::D], R h,
                                       const R (&F0)[Sys::D], R (&ynew)[Sys::D], R (&F2)[Sys::D],
                                       R (&err)[Sys::D]) {
   constexpr int D = Sys::D;
   LU<R, D> w;
-  build_w(sys, y, h, w);
+  build_w<R, Sys, SKIP>(sys, y, h, w);
   R k1[D], k2[D], Y1[D], F1[D], r[D], u[D], k3[D];
-  solve<R, D>(w, F0, k1);
+  solve<R, D, SKIP>(w, F0, k1);
   R hh = R(0.5) * h;
 #pragma unroll
   for (int c = 0; c < D; ++c) Y1[c] = fmaR(hh, k1[c], y[c]);
   sys.f(Y1, F1);
 #pragma unroll
   for (int c = 0; c < D; ++c) r[c] = F1[c] - k1[c];
-  solve<R, D>(w, r, u);
+  solve<R, D, SKIP>(w, r, u);
 #pragma unroll
   for (int c = 0; c < D; ++c) k2[c] = u[c] + k1[c];
 #pragma unroll
@@ -192,7 +198,7 @@ __device__ __forceinline__ void trial(const Sys& sys, const R (&y)[Sys::D], R h,
     R t2 = fmaR(R(-E32), k2[c] - F1[c], F2[c]);
     r[c] = fmaR(R(-2), k1[c] - F0[c], t2);
   }
-  solve<R, D>(w, r, k3);
+  solve<R, D, SKIP>(w, r, k3);
   R h6 = h / R(6);
 #pragma unroll
   for (int c = 0; c < D; ++c) err[c] = h6 * (fmaR(R(-2), k2[c], k1[c]) + k3[c]);
@@ -230,23 +236,23 @@ struct Stages {
   R u[D];       // W^-1 (F1 - k1)
 };
 
-template <class R, class Sys>
+template <class R, class Sys, bool SKIP = true>
 __device__ __forceinline__ void stages(const Sys& sys, const R (&y)[Sys::D], R h,
                                        Stages<R, Sys::D>& S) {
   constexpr int D = Sys::D;
-  build_w(sys, y, h, S.w);
+  build_w<R, Sys, SKIP>(sys, y, h, S.w);
   R F0[D], F1[D], r[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) S.y[c] = y[c];
   sys.f(y, F0);
-  solve<R, D>(S.w, F0, S.k1);
+  solve<R, D, SKIP>(S.w, F0, S.k1);
   R hh = R(0.5) * h;
 #pragma unroll
   for (int c = 0; c < D; ++c) S.Y1[c] = fmaR(hh, S.k1[c], y[c]);
   sys.f(S.Y1, F1);
 #pragma unroll
   for (int c = 0; c < D; ++c) r[c] = F1[c] - S.k1[c];
-  solve<R, D>(S.w, r, S.u);
+  solve<R, D, SKIP>(S.w, r, S.u);
 }
 
 template <class R, class Sys>
@@ -297,7 +303,7 @@ __device__ __forceinline__ void sweep(const Sys& sys, const Stages<R, Sys::D>& S
 //   Wd = -h d Jd,  k1d = W^-1 (F0d - Wd k1),  Y1d = yd + h/2 k1d,
 //   ud = W^-1 (F1d - k1d - Wd u),  y_new d = yd + h (ud + k1d),
 // with F0d, F1d the field's tangents at y and Y1 and Jd the Jacobian's.
-template <class R, class Sys, int NT>
+template <class R, class Sys, int NT, bool SKIP = true>
 __device__ __forceinline__ void tangent(const Sys& sys, const Stages<R, Sys::D>& St, R h,
                                         const int (&dir)[NT], R (&S)[Sys::D][NT]) {
   constexpr int D = Sys::D;
@@ -318,7 +324,7 @@ __device__ __forceinline__ void tangent(const Sys& sys, const Stages<R, Sys::D>&
       for (int j = 0; j < D; ++j) acc = fmaR(Jd[i][j], St.k1[j], acc);
       r[i] = fmaR(hd, acc, F0d[i]);
     }
-    solve<R, D>(St.w, r, k1d);
+    solve<R, D, SKIP>(St.w, r, k1d);
 #pragma unroll
     for (int c = 0; c < D; ++c) Y1d[c] = fmaR(hh, k1d[c], yd[c]);
     sys.jvp(St.Y1, Y1d, dir[t], F1d);
@@ -330,7 +336,7 @@ __device__ __forceinline__ void tangent(const Sys& sys, const Stages<R, Sys::D>&
       for (int j = 0; j < D; ++j) acc = fmaR(Jd[i][j], St.u[j], acc);
       r[i] = fmaR(hd, acc, F1d[i] - k1d[i]);
     }
-    solve<R, D>(St.w, r, ud);
+    solve<R, D, SKIP>(St.w, r, ud);
 #pragma unroll
     for (int c = 0; c < D; ++c) S[c][t] = fmaR(h, ud[c] + k1d[c], yd[c]);
   }
