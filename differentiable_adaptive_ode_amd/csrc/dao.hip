@@ -184,9 +184,13 @@ constexpr int32_t SOLVE_PROBE = 64;
 
 size_t solve_base_bytes() { return ALIGN + align_up((size_t)WAVE * 2 * sizeof(double)); }
 
-template <class R, int D>
-size_t solve_phase_bytes(int64_t n) {  // save, save_i, key, perm, histogram
-  return align_up((size_t)(2 * D + 2) * n * sizeof(R)) + align_up((size_t)2 * n * 4) +
+// save (the state of a suspended trajectory, with room for its
+// sensitivities), save_i, key, perm, histogram
+template <class R, int D, int P>
+size_t solve_save_reals() { return (size_t)(2 * D + 2 + D * P); }
+template <class R, int D, int P>
+size_t solve_phase_bytes(int64_t n) {
+  return align_up(solve_save_reals<R, D, P>() * n * sizeof(R)) + align_up((size_t)2 * n * 4) +
          2 * align_up((size_t)n * 4) + align_up((size_t)ORDER_BINS * 4);
 }
 
@@ -213,7 +217,7 @@ bool solve_two_phase(int64_t n, int64_t s_cap) {
 template <class R, class Sys, int M>
 size_t solve_ws_bytes(int64_t n) {
   return solve_base_bytes() +
-         (solve_two_phase<R, Sys, M>(n, -1) ? solve_phase_bytes<R, Sys::D>(n) : 0);
+         (solve_two_phase<R, Sys, M>(n, -1) ? solve_phase_bytes<R, Sys::D, Sys::P>(n) : 0);
 }
 
 template <class R, class Sys, int M, bool SENS = false>
@@ -250,13 +254,12 @@ dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0,
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)ws, (int64_t)2, 0u);
   // record staging ring: (t, h [, y]) x 8 slots x 64 lanes per wavefront
   const size_t lds = (size_t)BLOCK_WAVES * (rec->y ? 2 + Sys::D : 2) * 8 * WAVE * sizeof(R);
-  if constexpr (!SENS) {
+  {
     if (solve_two_phase<R, Sys, M>(n, rec->s_cap) &&
-        ws_bytes >= solve_base_bytes() + solve_phase_bytes<R, Sys::D>(n)) {
-      constexpr int D = Sys::D;
+        ws_bytes >= solve_base_bytes() + solve_phase_bytes<R, Sys::D, Sys::P>(n)) {
       char* p = (char*)ws + solve_base_bytes();
       a.save = (R*)p;
-      p += align_up((size_t)(2 * D + 2) * n * sizeof(R));
+      p += align_up(solve_save_reals<R, Sys::D, Sys::P>() * n * sizeof(R));
       a.save_i = (int32_t*)p;
       p += align_up((size_t)2 * n * 4);
       a.key = (int32_t*)p;
@@ -264,7 +267,7 @@ dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0,
       int32_t* perm = (int32_t*)p;
       p += align_up((size_t)n * 4);
       uint32_t* hist = (uint32_t*)p;
-      auto kern = solve_kernel<R, Sys, M, false, true>;
+      auto kern = solve_kernel<R, Sys, M, SENS, true>;
       int64_t blocks = (n + BLOCK - 1) / BLOCK;
       const int64_t res = resident_blocks(kern, lds);
       if (blocks > res) blocks = res;
@@ -555,9 +558,8 @@ struct Entry {
   }
   static dao_status solve_sens(int64_t n, const void* th, const void* y0, double t0, double t1,
                                const dao_tol* tol, void* y1, const dao_record* rec, void* ws,
-                               hipStream_t st, void* S_theta) {
-    return launch_solve<R, S<R>, M, true>(n, th, y0, t0, t1, tol, y1, rec, ws, solve_base_bytes(),
-                                          st, S_theta);
+                               size_t wsb, hipStream_t st, void* S_theta) {
+    return launch_solve<R, S<R>, M, true>(n, th, y0, t0, t1, tol, y1, rec, ws, wsb, st, S_theta);
   }
   static dao_status sens(int64_t n, const void* th, const void* y0, const dao_record* rec,
                          int64_t s_max, void* S_theta, void* S_y0, void* ws, hipStream_t st) {
@@ -580,8 +582,8 @@ typedef size_t (*solve_ws_fn)(int64_t);
 typedef dao_status (*grad_fn)(int, int64_t, const void*, const void*, const dao_record*, int64_t,
                               const void*, void*, void*, void*, size_t, hipStream_t);
 typedef dao_status (*solve_sens_fn)(int64_t, const void*, const void*, double, double,
-                                    const dao_tol*, void*, const dao_record*, void*, hipStream_t,
-                                    void*);
+                                    const dao_tol*, void*, const dao_record*, void*, size_t,
+                                    hipStream_t, void*);
 typedef dao_status (*sens_fn)(int64_t, const void*, const void*, const dao_record*, int64_t, void*,
                               void*, void*, hipStream_t);
 typedef dao_status (*states_fn)(int64_t, const void*, const void*, double, double,
@@ -718,7 +720,8 @@ dao_status solve_call(const char* fn, dao_system sys, dao_method method, dao_dty
     return fail(DAO_EWORKSPACE, "%s: workspace needs %zu bytes", fn,
                 dao_solve_workspace_size(sys, method, dtype, n));
   if (sens)
-    return im->solve_sens(n, theta, y0, t0, t1, tol, y1, rec, workspace, (hipStream_t)stream, S_theta);
+    return im->solve_sens(n, theta, y0, t0, t1, tol, y1, rec, workspace, workspace_bytes,
+                          (hipStream_t)stream, S_theta);
   return im->solve(n, theta, y0, t0, t1, tol, y1, rec, workspace, workspace_bytes,
                    (hipStream_t)stream);
 }

@@ -50,7 +50,7 @@ struct SolveArgs {
   // the queue order `order`.
   int phase;              // 1 or 2
   int32_t probe;          // attempts per trajectory in phase 1
-  R* save;                // [2D + 2][n]: y, f(y), t, h of a suspended trajectory
+  R* save;                // [2D + 2 (+ D P)][n]: y, f(y), t, h (and S) of a suspended trajectory
   int32_t* save_i;        // [2][n]: accepted count; rejected count * 2 + last-rejected flag
   int32_t* key;           // [n] phase 1: predicted remaining attempts, log scale
   const int32_t* order;   // [n] phase 2: queue position -> trajectory
@@ -131,7 +131,6 @@ __device__ R initial_step(const Sys& sys, const R (&y0)[Sys::D], const R (&f0)[S
 // and is written to S_theta when the trajectory finishes.
 template <class R, class Sys, int METHOD, bool SENS = false, bool PHASED = false>
 __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
-  static_assert(!(SENS && PHASED), "the two-phase solve carries no sensitivities");
   constexpr int D = Sys::D;
   constexpr int NS = SENS ? Sys::P : 1;
   R Sv[D][NS];
@@ -226,6 +225,12 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     }
     a.save[(2 * D) * a.n + traj] = t;
     a.save[(2 * D + 1) * a.n + traj] = h;
+    if constexpr (SENS) {
+#pragma unroll
+      for (int c = 0; c < D; ++c)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) a.save[(2 * D + 2 + c * NS + j) * a.n + traj] = Sv[c][j];
+    }
     a.save_i[traj] = nacc;
     a.save_i[a.n + traj] = nrej * 2 + (prev_rej ? 1 : 0);
     a.status[traj] = RUNNING;
@@ -300,6 +305,12 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
         }
         t = a.save[(2 * D) * a.n + traj];
         h = a.save[(2 * D + 1) * a.n + traj];
+        if constexpr (SENS) {
+#pragma unroll
+          for (int c = 0; c < D; ++c)
+#pragma unroll
+            for (int j = 0; j < NS; ++j) Sv[c][j] = a.save[(2 * D + 2 + c * NS + j) * a.n + traj];
+        }
         nacc = a.save_i[traj];
         const int32_t rj = a.save_i[a.n + traj];
         __builtin_amdgcn_s_waitcnt(0);

@@ -107,11 +107,11 @@ typedef struct {
  * Returns DAO_EINVAL for an unknown system.                                 */
 dao_status dao_system_dims(dao_system sys, int* d, int* p, int* shared);
 
-/* Workspace (device bytes) dao_solve needs for n trajectories.  For an
- * ensemble of at least four times the lanes the solve keeps resident (per
- * GPU; dao_solve_sens and the neural field excepted) this includes the
- * two-phase solve's saved states, ordering keys and order, about
- * (2d + 5) x 8 bytes per trajectory in binary64.                             */
+/* Workspace (device bytes) dao_solve and dao_solve_sens need for n
+ * trajectories.  For an ensemble of at least four times the lanes the solve
+ * keeps resident (the neural field excepted) this includes the two-phase
+ * solve's saved states (with room for the sensitivities), ordering keys and
+ * order, about (2d + 2 + dp) x 8 + 16 bytes per trajectory in binary64.     */
 size_t dao_solve_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n);
 
 /*

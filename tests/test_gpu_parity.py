@@ -532,3 +532,27 @@ def test_two_phase_solve_equals_one_phase(dao, name, n, s_cap, record_t, states,
         assert np.any(st != 0)  # the failure paths are exercised
     else:
         assert np.all(st == 0)
+
+
+@pytest.mark.parametrize("name,n,s_cap", [("lorenz63", 500, 1024), ("robertson", 300, 1024),
+                                          ("loghalo", 300, 4096), ("lotka_volterra", 64 * 5 + 9, 256)])
+def test_two_phase_solve_with_sensitivities_equals_one_phase(dao, name, n, s_cap, monkeypatch):
+    # The solve with forward sensitivities suspends and resumes S with the
+    # state: both ways give the same S, record and final states bit for bit.
+    w = di.make(name, n)
+    print(f"[two-phase sens] {name} n={n}", flush=True)
+    th = torch.tensor(w.theta, device=DEV)
+    y0 = torch.tensor(w.y0, device=DEV)
+    out = {}
+    for mode in ("1", "2"):
+        monkeypatch.setenv("DAO_SOLVE_PHASES", mode)
+        out[mode] = dao.solve_sens(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol,
+                                   s_cap=s_cap)
+        torch.cuda.synchronize()
+    (r1, y1a, Sa), (r2, y1b, Sb) = out["1"], out["2"]
+    assert torch.equal(r1.count, r2.count) and torch.equal(r1.status, r2.status)
+    assert torch.equal(y1a, y1b) and torch.equal(Sa, Sb)
+    assert np.all(r1.status.cpu().numpy() == 0)
+    cnt = r1.count.cpu().numpy()
+    mask = torch.tensor(np.arange(s_cap)[None, :] < cnt[:, None], device=DEV)
+    assert torch.equal(r1.h[mask], r2.h[mask]) and torch.equal(r1.t[mask], r2.t[mask])
