@@ -245,14 +245,15 @@ def main():
     # the two reduction kernels); the sort before it is timed apart.
     dom = "grad" if tk >= ts else "solve"
     ach = (fl_grad / tk) if dom == "grad" else (fl_solve / ts)
-    # Measured HBM bytes per launch of the dominant kernel (rocprofv3 FETCH_SIZE +
+    # Measured HBM bytes per call of the dominant kernel (rocprofv3 FETCH_SIZE +
     # WRITE_SIZE, copy-calibrated), only if taken on the current kernel sources.
     from differentiable_adaptive_ode_amd.profiling import load_traffic
 
     tr = load_traffic(w.name, w.n)
     traffic = None
-    if tr is not None and f"{dom}_kernel" in tr["kernels"]:
-        traffic = tr["kernels"][f"{dom}_kernel"]["hbm_bytes"]
+    for key in (f"{dom}_kernel", f"{dom}_phased_kernel"):  # one call, one or two launches
+        if tr is not None and traffic is None and key in tr["kernels"]:
+            traffic = tr["kernels"][key]["hbm_bytes"]
     dtype_name = {"f64": "f64", "f32": "f32"}[w.dtype]
     out = {
         "metric": "gradient trajectories/s (replay adjoint) + solves/s at 1 GPU; % of roofline",
@@ -284,7 +285,8 @@ def main():
         "roofline": {"bound": cfg["bound"], "kernel": f"{dom}_kernel",
                      "launch_ms": (tk if dom == "grad" else ts) * 1e3, "achieved": ach * 1e-12,
                      "peak": peak * 1e-12, "unit": "TFLOP/s", "frac": ach / peak,
-                     "traffic": traffic, "traffic_unit": "HBM bytes per launch"},
+                     "traffic": traffic,
+                     "traffic_unit": "HBM bytes per call (two launches for a two-phase solve)"},
         "roofline_solve_frac": fl_solve / ts / peak,
         "roofline_grad_frac": fl_grad / tk / peak,
     }
@@ -376,7 +378,10 @@ def bench_sens(args, w):
 
     tr = load_traffic(f"{w.name}_sens", w.n)
     kern = "solve_sens_kernel"
-    traffic = tr["kernels"][kern]["hbm_bytes"] if tr and kern in tr["kernels"] else None
+    traffic = None
+    for key in ("solve_sens_kernel", "solve_sens_phased_kernel"):  # one or two launches
+        if tr and traffic is None and key in tr["kernels"]:
+            traffic = tr["kernels"][key]["hbm_bytes"]
     out = {
         "metric": "forward-sensitivity trajectories/s (solve + dy1/dtheta in one kernel) at 1 GPU",
         "value": w.n / (wall / args.steps),
@@ -392,7 +397,7 @@ def bench_sens(args, w):
         "roofline": {"bound": cfg["bound"], "kernel": "solve_sens_kernel",
                      "launch_ms": tk * 1e3, "achieved": ach * 1e-12, "peak": cfg["peak"] * 1e-12,
                      "unit": "TFLOP/s", "frac": ach / cfg["peak"], "traffic": traffic,
-                     "traffic_unit": "HBM bytes per launch"},
+                     "traffic_unit": "HBM bytes per call (two launches for a two-phase solve)"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_sens(w, args.cpu_sample or min(cfg["cpu_n"], 4096),

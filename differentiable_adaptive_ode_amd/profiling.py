@@ -10,8 +10,8 @@ rocprofv3 CSV output.
 `rocprofv3 -f csv` wrote, and writes
 
 * profiles/<workload>_n<N>_kernels.md  -- per-kernel average durations, HBM
-  bytes per launch and (with --sq) instruction counts, with the commands;
-* profiles/traffic_<workload>.json     -- HBM bytes per launch of the solve and
+  bytes per call and (with --sq) instruction counts, with the commands;
+* profiles/traffic_<workload>.json     -- HBM bytes per call of the solve and
   gradient kernels, tagged with the digest of the kernel sources they were
   measured on.
 
@@ -51,7 +51,7 @@ def traffic_path(workload: str, root: str | None = None) -> str:
 
 
 def load_traffic(workload: str, n: int):
-    """Measured HBM bytes per launch for the current kernel sources at ensemble
+    """Measured HBM bytes per call for the current kernel sources at ensemble
     size n, or None (no profile, other sources, or another size)."""
     p = traffic_path(workload)
     if not os.path.exists(p):
@@ -69,11 +69,9 @@ def _short(name: str) -> str:
         # the forward sensitivities, the two-phase variant (two launches per
         # solve), or the plain solve
         m = re.search(r", (true|false), (true|false)>\(", name)
-        if m and m.group(1) == "true":
-            return "solve_sens_kernel"
-        if m and m.group(2) == "true":
-            return "solve_phased_kernel"
-        return "solve_kernel"
+        sens = bool(m) and m.group(1) == "true"
+        phased = bool(m) and m.group(2) == "true"
+        return "solve" + ("_sens" if sens else "") + ("_phased" if phased else "") + "_kernel"
     if "solve_kernel" in name:
         return "solve_kernel"
     if "grad_kernel" in name:
@@ -128,14 +126,16 @@ def summarize(args) -> None:
     w_fac = _copy_counter(write, "WRITE_SIZE", copy_bytes)
 
     def per_launch(vals, counter, fac, key):
+        # per call of the library: a two-phase solve is two launches
         xs = [v for (name, c), vv in vals.items() if c == counter and _short(name) == key for v in vv]
-        return (sum(xs) / len(xs)) * 1024.0 * fac if xs else None
+        per = 2.0 if "phased" in key else 1.0
+        return per * (sum(xs) / len(xs)) * 1024.0 * fac if xs else None
 
     traffic = {"workload": args.workload, "n": args.n, "kernel_source_sha256": kernel_source_digest(),
                "fetch_factor": f_fac, "write_factor": w_fac, "kernels": {}}
-    # (solve_phased_kernel: averaged over its two launches per solve)
-    for key in ("solve_kernel", "solve_phased_kernel", "solve_sens_kernel", "grad_kernel",
-                "sens_kernel"):
+    # (the *_phased_ kernels: the two launches of one two-phase solve together)
+    for key in ("solve_kernel", "solve_phased_kernel", "solve_sens_kernel",
+                "solve_sens_phased_kernel", "grad_kernel", "sens_kernel"):
         fb = per_launch(fetch, "FETCH_SIZE", f_fac, key)
         wb = per_launch(write, "WRITE_SIZE", w_fac, key)
         if fb is not None and wb is not None:
@@ -152,13 +152,14 @@ def summarize(args) -> None:
              "| kernel | calls | average us | share of GPU time |", "|---|---|---|---|"]
     for name, calls, avg, pct in stats:
         lines.append(f"| {_short(name)} | {calls} | {avg / 1e3:.2f} | {pct:.1f} % |")
-    lines += ["", "HBM bytes per launch (FETCH_SIZE, WRITE_SIZE in KiB per dispatch, scaled by the "
-              "calibration copy of the same run):", "", "    " + args.cmd_fetch, "    " + args.cmd_write, "",
+    lines += ["", "HBM bytes per call (FETCH_SIZE, WRITE_SIZE in KiB per dispatch, scaled by the "
+              "calibration copy of the same run; a two-phase solve's call is its two launches):",
+              "", "    " + args.cmd_fetch, "    " + args.cmd_write, "",
               f"Calibration: a device-to-device copy of {args.copy_mib} MiB reads "
               f"{copy_bytes / f_fac / 1024:.0f} KiB of FETCH_SIZE and {copy_bytes / w_fac / 1024:.0f} KiB of "
               f"WRITE_SIZE, so read bytes = {f_fac:.3f} x FETCH_SIZE x 1024 and write bytes = "
               f"{w_fac:.3f} x WRITE_SIZE x 1024.", "",
-              "| kernel | read MB / launch | write MB / launch |", "|---|---|---|"]
+              "| kernel | read MB / call | write MB / call |", "|---|---|---|"]
     for key, t in traffic["kernels"].items():
         lines.append(f"| {key} | {t['read_bytes'] / 1e6:.1f} | {t['write_bytes'] / 1e6:.1f} |")
     if sq:
