@@ -94,10 +94,12 @@ def parse():
                          "Lotka-Volterra system at n = 1048576, where its 256-trajectory "
                          "ensemble cannot fill the chip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("gradient", "sens"), default="gradient",
+    ap.add_argument("--mode", choices=("gradient", "sens", "replay_sens", "states"),
+                    default="gradient",
                     help="gradient: solve with record + replay-adjoint gradient (default); "
                          "sens: solve with the forward sensitivities dy1/dtheta in the same "
-                         "kernel")
+                         "kernel; replay_sens: dy1/dtheta by forward mode through the replay "
+                         "of a record; states: the states at 16 requested times on a record")
     ap.add_argument("--states", action="store_true",
                     help="record states in the solve; the gradient skips the forward replay")
     ap.add_argument("--cpu-sample", type=int, default=None,
@@ -164,6 +166,8 @@ def main():
     w = di.make(args.workload, args.n)
     if args.mode == "sens":
         return bench_sens(args, w)
+    if args.mode in ("replay_sens", "states"):
+        return bench_on_record(args, w)
     cfg = WORKLOADS[w.name]
     s_cap = cfg["s_cap"]
     th = torch.tensor(w.theta, device=dev)
@@ -402,6 +406,131 @@ def bench_sens(args, w):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_sens(w, args.cpu_sample or min(cfg["cpu_n"], 4096),
                                                 s_cap)
+    print(json.dumps(out), flush=True)
+
+
+STATES_M = 16  # requested times of the states benchmark, uniform over [t0, t1]
+
+
+def cpu_baseline_on_record(w, sample, s_cap, mode):
+    """The oracle, as is: forward mode through the replay, or the states at the
+    requested times, on a sample's own mesh (the solve is setup, not timed)."""
+    import numpy as np
+
+    import dao_inputs as di
+    import oracle
+
+    nthreads = min(os.cpu_count() or 1, 16)
+    ws = di.subset(w, np.arange(min(sample, w.n)))
+    r = oracle.solve(ws.system, ws.method, ws.theta, ws.y0, ws.t0, ws.t1, ws.rtol, ws.atol,
+                     s_cap=s_cap, dtype=ws.dtype, nthreads=nthreads)
+    t0 = time.perf_counter()
+    if mode == "replay_sens":
+        oracle.sens(ws.system, ws.method, ws.theta, ws.y0, r["count"], r["h"], with_y0=False,
+                    nthreads=nthreads)
+        what = "dual-number forward sensitivities through the replay of its mesh"
+    else:
+        tq = np.linspace(ws.t0, ws.t1, STATES_M)
+        oracle.states_at(ws.system, ws.method, ws.theta, ws.y0, ws.t0, ws.t1, r["count"], r["h"],
+                         tq, nthreads=nthreads)
+        what = f"states at {STATES_M} requested times on its mesh"
+    dt = time.perf_counter() - t0
+    return {"value": ws.n / dt, "unit": "trajectories/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"first {ws.n} of the {w.n} {w.name} trajectories, {what} (the oracle's "
+                      f"solve of the sample is setup), {dt:.2f} s wall on {nthreads} threads"}
+
+
+def bench_on_record(args, w):
+    """One step on a recorded mesh (the solve that writes it is setup, untimed):
+    replay_sens = dao_sens, dy1/dtheta by forward mode through the replay
+    (application paper arXiv 2609.28458 Sec. 2.3; gradsolve Sec. 3.1);
+    states = dao_states_at at STATES_M requested times, a shortened step from
+    the start of the step holding each (application paper Appendix A)."""
+    import numpy as np
+    import torch
+
+    import differentiable_adaptive_ode_amd as dao
+    from differentiable_adaptive_ode_amd import api
+
+    if w.name == "mlp":
+        raise SystemExit("bench: forward sensitivities and states at requested times are "
+                         "provided for the per-trajectory systems, not the neural field")
+    dev = torch.device("cuda:0")
+    cfg = WORKLOADS[w.name]
+    s_cap = cfg["s_cap"]
+    th = torch.tensor(w.theta, device=dev)
+    y0 = torch.tensor(w.y0, device=dev)
+    wsp = api.Workspace()
+    rec, _ = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=s_cap,
+                       record_t=cfg["with_t"], workspace=wsp)
+    torch.cuda.synchronize()
+    cnt = rec.count.cpu().numpy().astype(np.int64)
+    if not np.all(rec.status.cpu().numpy() == 0):
+        raise SystemExit("bench: some trajectories failed")
+    s_max = int(cnt.max())
+    steps_total = int(cnt.sum())
+    tq = torch.linspace(w.t0, w.t1, STATES_M, dtype=y0.dtype, device=dev)
+    yq = torch.empty((STATES_M, w.d, w.n), dtype=y0.dtype, device=dev)
+
+    def run(ev):
+        ev[0].record()
+        if args.mode == "replay_sens":
+            dao.sens(rec, s_max=s_max, workspace=wsp)
+        else:
+            dao.states_at(rec, tq, s_max=s_max, out=yq, workspace=wsp)
+        ev[1].record()
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    copy_calibration(args.copy_calibration, dev)
+    for _ in range(max(args.warmup, 1)):
+        run(events())
+    evs = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        run(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tk = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    p = int(w.theta.shape[0])
+    if args.mode == "replay_sens":
+        # per accepted step: the replay step and the tangent along p directions
+        fl = steps_total * (cfg["replay"] + _sens_step_flops(w.d, p, w.name, w.method))
+        kern, label, tag = "sens_kernel", "forward sensitivities through the replay", "rsens"
+        metric = "replay forward-mode sensitivity trajectories/s (dy1/dtheta on a record) at 1 GPU"
+    else:
+        # every lane takes count + m steps of the method (recorded or shortened),
+        # each a replay step plus its time update
+        fl = (steps_total + w.n * STATES_M) * (cfg["replay"] + 1)
+        kern, label, tag = "states_kernel", f"states at {STATES_M} requested times", "states"
+        metric = f"trajectories/s for the states at {STATES_M} requested times on a record, 1 GPU"
+    ach = fl / tk
+    from differentiable_adaptive_ode_amd.profiling import load_traffic
+
+    tr = load_traffic(f"{w.name}_{tag}", w.n)
+    traffic = tr["kernels"][kern]["hbm_bytes"] if tr and kern in tr["kernels"] else None
+    out = {
+        "metric": metric,
+        "value": w.n / (wall / args.steps),
+        "unit": "trajectories/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name} ensemble, {label}", "n_trajectories": w.n,
+                   "method": w.method, "t_span": [w.t0, w.t1], "rtol": w.rtol, "atol": w.atol,
+                   "s_cap": s_cap, "directions": p if args.mode == "replay_sens" else None,
+                   "requested_times": STATES_M if args.mode == "states" else None},
+        "call_ms": tk * 1e3, "accepted_steps_mean": float(cnt.mean()),
+        "roofline": {"bound": cfg["bound"], "kernel": kern, "launch_ms": tk * 1e3,
+                     "achieved": ach * 1e-12, "peak": cfg["peak"] * 1e-12, "unit": "TFLOP/s",
+                     "frac": ach / cfg["peak"], "traffic": traffic,
+                     "traffic_unit": "HBM bytes per call"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_on_record(
+            w, args.cpu_sample or min(cfg["cpu_n"], 4096), s_cap, args.mode)
     print(json.dumps(out), flush=True)
 
 

@@ -76,6 +76,8 @@ def _short(name: str) -> str:
         return "solve_kernel"
     if "grad_kernel" in name:
         return "grad_kernel"
+    if "states_kernel" in name:
+        return "states_kernel"
     if "sens_kernel" in name:
         return "sens_kernel"
     if "mlp" in name.lower():
@@ -135,7 +137,7 @@ def summarize(args) -> None:
                "fetch_factor": f_fac, "write_factor": w_fac, "kernels": {}}
     # (the *_phased_ kernels: the two launches of one two-phase solve together)
     for key in ("solve_kernel", "solve_phased_kernel", "solve_sens_kernel",
-                "solve_sens_phased_kernel", "grad_kernel", "sens_kernel"):
+                "solve_sens_phased_kernel", "grad_kernel", "sens_kernel", "states_kernel"):
         fb = per_launch(fetch, "FETCH_SIZE", f_fac, key)
         wb = per_launch(write, "WRITE_SIZE", w_fac, key)
         if fb is not None and wb is not None:
