@@ -827,6 +827,7 @@ struct StatesArgs {
   R* yq;        // [m][D][n]
   const int32_t* perm;
   unsigned long long* groups;
+  bool chunked;  // read h in chunks staged through LDS (2 x 8 slots x 64 lanes per wavefront)
 };
 
 template <class R, class Sys, int METHOD>
@@ -864,8 +865,44 @@ __global__ void __launch_bounds__(256) states_kernel(StatesArgs<R> a) {
     R t = a.t0, prev = a.t0;
     int j = 0;
     int64_t q = (k >= 0) ? 0 : a.m;  // lanes without a trajectory are done
-    R hc = (cnt > 0) ? hrow[0] : R(0);
-    R hn = (cnt > 1) ? hrow[1] : R(0);
+    // h of step r: read step by step, or (a.chunked) from an LDS ring of two
+    // 8-step chunks per lane.  A lane's row is read in 64-byte chunks (four
+    // 16-byte loads), each requested one chunk before it enters the ring, so
+    // every piece of the row is fetched once (read eight bytes per step the
+    // row's lines were fetched again and again).  Chunk c sits in slots
+    // 8 (c & 1) .. 8 (c & 1) + 7; when step 8c is first needed, chunk c goes
+    // from registers (nx) into the ring and chunk c + 1 is requested.
+    typedef R R2 __attribute__((ext_vector_type(2)));
+    HIP_DYNAMIC_SHARED(unsigned char, st_lds)
+    R(*const ring)[WAVE] = (R(*)[WAVE])((R*)st_lds + (threadIdx.x / WAVE) * (16 * WAVE));
+    R nx[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) nx[u] = R(0);
+    auto request = [&](int c) {  // chunk c into nx (rows 8c .. 8c + 7 < s_cap)
+#pragma unroll
+      for (int u = 0; u < 8; u += 2) {
+        const R2 v = *(const R2*)(hrow + 8 * c + u);
+        nx[u] = v.x;
+        nx[u + 1] = v.y;
+      }
+    };
+    auto put_ring = [&](int c) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ring[8 * (c & 1) + u][lane] = nx[u];
+    };
+    R hc = R(0), hn = R(0);
+    if (a.chunked) {
+      if (cnt > 0) {
+        request(0);
+        put_ring(0);
+        if (8 < cnt) request(1);
+        hc = ring[0][lane];
+        hn = ring[1][lane];
+      }
+    } else {
+      hc = (cnt > 0) ? hrow[0] : R(0);
+      hn = (cnt > 1) ? hrow[1] : R(0);
+    }
     R tau = (q < a.m) ? a.tq[q] : R(0);
     while (__ballot(q < a.m)) {
       const bool live = q < a.m;
@@ -887,7 +924,18 @@ __global__ void __launch_bounds__(256) states_kernel(StatesArgs<R> a) {
         t = t + hc;
         ++j;
         hc = hn;
-        if (j + 1 < cnt) hn = hrow[j + 1];
+        const int r = j + 1;
+        if (r < cnt) {
+          if (a.chunked) {
+            if ((r & 7) == 0) {
+              put_ring(r >> 3);
+              if (r + 8 < cnt) request((r >> 3) + 1);
+            }
+            hn = ring[r & 15][lane];
+          } else {
+            hn = hrow[r];
+          }
+        }
       }
       if (put) {
 #pragma unroll
