@@ -385,10 +385,14 @@ dao_status launch_sens(int64_t n, const void* theta, const void* y0, const dao_r
   auto kern = sens_kernel<R, Sys, M, P>;
   const int64_t ngroups = (n + WAVE - 1) / WAVE;
   int64_t blocks = (ngroups + BLOCK / WAVE - 1) / (BLOCK / WAVE);
-  const int64_t res = resident_blocks(kern);
+  // h read in chunks through an LDS ring when the record's rows allow it
+  const bool chunked = rec->s_cap % 8 == 0 && ((uintptr_t)rec->h % 16) == 0;
+  const size_t lds = chunked ? (size_t)BLOCK_WAVES * 16 * WAVE * sizeof(R) : 0;
+  const int64_t res = resident_blocks(kern, lds);
   if (blocks > res) blocks = res;
   launch_order(rec->count, n, s_max, hist, perm, stream);
   SensArgs<R> a;
+  a.chunked = chunked;
   a.n = n;
   a.theta = (const R*)theta;
   a.y0 = (const R*)y0;
@@ -405,7 +409,7 @@ dao_status launch_sens(int64_t n, const void* theta, const void* y0, const dao_r
   for (int d0 = first; d0 < last; d0 += P) {
     a.dir0 = d0;
     hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)groups, (int64_t)2, 0u);
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), 0, stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), lds, stream, a);
   }
   return check_hip(hipGetLastError(), "sensitivity kernel launch");
 }

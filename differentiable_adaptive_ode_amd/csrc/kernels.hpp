@@ -509,6 +509,53 @@ __device__ __forceinline__ void walk_row8(const R* row, int mx, Body&& body) {
   }
 }
 
+// The same chunked reading for a loop whose step index is the same in every
+// lane, without unrolling: each lane's chunks pass through an LDS ring of
+// two 8-step chunks (ring: this wavefront's 16 x 64 values); the chunk after
+// the current one is requested when the current one enters the ring.
+// Call at(i) for i = 0, 1, 2, ... < mx in order.  Same requirements as
+// walk_row8.
+template <class R>
+struct RowRing {
+  typedef R R2 __attribute__((ext_vector_type(2)));
+  R (*ring)[WAVE];
+  const R* row;
+  int mx, lane;
+  R nx[8];
+  __device__ __forceinline__ void request(int c) {
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      const R2 v = *(const R2*)(row + 8 * c + u);
+      nx[u] = v.x;
+      nx[u + 1] = v.y;
+    }
+  }
+  __device__ __forceinline__ void put(int c) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) ring[8 * (c & 1) + u][lane] = nx[u];
+  }
+  __device__ __forceinline__ void init(R (*ring_)[WAVE], const R* row_, int mx_, int lane_) {
+    ring = ring_;
+    row = row_;
+    mx = mx_;
+    lane = lane_;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) nx[u] = R(0);
+    if (mx > 0) {
+      request(0);
+      put(0);
+      if (8 < mx) request(1);
+    }
+  }
+  __device__ __forceinline__ R at(int i) {
+    if (i > 0 && (i & 7) == 0) {
+      put(i >> 3);
+      if (i + 8 < mx) request((i >> 3) + 1);
+    }
+    return ring[i & 15][lane];
+  }
+};
+
 template <class R, class Sys, int METHOD>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu((METHOD == M_ROS23 && Sys::D <= 3) ? 4 : 1)))
@@ -705,6 +752,7 @@ struct SensArgs {
   int dir0;    // first direction of this pass
   const int32_t* perm;
   unsigned long long* groups;
+  bool chunked;  // read h in chunks through an LDS ring (16 x 64 values per wavefront)
 };
 
 template <class R, class Sys, int METHOD, int NT>
@@ -756,11 +804,10 @@ __global__ void __launch_bounds__(256) sens_kernel(SensArgs<R> a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) S[c][t] = (dir[t] - P == c) ? R(1) : R(0);
     // Lockstep steps; past a lane's count h = 0, which leaves y and S
-    // unchanged.  h is loaded one step ahead.
-    R h_nx = (mx > 0) ? hrow[0] : R(0);
-    for (int i = 0; i < mx; ++i) {
-      const R hj = (i < cnt) ? h_nx : R(0);
-      if (i + 1 < mx) h_nx = hrow[i + 1];
+    // unchanged.  h is read a chunk at a time through the LDS ring where the
+    // record's layout allows (a.chunked), else loaded one step ahead.
+    auto step = [&](int i, R hv) {
+      const R hj = (i < cnt) ? hv : R(0);
       if constexpr (METHOD == M_TSIT5) {
         R kk[7][D], Y[D];
         sys.f(y, kk[0]);
@@ -779,6 +826,19 @@ __global__ void __launch_bounds__(256) sens_kernel(SensArgs<R> a) {
         ros23::tangent<R, Sys, NT, false>(sys, St, hj, pdir, S);
 #pragma unroll
         for (int c = 0; c < D; ++c) y[c] = fmaR(hj, St.u[c] + St.k1[c], y[c]);  // as ros23::replay
+      }
+    };
+    if (a.chunked) {
+      HIP_DYNAMIC_SHARED(unsigned char, sn_lds)
+      RowRing<R> rr;
+      rr.init((R(*)[WAVE])((R*)sn_lds + (threadIdx.x / WAVE) * (16 * WAVE)), hrow, mx, lane);
+      for (int i = 0; i < mx; ++i) step(i, rr.at(i));
+    } else {
+      R h_nx = (mx > 0) ? hrow[0] : R(0);
+      for (int i = 0; i < mx; ++i) {
+        const R hv = h_nx;
+        if (i + 1 < mx) h_nx = hrow[i + 1];
+        step(i, hv);
       }
     }
     if (k >= 0) {
