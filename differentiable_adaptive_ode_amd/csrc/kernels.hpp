@@ -473,48 +473,17 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   }
 }
 
-// Walks one record row forward, body(i, row[i]) for i < mx, reading the row
-// in chunks of eight values (four 16-byte loads per lane, the next chunk
-// requested one chunk ahead).  Each lane reads its own row: read eight bytes
-// per step, a row's lines are fetched again whenever they leave the cache
-// between two steps, and the record is read several times over; read a
-// chunk at a time, each 64-byte piece is used as soon as it arrives.
-// Requires s_cap % 8 == 0 (so a chunk at i0 < mx <= s_cap stays in the row)
-// and a 16-byte aligned row.
-template <class R, class Body>
-__device__ __forceinline__ void walk_row8(const R* row, int mx, Body&& body) {
-  typedef R R2 __attribute__((ext_vector_type(2)));
-  R cur[8], nxt[8];
-  auto load = [&](R (&b)[8], int i0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const R2 v = *(const R2*)(row + i0 + 2 * q);
-      b[2 * q] = v.x;
-      b[2 * q + 1] = v.y;
-    }
-  };
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    cur[u] = R(0);
-    nxt[u] = R(0);
-  }
-  if (mx > 0) load(cur, 0);
-  for (int i0 = 0; i0 < mx; i0 += 8) {
-    if (i0 + 8 < mx) load(nxt, i0 + 8);
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (i0 + u < mx) body(i0 + u, cur[u]);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
-  }
-}
-
-// The same chunked reading for a loop whose step index is the same in every
-// lane, without unrolling: each lane's chunks pass through an LDS ring of
-// two 8-step chunks (ring: this wavefront's 16 x 64 values); the chunk after
-// the current one is requested when the current one enters the ring.
-// Call at(i) for i = 0, 1, 2, ... < mx in order.  Same requirements as
-// walk_row8.
+// Reads one record row per lane forward in a loop whose step index is the
+// same in every lane.  Each lane reads its own row: read eight bytes per
+// step, a row's lines are fetched again whenever they leave the cache
+// between two steps, and the record is read several times over.  Here the
+// row goes in 64-byte chunks (four 16-byte loads per lane) through an LDS
+// ring of two 8-step chunks (ring: this wavefront's 16 x 64 values); the
+// chunk after the current one is requested when the current one enters the
+// ring, so each piece is fetched once and has a chunk's worth of steps to
+// arrive.  Call at(i) for i = 0, 1, 2, ... < mx in order.  Requires
+// s_cap % 8 == 0 (a chunk at 8c < mx <= s_cap stays in the row) and a
+// 16-byte aligned row.
 template <class R>
 struct RowRing {
   typedef R R2 __attribute__((ext_vector_type(2)));
@@ -647,8 +616,9 @@ grad_kernel(GradArgs<R> a) {
     const int64_t istr = rec_y ? D : (int64_t)SD * WAVE, cstr = rec_y ? 1 : WAVE;
     R h_nx = (mx > 0) ? hrow[0] : R(0);
     if (!rec_y) {
-      // (the Tsit5 kernels read the record's h a chunk at a time; the
-      // Rosenbrock23 kernel, held to 128 registers, step by step)
+      // (the Tsit5 kernels read the record's h a chunk at a time through
+      // the LDS ring; the Rosenbrock23 kernel, held to 128 registers, step
+      // by step)
       const bool rows8 = METHOD == M_TSIT5 && (a.s_cap % 8) == 0 && ((uintptr_t)a.h_rec % 16) == 0;
       auto fwd = [&](int i, R hv) {
         const R hj = (i < cnt) ? hv : R(0);
@@ -662,7 +632,12 @@ grad_kernel(GradArgs<R> a) {
           ros23::replay<R, Sys>(sys, y, hj);
       };
       if (rows8) {
-        if constexpr (METHOD == M_TSIT5) walk_row8<R>(hrow, mx, fwd);
+        if constexpr (METHOD == M_TSIT5) {
+          HIP_DYNAMIC_SHARED(unsigned char, gr_lds)
+          RowRing<R> rr;
+          rr.init((R(*)[WAVE])((R*)gr_lds + (threadIdx.x / WAVE) * (16 * WAVE)), hrow, mx, lane);
+          for (int i = 0; i < mx; ++i) fwd(i, rr.at(i));
+        }
       } else {
         for (int i = 0; i < mx; ++i) {
           const R hv = h_nx;
