@@ -616,10 +616,9 @@ grad_kernel(GradArgs<R> a) {
     const int64_t istr = rec_y ? D : (int64_t)SD * WAVE, cstr = rec_y ? 1 : WAVE;
     R h_nx = (mx > 0) ? hrow[0] : R(0);
     if (!rec_y) {
-      // (the Tsit5 kernels read the record's h a chunk at a time through
-      // the LDS ring; the Rosenbrock23 kernel, held to 128 registers, step
-      // by step)
-      const bool rows8 = METHOD == M_TSIT5 && (a.s_cap % 8) == 0 && ((uintptr_t)a.h_rec % 16) == 0;
+      // (the record's h a chunk at a time through the LDS ring, where the
+      // record's layout allows it)
+      const bool rows8 = (a.s_cap % 8) == 0 && ((uintptr_t)a.h_rec % 16) == 0;
       auto fwd = [&](int i, R hv) {
         const R hj = (i < cnt) ? hv : R(0);
 #pragma unroll
@@ -632,12 +631,10 @@ grad_kernel(GradArgs<R> a) {
           ros23::replay<R, Sys>(sys, y, hj);
       };
       if (rows8) {
-        if constexpr (METHOD == M_TSIT5) {
-          HIP_DYNAMIC_SHARED(unsigned char, gr_lds)
-          RowRing<R> rr;
-          rr.init((R(*)[WAVE])((R*)gr_lds + (threadIdx.x / WAVE) * (16 * WAVE)), hrow, mx, lane);
-          for (int i = 0; i < mx; ++i) fwd(i, rr.at(i));
-        }
+        HIP_DYNAMIC_SHARED(unsigned char, gr_lds)
+        RowRing<R> rr;
+        rr.init((R(*)[WAVE])((R*)gr_lds + (threadIdx.x / WAVE) * (16 * WAVE)), hrow, mx, lane);
+        for (int i = 0; i < mx; ++i) fwd(i, rr.at(i));
       } else {
         for (int i = 0; i < mx; ++i) {
           const R hv = h_nx;
