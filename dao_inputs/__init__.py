@@ -16,6 +16,10 @@ the five benchmark ensembles):
 * ``robertson``       k = (0.04, 3e7, 1e4) * exp(0.1 N(0,1)), y0 = (1,0,0), t in [0,1e5]
 * ``loghalo``         v0~U[0.9,1.1], Rc~U[0.1,0.3], q~U[0.8,1.0]; x0~N(0,1)^3, v0~N(0,0.5)^3, t in [0,50]
 * ``decay``           theta ~ U[0.5,2], y0 ~ U[0.5,2], t in [0,2]  (linear test system)
+* ``hires``           HIRES, 8 species; the twelve rate constants at their nominal values for
+                      every trajectory (the ensemble carries no free rate constant); the two
+                      nonzero components of the standard initial state (1, 0, ..., 0, 0.0057)
+                      each scaled by U[0.5,1.5]; t in [0, 321.8122]; targets U[0,0.01]^8
 
 "N(0, s)" is read as standard deviation s.
 """
@@ -50,13 +54,16 @@ class Workload:
 
 SEED_BASE = 1000
 DEFAULT_N = {"decay": 4096, "lotka_volterra": 256, "lorenz63": 65536, "mlp": 16384,
-             "robertson": 262144, "loghalo": 1048576}
+             "robertson": 262144, "loghalo": 1048576, "hires": 131072}
+HIRES_RATES = (1.71, 0.43, 8.32, 0.0007, 8.75, 10.03, 0.035, 1.12, 1.745, 280.0, 0.69, 1.81)
+HIRES_T1 = 321.8122
 CONFIG_ORDER = ["lotka_volterra", "lorenz63", "mlp", "robertson", "loghalo"]
 
 
 
 def _rng(name):
-    seed = SEED_BASE + ({"decay": 0} | {k: i + 1 for i, k in enumerate(CONFIG_ORDER)})[name]
+    seed = SEED_BASE + ({"decay": 0, "hires": len(CONFIG_ORDER) + 1}
+                        | {k: i + 1 for i, k in enumerate(CONFIG_ORDER)})[name]
     return np.random.Generator(np.random.PCG64(seed))
 
 
@@ -117,6 +124,14 @@ def make(name: str, n: int | None = None) -> Workload:
         target = np.concatenate([rng.normal(0.0, 1.0, size=(3, n)), np.zeros((3, n))])
         return Workload(name, name, "tsit5", "f64", n, 0.0, 50.0, 1e-8, 1e-10, theta, y0, target,
                         "half_sq_pos")
+    if name == "hires":
+        theta = np.repeat(np.array(HIRES_RATES)[:, None], n, axis=1)
+        y0 = np.zeros((8, n))
+        y0[0] = rng.uniform(0.5, 1.5, size=n)
+        y0[7] = 0.0057 * rng.uniform(0.5, 1.5, size=n)
+        target = rng.uniform(0.0, 0.01, size=(8, n))
+        return Workload(name, name, "rosenbrock23", "f64", n, 0.0, HIRES_T1, 1e-6, 1e-10, theta,
+                        y0, target, "half_sq")
     raise KeyError(name)
 
 

@@ -32,7 +32,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.cpp")
 
-SYSTEMS = {"decay": 0, "lotka_volterra": 1, "lorenz63": 2, "mlp": 3, "robertson": 4, "loghalo": 5}
+SYSTEMS = {"decay": 0, "lotka_volterra": 1, "lorenz63": 2, "mlp": 3, "robertson": 4, "loghalo": 5,
+           "hires": 6}
 METHODS = {"tsit5": 0, "rosenbrock23": 1}
 STATUS = {0: "ok", 1: "max_steps", 2: "nonfinite", 3: "dt_underflow", 4: "capacity"}
 

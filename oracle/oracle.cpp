@@ -134,7 +134,7 @@ inline double rv(Rev a) { return a.v; }
 // directions (the parameters, then the initial state), each propagated by
 // the chain rule through every operation.  Run through the replay it gives
 // the Jacobian of the final state, column by column, in one pass.
-const int MAXDIR = 9;
+const int MAXDIR = 20;
 thread_local int g_ndir = 0;  // directions in use
 struct Fwd {
   double v;
@@ -255,13 +255,13 @@ const double R23_E32 = 6.0 + 1.4142135623730951;
 // parameter vector (or, for the MLP, the shared weight vector).
 // ----------------------------------------------------------------------------
 enum { SYS_DECAY = 0, SYS_LV = 1, SYS_LORENZ = 2, SYS_MLP = 3, SYS_ROBERTSON = 4, SYS_LOGHALO = 5,
-       SYS_COUNT = 6 };
+       SYS_HIRES = 6, SYS_COUNT = 7 };
 enum { M_TSIT5 = 0, M_ROS23 = 1 };
 enum { ST_OK = 0, ST_MAXSTEPS = 1, ST_NONFINITE = 2, ST_DTMIN = 3, ST_CAPACITY = 4 };
 
-const int SYS_D[SYS_COUNT] = {1, 2, 3, 4, 3, 6};
-const int SYS_P[SYS_COUNT] = {1, 4, 3, 4740, 3, 3};
-const int MAXD = 6;
+const int SYS_D[SYS_COUNT] = {1, 2, 3, 4, 3, 6, 8};
+const int SYS_P[SYS_COUNT] = {1, 4, 3, 4740, 3, 3, 12};
+const int MAXD = 8;
 
 // y' = -theta y  (the linear test system; exact solution y0 exp(-theta t)).
 template <class T>
@@ -362,6 +362,44 @@ void j_halo(const T* th, const T* y, T* J) {
     }
 }
 
+// HIRES (Schaefer's high irradiance response of photomorphogenesis, as given
+// in Hairer & Wanner, Solving ODEs II, Sec. IV.10), eight species, written with
+// its twelve distinct rate constants k1..k12 = theta[0..11] (nominal 1.71,
+// 0.43, 8.32, 0.0007, 8.75, 10.03, 0.035, 1.12, 1.745, 280, 0.69, 1.81):
+//   y1' = -k1 y1 + k2 y2 + k3 y3 + k4        y2' = k1 y1 - k5 y2
+//   y3' = -k6 y3 + k2 y4 + k7 y5             y4' = k3 y2 + k1 y3 - k8 y4
+//   y5' = -k9 y5 + k2 (y6 + y7)
+//   y6' = k11 (y4 + y7) + k1 y5 - (k2 y6 + k10 y6 y8)
+//   y7' = k10 y6 y8 - k12 y7                 y8' = k12 y7 - k10 y6 y8
+template <class T>
+void f_hires(const T* th, const T* y, T* dy) {
+  T a = th[9] * (y[5] * y[7]);
+  T b = th[11] * y[6];
+  dy[0] = fma3(-th[0], y[0], fma3(th[1], y[1], fma3(th[2], y[2], th[3])));
+  dy[1] = fma3(th[0], y[0], -(th[4] * y[1]));
+  dy[2] = fma3(-th[5], y[2], fma3(th[1], y[3], th[6] * y[4]));
+  dy[3] = fma3(th[2], y[1], fma3(th[0], y[2], -(th[7] * y[3])));
+  dy[4] = fma3(-th[8], y[4], th[1] * (y[5] + y[6]));
+  dy[5] = fma3(th[10], y[3] + y[6], fma3(th[0], y[4], -fma3(th[1], y[5], a)));
+  dy[6] = a - b;
+  dy[7] = b - a;
+}
+template <class T>
+void j_hires(const T* th, const T* y, T* J) {
+  for (int i = 0; i < 64; ++i) J[i] = T(0.0);
+  T u = th[9] * y[7];  // d(k10 y6 y8)/d y6
+  T v = th[9] * y[5];  // d(k10 y6 y8)/d y8
+  J[0 * 8 + 0] = -th[0]; J[0 * 8 + 1] = th[1]; J[0 * 8 + 2] = th[2];
+  J[1 * 8 + 0] = th[0];  J[1 * 8 + 1] = -th[4];
+  J[2 * 8 + 2] = -th[5]; J[2 * 8 + 3] = th[1]; J[2 * 8 + 4] = th[6];
+  J[3 * 8 + 1] = th[2];  J[3 * 8 + 2] = th[0]; J[3 * 8 + 3] = -th[7];
+  J[4 * 8 + 4] = -th[8]; J[4 * 8 + 5] = th[1]; J[4 * 8 + 6] = th[1];
+  J[5 * 8 + 3] = th[10]; J[5 * 8 + 4] = th[0]; J[5 * 8 + 5] = -(th[1] + u);
+  J[5 * 8 + 6] = th[10]; J[5 * 8 + 7] = -v;
+  J[6 * 8 + 5] = u;      J[6 * 8 + 6] = -th[11]; J[6 * 8 + 7] = v;
+  J[7 * 8 + 5] = -u;     J[7 * 8 + 6] = th[11];  J[7 * 8 + 7] = -v;
+}
+
 // Neural field y' = W3 tanh(W2 tanh(W1 y + b1) + b2) + b3, sizes 4-64-64-4,
 // weights packed [W1 (64x4, row-major), b1 (64), W2 (64x64), b2 (64),
 // W3 (4x64), b3 (4)] = 4740 values shared by every trajectory.
@@ -396,6 +434,7 @@ void rhs(int sys, const T* th, const T* y, T* dy) {
     case SYS_MLP: f_mlp(th, y, dy); break;
     case SYS_ROBERTSON: f_rober(th, y, dy); break;
     case SYS_LOGHALO: f_halo(th, y, dy); break;
+    case SYS_HIRES: f_hires(th, y, dy); break;
   }
 }
 template <class T>
@@ -406,6 +445,7 @@ bool jac(int sys, const T* th, const T* y, T* J) {
     case SYS_LORENZ: j_lorenz(th, y, J); return true;
     case SYS_ROBERTSON: j_rober(th, y, J); return true;
     case SYS_LOGHALO: j_halo(th, y, J); return true;
+    case SYS_HIRES: j_hires(th, y, J); return true;
     default: return false;
   }
 }

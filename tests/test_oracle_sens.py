@@ -10,7 +10,8 @@ Sec. 3.1).  Pins:
 * the transpose identity lam^T S = the tape's reverse-mode gradient (two
   independent derivative codes: dual numbers forward, a tape backward);
 * complex-step directional derivatives S v;
-* special states: the Lorenz z axis, planar halo orbits, Robertson's mass.
+* special states: the Lorenz z axis, planar halo orbits, Robertson's mass,
+  HIRES's y7 + y8.
 """
 import numpy as np
 import pytest
@@ -47,7 +48,7 @@ def test_decay_sensitivities_closed_form(orc):
 
 
 CASES = [("decay", TSIT), ("lotka_volterra", TSIT), ("lorenz63", TSIT), ("loghalo", TSIT),
-         ("robertson", ROS), ("lorenz63", ROS)]
+         ("robertson", ROS), ("lorenz63", ROS), ("hires", ROS)]
 
 
 def _case(orc, system, method, n):
@@ -130,6 +131,20 @@ def test_robertson_mass_sensitivities(orc):
     scale = np.abs(S * w.theta[None]).max(axis=(0, 1))
     assert np.all(np.abs((S * w.theta[None]).sum(axis=0)).max(axis=0) < 1e-10 * scale)
     assert np.max(np.abs(Sy.sum(axis=0) - 1.0)) < 1e-12
+
+
+def test_hires_invariant_sensitivities(orc):
+    # y7 + y8 is conserved, so its sensitivity to every rate constant is zero
+    # and its sensitivity to y0 is the indicator of components 7 and 8.
+    w = di.make("hires", 3)
+    r = _solve(orc, w)
+    S_th, S_y0, _ = orc.sens(w.system, w.method, w.theta, w.y0, r["count"], r["h"], with_y0=True)
+    inv_th = S_th[6] + S_th[7]
+    assert np.all(np.abs(inv_th * w.theta).max(axis=0) < 1e-12)
+    inv_y0 = S_y0[6] + S_y0[7]
+    ind = np.zeros(8)
+    ind[6:8] = 1.0
+    assert np.allclose(inv_y0, ind[:, None], rtol=0, atol=1e-12)
 
 
 def test_planted_mistake_is_caught(orc):

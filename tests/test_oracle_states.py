@@ -44,7 +44,7 @@ def test_decay_states_closed_form(orc):
             assert abs(yq[q, 0, k] - cont) <= 50 * (w.rtol * abs(cont) + w.atol)
 
 
-@pytest.mark.parametrize("system", ["lorenz63", "lotka_volterra", "robertson", "loghalo"])
+@pytest.mark.parametrize("system", ["lorenz63", "lotka_volterra", "robertson", "loghalo", "hires"])
 def test_boundaries_reproduce_the_replay(orc, system):
     w = di.make(system, 4)
     if system == "loghalo":

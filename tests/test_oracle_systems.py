@@ -165,6 +165,62 @@ def test_robertson_mass_cotangent(orc):
     assert np.max(np.abs(dy0 - 1.0)) < 1e-12
 
 
+# ---------------------------------------------------------------- HIRES
+def test_hires_linear_invariant(orc):
+    # y7' + y8' = 0 identically, and the Jacobian's rows 7 and 8 sum to zero,
+    # so every Rosenbrock stage keeps k7 + k8 = 0 and y7 + y8 is carried
+    # through the solve up to rounding.
+    w = di.make("hires", 16)
+    r = solve_w(orc, w, s_cap=4096)
+    assert np.all(r["status"] == 0)
+    drift = np.abs((r["y1"][6] + r["y1"][7]) - (w.y0[6] + w.y0[7]))
+    assert drift.max() < 1e-15
+    assert np.all(r["y1"] > -1e-12)
+
+
+def test_hires_invariant_cotangent(orc):
+    # With dL/dy1 = e7 + e8 the loss is the invariant itself: no rate
+    # constant moves it (gradient zero to rounding) and dL/dy0 = e7 + e8.
+    w = di.make("hires", 4)
+    r = solve_w(orc, w, s_cap=4096)
+    lam = np.zeros((8, w.n))
+    lam[6:8] = 1.0
+    dth, dy0, _ = orc.grad(w.system, w.method, w.theta, w.y0, r["count"], r["h"], lam)
+    lam1 = np.zeros((8, w.n))
+    lam1[6] = 1.0
+    dth_ref, _, _ = orc.grad(w.system, w.method, w.theta, w.y0, r["count"], r["h"], lam1)
+    scale = np.abs(dth_ref * w.theta).max(axis=0)
+    assert np.all(np.abs(dth * w.theta).max(axis=0) < 1e-10 * scale)
+    assert np.max(np.abs(dy0 - lam)) < 1e-12
+
+
+def test_hires_matches_an_independent_implicit_solver(orc):
+    # The oracle's Rosenbrock23 solve at a tight tolerance against SciPy's
+    # Radau IIA (an independent fifth-order implicit method and code) at a
+    # tighter one: agreement to the tolerance scale pins the stiff solve with
+    # pivoting on an eight-dimensional system.
+    from scipy.integrate import solve_ivp
+
+    k = di.HIRES_RATES
+
+    def field(t, y):
+        a = k[9] * y[5] * y[7]
+        return [-k[0] * y[0] + k[1] * y[1] + k[2] * y[2] + k[3], k[0] * y[0] - k[4] * y[1],
+                -k[5] * y[2] + k[1] * y[3] + k[6] * y[4], k[2] * y[1] + k[0] * y[2] - k[7] * y[3],
+                -k[8] * y[4] + k[1] * (y[5] + y[6]),
+                k[10] * (y[3] + y[6]) + k[0] * y[4] - k[1] * y[5] - a, a - k[11] * y[6],
+                k[11] * y[6] - a]
+
+    w = di.make("hires", 3)
+    w.rtol, w.atol = 1e-8, 1e-12
+    r = solve_w(orc, w, s_cap=65536)
+    assert np.all(r["status"] == 0)
+    for j in range(w.n):
+        s = solve_ivp(field, (w.t0, w.t1), w.y0[:, j], method="Radau", rtol=1e-12, atol=1e-16)
+        ref = s.y[:, -1]
+        assert np.allclose(r["y1"][:, j], ref, rtol=2e-6, atol=1e-12), (j, r["y1"][:, j], ref)
+
+
 def test_ros23_error_estimate_tracks_local_error(orc):
     # The Rosenbrock23 estimate is the difference to the embedded third-order
     # solution, so est / (y_new - exact) -> 1 as h -> 0 on a smooth problem;
@@ -304,7 +360,8 @@ def test_mlp_constant_field(orc):
 
 # ---------------------------------------------------------------- derivative pins
 CASES = [("decay", TSIT), ("lotka_volterra", TSIT), ("lorenz63", TSIT), ("loghalo", TSIT),
-         ("robertson", ROS), ("mlp", TSIT), ("lotka_volterra", ROS), ("lorenz63", ROS)]
+         ("robertson", ROS), ("mlp", TSIT), ("lotka_volterra", ROS), ("lorenz63", ROS),
+         ("hires", ROS)]
 
 
 def _case(orc, system, method, n):
@@ -372,12 +429,12 @@ def test_gradient_is_per_trajectory(orc):
         assert np.array_equal(dk[:, 0], dth[:, k]) and np.array_equal(yk[:, 0], dy0[:, k])
 
 
-@pytest.mark.parametrize("system", ["lotka_volterra", "lorenz63", "robertson", "loghalo"])
+@pytest.mark.parametrize("system", ["lotka_volterra", "lorenz63", "robertson", "loghalo", "hires"])
 def test_jacobians_match_complex_step_of_fields(orc, system):
     w = di.make(system, 4)
     for k in range(4):
         th = w.theta[:, k]
-        y = w.y0[:, k] + (0.1 if system == "robertson" else 0.0)
+        y = w.y0[:, k] + (0.1 if system in ("robertson", "hires") else 0.0)
         J = orc.jac(system, th, y)
         d = len(y)
         for j in range(d):
