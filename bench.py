@@ -58,6 +58,13 @@ WORKLOADS = {
                       grad=105 + (105 - 9) + 144, peak=78.6e12, bound="alu", cpu_n=8192),
     "loghalo": dict(s_cap=8192, with_t=False, states=False, init=124, att=497, replay=378,
                     grad=_tsit5_grad(378, 6, 41), peak=78.6e12, bound="alu", cpu_n=2048),
+    # HIRES, Rosenbrock23 with the dense 8 x 8 LU of W = I - gamma h J.  Gradient
+    # step: replay + stages (replay - 3 d) + reverse 730 = two transposed solves
+    # 2 (2 d^2 - d) = 240, the Jacobian cotangent h gamma (rb u^T + F0b k1^T)
+    # 4 d^2 = 256, two field VJPs 2 x 76, the Jacobian's pull-back 32, and the
+    # cotangent updates 6 d + 2 = 50.
+    "hires": dict(s_cap=4096, with_t=True, states=False, init=192, att=1053, replay=807,
+                  grad=807 + (807 - 24) + 730, peak=78.6e12, bound="alu", cpu_n=1024),
 }
 # Forward sensitivities (solve_sens, Tsit5): per accepted step and parameter
 # direction, the stage tangents and the tangent update take 48 d flops, plus
@@ -164,6 +171,10 @@ def main():
 
     dev = torch.device("cuda:0")
     w = di.make(args.workload, args.n)
+    if args.mode in ("sens", "replay_sens") and w.name not in JVP_SUM:
+        # HIRES is differentiated with respect to its initial state (its rate
+        # constants are fixed), so its forward sensitivities are not benchmarked
+        raise SystemExit(f"bench: no forward-sensitivity benchmark for {w.name}")
     if args.mode == "sens":
         return bench_sens(args, w)
     if args.mode in ("replay_sens", "states"):

@@ -127,10 +127,10 @@ dao_status check_hip(hipError_t e, const char* what) {
   return fail(DAO_EDEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
-const int SYS_D[6] = {1, 2, 3, 4, 3, 6};
-const int SYS_P[6] = {1, 4, 3, 4740, 3, 3};
+const int SYS_D[7] = {1, 2, 3, 4, 3, 6, 8};
+const int SYS_P[7] = {1, 4, 3, 4740, 3, 3, 12};
 
-bool sys_ok(int sys) { return sys >= 0 && sys <= 5; }
+bool sys_ok(int sys) { return sys >= 0 && sys <= 6; }
 
 struct DevInfo {
   int cus = 0;
@@ -625,7 +625,7 @@ Impl make_impl() {
 }
 
 const Impl* find_impl(int sys, int method, int dtype) {
-  static Impl table[6][2][2];
+  static Impl table[7][2][2];
   static bool init = false;
   static std::mutex mu;
   std::lock_guard<std::mutex> lk(mu);
@@ -649,6 +649,9 @@ const Impl* find_impl(int sys, int method, int dtype) {
     table[DAO_SYS_ROBERTSON][M_ROS23][DAO_F32] = make_impl<float, Robertson, M_ROS23>();
     table[DAO_SYS_LOGHALO][M_TSIT5][DAO_F64] = make_impl<double, LogHalo, M_TSIT5>();
     table[DAO_SYS_LOGHALO][M_TSIT5][DAO_F32] = make_impl<float, LogHalo, M_TSIT5>();
+    table[DAO_SYS_HIRES][M_TSIT5][DAO_F64] = make_impl<double, Hires, M_TSIT5>();
+    table[DAO_SYS_HIRES][M_ROS23][DAO_F64] = make_impl<double, Hires, M_ROS23>();
+    table[DAO_SYS_HIRES][M_ROS23][DAO_F32] = make_impl<float, Hires, M_ROS23>();
     table[DAO_SYS_MLP][M_TSIT5][DAO_F32] =
         Impl{&launch_mlp_solve, &launch_mlp_grad, &mlp_slot_bytes, &mlp_resident_waves, mlp::SLOTS,
              nullptr, nullptr, nullptr, &mlp_solve_ws};

@@ -220,6 +220,138 @@ struct Robertson {
   }
 };
 
+// HIRES, the eight-species photomorphogenesis model (Schaefer 1975, in the
+// form of Hairer & Wanner, Solving ODEs II, Sec. IV.10; arXiv 2609.02876
+// Sec. 3.1 lists it among the fused kernels' stiff fields), with its twelve
+// distinct rate constants theta = (k1 .. k12):
+//   y1' = -k1 y1 + k2 y2 + k3 y3 + k4        y2' = k1 y1 - k5 y2
+//   y3' = -k6 y3 + k2 y4 + k7 y5             y4' = k3 y2 + k1 y3 - k8 y4
+//   y5' = -k9 y5 + k2 (y6 + y7)
+//   y6' = k11 (y4 + y7) + k1 y5 - (k2 y6 + a),  a = k10 y6 y8
+//   y7' = a - k12 y7                         y8' = k12 y7 - a
+// (indices below are 0-based: y[5] is y6, y[7] is y8).  Only a couples
+// states nonlinearly, so J is constant apart from four entries.
+template <class R>
+struct Hires {
+  static constexpr int D = 8, P = 12;
+  R k[P];
+  __device__ void load(const R* theta, int64_t n, int64_t kk) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) k[i] = theta[i * n + kk];
+  }
+  __device__ void f(const R (&y)[D], R (&dy)[D]) const {
+    const R a = k[9] * (y[5] * y[7]);
+    const R b = k[11] * y[6];
+    dy[0] = fmaR(-k[0], y[0], fmaR(k[1], y[1], fmaR(k[2], y[2], k[3])));
+    dy[1] = fmaR(k[0], y[0], -(k[4] * y[1]));
+    dy[2] = fmaR(-k[5], y[2], fmaR(k[1], y[3], k[6] * y[4]));
+    dy[3] = fmaR(k[2], y[1], fmaR(k[0], y[2], -(k[7] * y[3])));
+    dy[4] = fmaR(-k[8], y[4], k[1] * (y[5] + y[6]));
+    dy[5] = fmaR(k[10], y[3] + y[6], fmaR(k[0], y[4], -fmaR(k[1], y[5], a)));
+    dy[6] = a - b;
+    dy[7] = b - a;
+  }
+  // yb = J^T v;  pb += (df/dk)^T v
+  __device__ void vjp(const R (&y)[D], const R (&v)[D], R (&yb)[D], R (&pb)[P]) const {
+    const R u = k[9] * y[7], w = k[9] * y[5];
+    const R s5 = (v[6] - v[7]) - v[5];  // weight of a in (f5, f6, f7)
+    const R s6 = v[7] - v[6];           // weight of k12 y7 in (f6, f7)
+    yb[0] = k[0] * (v[1] - v[0]);
+    yb[1] = fmaR(k[1], v[0], fmaR(k[2], v[3], -(k[4] * v[1])));
+    yb[2] = fmaR(k[2], v[0], fmaR(k[0], v[3], -(k[5] * v[2])));
+    yb[3] = fmaR(k[1], v[2], fmaR(k[10], v[5], -(k[7] * v[3])));
+    yb[4] = fmaR(k[6], v[2], fmaR(k[0], v[5], -(k[8] * v[4])));
+    yb[5] = fmaR(k[1], v[4] - v[5], u * s5);
+    yb[6] = fmaR(k[1], v[4], fmaR(k[10], v[5], k[11] * s6));
+    yb[7] = w * s5;
+    pb[0] = fmaR(y[0], v[1] - v[0], fmaR(y[2], v[3], fmaR(y[4], v[5], pb[0])));
+    pb[1] = fmaR(y[1], v[0], fmaR(y[3], v[2], fmaR(y[5] + y[6], v[4], fmaR(-y[5], v[5], pb[1]))));
+    pb[2] = fmaR(y[2], v[0], fmaR(y[1], v[3], pb[2]));
+    pb[3] = pb[3] + v[0];
+    pb[4] = fmaR(-y[1], v[1], pb[4]);
+    pb[5] = fmaR(-y[2], v[2], pb[5]);
+    pb[6] = fmaR(y[4], v[2], pb[6]);
+    pb[7] = fmaR(-y[3], v[3], pb[7]);
+    pb[8] = fmaR(-y[4], v[4], pb[8]);
+    pb[9] = fmaR(y[5] * y[7], s5, pb[9]);
+    pb[10] = fmaR(y[3] + y[6], v[5], pb[10]);
+    pb[11] = fmaR(y[6], s6, pb[11]);
+  }
+  __device__ void jac(const R (&y)[D], R (&J)[D][D]) const {
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+#pragma unroll
+      for (int j = 0; j < D; ++j) J[i][j] = R(0);
+    const R u = k[9] * y[7], w = k[9] * y[5];
+    J[0][0] = -k[0]; J[0][1] = k[1]; J[0][2] = k[2];
+    J[1][0] = k[0];  J[1][1] = -k[4];
+    J[2][2] = -k[5]; J[2][3] = k[1]; J[2][4] = k[6];
+    J[3][1] = k[2];  J[3][2] = k[0]; J[3][3] = -k[7];
+    J[4][4] = -k[8]; J[4][5] = k[1]; J[4][6] = k[1];
+    J[5][3] = k[10]; J[5][4] = k[0]; J[5][5] = -(k[1] + u); J[5][6] = k[10]; J[5][7] = -w;
+    J[6][5] = u;     J[6][6] = -k[11]; J[6][7] = w;
+    J[7][5] = -u;    J[7][6] = k[11];  J[7][7] = -w;
+  }
+  // <Jb, J>: y6 and y8 enter through u = k10 y8 (J55, J65, J75) and
+  // w = k10 y6 (J57, J67, J77); the rate constants through every entry.
+  __device__ void jac_vjp(const R (&y)[D], const R (&Jb)[D][D], R (&yb)[D], R (&pb)[P]) const {
+    const R gu = (Jb[6][5] - Jb[5][5]) - Jb[7][5];
+    const R gw = (Jb[6][7] - Jb[5][7]) - Jb[7][7];
+    yb[7] = fmaR(k[9], gu, yb[7]);
+    yb[5] = fmaR(k[9], gw, yb[5]);
+    pb[0] += ((Jb[1][0] - Jb[0][0]) + Jb[3][2]) + Jb[5][4];
+    pb[1] += (((Jb[0][1] + Jb[2][3]) + Jb[4][5]) + Jb[4][6]) - Jb[5][5];
+    pb[2] += Jb[0][2] + Jb[3][1];
+    pb[4] -= Jb[1][1];
+    pb[5] -= Jb[2][2];
+    pb[6] += Jb[2][4];
+    pb[7] -= Jb[3][3];
+    pb[8] -= Jb[4][4];
+    pb[9] += fmaR(y[7], gu, y[5] * gw);
+    pb[10] += Jb[5][3] + Jb[5][6];
+    pb[11] += Jb[7][6] - Jb[6][6];
+  }
+  // fd = J yd + df/dk_j
+  __device__ void jvp(const R (&y)[D], const R (&yd)[D], int j, R (&fd)[D]) const {
+    R e[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) e[i] = (j == i) ? R(1) : R(0);
+    const R ad = fmaR(e[9], y[5] * y[7], k[9] * fmaR(yd[5], y[7], y[5] * yd[7]));
+    const R bd = fmaR(e[11], y[6], k[11] * yd[6]);
+    fd[0] = fmaR(-k[0], yd[0], fmaR(k[1], yd[1], fmaR(k[2], yd[2],
+            fmaR(-e[0], y[0], fmaR(e[1], y[1], fmaR(e[2], y[2], e[3]))))));
+    fd[1] = fmaR(k[0], yd[0], fmaR(-k[4], yd[1], fmaR(e[0], y[0], -(e[4] * y[1]))));
+    fd[2] = fmaR(-k[5], yd[2], fmaR(k[1], yd[3], fmaR(k[6], yd[4],
+            fmaR(-e[5], y[2], fmaR(e[1], y[3], e[6] * y[4])))));
+    fd[3] = fmaR(k[2], yd[1], fmaR(k[0], yd[2], fmaR(-k[7], yd[3],
+            fmaR(e[2], y[1], fmaR(e[0], y[2], -(e[7] * y[3]))))));
+    fd[4] = fmaR(-k[8], yd[4], fmaR(k[1], yd[5] + yd[6], fmaR(-e[8], y[4], e[1] * (y[5] + y[6]))));
+    fd[5] = fmaR(k[10], yd[3] + yd[6], fmaR(k[0], yd[4], fmaR(-k[1], yd[5],
+            fmaR(e[10], y[3] + y[6], fmaR(e[0], y[4], fmaR(-e[1], y[5], -ad))))));
+    fd[6] = ad - bd;
+    fd[7] = bd - ad;
+  }
+  __device__ void jac_jvp(const R (&y)[D], const R (&yd)[D], int j, R (&Jd)[D][D]) const {
+    R e[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) e[i] = (j == i) ? R(1) : R(0);
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+#pragma unroll
+      for (int c = 0; c < D; ++c) Jd[i][c] = R(0);
+    const R ud = fmaR(e[9], y[7], k[9] * yd[7]);
+    const R wd = fmaR(e[9], y[5], k[9] * yd[5]);
+    Jd[0][0] = -e[0]; Jd[0][1] = e[1]; Jd[0][2] = e[2];
+    Jd[1][0] = e[0];  Jd[1][1] = -e[4];
+    Jd[2][2] = -e[5]; Jd[2][3] = e[1]; Jd[2][4] = e[6];
+    Jd[3][1] = e[2];  Jd[3][2] = e[0]; Jd[3][3] = -e[7];
+    Jd[4][4] = -e[8]; Jd[4][5] = e[1]; Jd[4][6] = e[1];
+    Jd[5][3] = e[10]; Jd[5][4] = e[0]; Jd[5][5] = -(e[1] + ud); Jd[5][6] = e[10]; Jd[5][7] = -wd;
+    Jd[6][5] = ud;    Jd[6][6] = -e[11]; Jd[6][7] = wd;
+    Jd[7][5] = -ud;   Jd[7][6] = e[11];  Jd[7][7] = -wd;
+  }
+};
+
 // Star in a flattened logarithmic halo, Phi = 1/2 v0^2 ln(Rc^2 + x^2 + y^2 + z^2/q^2).
 // State (x, y, z, vx, vy, vz), theta = (v0, Rc, q).
 template <class R>

@@ -59,8 +59,13 @@ typedef enum {
   DAO_SYS_MLP = 3,            /* y'=W3 tanh(W2 tanh(W1 y+b1)+b2)+b3, 4-64-64-4, shared
                                  theta[4740] = [W1(64x4) b1 W2(64x64) b2 W3(4x64) b3]; d=4   */
   DAO_SYS_ROBERTSON = 4,      /* theta=(k1,k2,k3): Robertson kinetics; d=3, p=3              */
-  DAO_SYS_LOGHALO = 5         /* theta=(v0,Rc,q), y=(x,y,z,vx,vy,vz), potential
+  DAO_SYS_LOGHALO = 5,        /* theta=(v0,Rc,q), y=(x,y,z,vx,vy,vz), potential
                                  1/2 v0^2 ln(Rc^2+x^2+y^2+z^2/q^2); d=6, p=3                 */
+  DAO_SYS_HIRES = 6           /* HIRES photomorphogenesis kinetics (Sec. 3.1 lists it among
+                                 the stiff fields), theta = its twelve rate constants
+                                 (k1..k12, nominal 1.71 0.43 8.32 0.0007 8.75 10.03 0.035
+                                 1.12 1.745 280 0.69 1.81); d=8, p=12; f64 with either
+                                 method, f32 with Rosenbrock23                               */
 } dao_system;
 
 typedef enum {

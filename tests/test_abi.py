@@ -44,6 +44,7 @@ def test_system_dims(L):
     assert L.dao_system_dims(L.SYSTEMS["lorenz63"]) == (3, 3, False)
     assert L.dao_system_dims(L.SYSTEMS["mlp"]) == (4, 4740, True)
     assert L.dao_system_dims(L.SYSTEMS["loghalo"]) == (6, 3, False)
+    assert L.dao_system_dims(L.SYSTEMS["hires"]) == (8, 12, False)
     with pytest.raises(L.DaoError):
         L.dao_system_dims(17)
 

@@ -50,7 +50,7 @@ def solve_both(dao, w, s_cap):
 CASES = [("decay", 300, 256, None), ("lotka_volterra", 300, 256, None),
          ("lorenz63", 300, 1024, None), ("loghalo", 200, 4096, None),
          ("robertson", 200, 2048, None), ("lotka_volterra", 200, 1024, "rosenbrock23"),
-         ("lorenz63", 200, 2048, "rosenbrock23")]
+         ("lorenz63", 200, 2048, "rosenbrock23"), ("hires", 130, 4096, None)]
 
 
 def case(name, n, method):
@@ -75,8 +75,9 @@ def test_solve_sens_parity(dao, name, n, s_cap, method):
     h = np.where(mask.cpu().numpy(), r1.h.cpu().numpy(), 0.0)
     S_o, Sy_o, yS = oracle.sens(w.system, w.method, w.theta, w.y0, cnt, h, nthreads=8)
     assert rel_err_mat(yS, y1b.cpu().numpy()).max() <= 1e-13  # the oracle's replay of that mesh
-    # Robertson's rates span 0.04 ... 3e7: compare log-sensitivities theta dy/dtheta
-    sc = w.theta[None] if name == "robertson" else 1.0
+    # Robertson's rates span 0.04 ... 3e7 (HIRES's 7e-4 ... 280): compare
+    # log-sensitivities theta dy/dtheta
+    sc = w.theta[None] if name in ("robertson", "hires") else 1.0
     e = rel_err_mat(S.cpu().numpy() * sc, S_o * sc)
     assert e.max() <= TOL, e.max()
     # forward mode through the replay: the same numbers, bit for bit
@@ -91,7 +92,7 @@ def test_solve_sens_parity(dao, name, n, s_cap, method):
     torch.cuda.synchronize()
     fwd = torch.einsum("cjk,ck->jk", S, lam).cpu().numpy()
     fwd_y = torch.einsum("cjk,ck->jk", Sy, lam).cpu().numpy()
-    sc = w.theta if name == "robertson" else 1.0
+    sc = w.theta if name in ("robertson", "hires") else 1.0
     e_t = rel_err_mat(fwd * sc, gth.cpu().numpy() * sc)
     e_y = rel_err_mat(fwd_y, gy0.cpu().numpy())
     assert e_t.max() <= TOL and e_y.max() <= TOL, (e_t.max(), e_y.max())

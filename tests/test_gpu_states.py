@@ -31,7 +31,7 @@ def rel_err(a, b):
 
 
 CASES = [("decay", 300, 256), ("lotka_volterra", 300, 256), ("lorenz63", 300, 1024),
-         ("loghalo", 200, 4096), ("robertson", 200, 2048)]
+         ("loghalo", 200, 4096), ("robertson", 200, 2048), ("hires", 200, 4096)]
 
 
 @pytest.mark.parametrize("name,n,s_cap", CASES)
