@@ -58,6 +58,11 @@ WORKLOADS = {
                       grad=105 + (105 - 9) + 144, peak=78.6e12, bound="alu", cpu_n=8192),
     "loghalo": dict(s_cap=8192, with_t=False, states=False, init=124, att=497, replay=378,
                     grad=_tsit5_grad(378, 6, 41), peak=78.6e12, bound="alu", cpu_n=2048),
+    # the Lorenz ensemble with its difficulty spread (rho log-uniform on
+    # [20, 1000]): the same per-unit work, step counts over about 8x
+    "lorenz63_spread": dict(s_cap=2048, with_t=True, states=False, init=68, att=254, replay=192,
+                            grad=_tsit5_grad(192, 3, 19), peak=78.6e12, bound="alu",
+                            cpu_n=8192),
     # HIRES, Rosenbrock23 with the dense 8 x 8 LU of W = I - gamma h J.  Gradient
     # step: replay + stages (replay - 3 d) + reverse 730 = two transposed solves
     # 2 (2 d^2 - d) = 240, the Jacobian cotangent h gamma (rb u^T + F0b k1^T)
@@ -115,6 +120,22 @@ def parse():
                     help="before the steps, copy one buffer of MIB MiB once (a plain copy "
                          "kernel of known size, the reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def _divergence(cnt, nrej, attempts, steps_total, t_solve, t_grad):
+    import numpy as np
+
+    def lockstep(x):
+        pad = (-len(x)) % 64
+        g = np.concatenate([x, np.zeros(pad, x.dtype)]).reshape(-1, 64)
+        return float(g.max(axis=1).sum() * 64 / max(x.sum(), 1))
+
+    att = cnt + nrej
+    return {"attempts_per_s": attempts / t_solve, "replay_steps_per_s": steps_total / t_grad,
+            "attempts_p50_p99_max": [int(np.percentile(att, 50)), int(np.percentile(att, 99)),
+                                     int(att.max())],
+            "lockstep_factor_solve": lockstep(att),
+            "lockstep_factor_grad_sorted": lockstep(np.sort(cnt)[::-1].copy())}
 
 
 def copy_calibration(mib, dev):
@@ -295,6 +316,11 @@ def main():
         "accepted_steps_mean": float(cnt.mean()),
         "accepted_steps_max": int(cnt.max()),
         "attempts_total": attempts,
+        # divergence: the work rate per lane-attempt, and what a lockstep code
+        # would issue instead (groups of 64 consecutive trajectories for the
+        # solve, each group running as long as its longest member; the
+        # gradient's groups are sorted by step count first)
+        "divergence": _divergence(cnt, nrej, attempts, steps_total, ts, tk),
         "solve_tflops": fl_solve / ts * 1e-12,
         "grad_tflops": fl_grad / tk * 1e-12,
         "roofline": {"bound": cfg["bound"], "kernel": f"{dom}_kernel",

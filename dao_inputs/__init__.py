@@ -16,6 +16,9 @@ the five benchmark ensembles):
 * ``robertson``       k = (0.04, 3e7, 1e4) * exp(0.1 N(0,1)), y0 = (1,0,0), t in [0,1e5]
 * ``loghalo``         v0~U[0.9,1.1], Rc~U[0.1,0.3], q~U[0.8,1.0]; x0~N(0,1)^3, v0~N(0,0.5)^3, t in [0,50]
 * ``decay``           theta ~ U[0.5,2], y0 ~ U[0.5,2], t in [0,2]  (linear test system)
+* ``lorenz63_spread`` the Lorenz ensemble with its difficulty spread (the divergence stress
+                      test): rho log-uniform on [20, 1000], so that step counts range over
+                      about an order of magnitude; sigma, beta, y0 and targets as ``lorenz63``
 * ``hires``           HIRES, 8 species; the twelve rate constants at their nominal values for
                       every trajectory (the ensemble carries no free rate constant); the two
                       nonzero components of the standard initial state (1, 0, ..., 0, 0.0057)
@@ -54,7 +57,7 @@ class Workload:
 
 SEED_BASE = 1000
 DEFAULT_N = {"decay": 4096, "lotka_volterra": 256, "lorenz63": 65536, "mlp": 16384,
-             "robertson": 262144, "loghalo": 1048576, "hires": 131072}
+             "robertson": 262144, "loghalo": 1048576, "hires": 131072, "lorenz63_spread": 65536}
 HIRES_RATES = (1.71, 0.43, 8.32, 0.0007, 8.75, 10.03, 0.035, 1.12, 1.745, 280.0, 0.69, 1.81)
 HIRES_T1 = 321.8122
 CONFIG_ORDER = ["lotka_volterra", "lorenz63", "mlp", "robertson", "loghalo"]
@@ -62,7 +65,8 @@ CONFIG_ORDER = ["lotka_volterra", "lorenz63", "mlp", "robertson", "loghalo"]
 
 
 def _rng(name):
-    seed = SEED_BASE + ({"decay": 0, "hires": len(CONFIG_ORDER) + 1}
+    seed = SEED_BASE + ({"decay": 0, "hires": len(CONFIG_ORDER) + 1,
+                         "lorenz63_spread": len(CONFIG_ORDER) + 2}
                         | {k: i + 1 for i, k in enumerate(CONFIG_ORDER)})[name]
     return np.random.Generator(np.random.PCG64(seed))
 
@@ -96,6 +100,15 @@ def make(name: str, n: int | None = None) -> Workload:
         target = rng.normal(0.0, 5.0, size=(3, n))
         return Workload(name, name, "tsit5", "f64", n, 0.0, 2.0, 1e-8, 1e-10, theta, y0, target,
                         "half_sq")
+    if name == "lorenz63_spread":
+        sigma = rng.uniform(9.0, 11.0, size=n)
+        rho = 20.0 * np.power(50.0, rng.uniform(0.0, 1.0, size=n))
+        beta = rng.uniform(2.0, 3.0, size=n)
+        theta = np.stack([sigma, rho, beta])
+        y0 = rng.normal(0.0, 1.0, size=(3, n)) + np.array([1.0, 1.0, 20.0])[:, None]
+        target = rng.normal(0.0, 5.0, size=(3, n))
+        return Workload(name, "lorenz63", "tsit5", "f64", n, 0.0, 2.0, 1e-8, 1e-10, theta, y0,
+                        target, "half_sq")
     if name == "mlp":
         W1 = glorot(rng, 64, 4)
         W2 = glorot(rng, 64, 64)
