@@ -80,7 +80,26 @@ struct GradArgs {
   unsigned long long* groups;
 };
 
-// Mean of squares of the scaled error: (1/D) sum_c (e_c / sc_c)^2, summed in
+// The attempt's error test: the embedded error is e_c = s a_c (a_c the
+// unscaled stage combination, s = h for Tsit5 and h/6 for Rosenbrock23) and
+// its scaled component e_c / sc_c is formed as a_c w_c with the weight
+// w_c = s / sc_c.  The weights depend only on h and the two states, so their
+// divisions run while the last stage is still being evaluated and only one
+// multiply sits between the last stage and the accept decision.  Mean of
+// squares in component order, times the constant 1/D.
+template <class R, int D>
+__device__ __forceinline__ R error_msq(const R (&a)[D], const R (&w)[D]) {
+  R r = a[0] * w[0];
+  R acc = r * r;
+#pragma unroll
+  for (int c = 1; c < D; ++c) {
+    r = a[c] * w[c];
+    acc = fmaR(r, r, acc);
+  }
+  return acc * R(1.0 / D);
+}
+
+// Mean of squares of x_c / sc_c (the starting step's norms): summed in
 // component order, the mean taken as a product with the constant 1/D.
 template <class R, int D>
 __device__ __forceinline__ R mean_sq(const R (&e)[D], const R (&sc)[D]) {
@@ -378,13 +397,14 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     } else {
       ros23::trial<R, Sys, !SENS>(sys, y, hs, k[0], ynew, F2, err);
     }
-    R sc[D];
+    const R es = (METHOD == M_TSIT5) ? hs : hs / R(6);
+    R wt[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) {
       const R ay = absR(y[c]), an = absR(ynew[c]);
-      sc[c] = fmaR(a.rtol, (ay < an) ? an : ay, a.atol);
+      wt[c] = es / fmaR(a.rtol, (ay < an) ? an : ay, a.atol);
     }
-    const R msq = mean_sq<R, D>(err, sc);
+    const R msq = error_msq<R, D>(err, wt);
     const bool acc = msq <= R(1);
     // One controller evaluation serves both outcomes.
     const R root = ctrl_root<R, CTRL_Q>(msq, KC);

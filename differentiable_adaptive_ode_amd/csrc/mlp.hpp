@@ -203,7 +203,7 @@ __device__ __forceinline__ void trial(const Fwd& P, float y, float h, float (&k)
   float acc = tsit5::e<float>(0) * k[0];
 #pragma unroll
   for (int j = 1; j < 7; ++j) acc = fmaR(tsit5::e<float>(j), k[j], acc);
-  err = h * acc;
+  err = acc;  // the embedded error without its factor h (in the error weight)
 }
 
 // Stage state i from y and k[0..i-1] (one component).
@@ -215,7 +215,19 @@ __device__ __forceinline__ float stage(int i, float y, float h, const float (&k)
   return fmaR(h, acc, y);
 }
 
-// Mean square of the slot's scaled error, summed in component order.
+// The attempt's error test for the slot: the unscaled error a times the
+// weight w = h / sc (formed while the last stage is evaluated), squared and
+// averaged over the slot's four components in component order.
+__device__ __forceinline__ float slot_error_msq(float a, float w, int j) {
+  float r[4];
+  gather4(a * w, j, r);
+  float acc = r[0] * r[0];
+#pragma unroll
+  for (int c = 1; c < 4; ++c) acc = fmaR(r[c], r[c], acc);
+  return acc * (1.0f / 4.0f);
+}
+
+// Mean square of a slot vector e / sc, summed in component order.
 __device__ __forceinline__ float slot_mean_sq(float e, float sc, int j) {
   float r[4];
   gather4(e / sc, j, r);
@@ -346,8 +358,8 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs a) {
     float ynew, err;
     trial(P, y, hs, k, ynew, err);
     const float ay = absR(y), an = absR(ynew);
-    const float sc = fmaR(a.rtol, (ay < an) ? an : ay, a.atol);
-    const float msq = slot_mean_sq(err, sc, j);
+    const float wt = hs / fmaR(a.rtol, (ay < an) ? an : ay, a.atol);
+    const float msq = slot_error_msq(err, wt, j);
     const bool acc = msq <= 1.f;
     const float root = ctrl_root<float, 10>(msq, KC);
     const float fq = (msq == 0.f) ? 10.f : truncBits(0.9f * root);

@@ -11,7 +11,8 @@
 //   y_new = y + h k2
 //   F2 = f(y_new)                                   (reused as the next F0)
 //   k3 = W^-1 (F2 - e32 (k2 - F1) - 2 (k1 - F0)),   e32 = 6 + sqrt 2
-//   err = h/6 (k1 - 2 k2 + k3)
+//   err = h/6 (k1 - 2 k2 + k3)   (trial() returns k1 - 2 k2 + k3; the
+//                                 solve folds h/6 into its error weights)
 //
 // W is factored per lane as P W = L U with partial pivoting (first row of
 // largest magnitude); the reciprocal pivots are formed once per
@@ -199,9 +200,9 @@ __device__ __forceinline__ void trial(const Sys& sys, const R (&y)[Sys::D], R h,
     r[c] = fmaR(R(-2), k1[c] - F0[c], t2);
   }
   solve<R, D, SKIP>(w, r, k3);
-  R h6 = h / R(6);
+  // the embedded error without its factor h/6 (in the error weights)
 #pragma unroll
-  for (int c = 0; c < D; ++c) err[c] = h6 * (fmaR(R(-2), k2[c], k1[c]) + k3[c]);
+  for (int c = 0; c < D; ++c) err[c] = fmaR(R(-2), k2[c], k1[c]) + k3[c];
 }
 
 // Replay step y <- Phi(y; h) (no k3, no error estimate).

@@ -118,7 +118,7 @@ __device__ __forceinline__ void trial(const Coef<R>& C, const Sys& sys, const R 
     R acc = C.e[0] * k[0][c];
 #pragma unroll
     for (int j = 1; j < 7; ++j) acc = fmaR(C.e[j], k[j][c], acc);
-    err[c] = h * acc;
+    err[c] = acc;  // the embedded error without its factor h (in the error weights)
   }
 }
 

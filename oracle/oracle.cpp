@@ -453,10 +453,13 @@ bool jac(int sys, const T* th, const T* y, T* J) {
 // ----------------------------------------------------------------------------
 // One Tsit5 step (Section 2.1, Eqs. 1-2).  k[0] holds f(y) on entry.  Fills
 // k[1..6], ynew (= the seventh stage state) and, if err != nullptr, the
-// embedded error e = h * sum_j BT_j k_j (needs k[6] = f(ynew)).
+// embedded error e = h * sum_j BT_j k_j (needs k[6] = f(ynew)).  With
+// unscaled set, err receives sum_j BT_j k_j without the factor h (the solve
+// folds h into its error weights, see error_msq).
 // ----------------------------------------------------------------------------
 template <class T>
-void tsit5_step(int sys, const T* th, int d, const T* y, T h, T k[7][MAXD], T* ynew, T* err) {
+void tsit5_step(int sys, const T* th, int d, const T* y, T h, T k[7][MAXD], T* ynew, T* err,
+                bool unscaled = false) {
   T Y[MAXD];
   for (int i = 1; i < 7; ++i) {
     for (int c = 0; c < d; ++c) {
@@ -473,7 +476,7 @@ void tsit5_step(int sys, const T* th, int d, const T* y, T h, T k[7][MAXD], T* y
   for (int c = 0; c < d; ++c) {
     T acc = T(TS_BT[0]) * k[0][c];
     for (int j = 1; j < 7; ++j) acc = fma3(T(TS_BT[j]), k[j][c], acc);
-    err[c] = h * acc;
+    err[c] = unscaled ? acc : h * acc;
   }
 }
 
@@ -524,7 +527,8 @@ void lu_solve(int d, const T* LU, const int* piv, const T* rp, const T* b, T* x)
 // F2 = f(ynew) (returned for reuse as the next F0) and the error estimate.
 // ----------------------------------------------------------------------------
 template <class T>
-void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* ynew, T* F2, T* err) {
+void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* ynew, T* F2, T* err,
+                bool unscaled = false) {
   T J[MAXD * MAXD], W[MAXD * MAXD], rp[MAXD];
   int piv[MAXD];
   jac(sys, th, y, J);
@@ -549,6 +553,10 @@ void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* yn
     r[c] = fma3(T(-2.0), k1[c] - F0[c], t2);
   }
   lu_solve(d, W, piv, rp, r, k3);
+  if (unscaled) {  // without the factor h/6 (folded into the solve's error weights)
+    for (int c = 0; c < d; ++c) err[c] = fma3(T(-2.0), k2[c], k1[c]) + k3[c];
+    return;
+  }
   T h6 = h / T(6.0);
   for (int c = 0; c < d; ++c) err[c] = h6 * (fma3(T(-2.0), k2[c], k1[c]) + k3[c]);
 }
@@ -636,6 +644,24 @@ T mean_sq(int d, const T* e, const T* sc) {
   return acc * T(1.0 / d);
 }
 
+// The attempt's error test.  The embedded error is e_c = s a_c, with a_c
+// the unscaled combination of the stages and s the step's factor (h for
+// Tsit5, h/6 for Rosenbrock23); its scaled component e_c / sc_c is formed
+// as a_c w_c with the weight w_c = s / sc_c.  Every value of w is known
+// before the last stage is evaluated, so its division stays off the path
+// from the last stage to the accept decision.  Mean square in component
+// order, times the constant 1/d.
+template <class T>
+T error_msq(int d, const T* a, const T* w) {
+  T r = a[0] * w[0];
+  T acc = r * r;
+  for (int c = 1; c < d; ++c) {
+    r = a[c] * w[c];
+    acc = fma3(r, r, acc);
+  }
+  return acc * T(1.0 / d);
+}
+
 // Starting step (Hairer, Norsett & Wanner, Solving ODEs I, Sec. II.4).
 template <class T>
 T initial_step(int sys, const T* th, int d, const T* y0, const T* f0, T span, T rtol, T atol,
@@ -689,13 +715,17 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
       if (!finite_(hs)) { out.status = ST_NONFINITE; break; }
       if (!(t + hs > t)) { out.status = ST_DTMIN; break; }
       if (method == M_TSIT5) {
-        tsit5_step(sys, th, d, y, hs, k, ynew, e);
+        tsit5_step(sys, th, d, y, hs, k, ynew, e, true);
       } else {
-        ros23_step(sys, th, d, y, hs, k[0], ynew, F2, e);
+        ros23_step(sys, th, d, y, hs, k[0], ynew, F2, e, true);
       }
-      for (int c = 0; c < d; ++c)
+      const T es = (method == M_TSIT5) ? hs : hs / T(6.0);
+      T w[MAXD];
+      for (int c = 0; c < d; ++c) {
         sc[c] = fma3(rtol, std::max(abs_(y[c]), abs_(ynew[c])), atol);
-      T msq = mean_sq(d, e, sc);
+        w[c] = es / sc[c];
+      }
+      T msq = error_msq(d, e, w);
       if (!finite_(msq)) { out.status = ST_NONFINITE; break; }
       if (msq <= T(1.0)) {
         if (n >= s_cap) { out.status = ST_CAPACITY; break; }
