@@ -44,23 +44,26 @@ def _tsit5_grad(replay, d, v):
 
 
 WORKLOADS = {
+    # The record keeps h_n only (the pages: only the step sizes survive the
+    # record; t_n is their running sum, which the replay forms itself), 8 bytes
+    # per accepted step.  --record-t 1 keeps t_n too.
     # name: s_cap, keep t record, keep the states (the gradient then skips the
     # replay's forward pass; measured slower end to end on every workload here:
     # the solve's extra state writes cost what the replay saves, so off), flops,
     # peak (flop/s), bound, cpu sample size
-    "lotka_volterra": dict(s_cap=256, with_t=True, states=False, init=50, att=175, replay=132,
+    "lotka_volterra": dict(s_cap=256, with_t=False, states=False, init=50, att=175, replay=132,
                            grad=_tsit5_grad(132, 2, 21), peak=78.6e12, bound="alu", cpu_n=256),
-    "lorenz63": dict(s_cap=1024, with_t=True, states=False, init=68, att=254, replay=192,
+    "lorenz63": dict(s_cap=1024, with_t=False, states=False, init=68, att=254, replay=192,
                      grad=_tsit5_grad(192, 3, 19), peak=78.6e12, bound="alu", cpu_n=65536),
-    "mlp": dict(s_cap=64, with_t=True, states=False, init=18754, att=56337, replay=56256,
+    "mlp": dict(s_cap=64, with_t=False, states=False, init=18754, att=56337, replay=56256,
                 grad=_tsit5_grad(56256, 4, 18954), peak=157.3e12, bound="mfma", cpu_n=1024),
-    "robertson": dict(s_cap=1024, with_t=True, states=False, init=68, att=171, replay=105,
+    "robertson": dict(s_cap=1024, with_t=False, states=False, init=68, att=171, replay=105,
                       grad=105 + (105 - 9) + 144, peak=78.6e12, bound="alu", cpu_n=8192),
     "loghalo": dict(s_cap=8192, with_t=False, states=False, init=124, att=497, replay=378,
                     grad=_tsit5_grad(378, 6, 41), peak=78.6e12, bound="alu", cpu_n=2048),
     # the Lorenz ensemble with its difficulty spread (rho log-uniform on
     # [20, 1000]): the same per-unit work, step counts over about 8x
-    "lorenz63_spread": dict(s_cap=2048, with_t=True, states=False, init=68, att=254, replay=192,
+    "lorenz63_spread": dict(s_cap=2048, with_t=False, states=False, init=68, att=254, replay=192,
                             grad=_tsit5_grad(192, 3, 19), peak=78.6e12, bound="alu",
                             cpu_n=8192),
     # HIRES, Rosenbrock23 with the dense 8 x 8 LU of W = I - gamma h J.  Gradient
@@ -68,7 +71,7 @@ WORKLOADS = {
     # 2 (2 d^2 - d) = 240, the Jacobian cotangent h gamma (rb u^T + F0b k1^T)
     # 4 d^2 = 256, two field VJPs 2 x 76, the Jacobian's pull-back 32, and the
     # cotangent updates 6 d + 2 = 50.
-    "hires": dict(s_cap=4096, with_t=True, states=False, init=192, att=1053, replay=807,
+    "hires": dict(s_cap=4096, with_t=False, states=False, init=192, att=1053, replay=807,
                   grad=807 + (807 - 24) + 730, peak=78.6e12, bound="alu", cpu_n=1024),
 }
 # Forward sensitivities (solve_sens, Tsit5): per accepted step and parameter
@@ -114,6 +117,8 @@ def parse():
                          "of a record; states: the states at 16 requested times on a record")
     ap.add_argument("--states", action="store_true",
                     help="record states in the solve; the gradient skips the forward replay")
+    ap.add_argument("--record-t", type=int, choices=(0, 1), default=None,
+                    help="keep t_n in the record beside h_n (default: the workload's setting)")
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="trajectories in the CPU-baseline sample (default per workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -206,7 +211,8 @@ def main():
     y0 = torch.tensor(w.y0, device=dev)
     tgt = torch.tensor(w.target, device=dev)
     states = cfg["states"] or args.states
-    bufs = api.alloc_record(w.n, s_cap, w.dtype, dev, with_t=cfg["with_t"],
+    with_t = cfg["with_t"] if args.record_t is None else bool(args.record_t)
+    bufs = api.alloc_record(w.n, s_cap, w.dtype, dev, with_t=with_t,
                             states_dim=w.d if states else 0)
     # cotangent of the workload's loss: 1/2 |y - target|^2 (positions only for
     # the orbits), or the mean square over the n x d entries (neural field)
@@ -306,7 +312,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name} ensemble", "n_trajectories": w.n, "method": w.method,
                    "t_span": [w.t0, w.t1], "rtol": w.rtol, "atol": w.atol, "s_cap": s_cap,
-                   "recorded_states": states},
+                   "recorded_states": states, "record_t": with_t},
         "solves_per_s": w.n / ts,
         "grad_trajectories_per_s": w.n / tg,
         "solve_ms": ts * 1e3,
