@@ -70,6 +70,8 @@ def lib():
         L.oracle_grad_f64.argtypes = [I, I, I64, P, P, P, P, I64, P, P, P, P, I]
         L.oracle_sens_f64.argtypes = [I, I, I64, P, P, P, P, I64, P, P, P, I]
         L.oracle_states_at_f64.argtypes = [I, I, I64, P, P, D, D, P, P, I64, I64, P, P, I]
+        L.oracle_grad_at_f64.argtypes = [I, I, I64, P, P, D, D, P, P, I64, I64, P, P, P, P, P,
+                                         I]
         L.oracle_step_f64.argtypes = [I, I, P, P, D, P, P]
         L.oracle_rhs_f64.argtypes = [I, P, P, P]
         L.oracle_jac_f64.argtypes = [I, P, P, P]
@@ -203,6 +205,30 @@ def sens(system, method, theta, y0, count, h, with_y0=True, nthreads=1):
                                _p(h), h.shape[1], _p(S_th), _p(S_y0), _p(yS), int(nthreads))
     assert rc == 0
     return S_th, S_y0, yS
+
+
+def grad_at(system, method, theta, y0, t0, t1, count, h, tq, dLdyq, dLdy1=None, nthreads=1):
+    """Gradient of L = sum_q <dLdyq[q], y(tq[q])> + <dLdy1, y(t1)> on the mesh
+    (count, h), the states at tq taken as states_at takes them.  dLdyq
+    [m][d][n]; dLdy1 [d][n] or None.  Returns (dtheta [p][n], dy0 [d][n])."""
+    d, p, shared = dims(system)
+    assert not shared
+    theta = np.ascontiguousarray(theta, dtype=np.float64)
+    y0 = np.ascontiguousarray(y0, dtype=np.float64)
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    count = np.ascontiguousarray(count, dtype=np.int32)
+    tq = np.ascontiguousarray(tq, dtype=np.float64)
+    dLdyq = np.ascontiguousarray(dLdyq, dtype=np.float64)
+    dLdy1 = None if dLdy1 is None else np.ascontiguousarray(dLdy1, dtype=np.float64)
+    n = y0.shape[1]
+    dtheta = np.zeros((p, n))
+    dy0 = np.zeros((d, n))
+    rc = lib().oracle_grad_at_f64(SYSTEMS[system], METHODS[method], n, _p(theta), _p(y0),
+                                  float(t0), float(t1), _p(count), _p(h), h.shape[1], len(tq),
+                                  _p(tq), _p(dLdyq), _p(dLdy1), _p(dtheta), _p(dy0),
+                                  int(nthreads))
+    assert rc == 0
+    return dtheta, dy0
 
 
 def states_at(system, method, theta, y0, t0, t1, count, h, tq, nthreads=1):

@@ -1091,6 +1091,90 @@ int oracle_grad_f64(int sys, int method, int64_t n, const double* theta, const d
   return 0;
 }
 
+// Gradient of a loss on the states at requested times and at t1,
+//   L = sum_q <dLdyq[q], y(tau_q)> + <dLdy1, y(t1)>,
+// with y(tau) as in oracle_states_at_f64 (a shortened step from the start of
+// the step that holds tau), by reverse mode through the replay: one tape per
+// trajectory holds the replay chain and the shortened step to every
+// requested time; each cotangent seeds its state and one backward sweep
+// gives dL/dtheta and dL/dy0 (sg[h]: the recorded steps, the running time
+// and every tau - t_j are constants).  dLdyq [m][d][n]; dLdy1 [d][n] or
+// NULL (zero).  tq ascending in [t0, t1]; otherwise the trajectory's
+// outputs are NaN.  Per-trajectory parameters only.
+int oracle_grad_at_f64(int sys, int method, int64_t n, const double* theta, const double* y0,
+                       double t0, double t1, const int32_t* count, const double* h_rec,
+                       int64_t s_cap, int64_t m, const double* tq, const double* dLdyq,
+                       const double* dLdy1, double* dtheta, double* dy0, int nthreads) {
+  if (!valid_sys(sys, method) || n < 0 || m < 0 || sys == SYS_MLP) return 1;
+  const int d = SYS_D[sys], p = SYS_P[sys];
+  bool bad = false;
+  for (int64_t q = 0; q < m; ++q)
+    if (!(tq[q] >= t0 && tq[q] <= t1) || (q > 0 && tq[q] < tq[q - 1])) bad = true;
+  parallel_for(n, nthreads, [&](int, int64_t lo, int64_t hi) {
+    for (int64_t kk = lo; kk < hi; ++kk) {
+      if (bad) {
+        for (int i = 0; i < p; ++i) dtheta[i * n + kk] = NAN;
+        for (int c = 0; c < d; ++c) dy0[c * n + kk] = NAN;
+        continue;
+      }
+      Tape tape;
+      g_tape = &tape;
+      std::vector<Rev> rth(p);
+      Rev ry0[MAXD], y[MAXD], ys[MAXD], ynew[MAXD], k[7][MAXD];
+      for (int i = 0; i < p; ++i) rth[i] = rleaf(theta[i * n + kk]);
+      for (int c = 0; c < d; ++c) ry0[c] = y[c] = rleaf(y0[c * n + kk]);
+      auto step = [&](const Rev* from, double h, Rev* to) {
+        rhs(sys, rth.data(), from, k[0]);
+        if (method == M_TSIT5)
+          tsit5_step<Rev>(sys, rth.data(), d, from, Rev(h), k, to, nullptr);
+        else
+          ros23_step<Rev>(sys, rth.data(), d, from, Rev(h), k[0], to, nullptr, nullptr);
+      };
+      std::vector<std::pair<int64_t, double>> seeds;
+      const double* h = h_rec + kk * s_cap;
+      const int32_t S = count[kk];
+      double t = t0;
+      int32_t j = 0;
+      for (int64_t q = 0; q < m; ++q) {
+        const double tau = tq[q];
+        // advance to the step that holds tau (the last step holds up to t1)
+        while (j < S - 1 && tau >= t + h[j]) {
+          step(y, h[j], ynew);
+          for (int c = 0; c < d; ++c) y[c] = ynew[c];
+          t = t + h[j];
+          ++j;
+        }
+        const Rev* out = y;
+        if (S > 0) {
+          step(y, tau - t, ys);
+          out = ys;
+        }
+        for (int c = 0; c < d; ++c) seeds.push_back({out[c].id, dLdyq[(q * d + c) * n + kk]});
+      }
+      for (; j < S; ++j) {  // the rest of the replay, to y(t1)
+        step(y, h[j], ynew);
+        for (int c = 0; c < d; ++c) y[c] = ynew[c];
+      }
+      if (dLdy1)
+        for (int c = 0; c < d; ++c) seeds.push_back({y[c].id, dLdy1[c * n + kk]});
+      std::vector<double> adj(tape.nodes.size(), 0.0);
+      for (const auto& sd : seeds)
+        if (sd.first >= 0) adj[sd.first] += sd.second;
+      for (int64_t i = (int64_t)tape.nodes.size() - 1; i >= 0; --i) {
+        const double a = adj[i];
+        if (a == 0.0) continue;
+        const Node& nd = tape.nodes[i];
+        for (int r = 0; r < 3; ++r)
+          if (nd.p[r] >= 0) adj[nd.p[r]] += nd.d[r] * a;
+      }
+      for (int i = 0; i < p; ++i) dtheta[i * n + kk] = adj[rth[i].id];
+      for (int c = 0; c < d; ++c) dy0[c * n + kk] = adj[ry0[c].id];
+      g_tape = nullptr;
+    }
+  });
+  return 0;
+}
+
 // One attempted step from y with step h (no acceptance decision): returns the
 // new state and the embedded error estimate.  For tests of the pairs.
 int oracle_step_f64(int sys, int method, const double* th, const double* y, double h,
