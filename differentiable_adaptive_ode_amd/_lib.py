@@ -76,6 +76,11 @@ def _load():
     L.dao_states_at.argtypes = [I, I, I, I64, P, P, D, D, ctypes.POINTER(dao_record), I64, I64,
                                 P, P, P, SZ, P]
     L.dao_states_at.restype = I
+    L.dao_grad_at_workspace_size.argtypes = [I, I, I, I64, I64, I64]
+    L.dao_grad_at_workspace_size.restype = SZ
+    L.dao_grad_at.argtypes = [I, I, I, I64, P, P, D, D, ctypes.POINTER(dao_record), I64, I64, P,
+                              P, P, P, P, P, SZ, P]
+    L.dao_grad_at.restype = I
     L.dao_sqerr_cotangent.argtypes = [I, I64, I, I, P, P, D, P, P]
     L.dao_sqerr_cotangent.restype = I
     L.dao_last_error.argtypes = []
@@ -139,6 +144,17 @@ def dao_states_at(system, method, dtype, n, theta, y0, t0, t1, rec, s_max, m, tq
     return lib.dao_states_at(system, method, dtype, n, theta, y0, t0, t1,
                              ctypes.byref(rec) if rec is not None else None, s_max, m, tq, yq,
                              workspace, ws_bytes, stream)
+
+
+def dao_grad_at_workspace_size(system, method, dtype, n, s_max, m):
+    return lib.dao_grad_at_workspace_size(system, method, dtype, n, s_max, m)
+
+
+def dao_grad_at(system, method, dtype, n, theta, y0, t0, t1, rec, s_max, m, tq, dLdyq, dLdy1,
+                dLdtheta, dLdy0, workspace, ws_bytes, stream):
+    return lib.dao_grad_at(system, method, dtype, n, theta, y0, t0, t1,
+                           ctypes.byref(rec) if rec is not None else None, s_max, m, tq, dLdyq,
+                           dLdy1, dLdtheta, dLdy0, workspace, ws_bytes, stream)
 
 
 def dao_grad_workspace_size(system, method, dtype, n, s_max):

@@ -261,6 +261,37 @@ def states_at(rec: Record, tq: torch.Tensor, theta: torch.Tensor | None = None,
     return yq
 
 
+def grad_at(rec: Record, tq: torch.Tensor, dLdyq: torch.Tensor, dLdy1: torch.Tensor | None = None,
+            theta: torch.Tensor | None = None, s_max: int | None = None, out_theta=None,
+            out_y0=None, workspace=None, stream=None):
+    """dL/dtheta and dL/dy0 for L = sum_q <dLdyq[q], y(tq[q])> + <dLdy1, y(t1)>
+    on rec's mesh, the states at tq taken as states_at() takes them.
+    tq: device [m], ascending in [t0, t1]; dLdyq: [m][d][n]; dLdy1: [d][n] or None."""
+    th = rec.theta if theta is None else theta
+    _check_dev(th, tq, dLdyq)
+    if tq.dtype != rec.y0.dtype or dLdyq.dtype != rec.y0.dtype:
+        raise TypeError("tq and dLdyq must have the record's dtype")
+    n, m = rec.n, int(tq.numel())
+    d, _, _ = _lib.dao_system_dims(_lib.SYSTEMS[rec.system])
+    if tuple(dLdyq.shape) != (m, d, n):
+        raise ValueError(f"dLdyq must have shape {(m, d, n)}")
+    if s_max is None:
+        s_max = int(rec.count.max().item()) if n > 0 else 0
+    s_max = min(int(s_max), rec.s_cap)
+    ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
+    dev = rec.count.device
+    nb = _lib.dao_grad_at_workspace_size(*ids, n, s_max, m)
+    buf = _ws(dev, workspace).get(max(nb, 1), dev)
+    dth = torch.empty_like(th) if out_theta is None else out_theta
+    dy0 = torch.empty_like(rec.y0) if out_y0 is None else out_y0
+    g1 = None if dLdy1 is None else dLdy1.contiguous()
+    _lib.check(_lib.dao_grad_at(*ids, n, _ptr(th), _ptr(rec.y0), rec.t0, rec.t1,
+                                rec.c_struct(states=False), s_max, m, _ptr(tq.contiguous()),
+                                _ptr(dLdyq.contiguous()), _ptr(g1), _ptr(dth), _ptr(dy0),
+                                _ptr(buf), buf.numel(), _stream(stream)))
+    return dth, dy0
+
+
 def cotangent(y1: torch.Tensor, target: torch.Tensor, scale: float = 1.0, d_used: int | None = None,
               out=None, stream=None):
     """dL/dy1 = scale * (y1 - target) on the first d_used components, 0 elsewhere."""

@@ -294,9 +294,18 @@ dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0,
 // Per-wavefront scratch tile of the gradient: per step the D state
 // components and h, 64 lanes each.
 template <class R, int D>
-size_t grad_slot_bytes(int64_t s_max) {
-  return (size_t)(s_max > 0 ? s_max : 1) * (D + 1) * WAVE * sizeof(R);
+size_t grad_slot_bytes(int64_t s_max, int64_t m = 0) {
+  // the tile, then (cotangents at m requested times) the table [m][2][64]
+  return ((size_t)(s_max > 0 ? s_max : 1) * (D + 1) + (size_t)m * 2) * WAVE * sizeof(R);
 }
+
+// Cotangents at requested times (dao_grad_at).
+struct AtArgs {
+  int64_t m;
+  const void* tq;
+  const void* dLdyq;
+  double t0, t1;
+};
 
 size_t grad_header_bytes(int64_t n, int64_t s_max) {
   (void)s_max;
@@ -324,10 +333,10 @@ void launch_order(const int32_t* count, int64_t n, int64_t s_max, uint32_t* hist
 // workspace, run the gradient with the order the workspace holds, or both.
 enum { GRAD_ORDER = 1, GRAD_RUN = 2 };
 
-template <class R, class Sys, int M>
+template <class R, class Sys, int M, bool AT = false>
 dao_status launch_grad(int mode, int64_t n, const void* theta, const void* y0, const dao_record* rec,
                        int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
+                       size_t ws_bytes, hipStream_t stream, const AtArgs* at = nullptr) {
   constexpr int D = Sys::D;
   char* base = (char*)ws;
   unsigned long long* groups = (unsigned long long*)base;
@@ -335,10 +344,10 @@ dao_status launch_grad(int mode, int64_t n, const void* theta, const void* y0, c
   int32_t* perm = (int32_t*)(base + align_up(16) + align_up((size_t)ORDER_BINS * 4));
   const size_t hdr = grad_header_bytes(n, s_max);
   R* scratch = (R*)(base + hdr);
-  const size_t slot = grad_slot_bytes<R, D>(s_max);
+  const size_t slot = grad_slot_bytes<R, D>(s_max, AT ? at->m : 0);
   int64_t slots = (int64_t)((ws_bytes - hdr) / slot);
 
-  auto kern = grad_kernel<R, Sys, M>;
+  auto kern = grad_kernel<R, Sys, M, AT>;
   const int64_t ngroups = (n + WAVE - 1) / WAVE;
   const int64_t waves_per_block = BLOCK / WAVE;
   int64_t blocks = (ngroups + waves_per_block - 1) / waves_per_block;
@@ -367,6 +376,18 @@ dao_status launch_grad(int mode, int64_t n, const void* theta, const void* y0, c
   a.y_rec = (const R*)rec->y;
   a.perm = perm;
   a.groups = groups;
+  a.m = 0;
+  a.tq = nullptr;
+  a.dLdyq = nullptr;
+  a.t0 = a.t1 = R(0);
+  if (AT) {
+    a.m = at->m;
+    a.tq = (const R*)at->tq;
+    a.dLdyq = (const R*)at->dLdyq;
+    a.t0 = R(at->t0);
+    a.t1 = R(at->t1);
+    a.y_rec = nullptr;  // the forward replay assigns the times to steps
+  }
   // the LDS ring through which the forward pass reads the record's h
   const size_t lds = (size_t)BLOCK_WAVES * 16 * WAVE * sizeof(R);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), lds, stream, a);
@@ -580,6 +601,15 @@ struct Entry {
                            void* yq, void* ws, hipStream_t st) {
     return launch_states<R, S<R>, M>(n, th, y0, t0, t1, rec, s_max, m, tq, yq, ws, st);
   }
+  static dao_status grad_at(int64_t n, const void* th, const void* y0, const dao_record* rec,
+                            int64_t s_max, const void* g, void* dth, void* dy0, void* ws,
+                            size_t wsb, hipStream_t st, const AtArgs* at) {
+    return launch_grad<R, S<R>, M, true>(GRAD_ORDER | GRAD_RUN, n, th, y0, rec, s_max, g, dth, dy0,
+                                         ws, wsb, st, at);
+  }
+  static size_t slot_at_bytes(int64_t s_max, int64_t m) {
+    return grad_slot_bytes<R, S<R>::D>(s_max, m);
+  }
   static size_t slot_bytes(int64_t s_max) { return grad_slot_bytes<R, S<R>::D>(s_max); }
   static int64_t resident_waves() {
     return resident_blocks(grad_kernel<R, S<R>, M>) * (BLOCK / WAVE);
@@ -601,6 +631,10 @@ typedef dao_status (*states_fn)(int64_t, const void*, const void*, double, doubl
                                 hipStream_t);
 typedef size_t (*slot_fn)(int64_t);
 typedef int64_t (*res_fn)();
+typedef dao_status (*grad_at_fn)(int64_t, const void*, const void*, const dao_record*, int64_t,
+                                 const void*, void*, void*, void*, size_t, hipStream_t,
+                                 const AtArgs*);
+typedef size_t (*slot_at_fn)(int64_t, int64_t);
 
 struct Impl {
   solve_fn solve;
@@ -612,6 +646,8 @@ struct Impl {
   sens_fn sens;
   states_fn states;  // states at requested times (per-lane systems), else null
   solve_ws_fn solve_ws;  // workspace of dao_solve for n trajectories
+  grad_at_fn grad_at;    // gradient with cotangents at requested times, else null
+  slot_at_fn slot_at;
 };
 
 int64_t mlp_resident_waves() { return resident_blocks(mlp::grad_kernel) * (BLOCK / WAVE); }
@@ -621,7 +657,8 @@ template <class R, template <class> class S, int M>
 Impl make_impl() {
   return Impl{&Entry<R, S, M>::solve, &Entry<R, S, M>::grad, &Entry<R, S, M>::slot_bytes,
               &Entry<R, S, M>::resident_waves, WAVE, &Entry<R, S, M>::solve_sens,
-              &Entry<R, S, M>::sens, &Entry<R, S, M>::states, &Entry<R, S, M>::solve_ws};
+              &Entry<R, S, M>::sens, &Entry<R, S, M>::states, &Entry<R, S, M>::solve_ws,
+              &Entry<R, S, M>::grad_at, &Entry<R, S, M>::slot_at_bytes};
 }
 
 const Impl* find_impl(int sys, int method, int dtype) {
@@ -654,7 +691,7 @@ const Impl* find_impl(int sys, int method, int dtype) {
     table[DAO_SYS_HIRES][M_ROS23][DAO_F32] = make_impl<float, Hires, M_ROS23>();
     table[DAO_SYS_MLP][M_TSIT5][DAO_F32] =
         Impl{&launch_mlp_solve, &launch_mlp_grad, &mlp_slot_bytes, &mlp_resident_waves, mlp::SLOTS,
-             nullptr, nullptr, nullptr, &mlp_solve_ws};
+             nullptr, nullptr, nullptr, &mlp_solve_ws, nullptr, nullptr};
     init = true;
   }
   if (!sys_ok(sys) || method < 0 || method > 1 || dtype < 0 || dtype > 1) return nullptr;
@@ -921,6 +958,55 @@ dao_status dao_grad_ordered(dao_system sys, dao_method method, dao_dtype dtype, 
                             void* workspace, size_t workspace_bytes, void* stream) {
   return grad_call("dao_grad_ordered", GRAD_RUN, sys, method, dtype, n, theta, y0, rec, s_max,
                    dLdy1, dLdtheta, dLdy0, workspace, workspace_bytes, stream);
+}
+
+size_t dao_grad_at_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                                  int64_t s_max, int64_t m) {
+  const Impl* im = find_impl(sys, method, dtype);
+  if (!im || !im->grad_at || n < 0 || s_max < 0 || m < 0) return 0;
+  int64_t waves = (n + WAVE - 1) / WAVE;
+  waves = (waves + BLOCK / WAVE - 1) / (BLOCK / WAVE) * (BLOCK / WAVE);
+  const int64_t res = im->resident();
+  if (waves > res) waves = res;
+  if (waves < BLOCK / WAVE) waves = BLOCK / WAVE;
+  return grad_header_bytes(n, s_max) + (size_t)waves * im->slot_at(s_max, m);
+}
+
+dao_status dao_grad_at(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                       const void* theta, const void* y0, double t0, double t1,
+                       const dao_record* rec, int64_t s_max, int64_t m, const void* tq,
+                       const void* dLdyq, const void* dLdy1, void* dLdtheta, void* dLdy0,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "dao_grad_at";
+  g_err[0] = 0;
+  if (!sys_ok(sys)) return fail(DAO_EINVAL, "%s: unknown system %d", fn, (int)sys);
+  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
+    return fail(DAO_EINVAL, "%s: unknown method %d", fn, (int)method);
+  if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+  if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "%s: n = %lld out of range", fn, (long long)n);
+  if (m < 0 || m > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "%s: m = %lld out of range", fn, (long long)m);
+  if (!is_fin(t0) || !is_fin(t1) || t1 < t0) return fail(DAO_EINVAL, "%s: need finite t0 <= t1", fn);
+  if (!rec) return fail(DAO_EINVAL, "%s: rec is NULL", fn);
+  if (rec->s_cap < 0) return fail(DAO_EINVAL, "%s: rec->s_cap < 0", fn);
+  if (s_max < 0 || s_max > rec->s_cap) return fail(DAO_EINVAL, "%s: s_max must be in [0, rec->s_cap]", fn);
+  const Impl* im = find_impl(sys, method, dtype);
+  if (!im) return fail(DAO_EUNSUPPORTED, "%s: system %d with method %d dtype %d is not provided",
+                       fn, (int)sys, (int)method, (int)dtype);
+  if (!im->grad_at)
+    return fail(DAO_EUNSUPPORTED, "%s: cotangents at requested times are provided for the "
+                "per-trajectory systems, not the neural field", fn);
+  if (n == 0) return DAO_OK;
+  if (!rec->count) return fail(DAO_EINVAL, "%s: rec->count is NULL", fn);
+  if (!theta) return fail(DAO_EINVAL, "%s: theta is NULL", fn);
+  if (!y0) return fail(DAO_EINVAL, "%s: y0 is NULL", fn);
+  if (s_max > 0 && !rec->h) return fail(DAO_EINVAL, "%s: rec->h is NULL", fn);
+  if (m > 0 && (!tq || !dLdyq)) return fail(DAO_EINVAL, "%s: tq or dLdyq is NULL", fn);
+  const size_t need = grad_header_bytes(n, s_max) + (size_t)(BLOCK / WAVE) * im->slot_at(s_max, m);
+  if (!workspace || workspace_bytes < need)
+    return fail(DAO_EWORKSPACE, "%s: workspace needs at least %zu bytes", fn, need);
+  AtArgs at{m, tq, dLdyq, t0, t1};
+  return im->grad_at(n, theta, y0, rec, s_max, dLdy1, dLdtheta, dLdy0, workspace, workspace_bytes,
+                     (hipStream_t)stream, &at);
 }
 
 dao_status dao_sqerr_cotangent(dao_dtype dtype, int64_t n, int d, int d_used, const void* y1,

@@ -78,6 +78,14 @@ struct GradArgs {
   const R* y_rec;  // optional recorded states [n][s_cap][D] (skip the forward replay)
   const int32_t* perm;
   unsigned long long* groups;
+  // Cotangents at requested times (grad_kernel<..., true>): L also holds
+  // sum_q <dLdyq[q], y(tq[q])>, y(tau) the shortened step of the method from
+  // the start of the accepted step that holds tau.  m times tq[m] shared by
+  // the ensemble, ascending in [t0, t1]; dLdyq [m][D][n]; dLdy1 may be null.
+  int64_t m;
+  const R* tq;
+  const R* dLdyq;
+  R t0, t1;
 };
 
 // The attempt's error test: the embedded error is e_c = s a_c (a_c the
@@ -545,7 +553,15 @@ struct RowRing {
   }
 };
 
-template <class R, class Sys, int METHOD>
+// AT: the loss also holds cotangents of the states at requested times
+// (application paper arXiv 2609.28458 Sec. 2.3 fits residuals at observation
+// times; the states are those of states_kernel).  The forward pass assigns
+// each requested time to the step that holds it (per lane: that step's index
+// and the offset tau - t_j, in a table after the wavefront's tile); the
+// reverse sweep, after taking lam through step j, adds for each time held by
+// step j the vector-Jacobian product of the shortened step Phi(y_j; tau - t_j)
+// with that time's cotangent, to lam and the parameter cotangent.
+template <class R, class Sys, int METHOD, bool AT = false>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu((METHOD == M_ROS23 && Sys::D <= 3) ? 4 : 1)))
 grad_kernel(GradArgs<R> a) {
@@ -557,7 +573,21 @@ grad_kernel(GradArgs<R> a) {
   tsit5::Coef<R> C5;
   if constexpr (METHOD == M_TSIT5) C5 = (Sys::D <= 4) ? tsit5::Coef<R>::pinned() : tsit5::Coef<R>::literal();
   const int64_t slot = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
-  R* scr = a.scratch + slot * (a.s_max * (D + 1) * WAVE) + lane;  // tile [s_max][D + 1][64]
+  // per wavefront: the tile [s_max][D + 1][64], then (AT) the table [m][2][64]
+  const int64_t tile = (a.s_max > 0 ? a.s_max : 1) * (D + 1) * WAVE;
+  R* scr = a.scratch + slot * (tile + (AT ? a.m * 2 * WAVE : 0)) + lane;
+  R* const qt = scr + tile;
+  // (AT) the requested times must be ascending in [t0, t1]; otherwise every
+  // output is NaN (the same test for every lane)
+  bool tq_ok = true;
+  if constexpr (AT) {
+    R prev = a.t0;
+    for (int64_t q = 0; q < a.m; ++q) {
+      const R tau = a.tq[q];
+      tq_ok = tq_ok && tau >= a.t0 && tau <= a.t1 && tau >= prev;
+      prev = tau;
+    }
+  }
   const unsigned long long ngroups = (unsigned long long)((a.n + WAVE - 1) / WAVE);
 
   for (;;) {
@@ -602,7 +632,7 @@ grad_kernel(GradArgs<R> a) {
 #pragma unroll
       for (int c = 0; c < D; ++c) {
         y[c] = a.y0[c * a.n + k];
-        lam[c] = a.dLdy1[c * a.n + k];
+        lam[c] = (!AT || a.dLdy1) ? a.dLdy1[c * a.n + k] : R(0);
       }
       hrow = a.h_rec + k * a.s_cap;
     }
@@ -630,8 +660,10 @@ grad_kernel(GradArgs<R> a) {
     // The scratch tile holds, per step, the D state components and the
     // step's h (zero past the lane's count), so that the reverse sweep reads
     // both as whole 512-byte rows instead of h again from 64 record rows.
-    const bool rec_y = a.y_rec != nullptr;
+    const bool rec_y = !AT && a.y_rec != nullptr;
     constexpr int SD = D + 1;
+    int64_t qf = 0;    // (AT) requested times assigned so far
+    R tcur = a.t0;     // (AT) t_j, the solve's running time
     const R* ysrc = rec_y ? a.y_rec + (k >= 0 ? k : 0) * a.s_cap * D : scr;
     const int64_t istr = rec_y ? D : (int64_t)SD * WAVE, cstr = rec_y ? 1 : WAVE;
     R h_nx = (mx > 0) ? hrow[0] : R(0);
@@ -641,6 +673,20 @@ grad_kernel(GradArgs<R> a) {
       const bool rows8 = (a.s_cap % 8) == 0 && ((uintptr_t)a.h_rec % 16) == 0;
       auto fwd = [&](int i, R hv) {
         const R hj = (i < cnt) ? hv : R(0);
+        if constexpr (AT) {
+          if (i < cnt) {
+            // the times step i holds: tau < t_i + h_i, or all that are left at
+            // the last step (it holds up to t1)
+            while (qf < a.m) {
+              const R tau = a.tq[qf];
+              if (!(i == cnt - 1 || tau < tcur + hj)) break;
+              qt[(qf * 2) * WAVE] = R(i);
+              qt[(qf * 2 + 1) * WAVE] = tau - tcur;
+              ++qf;
+            }
+            tcur = tcur + hj;
+          }
+        }
 #pragma unroll
         for (int c = 0; c < D; ++c)
           __builtin_nontemporal_store(y[c], &scr[((int64_t)i * SD + c) * WAVE]);
@@ -702,9 +748,48 @@ grad_kernel(GradArgs<R> a) {
         ros23::stages<R, Sys>(sys, yj, hj, S);
         ros23::sweep<R, Sys>(sys, S, hj, lam, pb);
       }
+      if constexpr (AT) {
+        // the requested times step i holds, latest first; lanes with none
+        // take zero-size steps with zero cotangents (exact no-ops)
+        for (;;) {
+          bool mine = false;
+          R hq = R(0), lq[D];
+#pragma unroll
+          for (int c = 0; c < D; ++c) lq[c] = R(0);
+          if (tq_ok && k >= 0 && i < cnt && qf > 0) {
+            if (qt[((qf - 1) * 2) * WAVE] == R(i)) {
+              mine = true;
+              hq = qt[((qf - 1) * 2 + 1) * WAVE];
+#pragma unroll
+              for (int c = 0; c < D; ++c) lq[c] = a.dLdyq[((qf - 1) * D + c) * a.n + k];
+            }
+          }
+          if (__ballot(mine) == 0ull) break;
+          if constexpr (METHOD == M_TSIT5) {
+            tsit5::Stages<R, D> S;
+            tsit5::stages<R, Sys>(C5, sys, yj, hq, S);
+            tsit5::sweep<R, Sys>(C5, sys, S, hq, lq, pb);
+          } else {
+            ros23::Stages<R, D> S;
+            ros23::stages<R, Sys>(sys, yj, hq, S);
+            ros23::sweep<R, Sys>(sys, S, hq, lq, pb);
+          }
+#pragma unroll
+          for (int c = 0; c < D; ++c) lam[c] += mine ? lq[c] : R(0);
+          qf -= mine ? 1 : 0;
+        }
+      }
+    }
+    if constexpr (AT) {
+      // a trajectory with no steps (t0 = t1): y(tau) = y0 for every time
+      if (tq_ok && k >= 0 && ok && cnt == 0) {
+        for (int64_t q = 0; q < a.m; ++q)
+#pragma unroll
+          for (int c = 0; c < D; ++c) lam[c] += a.dLdyq[(q * D + c) * a.n + k];
+      }
     }
     if (k >= 0) {
-      if (!ok) {
+      if (!ok || !tq_ok) {
 #pragma unroll
         for (int c = 0; c < D; ++c) lam[c] = nanR(R(0));
 #pragma unroll

@@ -207,6 +207,35 @@ dao_status dao_grad_ordered(dao_system sys, dao_method method, dao_dtype dtype, 
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dao_grad_at -- the discrete-adjoint gradient of a loss that also holds the
+ * states at requested times (the application paper, arXiv 2609.28458,
+ * Sec. 2.3, fits residuals at observation times):
+ *   L = sum_q <dLdyq[q], y(tq[q])> + <dLdy1, y(t1)>,
+ * y(tau) exactly as dao_states_at returns it (a shortened step of the method
+ * from the start of the accepted step that holds tau).  The reverse sweep
+ * adds, at each step, the vector-Jacobian products of the shortened steps to
+ * the times that step holds; the recorded h, the running time and each
+ * tau - t_j are constants (sg[h], Sec. 3.1).
+ *   t0, t1   the span of the solve that wrote the record
+ *   m, tq    m requested times (device, real[m]) shared by the ensemble,
+ *            ascending in [t0, t1]; otherwise every output is NaN
+ *   dLdyq    real[m][d][n], the cotangents of the states at tq
+ *   dLdy1    real[d][n] or NULL (no final-state term)
+ *   rec->y   not used (the forward replay assigns the times to steps)
+ *   others   as dao_grad; per-trajectory systems (not DAO_SYS_MLP)
+ * Workspace: dao_grad_at_workspace_size (per resident wavefront the tile
+ * of dao_grad plus a table of m step indices and offsets).
+ * Errors: DAO_EINVAL, DAO_EUNSUPPORTED, DAO_EWORKSPACE, DAO_EDEVICE.
+ */
+size_t dao_grad_at_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                                  int64_t s_max, int64_t m);
+dao_status dao_grad_at(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                       const void* theta, const void* y0, double t0, double t1,
+                       const dao_record* rec, int64_t s_max, int64_t m, const void* tq,
+                       const void* dLdyq, const void* dLdy1, void* dLdtheta, void* dLdy0,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Forward sensitivities of the final state, S = dy1/dtheta (and dy1/dy0):
  * the derivatives the application paper (arXiv 2609.28458, "Differentiable
  * astrophysics at scale") obtains in the same kernel as the solve by

@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dao_solve", "dao_grad", "dao_grad_order", "dao_grad_ordered", "dao_solve_sens",
               "dao_sens", "dao_sens_workspace_size", "dao_states_at", "dao_states_workspace_size",
-              "dao_solve_workspace_size", "dao_grad_workspace_size",
+              "dao_solve_workspace_size", "dao_grad_workspace_size", "dao_grad_at",
+              "dao_grad_at_workspace_size",
               "dao_grad_workspace_min", "dao_system_dims", "dao_sqerr_cotangent",
               "dao_last_error", "dao_version"):
         assert n in names, n

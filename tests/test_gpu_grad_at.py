@@ -1,0 +1,142 @@
+"""GPU parity of the gradient with cotangents at requested times (dao_grad_at,
+through the C ABI) against the oracle's tape gradient of the same loss,
+L = sum_q <dLdyq[q], y(tq[q])> + <dLdy1, y(t1)>, on the oracle's mesh.
+
+Bar: per trajectory, relative 2-norm within 1e-9 (fp64) for dL/dtheta
+(rate constants as log-sensitivities theta * dL/dtheta) and dL/dy0."""
+import numpy as np
+import pytest
+import torch
+
+import dao_inputs as di
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-9
+DEV = "cuda:0"
+LOG_RATES = ("robertson", "hires")
+
+
+@pytest.fixture(scope="module")
+def dao():
+    import differentiable_adaptive_ode_amd as m
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def rel_err(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return np.linalg.norm(a - b, axis=0) / np.maximum(np.linalg.norm(b, axis=0), 1e-300)
+
+
+def import_mesh(w, ref, s_cap):
+    from differentiable_adaptive_ode_amd.api import Record
+
+    h = torch.zeros((w.n, s_cap), dtype=torch.float64, device=DEV)
+    h[:, :ref["h"].shape[1]] = torch.tensor(ref["h"], device=DEV)
+    return Record(w.system, w.method, w.dtype, torch.tensor(w.theta, device=DEV),
+                  torch.tensor(w.y0, device=DEV), w.t0, w.t1, h, None,
+                  torch.tensor(ref["count"], device=DEV), torch.tensor(ref["nrej"], device=DEV),
+                  torch.tensor(ref["status"], device=DEV))
+
+
+def times(w, ref, m):
+    """m requested times: interior points, t0, a step boundary of trajectory 0, t1."""
+    tq = list(np.linspace(w.t0, w.t1, m - 3)[1:-1] + 0.0123 * (w.t1 - w.t0) / m)
+    t = w.t0
+    for i in range(ref["count"][0] // 2):
+        t = t + ref["h"][0, i]
+    return np.array(sorted(tq + [w.t0, t, w.t1]))
+
+
+CASES = [("decay", 300, 256), ("lotka_volterra", 300, 256), ("lorenz63", 300, 1024),
+         ("loghalo", 130, 4096), ("robertson", 200, 2048), ("hires", 130, 4096)]
+
+
+@pytest.mark.parametrize("name,n,s_cap", CASES)
+def test_grad_at_parity(dao, name, n, s_cap):
+    w = di.make(name, n)
+    if name == "loghalo":
+        w.t1 = 10.0
+    print(f"[grad_at parity] {name} n={n}", flush=True)
+    ref = oracle.solve(w.system, w.method, w.theta, w.y0, w.t0, w.t1, w.rtol, w.atol,
+                       s_cap=s_cap, nthreads=8)
+    assert np.all(ref["status"] == 0)
+    tq = times(w, ref, 9)
+    rng = np.random.default_rng(21)
+    cq = rng.normal(size=(len(tq),) + w.y0.shape)
+    c1 = rng.normal(size=w.y0.shape)
+    dth_o, dy0_o = oracle.grad_at(w.system, w.method, w.theta, w.y0, w.t0, w.t1, ref["count"],
+                                  ref["h"], tq, cq, dLdy1=c1, nthreads=8)
+    rec = import_mesh(w, ref, s_cap)
+    dth, dy0 = dao.grad_at(rec, torch.tensor(tq, device=DEV), torch.tensor(cq, device=DEV),
+                           torch.tensor(c1, device=DEV))
+    torch.cuda.synchronize()
+    sc = w.theta if name in LOG_RATES else 1.0
+    e = rel_err(dth.cpu().numpy() * sc, dth_o * sc)
+    assert e.max() <= TOL, e.max()
+    e0 = rel_err(dy0.cpu().numpy(), dy0_o)
+    assert e0.max() <= TOL, e0.max()
+    # without the final-state term, and at a moved theta
+    th2 = w.theta * 1.002
+    dth_o2, dy0_o2 = oracle.grad_at(w.system, w.method, th2, w.y0, w.t0, w.t1, ref["count"],
+                                    ref["h"], tq, cq, nthreads=8)
+    dth2, dy02 = dao.grad_at(rec, torch.tensor(tq, device=DEV), torch.tensor(cq, device=DEV),
+                             theta=torch.tensor(th2, device=DEV))
+    torch.cuda.synchronize()
+    assert rel_err(dth2.cpu().numpy() * sc, dth_o2 * sc).max() <= TOL
+    assert rel_err(dy02.cpu().numpy(), dy0_o2).max() <= TOL
+
+
+def test_final_time_alone_matches_grad(dao):
+    w = di.make("lorenz63", 300)
+    th = torch.tensor(w.theta, device=DEV)
+    y0 = torch.tensor(w.y0, device=DEV)
+    rec, y1 = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=1024)
+    lam = torch.tensor(np.random.default_rng(3).normal(size=w.y0.shape), device=DEV)
+    g_th, g_y0 = dao.grad(rec, lam)
+    a_th, a_y0 = dao.grad_at(rec, torch.tensor([w.t1], dtype=torch.float64, device=DEV), lam[None])
+    b_th, b_y0 = dao.grad_at(rec, torch.zeros(0, dtype=torch.float64, device=DEV),
+                             torch.zeros((0, 3, w.n), dtype=torch.float64, device=DEV), lam)
+    torch.cuda.synchronize()
+    assert rel_err(a_th.cpu(), g_th.cpu()).max() <= 1e-12
+    assert rel_err(a_y0.cpu(), g_y0.cpu()).max() <= 1e-12
+    # no requested times: the plain gradient, bit for bit
+    assert torch.equal(b_th, g_th) and torch.equal(b_y0, g_y0)
+
+
+def test_grad_at_bad_times_and_unsupported(dao):
+    w = di.make("lorenz63", 70)
+    th = torch.tensor(w.theta, device=DEV)
+    y0 = torch.tensor(w.y0, device=DEV)
+    rec, _ = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=1024)
+    for tq in ([0.5, 0.2], [w.t1 + 0.1], [float("nan")]):
+        t = torch.tensor(tq, dtype=torch.float64, device=DEV)
+        cq = torch.ones((len(tq), 3, w.n), dtype=torch.float64, device=DEV)
+        dth, dy0 = dao.grad_at(rec, t, cq)
+        torch.cuda.synchronize()
+        assert torch.isnan(dth).all() and torch.isnan(dy0).all()
+    m = di.make("mlp", 32)
+    thm = torch.tensor(m.theta, device=DEV)
+    y0m = torch.tensor(m.y0, device=DEV)
+    recm, _ = dao.solve(m.system, m.method, thm, y0m, m.t0, m.t1, m.rtol, m.atol, s_cap=64)
+    with pytest.raises(dao.DaoError, match="neural field"):
+        dao.grad_at(recm, torch.tensor([0.5], device=DEV),
+                    torch.zeros((1, 4, 32), dtype=torch.float32, device=DEV))
+
+
+def test_grad_at_zero_span(dao):
+    # t0 = t1: no steps; every requested time (= t0) holds y0, so dL/dy0 is the
+    # sum of the cotangents and dL/dtheta is zero
+    w = di.make("lorenz63", 70)
+    th = torch.tensor(w.theta, device=DEV)
+    y0 = torch.tensor(w.y0, device=DEV)
+    rec, _ = dao.solve(w.system, w.method, th, y0, 0.0, 0.0, w.rtol, w.atol, s_cap=64)
+    cq = torch.tensor(np.random.default_rng(8).normal(size=(2, 3, w.n)), device=DEV)
+    dth, dy0 = dao.grad_at(rec, torch.zeros(2, dtype=torch.float64, device=DEV), cq)
+    torch.cuda.synchronize()
+    assert torch.equal(dth, torch.zeros_like(dth))
+    assert torch.allclose(dy0, cq.sum(0), rtol=0, atol=0)
