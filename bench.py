@@ -109,12 +109,14 @@ def parse():
                          "Lotka-Volterra system at n = 1048576, where its 256-trajectory "
                          "ensemble cannot fill the chip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("gradient", "sens", "replay_sens", "states"),
+    ap.add_argument("--mode", choices=("gradient", "sens", "replay_sens", "states", "grad_at"),
                     default="gradient",
                     help="gradient: solve with record + replay-adjoint gradient (default); "
                          "sens: solve with the forward sensitivities dy1/dtheta in the same "
                          "kernel; replay_sens: dy1/dtheta by forward mode through the replay "
-                         "of a record; states: the states at 16 requested times on a record")
+                         "of a record; states: the states at 16 requested times on a record; "
+                         "grad_at: the gradient of a loss on the states at 16 requested times "
+                         "and at t1, on a record")
     ap.add_argument("--states", action="store_true",
                     help="record states in the solve; the gradient skips the forward replay")
     ap.add_argument("--record-t", type=int, choices=(0, 1), default=None,
@@ -203,7 +205,7 @@ def main():
         raise SystemExit(f"bench: no forward-sensitivity benchmark for {w.name}")
     if args.mode == "sens":
         return bench_sens(args, w)
-    if args.mode in ("replay_sens", "states"):
+    if args.mode in ("replay_sens", "states", "grad_at"):
         return bench_on_record(args, w)
     cfg = WORKLOADS[w.name]
     s_cap = cfg["s_cap"]
@@ -472,6 +474,14 @@ def cpu_baseline_on_record(w, sample, s_cap, mode):
         oracle.sens(ws.system, ws.method, ws.theta, ws.y0, r["count"], r["h"], with_y0=False,
                     nthreads=nthreads)
         what = "dual-number forward sensitivities through the replay of its mesh"
+    elif mode == "grad_at":
+        tq = np.linspace(ws.t0, ws.t1, STATES_M)
+        rng = np.random.default_rng(0)
+        cq = rng.normal(size=(STATES_M,) + ws.y0.shape)
+        oracle.grad_at(ws.system, ws.method, ws.theta, ws.y0, ws.t0, ws.t1, r["count"], r["h"],
+                       tq, cq, dLdy1=rng.normal(size=ws.y0.shape), nthreads=nthreads)
+        what = (f"tape gradient of a loss on the states at {STATES_M} requested times and t1, "
+                "on its mesh")
     else:
         tq = np.linspace(ws.t0, ws.t1, STATES_M)
         oracle.states_at(ws.system, ws.method, ws.theta, ws.y0, ws.t0, ws.t1, r["count"], r["h"],
@@ -514,11 +524,18 @@ def bench_on_record(args, w):
     steps_total = int(cnt.sum())
     tq = torch.linspace(w.t0, w.t1, STATES_M, dtype=y0.dtype, device=dev)
     yq = torch.empty((STATES_M, w.d, w.n), dtype=y0.dtype, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    cq = torch.randn((STATES_M, w.d, w.n), dtype=y0.dtype, device=dev, generator=gen)
+    c1 = torch.randn((w.d, w.n), dtype=y0.dtype, device=dev, generator=gen)
+    dth = torch.empty_like(th)
+    dy0 = torch.empty_like(y0)
 
     def run(ev):
         ev[0].record()
         if args.mode == "replay_sens":
             dao.sens(rec, s_max=s_max, workspace=wsp)
+        elif args.mode == "grad_at":
+            dao.grad_at(rec, tq, cq, c1, s_max=s_max, out_theta=dth, out_y0=dy0, workspace=wsp)
         else:
             dao.states_at(rec, tq, s_max=s_max, out=yq, workspace=wsp)
         ev[1].record()
@@ -543,6 +560,14 @@ def bench_on_record(args, w):
         fl = steps_total * (cfg["replay"] + _sens_step_flops(w.d, p, w.name, w.method))
         kern, label, tag = "sens_kernel", "forward sensitivities through the replay", "rsens"
         metric = "replay forward-mode sensitivity trajectories/s (dy1/dtheta on a record) at 1 GPU"
+    elif args.mode == "grad_at":
+        # the gradient of every accepted step, plus per requested time the
+        # reverse of its shortened step (stages and sweep: a gradient step
+        # without its forward replay); the sort of the record is part of the call
+        fl = steps_total * cfg["grad"] + w.n * STATES_M * (cfg["grad"] - cfg["replay"])
+        kern, label, tag = "grad_kernel", f"gradient with cotangents at {STATES_M} times", "gat"
+        metric = (f"gradient trajectories/s for a loss on the states at {STATES_M} requested "
+                  "times and t1, on a record, 1 GPU")
     else:
         # every lane takes count + m steps of the method (recorded or shortened),
         # each a replay step plus its time update
@@ -564,7 +589,7 @@ def bench_on_record(args, w):
         "config": {"workload": f"{w.name} ensemble, {label}", "n_trajectories": w.n,
                    "method": w.method, "t_span": [w.t0, w.t1], "rtol": w.rtol, "atol": w.atol,
                    "s_cap": s_cap, "directions": p if args.mode == "replay_sens" else None,
-                   "requested_times": STATES_M if args.mode == "states" else None},
+                   "requested_times": STATES_M if args.mode in ("states", "grad_at") else None},
         "call_ms": tk * 1e3, "accepted_steps_mean": float(cnt.mean()),
         "roofline": {"bound": cfg["bound"], "kernel": kern, "launch_ms": tk * 1e3,
                      "achieved": ach * 1e-12, "peak": cfg["peak"] * 1e-12, "unit": "TFLOP/s",

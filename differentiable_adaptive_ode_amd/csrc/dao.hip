@@ -295,8 +295,9 @@ dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0,
 // components and h, 64 lanes each.
 template <class R, int D>
 size_t grad_slot_bytes(int64_t s_max, int64_t m = 0) {
-  // the tile, then (cotangents at m requested times) the table [m][2][64]
-  return ((size_t)(s_max > 0 ? s_max : 1) * (D + 1) + (size_t)m * 2) * WAVE * sizeof(R);
+  // the tile, then (cotangents at m requested times) the tables [m][2][64]
+  // and [m][D][64]
+  return ((size_t)(s_max > 0 ? s_max : 1) * (D + 1) + (size_t)m * (2 + D)) * WAVE * sizeof(R);
 }
 
 // Cotangents at requested times (dao_grad_at).

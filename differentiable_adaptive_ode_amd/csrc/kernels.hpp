@@ -557,10 +557,11 @@ struct RowRing {
 // (application paper arXiv 2609.28458 Sec. 2.3 fits residuals at observation
 // times; the states are those of states_kernel).  The forward pass assigns
 // each requested time to the step that holds it (per lane: that step's index
-// and the offset tau - t_j, in a table after the wavefront's tile); the
-// reverse sweep, after taking lam through step j, adds for each time held by
-// step j the vector-Jacobian product of the shortened step Phi(y_j; tau - t_j)
-// with that time's cotangent, to lam and the parameter cotangent.
+// and the offset tau - t_j, in a table after the wavefront's tile); before
+// the reverse sweep every lane takes the vector-Jacobian product of the
+// shortened step Phi(y_J; tau - t_J) with each time's cotangent (time by
+// time, all lanes together), and the sweep adds it to lam once it has taken
+// lam through step J.
 template <class R, class Sys, int METHOD, bool AT = false>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu((METHOD == M_ROS23 && Sys::D <= 3) ? 4 : 1)))
@@ -573,9 +574,10 @@ grad_kernel(GradArgs<R> a) {
   tsit5::Coef<R> C5;
   if constexpr (METHOD == M_TSIT5) C5 = (Sys::D <= 4) ? tsit5::Coef<R>::pinned() : tsit5::Coef<R>::literal();
   const int64_t slot = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
-  // per wavefront: the tile [s_max][D + 1][64], then (AT) the table [m][2][64]
+  // per wavefront: the tile [s_max][D + 1][64], then (AT) the tables
+  // [m][2][64] (step index and offset of each time) and [m][D][64] (its VJP)
   const int64_t tile = (a.s_max > 0 ? a.s_max : 1) * (D + 1) * WAVE;
-  R* scr = a.scratch + slot * (tile + (AT ? a.m * 2 * WAVE : 0)) + lane;
+  R* scr = a.scratch + slot * (tile + (AT ? a.m * (2 + D) * WAVE : 0)) + lane;
   R* const qt = scr + tile;
   // (AT) the requested times must be ascending in [t0, t1]; otherwise every
   // output is NaN (the same test for every lane)
@@ -664,6 +666,10 @@ grad_kernel(GradArgs<R> a) {
     constexpr int SD = D + 1;
     int64_t qf = 0;    // (AT) requested times assigned so far
     R tcur = a.t0;     // (AT) t_j, the solve's running time
+    R tnext = R(0);    // (AT) the next time to assign, kept in a register
+    if constexpr (AT) {
+      if (a.m > 0) tnext = a.tq[0];
+    }
     const R* ysrc = rec_y ? a.y_rec + (k >= 0 ? k : 0) * a.s_cap * D : scr;
     const int64_t istr = rec_y ? D : (int64_t)SD * WAVE, cstr = rec_y ? 1 : WAVE;
     R h_nx = (mx > 0) ? hrow[0] : R(0);
@@ -678,11 +684,11 @@ grad_kernel(GradArgs<R> a) {
             // the times step i holds: tau < t_i + h_i, or all that are left at
             // the last step (it holds up to t1)
             while (qf < a.m) {
-              const R tau = a.tq[qf];
-              if (!(i == cnt - 1 || tau < tcur + hj)) break;
+              if (!(i == cnt - 1 || tnext < tcur + hj)) break;
               qt[(qf * 2) * WAVE] = R(i);
-              qt[(qf * 2 + 1) * WAVE] = tau - tcur;
+              qt[(qf * 2 + 1) * WAVE] = tnext - tcur;
               ++qf;
+              if (qf < a.m) tnext = a.tq[qf];
             }
             tcur = tcur + hj;
           }
@@ -709,74 +715,93 @@ grad_kernel(GradArgs<R> a) {
         }
       }
     }
-    // Reverse sweep, with y_j and h_j of the next step (j - 1) prefetched the
-    // same way.  Past a lane's count the state is taken as zero (recorded rows
-    // there are unspecified), which keeps the zero-size steps exact no-ops.
-    // (Recomputing step j - 1's stages during step j's sweep, for two
-    // independent chains per iteration, measured no faster on any workload.)
-    R y_nx[D];
+    // (AT) Phase A: the reverse of the shortened step to every requested
+    // time, v_q = (d Phi(y_J; tau_q - t_J) / d y_J)^T dLdyq[q] with its
+    // parameter part added to pb.  None of it depends on lam, so all lanes
+    // take time q together (one unit each per iteration, whatever step holds
+    // it); the reverse sweep below adds v_q to lam_J once step J is done.
+    R* const vt = qt + a.m * 2 * WAVE;  // table [m][D][64]
+    int64_t qp = qf;                     // times whose v_q is not yet added
+    R nextJ = R(-1);                     // the step holding time qp - 1
+    if constexpr (AT) {
+      for (int64_t q = 0; q < a.m; ++q) {
+        const bool has = q < qf;  // assigned (lanes with steps have all m)
+        R hq = R(0), yq[D], lq[D];
 #pragma unroll
-    for (int c = 0; c < D; ++c) y_nx[c] = R(0);
-    h_nx = R(0);
-    // h of row i: from the tile (zero past the count already), or the record
-    auto h_at = [&](int i) -> R {
-      return rec_y ? hrow[i] : __builtin_nontemporal_load(&scr[((int64_t)i * SD + D) * WAVE]);
-    };
-    if (mx > 0) {
+        for (int c = 0; c < D; ++c) yq[c] = lq[c] = R(0);
+        if (has) {
+          const int64_t J = (int64_t)qt[(q * 2) * WAVE];
+          hq = qt[(q * 2 + 1) * WAVE];
 #pragma unroll
-      for (int c = 0; c < D; ++c)
-        y_nx[c] = __builtin_nontemporal_load(&ysrc[(int64_t)(mx - 1) * istr + c * cstr]);
-      h_nx = h_at(mx - 1);
+          for (int c = 0; c < D; ++c) {
+            yq[c] = __builtin_nontemporal_load(&scr[(J * SD + c) * WAVE]);
+            lq[c] = a.dLdyq[(q * D + c) * a.n + k];
+          }
+        }
+        if constexpr (METHOD == M_TSIT5) {
+          tsit5::Stages<R, D> S;
+          tsit5::stages<R, Sys>(C5, sys, yq, hq, S);
+          tsit5::sweep<R, Sys>(C5, sys, S, hq, lq, pb);
+        } else {
+          ros23::Stages<R, D> S;
+          ros23::stages<R, Sys>(sys, yq, hq, S);
+          ros23::sweep<R, Sys>(sys, S, hq, lq, pb);
+        }
+        if (has) {
+#pragma unroll
+          for (int c = 0; c < D; ++c) vt[(q * D + c) * WAVE] = lq[c];
+        }
+      }
+      if (qp > 0) nextJ = qt[((qp - 1) * 2) * WAVE];
     }
-    for (int i = mx - 1; i >= 0; --i) {
-      R yj[D];
-      const R hj = (i < cnt) ? h_nx : R(0);
+    {
+      // Reverse sweep, with y_j and h_j of the next step (j - 1) prefetched the
+      // same way.  Past a lane's count the state is taken as zero (recorded rows
+      // there are unspecified), which keeps the zero-size steps exact no-ops.
+      // (Recomputing step j - 1's stages during step j's sweep, for two
+      // independent chains per iteration, measured no faster on any workload.)
+      R y_nx[D];
 #pragma unroll
-      for (int c = 0; c < D; ++c) yj[c] = (i < cnt) ? y_nx[c] : R(0);
-      if (i >= 1) {
+      for (int c = 0; c < D; ++c) y_nx[c] = R(0);
+      h_nx = R(0);
+      // h of row i: from the tile (zero past the count already), or the record
+      auto h_at = [&](int i) -> R {
+        return rec_y ? hrow[i] : __builtin_nontemporal_load(&scr[((int64_t)i * SD + D) * WAVE]);
+      };
+      if (mx > 0) {
 #pragma unroll
         for (int c = 0; c < D; ++c)
-          y_nx[c] = __builtin_nontemporal_load(&ysrc[(int64_t)(i - 1) * istr + c * cstr]);
-        h_nx = h_at(i - 1);
+          y_nx[c] = __builtin_nontemporal_load(&ysrc[(int64_t)(mx - 1) * istr + c * cstr]);
+        h_nx = h_at(mx - 1);
       }
-      if constexpr (METHOD == M_TSIT5) {
-        tsit5::Stages<R, D> S;
-        tsit5::stages<R, Sys>(C5, sys, yj, hj, S);
-        tsit5::sweep<R, Sys>(C5, sys, S, hj, lam, pb);
-      } else {
-        ros23::Stages<R, D> S;
-        ros23::stages<R, Sys>(sys, yj, hj, S);
-        ros23::sweep<R, Sys>(sys, S, hj, lam, pb);
-      }
-      if constexpr (AT) {
-        // the requested times step i holds, latest first; lanes with none
-        // take zero-size steps with zero cotangents (exact no-ops)
-        for (;;) {
-          bool mine = false;
-          R hq = R(0), lq[D];
+      for (int i = mx - 1; i >= 0; --i) {
+        R yj[D];
+        const R hj = (i < cnt) ? h_nx : R(0);
 #pragma unroll
-          for (int c = 0; c < D; ++c) lq[c] = R(0);
-          if (tq_ok && k >= 0 && i < cnt && qf > 0) {
-            if (qt[((qf - 1) * 2) * WAVE] == R(i)) {
-              mine = true;
-              hq = qt[((qf - 1) * 2 + 1) * WAVE];
+        for (int c = 0; c < D; ++c) yj[c] = (i < cnt) ? y_nx[c] : R(0);
+        if (i >= 1) {
 #pragma unroll
-              for (int c = 0; c < D; ++c) lq[c] = a.dLdyq[((qf - 1) * D + c) * a.n + k];
-            }
+          for (int c = 0; c < D; ++c)
+            y_nx[c] = __builtin_nontemporal_load(&ysrc[(int64_t)(i - 1) * istr + c * cstr]);
+          h_nx = h_at(i - 1);
+        }
+        if constexpr (METHOD == M_TSIT5) {
+          tsit5::Stages<R, D> S;
+          tsit5::stages<R, Sys>(C5, sys, yj, hj, S);
+          tsit5::sweep<R, Sys>(C5, sys, S, hj, lam, pb);
+        } else {
+          ros23::Stages<R, D> S;
+          ros23::stages<R, Sys>(sys, yj, hj, S);
+          ros23::sweep<R, Sys>(sys, S, hj, lam, pb);
+        }
+        if constexpr (AT) {
+          // lam_i gains v_q of every time step i holds
+          while (qp > 0 && nextJ == R(i)) {
+#pragma unroll
+            for (int c = 0; c < D; ++c) lam[c] += vt[((qp - 1) * D + c) * WAVE];
+            --qp;
+            nextJ = (qp > 0) ? qt[((qp - 1) * 2) * WAVE] : R(-1);
           }
-          if (__ballot(mine) == 0ull) break;
-          if constexpr (METHOD == M_TSIT5) {
-            tsit5::Stages<R, D> S;
-            tsit5::stages<R, Sys>(C5, sys, yj, hq, S);
-            tsit5::sweep<R, Sys>(C5, sys, S, hq, lq, pb);
-          } else {
-            ros23::Stages<R, D> S;
-            ros23::stages<R, Sys>(sys, yj, hq, S);
-            ros23::sweep<R, Sys>(sys, S, hq, lq, pb);
-          }
-#pragma unroll
-          for (int c = 0; c < D; ++c) lam[c] += mine ? lq[c] : R(0);
-          qf -= mine ? 1 : 0;
         }
       }
     }
