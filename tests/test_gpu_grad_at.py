@@ -140,3 +140,58 @@ def test_grad_at_zero_span(dao):
     torch.cuda.synchronize()
     assert torch.equal(dth, torch.zeros_like(dth))
     assert torch.allclose(dy0, cq.sum(0), rtol=0, atol=0)
+
+
+def test_grad_at_full_size_sampled(dao):
+    # The Lorenz ensemble at full size (65,536 trajectories) with 16 requested
+    # times, in the benchmark's launch configuration; a seeded sample (plus the
+    # longest and shortest records) against the oracle on the GPU's own mesh.
+    w = di.make("lorenz63")
+    print(f"[grad_at full size] lorenz63 n={w.n}", flush=True)
+    th = torch.tensor(w.theta, device=DEV)
+    y0 = torch.tensor(w.y0, device=DEV)
+    rec, _ = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=1024)
+    tq = torch.linspace(w.t0, w.t1, 16, dtype=torch.float64, device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    cq = torch.randn((16, 3, w.n), dtype=torch.float64, device=DEV, generator=gen)
+    c1 = torch.randn((3, w.n), dtype=torch.float64, device=DEV, generator=gen)
+    dth, dy0 = dao.grad_at(rec, tq, cq, c1)
+    torch.cuda.synchronize()
+    cnt = rec.count.cpu().numpy()
+    assert np.all(rec.status.cpu().numpy() == 0)
+    rng = np.random.default_rng(2)
+    idx = np.unique(np.concatenate([rng.choice(w.n, 64, replace=False), [0, w.n - 1],
+                                    [np.argmax(cnt), np.argmin(cnt)]]))
+    ws = di.subset(w, idx)
+    h = rec.h.cpu().numpy()[idx]
+    mask = np.arange(h.shape[1])[None, :] < cnt[idx][:, None]
+    h = np.where(mask, h, 0.0)
+    dth_o, dy0_o = oracle.grad_at(ws.system, ws.method, ws.theta, ws.y0, w.t0, w.t1, cnt[idx], h,
+                                  tq.cpu().numpy(), cq.cpu().numpy()[:, :, idx],
+                                  dLdy1=c1.cpu().numpy()[:, idx], nthreads=8)
+    assert rel_err(dth.cpu().numpy()[:, idx], dth_o).max() <= TOL
+    assert rel_err(dy0.cpu().numpy()[:, idx], dy0_o).max() <= TOL
+
+
+def test_grad_at_single_precision(dao):
+    # binary32 on the GPU's own binary32 mesh against the binary64 oracle on
+    # that mesh (the gradient's single-precision bar, 1e-3)
+    w = di.make("lorenz63", 200)
+    w.t1 = 0.5
+    th = torch.tensor(w.theta, dtype=torch.float32, device=DEV)
+    y0 = torch.tensor(w.y0, dtype=torch.float32, device=DEV)
+    rec, _ = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, 1e-5, 1e-7, s_cap=1024)
+    tq = torch.tensor([0.1, 0.25, 0.4, 0.5], dtype=torch.float32, device=DEV)
+    rng = np.random.default_rng(12)
+    cq = rng.normal(size=(4, 3, w.n))
+    dth, dy0 = dao.grad_at(rec, tq, torch.tensor(cq, dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    cnt = rec.count.cpu().numpy()
+    assert np.all(rec.status.cpu().numpy() == 0)
+    h = rec.h.cpu().numpy().astype(np.float64)
+    h = np.where(np.arange(h.shape[1])[None, :] < cnt[:, None], h, 0.0)
+    dth_o, dy0_o = oracle.grad_at(w.system, w.method, th.cpu().numpy().astype(np.float64),
+                                  y0.cpu().numpy().astype(np.float64), w.t0, w.t1, cnt, h,
+                                  tq.cpu().numpy().astype(np.float64), cq, nthreads=8)
+    assert rel_err(dth.cpu().numpy(), dth_o).max() <= 1e-3
+    assert rel_err(dy0.cpu().numpy(), dy0_o).max() <= 1e-3
