@@ -129,6 +129,24 @@ def parse():
     return ap.parse_args()
 
 
+def _issued(tr, kern, fl_alg, f64):
+    """Issued floating-point work of one call of `kern` (its one or two
+    launches) from the profile's instruction counters, when they were taken on
+    the current kernel sources and ensemble size, and the vector units'
+    utilisation = algorithmic flops / issued flops (padding steps and masked
+    lanes are issued but are no work of the method)."""
+    if tr is None:
+        return None
+    for key in (kern, kern.replace("_kernel", "_phased_kernel")):
+        iss = tr["kernels"].get(key, {}).get("issued")
+        if iss:
+            tot = (iss["fp64_lane_flops"] if f64
+                   else iss["mfma_f32_flops"] + (iss.get("counter_flops_fp32") or 0.0))
+            if tot > 0:
+                return {"issued_flops": tot, "utilisation": fl_alg / tot}
+    return None
+
+
 def _divergence(cnt, nrej, attempts, steps_total, t_solve, t_grad):
     import numpy as np
 
@@ -338,6 +356,9 @@ def main():
                      "traffic_unit": "HBM bytes per call (two launches for a two-phase solve)"},
         "roofline_solve_frac": fl_solve / ts / peak,
         "roofline_grad_frac": fl_grad / tk / peak,
+        # issued vs algorithmic flops per call (profile counters), or null
+        "issue": {"solve": _issued(tr, "solve_kernel", fl_solve, w.dtype == "f64"),
+                  "grad": _issued(tr, "grad_kernel", fl_grad, w.dtype == "f64")},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample or cfg["cpu_n"], s_cap)
@@ -447,6 +468,7 @@ def bench_sens(args, w):
                      "launch_ms": tk * 1e3, "achieved": ach * 1e-12, "peak": cfg["peak"] * 1e-12,
                      "unit": "TFLOP/s", "frac": ach / cfg["peak"], "traffic": traffic,
                      "traffic_unit": "HBM bytes per call (two launches for a two-phase solve)"},
+        "issue": _issued(tr, "solve_sens_kernel", fl_solve + fl_sens, w.dtype == "f64"),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_sens(w, args.cpu_sample or min(cfg["cpu_n"], 4096),
@@ -595,6 +617,7 @@ def bench_on_record(args, w):
                      "achieved": ach * 1e-12, "peak": cfg["peak"] * 1e-12, "unit": "TFLOP/s",
                      "frac": ach / cfg["peak"], "traffic": traffic,
                      "traffic_unit": "HBM bytes per call"},
+        "issue": _issued(tr, kern, fl, w.dtype == "f64"),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_on_record(

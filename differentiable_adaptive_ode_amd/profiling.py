@@ -146,6 +146,33 @@ def summarize(args) -> None:
     with open(traffic_path(args.workload, args.out), "w") as f:
         json.dump(traffic, f, indent=1)
 
+    # Issued floating-point work per call (instruction counters): FP64 lane-flops
+    # as 64 x (add + mul + 2 fma + transcendental) wave-instructions, the
+    # counter's own FP64 and FP32 flop counts, and MFMA FP32 flops (ops / 512).
+    # Against the algorithmic flops of the same call this is the vector units'
+    # utilisation under divergence: masked-off lanes and zero-size padding
+    # steps are issued but are not work of the method.
+    fl = None
+    if getattr(args, "flops", None):
+        fl, _ = read_counters(args.flops)
+        for key, t in traffic["kernels"].items():
+            def cnt(c):
+                xs = [v for (name, cc), vv in fl.items() if cc == c and _short(name) == key for v in vv]
+                per = 2.0 if "phased" in key else 1.0
+                return per * sum(xs) / len(xs) if xs else None
+            add, mul, fma, trans = (cnt("SQ_INSTS_VALU_ADD_F64"), cnt("SQ_INSTS_VALU_MUL_F64"),
+                                    cnt("SQ_INSTS_VALU_FMA_F64"), cnt("SQ_INSTS_VALU_TRANS_F64"))
+            if None in (add, mul, fma, trans):
+                continue
+            mops = cnt("SQ_INSTS_VALU_MFMA_MOPS_F32") or 0.0
+            t["issued"] = {"fp64_lane_flops": 64.0 * (add + mul + 2.0 * fma + trans),
+                           "fp64_add": add, "fp64_mul": mul, "fp64_fma": fma, "fp64_trans": trans,
+                           "counter_flops_fp64": cnt("SQ_INSTS_VALU_FLOPS_FP64"),
+                           "counter_flops_fp32": cnt("SQ_INSTS_VALU_FLOPS_FP32"),
+                           "mfma_f32_flops": 512.0 * mops}
+        with open(traffic_path(args.workload, args.out), "w") as f:
+            json.dump(traffic, f, indent=1)
+
     sq = None
     if args.sq:
         sq, _ = read_counters(args.sq)
@@ -176,6 +203,22 @@ def summarize(args) -> None:
                 xs = [v for (name, cc), vv in sq.items() if cc == c and _short(name) == key for v in vv]
                 row.append(f"{sum(xs) / len(xs):.4g}" if xs else "-")
             lines.append(f"| {key} | " + " | ".join(row) + " |")
+    if fl:
+        lines += ["", "Issued floating-point work per call (instruction counters; FP64 lane-flops = "
+                  "64 x (add + mul + 2 fma + transcendental) wave-instructions):", "",
+                  "    " + args.cmd_flops, "",
+                  "| kernel | FP64 add | FP64 mul | FP64 fma | FP64 trans | FP64 lane-flops | "
+                  "SQ_INSTS_VALU_FLOPS_FP64 | SQ_INSTS_VALU_FLOPS_FP32 | MFMA FP32 flops |",
+                  "|---|---|---|---|---|---|---|---|---|"]
+        for key, t in traffic["kernels"].items():
+            iss = t.get("issued")
+            if not iss:
+                continue
+            g = lambda v: "-" if v is None else f"{v:.4g}"  # noqa: E731
+            lines.append(f"| {key} | {g(iss['fp64_add'])} | {g(iss['fp64_mul'])} | "
+                         f"{g(iss['fp64_fma'])} | {g(iss['fp64_trans'])} | "
+                         f"{g(iss['fp64_lane_flops'])} | {g(iss['counter_flops_fp64'])} | "
+                         f"{g(iss['counter_flops_fp32'])} | {g(iss['mfma_f32_flops'])} |")
     lines += ["", f"Kernel sources sha256: `{traffic['kernel_source_sha256']}`", ""]
     path = os.path.join(args.out, f"{args.workload}_n{args.n}_kernels.md")
     with open(path, "w") as f:
@@ -198,6 +241,8 @@ def main(argv=None):
     s.add_argument("--cmd-fetch", default="")
     s.add_argument("--cmd-write", default="")
     s.add_argument("--cmd-sq", default="")
+    s.add_argument("--flops", default=None)
+    s.add_argument("--cmd-flops", default="")
     s.add_argument("--out", default=os.path.join(os.path.dirname(HERE), "profiles"))
     a = ap.parse_args(argv)
     if a.cmd == "summarize":
