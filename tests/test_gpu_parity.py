@@ -562,3 +562,58 @@ def test_two_phase_solve_with_sensitivities_equals_one_phase(dao, name, n, s_cap
     cnt = r1.count.cpu().numpy()
     mask = torch.tensor(np.arange(s_cap)[None, :] < cnt[:, None], device=DEV)
     assert torch.equal(r1.h[mask], r2.h[mask]) and torch.equal(r1.t[mask], r2.t[mask])
+
+
+def test_hires_with_tsit5(dao):
+    # The explicit pair on the stiff eight-species field over a short span:
+    # the mesh bit for bit, y1 and the gradient on the oracle's mesh (1e-9).
+    w = di.make("hires", 130)
+    w.method, w.t1 = "tsit5", 5.0
+    print(f"[hires tsit5] n={w.n}", flush=True)
+    ref = oracle_solve(w, 1024)
+    rec, y1 = gpu_solve(dao, w, 1024)
+    assert np.array_equal(rec.status.cpu().numpy(), ref["status"])
+    assert np.array_equal(rec.count.cpu().numpy(), ref["count"])
+    assert rel_err(y1.cpu().numpy(), ref["y1"]).max() <= TOL
+    lam = di.cotangent(w, ref["y1"])
+    dth_o, dy0_o, _ = oracle.grad(w.system, w.method, w.theta, w.y0, ref["count"], ref["h"], lam,
+                                  nthreads=8)
+    dth, dy0 = dao.grad(import_mesh(dao, w, ref, 1024), torch.tensor(lam, device=DEV))
+    torch.cuda.synchronize()
+    assert rel_err(dth.cpu().numpy() * w.theta, dth_o * w.theta).max() <= TOL
+    assert rel_err(dy0.cpu().numpy(), dy0_o).max() <= TOL
+
+
+def test_hires_single_precision(dao):
+    # Rosenbrock23 in binary32 on HIRES against the oracle's binary32
+    # instantiation (the same arithmetic): accepted-step counts within one,
+    # and where they agree y1 within 1e-5; the gradient on the GPU's own mesh
+    # within 1e-3 of the binary64 oracle on that mesh.  (y1 itself differs
+    # from a binary64 replay of the mesh by up to ~1e-4 after a hundred
+    # binary32 stiff steps; that is the precision, not the kernel.)
+    w = di.make("hires", 130)
+    w.rtol, w.atol = 1e-4, 1e-6
+    th = torch.tensor(w.theta, dtype=torch.float32, device=DEV)
+    y0 = torch.tensor(w.y0, dtype=torch.float32, device=DEV)
+    rec, y1 = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=1024)
+    torch.cuda.synchronize()
+    assert np.all(rec.status.cpu().numpy() == 0)
+    ref32 = oracle.solve(w.system, w.method, w.theta.astype(np.float32), w.y0.astype(np.float32),
+                         w.t0, w.t1, w.rtol, w.atol, s_cap=1024, dtype="f32", nthreads=8)
+    cnt = rec.count.cpu().numpy()
+    assert np.all(np.abs(cnt - ref32["count"]) <= 1)
+    h = rec.h.cpu().numpy().astype(np.float64)
+    h = np.where(np.arange(h.shape[1])[None, :] < cnt[:, None], h, 0.0)
+    th64 = th.cpu().numpy().astype(np.float64)
+    y064 = y0.cpu().numpy().astype(np.float64)
+    same = cnt == ref32["count"]
+    assert same.mean() > 0.9
+    assert rel_err(y1.cpu().numpy()[:, same], ref32["y1"][:, same]).max() <= 1e-5
+    yS = oracle.replay(w.system, w.method, th64, y064, cnt, h)
+    assert rel_err(y1.cpu().numpy(), yS).max() <= 1e-3
+    lam = di.cotangent(w, yS)
+    dth_o, dy0_o, _ = oracle.grad(w.system, w.method, th64, y064, cnt, h, lam, nthreads=8)
+    dth, dy0 = dao.grad(rec, torch.tensor(lam, dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    assert rel_err(dth.cpu().numpy() * th64, dth_o * th64).max() <= 1e-3
+    assert rel_err(dy0.cpu().numpy(), dy0_o).max() <= 1e-3
