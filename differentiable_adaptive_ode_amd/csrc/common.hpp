@@ -115,8 +115,21 @@ struct CtrlCoef {
   }
 };
 
+// E(2b/Q - 1) ~ 2^(-b/Q), the power's fractional factor; it takes only the Q
+// values b = 0 .. Q-1, so a kernel may tabulate it once (ctrl_root_tab).
 template <class R, int Q>
-__device__ __forceinline__ R ctrl_root(R x, const CtrlCoef<R, Q>& K) {
+__device__ __forceinline__ R ctrl_frac(int b, const CtrlCoef<R, Q>& K) {
+  const R t = fmaR(R(b), R(2.0 / Q), R(-1));
+  const R t2 = t * t, t4 = t2 * t2;
+  const R q01 = fmaR(K.e[1], t, K.e[0]), q23 = fmaR(K.e[3], t, K.e[2]);
+  const R q45 = fmaR(K.e[5], t, K.e[4]);
+  return fmaR(fmaR(K.e[6], t2, q45), t4, fmaR(q23, t2, q01));
+}
+
+// The power with E(b) from `tab` (tab[b] = ctrl_frac(b)) or, for a null tab,
+// evaluated in place: the same values either way.
+template <class R, int Q>
+__device__ __forceinline__ R ctrl_root_tab(R x, const CtrlCoef<R, Q>& K, const R* tab) {
   using L = CtrlRoot<Q>;
   x = x > R(L::lo) ? x : R(L::lo);
   x = x < R(L::hi) ? x : R(L::hi);
@@ -132,12 +145,13 @@ __device__ __forceinline__ R ctrl_root(R x, const CtrlCoef<R, Q>& K) {
   const R p01 = fmaR(K.c[1], s, K.c[0]), p23 = fmaR(K.c[3], s, K.c[2]);
   const R p45 = fmaR(K.c[5], s, K.c[4]), p67 = fmaR(K.c[7], s, K.c[6]);
   const R p = fmaR(fmaR(p67, s2, p45), s4, fmaR(p23, s2, p01));
-  const R t = fmaR(R(b), R(2.0 / Q), R(-1));
-  const R t2 = t * t, t4 = t2 * t2;
-  const R q01 = fmaR(K.e[1], t, K.e[0]), q23 = fmaR(K.e[3], t, K.e[2]);
-  const R q45 = fmaR(K.e[5], t, K.e[4]);
-  const R q = fmaR(fmaR(K.e[6], t2, q45), t4, fmaR(q23, t2, q01));
+  const R q = tab ? tab[b] : ctrl_frac<R, Q>(b, K);
   return ldexpR(p * q, -a);
+}
+
+template <class R, int Q>
+__device__ __forceinline__ R ctrl_root(R x, const CtrlCoef<R, Q>& K) {
+  return ctrl_root_tab<R, Q>(x, K, nullptr);
 }
 
 // Lane index within the 64-wide wavefront and cross-lane helpers.

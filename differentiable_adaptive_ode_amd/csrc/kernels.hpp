@@ -177,6 +177,10 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   // the controller's coefficients likewise (with the Tsit5 table pinned the
   // scalar registers would otherwise overflow)
   const CtrlCoef<R, CTRL_Q> KC = CtrlCoef<R, CTRL_Q>::make(METHOD == M_TSIT5 && Sys::D <= 4);
+  // the power's fractional factor for its CTRL_Q possible arguments, once
+  __shared__ R ctrl_tab[16];
+  if (threadIdx.x < CTRL_Q) ctrl_tab[threadIdx.x] = ctrl_frac<R, CTRL_Q>((int)threadIdx.x, KC);
+  __syncthreads();
 
   Sys sys;
   R y[D];
@@ -415,7 +419,7 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     const R msq = error_msq<R, D>(err, wt);
     const bool acc = msq <= R(1);
     // One controller evaluation serves both outcomes.
-    const R root = ctrl_root<R, CTRL_Q>(msq, KC);
+    const R root = ctrl_root_tab<R, CTRL_Q>(msq, KC, ctrl_tab);
     const R fq = (msq == R(0)) ? R(10) : truncBits(R(0.9) * root);
     const R fmin = (R(0.2) < fq) ? fq : R(0.2);
 
