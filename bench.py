@@ -121,6 +121,11 @@ def parse():
                     help="record states in the solve; the gradient skips the forward replay")
     ap.add_argument("--record-t", type=int, choices=(0, 1), default=None,
                     help="keep t_n in the record beside h_n (default: the workload's setting)")
+    ap.add_argument("--graph", type=int, choices=(0, 1), default=1,
+                    help="gradient mode: also time the step replayed as one captured HIP graph "
+                         "(the same launches without per-launch host overhead); value and "
+                         "ms_per_step then come from the replays, the per-kernel figures from "
+                         "the eager steps")
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="trajectories in the CPU-baseline sample (default per workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -287,6 +292,42 @@ def main():
     t_grad = [e[2].elapsed_time(e[4]) * 1e-3 for e in evs]
     t_kern = [e[3].elapsed_time(e[4]) * 1e-3 for e in evs]
 
+    # The same step captured once as a HIP graph and replayed: identical launches
+    # on the same buffers, without the host's per-launch overhead.  Every
+    # replay must reproduce the eager step's outputs bit for bit.
+    ms_eager = wall / args.steps * 1e3
+    launch = "eager"
+    graph_note = None
+    if args.graph:
+        class _NoEvent:
+            def record(self):
+                pass
+
+        noev = [_NoEvent()] * 5
+        ref = (dth.clone(), dy0.clone(), y1.clone())
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(noev)
+            torch.cuda.synchronize()
+            for _ in range(max(args.warmup, 1)):
+                g.replay()
+            torch.cuda.synchronize()
+            if not (torch.equal(dth, ref[0]) and torch.equal(dy0, ref[1]) and
+                    torch.equal(y1, ref[2])):
+                raise RuntimeError("a graph replay differs from the eager step")
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                g.replay()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            if not (torch.equal(dth, ref[0]) and torch.equal(dy0, ref[1])):
+                raise RuntimeError("a graph replay differs from the eager step")
+            launch = "hip graph"
+        except Exception as e:  # report the eager timing instead
+            graph_note = f"graph replay not used: {e}"
+
     cnt = rec.count.cpu().numpy().astype(np.int64)
     nrej = rec.nrej.cpu().numpy().astype(np.int64)
     status = rec.status.cpu().numpy()
@@ -325,6 +366,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "launch": launch,
+        "ms_per_step_eager": ms_eager,
+        "launch_note": graph_note,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
