@@ -195,3 +195,34 @@ def test_grad_at_single_precision(dao):
                                   tq.cpu().numpy().astype(np.float64), cq, nthreads=8)
     assert rel_err(dth.cpu().numpy(), dth_o).max() <= 1e-3
     assert rel_err(dy0.cpu().numpy(), dy0_o).max() <= 1e-3
+
+
+def test_grad_at_invalid_arguments(dao):
+    # refused before anything is enqueued, with a message naming the call
+    from differentiable_adaptive_ode_amd import _lib
+
+    w = di.make("lorenz63", 70)
+    th = torch.tensor(w.theta, device=DEV)
+    y0 = torch.tensor(w.y0, device=DEV)
+    rec, _ = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=1024)
+    torch.cuda.synchronize()
+    ids = (_lib.SYSTEMS["lorenz63"], _lib.METHODS["tsit5"], _lib.DTYPES["f64"])
+    tq = torch.tensor([0.5], dtype=torch.float64, device=DEV)
+    cq = torch.zeros((1, 3, w.n), dtype=torch.float64, device=DEV)
+    out = torch.empty_like(th), torch.empty_like(y0)
+    s_max = int(rec.count.max().item())
+    nb = _lib.dao_grad_at_workspace_size(*ids, w.n, s_max, 1)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    crec = rec.c_struct(states=False)
+
+    def call(t0=w.t0, t1=w.t1, m=1, tqp=tq.data_ptr(), wsb=nb, smax=s_max):
+        return _lib.dao_grad_at(*ids, w.n, th.data_ptr(), y0.data_ptr(), t0, t1, crec, smax, m,
+                                tqp, cq.data_ptr(), None, out[0].data_ptr(), out[1].data_ptr(),
+                                ws.data_ptr(), wsb, None)
+
+    assert call() == _lib.DAO_OK
+    torch.cuda.synchronize()
+    for kw in (dict(t1=w.t0 - 1.0), dict(m=-1), dict(tqp=None), dict(smax=rec.s_cap + 1)):
+        assert call(**kw) == _lib.DAO_EINVAL
+        assert "dao_grad_at" in _lib.lib.dao_last_error().decode()
+    assert call(wsb=16) == _lib.DAO_EWORKSPACE
