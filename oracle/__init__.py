@@ -63,7 +63,8 @@ def lib():
         L.oracle_dims.argtypes = [I, P, P, P]
         L.oracle_tsit5_table.argtypes = [P, P, P]
         L.oracle_ros23_consts.argtypes = [P, P]
-        for name in ("oracle_solve_f64", "oracle_solve_f32"):
+        for name in ("oracle_solve_f64", "oracle_solve_f32", "oracle_solve_plain_f64",
+                     "oracle_solve_plain_f32"):
             getattr(L, name).argtypes = [I, I, I64, P, P, D, D, D, D, D, I64, I64, P, P, P, P, P, P, I]
         L.oracle_replay_f64.argtypes = [I, I, I64, P, P, P, P, I64, P, I]
         L.oracle_replay_cs.argtypes = [I, I, I64, P, P, P, P, D, P, P, I64, P, P]
@@ -112,8 +113,11 @@ def ros23_consts():
 
 
 def solve(system, method, theta, y0, t0, t1, rtol, atol, dt0=0.0, max_steps=100000, s_cap=4096,
-          dtype="f64", nthreads=1, record=True):
-    """Adaptive solve with record.  Returns a dict of numpy arrays."""
+          dtype="f64", nthreads=1, record=True, plain=False):
+    """Adaptive solve with record.  Returns a dict of numpy arrays.  plain=True
+    runs the PLAIN instantiation: the error test e_c / sc_c by IEEE division,
+    the controller power by the library pow, the LU by division by the pivot
+    (the contract arithmetic's readings undone; rounding-level differences)."""
     d, p, shared = dims(system)
     np_t = np.float64 if dtype == "f64" else np.float32
     theta = np.ascontiguousarray(theta, dtype=np_t)
@@ -127,7 +131,7 @@ def solve(system, method, theta, y0, t0, t1, rtol, atol, dt0=0.0, max_steps=1000
     status = np.zeros(n, np.int32)
     t_rec = np.zeros((n, s_cap), np_t) if record else None
     h_rec = np.zeros((n, s_cap), np_t) if record else None
-    fn = lib().oracle_solve_f64 if dtype == "f64" else lib().oracle_solve_f32
+    fn = getattr(lib(), f"oracle_solve{'_plain' if plain else ''}_{dtype}")
     rc = fn(SYSTEMS[system], METHODS[method], n, _p(theta), _p(y0), float(t0), float(t1),
             float(rtol), float(atol), float(dt0), int(max_steps), int(s_cap), _p(y1), _p(count),
             _p(nrej), _p(status), _p(t_rec), _p(h_rec), int(nthreads))

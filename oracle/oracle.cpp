@@ -484,9 +484,12 @@ void tsit5_step(int sys, const T* th, int d, const T* y, T h, T k[7][MAXD], T* y
 // Dense LU with partial pivoting (first row of largest magnitude) and the
 // solve with its factors.  Used for the Rosenbrock matrix W = I - h d J.
 // The reciprocal of each pivot is formed once (rp[k] = 1 / u_kk) and the
-// elimination and the solves multiply by it.
+// elimination and the solves multiply by it (reading R7).  PLAIN = true is
+// the textbook form instead: every multiplier and every back-substituted
+// unknown is a division by the pivot itself (rp then holds u_kk).  The two
+// differ in rounding only.
 // ----------------------------------------------------------------------------
-template <class T>
+template <class T, bool PLAIN = false>
 void lu_factor(int d, T* A, int* piv, T* rp) {
   for (int k = 0; k < d; ++k) {
     int p = k;
@@ -498,15 +501,15 @@ void lu_factor(int d, T* A, int* piv, T* rp) {
     piv[k] = p;
     if (p != k)
       for (int j = 0; j < d; ++j) std::swap(A[k * d + j], A[p * d + j]);
-    rp[k] = T(1.0) / A[k * d + k];
+    rp[k] = PLAIN ? A[k * d + k] : T(1.0) / A[k * d + k];
     for (int i = k + 1; i < d; ++i) {
-      T l = A[i * d + k] * rp[k];
+      T l = PLAIN ? A[i * d + k] / A[k * d + k] : A[i * d + k] * rp[k];
       A[i * d + k] = l;
       for (int j = k + 1; j < d; ++j) A[i * d + j] = fma3(-l, A[k * d + j], A[i * d + j]);
     }
   }
 }
-template <class T>
+template <class T, bool PLAIN = false>
 void lu_solve(int d, const T* LU, const int* piv, const T* rp, const T* b, T* x) {
   T z[MAXD];
   for (int i = 0; i < d; ++i) z[i] = b[i];
@@ -517,7 +520,7 @@ void lu_solve(int d, const T* LU, const int* piv, const T* rp, const T* b, T* x)
   for (int i = d - 1; i >= 0; --i) {
     T acc = z[i];
     for (int j = i + 1; j < d; ++j) acc = fma3(-LU[i * d + j], x[j], acc);
-    x[i] = acc * rp[i];
+    x[i] = PLAIN ? acc / rp[i] : acc * rp[i];
   }
 }
 
@@ -526,7 +529,7 @@ void lu_solve(int d, const T* LU, const int* piv, const T* rp, const T* b, T* x)
 // F0 = f(y) on entry.  Returns ynew; if err != nullptr also evaluates
 // F2 = f(ynew) (returned for reuse as the next F0) and the error estimate.
 // ----------------------------------------------------------------------------
-template <class T>
+template <class T, bool PLAIN = false>
 void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* ynew, T* F2, T* err,
                 bool unscaled = false) {
   T J[MAXD * MAXD], W[MAXD * MAXD], rp[MAXD];
@@ -535,14 +538,14 @@ void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* yn
   T hd = h * T(R23_D);
   for (int i = 0; i < d; ++i)
     for (int j = 0; j < d; ++j) W[i * d + j] = fma3(-hd, J[i * d + j], T(i == j ? 1.0 : 0.0));
-  lu_factor(d, W, piv, rp);
+  lu_factor<T, PLAIN>(d, W, piv, rp);
   T k1[MAXD], k2[MAXD], Y1[MAXD], F1[MAXD], r[MAXD], u[MAXD];
-  lu_solve(d, W, piv, rp, F0, k1);
+  lu_solve<T, PLAIN>(d, W, piv, rp, F0, k1);
   T hh = T(0.5) * h;
   for (int c = 0; c < d; ++c) Y1[c] = fma3(hh, k1[c], y[c]);
   rhs(sys, th, Y1, F1);
   for (int c = 0; c < d; ++c) r[c] = F1[c] - k1[c];
-  lu_solve(d, W, piv, rp, r, u);
+  lu_solve<T, PLAIN>(d, W, piv, rp, r, u);
   for (int c = 0; c < d; ++c) k2[c] = u[c] + k1[c];
   for (int c = 0; c < d; ++c) ynew[c] = fma3(h, k2[c], y[c]);
   if (err == nullptr) return;
@@ -552,7 +555,7 @@ void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* yn
     T t2 = fma3(T(-R23_E32), k2[c] - F1[c], F2[c]);
     r[c] = fma3(T(-2.0), k1[c] - F0[c], t2);
   }
-  lu_solve(d, W, piv, rp, r, k3);
+  lu_solve<T, PLAIN>(d, W, piv, rp, r, k3);
   if (unscaled) {  // without the factor h/6 (folded into the solve's error weights)
     for (int c = 0; c < d; ++c) err[c] = fma3(T(-2.0), k2[c], k1[c]) + k3[c];
     return;
@@ -662,6 +665,26 @@ T error_msq(int d, const T* a, const T* w) {
   return acc * T(1.0 / d);
 }
 
+// The PLAIN instantiation of the solve (test of the readings above): the
+// error test and the controller written as their plain definitions, the
+// scaled component e_c / sc_c by one IEEE division (e_c = s a_c formed
+// first), the mean of squares as the sum over d, and the controller power by
+// the library pow.  Only rounding separates it from the contract arithmetic.
+template <class T>
+T plain_msq(int d, const T* e, const T* sc) {
+  T acc = T(0.0);
+  for (int c = 0; c < d; ++c) {
+    T r = e[c] / sc[c];
+    acc = acc + r * r;
+  }
+  return acc / T(double(d));
+}
+template <class T, bool PLAIN>
+T ctrl_power(T msq, int q) {
+  if (PLAIN) return pow_(msq, T(-1.0 / q));
+  return ctrl_root(msq, q);
+}
+
 // Starting step (Hairer, Norsett & Wanner, Solving ODEs I, Sec. II.4).
 template <class T>
 T initial_step(int sys, const T* th, int d, const T* y0, const T* f0, T span, T rtol, T atol,
@@ -691,7 +714,7 @@ struct SolveOut {
   int32_t count, nrej, status;
 };
 
-template <class T>
+template <class T, bool PLAIN = false>
 SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1, T rtol, T atol,
                       T dt0, int64_t max_steps, int64_t s_cap, T* y1, T* t_rec, T* h_rec) {
   const int d = SYS_D[sys];
@@ -715,9 +738,9 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
       if (!finite_(hs)) { out.status = ST_NONFINITE; break; }
       if (!(t + hs > t)) { out.status = ST_DTMIN; break; }
       if (method == M_TSIT5) {
-        tsit5_step(sys, th, d, y, hs, k, ynew, e, true);
+        tsit5_step(sys, th, d, y, hs, k, ynew, e, !PLAIN);
       } else {
-        ros23_step(sys, th, d, y, hs, k[0], ynew, F2, e, true);
+        ros23_step<T, PLAIN>(sys, th, d, y, hs, k[0], ynew, F2, e, !PLAIN);
       }
       const T es = (method == M_TSIT5) ? hs : hs / T(6.0);
       T w[MAXD];
@@ -725,7 +748,7 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
         sc[c] = fma3(rtol, std::max(abs_(y[c]), abs_(ynew[c])), atol);
         w[c] = es / sc[c];
       }
-      T msq = error_msq(d, e, w);
+      T msq = PLAIN ? plain_msq(d, e, sc) : error_msq(d, e, w);
       if (!finite_(msq)) { out.status = ST_NONFINITE; break; }
       if (msq <= T(1.0)) {
         if (n >= s_cap) { out.status = ST_CAPACITY; break; }
@@ -738,14 +761,14 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
           for (int c = 0; c < d; ++c) k[0][c] = k[6][c];
         else
           for (int c = 0; c < d; ++c) k[0][c] = F2[c];
-        T fac = (msq == T(0)) ? T(10.0) : trunc_bits(T(0.9) * ctrl_root(msq, q));
+        T fac = (msq == T(0)) ? T(10.0) : trunc_bits(T(0.9) * ctrl_power<T, PLAIN>(msq, q));
         fac = std::min(T(10.0), std::max(T(0.2), fac));
         if (prev_rejected) fac = std::min(fac, T(1.0));
         h = hs * fac;
         prev_rejected = false;
       } else {
         ++out.nrej;
-        T fac = std::max(T(0.2), trunc_bits(T(0.9) * ctrl_root(msq, q)));
+        T fac = std::max(T(0.2), trunc_bits(T(0.9) * ctrl_power<T, PLAIN>(msq, q)));
         h = hs * fac;
         prev_rejected = true;
       }
@@ -836,7 +859,7 @@ bool valid_sys(int sys, int method) {
   return true;
 }
 
-template <class T>
+template <class T, bool PLAIN = false>
 int solve_impl(int sys, int method, int64_t n, const T* theta, const T* y0, double t0, double t1,
                double rtol, double atol, double dt0, int64_t max_steps, int64_t s_cap, T* y1,
                int32_t* count, int32_t* nrej, int32_t* status, T* t_rec, T* h_rec, int nthreads) {
@@ -851,7 +874,7 @@ int solve_impl(int sys, int method, int64_t n, const T* theta, const T* y0, doub
     for (int64_t k = lo; k < hi; ++k) {
       for (int i = 0; i < p; ++i) th[i] = shared ? theta[i] : theta[i * n + k];
       for (int c = 0; c < d; ++c) yy0[c] = y0[c * n + k];
-      SolveOut<T> o = solve_one<T>(sys, method, th.data(), yy0, T(t0), T(t1), T(rtol), T(atol),
+      SolveOut<T> o = solve_one<T, PLAIN>(sys, method, th.data(), yy0, T(t0), T(t1), T(rtol), T(atol),
                                    T(dt0), max_steps, s_cap, yy1, t_rec ? t_rec + k * s_cap : nullptr,
                                    h_rec ? h_rec + k * s_cap : nullptr);
       for (int c = 0; c < d; ++c) y1[c * n + k] = yy1[c];
@@ -908,6 +931,27 @@ int oracle_solve_f32(int sys, int method, int64_t n, const float* theta, const f
                      float* t_rec, float* h_rec, int nthreads) {
   return solve_impl<float>(sys, method, n, theta, y0, t0, t1, rtol, atol, dt0, max_steps, s_cap,
                            y1, count, nrej, status, t_rec, h_rec, nthreads);
+}
+
+// The same solves in the PLAIN instantiation (plain error test, library pow
+// in the controller, division by the pivot): a test that the contract
+// arithmetic changes rounding only.
+int oracle_solve_plain_f64(int sys, int method, int64_t n, const double* theta, const double* y0,
+                           double t0, double t1, double rtol, double atol, double dt0,
+                           int64_t max_steps, int64_t s_cap, double* y1, int32_t* count,
+                           int32_t* nrej, int32_t* status, double* t_rec, double* h_rec,
+                           int nthreads) {
+  return solve_impl<double, true>(sys, method, n, theta, y0, t0, t1, rtol, atol, dt0, max_steps,
+                                  s_cap, y1, count, nrej, status, t_rec, h_rec, nthreads);
+}
+
+int oracle_solve_plain_f32(int sys, int method, int64_t n, const float* theta, const float* y0,
+                           double t0, double t1, double rtol, double atol, double dt0,
+                           int64_t max_steps, int64_t s_cap, float* y1, int32_t* count,
+                           int32_t* nrej, int32_t* status, float* t_rec, float* h_rec,
+                           int nthreads) {
+  return solve_impl<float, true>(sys, method, n, theta, y0, t0, t1, rtol, atol, dt0, max_steps,
+                                 s_cap, y1, count, nrej, status, t_rec, h_rec, nthreads);
 }
 
 // Replay in binary64 on a given mesh (h_rec [n][s_cap], count [n]).
