@@ -305,6 +305,18 @@ def main():
 
         noev = [_NoEvent()] * 5
         ref = (dth.clone(), dy0.clone(), y1.clone())
+
+        def same():
+            # Per-trajectory outputs are bit-reproducible.  The neural field's
+            # shared-weight sum is not: which wavefront sums which group of
+            # trajectories depends on the order they claim groups, so it is
+            # compared to float32 rounding.
+            if w.system == "mlp":
+                ok_th = torch.allclose(dth, ref[0], rtol=1e-4, atol=1e-6 * ref[0].abs().max())
+            else:
+                ok_th = torch.equal(dth, ref[0])
+            return ok_th and torch.equal(dy0, ref[1]) and torch.equal(y1, ref[2])
+
         try:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -313,17 +325,17 @@ def main():
             for _ in range(max(args.warmup, 1)):
                 g.replay()
             torch.cuda.synchronize()
-            if not (torch.equal(dth, ref[0]) and torch.equal(dy0, ref[1]) and
-                    torch.equal(y1, ref[2])):
+            if not same():
                 raise RuntimeError("a graph replay differs from the eager step")
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for _ in range(args.steps):
                 g.replay()
             torch.cuda.synchronize()
-            wall = time.perf_counter() - t0
-            if not (torch.equal(dth, ref[0]) and torch.equal(dy0, ref[1])):
+            wall_graph = time.perf_counter() - t0
+            if not same():
                 raise RuntimeError("a graph replay differs from the eager step")
+            wall = wall_graph  # only once every replay checked out
             launch = "hip graph"
         except Exception as e:  # report the eager timing instead
             graph_note = f"graph replay not used: {e}"

@@ -24,7 +24,7 @@ TRAJ_STATUS = {0: "ok", 1: "max_steps", 2: "nonfinite", 3: "dt_underflow", 4: "c
 
 class dao_tol(ctypes.Structure):
     _fields_ = [("rtol", ctypes.c_double), ("atol", ctypes.c_double), ("dt0", ctypes.c_double),
-                ("max_steps", ctypes.c_int64)]
+                ("max_steps", ctypes.c_int64), ("phases", ctypes.c_int32)]
 
 
 class dao_record(ctypes.Structure):
@@ -81,6 +81,8 @@ def _load():
     L.dao_grad_at.argtypes = [I, I, I, I64, P, P, D, D, ctypes.POINTER(dao_record), I64, I64, P,
                               P, P, P, P, P, SZ, P]
     L.dao_grad_at.restype = I
+    L.dao_record_stats.argtypes = [I64, ctypes.POINTER(dao_record), P, P]
+    L.dao_record_stats.restype = I
     L.dao_sqerr_cotangent.argtypes = [I, I64, I, I, P, P, D, P, P]
     L.dao_sqerr_cotangent.restype = I
     L.dao_last_error.argtypes = []
@@ -183,6 +185,10 @@ def dao_grad_ordered(system, method, dtype, n, theta, y0, rec, s_max, dLdy1, dLd
     return lib.dao_grad_ordered(system, method, dtype, n, theta, y0,
                                 ctypes.byref(rec) if rec is not None else None, s_max, dLdy1,
                                 dLdtheta, dLdy0, workspace, ws_bytes, stream)
+
+
+def dao_record_stats(n, rec, out, stream):
+    return lib.dao_record_stats(n, ctypes.byref(rec) if rec is not None else None, out, stream)
 
 
 def dao_sqerr_cotangent(dtype, n, d, d_used, y1, target, scale, out, stream):

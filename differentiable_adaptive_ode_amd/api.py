@@ -29,9 +29,12 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _tstream(stream=None):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
 def _stream(stream=None):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    return _tstream(stream).cuda_stream
 
 
 def _check_dev(*ts):
@@ -74,6 +77,22 @@ class Record:
     def s_cap(self):
         return self.h.shape[1]
 
+    def stats(self, out=None, stream=None) -> torch.Tensor:
+        """Device int64[4] = (max count, total accepted steps, failed
+        trajectories, total rejected attempts), written in stream order by
+        dao_record_stats; nothing is synchronised."""
+        o = torch.empty(4, dtype=torch.int64, device=self.count.device) if out is None else out
+        _lib.check(_lib.dao_record_stats(self.n, self.c_struct(), _ptr(o), _stream(stream)))
+        return o
+
+    def stats_host(self, stream=None) -> dict:
+        """stats() read back to the host: this call synchronises the stream."""
+        s = _tstream(stream)
+        v = self.stats(stream=stream)
+        s.synchronize()
+        m, tot, bad, rej = (int(x) for x in v.cpu().tolist())
+        return dict(s_max=m, steps=tot, failed=bad, rejected=rej)
+
     def c_struct(self, states: bool = True):
         return _lib.dao_record(self.s_cap, _ptr(self.t), _ptr(self.h), _ptr(self.count),
                                _ptr(self.nrej), _ptr(self.status),
@@ -81,26 +100,33 @@ class Record:
 
 
 class Workspace:
-    """Grow-only device scratch shared by calls on one stream."""
+    """Grow-only device scratch for calls on ONE stream (calls that share a
+    workspace must not overlap in time).  The buffer is allocated on the
+    stream the call launches on, so when it grows the caching allocator hands
+    the old block only to later work on that same stream."""
 
     def __init__(self, device=None):
         self.buf = None
         self.device = device
 
-    def get(self, nbytes: int, device) -> torch.Tensor:
+    def get(self, nbytes: int, device, stream=None) -> torch.Tensor:
         nbytes = max(int(nbytes), 256)
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            self.buf = None
+            with torch.cuda.stream(_tstream(stream)):
+                self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         return self.buf
 
 
 _default_ws: dict = {}
 
 
-def _ws(device, ws=None):
+def _ws(device, ws=None, stream=None):
+    """The caller's workspace, or the default one of the stream the call
+    launches on (one per device and stream)."""
     if ws is not None:
         return ws
-    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    key = (str(device), _stream(stream))
     if key not in _default_ws:
         _default_ws[key] = Workspace()
     return _default_ws[key]
@@ -122,11 +148,13 @@ def alloc_record(n: int, s_cap: int, dtype: str, device, with_t: bool = True,
 def solve(system: str, method: str, theta: torch.Tensor, y0: torch.Tensor, t0: float, t1: float,
           rtol: float, atol: float, dt0: float = 0.0, max_steps: int = 100000, s_cap: int = 4096,
           record_t: bool = True, record_states: bool = False, out=None, rec_buffers=None,
-          workspace=None, stream=None, out_sens=None, _sens=False):
+          workspace=None, stream=None, out_sens=None, phases: int = 0, _sens=False):
     """Adaptive solve with record.  Returns (Record, y1).
 
     record_states: also keep the state at the start of every accepted step, so
     that grad() at the solve's theta skips the replay's forward pass.
+    phases: 0 automatic, 1 or 2 forces one or two phases (same results).
+    Failed trajectories do not raise: see Record.stats().
     """
     _check_dev(theta, y0)
     dtype = _dtype_name(y0)
@@ -144,11 +172,11 @@ def solve(system: str, method: str, theta: torch.Tensor, y0: torch.Tensor, t0: f
         n, s_cap, dtype, dev, record_t, d if record_states else 0)
     rec = Record(system, method, dtype, theta, y0, float(t0), float(t1), bufs["h"], bufs.get("t"),
                  bufs["count"], bufs["nrej"], bufs["status"], bufs.get("y"))
-    ws = _ws(dev, workspace)
+    ws = _ws(dev, workspace, stream)
     sysid, mid, did = _lib.SYSTEMS[system], _lib.METHODS[method], _lib.DTYPES[dtype]
     nb = _lib.dao_solve_workspace_size(sysid, mid, did, n)
-    buf = ws.get(nb, dev)
-    tol = _lib.dao_tol(float(rtol), float(atol), float(dt0), int(max_steps))
+    buf = ws.get(nb, dev, stream)
+    tol = _lib.dao_tol(float(rtol), float(atol), float(dt0), int(max_steps), int(phases))
     crec = rec.c_struct()
     if _sens:
         S = torch.empty((d, p, n), dtype=y0.dtype, device=dev) if out_sens is None else out_sens
@@ -177,28 +205,24 @@ def sens(rec: Record, theta: torch.Tensor | None = None, with_theta: bool = True
     _check_dev(th)
     n = rec.n
     d, p, _ = _lib.dao_system_dims(_lib.SYSTEMS[rec.system])
-    if s_max is None:
-        s_max = int(rec.count.max().item()) if n > 0 else 0
-    s_max = min(int(s_max), rec.s_cap)
+    s_max = rec.s_cap if s_max is None else min(int(s_max), rec.s_cap)
     ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
     dev = rec.count.device
     S_th = torch.empty((d, p, n), dtype=rec.y0.dtype, device=dev) if with_theta else None
     S_y0 = torch.empty((d, d, n), dtype=rec.y0.dtype, device=dev) if with_y0 else None
     nb = _lib.dao_sens_workspace_size(*ids, n, s_max)
-    buf = _ws(dev, workspace).get(nb, dev)
+    buf = _ws(dev, workspace, stream).get(nb, dev, stream)
     _lib.check(_lib.dao_sens(*ids, n, _ptr(th), _ptr(rec.y0), rec.c_struct(states=False), s_max,
                              _ptr(S_th), _ptr(S_y0), _ptr(buf), buf.numel(), _stream(stream)))
     return S_th, S_y0
 
 
-def _grad_setup(rec: Record, s_max, workspace, device):
+def _grad_setup(rec: Record, s_max, workspace, device, stream):
     n = rec.n
-    if s_max is None:
-        s_max = int(rec.count.max().item()) if n > 0 else 0
-    s_max = min(int(s_max), rec.s_cap)
+    s_max = rec.s_cap if s_max is None else min(int(s_max), rec.s_cap)
     ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
     nb = _lib.dao_grad_workspace_size(*ids, n, s_max)
-    buf = _ws(device, workspace).get(nb, device)
+    buf = _ws(device, workspace, stream).get(nb, device, stream)
     return ids, n, s_max, buf
 
 
@@ -206,7 +230,7 @@ def grad_order(rec: Record, s_max: int | None = None, workspace=None, stream=Non
     """Sort rec's trajectories by step count into the workspace, for later
     grad(..., ordered=True) calls on the same record and workspace.  Returns
     the s_max it used (pass the same value to those calls)."""
-    ids, n, s_max, buf = _grad_setup(rec, s_max, workspace, rec.count.device)
+    ids, n, s_max, buf = _grad_setup(rec, s_max, workspace, rec.count.device, stream)
     _lib.check(_lib.dao_grad_order(*ids, n, rec.c_struct(), s_max, _ptr(buf), buf.numel(),
                                    _stream(stream)))
     return s_max
@@ -218,7 +242,9 @@ def grad(rec: Record, dLdy1: torch.Tensor, theta: torch.Tensor | None = None, s_
 
     theta:   parameters to differentiate at (default: the solve's theta).  At a
              theta other than the solve's, recorded states are not used.
-    s_max:   an upper bound on rec.count (default: read back from the device).
+    s_max:   an upper bound on rec.count (default: the record's capacity, which
+             needs no read-back but a larger workspace; Record.stats() gives
+             the exact one in stream order).
     ordered: the workspace already holds this record's order (grad_order with
              the same workspace and s_max); skips the sort.
     """
@@ -226,7 +252,7 @@ def grad(rec: Record, dLdy1: torch.Tensor, theta: torch.Tensor | None = None, s_
     th = rec.theta if theta is None else theta
     _check_dev(th)
     dev = dLdy1.device
-    ids, n, s_max, buf = _grad_setup(rec, s_max, workspace, dev)
+    ids, n, s_max, buf = _grad_setup(rec, s_max, workspace, dev, stream)
     dth = torch.empty_like(th) if out_theta is None else out_theta
     dy0 = torch.empty_like(rec.y0) if out_y0 is None else out_y0
     crec = rec.c_struct(states=theta is None)
@@ -247,17 +273,18 @@ def states_at(rec: Record, tq: torch.Tensor, theta: torch.Tensor | None = None,
     d, _, _ = _lib.dao_system_dims(_lib.SYSTEMS[rec.system])
     if tq.dtype != rec.y0.dtype:
         raise TypeError("tq must have the record's dtype")
-    if s_max is None:
-        s_max = int(rec.count.max().item()) if n > 0 else 0
-    s_max = min(int(s_max), rec.s_cap)
+    s_max = rec.s_cap if s_max is None else min(int(s_max), rec.s_cap)
     ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
     dev = rec.count.device
     yq = torch.empty((m, d, n), dtype=rec.y0.dtype, device=dev) if out is None else out
     nb = _lib.dao_states_workspace_size(*ids, n, s_max)
-    buf = _ws(dev, workspace).get(nb, dev)
+    buf = _ws(dev, workspace, stream).get(nb, dev, stream)
+    tqc = tq.contiguous()  # kept alive until the call has enqueued its reads
     _lib.check(_lib.dao_states_at(*ids, n, _ptr(th), _ptr(rec.y0), rec.t0, rec.t1,
-                                  rec.c_struct(states=False), s_max, m, _ptr(tq.contiguous()),
+                                  rec.c_struct(states=False), s_max, m, _ptr(tqc),
                                   _ptr(yq), _ptr(buf), buf.numel(), _stream(stream)))
+    if tqc is not tq:
+        tqc.record_stream(_tstream(stream))
     return yq
 
 
@@ -275,20 +302,24 @@ def grad_at(rec: Record, tq: torch.Tensor, dLdyq: torch.Tensor, dLdy1: torch.Ten
     d, _, _ = _lib.dao_system_dims(_lib.SYSTEMS[rec.system])
     if tuple(dLdyq.shape) != (m, d, n):
         raise ValueError(f"dLdyq must have shape {(m, d, n)}")
-    if s_max is None:
-        s_max = int(rec.count.max().item()) if n > 0 else 0
-    s_max = min(int(s_max), rec.s_cap)
+    s_max = rec.s_cap if s_max is None else min(int(s_max), rec.s_cap)
     ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
     dev = rec.count.device
     nb = _lib.dao_grad_at_workspace_size(*ids, n, s_max, m)
-    buf = _ws(dev, workspace).get(max(nb, 1), dev)
+    buf = _ws(dev, workspace, stream).get(max(nb, 1), dev, stream)
     dth = torch.empty_like(th) if out_theta is None else out_theta
     dy0 = torch.empty_like(rec.y0) if out_y0 is None else out_y0
+    # contiguous copies, kept alive (and tied to the launch stream) until the
+    # kernels that read them have run
+    tqc, cqc = tq.contiguous(), dLdyq.contiguous()
     g1 = None if dLdy1 is None else dLdy1.contiguous()
     _lib.check(_lib.dao_grad_at(*ids, n, _ptr(th), _ptr(rec.y0), rec.t0, rec.t1,
-                                rec.c_struct(states=False), s_max, m, _ptr(tq.contiguous()),
-                                _ptr(dLdyq.contiguous()), _ptr(g1), _ptr(dth), _ptr(dy0),
+                                rec.c_struct(states=False), s_max, m, _ptr(tqc),
+                                _ptr(cqc), _ptr(g1), _ptr(dth), _ptr(dy0),
                                 _ptr(buf), buf.numel(), _stream(stream)))
+    for c, orig in ((tqc, tq), (cqc, dLdyq), (g1, dLdy1)):
+        if c is not None and c is not orig:
+            c.record_stream(_tstream(stream))
     return dth, dy0
 
 

@@ -96,6 +96,47 @@ __global__ void __launch_bounds__(256) order_scatter_kernel(const int32_t* count
     perm[atomicAdd(&lh[bucket_of(count[i], s_max, shift)], 1u)] = (int32_t)i;
 }
 
+// Record summary: max and sum of count, failed trajectories, sum of nrej.
+// Each workgroup reduces its grid-stride share in LDS, then one lane adds it
+// into out[] with device atomics (out[] cleared by the fill kernel first).
+__global__ void __launch_bounds__(256) record_stats_kernel(const int32_t* count,
+                                                           const int32_t* status,
+                                                           const int32_t* nrej, int64_t n,
+                                                           unsigned long long* out) {
+  __shared__ unsigned long long red[4][256];
+  unsigned long long mx = 0, sum = 0, bad = 0, rej = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int32_t c = count[i];
+    const unsigned long long cu = c > 0 ? (unsigned long long)c : 0ull;
+    mx = cu > mx ? cu : mx;
+    sum += cu;
+    bad += (status[i] != TRAJ_OK) ? 1ull : 0ull;
+    if (nrej) rej += nrej[i] > 0 ? (unsigned long long)nrej[i] : 0ull;
+  }
+  const int t = threadIdx.x;
+  red[0][t] = mx;
+  red[1][t] = sum;
+  red[2][t] = bad;
+  red[3][t] = rej;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (t < off) {
+      red[0][t] = red[0][t + off] > red[0][t] ? red[0][t + off] : red[0][t];
+      red[1][t] += red[1][t + off];
+      red[2][t] += red[2][t + off];
+      red[3][t] += red[3][t + off];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    atomicMax(&out[0], red[0][0]);
+    atomicAdd(&out[1], red[1][0]);
+    atomicAdd(&out[2], red[2][0]);
+    atomicAdd(&out[3], red[3][0]);
+  }
+}
+
 template <class R>
 __global__ void sqerr_cotangent_kernel(int64_t n, int d, int d_used, const R* y1, const R* tgt,
                                        R scale, R* out) {
@@ -194,30 +235,28 @@ size_t solve_phase_bytes(int64_t n) {
          2 * align_up((size_t)n * 4) + align_up((size_t)ORDER_BINS * 4);
 }
 
-// Whether a solve of n trajectories takes two phases: n at least four times
-// the resident lanes and a record capacity of at least 1024 steps
-// (DAO_SOLVE_PHASES=1 or 2 forces one or two).  The capacity is the caller's
-// bound on a trajectory's length: resuming a trajectory costs its wavefront
-// a few memory round trips, which short trajectories (tens of steps) do not
-// repay, while long ones are where a late start runs alone.
-// s_cap < 0 asks whether two phases are possible at all (workspace sizing).
+// Whether a solve of n trajectories takes two phases.  phases = 1 or 2 (the
+// caller's dao_tol) forces one or two; 0 chooses two for n at least four
+// times the resident lanes and a record capacity of at least 1024 steps.
+// The capacity is the caller's bound on a trajectory's length: resuming a
+// trajectory costs its wavefront a few memory round trips, which short
+// trajectories (tens of steps) do not repay, while long ones are where a
+// late start runs alone.
 template <class R, class Sys, int M>
-bool solve_two_phase(int64_t n, int64_t s_cap) {
-  if (n <= 0) return false;
-  if (const char* e = getenv("DAO_SOLVE_PHASES")) {
-    if (e[0] == '1') return false;
-    if (e[0] == '2') return true;
-  }
-  if (s_cap >= 0 && s_cap < 1024) return false;
+bool solve_two_phase(int64_t n, int64_t s_cap, int phases) {
+  if (n <= 0 || phases == 1) return false;
+  if (phases == 2) return true;
+  if (s_cap < 1024) return false;
   auto kern = solve_kernel<R, Sys, M, false, true>;
   const size_t lds = (size_t)BLOCK_WAVES * 2 * 8 * WAVE * sizeof(R);
   return n >= 4 * resident_blocks(kern, lds) * BLOCK;
 }
 
+// Workspace of a solve: the queue and trash slots, and room for two phases
+// (which any solve may be asked to take).
 template <class R, class Sys, int M>
 size_t solve_ws_bytes(int64_t n) {
-  return solve_base_bytes() +
-         (solve_two_phase<R, Sys, M>(n, -1) ? solve_phase_bytes<R, Sys::D, Sys::P>(n) : 0);
+  return solve_base_bytes() + (n > 0 ? solve_phase_bytes<R, Sys::D, Sys::P>(n) : 0);
 }
 
 template <class R, class Sys, int M, bool SENS = false>
@@ -255,7 +294,7 @@ dao_status launch_solve(int64_t n, const void* theta, const void* y0, double t0,
   // record staging ring: (t, h [, y]) x 8 slots x 64 lanes per wavefront
   const size_t lds = (size_t)BLOCK_WAVES * (rec->y ? 2 + Sys::D : 2) * 8 * WAVE * sizeof(R);
   {
-    if (solve_two_phase<R, Sys, M>(n, rec->s_cap) &&
+    if (solve_two_phase<R, Sys, M>(n, rec->s_cap, tol->phases) &&
         ws_bytes >= solve_base_bytes() + solve_phase_bytes<R, Sys::D, Sys::P>(n)) {
       char* p = (char*)ws + solve_base_bytes();
       a.save = (R*)p;
@@ -751,6 +790,8 @@ dao_status solve_call(const char* fn, dao_system sys, dao_method method, dao_dty
   if (!(tol->atol > 0) || !is_fin(tol->atol)) return fail(DAO_EINVAL, "%s: atol must be > 0", fn);
   if (!is_fin(tol->dt0)) return fail(DAO_EINVAL, "%s: dt0 not finite", fn);
   if (tol->max_steps < 1) return fail(DAO_EINVAL, "%s: max_steps must be >= 1", fn);
+  if (tol->phases < 0 || tol->phases > 2)
+    return fail(DAO_EINVAL, "%s: tol->phases must be 0 (automatic), 1 or 2", fn);
   const Impl* im = find_impl(sys, method, dtype);
   if (!im || (sens && !im->solve_sens))
     return fail(DAO_EUNSUPPORTED, "%s: system %d with method %d dtype %d is not provided", fn,
@@ -768,8 +809,8 @@ dao_status solve_call(const char* fn, dao_system sys, dao_method method, dao_dty
   if (rec->y && sys == DAO_SYS_MLP)
     return fail(DAO_EUNSUPPORTED, "%s: recorded states (rec->y) are not provided for the neural field", fn);
   if (!workspace || workspace_bytes < solve_base_bytes())
-    return fail(DAO_EWORKSPACE, "%s: workspace needs %zu bytes", fn,
-                dao_solve_workspace_size(sys, method, dtype, n));
+    return fail(DAO_EWORKSPACE, "%s: workspace needs at least %zu bytes (%zu for two phases)", fn,
+                solve_base_bytes(), dao_solve_workspace_size(sys, method, dtype, n));
   if (sens)
     return im->solve_sens(n, theta, y0, t0, t1, tol, y1, rec, workspace, workspace_bytes,
                           (hipStream_t)stream, S_theta);
@@ -1008,6 +1049,27 @@ dao_status dao_grad_at(dao_system sys, dao_method method, dao_dtype dtype, int64
   AtArgs at{m, tq, dLdyq, t0, t1};
   return im->grad_at(n, theta, y0, rec, s_max, dLdy1, dLdtheta, dLdy0, workspace, workspace_bytes,
                      (hipStream_t)stream, &at);
+}
+
+dao_status dao_record_stats(int64_t n, const dao_record* rec, int64_t* out, void* stream) {
+  g_err[0] = 0;
+  if (n < 0 || n > (int64_t)INT32_MAX)
+    return fail(DAO_EINVAL, "dao_record_stats: n = %lld out of range", (long long)n);
+  if (!out) return fail(DAO_EINVAL, "dao_record_stats: out is NULL");
+  if (n > 0 && !rec) return fail(DAO_EINVAL, "dao_record_stats: rec is NULL");
+  if (n > 0 && (!rec->count || !rec->status))
+    return fail(DAO_EINVAL, "dao_record_stats: rec->count or rec->status is NULL");
+  hipStream_t st = (hipStream_t)stream;
+  // out[0..3] (int64) cleared as eight 32-bit words by a fill kernel, not a
+  // memset, so the call may be captured into a graph
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, (uint32_t*)out, (int64_t)8, 0u);
+  if (n > 0) {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(record_stats_kernel, dim3((unsigned)blocks), dim3(256), 0, st, rec->count,
+                       rec->status, rec->nrej, n, (unsigned long long*)out);
+  }
+  return check_hip(hipGetLastError(), "record stats kernel launch");
 }
 
 dao_status dao_sqerr_cotangent(dao_dtype dtype, int64_t n, int d, int d_used, const void* y1,

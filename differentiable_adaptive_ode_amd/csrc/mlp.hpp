@@ -625,6 +625,10 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
     G.b2[T] = 0.f;
   }
   G.b3 = 0.f;
+  // A trajectory of the ensemble that failed, or holds more than s_max steps,
+  // has no gradient: its wavefront's partial sum becomes NaN, so the summed
+  // shared-weight gradient is NaN rather than silently partial.
+  bool failed = false;
 
   for (;;) {
     unsigned long long grp = 0;
@@ -643,6 +647,7 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
         cnt = a.count[k];
         ok = cnt >= 0 && cnt <= a.s_max && (a.status == nullptr || a.status[k] == TRAJ_OK);
         if (!ok) cnt = 0;
+        failed = failed || !ok;
       }
     }
     int mx = cnt;
@@ -676,30 +681,32 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
 
   // Write this wavefront's partial weight gradient (packed like theta).
   float* out = a.partial + slot * NP;
+  const bool poison = __ballot(failed) != 0ull;
+  auto pv = [&](float v) { return poison ? nanR(0.f) : v; };
 #pragma unroll
   for (int T2 = 0; T2 < 4; ++T2)
 #pragma unroll
     for (int T1 = 0; T1 < 4; ++T1)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        out[OW2 + (16 * T2 + 4 * g + r) * NH + 16 * T1 + j] = G.w2[T2 * 4 + T1][r];
+        out[OW2 + (16 * T2 + 4 * g + r) * NH + 16 * T1 + j] = pv(G.w2[T2 * 4 + T1][r]);
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int u = 16 * T + 4 * g + r;
       if (j < 4) {
-        out[OW3 + j * NH + u] = G.w3t[T][r];
-        out[OW1 + u * 4 + j] = G.w1t[T][r];
+        out[OW3 + j * NH + u] = pv(G.w3t[T][r]);
+        out[OW1 + u * 4 + j] = pv(G.w1t[T][r]);
       }
     }
     if (g == 0) {
-      out[OB1 + 16 * T + j] = G.b1[T];
-      out[OB2 + 16 * T + j] = G.b2[T];
+      out[OB1 + 16 * T + j] = pv(G.b1[T]);
+      out[OB2 + 16 * T + j] = pv(G.b2[T]);
     }
   }
   const float s3 = row_sum(G.b3);
-  if (j == 0) out[OB3 + g] = s3;
+  if (j == 0) out[OB3 + g] = pv(s3);
 }
 
 // dL/dtheta[p] = sum over wavefronts w of partial[w][p], deterministically:

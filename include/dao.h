@@ -90,6 +90,9 @@ typedef struct {
   double atol;       /* absolute tolerance, > 0                                         */
   double dt0;        /* > 0: first trial step; <= 0: automatic starting step           */
   int64_t max_steps; /* cap on attempted steps per trajectory, >= 1                     */
+  int32_t phases;    /* work order of dao_solve / dao_solve_sens: 0 = automatic, 1 = one
+                        phase, 2 = two phases whenever the workspace holds them (see
+                        dao_solve); the outputs are the same bit for bit either way      */
 } dao_tol;
 
 /* Step record (Sec. 3, Fig. 2): host struct of caller-owned device arrays.
@@ -113,8 +116,7 @@ typedef struct {
 dao_status dao_system_dims(dao_system sys, int* d, int* p, int* shared);
 
 /* Workspace (device bytes) dao_solve and dao_solve_sens need for n
- * trajectories.  For an ensemble of at least four times the lanes the solve
- * keeps resident (the neural field excepted) this includes the two-phase
+ * trajectories.  Except for the neural field this includes the two-phase
  * solve's saved states (with room for the sensitivities), ordering keys and
  * order, about (2d + 2 + dp) x 8 + 16 bytes per trajectory in binary64.     */
 size_t dao_solve_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n);
@@ -131,18 +133,22 @@ size_t dao_solve_workspace_size(dao_system sys, dao_method method, dao_dtype dty
  *   rec      required; rec->h may be NULL only when rec->s_cap == 0
  *   workspace >= dao_solve_workspace_size() device bytes (work-queue
  *            counter and trash slots); its contents need no initialisation.
- *            Large ensembles (see dao_solve_workspace_size) with
- *            rec->s_cap >= 1024 are solved in two phases when the workspace
- *            holds the extra: the first 64 attempts of every trajectory,
- *            then the unfinished ones resumed longest-predicted first (the
- *            remaining attempts extrapolated from the time the first ones
- *            covered), so that long trajectories do not run alone at the
- *            end.  Every trajectory takes the same attempts either way: the
- *            outputs are identical bit for bit.  A workspace of at least the
- *            size for one trajectory runs one phase.  The environment
- *            variable DAO_SOLVE_PHASES=1 or 2 forces one or two phases.
+ *            With tol->phases = 0, ensembles of at least four times the
+ *            lanes the solve keeps resident with rec->s_cap >= 1024 are
+ *            solved in two phases: the first 64 attempts of every
+ *            trajectory, then the unfinished ones resumed longest-predicted
+ *            first (the remaining attempts extrapolated from the time the
+ *            first ones covered), so that long trajectories do not run alone
+ *            at the end.  tol->phases = 1 or 2 forces one or two phases.  Two
+ *            phases need the whole dao_solve_workspace_size(); a smaller
+ *            workspace (at least dao_solve_workspace_size() for n = 0)
+ *            runs one phase.  Every trajectory
+ *            takes the same attempts either way: the outputs are identical
+ *            bit for bit.  The library reads no environment variable.
  * Errors: DAO_EINVAL (NULL array with n > 0, t1 < t0, bad tolerances,
- * rec NULL, rec->s_cap < 0), DAO_EUNSUPPORTED, DAO_EWORKSPACE, DAO_EDEVICE.
+ * tol->phases outside 0..2, rec NULL, rec->s_cap < 0), DAO_EUNSUPPORTED,
+ * DAO_EWORKSPACE, DAO_EDEVICE.  Trajectories that fail do not fail the call
+ * (it returns before they run): dao_record_stats counts them, stream-ordered.
  */
 dao_status dao_solve(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
                      const void* theta, const void* y0, double t0, double t1,
@@ -174,7 +180,10 @@ size_t dao_grad_workspace_min(dao_system sys, dao_method method, dao_dtype dtype
  *            steps get NaN outputs)
  *   dLdy1    real[d][n], the cotangent of the final state
  *   dLdtheta real[p][n], or real[4740] summed over the ensemble (MLP);
- *            may be NULL
+ *            may be NULL.  A trajectory whose status is not DAO_TRAJ_OK, or
+ *            whose count exceeds s_max, gets NaN in its entries; for the
+ *            shared weights of DAO_SYS_MLP one such trajectory makes the
+ *            whole summed gradient NaN (a partial sum is never returned).
  *   dLdy0    real[d][n]; may be NULL
  * Errors: DAO_EINVAL, DAO_EUNSUPPORTED, DAO_EWORKSPACE, DAO_EDEVICE.
  */
@@ -305,6 +314,26 @@ dao_status dao_states_at(dao_system sys, dao_method method, dao_dtype dtype, int
                          const void* theta, const void* y0, double t0, double t1,
                          const dao_record* rec, int64_t s_max, int64_t m, const void* tq,
                          void* yq, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dao_record_stats -- summary of a record, computed on the device in stream
+ * order (so a caller that must not synchronise can still size a gradient or
+ * detect failed trajectories at a point of its choosing).  gradsolve Sec. 3
+ * (Fig. 2): the record is the accepted steps of every trajectory, padded to
+ * a common length for the replay, whose length is the longest record; Sec.
+ * 3.4: a call that cannot produce its result says so.
+ *   n        trajectories in the record (>= 0)
+ *   rec      rec->count and rec->status are read (rec->nrej if not NULL)
+ *   out      device int64[4], written after every earlier call on the
+ *            stream:
+ *              out[0] = max_k count[k]   (the s_max a gradient needs; 0 if n = 0)
+ *              out[1] = sum_k count[k]   (accepted steps of the ensemble)
+ *              out[2] = number of k with status[k] != DAO_TRAJ_OK
+ *              out[3] = sum_k nrej[k]    (0 when rec->nrej is NULL)
+ * Errors: DAO_EINVAL (n < 0, rec / count / status / out NULL with n > 0 --
+ * out must not be NULL even for n = 0), DAO_EDEVICE.
+ */
+dao_status dao_record_stats(int64_t n, const dao_record* rec, int64_t* out, void* stream);
 
 /*
  * dao_sqerr_cotangent -- cotangent of a squared-error loss (the misfit

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
               "dao_solve_workspace_size", "dao_grad_workspace_size", "dao_grad_at",
               "dao_grad_at_workspace_size",
               "dao_grad_workspace_min", "dao_system_dims", "dao_sqerr_cotangent",
-              "dao_last_error", "dao_version"):
+              "dao_record_stats", "dao_last_error", "dao_version"):
         assert n in names, n
 
 
@@ -74,7 +74,7 @@ def test_solve_argument_errors(L, over, code):
 
 
 @pytest.mark.parametrize("field,val", [("rtol", 0.0), ("atol", -1.0), ("max_steps", 0),
-                                       ("dt0", float("inf"))])
+                                       ("dt0", float("inf")), ("phases", 3), ("phases", -1)])
 def test_solve_tolerance_errors(L, field, val):
     tol = L.dao_tol(1e-6, 1e-8, 0.0, 1000)
     setattr(tol, field, val)
@@ -190,3 +190,26 @@ def test_cotangent_argument_errors(L):
     assert L.dao_sqerr_cotangent(0, 4, 0, 0, 1, 1, 1.0, 1, None) == 1
     assert L.dao_sqerr_cotangent(0, 4, 3, 3, None, 1, 1.0, 1, None) == 1
     assert L.dao_sqerr_cotangent(0, 0, 3, 3, None, None, 1.0, None, None) == 0
+
+
+def test_record_stats_argument_errors(L):
+    rec = L.dao_record(16, None, 1, 1, None, 1)
+    assert L.dao_record_stats(-1, rec, 1, None) == 1
+    assert "n = -1" in L.dao_last_error()
+    assert L.dao_record_stats(4, rec, None, None) == 1
+    assert "out" in L.dao_last_error()
+    assert L.dao_record_stats(4, None, 1, None) == 1
+    assert L.dao_record_stats(4, L.dao_record(16, None, 1, None, None, 1), 1, None) == 1
+    assert L.dao_record_stats(4, L.dao_record(16, None, 1, 1, None, None), 1, None) == 1
+    assert L.dao_record_stats(0, None, None, None) == 1
+
+
+def test_solve_workspace_holds_two_phases(L):
+    """The size dao_solve_workspace_size reports covers two phases for every
+    per-trajectory system (any solve may be asked for them), and only the
+    queue for the neural field; n = 0 gives the one-phase minimum."""
+    ids = (L.SYSTEMS["lorenz63"], 0, 0)
+    base = L.dao_solve_workspace_size(*ids, 0)
+    assert L.dao_solve_workspace_size(*ids, 1000) >= base + 1000 * (2 * 3 + 2 + 9) * 8
+    assert L.dao_solve_workspace_size(L.SYSTEMS["mlp"], 0, 1, 1000) == \
+        L.dao_solve_workspace_size(L.SYSTEMS["mlp"], 0, 1, 0)

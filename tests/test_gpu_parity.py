@@ -502,11 +502,10 @@ def test_gradient_with_the_minimum_workspace(dao, name, n, s_cap):
                           ("lorenz63", 200, 64, True, False, 100000),
                           ("lorenz63", 200, 1024, True, False, 150),
                           ("lorenz63", 200, 1024, True, False, 40)])
-def test_two_phase_solve_equals_one_phase(dao, name, n, s_cap, record_t, states, max_steps,
-                                          monkeypatch):
+def test_two_phase_solve_equals_one_phase(dao, name, n, s_cap, record_t, states, max_steps):
     # Large ensembles are solved in two phases (64 probe attempts per
     # trajectory, then the unfinished ones longest-predicted first);
-    # DAO_SOLVE_PHASES forces either.  Every trajectory takes the same
+    # the solve's phases argument forces either.  Every trajectory takes the same
     # attempts: record, counts, statuses and final states equal bit for bit,
     # also when the record fills (s_cap 64), when the attempt cap ends
     # trajectories in phase 2 (150) or in phase 1 (40), and with recorded
@@ -517,9 +516,9 @@ def test_two_phase_solve_equals_one_phase(dao, name, n, s_cap, record_t, states,
     y0 = torch.tensor(w.y0, device=DEV)
     out = {}
     for mode in ("1", "2"):
-        monkeypatch.setenv("DAO_SOLVE_PHASES", mode)
         rec, y1 = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=s_cap,
-                            record_t=record_t, record_states=states, max_steps=max_steps)
+                            record_t=record_t, record_states=states, max_steps=max_steps,
+                            phases=int(mode))
         torch.cuda.synchronize()
         out[mode] = (rec, y1)
     (r1, y1a), (r2, y1b) = out["1"], out["2"]
@@ -542,7 +541,7 @@ def test_two_phase_solve_equals_one_phase(dao, name, n, s_cap, record_t, states,
 
 @pytest.mark.parametrize("name,n,s_cap", [("lorenz63", 500, 1024), ("robertson", 300, 1024),
                                           ("loghalo", 300, 4096), ("lotka_volterra", 64 * 5 + 9, 256)])
-def test_two_phase_solve_with_sensitivities_equals_one_phase(dao, name, n, s_cap, monkeypatch):
+def test_two_phase_solve_with_sensitivities_equals_one_phase(dao, name, n, s_cap):
     # The solve with forward sensitivities suspends and resumes S with the
     # state: both ways give the same S, record and final states bit for bit.
     w = di.make(name, n)
@@ -551,9 +550,8 @@ def test_two_phase_solve_with_sensitivities_equals_one_phase(dao, name, n, s_cap
     y0 = torch.tensor(w.y0, device=DEV)
     out = {}
     for mode in ("1", "2"):
-        monkeypatch.setenv("DAO_SOLVE_PHASES", mode)
         out[mode] = dao.solve_sens(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol,
-                                   s_cap=s_cap)
+                                   s_cap=s_cap, phases=int(mode))
         torch.cuda.synchronize()
     (r1, y1a, Sa), (r2, y1b, Sb) = out["1"], out["2"]
     assert torch.equal(r1.count, r2.count) and torch.equal(r1.status, r2.status)
