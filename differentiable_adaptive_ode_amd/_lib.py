@@ -64,6 +64,9 @@ def _load():
     L.dao_grad_ordered.argtypes = [I, I, I, I64, P, P, ctypes.POINTER(dao_record), I64, P, P, P,
                                    P, SZ, P]
     L.dao_grad_ordered.restype = I
+    L.dao_grad_noalloc.argtypes = [I, I, I, I64, P, P, ctypes.POINTER(dao_record), I64, P, P, P,
+                                   P]
+    L.dao_grad_noalloc.restype = I
     L.dao_solve_sens.argtypes = [I, I, I, I64, P, P, D, D, ctypes.POINTER(dao_tol), P,
                                  ctypes.POINTER(dao_record), P, P, SZ, P]
     L.dao_solve_sens.restype = I
@@ -189,6 +192,13 @@ def dao_grad_ordered(system, method, dtype, n, theta, y0, rec, s_max, dLdy1, dLd
 
 def dao_record_stats(n, rec, out, stream):
     return lib.dao_record_stats(n, ctypes.byref(rec) if rec is not None else None, out, stream)
+
+
+def dao_grad_noalloc(system, method, dtype, n, theta, y0, rec, s_max, dLdy1, dLdtheta, dLdy0,
+                     stream):
+    return lib.dao_grad_noalloc(system, method, dtype, n, theta, y0,
+                                ctypes.byref(rec) if rec is not None else None, s_max, dLdy1,
+                                dLdtheta, dLdy0, stream)
 
 
 def dao_sqerr_cotangent(dtype, n, d, d_used, y1, target, scale, out, stream):

@@ -741,6 +741,43 @@ const Impl* find_impl(int sys, int method, int dtype) {
 
 bool is_fin(double x) { return std::isfinite(x); }
 
+// ------------------------------------------- static scratch (dao_grad_noalloc)
+// For callers that cannot allocate device memory: the gradient's workspace
+// (queue counter, step-count histogram, trajectory order, per-wavefront
+// tiles) in one file-scope device array.  Every GPU the library runs on holds
+// its own copy until the process ends.  In host code `scratch` only names the
+// symbol: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is ever passed to kernels.
+constexpr size_t SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+// The device address of `scratch` on the current device (looked up on the
+// first call per device), or null with the error set.
+void* scratch_address(dao_status* st) {
+  static std::mutex mu;
+  static std::vector<void*> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = check_hip(e, "dao_grad_noalloc: hipGetDevice");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *st = check_hip(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "dao_grad_noalloc: hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  *st = DAO_OK;
+  return addr[dev];
+}
+
 }  // namespace
 
 // ================================================================== C ABI
@@ -945,7 +982,8 @@ namespace {
 dao_status grad_call(const char* fn, int mode, dao_system sys, dao_method method, dao_dtype dtype,
                      int64_t n, const void* theta, const void* y0, const dao_record* rec,
                      int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     void* workspace, size_t workspace_bytes, void* stream,
+                     bool static_scratch = false) {
   g_err[0] = 0;
   if (!sys_ok(sys)) return fail(DAO_EINVAL, "%s: unknown system %d", fn, (int)sys);
   if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
@@ -969,6 +1007,17 @@ dao_status grad_call(const char* fn, int mode, dao_system sys, dao_method method
       return fail(DAO_EUNSUPPORTED, "%s: recorded states (rec->y) are not provided for the neural field", fn);
   }
   const size_t need = dao_grad_workspace_min(sys, method, dtype, n, s_max);
+  if (static_scratch) {
+    if (need > SCRATCH_BYTES)
+      return fail(DAO_EWORKSPACE,
+                  "%s: n = %lld with s_max = %lld needs at least %zu bytes of scratch, more than "
+                  "the library's static %zu bytes (use dao_grad with a workspace)",
+                  fn, (long long)n, (long long)s_max, need, SCRATCH_BYTES);
+    dao_status st = DAO_OK;
+    workspace = scratch_address(&st);
+    if (!workspace) return st;
+    workspace_bytes = SCRATCH_BYTES;
+  }
   if (!workspace || workspace_bytes < need)
     return fail(DAO_EWORKSPACE, "%s: workspace needs at least %zu bytes", fn, need);
   return im->grad(mode, n, theta, y0, rec, s_max, dLdy1, dLdtheta, dLdy0, workspace,
@@ -1000,6 +1049,14 @@ dao_status dao_grad_ordered(dao_system sys, dao_method method, dao_dtype dtype, 
                             void* workspace, size_t workspace_bytes, void* stream) {
   return grad_call("dao_grad_ordered", GRAD_RUN, sys, method, dtype, n, theta, y0, rec, s_max,
                    dLdy1, dLdtheta, dLdy0, workspace, workspace_bytes, stream);
+}
+
+dao_status dao_grad_noalloc(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                            const void* theta, const void* y0, const dao_record* rec,
+                            int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0,
+                            void* stream) {
+  return grad_call("dao_grad_noalloc", GRAD_ORDER | GRAD_RUN, sys, method, dtype, n, theta, y0,
+                   rec, s_max, dLdy1, dLdtheta, dLdy0, nullptr, 0, stream, true);
 }
 
 size_t dao_grad_at_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,

@@ -216,6 +216,31 @@ dao_status dao_grad_ordered(dao_system sys, dao_method method, dao_dtype dtype, 
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dao_grad_noalloc -- dao_grad for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same gradient, bit for bit for the per-trajectory
+ * systems (the neural field's shared-weight sum to binary32 rounding), with
+ * its scratch (queue counter, step-count histogram, trajectory order and
+ * per-wavefront tiles) in a static device array of the library instead of a
+ * workspace argument.  Arguments, results and errors as dao_grad.
+ *   Limit: the array is 64 MiB (67,108,864 bytes) per GPU, held from the
+ *   library's first use on that GPU until the process ends.  A call whose
+ *   dao_grad_workspace_min(sys, method, dtype, n, s_max) exceeds it returns
+ *   DAO_EWORKSPACE before anything is enqueued; below that, the gradient runs
+ *   as many trajectory groups at once as the array holds (fewer than with
+ *   the full dao_grad_workspace_size, so it may be slower).
+ *   The call allocates nothing: no hipMalloc, no hipFree.  Its first call on
+ *   a GPU looks up the array's device address (hipGetSymbolAddress).
+ *   Every call on one GPU shares that GPU's array and leaves its contents
+ *   behind (each call clears what it counts with first): calls that overlap
+ *   in time on one GPU, on any streams, race and give wrong results.
+ */
+dao_status dao_grad_noalloc(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
+                            const void* theta, const void* y0, const dao_record* rec,
+                            int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0,
+                            void* stream);
+
+/*
  * dao_grad_at -- the discrete-adjoint gradient of a loss that also holds the
  * states at requested times (the application paper, arXiv 2609.28458,
  * Sec. 2.3, fits residuals at observation times):

@@ -213,3 +213,17 @@ def test_solve_workspace_holds_two_phases(L):
     assert L.dao_solve_workspace_size(*ids, 1000) >= base + 1000 * (2 * 3 + 2 + 9) * 8
     assert L.dao_solve_workspace_size(L.SYSTEMS["mlp"], 0, 1, 1000) == \
         L.dao_solve_workspace_size(L.SYSTEMS["mlp"], 0, 1, 0)
+
+
+def test_grad_noalloc_rejects_before_touching_the_device(L):
+    """More scratch than the static array holds is refused on the host, with
+    the sizes in the message; argument errors come first, as in dao_grad."""
+    rec = L.dao_record(1 << 20, None, 1, 1, None, 1)
+    ids = (L.SYSTEMS["lorenz63"], 0, 0)
+    assert L.dao_grad_noalloc(*ids, 64, 1, 1, rec, 1 << 20, 1, None, None, None) == \
+        L.DAO_EWORKSPACE
+    msg = L.dao_last_error()
+    assert "dao_grad_noalloc" in msg and "static" in msg
+    assert L.dao_grad_noalloc(*ids, 64, 1, 1, rec, -1, 1, None, None, None) == L.DAO_EINVAL
+    assert L.dao_grad_noalloc(*ids, 64, None, 1, rec, 8, 1, None, None, None) == L.DAO_EINVAL
+    assert L.dao_grad_noalloc(9, 0, 0, 64, 1, 1, rec, 8, 1, None, None, None) == L.DAO_EINVAL
