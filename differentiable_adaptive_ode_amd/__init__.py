@@ -7,8 +7,8 @@ that record (arXiv 2609.02876, Sec. 2.1 and 3.1).  The work runs in the HIP
 library libdao.so behind the C ABI of include/dao.h; this package binds it.
 """
 from ._lib import DaoError, dao_version  # noqa: F401  (loads libdao.so or raises)
-from .api import (Record, cotangent, grad, grad_at, grad_order, sens, solve,  # noqa: F401
-                  solve_sens, states_at)
+from .api import (Record, Workspace, cotangent, grad, grad_at, grad_order, sens,  # noqa: F401
+                  solve, solve_sens, states_at)
 
 __all__ = ["solve", "solve_sens", "sens", "states_at", "grad", "grad_at", "grad_order",
-           "cotangent", "Record", "DaoError", "dao_version"]
+           "cotangent", "Record", "Workspace", "DaoError", "dao_version"]

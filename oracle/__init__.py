@@ -66,6 +66,9 @@ def lib():
         for name in ("oracle_solve_f64", "oracle_solve_f32", "oracle_solve_plain_f64",
                      "oracle_solve_plain_f32"):
             getattr(L, name).argtypes = [I, I, I64, P, P, D, D, D, D, D, I64, I64, P, P, P, P, P, P, I]
+        for name in ("oracle_trace_f32", "oracle_trace_f64"):
+            getattr(L, name).argtypes = [I, I, P, P, D, D, D, D, I64, I64, P, P, P, P, P]
+            getattr(L, name).restype = I64
         L.oracle_replay_f64.argtypes = [I, I, I64, P, P, P, P, I64, P, I]
         L.oracle_replay_cs.argtypes = [I, I, I64, P, P, P, P, D, P, P, I64, P, P]
         L.oracle_grad_f64.argtypes = [I, I, I64, P, P, P, P, I64, P, P, P, P, I]
@@ -138,6 +141,27 @@ def solve(system, method, theta, y0, t0, t1, rtol, atol, dt0=0.0, max_steps=1000
     if rc != 0:
         raise ValueError("oracle_solve: invalid argument")
     return dict(y1=y1, count=count, nrej=nrej, status=status, t=t_rec, h=h_rec)
+
+
+def trace(system, method, theta, y0, t0, t1, rtol, atol, s_cap=4096, dtype="f64", cap=100000):
+    """Per-attempt trace of ONE trajectory's solve (theta [p] or the shared
+    weights, y0 [d]): dict of arrays h, msq, fac (0.9 msq^(-1/q) before
+    truncation and clamping), floor (the mean square of the error
+    combination's term sizes over sc, the scale of its rounding), acc."""
+    np_t = np.float64 if dtype == "f64" else np.float32
+    theta = np.ascontiguousarray(theta, dtype=np_t)
+    y0 = np.ascontiguousarray(y0, dtype=np_t)
+    out = {k: np.zeros(cap) for k in ("h", "msq", "fac", "floor")}
+    acc = np.zeros(cap, np.int32)
+    fn = lib().oracle_trace_f32 if dtype == "f32" else lib().oracle_trace_f64
+    m = fn(SYSTEMS[system], METHODS[method], _p(theta), _p(y0), float(t0), float(t1),
+           float(rtol), float(atol), int(s_cap), int(cap), _p(out["h"]), _p(out["msq"]),
+           _p(out["fac"]), _p(out["floor"]), _p(acc))
+    if m < 0:
+        raise ValueError("oracle_trace: invalid argument")
+    res = {k: v[:m] for k, v in out.items()}
+    res["acc"] = acc[:m].astype(bool)
+    return res
 
 
 def replay(system, method, theta, y0, count, h, nthreads=1):

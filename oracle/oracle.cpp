@@ -531,7 +531,7 @@ void lu_solve(int d, const T* LU, const int* piv, const T* rp, const T* b, T* x)
 // ----------------------------------------------------------------------------
 template <class T, bool PLAIN = false>
 void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* ynew, T* F2, T* err,
-                bool unscaled = false) {
+                bool unscaled = false, double* kabs = nullptr) {
   T J[MAXD * MAXD], W[MAXD * MAXD], rp[MAXD];
   int piv[MAXD];
   jac(sys, th, y, J);
@@ -556,6 +556,9 @@ void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* yn
     r[c] = fma3(T(-2.0), k1[c] - F0[c], t2);
   }
   lu_solve<T, PLAIN>(d, W, piv, rp, r, k3);
+  if (kabs)  // magnitudes of the error combination's terms (trace only)
+    for (int c = 0; c < d; ++c)
+      kabs[c] = std::fabs(rv(k1[c])) + 2.0 * std::fabs(rv(k2[c])) + std::fabs(rv(k3[c]));
   if (unscaled) {  // without the factor h/6 (folded into the solve's error weights)
     for (int c = 0; c < d; ++c) err[c] = fma3(T(-2.0), k2[c], k1[c]) + k3[c];
     return;
@@ -714,9 +717,26 @@ struct SolveOut {
   int32_t count, nrej, status;
 };
 
+// Optional per-attempt trace of a solve (test instrumentation; it reads the
+// solve's values and changes none of them): the attempted step, the mean
+// square msq, the controller factor 0.9 msq^(-1/q) before truncation and
+// clamping, the decision, and the rounding floor of msq: the mean square of
+// s * kabs_c / sc_c, with kabs_c = sum_j |b_j - bhat_j| |k_j,c| (Tsit5) or
+// |k1| + 2|k2| + |k3| (Rosenbrock23), the size of the terms the embedded
+// error cancels (times the unit roundoff it bounds the estimate's rounding).
+struct Trace {
+  double* h;
+  double* msq;
+  double* fac;
+  double* floor_;
+  int32_t* acc;
+  int64_t cap, n;
+};
+
 template <class T, bool PLAIN = false>
 SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1, T rtol, T atol,
-                      T dt0, int64_t max_steps, int64_t s_cap, T* y1, T* t_rec, T* h_rec) {
+                      T dt0, int64_t max_steps, int64_t s_cap, T* y1, T* t_rec, T* h_rec,
+                      Trace* trace = nullptr) {
   const int d = SYS_D[sys];
   const int order = (method == M_TSIT5) ? 5 : 2;
   const int q = (method == M_TSIT5) ? 10 : 6;  // msq^(-1/q) = err^(-1/(order+1))
@@ -737,10 +757,16 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
       T hs = last ? (t1 - t) : h;
       if (!finite_(hs)) { out.status = ST_NONFINITE; break; }
       if (!(t + hs > t)) { out.status = ST_DTMIN; break; }
+      double kabs[MAXD];
       if (method == M_TSIT5) {
         tsit5_step(sys, th, d, y, hs, k, ynew, e, !PLAIN);
+        if (trace)
+          for (int c = 0; c < d; ++c) {
+            kabs[c] = 0.0;
+            for (int j = 0; j < 7; ++j) kabs[c] += std::fabs(TS_BT[j]) * std::fabs(rv(k[j][c]));
+          }
       } else {
-        ros23_step<T, PLAIN>(sys, th, d, y, hs, k[0], ynew, F2, e, !PLAIN);
+        ros23_step<T, PLAIN>(sys, th, d, y, hs, k[0], ynew, F2, e, !PLAIN, trace ? kabs : nullptr);
       }
       const T es = (method == M_TSIT5) ? hs : hs / T(6.0);
       T w[MAXD];
@@ -749,6 +775,19 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
         w[c] = es / sc[c];
       }
       T msq = PLAIN ? plain_msq(d, e, sc) : error_msq(d, e, w);
+      if (trace && trace->n < trace->cap) {
+        const int64_t i = trace->n++;
+        double fl = 0.0;
+        for (int c = 0; c < d; ++c) {
+          const double r = rv(es) * kabs[c] / rv(sc[c]);
+          fl += r * r;
+        }
+        trace->h[i] = rv(hs);
+        trace->msq[i] = rv(msq);
+        trace->fac[i] = (msq == T(0)) ? 10.0 : rv(T(0.9) * ctrl_power<T, PLAIN>(msq, q));
+        trace->floor_[i] = fl / d;
+        trace->acc[i] = finite_(msq) && msq <= T(1.0);
+      }
       if (!finite_(msq)) { out.status = ST_NONFINITE; break; }
       if (msq <= T(1.0)) {
         if (n >= s_cap) { out.status = ST_CAPACITY; break; }
@@ -886,6 +925,23 @@ int solve_impl(int sys, int method, int64_t n, const T* theta, const T* y0, doub
   return 0;
 }
 
+// Per-attempt trace of one trajectory's solve (see Trace), binary32 or
+// binary64: theta [p] (or the 4740 shared weights), y0 [d].  Returns the
+// number of attempts traced (at most cap), or -1 for an invalid argument.
+template <class T>
+int64_t trace_impl(int sys, int method, const T* theta, const T* y0, double t0, double t1,
+                   double rtol, double atol, int64_t s_cap, int64_t cap, double* h, double* msq,
+                   double* fac, double* floor_, int32_t* acc) {
+  if (!valid_sys(sys, method) || !(t1 >= t0) || cap < 0) return -1;
+  const int d = SYS_D[sys];
+  Trace tr{h, msq, fac, floor_, acc, cap, 0};
+  std::vector<T> hr(s_cap > 0 ? s_cap : 1), tr_t(s_cap > 0 ? s_cap : 1);
+  T y1[MAXD];
+  (void)d;
+  solve_one<T>(sys, method, theta, y0, T(t0), T(t1), T(rtol), T(atol), T(0), 100000, s_cap, y1,
+               tr_t.data(), hr.data(), &tr);
+  return tr.n;
+}
 }  // namespace
 
 // ============================================================================
@@ -952,6 +1008,19 @@ int oracle_solve_plain_f32(int sys, int method, int64_t n, const float* theta, c
                            int nthreads) {
   return solve_impl<float, true>(sys, method, n, theta, y0, t0, t1, rtol, atol, dt0, max_steps,
                                  s_cap, y1, count, nrej, status, t_rec, h_rec, nthreads);
+}
+
+int64_t oracle_trace_f32(int sys, int method, const float* theta, const float* y0, double t0,
+                         double t1, double rtol, double atol, int64_t s_cap, int64_t cap,
+                         double* h, double* msq, double* fac, double* floor_, int32_t* acc) {
+  return trace_impl<float>(sys, method, theta, y0, t0, t1, rtol, atol, s_cap, cap, h, msq, fac,
+                           floor_, acc);
+}
+int64_t oracle_trace_f64(int sys, int method, const double* theta, const double* y0, double t0,
+                         double t1, double rtol, double atol, int64_t s_cap, int64_t cap,
+                         double* h, double* msq, double* fac, double* floor_, int32_t* acc) {
+  return trace_impl<double>(sys, method, theta, y0, t0, t1, rtol, atol, s_cap, cap, h, msq, fac,
+                            floor_, acc);
 }
 
 // Replay in binary64 on a given mesh (h_rec [n][s_cap], count [n]).
