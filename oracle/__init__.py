@@ -82,6 +82,7 @@ def lib():
         L.oracle_count_solve.argtypes = [I, I, P, P, D, D, D, D, I64, P]
         L.oracle_count_replay_step.argtypes = [I, I, P, P, D]
         L.oracle_count_replay_step.restype = I64
+        L.oracle_count_grad_step.argtypes = [I, I, P, P, D, P]
         L.oracle_ctrl_root_f64.argtypes = [D, I]
         L.oracle_ctrl_root_f64.restype = D
         L.oracle_ctrl_root_f32.argtypes = [ctypes.c_float, I]
@@ -307,6 +308,19 @@ def count_replay_step(system, method, theta, y, h):
     y = np.ascontiguousarray(y, dtype=np.float64)
     return int(lib().oracle_count_replay_step(SYSTEMS[system], METHODS[method], _p(theta), _p(y),
                                               float(h)))
+
+
+def count_grad_step(system, method, theta, y, h):
+    """Tally of one gradient step's parts: (replay step flops, reverse-mode
+    flops of that step on the tape: 2 per local partial of a variable plus the
+    partials' own quotients and tanh derivatives)."""
+    theta = np.ascontiguousarray(theta, dtype=np.float64)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.zeros(2, np.int64)
+    rc = lib().oracle_count_grad_step(SYSTEMS[system], METHODS[method], _p(theta), _p(y),
+                                      float(h), _p(out))
+    assert rc == 0
+    return int(out[0]), int(out[1])
 
 
 def ctrl_root(x, q, dtype="f64"):

@@ -116,8 +116,13 @@ inline Rev rleaf(double v) {
 inline Rev operator+(Rev a, Rev b) { return rnode(a.v + b.v, a.id, 1.0, b.id, 1.0); }
 inline Rev operator-(Rev a, Rev b) { return rnode(a.v - b.v, a.id, 1.0, b.id, -1.0); }
 inline Rev operator*(Rev a, Rev b) { return rnode(a.v * b.v, a.id, b.v, b.id, a.v); }
+// Flops spent forming local partial derivatives (the flop tally of reverse
+// mode, oracle_count_grad_step): 1/b for a quotient's numerator, -q/b for its
+// denominator, 1 - t^2 for tanh.  Products and sums have free partials.
+thread_local int64_t g_partial_flops = 0;
 inline Rev operator/(Rev a, Rev b) {
   double q = a.v / b.v;
+  g_partial_flops += (a.id >= 0 ? 1 : 0) + (b.id >= 0 ? 1 : 0);
   return rnode(q, a.id, 1.0 / b.v, b.id, -q / b.v);
 }
 inline Rev operator-(Rev a) { return rnode(-a.v, a.id, -1.0); }
@@ -126,6 +131,7 @@ inline Rev fma3(Rev a, Rev b, Rev c) {
 }
 inline Rev tanh_(Rev a) {
   double t = std::tanh(a.v);
+  if (a.id >= 0) g_partial_flops += 2;
   return rnode(t, a.id, 1.0 - t * t);
 }
 inline double rv(Rev a) { return a.v; }
@@ -1342,6 +1348,34 @@ int64_t oracle_count_replay_step(int sys, int method, const double* theta, const
   g_flops = 0;
   replay_one<Cnt>(sys, method, th.data(), y, 1, hh, yS);
   return g_flops;
+}
+
+// Tally of the reverse mode of one replay step from y with step h: the step is
+// recorded on the tape (theta and y as inputs) and its reverse sweep costs one
+// multiply-add (2 flops) per local partial derivative of a variable, plus
+// the flops that form the partials themselves (quotients, tanh).  out[0] =
+// the replay step (counting scalar), out[1] = the reverse sweep.
+int oracle_count_grad_step(int sys, int method, const double* theta, const double* y0, double h,
+                           int64_t* out) {
+  if (!valid_sys(sys, method)) return 1;
+  const int d = SYS_D[sys], p = SYS_P[sys];
+  out[0] = oracle_count_replay_step(sys, method, theta, y0, h);
+  Tape tape;
+  g_tape = &tape;
+  std::vector<Rev> rth(p);
+  Rev ry[MAXD], ryS[MAXD];
+  for (int i = 0; i < p; ++i) rth[i] = rleaf(theta[i]);
+  for (int c = 0; c < d; ++c) ry[c] = rleaf(y0[c]);
+  const int64_t leaves = (int64_t)tape.nodes.size();
+  g_partial_flops = 0;
+  const double hh[1] = {h};
+  replay_one<Rev>(sys, method, rth.data(), ry, 1, hh, ryS);
+  int64_t edges = 0;
+  for (int64_t i = leaves; i < (int64_t)tape.nodes.size(); ++i)
+    for (int j = 0; j < 3; ++j) edges += tape.nodes[i].p[j] >= 0 ? 1 : 0;
+  out[1] = 2 * edges + g_partial_flops;
+  g_tape = nullptr;
+  return 0;
 }
 
 // The controller power x^(-1/q) of the solve (for tests of its accuracy).
