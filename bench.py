@@ -2,15 +2,22 @@
 discrete-adjoint gradient of a full ensemble (arXiv 2609.02876 Sec. 2.1,
 3.1), inputs resident in HBM.
 
-Workload: Lorenz-63, 65,536 trajectories with per-trajectory (sigma, rho,
-beta) ~ U[9,11] x U[20,30] x U[2,3], y0 ~ N(0,1)^3 + (1,1,20), t in [0, 2],
-Tsit5 rtol 1e-8 atol 1e-10, fp64, loss sum 1/2 |y(2) - target|^2.
+Headline workload (the largest benchmark ensemble): 1,048,576 orbits in the
+flattened logarithmic halo (arXiv 2609.28458 Sec. 3), per-trajectory (v0, Rc,
+q) ~ U[0.9,1.1] x U[0.1,0.3] x U[0.8,1.0], positions ~ N(0,1)^3, velocities
+~ N(0,0.5)^3, t in [0, 50], Tsit5 rtol 1e-8 atol 1e-10, fp64, loss on the
+final positions.  The line also carries every benchmark ensemble at its own
+size (`configs`: Lotka-Volterra 256, Lorenz-63 65,536, the neural field
+16,384 in fp32, Robertson 262,144 with Rosenbrock23, the orbits), each with
+its solve and gradient times, their fractions of the FP64 vector (or FP32
+matrix) peak, algorithmic HBM bytes and the grade against min(peak, AI x HBM
+bandwidth), and the oracle timed on the host cores.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload lorenz63]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload loghalo]
+                    [--configs 0|1] [--no-cpu-baseline]
 
-Prints one JSON line.  `value` = whole-path trajectories/s (solve + gradient);
-solves/s and gradient trajectories/s are reported next to it.
+Prints one JSON line.  `value` = whole-path trajectories/s (solve + gradient)
+of the headline ensemble; solves/s and gradient trajectories/s beside it.
 """
 from __future__ import annotations
 
@@ -103,12 +110,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="lorenz63")
+    ap.add_argument("--workload", default="loghalo",
+                    help="the headline ensemble (default: the largest, the log-halo orbits)")
     ap.add_argument("--n", type=int, default=None,
                     help="trajectories (default: the workload's own ensemble size); e.g. the "
                          "Lotka-Volterra system at n = 1048576, where its 256-trajectory "
                          "ensemble cannot fill the chip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--configs", type=int, choices=(0, 1), default=1,
+                    help="gradient mode: also measure every benchmark ensemble at its own size "
+                         "(the per-config block of the line)")
+    ap.add_argument("--config-steps", type=int, default=10,
+                    help="timed steps of each other ensemble in the per-config block")
     ap.add_argument("--mode", choices=("gradient", "sens", "replay_sens", "states", "grad_at"),
                     default="gradient",
                     help="gradient: solve with record + replay-adjoint gradient (default); "
@@ -181,55 +194,119 @@ def copy_calibration(mib, dev):
         del src, dst
 
 
-def cpu_baseline(w, sample, s_cap):
-    """The oracle, as is, on the host cores: solve + gradient of a sample."""
+# The five benchmark ensembles, in order (Lotka-Volterra 256; Lorenz-63 65,536;
+# the neural field 16,384 in binary32; Robertson 262,144 with Rosenbrock23;
+# the log-halo orbits 1,048,576).  The headline is the largest, the orbits.
+CONFIGS = ["lotka_volterra", "lorenz63", "mlp", "robertson", "loghalo"]
+HBM_PEAK = 8.0e12  # bytes/s, MI355X HBM3E (published)
+# oracle samples per workload: (solve, gradient, one-thread) trajectories
+CPU_SAMPLES = {"lotka_volterra": (256, 256, 256), "lorenz63": (65536, 32768, 1024),
+               "mlp": (16384, 4096, 128), "robertson": (131072, 32768, 1024),
+               "loghalo": (16384, 4096, 64), "hires": (8192, 2048, 64),
+               "lorenz63_spread": (32768, 8192, 512)}
+
+
+def cpu_threads():
+    """Host threads the oracle baseline runs on: the threads this process may
+    use, at most 16 (a one-GPU machine's CPU share)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, min(avail, 16))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, s_cap, n_solve, n_grad, n_single):
+    """The oracle, as is, on the host cores: its solve with record and its
+    tape reverse-mode gradient timed separately on samples of the ensemble
+    (the gradient on the sample's own oracle mesh) on the machine's CPU share, and
+    both again on one thread for the time per trajectory."""
     import numpy as np
 
     import dao_inputs as di
     import oracle
 
-    nthreads = min(os.cpu_count() or 1, 16)
-    ws = di.subset(w, np.arange(min(sample, w.n)))
-    t0 = time.perf_counter()
-    r = oracle.solve(ws.system, ws.method, ws.theta, ws.y0, ws.t0, ws.t1, ws.rtol, ws.atol,
-                     s_cap=s_cap, dtype=ws.dtype, nthreads=nthreads)
-    lam = di.cotangent(ws, r["y1"])
-    oracle.grad(ws.system, ws.method, ws.theta.astype(np.float64), ws.y0.astype(np.float64),
-                r["count"], r["h"].astype(np.float64), lam, nthreads=nthreads)
-    dt = time.perf_counter() - t0
-    return {"value": ws.n / dt, "unit": "trajectories/s (solve + gradient)", "cores": nthreads,
-            "kind": "oracle",
-            "sample": f"first {ws.n} of the {w.n} {w.name} trajectories, full solve + tape "
-                      f"reverse-mode gradient ({ws.dtype} solve, f64 gradient), {dt:.2f} s wall "
-                      f"on {nthreads} threads"}
+    T = cpu_threads()
+
+    def run(n, threads, grad=True):
+        ws = di.subset(w, np.arange(min(n, w.n)))
+        t0 = time.perf_counter()
+        r = oracle.solve(ws.system, ws.method, ws.theta, ws.y0, ws.t0, ws.t1, ws.rtol, ws.atol,
+                         s_cap=s_cap, dtype=ws.dtype, nthreads=threads)
+        ts = time.perf_counter() - t0
+        tg = None
+        if grad:
+            lam = di.cotangent(ws, r["y1"].astype(np.float64))
+            t0 = time.perf_counter()
+            oracle.grad(ws.system, ws.method, ws.theta.astype(np.float64),
+                        ws.y0.astype(np.float64), r["count"], r["h"].astype(np.float64), lam,
+                        nthreads=threads)
+            tg = time.perf_counter() - t0
+        return ws.n, ts, tg
+
+    ns, ts, _ = run(n_solve, T, grad=False)
+    ng, _, tg = run(n_grad, T)
+    n1, ts1, tg1 = run(n_single, 1)
+    solve_rate, grad_rate = ns / ts, ng / tg
+    return {"value": 1.0 / (1.0 / solve_rate + 1.0 / grad_rate),
+            "unit": "trajectories/s (solve with record + replay-adjoint gradient)",
+            "cores": T, "kind": "oracle", "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+            "solves_per_s": solve_rate, "grad_trajectories_per_s": grad_rate,
+            "single_thread_us_per_trajectory": {"solve": ts1 / n1 * 1e6, "grad": tg1 / n1 * 1e6},
+            "sample": (f"{w.name}: solve of the first {ns} of {w.n} trajectories "
+                       f"({ts:.2f} s), tape gradient of the first {ng} on their oracle mesh "
+                       f"({tg:.2f} s), {T} threads; one thread: {n1} trajectories")}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; the ensemble would shard by "
-              "trajectory index across GPUs, with no exchange for per-trajectory parameters "
-              "and one all-reduce of the shared weights otherwise. Use --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
+def solve_bytes(w, steps_total, with_t):
+    """Algorithmic HBM bytes of one solve call: parameters and initial states
+    read, final states, counts and statuses written, one record row (h, and
+    t when kept) per accepted step."""
+    r = 8 if w.dtype == "f64" else 4
+    p = w.theta.shape[0]
+    th = p * r if w.system == "mlp" else p * r * w.n
+    return th + w.n * (2 * w.d * r + 12) + steps_total * r * (2 if with_t else 1)
 
+
+def grad_bytes(w, steps_total, waves):
+    """Algorithmic HBM bytes of one ordered gradient call: per trajectory the
+    parameters, initial state, cotangent, count, status and order read and the
+    two gradients written; per accepted step h read once and the stored state
+    written and read back (with the step's h: d + 1 values each way); the
+    neural field keeps d values per step and adds each wavefront's partial
+    weight gradient, written and read by the reduction."""
+    r = 8 if w.dtype == "f64" else 4
+    p = w.theta.shape[0]
+    if w.system == "mlp":
+        per_traj = 3 * w.d * r + 12
+        return (p * r + w.n * per_traj + steps_total * (r + 2 * w.d * r)
+                + waves * p * r * 2 + p * r)
+    per_traj = (2 * p + 3 * w.d) * r + 12
+    return w.n * per_traj + steps_total * (r + 2 * (w.d + 1) * r)
+
+
+def measure_gradient(w, args, steps, warmup, graph):
+    """One step = solve with record + loss cotangent + sort + replay-adjoint
+    gradient, timed `steps` times after `warmup` (and, with graph, replayed as
+    one captured HIP graph).  Returns the workload's measurement record."""
     import numpy as np
     import torch
 
-    import dao_inputs as di
     import differentiable_adaptive_ode_amd as dao
     from differentiable_adaptive_ode_amd import api
 
     dev = torch.device("cuda:0")
-    w = di.make(args.workload, args.n)
-    if args.mode in ("sens", "replay_sens") and w.name not in JVP_SUM:
-        # HIRES is differentiated with respect to its initial state (its rate
-        # constants are fixed), so its forward sensitivities are not benchmarked
-        raise SystemExit(f"bench: no forward-sensitivity benchmark for {w.name}")
-    if args.mode == "sens":
-        return bench_sens(args, w)
-    if args.mode in ("replay_sens", "states", "grad_at"):
-        return bench_on_record(args, w)
     cfg = WORKLOADS[w.name]
     s_cap = cfg["s_cap"]
     th = torch.tensor(w.theta, device=dev)
@@ -248,7 +325,6 @@ def main():
     dth = torch.empty_like(th)
     dy0 = torch.empty_like(y0)
     wsp = api.Workspace()
-
     s_max = [s_cap]
 
     # One step: solve with record | loss cotangent | order the trajectories by
@@ -273,18 +349,18 @@ def main():
     copy_calibration(args.copy_calibration, dev)
 
     # The record's longest row sizes the gradient's checkpoint scratch.  Every
-    # step solves the same inputs, so it is read once, after the first solve.
+    # step solves the same inputs, so it is read once, after the first solve
+    # (the record summary, read back before the timed steps).
     rec = step(events())
-    torch.cuda.synchronize()
-    s_max[0] = int(rec.count.max().item())
-    for _ in range(max(args.warmup - 1, 0)):
+    s_max[0] = rec.stats_host()["s_max"]
+    for _ in range(max(warmup - 1, 0)):
         rec = step(events())
     torch.cuda.synchronize()
 
-    evs = [events() for _ in range(args.steps)]
+    evs = [events() for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         rec = step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -294,11 +370,11 @@ def main():
 
     # The same step captured once as a HIP graph and replayed: identical launches
     # on the same buffers, without the host's per-launch overhead.  Every
-    # replay must reproduce the eager step's outputs bit for bit.
-    ms_eager = wall / args.steps * 1e3
+    # replay must reproduce the eager step's outputs.
+    ms_eager = wall / steps * 1e3
     launch = "eager"
     graph_note = None
-    if args.graph:
+    if graph:
         class _NoEvent:
             def record(self):
                 pass
@@ -322,14 +398,14 @@ def main():
             with torch.cuda.graph(g):
                 step(noev)
             torch.cuda.synchronize()
-            for _ in range(max(args.warmup, 1)):
+            for _ in range(max(warmup, 1)):
                 g.replay()
             torch.cuda.synchronize()
             if not same():
                 raise RuntimeError("a graph replay differs from the eager step")
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            for _ in range(args.steps):
+            for _ in range(steps):
                 g.replay()
             torch.cuda.synchronize()
             wall_graph = time.perf_counter() - t0
@@ -348,76 +424,151 @@ def main():
         raise SystemExit(f"bench: some trajectories failed (status counts {bad.tolist()})")
     attempts = int((cnt + nrej).sum())
     steps_total = int(cnt.sum())
-    ms = wall / args.steps * 1e3
     ts, tg, tk = float(np.mean(t_solve)), float(np.mean(t_grad)), float(np.mean(t_kern))
     fl_solve = w.n * cfg["init"] + attempts * cfg["att"] + steps_total
     # with recorded states the gradient does no forward replay
     fl_grad = steps_total * (cfg["grad"] - (cfg["replay"] if states else 0))
     peak = cfg["peak"]
-    # The roofline is taken on the dominant kernel's own launches: the solve
-    # call (its queue reset and the solve kernel), or the ordered gradient call
-    # (its queue reset, the gradient kernel and, for the shared-weight field,
-    # the two reduction kernels); the sort before it is timed apart.
-    dom = "grad" if tk >= ts else "solve"
-    ach = (fl_grad / tk) if dom == "grad" else (fl_solve / ts)
-    # Measured HBM bytes per call of the dominant kernel (rocprofv3 FETCH_SIZE +
-    # WRITE_SIZE, copy-calibrated), only if taken on the current kernel sources.
+    waves = min(-(-w.n // 16), 1024)  # the neural gradient's wavefronts (one per SIMD)
+    by_solve = solve_bytes(w, steps_total, with_t)
+    by_grad = grad_bytes(w, steps_total, waves)
+
+    def part(fl, by, t):
+        # graded against the attainable rate min(peak, AI x HBM bandwidth)
+        ai = fl / by
+        attain = min(peak, ai * HBM_PEAK)
+        return {"ms": t * 1e3, "alg_flops": fl, "tflops": fl / t * 1e-12,
+                "frac_peak": fl / t / peak, "alg_bytes": by, "alg_hbm_gbps": by / t * 1e-9,
+                "hbm_frac": by / t / HBM_PEAK, "arith_intensity": ai,
+                "bound": "hbm" if ai * HBM_PEAK < peak else cfg["bound"],
+                "attainable_tflops": attain * 1e-12, "graded_frac": fl / t / attain}
+
+    # Measured HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE,
+    # copy-calibrated), only if taken on the current kernel sources.
     from differentiable_adaptive_ode_amd.profiling import load_traffic
 
     tr = load_traffic(w.name, w.n)
-    traffic = None
-    for key in (f"{dom}_kernel", f"{dom}_phased_kernel"):  # one call, one or two launches
-        if tr is not None and traffic is None and key in tr["kernels"]:
-            traffic = tr["kernels"][key]["hbm_bytes"]
-    dtype_name = {"f64": "f64", "f32": "f32"}[w.dtype]
+    psolve, pgrad = part(fl_solve, by_solve, ts), part(fl_grad, by_grad, tk)
+    for kind, pk in (("solve", psolve), ("grad", pgrad)):
+        pk["measured_hbm_bytes"] = None
+        for key in (f"{kind}_kernel", f"{kind}_phased_kernel"):  # one or two launches
+            if tr is not None and pk["measured_hbm_bytes"] is None and key in tr["kernels"]:
+                pk["measured_hbm_bytes"] = tr["kernels"][key]["hbm_bytes"]
     out = {
-        "metric": "gradient trajectories/s (replay adjoint) + solves/s at 1 GPU; % of roofline",
-        "value": w.n / (wall / args.steps),
-        "unit": "trajectories/s (solve with record + replay-adjoint gradient)",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "launch": launch,
-        "ms_per_step_eager": ms_eager,
-        "launch_note": graph_note,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dtype_name,
-        "data": "synthetic",
-        "config": {"workload": f"{w.name} ensemble", "n_trajectories": w.n, "method": w.method,
-                   "t_span": [w.t0, w.t1], "rtol": w.rtol, "atol": w.atol, "s_cap": s_cap,
-                   "recorded_states": states, "record_t": with_t},
-        "solves_per_s": w.n / ts,
-        "grad_trajectories_per_s": w.n / tg,
-        "solve_ms": ts * 1e3,
-        "grad_ms": tg * 1e3,
-        "grad_kernel_ms": tk * 1e3,
+        "workload": f"{w.name} ensemble", "n_trajectories": w.n, "method": w.method,
+        "dtype": w.dtype, "t_span": [w.t0, w.t1], "rtol": w.rtol, "atol": w.atol,
+        "s_cap": s_cap, "s_max": s_max[0], "recorded_states": states, "record_t": with_t,
+        "ms_per_step": wall / steps * 1e3, "launch": launch, "ms_per_step_eager": ms_eager,
+        "launch_note": graph_note, "steps": steps, "warmup": warmup,
+        "trajectories_per_s": w.n / (wall / steps),
+        "solves_per_s": w.n / ts, "grad_trajectories_per_s": w.n / tg,
+        "solve_ms": ts * 1e3, "grad_ms": tg * 1e3, "grad_kernel_ms": tk * 1e3,
         "grad_order_ms": (tg - tk) * 1e3,
-        "accepted_steps_mean": float(cnt.mean()),
-        "accepted_steps_max": int(cnt.max()),
+        "accepted_steps_mean": float(cnt.mean()), "accepted_steps_max": int(cnt.max()),
         "attempts_total": attempts,
         # divergence: the work rate per lane-attempt, and what a lockstep code
         # would issue instead (groups of 64 consecutive trajectories for the
         # solve, each group running as long as its longest member; the
         # gradient's groups are sorted by step count first)
         "divergence": _divergence(cnt, nrej, attempts, steps_total, ts, tk),
-        "solve_tflops": fl_solve / ts * 1e-12,
-        "grad_tflops": fl_grad / tk * 1e-12,
-        "roofline": {"bound": cfg["bound"], "kernel": f"{dom}_kernel",
-                     "launch_ms": (tk if dom == "grad" else ts) * 1e3, "achieved": ach * 1e-12,
-                     "peak": peak * 1e-12, "unit": "TFLOP/s", "frac": ach / peak,
-                     "traffic": traffic,
-                     "traffic_unit": "HBM bytes per call (two launches for a two-phase solve)"},
-        "roofline_solve_frac": fl_solve / ts / peak,
-        "roofline_grad_frac": fl_grad / tk / peak,
+        "solve": psolve, "grad": pgrad, "peak_tflops": peak * 1e-12, "peak_kind": cfg["bound"],
         # issued vs algorithmic flops per call (profile counters), or null
         "issue": {"solve": _issued(tr, "solve_kernel", fl_solve, w.dtype == "f64"),
                   "grad": _issued(tr, "grad_kernel", fl_grad, w.dtype == "f64")},
     }
+    del bufs, wsp, th, y0, tgt, y1, lam, dth, dy0, rec
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def roofline_of(m):
+    """The bench line's roofline object: the dominant kernel of the step (the
+    solve call or the ordered gradient call), graded against its own bound:
+    FP64 vector (or FP32 matrix) flops at or above the ridge AI = peak / HBM
+    bandwidth, HBM bytes below it."""
+    dom = "grad" if m["grad_kernel_ms"] >= m["solve_ms"] else "solve"
+    p = m[dom]
+    if p["bound"] == "hbm":
+        ach, peak, unit = p["alg_hbm_gbps"], HBM_PEAK * 1e-9, "GB/s"
+    else:
+        ach, peak, unit = p["tflops"], m["peak_tflops"], "TFLOP/s"
+    return {"bound": p["bound"], "kernel": f"{dom}_kernel", "launch_ms": p["ms"],
+            "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+            "traffic": p["measured_hbm_bytes"],
+            "traffic_unit": "HBM bytes per call (two launches for a two-phase solve)",
+            "alg_bytes": p["alg_bytes"], "arith_intensity": p["arith_intensity"],
+            "graded_frac": p["graded_frac"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; the ensemble would shard by "
+              "trajectory index across GPUs, with no exchange for per-trajectory parameters "
+              "and one all-reduce of the shared weights otherwise. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import dao_inputs as di
+
+    w = di.make(args.workload, args.n)
+    if args.mode in ("sens", "replay_sens") and w.name not in JVP_SUM:
+        # HIRES is differentiated with respect to its initial state (its rate
+        # constants are fixed), so its forward sensitivities are not benchmarked
+        raise SystemExit(f"bench: no forward-sensitivity benchmark for {w.name}")
+    if args.mode == "sens":
+        return bench_sens(args, w)
+    if args.mode in ("replay_sens", "states", "grad_at"):
+        return bench_on_record(args, w)
+
+    head = measure_gradient(w, args, args.steps, args.warmup, bool(args.graph))
+    print(f"bench: {w.name} n={w.n} measured ({head['ms_per_step']:.3f} ms/step)",
+          file=sys.stderr, flush=True)
+    out = {
+        "metric": "gradient trajectories/s (replay adjoint) + solves/s at 1 GPU; % of roofline",
+        "value": head["trajectories_per_s"],
+        "unit": "trajectories/s (solve with record + replay-adjoint gradient)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "launch": head["launch"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": head["workload"], "n_trajectories": w.n, "method": w.method,
+                   "t_span": [w.t0, w.t1], "rtol": w.rtol, "atol": w.atol,
+                   "s_cap": head["s_cap"]},
+        "solves_per_s": head["solves_per_s"],
+        "grad_trajectories_per_s": head["grad_trajectories_per_s"],
+        "solve_ms": head["solve_ms"], "grad_ms": head["grad_ms"],
+        "roofline": roofline_of(head),
+        "roofline_solve_frac": head["solve"]["frac_peak"],
+        "roofline_grad_frac": head["grad"]["frac_peak"],
+        "headline": head,
+    }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample or cfg["cpu_n"], s_cap)
+        samp = CPU_SAMPLES[w.name] if args.cpu_sample is None else (args.cpu_sample,) * 3
+        out["cpu_baseline"] = cpu_baseline(w, WORKLOADS[w.name]["s_cap"], *samp)
+        print("bench: cpu baseline done", file=sys.stderr, flush=True)
+    if args.configs and args.n is None:
+        # every benchmark ensemble at its own size: the same step and figures
+        per = {}
+        for name in CONFIGS:
+            wc = w if name == w.name else di.make(name)
+            m = head if name == w.name else measure_gradient(wc, args, args.config_steps,
+                                                             args.warmup, bool(args.graph))
+            rec = {k: m[k] for k in ("n_trajectories", "method", "dtype", "ms_per_step",
+                                      "launch", "trajectories_per_s", "solves_per_s",
+                                      "grad_trajectories_per_s", "solve_ms", "grad_ms",
+                                      "grad_kernel_ms", "accepted_steps_mean",
+                                      "accepted_steps_max", "solve", "grad", "issue")}
+            rec["roofline"] = roofline_of(m)
+            if not args.no_cpu_baseline:
+                rec["cpu_baseline"] = (out["cpu_baseline"] if name == w.name else
+                                       cpu_baseline(wc, WORKLOADS[name]["s_cap"],
+                                                    *CPU_SAMPLES[name]))
+            per[name] = rec
+            print(f"bench: config {name} done ({m['ms_per_step']:.3f} ms/step)", file=sys.stderr,
+                  flush=True)
+        out["configs"] = per
     print(json.dumps(out), flush=True)
 
 
