@@ -19,6 +19,8 @@ the five benchmark ensembles):
 * ``lorenz63_spread`` the Lorenz ensemble with its difficulty spread (the divergence stress
                       test): rho log-uniform on [20, 1000], so that step counts range over
                       about an order of magnitude; sigma, beta, y0 and targets as ``lorenz63``
+* ``lorenz63_vern7``, ``loghalo_vern7``  the Lorenz and orbit ensembles (same draws)
+                      integrated with the Verner 7(6) pair
 * ``hires``           HIRES, 8 species; the twelve rate constants at their nominal values for
                       every trajectory (the ensemble carries no free rate constant); the two
                       nonzero components of the standard initial state (1, 0, ..., 0, 0.0057)
@@ -76,7 +78,16 @@ def glorot(rng, fan_out, fan_in):
     return rng.uniform(-lim, lim, size=(fan_out, fan_in))
 
 
+VERN7_OF = {"lorenz63_vern7": "lorenz63", "loghalo_vern7": "loghalo"}
+
+
 def make(name: str, n: int | None = None) -> Workload:
+    if name in VERN7_OF:
+        # the same ensemble (same draws) integrated with the Verner 7(6) pair
+        base = make(VERN7_OF[name], n)
+        return Workload(name, base.system, "vern7", base.dtype, base.n, base.t0, base.t1,
+                        base.rtol, base.atol, base.theta, base.y0, base.target, base.loss,
+                        dict(base.extra))
     n = DEFAULT_N[name] if n is None else int(n)
     rng = _rng(name)
     if name == "decay":

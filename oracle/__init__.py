@@ -34,7 +34,7 @@ _SRC = os.path.join(_HERE, "oracle.cpp")
 
 SYSTEMS = {"decay": 0, "lotka_volterra": 1, "lorenz63": 2, "mlp": 3, "robertson": 4, "loghalo": 5,
            "hires": 6}
-METHODS = {"tsit5": 0, "rosenbrock23": 1}
+METHODS = {"tsit5": 0, "rosenbrock23": 1, "vern7": 2}
 STATUS = {0: "ok", 1: "max_steps", 2: "nonfinite", 3: "dt_underflow", 4: "capacity"}
 
 _lib = None
@@ -63,6 +63,7 @@ def lib():
         L.oracle_dims.argtypes = [I, P, P, P]
         L.oracle_tsit5_table.argtypes = [P, P, P]
         L.oracle_ros23_consts.argtypes = [P, P]
+        L.oracle_vern7_table.argtypes = [P, P, P, P]
         for name in ("oracle_solve_f64", "oracle_solve_f32", "oracle_solve_plain_f64",
                      "oracle_solve_plain_f32"):
             getattr(L, name).argtypes = [I, I, I64, P, P, D, D, D, D, D, I64, I64, P, P, P, P, P, P, I]
@@ -108,6 +109,14 @@ def tsit5_table():
     bt = np.zeros(7)
     lib().oracle_tsit5_table(_p(c), _p(A), _p(bt))
     return c, A, A[6].copy(), bt
+
+
+def vern7_table():
+    """(c, A, b, bhat) of the Verner 7(6) pair as the oracle holds them."""
+    c, b, bh = np.zeros(10), np.zeros(10), np.zeros(10)
+    A = np.zeros((10, 10))
+    lib().oracle_vern7_table(_p(c), _p(A), _p(b), _p(bh))
+    return c, A, b, bh
 
 
 def ros23_consts():

@@ -31,7 +31,8 @@
 //   * Rosenbrock23: Shampine & Reichelt, SIAM J. Sci. Comput. 18 (1997) 1-22
 //     (the ode23s triple, autonomous form).
 //   * Controller: integral controller fac = 0.9 * err^(-1/(q+1)) with
-//     q+1 = 5 (Tsit5) or 3 (Rosenbrock23), clamped to [0.2, 10], no growth on
+//     q+1 = 5 (Tsit5), 7 (Verner 7) or 3 (Rosenbrock23), the lower order of
+//     the pair plus one, clamped to [0.2, 10], no growth on
 //     the step after a rejection.  The test works on the mean square
 //     msq = err^2, so the power is msq^(-1/10) or msq^(-1/6); it is evaluated
 //     by the fixed rule of ctrl_root() below (relative error under 1e-7, only
@@ -43,6 +44,8 @@
 //   * The last step is clipped to land exactly on t1.
 //   * Arithmetic contract: fused multiply-adds appear exactly where fma3() is
 //     written below; build with -ffp-contract=off.
+//   * Verner 7(6) pair: Verner's published ten-stage table (the pages name
+//     the pair; they print no coefficients).
 // ============================================================================
 #include <algorithm>
 #include <cmath>
@@ -251,6 +254,36 @@ const double TS_BT[7] = {-0.00178001105222577714, -0.0008164344596567469, 0.0078
                          -0.1447110071732629,     0.5823571654525552,     -0.45808210592918697,
                          0.015151515151515152};
 
+// Verner's "most efficient" 7(6) pair (J. H. Verner, Numerical Algorithms 53
+// (2010) 383-396, and his published coefficient tables): ten stages, the
+// seventh-order weights b use stages 1 and 4-9, the sixth-order weights bhat
+// stages 1, 4-7 and 10; stage 10 serves only the error estimate, and the
+// pair is not FSAL (f(y_new) is a new evaluation).  VN_BT = b - bhat, the
+// error weights.  Structurally zero entries are skipped in every sum.
+const double VN_C[10] = {0.0, 0.005, 0.10888888888888888, 0.16333333333333333, 0.4555,
+                         0.6095094489978381, 0.884, 0.925, 1.0, 1.0};
+const double VN_A[10][10] = {
+    {0, 0, 0, 0, 0, 0, 0, 0, 0, 0},
+    {0.005, 0, 0, 0, 0, 0, 0, 0, 0, 0},
+    {-1.07679012345679, 1.185679012345679, 0, 0, 0, 0, 0, 0, 0, 0},
+    {0.04083333333333333, 0, 0.1225, 0, 0, 0, 0, 0, 0, 0},
+    {0.6389139236255726, 0, -2.455672638223657, 2.272258714598084, 0, 0, 0, 0, 0, 0},
+    {-2.6615773750187572, 0, 10.804513886456137, -8.3539146573962, 0.820487594956657, 0, 0, 0, 0,
+     0},
+    {6.067741434696772, 0, -24.711273635911088, 20.427517930788895, -1.9061579788166472,
+     1.006172249242068, 0, 0, 0, 0},
+    {12.054670076253203, 0, -49.75478495046899, 41.142888638604674, -4.461760149974004,
+     2.042334822239175, -0.09834843665406107, 0, 0, 0},
+    {10.138146522881808, 0, -42.6411360317175, 35.76384003992257, -4.3480228403929075,
+     2.0098622683770357, 0.3487490460338272, -0.27143900510483127, 0, 0},
+    {-45.030072034298676, 0, 187.3272437654589, -154.02882369350186, 18.56465306347536,
+     -7.141809679295079, 1.3088085781613787, 0, 0, 0}};
+const double VN_B[10] = {0.04715561848627222, 0, 0, 0.25750564298434153, 0.26216653977412624,
+                         0.15216092656738558, 0.4939969170032485, -0.29430311714032503,
+                         0.08131747232495111, 0};
+const double VN_BH[10] = {0.044608606606341174, 0, 0, 0.26716403785713727, 0.22010183001772932,
+                          0.2188431703143157, 0.22898717054112028, 0, 0, 0.02029518466335628};
+
 // Rosenbrock23 (Shampine & Reichelt 1997): gamma = d = 1/(2+sqrt 2),
 // e32 = 6 + sqrt 2.
 const double R23_D = 1.0 / (2.0 + 1.4142135623730951);
@@ -262,7 +295,8 @@ const double R23_E32 = 6.0 + 1.4142135623730951;
 // ----------------------------------------------------------------------------
 enum { SYS_DECAY = 0, SYS_LV = 1, SYS_LORENZ = 2, SYS_MLP = 3, SYS_ROBERTSON = 4, SYS_LOGHALO = 5,
        SYS_HIRES = 6, SYS_COUNT = 7 };
-enum { M_TSIT5 = 0, M_ROS23 = 1 };
+enum { M_TSIT5 = 0, M_ROS23 = 1, M_VERN7 = 2 };
+const int MAXK = 10;  // stage derivatives kept per step (Verner 7's ten)
 enum { ST_OK = 0, ST_MAXSTEPS = 1, ST_NONFINITE = 2, ST_DTMIN = 3, ST_CAPACITY = 4 };
 
 const int SYS_D[SYS_COUNT] = {1, 2, 3, 4, 3, 6, 8};
@@ -464,7 +498,7 @@ bool jac(int sys, const T* th, const T* y, T* J) {
 // folds h into its error weights, see error_msq).
 // ----------------------------------------------------------------------------
 template <class T>
-void tsit5_step(int sys, const T* th, int d, const T* y, T h, T k[7][MAXD], T* ynew, T* err,
+void tsit5_step(int sys, const T* th, int d, const T* y, T h, T (*k)[MAXD], T* ynew, T* err,
                 bool unscaled = false) {
   T Y[MAXD];
   for (int i = 1; i < 7; ++i) {
@@ -482,6 +516,45 @@ void tsit5_step(int sys, const T* th, int d, const T* y, T h, T k[7][MAXD], T* y
   for (int c = 0; c < d; ++c) {
     T acc = T(TS_BT[0]) * k[0][c];
     for (int j = 1; j < 7; ++j) acc = fma3(T(TS_BT[j]), k[j][c], acc);
+    err[c] = unscaled ? acc : h * acc;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// One Verner 7(6) step (the explicit Runge-Kutta step of Section 2.1 with
+// Verner's ten-stage pair).  k[0] holds f(y) on entry.  Fills k[1..8] and
+// ynew = y + h sum_j b_j k_j; if err != nullptr also k[9] (stage 10) and the
+// embedded error sum_j (b_j - bhat_j) k_j, times h unless unscaled.  Sums run
+// over the table's nonzero entries, j ascending.
+// ----------------------------------------------------------------------------
+template <class T>
+void vern7_step(int sys, const T* th, int d, const T* y, T h, T (*k)[MAXD], T* ynew, T* err,
+                bool unscaled = false) {
+  T Y[MAXD];
+  auto stage = [&](int i) {
+    for (int c = 0; c < d; ++c) {
+      T acc = T(VN_A[i][0]) * k[0][c];
+      for (int j = 1; j < i; ++j)
+        if (VN_A[i][j] != 0.0) acc = fma3(T(VN_A[i][j]), k[j][c], acc);
+      Y[c] = fma3(h, acc, y[c]);
+    }
+    rhs(sys, th, Y, k[i]);
+  };
+  for (int i = 1; i < 9; ++i) stage(i);
+  for (int c = 0; c < d; ++c) {
+    T acc = T(VN_B[0]) * k[0][c];
+    for (int j = 1; j < 9; ++j)
+      if (VN_B[j] != 0.0) acc = fma3(T(VN_B[j]), k[j][c], acc);
+    ynew[c] = fma3(h, acc, y[c]);
+  }
+  if (err == nullptr) return;
+  stage(9);
+  for (int c = 0; c < d; ++c) {
+    T acc = T(VN_B[0] - VN_BH[0]) * k[0][c];
+    for (int j = 1; j < 10; ++j) {
+      const double bt = VN_B[j] - VN_BH[j];
+      if (bt != 0.0) acc = fma3(T(bt), k[j][c], acc);
+    }
     err[c] = unscaled ? acc : h * acc;
   }
 }
@@ -593,7 +666,8 @@ inline float trunc_bits(float x) {  // keep 8 explicit mantissa bits
 
 inline Cnt trunc_bits(Cnt x) { return Cnt(trunc_bits(x.v)); }
 
-// Controller power x^(-1/q), q = 10 (Tsit5) or 6 (Rosenbrock23), for x > 0.
+// Controller power x^(-1/q), q = 10 (Tsit5), 14 (Verner 7) or 6
+// (Rosenbrock23), for x > 0.
 // x is first clamped to a range outside which 0.9 x^(-1/q) lies beyond the
 // controller's limits [0.2, 10] anyway.  With x = m 2^e (m in [1, 2)) and
 // e = q a + b (0 <= b < q):
@@ -608,15 +682,18 @@ const double ROOT10_C[8] = {0.9602644780153649,     -0.03200878522189435,  0.005
 const double ROOT6_C[8] = {0.9346552216460542,     -0.05192523185937651,    0.010097959271667333,
                            -0.0024314560515976726, 0.0006347021852295785,   -0.0001753744494318341,
                            6.143024330877807e-05,  -1.8571447204984547e-05};
+const double ROOT14_C[8] = {0.971453564346184, -0.02312982604893814, 0.004130813507010568,
+                            -0.0009509085609683622, 0.00024095017603375496, -6.506922272280208e-05,
+                            2.2232410031470908e-05, -6.6171886469205804e-06};
 const double EXP2N_C[7] = {0.7071067811579441,     -0.24506454511279616,  0.042466448938030865,
                            -0.004905842513716687,  0.00042506069534188184, -2.9611051419632863e-05,
                            1.7091800607644192e-06};
 
 template <class T>
 T ctrl_root(T x, int q) {
-  const double* rc = (q == 10) ? ROOT10_C : ROOT6_C;
-  const T lo = (q == 10) ? T(1e-12) : T(1e-8);
-  const T hi = (q == 10) ? T(1e8) : T(1e5);
+  const double* rc = (q == 10) ? ROOT10_C : (q == 14) ? ROOT14_C : ROOT6_C;
+  const T lo = (q == 10) ? T(1e-12) : (q == 14) ? T(1e-15) : T(1e-8);
+  const T hi = (q == 10) ? T(1e8) : (q == 14) ? T(1e10) : T(1e5);
   x = std::min(std::max(x, lo), hi);
   int e = 0;
   const T mh = std::frexp(x, &e);  // x = mh 2^e, mh in [1/2, 1): m = 2 mh in [1, 2)
@@ -744,10 +821,12 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
                       T dt0, int64_t max_steps, int64_t s_cap, T* y1, T* t_rec, T* h_rec,
                       Trace* trace = nullptr) {
   const int d = SYS_D[sys];
-  const int order = (method == M_TSIT5) ? 5 : 2;
-  const int q = (method == M_TSIT5) ? 10 : 6;  // msq^(-1/q) = err^(-1/(order+1))
+  const int order = (method == M_TSIT5) ? 5 : (method == M_VERN7) ? 7 : 2;
+  // msq^(-1/q) = err^(-1/(p+1)), p the lower order of the pair: 4 (Tsit5 5(4)),
+  // 6 (Verner 7(6)), 2 (Rosenbrock23, whose estimate is of third order)
+  const int q = (method == M_TSIT5) ? 10 : (method == M_VERN7) ? 14 : 6;
   SolveOut<T> out = {0, 0, ST_OK};
-  T y[MAXD], ynew[MAXD], e[MAXD], sc[MAXD], k[7][MAXD], F2[MAXD];
+  T y[MAXD], ynew[MAXD], e[MAXD], sc[MAXD], k[MAXK][MAXD], F2[MAXD];
   for (int c = 0; c < d; ++c) y[c] = y0[c];
   T t = t0;
   if (t1 > t0) {
@@ -771,10 +850,18 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
             kabs[c] = 0.0;
             for (int j = 0; j < 7; ++j) kabs[c] += std::fabs(TS_BT[j]) * std::fabs(rv(k[j][c]));
           }
+      } else if (method == M_VERN7) {
+        vern7_step(sys, th, d, y, hs, k, ynew, e, !PLAIN);
+        if (trace)
+          for (int c = 0; c < d; ++c) {
+            kabs[c] = 0.0;
+            for (int j = 0; j < 10; ++j)
+              kabs[c] += std::fabs(VN_B[j] - VN_BH[j]) * std::fabs(rv(k[j][c]));
+          }
       } else {
         ros23_step<T, PLAIN>(sys, th, d, y, hs, k[0], ynew, F2, e, !PLAIN, trace ? kabs : nullptr);
       }
-      const T es = (method == M_TSIT5) ? hs : hs / T(6.0);
+      const T es = (method == M_ROS23) ? hs / T(6.0) : hs;
       T w[MAXD];
       for (int c = 0; c < d; ++c) {
         sc[c] = fma3(rtol, std::max(abs_(y[c]), abs_(ynew[c])), atol);
@@ -804,6 +891,8 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
         for (int c = 0; c < d; ++c) y[c] = ynew[c];
         if (method == M_TSIT5)
           for (int c = 0; c < d; ++c) k[0][c] = k[6][c];
+        else if (method == M_VERN7)
+          rhs(sys, th, y, k[0]);  // not FSAL: f at the new state
         else
           for (int c = 0; c < d; ++c) k[0][c] = F2[c];
         T fac = (msq == T(0)) ? T(10.0) : trunc_bits(T(0.9) * ctrl_power<T, PLAIN>(msq, q));
@@ -831,13 +920,15 @@ template <class T>
 void replay_one(int sys, int method, const T* th, const T* y0, int32_t count, const double* h_rec,
                 T* yS) {
   const int d = SYS_D[sys];
-  T y[MAXD], ynew[MAXD], k[7][MAXD];
+  T y[MAXD], ynew[MAXD], k[MAXK][MAXD];
   for (int c = 0; c < d; ++c) y[c] = y0[c];
   for (int32_t n = 0; n < count; ++n) {
     T h = T(h_rec[n]);
     rhs(sys, th, y, k[0]);
     if (method == M_TSIT5)
       tsit5_step<T>(sys, th, d, y, h, k, ynew, nullptr);
+    else if (method == M_VERN7)
+      vern7_step<T>(sys, th, d, y, h, k, ynew, nullptr);
     else
       ros23_step<T>(sys, th, d, y, h, k[0], ynew, nullptr, nullptr);
     for (int c = 0; c < d; ++c) y[c] = ynew[c];
@@ -899,8 +990,8 @@ void parallel_for(int64_t n, int nthreads, F fn) {
 
 bool valid_sys(int sys, int method) {
   if (sys < 0 || sys >= SYS_COUNT) return false;
-  if (method != M_TSIT5 && method != M_ROS23) return false;
-  if (method == M_ROS23 && sys == SYS_MLP) return false;
+  if (method != M_TSIT5 && method != M_ROS23 && method != M_VERN7) return false;
+  if (method != M_TSIT5 && sys == SYS_MLP) return false;
   return true;
 }
 
@@ -971,6 +1062,15 @@ void oracle_tsit5_table(double* c, double* A, double* bt) {
     c[i] = TS_C[i];
     bt[i] = TS_BT[i];
     for (int j = 0; j < 7; ++j) A[i * 7 + j] = TS_A[i][j];
+  }
+}
+
+void oracle_vern7_table(double* c, double* A, double* b, double* bhat) {
+  for (int i = 0; i < 10; ++i) {
+    c[i] = VN_C[i];
+    b[i] = VN_B[i];
+    bhat[i] = VN_BH[i];
+    for (int j = 0; j < 10; ++j) A[i * 10 + j] = VN_A[i][j];
   }
 }
 
@@ -1090,11 +1190,13 @@ int oracle_states_at_f64(int sys, int method, int64_t n, const double* theta, co
   const bool shared = (sys == SYS_MLP);
   parallel_for(n, nthreads, [&](int, int64_t lo, int64_t hi) {
     std::vector<double> th(p);
-    double y[MAXD], ys[MAXD], k[7][MAXD], ynew[MAXD];
+    double y[MAXD], ys[MAXD], k[MAXK][MAXD], ynew[MAXD];
     auto step = [&](const double* from, double h, double* to) {
       rhs(sys, th.data(), from, k[0]);
       if (method == M_TSIT5)
         tsit5_step<double>(sys, th.data(), d, from, h, k, to, nullptr);
+      else if (method == M_VERN7)
+        vern7_step<double>(sys, th.data(), d, from, h, k, to, nullptr);
       else
         ros23_step<double>(sys, th.data(), d, from, h, k[0], to, nullptr, nullptr);
     };
@@ -1239,13 +1341,15 @@ int oracle_grad_at_f64(int sys, int method, int64_t n, const double* theta, cons
       Tape tape;
       g_tape = &tape;
       std::vector<Rev> rth(p);
-      Rev ry0[MAXD], y[MAXD], ys[MAXD], ynew[MAXD], k[7][MAXD];
+      Rev ry0[MAXD], y[MAXD], ys[MAXD], ynew[MAXD], k[MAXK][MAXD];
       for (int i = 0; i < p; ++i) rth[i] = rleaf(theta[i * n + kk]);
       for (int c = 0; c < d; ++c) ry0[c] = y[c] = rleaf(y0[c * n + kk]);
       auto step = [&](const Rev* from, double h, Rev* to) {
         rhs(sys, rth.data(), from, k[0]);
         if (method == M_TSIT5)
           tsit5_step<Rev>(sys, rth.data(), d, from, Rev(h), k, to, nullptr);
+        else if (method == M_VERN7)
+          vern7_step<Rev>(sys, rth.data(), d, from, Rev(h), k, to, nullptr);
         else
           ros23_step<Rev>(sys, rth.data(), d, from, Rev(h), k[0], to, nullptr, nullptr);
       };
@@ -1300,10 +1404,12 @@ int oracle_step_f64(int sys, int method, const double* th, const double* y, doub
                     double* ynew, double* err) {
   if (!valid_sys(sys, method)) return 1;
   const int d = SYS_D[sys];
-  double k[7][MAXD], F2[MAXD];
+  double k[MAXK][MAXD], F2[MAXD];
   rhs(sys, th, y, k[0]);
   if (method == M_TSIT5)
     tsit5_step(sys, th, d, y, h, k, ynew, err);
+  else if (method == M_VERN7)
+    vern7_step(sys, th, d, y, h, k, ynew, err);
   else
     ros23_step(sys, th, d, y, h, k[0], ynew, F2, err);
   return 0;
@@ -1323,7 +1429,7 @@ int oracle_count_solve(int sys, int method, const double* theta, const double* y
   g_flops = 0;
   rhs(sys, th.data(), y, f0);
   initial_step(sys, th.data(), d, y, f0, Cnt(t1 - t0), Cnt(rtol), Cnt(atol),
-               method == M_TSIT5 ? 5 : 2);
+               method == M_TSIT5 ? 5 : method == M_VERN7 ? 7 : 2);
   out[1] = g_flops;
   g_flops = 0;
   SolveOut<Cnt> o = solve_one<Cnt>(sys, method, th.data(), y, Cnt(t0), Cnt(t1), Cnt(rtol),

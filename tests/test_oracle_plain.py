@@ -34,6 +34,8 @@ SAMPLES = {
     "loghalo": (1024, 8192),
     "hires": (512, 4096),
     "lorenz63_spread": (1024, 2048),
+    "lorenz63_vern7": (2048, 1024),
+    "loghalo_vern7": (512, 8192),
 }
 
 

@@ -19,6 +19,7 @@ import dao_inputs as di
 
 TSIT = "tsit5"
 ROS = "rosenbrock23"
+VERN = "vern7"
 
 
 def R_poly(orc, z):
@@ -65,6 +66,36 @@ def test_decay_discrete_closed_form(orc):
         cont = w.y0[0, k] * np.exp(-w.theta[0, k] * w.t1)
         assert abs(r["y1"][0, k] - cont) <= 50 * (w.rtol * abs(cont) + w.atol)
         assert abs(dth[0, k] - (-w.t1 * cont)) <= 1e-5 * abs(w.t1 * cont)
+
+
+def test_decay_discrete_closed_form_vern7(orc):
+    # The same closed forms with Verner 7's stability polynomial.
+    c, A, b, bh = orc.vern7_table()
+
+    def R(z):
+        return 1.0 + z * b @ np.linalg.solve(np.eye(10) - z * A, np.ones(10))
+
+    def dR(z, eps=1e-30):
+        zc = complex(z, eps)
+        return (1.0 + zc * b @ np.linalg.solve(np.eye(10) - zc * A, np.ones(10))).imag / eps
+
+    w = di.make("decay", 32)
+    w.method = VERN
+    r = solve_w(orc, w)
+    assert np.all(r["status"] == 0)
+    dth, dy0, yS = orc.grad(w.system, w.method, w.theta, w.y0, r["count"], r["h"],
+                            np.ones((1, w.n)))
+    for k in range(w.n):
+        h = r["h"][k, :r["count"][k]]
+        z = -w.theta[0, k] * h
+        Rz = np.array([R(zz) for zz in z])
+        exact = w.y0[0, k] * np.prod(Rz)
+        dexact = exact * np.sum(-h * np.array([dR(zz) for zz in z]) / Rz)
+        assert yS[0, k] == pytest.approx(exact, rel=1e-13)
+        assert r["y1"][0, k] == yS[0, k]
+        assert dth[0, k] == pytest.approx(dexact, rel=1e-12)
+        cont = w.y0[0, k] * np.exp(-w.theta[0, k] * w.t1)
+        assert abs(r["y1"][0, k] - cont) <= 50 * (w.rtol * abs(cont) + w.atol)
 
 
 def test_record_mesh_invariants(orc):
@@ -240,6 +271,15 @@ def test_ros23_error_estimate_tracks_local_error(orc):
     assert abs(ratios[-1] - 1.0) < abs(ratios[0] - 1.0) + 1e-3
 
 
+def test_vern7_error_estimate_order(orc):
+    # e = h sum (b - bhat) k is O(h^7): halving h divides it by ~128.
+    th = np.array([1.0, 0.7, 0.9, 1.2])
+    y = np.array([1.3, 0.8])
+    e = [np.linalg.norm(orc.step("lotka_volterra", VERN, th, y, h)[1]) for h in (0.08, 0.04, 0.02)]
+    slopes = np.log2(np.array(e[:-1]) / np.array(e[1:]))
+    assert np.all(np.abs(slopes - 7.0) < 0.3), slopes
+
+
 def test_tsit5_error_estimate_order(orc):
     # e = h sum (b - bhat) k is O(h^5): halving h divides it by ~32.
     th = np.array([1.0, 0.7, 0.9, 1.2])
@@ -251,7 +291,8 @@ def test_tsit5_error_estimate_order(orc):
 
 @pytest.mark.parametrize("method,order,system", [(TSIT, 5, "lotka_volterra"),
                                                   (ROS, 2, "lotka_volterra"),
-                                                  (TSIT, 5, "loghalo")])
+                                                  (TSIT, 5, "loghalo"),
+                                                  (VERN, 7, "lotka_volterra")])
 def test_fixed_step_convergence_order(orc, method, order, system):
     # Global error of the fixed-step replay against a 20000-step reference.
     # Tsit5 approaches its asymptotic slope 5 from above at these step sizes.
@@ -260,12 +301,18 @@ def test_fixed_step_convergence_order(orc, method, order, system):
     nref = 20000
     ref = orc.replay(system, TSIT, w.theta, w.y0, np.array([nref]), np.full((1, nref), T / nref))
     errs = []
-    ns = (32, 64, 128, 256) if method == TSIT else (64, 128, 256, 512)
+    ns = {TSIT: (32, 64, 128, 256), ROS: (64, 128, 256, 512), VERN: (16, 24, 32, 48, 64)}[method]
     for n in ns:
         y = orc.replay(system, method, w.theta, w.y0, np.array([n]), np.full((1, n), T / n))
         errs.append(np.linalg.norm(y - ref))
-    slopes = np.log2(np.array(errs[:-1]) / np.array(errs[1:]))
-    if method == TSIT:
+    slopes = np.log2(np.array(errs[:-1]) / np.array(errs[1:])) / np.log2(
+        np.array(ns[1:]) / np.array(ns[:-1]))
+    if method == VERN:
+        # Verner's pair keeps its principal error coefficients small, so at
+        # the step sizes where the error is above rounding (1e-5 .. 1e-12) the
+        # slope is that of the next term, about 8; it is at least 7 and not 9.
+        assert np.all((slopes > order - 0.5) & (slopes < order + 1.6)), slopes
+    elif method == TSIT:
         assert np.all((slopes > 4.6) & (slopes < 6.2)), slopes
         assert abs(slopes[-1] - order) < 0.6, slopes
     else:
@@ -361,7 +408,8 @@ def test_mlp_constant_field(orc):
 # ---------------------------------------------------------------- derivative pins
 CASES = [("decay", TSIT), ("lotka_volterra", TSIT), ("lorenz63", TSIT), ("loghalo", TSIT),
          ("robertson", ROS), ("mlp", TSIT), ("lotka_volterra", ROS), ("lorenz63", ROS),
-         ("hires", ROS)]
+         ("hires", ROS), ("decay", VERN), ("lotka_volterra", VERN), ("lorenz63", VERN),
+         ("loghalo", VERN)]
 
 
 def _case(orc, system, method, n):

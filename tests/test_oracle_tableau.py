@@ -67,8 +67,9 @@ def residuals(A, b, max_order):
 
 
 def test_tree_counts():
-    # Number of rooted trees of order 1..5 is 1, 1, 2, 4, 9 (OEIS A000081).
-    assert [len(trees(p)) for p in range(1, 6)] == [1, 1, 2, 4, 9]
+    # Number of rooted trees of order 1..7 is 1, 1, 2, 4, 9, 20, 48 (OEIS
+    # A000081): 85 conditions up to order 7, 37 up to order 6.
+    assert [len(trees(p)) for p in range(1, 8)] == [1, 1, 2, 4, 9, 20, 48]
 
 
 def test_tsit5_row_sums_and_fsal(orc):
@@ -166,14 +167,14 @@ def test_tsit5_stability_function_from_table(orc):
         assert abs(_tsit5_R(orc, z) - np.exp(z)) < 1e-2 * abs(z) ** 6
 
 
-@pytest.mark.parametrize("q", [10, 6])
+@pytest.mark.parametrize("q", [10, 6, 14])
 def test_controller_power_matches_exact_power(orc, q):
     # The controller factor 0.9 * msq^(-1/q), clamped to [0.2, 10], is the
     # integral controller err^(-1/(order+1)) on the mean square msq = err^2.
     # The oracle evaluates the power by a polynomial rule; pin it to the exact
     # power inside its range, and check that the clamped range only cuts where
     # the clamped factor saturates anyway.
-    lo, hi = (1e-12, 1e8) if q == 10 else (1e-8, 1e5)
+    lo, hi = {10: (1e-12, 1e8), 6: (1e-8, 1e5), 14: (1e-15, 1e10)}[q]
     x = np.logspace(np.log10(lo), np.log10(hi), 4001)
     x = np.concatenate([x, x * (1 + 1e-9), np.nextafter(x, 0)])
     x = x[(x >= lo) & (x <= hi)]
@@ -187,3 +188,80 @@ def test_controller_power_matches_exact_power(orc, q):
     out = orc.ctrl_root(np.array([lo * 1e-3, hi * 1e3]), q)
     assert out[0] == orc.ctrl_root(np.array([lo]), q)[0]
     assert out[1] == orc.ctrl_root(np.array([hi]), q)[0]
+
+
+# --- Verner 7(6) --------------------------------------------------------------
+# The pages name the pair (the library paper's method list; the application
+# paper's precession arm runs on it) and print no coefficients; the oracle
+# holds Verner's published ten-stage table.  Pinned here by all 85 conditions
+# of order 7 on b, all 37 of order 6 on bhat (and bhat genuinely of order 6),
+# the structure of the table, and its stability polynomial.
+def test_vern7_structure(orc):
+    c, A, b, bh = orc.vern7_table()
+    assert np.max(np.abs(A.sum(axis=1) - c)) < 2e-14
+    assert np.all(np.triu(A) == 0.0)  # explicit
+    assert c[8] == 1.0 and c[9] == 1.0
+    assert b[1] == b[2] == b[9] == 0.0  # seventh order uses stages 1, 4-9
+    assert bh[1] == bh[2] == bh[7] == bh[8] == 0.0  # sixth order: 1, 4-7, 10
+    assert A[9, 7] == A[9, 8] == 0.0  # stage 10 needs only stages 1-7
+    assert not np.allclose(A[9], b)  # not FSAL: stage 10 is not the new state
+
+
+def test_vern7_seventh_order(orc):
+    c, A, b, bh = orc.vern7_table()
+    r = residuals(A, b, 7)
+    assert r.size == 85
+    assert np.max(np.abs(r)) < 1e-14
+
+
+def test_vern7_embedded_sixth_order(orc):
+    c, A, b, bh = orc.vern7_table()
+    r6 = residuals(A, bh, 6)
+    assert r6.size == 37
+    assert np.max(np.abs(r6)) < 1e-14
+    # ... and not seventh order, so the estimate b - bhat is O(h^7)
+    assert np.max(np.abs(residuals(A, bh, 7)[37:])) > 1e-5
+
+
+def test_vern7_order_conditions_catch_a_wrong_coefficient(orc):
+    # Planted mistakes in a copy of the table: each nonzero coefficient of A,
+    # b or bhat off in its 8th significant digit, or sign-flipped, breaks an
+    # order condition or a row sum.
+    c, A, b, bh = orc.vern7_table()
+    for i, j in itertools.product(range(10), range(10)):
+        if A[i, j] == 0.0:
+            continue
+        for bad in (A[i, j] * (1 + 1e-8), -A[i, j]):
+            A2 = A.copy()
+            A2[i, j] = bad
+            row = np.max(np.abs(A2.sum(axis=1) - c))
+            cond = max(np.max(np.abs(residuals(A2, b, 7))), np.max(np.abs(residuals(A2, bh, 6))))
+            assert max(row, cond) > 1e-12, (i, j)
+    for w, order in ((b, 7), (bh, 6)):
+        for j in np.flatnonzero(w):
+            for bad in (w[j] * (1 + 1e-8), -w[j]):
+                w2 = w.copy()
+                w2[j] = bad
+                assert np.max(np.abs(residuals(A, w2, order))) > 1e-12, j
+
+
+def test_vern7_stability_function_from_table(orc):
+    # the replay of y' = -theta y multiplies by the table's stability
+    # polynomial; seventh order: R(z) - exp(z) = O(z^8)
+    c, A, b, bh = orc.vern7_table()
+
+    def R(z):
+        return 1.0 + z * b @ np.linalg.solve(np.eye(10) - z * A, np.ones(10))
+
+    for z in (-0.01, -0.3, -1.0, -2.5):
+        ynew, _ = orc.step("decay", "vern7", [-z], [1.0], 1.0)
+        assert ynew[0] == pytest.approx(R(z), rel=2e-15)
+    for z in (-0.05, -0.1):
+        assert abs(R(z) - np.exp(z)) < 1e-3 * abs(z) ** 8
+    # the polynomial's coefficients b^T A^(j-1) 1 are 1/j! for j <= 7, and
+    # the eighth is not (order exactly 7 on the linear test equation)
+    v = np.ones(10)
+    for j in range(1, 8):
+        assert b @ v == pytest.approx(1.0 / np.prod(np.arange(1, j + 1)), rel=1e-12)
+        v = A @ v
+    assert abs((b @ v) * 40320.0 - 1.0) > 1e-3
