@@ -80,6 +80,17 @@ WORKLOADS = {
     # cotangent updates 6 d + 2 = 50.
     "hires": dict(s_cap=4096, with_t=False, states=False, init=192, att=1053, replay=807,
                   grad=807 + (807 - 24) + 730, peak=78.6e12, bound="alu", cpu_n=1024),
+    # The Verner 7(6) pair on the Lorenz and orbit ensembles.  Not FSAL: an
+    # accepted attempt adds one field evaluation (f at the new state; acc_extra
+    # = F_f, 8 for Lorenz, 15 for the halo).  Gradient step: replay R + the
+    # recomputed stages (R - F_f - 15 d) + the reverse sweep 37 + 76 d + 9 V
+    # (seven nonzero weights, nine stage VJPs, thirty nonzero stage couplings).
+    "lorenz63_vern7": dict(s_cap=1024, with_t=False, states=False, init=68, att=428,
+                           acc_extra=8, replay=321, grad=2 * 321 - 8 - 45 + 37 + 228 + 9 * 19,
+                           peak=78.6e12, bound="alu", cpu_n=8192),
+    "loghalo_vern7": dict(s_cap=8192, with_t=False, states=False, init=124, att=842,
+                          acc_extra=15, replay=633, grad=2 * 633 - 15 - 90 + 37 + 456 + 9 * 41,
+                          peak=78.6e12, bound="alu", cpu_n=1024),
 }
 # Forward sensitivities (solve_sens, Tsit5): per accepted step and parameter
 # direction, the stage tangents and the tangent update take 48 d flops, plus
@@ -203,7 +214,8 @@ HBM_PEAK = 8.0e12  # bytes/s, MI355X HBM3E (published)
 CPU_SAMPLES = {"lotka_volterra": (256, 256, 256), "lorenz63": (65536, 32768, 1024),
                "mlp": (16384, 4096, 128), "robertson": (131072, 32768, 1024),
                "loghalo": (16384, 4096, 64), "hires": (8192, 2048, 64),
-               "lorenz63_spread": (32768, 8192, 512)}
+               "lorenz63_spread": (32768, 8192, 512), "lorenz63_vern7": (65536, 32768, 1024),
+               "loghalo_vern7": (16384, 4096, 64)}
 
 
 def cpu_threads():
@@ -425,7 +437,8 @@ def measure_gradient(w, args, steps, warmup, graph):
     attempts = int((cnt + nrej).sum())
     steps_total = int(cnt.sum())
     ts, tg, tk = float(np.mean(t_solve)), float(np.mean(t_grad)), float(np.mean(t_kern))
-    fl_solve = w.n * cfg["init"] + attempts * cfg["att"] + steps_total
+    fl_solve = (w.n * cfg["init"] + attempts * cfg["att"]
+                + steps_total * (1 + cfg.get("acc_extra", 0)))
     # with recorded states the gradient does no forward replay
     fl_grad = steps_total * (cfg["grad"] - (cfg["replay"] if states else 0))
     peak = cfg["peak"]

@@ -78,7 +78,8 @@ def glorot(rng, fan_out, fan_in):
     return rng.uniform(-lim, lim, size=(fan_out, fan_in))
 
 
-VERN7_OF = {"lorenz63_vern7": "lorenz63", "loghalo_vern7": "loghalo"}
+VERN7_OF = {"lorenz63_vern7": "lorenz63", "loghalo_vern7": "loghalo", "decay_vern7": "decay",
+            "lotka_volterra_vern7": "lotka_volterra"}
 
 
 def make(name: str, n: int | None = None) -> Workload:

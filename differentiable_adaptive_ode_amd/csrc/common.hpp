@@ -54,8 +54,9 @@ __device__ __forceinline__ float truncBits(float x) {
   return __uint_as_float(u);
 }
 
-// Step-size controller power x^(-1/Q) (Q = 10 for Tsit5, 6 for Rosenbrock23;
-// x is the mean square of the scaled error, so this is err^(-1/(order+1))).
+// Step-size controller power x^(-1/Q) (Q = 10 for Tsit5, 14 for Verner 7, 6
+// for Rosenbrock23; x is the mean square of the scaled error, so this is
+// err^(-1/(p+1)) with p the pair's lower order).
 // A libm pow costs about a thousand cycles of dependent FP64 work per call on
 // one wavefront; this rule costs two short polynomial evaluations:
 //   clamp x to [lo, hi] (beyond it 0.9 x^(-1/Q) is outside the controller's
@@ -83,6 +84,14 @@ struct CtrlRoot<6> {
                                   0.010097959271667333,   -0.0024314560515976726,
                                   0.0006347021852295785,  -0.0001753744494318341,
                                   6.143024330877807e-05,  -1.8571447204984547e-05};
+};
+template <>
+struct CtrlRoot<14> {
+  static constexpr double lo = 1e-15, hi = 1e10;
+  static constexpr double c[8] = {0.971453564346184,      -0.02312982604893814,
+                                  0.004130813507010568,   -0.0009509085609683622,
+                                  0.00024095017603375496, -6.506922272280208e-05,
+                                  2.2232410031470908e-05, -6.6171886469205804e-06};
 };
 __device__ constexpr double EXP2_NEG[7] = {0.7071067811579441,    -0.24506454511279616,
                                            0.042466448938030865,  -0.004905842513716687,

@@ -172,6 +172,7 @@ const int SYS_D[7] = {1, 2, 3, 4, 3, 6, 8};
 const int SYS_P[7] = {1, 4, 3, 4740, 3, 3, 12};
 
 bool sys_ok(int sys) { return sys >= 0 && sys <= 6; }
+bool method_ok(int m) { return m == DAO_TSIT5 || m == DAO_ROSENBROCK23 || m == DAO_VERNER7; }
 
 struct DevInfo {
   int cus = 0;
@@ -701,8 +702,17 @@ Impl make_impl() {
               &Entry<R, S, M>::grad_at, &Entry<R, S, M>::slot_at_bytes};
 }
 
+// Verner 7: solve, gradient, states and gradient at requested times; no
+// forward sensitivities.
+template <class R, template <class> class S>
+Impl make_impl_vern7() {
+  using E = Entry<R, S, M_VERN7>;
+  return Impl{&E::solve, &E::grad, &E::slot_bytes, &E::resident_waves, WAVE, nullptr, nullptr,
+              &E::states, &E::solve_ws, &E::grad_at, &E::slot_at_bytes};
+}
+
 const Impl* find_impl(int sys, int method, int dtype) {
-  static Impl table[7][2][2];
+  static Impl table[7][3][2];
   static bool init = false;
   static std::mutex mu;
   std::lock_guard<std::mutex> lk(mu);
@@ -729,12 +739,16 @@ const Impl* find_impl(int sys, int method, int dtype) {
     table[DAO_SYS_HIRES][M_TSIT5][DAO_F64] = make_impl<double, Hires, M_TSIT5>();
     table[DAO_SYS_HIRES][M_ROS23][DAO_F64] = make_impl<double, Hires, M_ROS23>();
     table[DAO_SYS_HIRES][M_ROS23][DAO_F32] = make_impl<float, Hires, M_ROS23>();
+    table[DAO_SYS_DECAY][M_VERN7][DAO_F64] = make_impl_vern7<double, Decay>();
+    table[DAO_SYS_LOTKA_VOLTERRA][M_VERN7][DAO_F64] = make_impl_vern7<double, LotkaVolterra>();
+    table[DAO_SYS_LORENZ63][M_VERN7][DAO_F64] = make_impl_vern7<double, Lorenz63>();
+    table[DAO_SYS_LOGHALO][M_VERN7][DAO_F64] = make_impl_vern7<double, LogHalo>();
     table[DAO_SYS_MLP][M_TSIT5][DAO_F32] =
         Impl{&launch_mlp_solve, &launch_mlp_grad, &mlp_slot_bytes, &mlp_resident_waves, mlp::SLOTS,
              nullptr, nullptr, nullptr, &mlp_solve_ws, nullptr, nullptr};
     init = true;
   }
-  if (!sys_ok(sys) || method < 0 || method > 1 || dtype < 0 || dtype > 1) return nullptr;
+  if (!sys_ok(sys) || !method_ok(method) || dtype < 0 || dtype > 1) return nullptr;
   const Impl* im = &table[sys][method][dtype];
   return im->solve ? im : nullptr;
 }
@@ -816,7 +830,7 @@ dao_status solve_call(const char* fn, dao_system sys, dao_method method, dao_dty
   const bool sens = std::strcmp(fn, "dao_solve_sens") == 0;
   g_err[0] = 0;
   if (!sys_ok(sys)) return fail(DAO_EINVAL, "%s: unknown system %d", fn, (int)sys);
-  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
+  if (!method_ok(method))
     return fail(DAO_EINVAL, "%s: unknown method %d", fn, (int)method);
   if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
   if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "%s: n = %lld out of range", fn, (long long)n);
@@ -896,7 +910,7 @@ dao_status dao_states_at(dao_system sys, dao_method method, dao_dtype dtype, int
   const char* fn = "dao_states_at";
   g_err[0] = 0;
   if (!sys_ok(sys)) return fail(DAO_EINVAL, "%s: unknown system %d", fn, (int)sys);
-  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
+  if (!method_ok(method))
     return fail(DAO_EINVAL, "%s: unknown method %d", fn, (int)method);
   if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
   if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "%s: n = %lld out of range", fn, (long long)n);
@@ -930,7 +944,7 @@ dao_status dao_sens(dao_system sys, dao_method method, dao_dtype dtype, int64_t 
   const char* fn = "dao_sens";
   g_err[0] = 0;
   if (!sys_ok(sys)) return fail(DAO_EINVAL, "%s: unknown system %d", fn, (int)sys);
-  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
+  if (!method_ok(method))
     return fail(DAO_EINVAL, "%s: unknown method %d", fn, (int)method);
   if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
   if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "%s: n = %lld out of range", fn, (long long)n);
@@ -986,7 +1000,7 @@ dao_status grad_call(const char* fn, int mode, dao_system sys, dao_method method
                      bool static_scratch = false) {
   g_err[0] = 0;
   if (!sys_ok(sys)) return fail(DAO_EINVAL, "%s: unknown system %d", fn, (int)sys);
-  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
+  if (!method_ok(method))
     return fail(DAO_EINVAL, "%s: unknown method %d", fn, (int)method);
   if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
   if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "%s: n = %lld out of range", fn, (long long)n);
@@ -1079,7 +1093,7 @@ dao_status dao_grad_at(dao_system sys, dao_method method, dao_dtype dtype, int64
   const char* fn = "dao_grad_at";
   g_err[0] = 0;
   if (!sys_ok(sys)) return fail(DAO_EINVAL, "%s: unknown system %d", fn, (int)sys);
-  if (method != DAO_TSIT5 && method != DAO_ROSENBROCK23)
+  if (!method_ok(method))
     return fail(DAO_EINVAL, "%s: unknown method %d", fn, (int)method);
   if (dtype != DAO_F64 && dtype != DAO_F32) return fail(DAO_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
   if (n < 0 || n > (int64_t)INT32_MAX) return fail(DAO_EINVAL, "%s: n = %lld out of range", fn, (long long)n);

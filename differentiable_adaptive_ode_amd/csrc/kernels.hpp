@@ -21,10 +21,11 @@
 #include "ros23.hpp"
 #include "systems.hpp"
 #include "tsit5.hpp"
+#include "vern7.hpp"
 
 namespace dao {
 
-enum Method : int { M_TSIT5 = 0, M_ROS23 = 1 };
+enum Method : int { M_TSIT5 = 0, M_ROS23 = 1, M_VERN7 = 2 };
 
 template <class R>
 struct SolveArgs {
@@ -164,8 +165,10 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   int sdir[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) sdir[j] = j;
-  constexpr int ORDER = (METHOD == M_TSIT5) ? 5 : 2;
-  constexpr int CTRL_Q = (METHOD == M_TSIT5) ? 10 : 6;  // msq^(-1/Q) = err^(-1/(ORDER+1))
+  constexpr int ORDER = (METHOD == M_TSIT5) ? 5 : (METHOD == M_VERN7) ? 7 : 2;
+  // msq^(-1/Q) = err^(-1/(p+1)), p the pair's lower order (4, 6, 2)
+  constexpr int CTRL_Q = (METHOD == M_TSIT5) ? 10 : (METHOD == M_VERN7) ? 14 : 6;
+  constexpr int NK = (METHOD == M_VERN7) ? 10 : 7;  // stage derivatives per attempt
   constexpr int32_t RUNNING = -1;
   const int lane = laneId();
   R* const trash = a.trash + 2 * lane;
@@ -184,7 +187,7 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
 
   Sys sys;
   R y[D];
-  R k[7][D];  // Tsit5: stages, k[0] = f(y) (FSAL); Rosenbrock23: k[0] = F0 = f(y)
+  R k[NK][D];  // stages, k[0] = f(y) (Tsit5: FSAL); Rosenbrock23: k[0] = F0 = f(y)
   R t = R(0), h = R(0);
   int32_t nacc = 0, nrej = 0;
   int64_t attempts = 0;
@@ -406,10 +409,13 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     R ynew[D], err[D], F2[D];
     if constexpr (METHOD == M_TSIT5) {
       tsit5::trial<R, Sys>(C5, sys, y, hs, k, ynew, err);
+    } else if constexpr (METHOD == M_VERN7) {
+      vern7::trial<R, Sys>(sys, y, hs, k, ynew, err);
+      sys.f(ynew, F2);  // not FSAL: f at the new state, kept if the step is taken
     } else {
       ros23::trial<R, Sys, !SENS>(sys, y, hs, k[0], ynew, F2, err);
     }
-    const R es = (METHOD == M_TSIT5) ? hs : hs / R(6);
+    const R es = (METHOD == M_ROS23) ? hs / R(6) : hs;
     R wt[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) {
@@ -452,6 +458,7 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
 
     const bool take = (st == RUNNING) && acc;
     const R tn = last ? a.t1 : t + hs;
+    static_assert(!(SENS && METHOD == M_VERN7), "no in-solve sensitivities for Verner 7");
     if constexpr (SENS) {
       if (take) {
         if constexpr (METHOD == M_TSIT5) {
@@ -703,6 +710,8 @@ grad_kernel(GradArgs<R> a) {
         __builtin_nontemporal_store(hj, &scr[((int64_t)i * SD + D) * WAVE]);
         if constexpr (METHOD == M_TSIT5)
           tsit5::replay<R, Sys>(C5, sys, y, hj);
+        else if constexpr (METHOD == M_VERN7)
+          vern7::replay<R, Sys>(sys, y, hj);
         else
           ros23::replay<R, Sys>(sys, y, hj);
       };
@@ -746,6 +755,10 @@ grad_kernel(GradArgs<R> a) {
           tsit5::Stages<R, D> S;
           tsit5::stages<R, Sys>(C5, sys, yq, hq, S);
           tsit5::sweep<R, Sys>(C5, sys, S, hq, lq, pb);
+        } else if constexpr (METHOD == M_VERN7) {
+          vern7::Stages<R, D> S;
+          vern7::stages<R, Sys>(sys, yq, hq, S);
+          vern7::sweep<R, Sys>(sys, S, hq, lq, pb);
         } else {
           ros23::Stages<R, D> S;
           ros23::stages<R, Sys>(sys, yq, hq, S);
@@ -793,6 +806,10 @@ grad_kernel(GradArgs<R> a) {
           tsit5::Stages<R, D> S;
           tsit5::stages<R, Sys>(C5, sys, yj, hj, S);
           tsit5::sweep<R, Sys>(C5, sys, S, hj, lam, pb);
+        } else if constexpr (METHOD == M_VERN7) {
+          vern7::Stages<R, D> S;
+          vern7::stages<R, Sys>(sys, yj, hj, S);
+          vern7::sweep<R, Sys>(sys, S, hj, lam, pb);
         } else {
           ros23::Stages<R, D> S;
           ros23::stages<R, Sys>(sys, yj, hj, S);
@@ -1082,6 +1099,8 @@ __global__ void __launch_bounds__(256) states_kernel(StatesArgs<R> a) {
       for (int c = 0; c < D; ++c) ys[c] = y[c];
       if constexpr (METHOD == M_TSIT5)
         tsit5::replay<R, Sys>(C5, sys, ys, hs);
+      else if constexpr (METHOD == M_VERN7)
+        vern7::replay<R, Sys>(sys, ys, hs);
       else
         ros23::replay<R, Sys>(sys, ys, hs);
       if (adv) {

@@ -70,7 +70,11 @@ typedef enum {
 
 typedef enum {
   DAO_TSIT5 = 0,        /* Tsitouras 5(4) pair, 7 stages, FSAL (Sec. 2.1)                  */
-  DAO_ROSENBROCK23 = 1  /* Shampine-Reichelt second-order Rosenbrock, autonomous (Sec. 3.2) */
+  DAO_ROSENBROCK23 = 1, /* Shampine-Reichelt second-order Rosenbrock, autonomous (Sec. 3.2) */
+  DAO_VERNER7 = 2       /* Verner 7(6) pair, 10 stages, not FSAL (Sec. 3.1 method list);
+                           binary64 with decay, Lotka-Volterra, Lorenz-63 and the log halo;
+                           solve, gradients and states at requested times (no forward
+                           sensitivities: DAO_EUNSUPPORTED)                               */
 } dao_method;
 
 typedef enum { DAO_F64 = 0, DAO_F32 = 1 } dao_dtype;

@@ -19,7 +19,7 @@ def test_solve_and_replay_tallies(orc, name):
         c = orc.count_solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol)
         assert c["init"] == cfg["init"]
         tot += c["total"]
-        pred += cfg["init"] + c["attempts"] * cfg["att"] + c["accepted"]
+        pred += cfg["init"] + c["attempts"] * cfg["att"] + c["accepted"] * (1 + cfg.get("acc_extra", 0))
         assert orc.count_replay_step(w.system, w.method, th, y0, 1e-3) == cfg["replay"]
     # the model leaves out only the clip of the last step (one flop per trajectory)
     assert abs(pred - tot) / tot < 1e-3, (pred, tot)

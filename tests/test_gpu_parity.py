@@ -66,7 +66,9 @@ def import_mesh(dao, w, ref, s_cap):
 
 CASES = [("decay", 300, 256), ("lotka_volterra", 300, 256), ("lorenz63", 300, 1024),
          ("loghalo", 200, 4096), ("robertson", 200, 2048), ("hires", 200, 4096),
-         ("lorenz63_spread", 300, 2048)]
+         ("lorenz63_spread", 300, 2048),
+         ("decay_vern7", 300, 256), ("lotka_volterra_vern7", 300, 256),
+         ("lorenz63_vern7", 300, 1024), ("loghalo_vern7", 200, 4096)]
 # systems whose rate constants span orders of magnitude: their gradients are
 # compared as log-sensitivities theta * dL/dtheta
 LOG_RATES = ("robertson", "hires")

@@ -31,7 +31,9 @@ def rel_err(a, b):
 
 
 CASES = [("decay", 300, 256), ("lotka_volterra", 300, 256), ("lorenz63", 300, 1024),
-         ("loghalo", 200, 4096), ("robertson", 200, 2048), ("hires", 200, 4096)]
+         ("loghalo", 200, 4096), ("robertson", 200, 2048), ("hires", 200, 4096),
+         ("decay_vern7", 300, 256), ("lotka_volterra_vern7", 300, 256),
+         ("lorenz63_vern7", 300, 1024), ("loghalo_vern7", 200, 4096)]
 
 
 @pytest.mark.parametrize("name,n,s_cap", CASES)
