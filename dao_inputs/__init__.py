@@ -19,8 +19,8 @@ the five benchmark ensembles):
 * ``lorenz63_spread`` the Lorenz ensemble with its difficulty spread (the divergence stress
                       test): rho log-uniform on [20, 1000], so that step counts range over
                       about an order of magnitude; sigma, beta, y0 and targets as ``lorenz63``
-* ``lorenz63_vern7``, ``loghalo_vern7``  the Lorenz and orbit ensembles (same draws)
-                      integrated with the Verner 7(6) pair
+* ``<ensemble>_vern7``, ``<ensemble>_rodas5p``  an ensemble (same draws) integrated with
+                      the Verner 7(6) pair or Rodas5P (METHOD_VARIANTS)
 * ``hires``           HIRES, 8 species; the twelve rate constants at their nominal values for
                       every trajectory (the ensemble carries no free rate constant); the two
                       nonzero components of the standard initial state (1, 0, ..., 0, 0.0057)
@@ -78,15 +78,22 @@ def glorot(rng, fan_out, fan_in):
     return rng.uniform(-lim, lim, size=(fan_out, fan_in))
 
 
-VERN7_OF = {"lorenz63_vern7": "lorenz63", "loghalo_vern7": "loghalo", "decay_vern7": "decay",
-            "lotka_volterra_vern7": "lotka_volterra"}
+# the same ensembles (same draws) integrated with another method: name ->
+# (ensemble, method)
+METHOD_VARIANTS = {"lorenz63_vern7": ("lorenz63", "vern7"), "loghalo_vern7": ("loghalo", "vern7"),
+                   "decay_vern7": ("decay", "vern7"),
+                   "lotka_volterra_vern7": ("lotka_volterra", "vern7"),
+                   "robertson_rodas5p": ("robertson", "rodas5p"),
+                   "decay_rodas5p": ("decay", "rodas5p"),
+                   "lotka_volterra_rodas5p": ("lotka_volterra", "rodas5p"),
+                   "hires_rodas5p": ("hires", "rodas5p")}
 
 
 def make(name: str, n: int | None = None) -> Workload:
-    if name in VERN7_OF:
-        # the same ensemble (same draws) integrated with the Verner 7(6) pair
-        base = make(VERN7_OF[name], n)
-        return Workload(name, base.system, "vern7", base.dtype, base.n, base.t0, base.t1,
+    if name in METHOD_VARIANTS:
+        ens, method = METHOD_VARIANTS[name]
+        base = make(ens, n)
+        return Workload(name, base.system, method, base.dtype, base.n, base.t0, base.t1,
                         base.rtol, base.atol, base.theta, base.y0, base.target, base.loss,
                         dict(base.extra))
     n = DEFAULT_N[name] if n is None else int(n)

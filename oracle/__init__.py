@@ -34,7 +34,7 @@ _SRC = os.path.join(_HERE, "oracle.cpp")
 
 SYSTEMS = {"decay": 0, "lotka_volterra": 1, "lorenz63": 2, "mlp": 3, "robertson": 4, "loghalo": 5,
            "hires": 6}
-METHODS = {"tsit5": 0, "rosenbrock23": 1, "vern7": 2}
+METHODS = {"tsit5": 0, "rosenbrock23": 1, "vern7": 2, "rodas5p": 3}
 STATUS = {0: "ok", 1: "max_steps", 2: "nonfinite", 3: "dt_underflow", 4: "capacity"}
 
 _lib = None
@@ -64,6 +64,7 @@ def lib():
         L.oracle_tsit5_table.argtypes = [P, P, P]
         L.oracle_ros23_consts.argtypes = [P, P]
         L.oracle_vern7_table.argtypes = [P, P, P, P]
+        L.oracle_rodas5p_table.argtypes = [P, P, P]
         for name in ("oracle_solve_f64", "oracle_solve_f32", "oracle_solve_plain_f64",
                      "oracle_solve_plain_f32"):
             getattr(L, name).argtypes = [I, I, I64, P, P, D, D, D, D, D, I64, I64, P, P, P, P, P, P, I]
@@ -117,6 +118,15 @@ def vern7_table():
     A = np.zeros((10, 10))
     lib().oracle_vern7_table(_p(c), _p(A), _p(b), _p(bh))
     return c, A, b, bh
+
+
+def rodas5p_table():
+    """(gamma, a [8][8] (rows 1-5 of the stage sums; rows 6-7 are Y6 + u6,
+    Y7 + u7), C [8][8]) of Rodas5P as the oracle holds them."""
+    g = ctypes.c_double()
+    A, C = np.zeros((8, 8)), np.zeros((8, 8))
+    lib().oracle_rodas5p_table(ctypes.byref(g), _p(A), _p(C))
+    return g.value, A, C
 
 
 def ros23_consts():

@@ -46,6 +46,8 @@
 //     written below; build with -ffp-contract=off.
 //   * Verner 7(6) pair: Verner's published ten-stage table (the pages name
 //     the pair; they print no coefficients).
+//   * Rodas5P: Steinebach's published table (named on the pages, not
+//     printed), in the form with W = I/(gamma h) - J.
 // ============================================================================
 #include <algorithm>
 #include <cmath>
@@ -284,6 +286,36 @@ const double VN_B[10] = {0.04715561848627222, 0, 0, 0.25750564298434153, 0.26216
 const double VN_BH[10] = {0.044608606606341174, 0, 0, 0.26716403785713727, 0.22010183001772932,
                           0.2188431703143157, 0.22898717054112028, 0, 0, 0.02029518466335628};
 
+// Rodas5P (G. Steinebach, BIT Numer. Math. 63 (2023) 27): an eight-stage,
+// stiffly accurate, L-stable Rosenbrock-Wanner method of order 5 with an
+// embedded order-4 solution, in the form with W = I/(gamma h) - J(y):
+//   W u_i = f(Y_i) + (1/h) sum_{j<i} C_ij u_j,   Y_1 = y,
+//   Y_i = y + sum_{j<i} a_ij u_j (i = 2..6),  Y_7 = Y_6 + u_6,  Y_8 = Y_7 + u_7,
+//   y_new = Y_8 + u_8,   error estimate u_8 (y_new minus the embedded Y_8).
+// Autonomous systems only (the df/dt terms of the method vanish).  Row i of
+// RP_A / RP_C holds a_ij / C_ij, j < i (0-based: stage i+1).
+const double RP_GAMMA = 0.21193756319429014;
+const double RP_A[6][6] = {
+    {0, 0, 0, 0, 0, 0},
+    {3.0, 0, 0, 0, 0, 0},
+    {2.849394379747939, 0.45842242204463923, 0, 0, 0, 0},
+    {-6.954028509809101, 2.489845061869568, -10.358996098473584, 0, 0, 0},
+    {2.8029986275628964, 0.5072464736228206, -0.3988312541770524, -0.04721187230404641, 0, 0},
+    {-7.502846399306121, 2.561846144803919, -11.627539656261098, -0.18268767659942256,
+     0.030198172008377946, 0}};
+const double RP_C[8][8] = {
+    {0, 0, 0, 0, 0, 0, 0, 0},
+    {-14.155112264123755, 0, 0, 0, 0, 0, 0, 0},
+    {-17.97296035885952, -2.859693295451294, 0, 0, 0, 0, 0, 0},
+    {147.12150275711716, -1.41221402718213, 71.68940251302358, 0, 0, 0, 0, 0},
+    {165.43517024871676, -0.4592823456491126, 42.90938336958603, -5.961986721573306, 0, 0, 0, 0},
+    {24.854864614690072, -3.0009227002832186, 47.4931110020768, 5.5814197821558125,
+     -0.6610691825249471, 0, 0, 0},
+    {30.91273214028599, -3.1208243349937974, 77.79954646070892, 34.28646028294783,
+     -19.097331116725623, -28.087943162872662, 0, 0},
+    {37.80277123390563, -3.2571969029072276, 112.26918849496327, 66.9347231244047,
+     -40.06618937091002, -54.66780262877968, -9.48861652309627, 0}};
+
 // Rosenbrock23 (Shampine & Reichelt 1997): gamma = d = 1/(2+sqrt 2),
 // e32 = 6 + sqrt 2.
 const double R23_D = 1.0 / (2.0 + 1.4142135623730951);
@@ -295,7 +327,7 @@ const double R23_E32 = 6.0 + 1.4142135623730951;
 // ----------------------------------------------------------------------------
 enum { SYS_DECAY = 0, SYS_LV = 1, SYS_LORENZ = 2, SYS_MLP = 3, SYS_ROBERTSON = 4, SYS_LOGHALO = 5,
        SYS_HIRES = 6, SYS_COUNT = 7 };
-enum { M_TSIT5 = 0, M_ROS23 = 1, M_VERN7 = 2 };
+enum { M_TSIT5 = 0, M_ROS23 = 1, M_VERN7 = 2, M_RODAS5P = 3 };
 const int MAXK = 10;  // stage derivatives kept per step (Verner 7's ten)
 enum { ST_OK = 0, ST_MAXSTEPS = 1, ST_NONFINITE = 2, ST_DTMIN = 3, ST_CAPACITY = 4 };
 
@@ -647,6 +679,58 @@ void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* yn
 }
 
 // ----------------------------------------------------------------------------
+// One Rodas5P step (Section 3.2's linearly implicit step with Steinebach's
+// eight-stage table).  F0 = f(y) on entry.  Returns ynew and, if err !=
+// nullptr, the estimate u_8.  W = I/(gamma h) - J(y) is factored once; the
+// stage right-hand sides are f(Y_i) + (1/h) sum_j C_ij u_j, the sum formed
+// first (j ascending) and added by one fused multiply-add with 1/h.
+// ----------------------------------------------------------------------------
+template <class T, bool PLAIN = false>
+void rodas5p_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* ynew, T* err,
+                  double* kabs = nullptr) {
+  T J[MAXD * MAXD], W[MAXD * MAXD], rp[MAXD];
+  int piv[MAXD];
+  jac(sys, th, y, J);
+  const T ginv = T(1.0) / (T(RP_GAMMA) * h);
+  const T hinv = T(1.0) / h;
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) W[i * d + j] = (i == j) ? ginv - J[i * d + j] : -J[i * d + j];
+  lu_factor<T, PLAIN>(d, W, piv, rp);
+  T u[8][MAXD], Y[MAXD], F[MAXD], r[MAXD];
+  for (int i = 0; i < 8; ++i) {
+    // stage state
+    if (i == 0) {
+      for (int c = 0; c < d; ++c) Y[c] = y[c];
+    } else if (i <= 5) {
+      for (int c = 0; c < d; ++c) {
+        T acc = T(RP_A[i][0]) * u[0][c];
+        for (int j = 1; j < i; ++j) acc = fma3(T(RP_A[i][j]), u[j][c], acc);
+        Y[c] = acc + y[c];
+      }
+    } else {
+      for (int c = 0; c < d; ++c) Y[c] = Y[c] + u[i - 1][c];  // Y_7 = Y_6 + u_6, Y_8 = Y_7 + u_7
+    }
+    // right-hand side and solve
+    if (i == 0) {
+      for (int c = 0; c < d; ++c) r[c] = F0[c];
+    } else {
+      rhs(sys, th, Y, F);
+      for (int c = 0; c < d; ++c) {
+        T acc = T(RP_C[i][0]) * u[0][c];
+        for (int j = 1; j < i; ++j) acc = fma3(T(RP_C[i][j]), u[j][c], acc);
+        r[c] = fma3(acc, hinv, F[c]);
+      }
+    }
+    lu_solve<T, PLAIN>(d, W, piv, rp, r, u[i]);
+  }
+  for (int c = 0; c < d; ++c) ynew[c] = Y[c] + u[7][c];
+  if (err == nullptr) return;
+  for (int c = 0; c < d; ++c) err[c] = u[7][c];
+  if (kabs)
+    for (int c = 0; c < d; ++c) kabs[c] = std::fabs(rv(u[7][c]));
+}
+
+// ----------------------------------------------------------------------------
 // Step-size helpers.
 // ----------------------------------------------------------------------------
 inline double trunc_bits(double x) {  // keep 16 explicit mantissa bits
@@ -821,10 +905,11 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
                       T dt0, int64_t max_steps, int64_t s_cap, T* y1, T* t_rec, T* h_rec,
                       Trace* trace = nullptr) {
   const int d = SYS_D[sys];
-  const int order = (method == M_TSIT5) ? 5 : (method == M_VERN7) ? 7 : 2;
-  // msq^(-1/q) = err^(-1/(p+1)), p the lower order of the pair: 4 (Tsit5 5(4)),
-  // 6 (Verner 7(6)), 2 (Rosenbrock23, whose estimate is of third order)
-  const int q = (method == M_TSIT5) ? 10 : (method == M_VERN7) ? 14 : 6;
+  const int order = (method == M_TSIT5 || method == M_RODAS5P) ? 5 : (method == M_VERN7) ? 7 : 2;
+  // msq^(-1/q) = err^(-1/(p+1)), p the lower order of the pair: 4 (Tsit5 5(4)
+  // and Rodas5P 5(4)), 6 (Verner 7(6)), 2 (Rosenbrock23, whose estimate is of
+  // third order)
+  const int q = (method == M_VERN7) ? 14 : (method == M_ROS23) ? 6 : 10;
   SolveOut<T> out = {0, 0, ST_OK};
   T y[MAXD], ynew[MAXD], e[MAXD], sc[MAXD], k[MAXK][MAXD], F2[MAXD];
   for (int c = 0; c < d; ++c) y[c] = y0[c];
@@ -858,10 +943,14 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
             for (int j = 0; j < 10; ++j)
               kabs[c] += std::fabs(VN_B[j] - VN_BH[j]) * std::fabs(rv(k[j][c]));
           }
+      } else if (method == M_RODAS5P) {
+        rodas5p_step<T, PLAIN>(sys, th, d, y, hs, k[0], ynew, e, trace ? kabs : nullptr);
       } else {
         ros23_step<T, PLAIN>(sys, th, d, y, hs, k[0], ynew, F2, e, !PLAIN, trace ? kabs : nullptr);
       }
-      const T es = (method == M_ROS23) ? hs / T(6.0) : hs;
+      // the error estimate's factor: h (explicit pairs), h/6 (Rosenbrock23), 1
+      // (Rodas5P, whose estimate u_8 is already a state difference)
+      const T es = (method == M_ROS23) ? hs / T(6.0) : (method == M_RODAS5P) ? T(1.0) : hs;
       T w[MAXD];
       for (int c = 0; c < d; ++c) {
         sc[c] = fma3(rtol, std::max(abs_(y[c]), abs_(ynew[c])), atol);
@@ -891,7 +980,7 @@ SolveOut<T> solve_one(int sys, int method, const T* th, const T* y0, T t0, T t1,
         for (int c = 0; c < d; ++c) y[c] = ynew[c];
         if (method == M_TSIT5)
           for (int c = 0; c < d; ++c) k[0][c] = k[6][c];
-        else if (method == M_VERN7)
+        else if (method == M_VERN7 || method == M_RODAS5P)
           rhs(sys, th, y, k[0]);  // not FSAL: f at the new state
         else
           for (int c = 0; c < d; ++c) k[0][c] = F2[c];
@@ -929,6 +1018,8 @@ void replay_one(int sys, int method, const T* th, const T* y0, int32_t count, co
       tsit5_step<T>(sys, th, d, y, h, k, ynew, nullptr);
     else if (method == M_VERN7)
       vern7_step<T>(sys, th, d, y, h, k, ynew, nullptr);
+    else if (method == M_RODAS5P)
+      rodas5p_step<T>(sys, th, d, y, h, k[0], ynew, nullptr);
     else
       ros23_step<T>(sys, th, d, y, h, k[0], ynew, nullptr, nullptr);
     for (int c = 0; c < d; ++c) y[c] = ynew[c];
@@ -990,7 +1081,7 @@ void parallel_for(int64_t n, int nthreads, F fn) {
 
 bool valid_sys(int sys, int method) {
   if (sys < 0 || sys >= SYS_COUNT) return false;
-  if (method != M_TSIT5 && method != M_ROS23 && method != M_VERN7) return false;
+  if (method < M_TSIT5 || method > M_RODAS5P) return false;
   if (method != M_TSIT5 && sys == SYS_MLP) return false;
   return true;
 }
@@ -1072,6 +1163,15 @@ void oracle_vern7_table(double* c, double* A, double* b, double* bhat) {
     bhat[i] = VN_BH[i];
     for (int j = 0; j < 10; ++j) A[i * 10 + j] = VN_A[i][j];
   }
+}
+
+void oracle_rodas5p_table(double* gamma, double* A, double* C) {
+  *gamma = RP_GAMMA;
+  for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < 8; ++j) {
+      A[i * 8 + j] = (i < 6 && j < 6) ? RP_A[i][j] : 0.0;
+      C[i * 8 + j] = RP_C[i][j];
+    }
 }
 
 void oracle_ros23_consts(double* d, double* e32) {
@@ -1197,6 +1297,8 @@ int oracle_states_at_f64(int sys, int method, int64_t n, const double* theta, co
         tsit5_step<double>(sys, th.data(), d, from, h, k, to, nullptr);
       else if (method == M_VERN7)
         vern7_step<double>(sys, th.data(), d, from, h, k, to, nullptr);
+      else if (method == M_RODAS5P)
+        rodas5p_step<double>(sys, th.data(), d, from, h, k[0], to, nullptr);
       else
         ros23_step<double>(sys, th.data(), d, from, h, k[0], to, nullptr, nullptr);
     };
@@ -1350,6 +1452,8 @@ int oracle_grad_at_f64(int sys, int method, int64_t n, const double* theta, cons
           tsit5_step<Rev>(sys, rth.data(), d, from, Rev(h), k, to, nullptr);
         else if (method == M_VERN7)
           vern7_step<Rev>(sys, rth.data(), d, from, Rev(h), k, to, nullptr);
+        else if (method == M_RODAS5P)
+          rodas5p_step<Rev>(sys, rth.data(), d, from, Rev(h), k[0], to, nullptr);
         else
           ros23_step<Rev>(sys, rth.data(), d, from, Rev(h), k[0], to, nullptr, nullptr);
       };
@@ -1410,6 +1514,8 @@ int oracle_step_f64(int sys, int method, const double* th, const double* y, doub
     tsit5_step(sys, th, d, y, h, k, ynew, err);
   else if (method == M_VERN7)
     vern7_step(sys, th, d, y, h, k, ynew, err);
+  else if (method == M_RODAS5P)
+    rodas5p_step(sys, th, d, y, h, k[0], ynew, err);
   else
     ros23_step(sys, th, d, y, h, k[0], ynew, F2, err);
   return 0;
@@ -1429,7 +1535,7 @@ int oracle_count_solve(int sys, int method, const double* theta, const double* y
   g_flops = 0;
   rhs(sys, th.data(), y, f0);
   initial_step(sys, th.data(), d, y, f0, Cnt(t1 - t0), Cnt(rtol), Cnt(atol),
-               method == M_TSIT5 ? 5 : method == M_VERN7 ? 7 : 2);
+               method == M_VERN7 ? 7 : method == M_ROS23 ? 2 : 5);
   out[1] = g_flops;
   g_flops = 0;
   SolveOut<Cnt> o = solve_one<Cnt>(sys, method, th.data(), y, Cnt(t0), Cnt(t1), Cnt(rtol),

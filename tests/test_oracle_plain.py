@@ -36,6 +36,8 @@ SAMPLES = {
     "lorenz63_spread": (1024, 2048),
     "lorenz63_vern7": (2048, 1024),
     "loghalo_vern7": (512, 8192),
+    "robertson_rodas5p": (2048, 1024),
+    "hires_rodas5p": (256, 2048),
 }
 
 

@@ -20,6 +20,7 @@ import dao_inputs as di
 TSIT = "tsit5"
 ROS = "rosenbrock23"
 VERN = "vern7"
+RODAS = "rodas5p"
 
 
 def R_poly(orc, z):
@@ -280,6 +281,59 @@ def test_vern7_error_estimate_order(orc):
     assert np.all(np.abs(slopes - 7.0) < 0.3), slopes
 
 
+@pytest.mark.parametrize("system", ["loghalo", "lorenz63"])
+def test_rodas5p_local_orders(orc, system):
+    # One Rodas5P step from a state against a tight reference (Verner 7 with
+    # many substeps): the local error of y_new falls like h^6 (order 5) and
+    # that of the embedded solution y_new - estimate like h^5 (order 4).  The
+    # halo's field is not polynomial, so every elementary differential enters.
+    w = di.make(system, 1)
+    th = w.theta[:, 0]
+    y = w.y0[:, 0] + (np.array([0.3, -0.2, 0.1, 0.05, 0.2, -0.1]) if system == "loghalo" else 0.0)
+    # (the step sizes keep the error above rounding, where the slope is clean)
+    hs = (0.08, 0.04, 0.02, 0.01) if system == "loghalo" else (0.02, 0.01, 0.005, 0.0025)
+    e_main, e_emb = [], []
+    for h in hs:
+        ynew, est = orc.step(system, RODAS, th, y, h)
+        nsub = 400
+        ref = orc.replay(system, VERN, th[:, None], y[:, None], np.array([nsub]),
+                         np.full((1, nsub), h / nsub))[:, 0]
+        e_main.append(np.linalg.norm(ynew - ref))
+        e_emb.append(np.linalg.norm(ynew - est - ref))
+    s_main = np.log2(np.array(e_main[:-1]) / np.array(e_main[1:]))
+    s_emb = np.log2(np.array(e_emb[:-1]) / np.array(e_emb[1:]))
+    assert np.all(np.abs(s_main - 6.0) < 0.35) and abs(s_main[-1] - 6.0) < 0.1, s_main
+    assert np.all(np.abs(s_emb - 5.0) < 0.3) and abs(s_emb[-1] - 5.0) < 0.1, s_emb
+
+
+def test_rodas5p_decay_closed_form_and_robertson_invariants(orc):
+    from test_oracle_tableau import _rodas_R
+
+    w = di.make("decay", 24)
+    w.method = RODAS
+    r = solve_w(orc, w)
+    assert np.all(r["status"] == 0)
+    dth, dy0, yS = orc.grad(w.system, w.method, w.theta, w.y0, r["count"], r["h"],
+                            np.ones((1, w.n)))
+    for k in range(w.n):
+        h = r["h"][k, :r["count"][k]]
+        Rz = np.array([_rodas_R(orc, -w.theta[0, k] * hh).real for hh in h])
+        assert yS[0, k] == pytest.approx(w.y0[0, k] * np.prod(Rz), rel=1e-12)
+        assert dy0[0, k] == pytest.approx(np.prod(Rz), rel=1e-12)
+        cont = w.y0[0, k] * np.exp(-w.theta[0, k] * w.t1)
+        assert abs(r["y1"][0, k] - cont) <= 50 * (w.rtol * abs(cont) + w.atol)
+    # Robertson: mass conserved by every stage solve; the cotangent (1,1,1)
+    # gives zero rate gradient and dL/dy0 = (1,1,1)
+    w = di.make("robertson_rodas5p", 16)
+    r = solve_w(orc, w, s_cap=4096)
+    assert np.all(r["status"] == 0)
+    assert np.max(np.abs(r["y1"].sum(axis=0) - 1.0)) < 1e-13
+    dth, dy0, _ = orc.grad(w.system, w.method, w.theta, w.y0, r["count"], r["h"],
+                           np.ones((3, w.n)))
+    assert np.max(np.abs(dth * w.theta)) < 1e-10
+    assert np.max(np.abs(dy0 - 1.0)) < 1e-11
+
+
 def test_tsit5_error_estimate_order(orc):
     # e = h sum (b - bhat) k is O(h^5): halving h divides it by ~32.
     th = np.array([1.0, 0.7, 0.9, 1.2])
@@ -409,7 +463,7 @@ def test_mlp_constant_field(orc):
 CASES = [("decay", TSIT), ("lotka_volterra", TSIT), ("lorenz63", TSIT), ("loghalo", TSIT),
          ("robertson", ROS), ("mlp", TSIT), ("lotka_volterra", ROS), ("lorenz63", ROS),
          ("hires", ROS), ("decay", VERN), ("lotka_volterra", VERN), ("lorenz63", VERN),
-         ("loghalo", VERN)]
+         ("loghalo", VERN), ("robertson", RODAS), ("lotka_volterra", RODAS), ("hires", RODAS)]
 
 
 def _case(orc, system, method, n):

