@@ -91,6 +91,20 @@ WORKLOADS = {
     "loghalo_vern7": dict(s_cap=8192, with_t=False, states=False, init=124, att=842,
                           acc_extra=15, replay=633, grad=2 * 633 - 15 - 90 + 37 + 456 + 9 * 41,
                           peak=78.6e12, bound="alu", cpu_n=1024),
+    # Rodas5P on the stiff ensembles.  Not FSAL (acc_extra = F_f: Robertson 8,
+    # HIRES 35).  Gradient step: replay R + the recomputed stages (R - d) + the
+    # reverse 32 d^2 + 93 d + 8 V + 29 + JV: eight transposed solves
+    # 8 (2 d^2 - d), the Jacobian cotangent 8 x 2 d^2, eight field VJPs of V
+    # flops (Robertson 20, HIRES 76), the 28 C and 15 a stage couplings, the
+    # cotangent sums and 1/h, and the Jacobian's pull-back JV (19, 32).
+    "robertson_rodas5p": dict(s_cap=1024, with_t=False, states=False, init=68, att=514,
+                              acc_extra=8, replay=499,
+                              grad=2 * 499 - 3 + 32 * 9 + 93 * 3 + 8 * 20 + 29 + 19,
+                              peak=78.6e12, bound="alu", cpu_n=8192),
+    "hires_rodas5p": dict(s_cap=2048, with_t=False, states=False, init=192, att=2356,
+                          acc_extra=35, replay=2338,
+                          grad=2 * 2338 - 8 + 32 * 64 + 93 * 8 + 8 * 76 + 29 + 32,
+                          peak=78.6e12, bound="alu", cpu_n=1024),
 }
 # Forward sensitivities (solve_sens, Tsit5): per accepted step and parameter
 # direction, the stage tangents and the tangent update take 48 d flops, plus
@@ -215,7 +229,8 @@ CPU_SAMPLES = {"lotka_volterra": (256, 256, 256), "lorenz63": (65536, 32768, 102
                "mlp": (16384, 4096, 128), "robertson": (131072, 32768, 1024),
                "loghalo": (16384, 4096, 64), "hires": (8192, 2048, 64),
                "lorenz63_spread": (32768, 8192, 512), "lorenz63_vern7": (65536, 32768, 1024),
-               "loghalo_vern7": (16384, 4096, 64)}
+               "loghalo_vern7": (16384, 4096, 64), "robertson_rodas5p": (131072, 32768, 1024),
+               "hires_rodas5p": (8192, 2048, 64)}
 
 
 def cpu_threads():

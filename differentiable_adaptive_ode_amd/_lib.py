@@ -17,7 +17,7 @@ STATUS_NAMES = {0: "DAO_OK", 1: "DAO_EINVAL", 2: "DAO_EDEVICE", 3: "DAO_EWORKSPA
                 4: "DAO_EUNSUPPORTED"}
 SYSTEMS = {"decay": 0, "lotka_volterra": 1, "lorenz63": 2, "mlp": 3, "robertson": 4,
            "loghalo": 5, "hires": 6}
-METHODS = {"tsit5": 0, "rosenbrock23": 1, "vern7": 2}
+METHODS = {"tsit5": 0, "rosenbrock23": 1, "vern7": 2, "rodas5p": 3}
 DTYPES = {"f64": 0, "f32": 1}
 TRAJ_STATUS = {0: "ok", 1: "max_steps", 2: "nonfinite", 3: "dt_underflow", 4: "capacity"}
 

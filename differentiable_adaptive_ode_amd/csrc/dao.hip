@@ -172,7 +172,7 @@ const int SYS_D[7] = {1, 2, 3, 4, 3, 6, 8};
 const int SYS_P[7] = {1, 4, 3, 4740, 3, 3, 12};
 
 bool sys_ok(int sys) { return sys >= 0 && sys <= 6; }
-bool method_ok(int m) { return m == DAO_TSIT5 || m == DAO_ROSENBROCK23 || m == DAO_VERNER7; }
+bool method_ok(int m) { return m >= DAO_TSIT5 && m <= DAO_RODAS5P; }
 
 struct DevInfo {
   int cus = 0;
@@ -702,17 +702,17 @@ Impl make_impl() {
               &Entry<R, S, M>::grad_at, &Entry<R, S, M>::slot_at_bytes};
 }
 
-// Verner 7: solve, gradient, states and gradient at requested times; no
-// forward sensitivities.
-template <class R, template <class> class S>
-Impl make_impl_vern7() {
-  using E = Entry<R, S, M_VERN7>;
+// Verner 7 and Rodas5P: solve, gradient, states and gradient at requested
+// times; no forward sensitivities.
+template <class R, template <class> class S, int M>
+Impl make_impl_no_sens() {
+  using E = Entry<R, S, M>;
   return Impl{&E::solve, &E::grad, &E::slot_bytes, &E::resident_waves, WAVE, nullptr, nullptr,
               &E::states, &E::solve_ws, &E::grad_at, &E::slot_at_bytes};
 }
 
 const Impl* find_impl(int sys, int method, int dtype) {
-  static Impl table[7][3][2];
+  static Impl table[7][4][2];
   static bool init = false;
   static std::mutex mu;
   std::lock_guard<std::mutex> lk(mu);
@@ -739,10 +739,17 @@ const Impl* find_impl(int sys, int method, int dtype) {
     table[DAO_SYS_HIRES][M_TSIT5][DAO_F64] = make_impl<double, Hires, M_TSIT5>();
     table[DAO_SYS_HIRES][M_ROS23][DAO_F64] = make_impl<double, Hires, M_ROS23>();
     table[DAO_SYS_HIRES][M_ROS23][DAO_F32] = make_impl<float, Hires, M_ROS23>();
-    table[DAO_SYS_DECAY][M_VERN7][DAO_F64] = make_impl_vern7<double, Decay>();
-    table[DAO_SYS_LOTKA_VOLTERRA][M_VERN7][DAO_F64] = make_impl_vern7<double, LotkaVolterra>();
-    table[DAO_SYS_LORENZ63][M_VERN7][DAO_F64] = make_impl_vern7<double, Lorenz63>();
-    table[DAO_SYS_LOGHALO][M_VERN7][DAO_F64] = make_impl_vern7<double, LogHalo>();
+    table[DAO_SYS_DECAY][M_VERN7][DAO_F64] = make_impl_no_sens<double, Decay, M_VERN7>();
+    table[DAO_SYS_LOTKA_VOLTERRA][M_VERN7][DAO_F64] =
+        make_impl_no_sens<double, LotkaVolterra, M_VERN7>();
+    table[DAO_SYS_LORENZ63][M_VERN7][DAO_F64] = make_impl_no_sens<double, Lorenz63, M_VERN7>();
+    table[DAO_SYS_LOGHALO][M_VERN7][DAO_F64] = make_impl_no_sens<double, LogHalo, M_VERN7>();
+    table[DAO_SYS_DECAY][M_RODAS5P][DAO_F64] = make_impl_no_sens<double, Decay, M_RODAS5P>();
+    table[DAO_SYS_LOTKA_VOLTERRA][M_RODAS5P][DAO_F64] =
+        make_impl_no_sens<double, LotkaVolterra, M_RODAS5P>();
+    table[DAO_SYS_ROBERTSON][M_RODAS5P][DAO_F64] =
+        make_impl_no_sens<double, Robertson, M_RODAS5P>();
+    table[DAO_SYS_HIRES][M_RODAS5P][DAO_F64] = make_impl_no_sens<double, Hires, M_RODAS5P>();
     table[DAO_SYS_MLP][M_TSIT5][DAO_F32] =
         Impl{&launch_mlp_solve, &launch_mlp_grad, &mlp_slot_bytes, &mlp_resident_waves, mlp::SLOTS,
              nullptr, nullptr, nullptr, &mlp_solve_ws, nullptr, nullptr};

@@ -18,6 +18,7 @@
 
 #include "common.hpp"
 #include "mlp.hpp"
+#include "rodas5p.hpp"
 #include "ros23.hpp"
 #include "systems.hpp"
 #include "tsit5.hpp"
@@ -25,7 +26,7 @@
 
 namespace dao {
 
-enum Method : int { M_TSIT5 = 0, M_ROS23 = 1, M_VERN7 = 2 };
+enum Method : int { M_TSIT5 = 0, M_ROS23 = 1, M_VERN7 = 2, M_RODAS5P = 3 };
 
 template <class R>
 struct SolveArgs {
@@ -165,9 +166,10 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   int sdir[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) sdir[j] = j;
-  constexpr int ORDER = (METHOD == M_TSIT5) ? 5 : (METHOD == M_VERN7) ? 7 : 2;
-  // msq^(-1/Q) = err^(-1/(p+1)), p the pair's lower order (4, 6, 2)
-  constexpr int CTRL_Q = (METHOD == M_TSIT5) ? 10 : (METHOD == M_VERN7) ? 14 : 6;
+  constexpr int ORDER = (METHOD == M_VERN7) ? 7 : (METHOD == M_ROS23) ? 2 : 5;
+  // msq^(-1/Q) = err^(-1/(p+1)), p the pair's lower order (Tsit5 and Rodas5P 4,
+  // Verner 7 6, Rosenbrock23 2)
+  constexpr int CTRL_Q = (METHOD == M_VERN7) ? 14 : (METHOD == M_ROS23) ? 6 : 10;
   constexpr int NK = (METHOD == M_VERN7) ? 10 : 7;  // stage derivatives per attempt
   constexpr int32_t RUNNING = -1;
   const int lane = laneId();
@@ -412,10 +414,14 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     } else if constexpr (METHOD == M_VERN7) {
       vern7::trial<R, Sys>(sys, y, hs, k, ynew, err);
       sys.f(ynew, F2);  // not FSAL: f at the new state, kept if the step is taken
+    } else if constexpr (METHOD == M_RODAS5P) {
+      rodas5p::trial<R, Sys>(sys, y, hs, k[0], ynew, err);
+      sys.f(ynew, F2);  // not FSAL
     } else {
       ros23::trial<R, Sys, !SENS>(sys, y, hs, k[0], ynew, F2, err);
     }
-    const R es = (METHOD == M_ROS23) ? hs / R(6) : hs;
+    // the estimate's factor: h (explicit pairs), h/6 (Rosenbrock23), 1 (Rodas5P)
+    const R es = (METHOD == M_ROS23) ? hs / R(6) : (METHOD == M_RODAS5P) ? R(1) : hs;
     R wt[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) {
@@ -458,7 +464,8 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
 
     const bool take = (st == RUNNING) && acc;
     const R tn = last ? a.t1 : t + hs;
-    static_assert(!(SENS && METHOD == M_VERN7), "no in-solve sensitivities for Verner 7");
+    static_assert(!(SENS && (METHOD == M_VERN7 || METHOD == M_RODAS5P)),
+                  "in-solve sensitivities are for Tsit5 and Rosenbrock23");
     if constexpr (SENS) {
       if (take) {
         if constexpr (METHOD == M_TSIT5) {
@@ -712,6 +719,8 @@ grad_kernel(GradArgs<R> a) {
           tsit5::replay<R, Sys>(C5, sys, y, hj);
         else if constexpr (METHOD == M_VERN7)
           vern7::replay<R, Sys>(sys, y, hj);
+        else if constexpr (METHOD == M_RODAS5P)
+          rodas5p::replay<R, Sys>(sys, y, hj);
         else
           ros23::replay<R, Sys>(sys, y, hj);
       };
@@ -759,6 +768,10 @@ grad_kernel(GradArgs<R> a) {
           vern7::Stages<R, D> S;
           vern7::stages<R, Sys>(sys, yq, hq, S);
           vern7::sweep<R, Sys>(sys, S, hq, lq, pb);
+        } else if constexpr (METHOD == M_RODAS5P) {
+          rodas5p::Stages<R, D> S;
+          rodas5p::stages<R, Sys>(sys, yq, hq, S);
+          rodas5p::sweep<R, Sys>(sys, S, hq, lq, pb);
         } else {
           ros23::Stages<R, D> S;
           ros23::stages<R, Sys>(sys, yq, hq, S);
@@ -810,6 +823,10 @@ grad_kernel(GradArgs<R> a) {
           vern7::Stages<R, D> S;
           vern7::stages<R, Sys>(sys, yj, hj, S);
           vern7::sweep<R, Sys>(sys, S, hj, lam, pb);
+        } else if constexpr (METHOD == M_RODAS5P) {
+          rodas5p::Stages<R, D> S;
+          rodas5p::stages<R, Sys>(sys, yj, hj, S);
+          rodas5p::sweep<R, Sys>(sys, S, hj, lam, pb);
         } else {
           ros23::Stages<R, D> S;
           ros23::stages<R, Sys>(sys, yj, hj, S);
@@ -1101,6 +1118,8 @@ __global__ void __launch_bounds__(256) states_kernel(StatesArgs<R> a) {
         tsit5::replay<R, Sys>(C5, sys, ys, hs);
       else if constexpr (METHOD == M_VERN7)
         vern7::replay<R, Sys>(sys, ys, hs);
+      else if constexpr (METHOD == M_RODAS5P)
+        rodas5p::replay<R, Sys>(sys, ys, hs);
       else
         ros23::replay<R, Sys>(sys, ys, hs);
       if (adv) {

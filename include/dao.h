@@ -71,10 +71,16 @@ typedef enum {
 typedef enum {
   DAO_TSIT5 = 0,        /* Tsitouras 5(4) pair, 7 stages, FSAL (Sec. 2.1)                  */
   DAO_ROSENBROCK23 = 1, /* Shampine-Reichelt second-order Rosenbrock, autonomous (Sec. 3.2) */
-  DAO_VERNER7 = 2       /* Verner 7(6) pair, 10 stages, not FSAL (Sec. 3.1 method list);
+  DAO_VERNER7 = 2,      /* Verner 7(6) pair, 10 stages, not FSAL (Sec. 3.1 method list);
                            binary64 with decay, Lotka-Volterra, Lorenz-63 and the log halo;
                            solve, gradients and states at requested times (no forward
                            sensitivities: DAO_EUNSUPPORTED)                               */
+  DAO_RODAS5P = 3       /* Rodas5P, 8-stage stiffly accurate L-stable Rosenbrock-Wanner
+                           method of order 5(4) (Sec. 3.1: the general stiff engine;
+                           Sec. 3.2: one factorisation of I/(gamma h) - J per step, one
+                           solve per stage); autonomous systems; binary64 with decay,
+                           Lotka-Volterra, Robertson and HIRES; solve, gradients and
+                           states at requested times (no forward sensitivities)           */
 } dao_method;
 
 typedef enum { DAO_F64 = 0, DAO_F32 = 1 } dao_dtype;

@@ -688,6 +688,14 @@ void ros23_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* yn
 template <class T, bool PLAIN = false>
 void rodas5p_step(int sys, const T* th, int d, const T* y, T h, const T* F0, T* ynew, T* err,
                   double* kabs = nullptr) {
+  if (rv(h) == 0.0) {  // the step map's limit at h = 0 is the identity (1/h stays out)
+    for (int c = 0; c < d; ++c) ynew[c] = y[c];
+    if (err)
+      for (int c = 0; c < d; ++c) err[c] = T(0.0);
+    if (kabs)
+      for (int c = 0; c < d; ++c) kabs[c] = 0.0;
+    return;
+  }
   T J[MAXD * MAXD], W[MAXD * MAXD], rp[MAXD];
   int piv[MAXD];
   jac(sys, th, y, J);

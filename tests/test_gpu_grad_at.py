@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = 1e-9
 DEV = "cuda:0"
-LOG_RATES = ("robertson", "hires")
+LOG_RATES = ("robertson", "hires", "robertson_rodas5p", "hires_rodas5p")
 
 
 @pytest.fixture(scope="module")
@@ -55,7 +55,9 @@ def times(w, ref, m):
 CASES = [("decay", 300, 256), ("lotka_volterra", 300, 256), ("lorenz63", 300, 1024),
          ("loghalo", 130, 4096), ("robertson", 200, 2048), ("hires", 130, 4096),
          ("decay_vern7", 300, 256), ("lotka_volterra_vern7", 300, 256),
-         ("lorenz63_vern7", 300, 1024), ("loghalo_vern7", 200, 4096)]
+         ("lorenz63_vern7", 300, 1024), ("loghalo_vern7", 200, 4096),
+         ("decay_rodas5p", 300, 256), ("robertson_rodas5p", 200, 1024),
+         ("lotka_volterra_rodas5p", 200, 256), ("hires_rodas5p", 130, 2048)]
 
 
 @pytest.mark.parametrize("name,n,s_cap", CASES)

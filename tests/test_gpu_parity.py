@@ -68,10 +68,12 @@ CASES = [("decay", 300, 256), ("lotka_volterra", 300, 256), ("lorenz63", 300, 10
          ("loghalo", 200, 4096), ("robertson", 200, 2048), ("hires", 200, 4096),
          ("lorenz63_spread", 300, 2048),
          ("decay_vern7", 300, 256), ("lotka_volterra_vern7", 300, 256),
-         ("lorenz63_vern7", 300, 1024), ("loghalo_vern7", 200, 4096)]
+         ("lorenz63_vern7", 300, 1024), ("loghalo_vern7", 200, 4096),
+         ("decay_rodas5p", 300, 256), ("robertson_rodas5p", 200, 1024),
+         ("lotka_volterra_rodas5p", 200, 256), ("hires_rodas5p", 130, 2048)]
 # systems whose rate constants span orders of magnitude: their gradients are
 # compared as log-sensitivities theta * dL/dtheta
-LOG_RATES = ("robertson", "hires")
+LOG_RATES = ("robertson", "hires", "robertson_rodas5p", "hires_rodas5p")
 
 
 @pytest.mark.parametrize("name,n,s_cap", CASES)

@@ -1,0 +1,112 @@
+"""GPU tests of Rodas5P beyond the shared parity lists: the gradient at a
+moved theta on the GPU's own mesh, the full-size Robertson ensemble
+(262,144 trajectories) in the benchmark's launch configuration sampled against
+the oracle, the two-phase solve equal to one phase bit for bit, and the
+refusal of the forward sensitivities it does not provide."""
+import numpy as np
+import pytest
+import torch
+
+import dao_inputs as di
+import oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 1e-9
+
+
+@pytest.fixture(scope="module")
+def dao():
+    import differentiable_adaptive_ode_amd as m
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def rel_err(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return np.linalg.norm(a - b, axis=0) / np.maximum(np.linalg.norm(b, axis=0), 1e-300)
+
+
+def _solve(dao, w, s_cap, **kw):
+    th = torch.tensor(w.theta, device=DEV)
+    y0 = torch.tensor(w.y0, device=DEV)
+    rec, y1 = dao.solve(w.system, w.method, th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=s_cap, **kw)
+    torch.cuda.synchronize()
+    return rec, y1
+
+
+@pytest.mark.parametrize("name,n,s_cap", [("robertson_rodas5p", 200, 1024),
+                                          ("hires_rodas5p", 130, 2048)])
+def test_rodas5p_gradient_at_moved_theta(dao, name, n, s_cap):
+    w = di.make(name, n)
+    print(f"[rodas5p moved theta] {name} n={n}", flush=True)
+    rec, y1 = _solve(dao, w, s_cap)
+    ref = oracle.solve(w.system, w.method, w.theta, w.y0, w.t0, w.t1, w.rtol, w.atol,
+                       s_cap=s_cap, nthreads=8)
+    assert np.array_equal(rec.count.cpu().numpy(), ref["count"])
+    th2 = w.theta * 1.001
+    lam = np.random.default_rng(3).normal(size=w.y0.shape)
+    dth_o, dy0_o, _ = oracle.grad(w.system, w.method, th2, w.y0, ref["count"], ref["h"], lam,
+                                  nthreads=8)
+    dth, dy0 = dao.grad(rec, torch.tensor(lam, device=DEV), theta=torch.tensor(th2, device=DEV))
+    torch.cuda.synchronize()
+    # rates span orders of magnitude: compared as log-sensitivities
+    assert rel_err(dth.cpu().numpy() * th2, dth_o * th2).max() <= TOL
+    assert rel_err(dy0.cpu().numpy(), dy0_o).max() <= TOL
+
+
+def test_rodas5p_robertson_full_size_sampled(dao):
+    w = di.make("robertson_rodas5p")
+    print(f"[rodas5p full size] robertson n={w.n}", flush=True)
+    rec, y1 = _solve(dao, w, 1024, record_t=False)
+    assert rec.stats_host()["failed"] == 0
+    cnt = rec.count.cpu().numpy()
+    lam_all = torch.tensor(di.cotangent(w, y1.cpu().numpy()), device=DEV)
+    dth, dy0 = dao.grad(rec, lam_all, s_max=int(cnt.max()))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    idx = np.unique(np.concatenate([rng.choice(w.n, 96, replace=False), [0, w.n - 1],
+                                    [np.argmax(cnt), np.argmin(cnt)]]))
+    ws = di.subset(w, idx)
+    ref = oracle.solve(ws.system, ws.method, ws.theta, ws.y0, ws.t0, ws.t1, ws.rtol, ws.atol,
+                       s_cap=1024, nthreads=8)
+    assert np.array_equal(cnt[idx], ref["count"])
+    assert rel_err(y1.cpu().numpy()[:, idx], ref["y1"]).max() <= TOL
+    h = rec.h.cpu().numpy()[idx]
+    mask = np.arange(1024)[None, :] < cnt[idx][:, None]
+    assert np.array_equal(h[mask], ref["h"][mask])
+    dth_o, dy0_o, _ = oracle.grad(ws.system, ws.method, ws.theta, ws.y0, ref["count"], ref["h"],
+                                  lam_all.cpu().numpy()[:, idx], nthreads=8)
+    g = dth.cpu().numpy()[:, idx]
+    assert rel_err(g * ws.theta, dth_o * ws.theta).max() <= TOL
+    assert rel_err(dy0.cpu().numpy()[:, idx], dy0_o).max() <= TOL
+
+
+def test_rodas5p_two_phase_equals_one_phase(dao):
+    w = di.make("robertson_rodas5p", 300)
+    print("[rodas5p two-phase] robertson n=300", flush=True)
+    out = [_solve(dao, w, 1024, phases=p) for p in (1, 2)]
+    (r1, y1a), (r2, y1b) = out
+    assert torch.equal(r1.count, r2.count) and torch.equal(r1.nrej, r2.nrej)
+    assert torch.equal(y1a, y1b)
+    cnt = r1.count.cpu().numpy()
+    mask = torch.tensor(np.arange(1024)[None, :] < cnt[:, None], device=DEV)
+    assert torch.equal(r1.h[mask], r2.h[mask])
+
+
+def test_rodas5p_refuses_forward_sensitivities_and_other_systems(dao):
+    from differentiable_adaptive_ode_amd import DaoError
+
+    w = di.make("robertson_rodas5p", 70)
+    th = torch.tensor(w.theta, device=DEV)
+    y0 = torch.tensor(w.y0, device=DEV)
+    with pytest.raises(DaoError, match="not provided"):
+        dao.solve_sens(w.system, "rodas5p", th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=1024)
+    rec, _ = dao.solve(w.system, "rodas5p", th, y0, w.t0, w.t1, w.rtol, w.atol, s_cap=1024)
+    with pytest.raises(DaoError, match="not provided"):
+        dao.sens(rec)
+    wl = di.make("lorenz63", 8)
+    with pytest.raises(DaoError, match="not provided"):
+        dao.solve("lorenz63", "rodas5p", torch.tensor(wl.theta, device=DEV),
+                  torch.tensor(wl.y0, device=DEV), 0.0, 1.0, 1e-6, 1e-10, s_cap=64)

@@ -33,7 +33,9 @@ def rel_err(a, b):
 CASES = [("decay", 300, 256), ("lotka_volterra", 300, 256), ("lorenz63", 300, 1024),
          ("loghalo", 200, 4096), ("robertson", 200, 2048), ("hires", 200, 4096),
          ("decay_vern7", 300, 256), ("lotka_volterra_vern7", 300, 256),
-         ("lorenz63_vern7", 300, 1024), ("loghalo_vern7", 200, 4096)]
+         ("lorenz63_vern7", 300, 1024), ("loghalo_vern7", 200, 4096),
+         ("decay_rodas5p", 300, 256), ("robertson_rodas5p", 200, 1024),
+         ("lotka_volterra_rodas5p", 200, 256), ("hires_rodas5p", 130, 2048)]
 
 
 @pytest.mark.parametrize("name,n,s_cap", CASES)
@@ -46,7 +48,7 @@ def test_states_at_parity(dao, name, n, s_cap):
     rng = np.random.default_rng(3)
     span = w.t1 - w.t0
     tq = np.sort(np.concatenate([[w.t0, w.t1], w.t0 + span * rng.random(37)]))
-    if name == "robertson":  # stiff transient early on: log-spaced times too
+    if name in ("robertson", "robertson_rodas5p"):  # stiff transient early on: log-spaced times too
         tq = np.sort(np.concatenate([tq, np.logspace(-5, 4.9, 12)]))
     tq_d = torch.tensor(tq, device=DEV)
     yq = dao.states_at(rec, tq_d)
