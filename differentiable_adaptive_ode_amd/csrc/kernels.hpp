@@ -420,13 +420,17 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     } else {
       ros23::trial<R, Sys, !SENS>(sys, y, hs, k[0], ynew, F2, err);
     }
-    // the estimate's factor: h (explicit pairs), h/6 (Rosenbrock23), 1 (Rodas5P)
-    const R es = (METHOD == M_ROS23) ? hs / R(6) : (METHOD == M_RODAS5P) ? R(1) : hs;
+    // the estimate's factor: h (explicit pairs), h/6 (Rosenbrock23), 1 (Rodas5P).
+    // The weights s / sc_c only scale the mean square, whose accept test and
+    // 16-bit-truncated controller factor absorb last-ulp differences (a flip
+    // needs msq within ~1e-16 relative of 1 or of a truncation boundary), so
+    // they are formed with a refined hardware reciprocal, not IEEE division.
+    const R es = (METHOD == M_ROS23) ? hs * R(1.0 / 6.0) : (METHOD == M_RODAS5P) ? R(1) : hs;
     R wt[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) {
       const R ay = absR(y[c]), an = absR(ynew[c]);
-      wt[c] = es / fmaR(a.rtol, (ay < an) ? an : ay, a.atol);
+      wt[c] = es * rcpR(fmaR(a.rtol, (ay < an) ? an : ay, a.atol));
     }
     const R msq = error_msq<R, D>(err, wt);
     const bool acc = msq <= R(1);
