@@ -219,6 +219,27 @@ def summarize(args) -> None:
                          f"{g(iss['fp64_fma'])} | {g(iss['fp64_trans'])} | "
                          f"{g(iss['fp64_lane_flops'])} | {g(iss['counter_flops_fp64'])} | "
                          f"{g(iss['counter_flops_fp32'])} | {g(iss['mfma_f32_flops'])} |")
+    if getattr(args, "stall", None):
+        # Where the wavefronts' cycles go: issuing vector instructions, issuing
+        # any instruction, waiting on anything (memory, dependencies), waiting
+        # for an instruction to be issued -- each over the wavefronts' lifetime.
+        st, _ = read_counters(args.stall)
+        lines += ["", "Stall counters (fractions of SQ_WAVE_CYCLES, summed over the device; "
+                  "SQ_WAVES wavefronts of the launch):", "", "    " + args.cmd_stall, "",
+                  "| kernel | SQ_WAVES | VALU active | any instruction active | waiting (any) | "
+                  "waiting for issue | VALU thread utilisation |", "|---|---|---|---|---|---|---|"]
+        for key in traffic["kernels"]:
+            def c(name):
+                xs = [v for (nm, cc), vv in st.items() if cc == name and _short(nm) == key for v in vv]
+                return sum(xs) / len(xs) if xs else None
+            wc = c("SQ_WAVE_CYCLES")
+            if not wc:
+                continue
+            r = lambda v: "-" if v is None else f"{v / wc:.3f}"  # noqa: E731
+            tv, iv = c("SQ_THREAD_CYCLES_VALU"), c("SQ_ACTIVE_INST_VALU")
+            util = "-" if not (tv and iv) else f"{tv / (64.0 * iv):.3f}"
+            lines.append(f"| {key} | {c('SQ_WAVES'):.0f} | {r(iv)} | {r(c('SQ_ACTIVE_INST_ANY'))} | "
+                         f"{r(c('SQ_WAIT_ANY'))} | {r(c('SQ_WAIT_INST_ANY'))} | {util} |")
     lines += ["", f"Kernel sources sha256: `{traffic['kernel_source_sha256']}`", ""]
     path = os.path.join(args.out, f"{args.workload}_n{args.n}_kernels.md")
     with open(path, "w") as f:
@@ -243,6 +264,8 @@ def main(argv=None):
     s.add_argument("--cmd-sq", default="")
     s.add_argument("--flops", default=None)
     s.add_argument("--cmd-flops", default="")
+    s.add_argument("--stall", default=None)
+    s.add_argument("--cmd-stall", default="")
     s.add_argument("--out", default=os.path.join(os.path.dirname(HERE), "profiles"))
     a = ap.parse_args(argv)
     if a.cmd == "summarize":
