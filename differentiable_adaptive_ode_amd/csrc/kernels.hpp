@@ -425,13 +425,14 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     // 16-bit-truncated controller factor absorb last-ulp differences (a flip
     // needs msq within ~1e-16 relative of 1 or of a truncation boundary), so
     // they are formed with a refined hardware reciprocal, not IEEE division.
+    // max(|y_c|, |y_new,c|) is one instruction (absmaxR: equal to the
+    // comparison's choice for every non-NaN pair; a NaN state fails the step
+    // either way, through msq).
     const R es = (METHOD == M_ROS23) ? hs * R(1.0 / 6.0) : (METHOD == M_RODAS5P) ? R(1) : hs;
     R wt[D];
 #pragma unroll
-    for (int c = 0; c < D; ++c) {
-      const R ay = absR(y[c]), an = absR(ynew[c]);
-      wt[c] = es * rcpR(fmaR(a.rtol, (ay < an) ? an : ay, a.atol));
-    }
+    for (int c = 0; c < D; ++c)
+      wt[c] = es * rcpR(fmaR(a.rtol, absmaxR(y[c], ynew[c]), a.atol));
     const R msq = error_msq<R, D>(err, wt);
     const bool acc = msq <= R(1);
     // One controller evaluation serves both outcomes.
@@ -584,9 +585,16 @@ struct RowRing {
 // shortened step Phi(y_J; tau - t_J) with each time's cotangent (time by
 // time, all lanes together), and the sweep adds it to lam once it has taken
 // lam through step J.
+//
+// Register budgets (measured choices): Rosenbrock23 with d <= 3 is held to
+// 128 registers, four wavefronts per SIMD; Verner 7 without requested times
+// to 256, two wavefronts per SIMD with a few spills, which beats one
+// wavefront with its overflow in accumulation registers (log-halo gradient
+// 15.7 -> 14.9 ms); with requested times the spills would be many and one
+// wavefront is faster.
 template <class R, class Sys, int METHOD, bool AT = false>
 __global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu((METHOD == M_ROS23 && Sys::D <= 3) ? 4 : 1)))
+__attribute__((amdgpu_waves_per_eu((METHOD == M_ROS23 && Sys::D <= 3) ? 4 : (METHOD == M_VERN7 && !AT) ? 2 : 1)))
 grad_kernel(GradArgs<R> a) {
   constexpr int D = Sys::D, P = Sys::P;
   const int lane = laneId();

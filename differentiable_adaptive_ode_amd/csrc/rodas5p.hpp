@@ -60,8 +60,8 @@ __device__ __forceinline__ void run(const Sys& sys, const R (&y)[Sys::D], R h,
   constexpr int D = Sys::D;
   R J[D][D];
   sys.jac(y, J);
-  const R ginv = R(1) / (R(GAMMA) * h);
-  const R hinv = R(1) / h;
+  const R ginv = recipR(R(GAMMA) * h);
+  const R hinv = recipR(h);
 #pragma unroll
   for (int i = 0; i < D; ++i)
 #pragma unroll
@@ -152,7 +152,7 @@ __device__ __forceinline__ void sweep(const Sys& sys, const Stages<R, Sys::D>& S
                                       R (&lam)[Sys::D], R (&pb)[Sys::P]) {
   constexpr int D = Sys::D, P = Sys::P;
   const bool zero = (h == R(0));
-  const R hinv = R(1) / (zero ? R(1) : h);
+  const R hinv = recipR(zero ? R(1) : h);
   R ub[8][D], yb[D], Yb[D], Jb[D][D], pt[P];
 #pragma unroll
   for (int c = 0; c < D; ++c) {

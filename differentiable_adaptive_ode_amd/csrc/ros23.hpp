@@ -78,7 +78,7 @@ __device__ __forceinline__ void factor(LU<R, D>& f) {
         }
       }
     }
-    f.rp[k] = R(1) / f.m[k][k];
+    f.rp[k] = recipR(f.m[k][k]);
 #pragma unroll
     for (int i = k + 1; i < D; ++i) {
       R l = f.m[i][k] * f.rp[k];

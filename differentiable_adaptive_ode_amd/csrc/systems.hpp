@@ -357,17 +357,18 @@ struct Hires {
 template <class R>
 struct LogHalo {
   static constexpr int D = 6, P = 3;
-  R v0, rc, q, v2, r2, iq2;
+  R v0, rc, q, v2, r2, iq2, diq2;
   __device__ void load(const R* theta, int64_t n, int64_t k) {
     v0 = theta[k]; rc = theta[n + k]; q = theta[2 * n + k];
     v2 = v0 * v0;
     r2 = rc * rc;
     iq2 = R(1) / (q * q);
+    diq2 = (R(-2) * iq2) / q;  // d(1/q^2)/dq, once per trajectory
   }
   __device__ void f(const R (&y)[D], R (&dy)[D]) const {
     R zq = y[2] * iq2;
     R Dn = fmaR(y[0], y[0], fmaR(y[1], y[1], fmaR(y[2], zq, r2)));
-    R A = v2 / Dn;
+    R A = divR(v2, Dn);
     dy[0] = y[3];
     dy[1] = y[4];
     dy[2] = y[5];
@@ -382,7 +383,7 @@ struct LogHalo {
   __device__ void vjp(const R (&y)[D], const R (&v)[D], R (&yb)[D], R (&pb)[P]) const {
     R zq = y[2] * iq2;
     R Dn = fmaR(y[0], y[0], fmaR(y[1], y[1], fmaR(y[2], zq, r2)));
-    R iD = R(1) / Dn;
+    R iD = recipR(Dn);
     R A = v2 * iD;
     R s = fmaR(v[3], y[0], fmaR(v[4], y[1], v[5] * zq));
     R u = (s * A) * iD;
@@ -395,13 +396,12 @@ struct LogHalo {
     yb[5] = v[2];
     pb[0] = fmaR(-(s + s) * v0, iD, pb[0]);
     pb[1] = fmaR(u2, rc, pb[1]);
-    R dq = (R(-2) * iq2) / q;
-    pb[2] = fmaR(fmaR(u, y[2], -A * v[5]) * y[2], dq, pb[2]);
+    pb[2] = fmaR(fmaR(u, y[2], -A * v[5]) * y[2], diq2, pb[2]);
   }
   __device__ void jac(const R (&y)[D], R (&J)[D][D]) const {
     R zq = y[2] * iq2;
     R Dn = fmaR(y[0], y[0], fmaR(y[1], y[1], fmaR(y[2], zq, r2)));
-    R iD = R(1) / Dn;
+    R iD = recipR(Dn);
     R A = v2 * iD;
     R g[3] = {y[0], y[1], zq};
     R dD[3] = {R(2) * y[0], R(2) * y[1], R(2) * zq};
@@ -436,12 +436,12 @@ struct LogHalo {
   __device__ void jvp(const R (&y)[D], const R (&yd)[D], int j, R (&fd)[D]) const {
     const R zq = y[2] * iq2;
     const R Dn = fmaR(y[0], y[0], fmaR(y[1], y[1], fmaR(y[2], zq, r2)));
-    const R iD = R(1) / Dn;
+    const R iD = recipR(Dn);
     const R A = v2 * iD;
-    const R diq2 = (j == 2) ? (R(-2) * iq2) / q : R(0);  // d(1/q^2)/dq
-    const R gzd = fmaR(yd[2], iq2, y[2] * diq2);
+    const R dq2 = (j == 2) ? diq2 : R(0);  // d(1/q^2)/dq along direction j
+    const R gzd = fmaR(yd[2], iq2, y[2] * dq2);
     R Dnd = R(2) * fmaR(y[0], yd[0], fmaR(y[1], yd[1], zq * yd[2]));
-    Dnd = fmaR(y[2] * y[2], diq2, (j == 1) ? fmaR(R(2) * rc, R(1), Dnd) : Dnd);
+    Dnd = fmaR(y[2] * y[2], dq2, (j == 1) ? fmaR(R(2) * rc, R(1), Dnd) : Dnd);
     const R Ad = fmaR(-A, Dnd, (j == 0) ? R(2) * v0 : R(0)) * iD;
     fd[0] = yd[3];
     fd[1] = yd[4];
