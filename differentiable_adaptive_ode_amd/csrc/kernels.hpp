@@ -588,10 +588,9 @@ struct RowRing {
 //
 // Register budgets (measured choices): Rosenbrock23 with d <= 3 is held to
 // 128 registers, four wavefronts per SIMD; Verner 7 without requested times
-// to 256, two wavefronts per SIMD with a few spills, which beats one
-// wavefront with its overflow in accumulation registers (log-halo gradient
-// 15.7 -> 14.9 ms); with requested times the spills would be many and one
-// wavefront is faster.
+// to 256, two wavefronts per SIMD (one wavefront with its overflow in
+// accumulation registers was slower); with requested times the spills would
+// be many and one wavefront is faster.
 template <class R, class Sys, int METHOD, bool AT = false>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu((METHOD == M_ROS23 && Sys::D <= 3) ? 4 : (METHOD == M_VERN7 && !AT) ? 2 : 1)))

@@ -205,14 +205,32 @@ template <class R, class Sys>
 __device__ __forceinline__ void stages(const Coef<R>& C, const Sys& sys, const R (&y)[Sys::D], R h,
                                        Stages<R, Sys::D>& S) {
   constexpr int D = Sys::D;
-  R k[7][D];
+  // Each stage's sum a_i0 k_0 + a_i1 k_1 + ... is built as the k_j appear, j
+  // ascending (the order stage_state uses, so the same bits), and each k_j
+  // dies as soon as it is added: the live set is the sums still open plus
+  // the stage states kept, not every k_j beside every stage state.
+  R acc[6][D];
+  R k[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) S.Y[0][c] = y[c];
-  sys.f(S.Y[0], k[0]);
+  sys.f(S.Y[0], k);
 #pragma unroll
-  for (int i = 1; i < 6; ++i) {
-    stage_state<R, D>(C, i, y, h, k, S.Y[i]);
-    sys.f(S.Y[i], k[i]);
+  for (int i = 1; i < 6; ++i)
+#pragma unroll
+    for (int c = 0; c < D; ++c) acc[i][c] = C.a[i][0] * k[c];
+#pragma unroll
+  for (int j = 1; j < 6; ++j) {
+#pragma unroll
+    for (int c = 0; c < D; ++c) S.Y[j][c] = fmaR(h, acc[j][c], y[c]);
+    if (j < 5) {
+      sys.f(S.Y[j], k);
+#pragma unroll
+      for (int i = 2; i < 6; ++i)
+        if (i > j) {
+#pragma unroll
+          for (int c = 0; c < D; ++c) acc[i][c] = fmaR(C.a[i][j], k[c], acc[i][c]);
+        }
+    }
   }
 }
 
@@ -220,28 +238,34 @@ template <class R, class Sys>
 __device__ __forceinline__ void sweep(const Coef<R>& C, const Sys& sys, const Stages<R, Sys::D>& S,
                                       R h, R (&lam)[Sys::D], R (&pb)[Sys::P]) {
   constexpr int D = Sys::D;
-  // y_new = y + h * sum_j b_j k_j with b_j = a(6, j):  kb_j = h b_j lam.
-  R kb[6][D];
+  // y_new = y + h sum_j b_j k_j (b_j = a(6, j)) and Y_i = y + h sum_{j<i} a_ij k_j,
+  // so the cotangent of k_i is
+  //   kb_i = h b_i lam + sum_{m > i} h a_mi yb_m,  yb_m = (df/dy)(Y_m)^T kb_m,
+  // with lam = dL/dy_{j+1} as it was on entry.  kb_i is formed when stage i
+  // is reached, from the yb of the stages already swept, added m = 5, 4, ...,
+  // i + 1 (the order in which each would be pushed into it as it appears;
+  // the same bits): only the yb of swept stages are live, not an open
+  // cotangent for every stage.
+  R lam0[D];
 #pragma unroll
-  for (int j = 0; j < 6; ++j) {
-    R hb = h * C.a[6][j];
-#pragma unroll
-    for (int c = 0; c < D; ++c) kb[j][c] = hb * lam[c];
-  }
-  R yb[D];
+  for (int c = 0; c < D; ++c) lam0[c] = lam[c];
+  R yb[6][D];
 #pragma unroll
   for (int i = 5; i >= 0; --i) {
-    sys.vjp(S.Y[i], kb[i], yb, pb);
+    R kb[D];
+    const R hb = h * C.a[6][i];
 #pragma unroll
-    for (int c = 0; c < D; ++c) lam[c] += yb[c];
+    for (int c = 0; c < D; ++c) kb[c] = hb * lam0[c];
 #pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      if (j < i) {
-        R ha = h * C.a[i][j];
+    for (int m = 5; m > 0; --m)
+      if (m > i) {
+        const R ha = h * C.a[m][i];
 #pragma unroll
-        for (int c = 0; c < D; ++c) kb[j][c] = fmaR(ha, yb[c], kb[j][c]);
+        for (int c = 0; c < D; ++c) kb[c] = fmaR(ha, yb[m][c], kb[c]);
       }
-    }
+    sys.vjp(S.Y[i], kb, yb[i], pb);
+#pragma unroll
+    for (int c = 0; c < D; ++c) lam[c] += yb[i][c];
   }
 }
 

@@ -128,14 +128,32 @@ template <class R, class Sys>
 __device__ __forceinline__ void stages(const Sys& sys, const R (&y)[Sys::D], R h,
                                        Stages<R, Sys::D>& S) {
   constexpr int D = Sys::D;
-  R k[9][D];
+  // Each stage's sum is built as the k_j appear, j ascending with the zero
+  // entries skipped (the order stage_state uses, so the same bits); each k_j
+  // dies once added, so the live set is the open sums plus the stage states
+  // kept, not every k_j beside every stage state.
+  R acc[9][D];
+  R k[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) S.Y[0][c] = y[c];
-  sys.f(S.Y[0], k[0]);
+  sys.f(S.Y[0], k);
 #pragma unroll
-  for (int i = 1; i < 9; ++i) {
-    stage_state<R, D, 9>(i, y, h, k, S.Y[i]);
-    if (i < 8) sys.f(S.Y[i], k[i]);
+  for (int i = 1; i < 9; ++i)
+#pragma unroll
+    for (int c = 0; c < D; ++c) acc[i][c] = R(A[i][0]) * k[c];
+#pragma unroll
+  for (int j = 1; j < 9; ++j) {
+#pragma unroll
+    for (int c = 0; c < D; ++c) S.Y[j][c] = fmaR(h, acc[j][c], y[c]);
+    if (j < 8) {
+      sys.f(S.Y[j], k);
+#pragma unroll
+      for (int i = 2; i < 9; ++i)
+        if (i > j && A[i][j] != 0.0) {
+#pragma unroll
+          for (int c = 0; c < D; ++c) acc[i][c] = fmaR(R(A[i][j]), k[c], acc[i][c]);
+        }
+    }
   }
 }
 
@@ -143,28 +161,32 @@ template <class R, class Sys>
 __device__ __forceinline__ void sweep(const Sys& sys, const Stages<R, Sys::D>& S, R h,
                                       R (&lam)[Sys::D], R (&pb)[Sys::P]) {
   constexpr int D = Sys::D;
-  // y_new = y + h sum_j b_j k_j:  kb_j = h b_j lam (zero for stages 2, 3).
-  R kb[9][D];
+  // y_new = y + h sum_j b_j k_j and Y_i = y + h sum_{j<i} a_ij k_j, so
+  //   kb_i = h b_i lam + sum_{m > i} h a_mi yb_m,  yb_m = (df/dy)(Y_m)^T kb_m,
+  // with lam as it was on entry (b_i = 0 for stages 2, 3: the sum alone).
+  // kb_i is formed when stage i is reached, from the yb of the stages already
+  // swept, added m = 8, 7, ..., i + 1 (the order in which each would be
+  // pushed into it; the same bits): only the yb of swept stages are live.
+  R lam0[D];
 #pragma unroll
-  for (int j = 0; j < 9; ++j) {
-    const R hb = h * R(B[j]);
-#pragma unroll
-    for (int c = 0; c < D; ++c) kb[j][c] = (B[j] != 0.0) ? hb * lam[c] : R(0);
-  }
-  R yb[D];
+  for (int c = 0; c < D; ++c) lam0[c] = lam[c];
+  R yb[9][D];
 #pragma unroll
   for (int i = 8; i >= 0; --i) {
-    sys.vjp(S.Y[i], kb[i], yb, pb);
+    R kb[D];
+    const R hb = h * R(B[i]);
 #pragma unroll
-    for (int c = 0; c < D; ++c) lam[c] += yb[c];
+    for (int c = 0; c < D; ++c) kb[c] = (B[i] != 0.0) ? hb * lam0[c] : R(0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < i && A[i][j] != 0.0) {
-        const R ha = h * R(A[i][j]);
+    for (int m = 8; m > 0; --m)
+      if (m > i && i < 8 && A[m][i] != 0.0) {
+        const R ha = h * R(A[m][i]);
 #pragma unroll
-        for (int c = 0; c < D; ++c) kb[j][c] = fmaR(ha, yb[c], kb[j][c]);
+        for (int c = 0; c < D; ++c) kb[c] = fmaR(ha, yb[m][c], kb[c]);
       }
-    }
+    sys.vjp(S.Y[i], kb, yb[i], pb);
+#pragma unroll
+    for (int c = 0; c < D; ++c) lam[c] += yb[i][c];
   }
 }
 
