@@ -135,7 +135,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="loghalo",
+    ap.add_argument("--workload", default="loghalo", choices=sorted(WORKLOADS),
                     help="the headline ensemble (default: the largest, the log-halo orbits)")
     ap.add_argument("--n", type=int, default=None,
                     help="trajectories (default: the workload's own ensemble size); e.g. the "
