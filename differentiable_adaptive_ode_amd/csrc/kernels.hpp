@@ -432,7 +432,7 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     R wt[D];
 #pragma unroll
     for (int c = 0; c < D; ++c)
-      wt[c] = es * rcpR(fmaR(a.rtol, absmaxR(y[c], ynew[c]), a.atol));
+      wt[c] = es * rcpW(fmaR(a.rtol, absmaxR(y[c], ynew[c]), a.atol));
     const R msq = error_msq<R, D>(err, wt);
     const bool acc = msq <= R(1);
     // One controller evaluation serves both outcomes.
