@@ -7,9 +7,9 @@
 // recipR / divR below, which return the same bits for operands of normal
 // magnitude.  So a forward solve computes the same bits as any other
 // implementation that follows the same contract.  The one exception is the
-// error weights s / sc_c, formed as s times the reciprocal (two roundings
-// where a quotient has one): they only scale the mean square that the accept
-// test and the truncated controller factor read.
+// error weights s / sc_c, formed as s times a reciprocal within 11 ulp (rcpW):
+// they only scale the mean square that the accept test and the truncated
+// controller factor read.
 #pragma once
 
 #include <hip/hip_runtime.h>
