@@ -422,9 +422,10 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
     }
     // the estimate's factor: h (explicit pairs), h/6 (Rosenbrock23), 1 (Rodas5P).
     // The weights s / sc_c only scale the mean square, whose accept test and
-    // 16-bit-truncated controller factor absorb last-ulp differences (a flip
-    // needs msq within ~1e-16 relative of 1 or of a truncation boundary), so
-    // they are formed with a refined hardware reciprocal, not IEEE division.
+    // 16-bit-truncated controller factor absorb differences of a few ulp (a
+    // flip needs msq within ~3e-15 relative of 1 or of a truncation
+    // boundary), so they are formed with the hardware reciprocal and one
+    // Newton step (rcpW, within 11 ulp), not IEEE division.
     // max(|y_c|, |y_new,c|) is one instruction (absmaxR: equal to the
     // comparison's choice for every non-NaN pair; a NaN state fails the step
     // either way, through msq).

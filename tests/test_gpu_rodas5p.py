@@ -1,7 +1,7 @@
 """GPU tests of Rodas5P beyond the shared parity lists: the gradient at a
-moved theta on the GPU's own mesh, the full-size Robertson ensemble
-(262,144 trajectories) in the benchmark's launch configuration sampled against
-the oracle, the two-phase solve equal to one phase bit for bit, and the
+moved theta on the GPU's own mesh, the full-size Robertson (262,144) and
+HIRES (131,072) ensembles in the benchmark's launch configuration sampled
+against the oracle, the two-phase solve equal to one phase bit for bit, and the
 refusal of the forward sensitivities it does not provide."""
 import numpy as np
 import pytest
@@ -56,10 +56,12 @@ def test_rodas5p_gradient_at_moved_theta(dao, name, n, s_cap):
     assert rel_err(dy0.cpu().numpy(), dy0_o).max() <= TOL
 
 
-def test_rodas5p_robertson_full_size_sampled(dao):
-    w = di.make("robertson_rodas5p")
-    print(f"[rodas5p full size] robertson n={w.n}", flush=True)
-    rec, y1 = _solve(dao, w, 1024, record_t=False)
+@pytest.mark.parametrize("name,s_cap", [("robertson_rodas5p", 1024), ("hires_rodas5p", 2048)])
+def test_rodas5p_full_size_sampled(dao, name, s_cap):
+    # the benchmark's ensemble at its own size and record capacity
+    w = di.make(name)
+    print(f"[rodas5p full size] {name} n={w.n}", flush=True)
+    rec, y1 = _solve(dao, w, s_cap, record_t=False)
     assert rec.stats_host()["failed"] == 0
     cnt = rec.count.cpu().numpy()
     lam_all = torch.tensor(di.cotangent(w, y1.cpu().numpy()), device=DEV)
@@ -70,11 +72,11 @@ def test_rodas5p_robertson_full_size_sampled(dao):
                                     [np.argmax(cnt), np.argmin(cnt)]]))
     ws = di.subset(w, idx)
     ref = oracle.solve(ws.system, ws.method, ws.theta, ws.y0, ws.t0, ws.t1, ws.rtol, ws.atol,
-                       s_cap=1024, nthreads=8)
+                       s_cap=s_cap, nthreads=8)
     assert np.array_equal(cnt[idx], ref["count"])
     assert rel_err(y1.cpu().numpy()[:, idx], ref["y1"]).max() <= TOL
     h = rec.h.cpu().numpy()[idx]
-    mask = np.arange(1024)[None, :] < cnt[idx][:, None]
+    mask = np.arange(s_cap)[None, :] < cnt[idx][:, None]
     assert np.array_equal(h[mask], ref["h"][mask])
     dth_o, dy0_o, _ = oracle.grad(ws.system, ws.method, ws.theta, ws.y0, ref["count"], ref["h"],
                                   lam_all.cpu().numpy()[:, idx], nthreads=8)

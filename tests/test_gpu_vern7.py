@@ -1,6 +1,7 @@
 """GPU tests of the Verner 7(6) pair beyond the shared parity lists: the
-gradient at a moved theta on the GPU's own mesh, the full-size Lorenz ensemble
-in the benchmark's launch configuration (sampled against the oracle), the
+gradient at a moved theta on the GPU's own mesh, the full-size Lorenz and
+orbit ensembles in the benchmark's launch configuration (sampled against the
+oracle), the
 two-phase solve of the orbit ensemble equal to one phase bit for bit, and the
 refusal of the forward sensitivities it does not provide."""
 import numpy as np
@@ -55,10 +56,13 @@ def test_vern7_gradient_at_moved_theta(dao, name, n, s_cap):
     assert rel_err(dy0.cpu().numpy(), dy0_o).max() <= TOL
 
 
-def test_vern7_lorenz_full_size_sampled(dao):
-    w = di.make("lorenz63_vern7")
-    print(f"[vern7 full size] lorenz63 n={w.n}", flush=True)
-    rec, y1 = _solve(dao, w, 1024, record_t=False)
+@pytest.mark.parametrize("name,s_cap", [("lorenz63_vern7", 1024), ("loghalo_vern7", 8192)])
+def test_vern7_full_size_sampled(dao, name, s_cap):
+    # the benchmark's ensemble at its own size and record capacity (the
+    # orbits' 2^20 trajectories take the two-phase solve)
+    w = di.make(name)
+    print(f"[vern7 full size] {name} n={w.n}", flush=True)
+    rec, y1 = _solve(dao, w, s_cap, record_t=False)
     assert rec.stats_host()["failed"] == 0
     cnt = rec.count.cpu().numpy()
     lam_all = torch.tensor(di.cotangent(w, y1.cpu().numpy()), device=DEV)
@@ -70,11 +74,11 @@ def test_vern7_lorenz_full_size_sampled(dao):
                                     [np.argmax(cnt), np.argmin(cnt)]]))
     ws = di.subset(w, idx)
     ref = oracle.solve(ws.system, ws.method, ws.theta, ws.y0, ws.t0, ws.t1, ws.rtol, ws.atol,
-                       s_cap=1024, nthreads=8)
+                       s_cap=s_cap, nthreads=8)
     assert np.array_equal(cnt[idx], ref["count"])
     assert rel_err(y1.cpu().numpy()[:, idx], ref["y1"]).max() <= TOL
     h = rec.h.cpu().numpy()[idx]
-    mask = np.arange(1024)[None, :] < cnt[idx][:, None]
+    mask = np.arange(s_cap)[None, :] < cnt[idx][:, None]
     assert np.array_equal(h[mask], ref["h"][mask])
     dth_o, dy0_o, _ = oracle.grad(ws.system, ws.method, ws.theta, ws.y0, ref["count"], ref["h"],
                                   lam_all.cpu().numpy()[:, idx], nthreads=8)
