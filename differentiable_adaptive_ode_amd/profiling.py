@@ -34,14 +34,40 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments, whitespace runs collapsed: what the
+    compiler sees, so that an edited comment does not invalidate a profile."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":  # string or character literal, copied whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest() -> str:
-    """sha256 over the HIP sources (file names and contents, sorted)."""
+    """sha256 over the HIP sources' code (file names and contents without
+    comments, sorted)."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".hpp", ".h")):
             h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
