@@ -227,9 +227,10 @@ constexpr int32_t SOLVE_PROBE = 64;
 size_t solve_base_bytes() { return ALIGN + align_up((size_t)WAVE * 2 * sizeof(double)); }
 
 // save (the state of a suspended trajectory, with room for its
-// sensitivities), save_i, key, perm, histogram
+// sensitivities; one contiguous record per trajectory), save_i, key, perm,
+// histogram
 template <class R, int D, int P>
-size_t solve_save_reals() { return (size_t)(2 * D + 2 + D * P); }
+size_t solve_save_reals() { return (size_t)save_stride<R, D, P>(); }
 template <class R, int D, int P>
 size_t solve_phase_bytes(int64_t n) {
   return align_up(solve_save_reals<R, D, P>() * n * sizeof(R)) + align_up((size_t)2 * n * 4) +

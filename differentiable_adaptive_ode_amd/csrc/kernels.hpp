@@ -28,6 +28,17 @@ namespace dao {
 
 enum Method : int { M_TSIT5 = 0, M_ROS23 = 1, M_VERN7 = 2, M_RODAS5P = 3 };
 
+// Values per trajectory in the two-phase solve's parking area: y, f(y), t, h
+// and room for the sensitivities, rounded up to whole 64-byte lines.  A
+// trajectory's record is contiguous, so the phase-2 resume, which visits
+// trajectories in an order unrelated to their index, reads one or two lines
+// per trajectory instead of one line per value.
+template <class R, int D, int P>
+constexpr int save_stride() {
+  constexpr int v = 2 * D + 2 + D * P, u = 64 / (int)sizeof(R);
+  return (v + u - 1) / u * u;
+}
+
 template <class R>
 struct SolveArgs {
   int64_t n;
@@ -52,8 +63,8 @@ struct SolveArgs {
   // the queue order `order`.
   int phase;              // 1 or 2
   int32_t probe;          // attempts per trajectory in phase 1
-  R* save;                // [2D + 2 (+ D P)][n]: y, f(y), t, h (and S) of a suspended trajectory
-  int32_t* save_i;        // [2][n]: accepted count; rejected count * 2 + last-rejected flag
+  R* save;                // [n][save_stride]: y, f(y), t, h (and S) of a suspended trajectory
+  int32_t* save_i;        // [n][2]: accepted count; rejected count * 2 + last-rejected flag
   int32_t* key;           // [n] phase 1: predicted remaining attempts, log scale
   const int32_t* order;   // [n] phase 2: queue position -> trajectory
 };
@@ -254,21 +265,22 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
   // for the next attempt goes to a.save, its unwritten record rows to memory
   // (phase 2 reloads them into the ring), and status stays RUNNING.
   auto suspend = [&]() {
+    R* const sv = a.save + traj * save_stride<R, D, Sys::P>();
 #pragma unroll
     for (int c = 0; c < D; ++c) {
-      a.save[c * a.n + traj] = y[c];
-      a.save[(D + c) * a.n + traj] = k[0][c];
+      sv[c] = y[c];
+      sv[D + c] = k[0][c];
     }
-    a.save[(2 * D) * a.n + traj] = t;
-    a.save[(2 * D + 1) * a.n + traj] = h;
+    sv[2 * D] = t;
+    sv[2 * D + 1] = h;
     if constexpr (SENS) {
 #pragma unroll
       for (int c = 0; c < D; ++c)
 #pragma unroll
-        for (int j = 0; j < NS; ++j) a.save[(2 * D + 2 + c * NS + j) * a.n + traj] = Sv[c][j];
+        for (int j = 0; j < NS; ++j) sv[2 * D + 2 + c * NS + j] = Sv[c][j];
     }
-    a.save_i[traj] = nacc;
-    a.save_i[a.n + traj] = nrej * 2 + (prev_rej ? 1 : 0);
+    a.save_i[2 * traj] = nacc;
+    a.save_i[2 * traj + 1] = nrej * 2 + (prev_rej ? 1 : 0);
     a.status[traj] = RUNNING;
     const double done = (double)(t - a.t0), left = (double)(a.t1 - t);
     const double rem = (done > 0.0) ? (double)attempts * left / done : 1e30;
@@ -334,21 +346,22 @@ __global__ void __launch_bounds__(256) solve_kernel(SolveArgs<R> a) {
       if (PHASED && a.phase == 2 && go) {
         traj = tk;
         sys.load(a.theta, a.n, traj);
+        const R* const sv = a.save + traj * save_stride<R, D, Sys::P>();
 #pragma unroll
         for (int c = 0; c < D; ++c) {
-          y[c] = a.save[c * a.n + traj];
-          k[0][c] = a.save[(D + c) * a.n + traj];
+          y[c] = sv[c];
+          k[0][c] = sv[D + c];
         }
-        t = a.save[(2 * D) * a.n + traj];
-        h = a.save[(2 * D + 1) * a.n + traj];
+        t = sv[2 * D];
+        h = sv[2 * D + 1];
         if constexpr (SENS) {
 #pragma unroll
           for (int c = 0; c < D; ++c)
 #pragma unroll
-            for (int j = 0; j < NS; ++j) Sv[c][j] = a.save[(2 * D + 2 + c * NS + j) * a.n + traj];
+            for (int j = 0; j < NS; ++j) Sv[c][j] = sv[2 * D + 2 + c * NS + j];
         }
-        nacc = a.save_i[traj];
-        const int32_t rj = a.save_i[a.n + traj];
+        nacc = a.save_i[2 * traj];
+        const int32_t rj = a.save_i[2 * traj + 1];
         __builtin_amdgcn_s_waitcnt(0);
         nrej = rj >> 1;
         prev_rej = (rj & 1) != 0;
