@@ -37,6 +37,32 @@ def _stream(stream=None):
     return _tstream(stream).cuda_stream
 
 
+def _expect(device, *specs):
+    """Each (name, tensor, dtype, shape) of specs (None tensors skipped) must
+    have that dtype and shape and be a contiguous device tensor on `device`
+    (if given).  The kernels take plain pointers and trust the sizes they are
+    told, so every array is checked before its pointer is passed: a cotangent
+    of the wrong type would be read as the record's type, a short one read
+    past its end.  Types and shapes of all arrays are checked first, then
+    where they live."""
+    for name, t, dtype, shape in specs:
+        if t is None:
+            continue
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    for name, t, _, _ in specs:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device (cuda) tensor")
+        if device is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
 def _check_dev(*ts):
     for t in ts:
         if t is not None:
@@ -81,6 +107,7 @@ class Record:
         """Device int64[4] = (max count, total accepted steps, failed
         trajectories, total rejected attempts), written in stream order by
         dao_record_stats; nothing is synchronised."""
+        _expect(self.count.device, ("out", out, torch.int64, (4,)))
         o = torch.empty(4, dtype=torch.int64, device=self.count.device) if out is None else out
         _lib.check(_lib.dao_record_stats(self.n, self.c_struct(), _ptr(o), _stream(stream)))
         return o
@@ -145,6 +172,15 @@ def alloc_record(n: int, s_cap: int, dtype: str, device, with_t: bool = True,
                    if states_dim > 0 else None))
 
 
+def _check_record_buffers(b: dict, n: int, d: int, dtype, device):
+    """Record buffers passed in by the caller (see alloc_record)."""
+    s_cap = b["h"].shape[1] if b["h"].dim() == 2 else -1
+    _expect(device, ("rec_buffers['h']", b["h"], dtype, (n, s_cap)),
+            ("rec_buffers['t']", b.get("t"), dtype, (n, s_cap)),
+            *((f"rec_buffers['{k}']", b[k], torch.int32, (n,)) for k in ("count", "nrej", "status")),
+            ("rec_buffers['y']", b.get("y"), dtype, (n, s_cap, d)))
+
+
 def solve(system: str, method: str, theta: torch.Tensor, y0: torch.Tensor, t0: float, t1: float,
           rtol: float, atol: float, dt0: float = 0.0, max_steps: int = 100000, s_cap: int = 4096,
           record_t: bool = True, record_states: bool = False, out=None, rec_buffers=None,
@@ -167,7 +203,11 @@ def solve(system: str, method: str, theta: torch.Tensor, y0: torch.Tensor, t0: f
     if tuple(theta.shape) != ((p,) if shared else (p, n)):
         raise ValueError("theta has the wrong shape")
     dev = y0.device
+    _expect(dev, ("theta", theta, y0.dtype, theta.shape), ("out", out, y0.dtype, (d, n)),
+            ("out_sens", out_sens if _sens else None, y0.dtype, (d, p, n)))
     y1 = torch.empty_like(y0) if out is None else out
+    if rec_buffers is not None:
+        _check_record_buffers(rec_buffers, n, d, y0.dtype, dev)
     bufs = rec_buffers if rec_buffers is not None else alloc_record(
         n, s_cap, dtype, dev, record_t, d if record_states else 0)
     rec = Record(system, method, dtype, theta, y0, float(t0), float(t1), bufs["h"], bufs.get("t"),
@@ -202,7 +242,7 @@ def sens(rec: Record, theta: torch.Tensor | None = None, with_theta: bool = True
     """Forward sensitivities of y1 through the replay of rec's mesh:
     (S_theta [d][p][n] or None, S_y0 [d][d][n] or None)."""
     th = rec.theta if theta is None else theta
-    _check_dev(th)
+    _expect(rec.count.device, ("theta", th, rec.y0.dtype, rec.theta.shape))
     n = rec.n
     d, p, _ = _lib.dao_system_dims(_lib.SYSTEMS[rec.system])
     s_max = rec.s_cap if s_max is None else min(int(s_max), rec.s_cap)
@@ -224,6 +264,13 @@ def _grad_setup(rec: Record, s_max, workspace, device, stream):
     nb = _lib.dao_grad_workspace_size(*ids, n, s_max)
     buf = _ws(device, workspace, stream).get(nb, device, stream)
     return ids, n, s_max, buf
+
+
+def _check_grad_arrays(rec: Record, th, dLdy1, out_theta, out_y0):
+    """theta and the outputs like the solve's theta and y0; dLdy1 [d][n]."""
+    td, shape = rec.y0.dtype, tuple(rec.y0.shape)
+    _expect(rec.count.device, ("theta", th, td, rec.theta.shape), ("dLdy1", dLdy1, td, shape),
+            ("out_theta", out_theta, td, rec.theta.shape), ("out_y0", out_y0, td, shape))
 
 
 def grad_order(rec: Record, s_max: int | None = None, workspace=None, stream=None) -> int:
@@ -248,10 +295,11 @@ def grad(rec: Record, dLdy1: torch.Tensor, theta: torch.Tensor | None = None, s_
     ordered: the workspace already holds this record's order (grad_order with
              the same workspace and s_max); skips the sort.
     """
-    _check_dev(dLdy1)
     th = rec.theta if theta is None else theta
-    _check_dev(th)
-    dev = dLdy1.device
+    dev = rec.count.device
+    if dLdy1 is None:
+        raise ValueError("dLdy1 is required")
+    _check_grad_arrays(rec, th, dLdy1, out_theta, out_y0)
     ids, n, s_max, buf = _grad_setup(rec, s_max, workspace, dev, stream)
     dth = torch.empty_like(th) if out_theta is None else out_theta
     dy0 = torch.empty_like(rec.y0) if out_y0 is None else out_y0
@@ -268,11 +316,16 @@ def states_at(rec: Record, tq: torch.Tensor, theta: torch.Tensor | None = None,
     rec's mesh, by a shortened step from the start of the step that holds
     each time: [m][d][n]."""
     th = rec.theta if theta is None else theta
-    _check_dev(th, tq)
     n, m = rec.n, int(tq.numel())
     d, _, _ = _lib.dao_system_dims(_lib.SYSTEMS[rec.system])
+    dev = rec.count.device
+    if tq.dim() != 1:
+        raise ValueError("tq must be one-dimensional")
     if tq.dtype != rec.y0.dtype:
         raise TypeError("tq must have the record's dtype")
+    _expect(dev, ("theta", th, rec.y0.dtype, rec.theta.shape),
+            ("out", out, rec.y0.dtype, (m, d, n)))
+    _check_dev(tq)
     s_max = rec.s_cap if s_max is None else min(int(s_max), rec.s_cap)
     ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
     dev = rec.count.device
@@ -295,13 +348,16 @@ def grad_at(rec: Record, tq: torch.Tensor, dLdyq: torch.Tensor, dLdy1: torch.Ten
     on rec's mesh, the states at tq taken as states_at() takes them.
     tq: device [m], ascending in [t0, t1]; dLdyq: [m][d][n]; dLdy1: [d][n] or None."""
     th = rec.theta if theta is None else theta
-    _check_dev(th, tq, dLdyq)
+    if tq.dim() != 1:
+        raise ValueError("tq must be one-dimensional")
     if tq.dtype != rec.y0.dtype or dLdyq.dtype != rec.y0.dtype:
         raise TypeError("tq and dLdyq must have the record's dtype")
     n, m = rec.n, int(tq.numel())
     d, _, _ = _lib.dao_system_dims(_lib.SYSTEMS[rec.system])
     if tuple(dLdyq.shape) != (m, d, n):
         raise ValueError(f"dLdyq must have shape {(m, d, n)}")
+    _check_grad_arrays(rec, th, dLdy1, out_theta, out_y0)
+    _check_dev(tq, dLdyq)
     s_max = rec.s_cap if s_max is None else min(int(s_max), rec.s_cap)
     ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
     dev = rec.count.device
@@ -326,9 +382,14 @@ def grad_at(rec: Record, tq: torch.Tensor, dLdyq: torch.Tensor, dLdy1: torch.Ten
 def cotangent(y1: torch.Tensor, target: torch.Tensor, scale: float = 1.0, d_used: int | None = None,
               out=None, stream=None):
     """dL/dy1 = scale * (y1 - target) on the first d_used components, 0 elsewhere."""
-    _check_dev(y1, target)
+    _check_dev(y1)
+    if y1.dim() != 2:
+        raise ValueError("y1 must be [d, n]")
     d, n = y1.shape
-    d_used = d if d_used is None else d_used
+    d_used = d if d_used is None else int(d_used)
+    if not 0 <= d_used <= d:
+        raise ValueError(f"d_used must lie in [0, {d}]")
+    _expect(y1.device, ("target", target, y1.dtype, (d, n)), ("out", out, y1.dtype, (d, n)))
     o = torch.empty_like(y1) if out is None else out
     _lib.check(_lib.dao_sqerr_cotangent(_lib.DTYPES[_dtype_name(y1)], n, d, d_used, _ptr(y1),
                                         _ptr(target), float(scale), _ptr(o), _stream(stream)))
