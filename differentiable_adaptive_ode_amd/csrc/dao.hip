@@ -25,8 +25,9 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
 // accepted-step count, so that the 64 lanes of a wavefront replay meshes of
 // similar length.  Counts are binned as
 //   bucket = ((s_max + 1) - min(count, s_max + 1)) >> shift
-// with shift chosen so that at most ORDER_BINS bins exist; the order within a
-// bin is arbitrary (each lane's result does not depend on its neighbours).
+// with shift chosen so that at most ORDER_BINS bins exist.  This order (the
+// two-phase solve's) is arbitrary within a bin: a trajectory's solve does not
+// depend on its neighbours.
 // Both passes histogram in LDS first, so global atomics are one per non-empty
 // bin per workgroup rather than one per trajectory.
 __device__ __forceinline__ int bucket_of(int32_t c, int64_t s_max, int shift) {
@@ -94,6 +95,144 @@ __global__ void __launch_bounds__(256) order_scatter_kernel(const int32_t* count
   __syncthreads();
   for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x)
     perm[atomicAdd(&lh[bucket_of(count[i], s_max, shift)], 1u)] = (int32_t)i;
+}
+
+// Stable variant, for the replays of a record (gradient, sensitivities,
+// states at requested times): within a bin the trajectories keep their index
+// order, so the order, and with it which trajectories share a wavefront, is a
+// function of the counts alone.  The ensemble is cut into slices of whole
+// 64-trajectory tiles (order_slice_len); order_slice_hist_kernel writes each
+// slice's histogram into a table [slice][bin], order_slice_scan_kernel turns
+// each bin's column into the slices' starting ranks within the bin (and the
+// bin's total into hist), scan_buckets_kernel makes hist the bins' starting
+// positions, and order_stable_scatter_kernel, one workgroup per slice, places
+// the slice's trajectories tile by tile: a trajectory's position is its bin's
+// next free position plus the number of lower lanes of its tile in the same
+// bin.
+__global__ void __launch_bounds__(256) order_slice_hist_kernel(const int32_t* count, int64_t n,
+                                                               int64_t s_max, int shift, int nb,
+                                                               int64_t len, uint32_t* table) {
+  __shared__ uint32_t lh[ORDER_BINS];
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) lh[b] = 0u;
+  __syncthreads();
+  const int64_t lo = (int64_t)blockIdx.x * len;
+  const int64_t hi = (lo + len < n) ? lo + len : n;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x)
+    atomicAdd(&lh[bucket_of(count[i], s_max, shift)], 1u);
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) table[(int64_t)blockIdx.x * nb + b] = lh[b];
+}
+
+// One thread per bin: exclusive prefix of the bin's column over the slices,
+// in place, and the bin's total into hist[b].
+__global__ void __launch_bounds__(256) order_slice_scan_kernel(uint32_t* table, int64_t slices,
+                                                               int nb, uint32_t* hist) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nb) return;
+  uint32_t run = 0;
+  int64_t s = 0;
+  for (; s + 8 <= slices; s += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = table[(s + u) * nb + b];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      table[(s + u) * nb + b] = run;
+      run += v[u];
+    }
+  }
+  for (; s < slices; ++s) {
+    const uint32_t v = table[s * nb + b];
+    table[s * nb + b] = run;
+    run += v;
+  }
+  hist[b] = run;
+}
+
+constexpr int ORDER_BATCH = 8;  // tiles whose counts are loaded at once
+// The workgroup's four wavefronts place a quarter of the slice's tiles each:
+// a histogram per wavefront in LDS, then for every bin its slice's starting
+// position plus the counts of the lower wavefronts, then each wavefront walks
+// its tiles in order.  Lanes of a tile in the same bin are those whose bin
+// agrees in every bit: one ballot per bit, and m ^ (bit ? 0 : ~0) keeps the
+// lanes that agree with this lane on it.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+__global__ void __launch_bounds__(256) order_stable_scatter_kernel(
+    const int32_t* count, int64_t n, int64_t s_max, int shift, int nb, int64_t len,
+    const uint32_t* table, const uint32_t* off, int32_t* perm) {
+  __shared__ uint32_t next[4][ORDER_BINS];
+  const int lane = threadIdx.x % WAVE;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  for (int b = threadIdx.x; b < 4 * ORDER_BINS; b += 256) (&next[0][0])[b] = 0u;
+  __syncthreads();
+  const int64_t lo = (int64_t)blockIdx.x * len;
+  const int64_t hi = (lo + len < n) ? lo + len : n;
+  const int64_t tiles = (hi - lo + WAVE - 1) / WAVE;
+  const int64_t per = (tiles + 3) / 4;
+  const int64_t t0 = wv * per, t1 = (t0 + per < tiles) ? t0 + per : tiles;
+  // bins of ORDER_BATCH tiles at a time (-1: past the slice); the loads
+  // are unconditional (index clamped into the slice) so that they overlap
+  auto load = [&](int64_t tb, int (&bk)[ORDER_BATCH]) {
+    int32_t c[ORDER_BATCH];
+#pragma unroll
+    for (int u = 0; u < ORDER_BATCH; ++u) {
+      const int64_t i = lo + (tb + u) * WAVE + lane;
+      c[u] = count[i < hi ? i : hi - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < ORDER_BATCH; ++u) {
+      const int64_t i = lo + (tb + u) * WAVE + lane;
+      bk[u] = (tb + u < t1 && i < hi) ? bucket_of(c[u], s_max, shift) : -1;
+    }
+  };
+  for (int64_t tb = t0; tb < t1; tb += ORDER_BATCH) {
+    int bk[ORDER_BATCH];
+    load(tb, bk);
+#pragma unroll
+    for (int u = 0; u < ORDER_BATCH; ++u)
+      if (bk[u] >= 0) atomicAdd(&next[wv][bk[u]], 1u);
+  }
+  __syncthreads();
+  const uint32_t* row = table + (int64_t)blockIdx.x * nb;
+  for (int b = threadIdx.x; b < nb; b += 256) {
+    uint32_t run = off[b] + row[b];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t v = next[w][b];
+      next[w][b] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < nb) ++nbits;
+  uint32_t* nx = next[wv];
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int64_t tb = t0; tb < t1; tb += ORDER_BATCH) {
+    int bks[ORDER_BATCH];
+    load(tb, bks);
+#pragma unroll
+    for (int u = 0; u < ORDER_BATCH; ++u) {
+      if (tb + u >= t1) break;  // the same for every lane
+      const bool valid = bks[u] >= 0;
+      const int bk = valid ? bks[u] : 0;
+      unsigned long long peers = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const unsigned long long m = __ballot((bk >> bit) & 1);
+        peers &= m ^ ((unsigned long long)((bk >> bit) & 1) - 1ull);
+      }
+      const uint32_t p = valid ? nx[bk] + (uint32_t)__popcll(peers & below) : 0u;
+      wave_sync();
+      // the highest lane of each bin advances the bin's next position
+      if (valid && (peers >> lane) == 1ull) nx[bk] += (uint32_t)__popcll(peers);
+      wave_sync();
+      if (valid) perm[p] = (int32_t)(lo + (tb + u) * WAVE + lane);
+    }
+  }
 }
 
 // Record summary: max and sum of count, failed trajectories, sum of nrej.
@@ -349,9 +488,64 @@ struct AtArgs {
   double t0, t1;
 };
 
+// The stable order's slices: at most ORDER_SLICES of them, each a whole
+// number of 64-trajectory tiles and at least ORDER_SLICE_MIN long.
+constexpr int64_t ORDER_SLICES = 128;
+constexpr int64_t ORDER_SLICE_MIN = 1024;
+int64_t order_slice_len(int64_t n) {
+  int64_t len = (n + ORDER_SLICES - 1) / ORDER_SLICES;
+  len = (len + WAVE - 1) / WAVE * WAVE;
+  return len < ORDER_SLICE_MIN ? ORDER_SLICE_MIN : len;
+}
+int64_t order_slice_count(int64_t n) {
+  const int64_t k = (n + order_slice_len(n) - 1) / order_slice_len(n);
+  return k < 1 ? 1 : k;
+}
+// Bins of the order by step count: bin = ((s_max + 1) - min(count, s_max + 1)) >> shift.
+int order_shift(int64_t s_max) {
+  int shift = 0;
+  while (((s_max + 1) >> shift) + 1 > ORDER_BINS) ++shift;
+  return shift;
+}
+int order_bins(int64_t s_max) { return (int)(((s_max + 1) >> order_shift(s_max)) + 1); }
+
+// Head of the workspace of a record's replays: queue counter, bin offsets,
+// the order, and the stable order's slice table.
 size_t grad_header_bytes(int64_t n, int64_t s_max) {
-  (void)s_max;
-  return align_up(16) + align_up((size_t)ORDER_BINS * 4) + align_up((size_t)(n > 0 ? n : 1) * 4);
+  return align_up(16) + align_up((size_t)ORDER_BINS * 4) + align_up((size_t)(n > 0 ? n : 1) * 4) +
+         align_up((size_t)order_slice_count(n) * order_bins(s_max) * 4);
+}
+struct OrderWs {
+  unsigned long long* groups;
+  uint32_t* hist;
+  int32_t* perm;
+  uint32_t* table;
+};
+OrderWs order_ws(void* ws, int64_t n) {
+  char* base = (char*)ws;
+  OrderWs o;
+  o.groups = (unsigned long long*)base;
+  o.hist = (uint32_t*)(base + align_up(16));
+  o.perm = (int32_t*)(base + align_up(16) + align_up((size_t)ORDER_BINS * 4));
+  o.table = (uint32_t*)(base + align_up(16) + align_up((size_t)ORDER_BINS * 4) +
+                        align_up((size_t)(n > 0 ? n : 1) * 4));
+  return o;
+}
+
+// Orders a record's trajectories by decreasing step count into o.perm, equal
+// bins in index order.
+void launch_order_stable(const int32_t* count, int64_t n, int64_t s_max, const OrderWs& o,
+                         hipStream_t stream) {
+  const int shift = order_shift(s_max), nb = order_bins(s_max);
+  const int64_t len = order_slice_len(n), slices = order_slice_count(n);
+  hipLaunchKernelGGL(order_slice_hist_kernel, dim3((unsigned)slices), dim3(256), 0, stream, count,
+                     n, s_max, shift, nb, len, o.table);
+  hipLaunchKernelGGL(order_slice_scan_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0,
+                     stream, o.table, slices, nb, o.hist);
+  hipLaunchKernelGGL(scan_buckets_kernel, dim3(1), dim3(1024), 0, stream, o.hist, (int64_t)nb);
+  hipLaunchKernelGGL(order_stable_scatter_kernel, dim3((unsigned)slices), dim3(256), 0, stream,
+                     count, n, s_max, shift, nb, len, (const uint32_t*)o.table,
+                     (const uint32_t*)o.hist, o.perm);
 }
 
 // Orders trajectories by decreasing step count into perm.
@@ -381,9 +575,9 @@ dao_status launch_grad(int mode, int64_t n, const void* theta, const void* y0, c
                        size_t ws_bytes, hipStream_t stream, const AtArgs* at = nullptr) {
   constexpr int D = Sys::D;
   char* base = (char*)ws;
-  unsigned long long* groups = (unsigned long long*)base;
-  uint32_t* hist = (uint32_t*)(base + align_up(16));
-  int32_t* perm = (int32_t*)(base + align_up(16) + align_up((size_t)ORDER_BINS * 4));
+  const OrderWs ow = order_ws(ws, n);
+  unsigned long long* groups = ow.groups;
+  int32_t* perm = ow.perm;
   const size_t hdr = grad_header_bytes(n, s_max);
   R* scratch = (R*)(base + hdr);
   const size_t slot = grad_slot_bytes<R, D>(s_max, AT ? at->m : 0);
@@ -398,7 +592,7 @@ dao_status launch_grad(int mode, int64_t n, const void* theta, const void* y0, c
   if (blocks > slots / waves_per_block) blocks = slots / waves_per_block;
   if (blocks < 1) return fail(DAO_EWORKSPACE, "dao_grad: workspace too small");
 
-  if (mode & GRAD_ORDER) launch_order(rec->count, n, s_max, hist, perm, stream);
+  if (mode & GRAD_ORDER) launch_order_stable(rec->count, n, s_max, ow, stream);
   if (!(mode & GRAD_RUN)) return check_hip(hipGetLastError(), "order kernel launch");
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)groups, (int64_t)2, 0u);
 
@@ -444,9 +638,9 @@ dao_status launch_sens(int64_t n, const void* theta, const void* y0, const dao_r
                        int64_t s_max, void* S_theta, void* S_y0, void* ws, hipStream_t stream) {
   constexpr int D = Sys::D, P = Sys::P;
   char* base = (char*)ws;
-  unsigned long long* groups = (unsigned long long*)base;
-  uint32_t* hist = (uint32_t*)(base + align_up(16));
-  int32_t* perm = (int32_t*)(base + align_up(16) + align_up((size_t)ORDER_BINS * 4));
+  const OrderWs ow = order_ws(ws, n);
+  unsigned long long* groups = ow.groups;
+  int32_t* perm = ow.perm;
   auto kern = sens_kernel<R, Sys, M, P>;
   const int64_t ngroups = (n + WAVE - 1) / WAVE;
   int64_t blocks = (ngroups + BLOCK / WAVE - 1) / (BLOCK / WAVE);
@@ -455,7 +649,7 @@ dao_status launch_sens(int64_t n, const void* theta, const void* y0, const dao_r
   const size_t lds = chunked ? (size_t)BLOCK_WAVES * 16 * WAVE * sizeof(R) : 0;
   const int64_t res = resident_blocks(kern, lds);
   if (blocks > res) blocks = res;
-  launch_order(rec->count, n, s_max, hist, perm, stream);
+  launch_order_stable(rec->count, n, s_max, ow, stream);
   SensArgs<R> a;
   a.chunked = chunked;
   a.n = n;
@@ -486,9 +680,9 @@ dao_status launch_states(int64_t n, const void* theta, const void* y0, double t0
                          const dao_record* rec, int64_t s_max, int64_t m, const void* tq, void* yq,
                          void* ws, hipStream_t stream) {
   char* base = (char*)ws;
-  unsigned long long* groups = (unsigned long long*)base;
-  uint32_t* hist = (uint32_t*)(base + align_up(16));
-  int32_t* perm = (int32_t*)(base + align_up(16) + align_up((size_t)ORDER_BINS * 4));
+  const OrderWs ow = order_ws(ws, n);
+  unsigned long long* groups = ow.groups;
+  int32_t* perm = ow.perm;
   auto kern = states_kernel<R, Sys, M>;
   // h read in chunks staged through LDS when the record's rows allow it
   const bool chunked = rec->s_cap % 8 == 0 && ((uintptr_t)rec->h % 16) == 0;
@@ -497,7 +691,7 @@ dao_status launch_states(int64_t n, const void* theta, const void* y0, double t0
   int64_t blocks = (ngroups + BLOCK / WAVE - 1) / (BLOCK / WAVE);
   const int64_t res = resident_blocks(kern, lds);
   if (blocks > res) blocks = res;
-  launch_order(rec->count, n, s_max, hist, perm, stream);
+  launch_order_stable(rec->count, n, s_max, ow, stream);
   StatesArgs<R> a;
   a.chunked = chunked;
   a.n = n;
@@ -554,22 +748,30 @@ dao_status launch_mlp_solve(int64_t n, const void* theta, const void* y0, double
 }
 
 // Per-wavefront workspace of the neural gradient: the state tile
-// [s_max][64] and the partial weight gradient [4740], both float.
+// [s_max][64] floats.
 size_t mlp_slot_bytes(int64_t s_max) {
-  return align_up((size_t)(s_max > 0 ? s_max : 1) * WAVE * sizeof(float)) +
-         align_up((size_t)mlp::NP * sizeof(float));
+  return align_up((size_t)(s_max > 0 ? s_max : 1) * WAVE * sizeof(float));
+}
+
+// Workspace of the neural gradient that depends on n alone: one row of
+// partial weight-gradient sums [4740] floats per chunk.
+size_t mlp_fixed_bytes(int64_t n) {
+  return align_up((size_t)mlp::grad_chunks(n) * mlp::NP * sizeof(float));
 }
 
 dao_status launch_mlp_grad(int mode, int64_t n, const void* theta, const void* y0, const dao_record* rec,
                            int64_t s_max, const void* dLdy1, void* dLdtheta, void* dLdy0, void* ws,
                            size_t ws_bytes, hipStream_t stream) {
   char* base = (char*)ws;
-  unsigned long long* groups = (unsigned long long*)base;
-  uint32_t* hist = (uint32_t*)(base + align_up(16));
-  int32_t* perm = (int32_t*)(base + align_up(16) + align_up((size_t)ORDER_BINS * 4));
+  const OrderWs ow = order_ws(ws, n);
+  unsigned long long* groups = ow.groups;
+  int32_t* perm = ow.perm;
   const size_t hdr = grad_header_bytes(n, s_max);
+  const size_t fixed = mlp_fixed_bytes(n);
+  const int64_t chunks = mlp::grad_chunks(n);
   const size_t slot = mlp_slot_bytes(s_max);
-  const int64_t slots = (int64_t)((ws_bytes - hdr) / slot);
+  if (ws_bytes < hdr + fixed) return fail(DAO_EWORKSPACE, "dao_grad: workspace too small");
+  const int64_t slots = (int64_t)((ws_bytes - hdr - fixed) / slot);
   const int64_t ngroups = (n + mlp::SLOTS - 1) / mlp::SLOTS;
   const int64_t waves_per_block = BLOCK / WAVE;
   int64_t blocks = (ngroups + waves_per_block - 1) / waves_per_block;
@@ -577,12 +779,10 @@ dao_status launch_mlp_grad(int mode, int64_t n, const void* theta, const void* y
   if (blocks > res) blocks = res;
   if (blocks > slots / waves_per_block) blocks = slots / waves_per_block;
   if (blocks < 1) return fail(DAO_EWORKSPACE, "dao_grad: workspace too small");
-  const int64_t nw = blocks * waves_per_block;
-  float* scratch = (float*)(base + hdr);
-  float* partial = (float*)(base + hdr + (size_t)nw * align_up((size_t)(s_max > 0 ? s_max : 1) *
-                                                                WAVE * sizeof(float)));
+  float* partial = (float*)(base + hdr);
+  float* scratch = (float*)(base + hdr + fixed);
 
-  if (mode & GRAD_ORDER) launch_order(rec->count, n, s_max, hist, perm, stream);
+  if (mode & GRAD_ORDER) launch_order_stable(rec->count, n, s_max, ow, stream);
   if (!(mode & GRAD_RUN)) return check_hip(hipGetLastError(), "order kernel launch");
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)groups, (int64_t)2, 0u);
 
@@ -599,17 +799,18 @@ dao_status launch_mlp_grad(int mode, int64_t n, const void* theta, const void* y
   a.dLdy0 = (float*)dLdy0;
   a.scratch = scratch;
   a.partial = partial;
+  a.chunks = chunks;
   a.perm = perm;
   a.groups = groups;
   hipLaunchKernelGGL(mlp::grad_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, stream, a);
   dao_status st = check_hip(hipGetLastError(), "mlp grad kernel launch");
   if (st != DAO_OK) return st;
   if (dLdtheta) {
-    const int64_t nchunks = (nw + mlp::REDUCE_CHUNK - 1) / mlp::REDUCE_CHUNK;
-    hipLaunchKernelGGL(mlp::reduce_chunks_kernel, dim3((mlp::NP + 255) / 256, (unsigned)nchunks),
-                       dim3(256), 0, stream, partial, nw);
+    const int64_t runs = (chunks + mlp::REDUCE_CHUNK - 1) / mlp::REDUCE_CHUNK;
+    hipLaunchKernelGGL(mlp::reduce_chunks_kernel, dim3((mlp::NP + 255) / 256, (unsigned)runs),
+                       dim3(256), 0, stream, partial, chunks);
     hipLaunchKernelGGL(mlp::reduce_kernel, dim3((mlp::NP + 255) / 256), dim3(256), 0, stream,
-                       (const float*)partial, nw, (float*)dLdtheta);
+                       (const float*)partial, chunks, (float*)dLdtheta);
     st = check_hip(hipGetLastError(), "mlp reduce kernel launch");
   }
   return st;
@@ -690,6 +891,7 @@ struct Impl {
   solve_ws_fn solve_ws;  // workspace of dao_solve for n trajectories
   grad_at_fn grad_at;    // gradient with cotangents at requested times, else null
   slot_at_fn slot_at;
+  solve_ws_fn grad_fixed;  // gradient workspace that depends on n alone, else null
 };
 
 int64_t mlp_resident_waves() { return resident_blocks(mlp::grad_kernel) * (BLOCK / WAVE); }
@@ -753,7 +955,7 @@ const Impl* find_impl(int sys, int method, int dtype) {
     table[DAO_SYS_HIRES][M_RODAS5P][DAO_F64] = make_impl_no_sens<double, Hires, M_RODAS5P>();
     table[DAO_SYS_MLP][M_TSIT5][DAO_F32] =
         Impl{&launch_mlp_solve, &launch_mlp_grad, &mlp_slot_bytes, &mlp_resident_waves, mlp::SLOTS,
-             nullptr, nullptr, nullptr, &mlp_solve_ws, nullptr, nullptr};
+             nullptr, nullptr, nullptr, &mlp_solve_ws, nullptr, nullptr, &mlp_fixed_bytes};
     init = true;
   }
   if (!sys_ok(sys) || !method_ok(method) || dtype < 0 || dtype > 1) return nullptr;
@@ -979,7 +1181,8 @@ size_t dao_grad_workspace_min(dao_system sys, dao_method method, dao_dtype dtype
                               int64_t s_max) {
   const Impl* im = find_impl(sys, method, dtype);
   if (!im || n < 0 || s_max < 0) return 0;
-  return grad_header_bytes(n, s_max) + (size_t)(BLOCK / WAVE) * im->slot(s_max);
+  return grad_header_bytes(n, s_max) + (im->grad_fixed ? im->grad_fixed(n) : 0) +
+         (size_t)(BLOCK / WAVE) * im->slot(s_max);
 }
 
 size_t dao_grad_workspace_size(dao_system sys, dao_method method, dao_dtype dtype, int64_t n,
@@ -991,7 +1194,8 @@ size_t dao_grad_workspace_size(dao_system sys, dao_method method, dao_dtype dtyp
   const int64_t res = im->resident();
   if (waves > res) waves = res;
   if (waves < BLOCK / WAVE) waves = BLOCK / WAVE;
-  return grad_header_bytes(n, s_max) + (size_t)waves * im->slot(s_max);
+  return grad_header_bytes(n, s_max) + (im->grad_fixed ? im->grad_fixed(n) : 0) +
+         (size_t)waves * im->slot(s_max);
 }
 
 }  // extern "C"

@@ -1185,5 +1185,11 @@ __global__ void order_hist_kernel(const int32_t* count, int64_t n, int64_t s_max
 __global__ void scan_buckets_kernel(uint32_t* hist, int64_t nb);
 __global__ void order_scatter_kernel(const int32_t* count, int64_t n, int64_t s_max, int shift,
                                      int nb, uint32_t* off, int32_t* perm);
+__global__ void order_slice_hist_kernel(const int32_t* count, int64_t n, int64_t s_max, int shift,
+                                        int nb, int64_t len, uint32_t* table);
+__global__ void order_slice_scan_kernel(uint32_t* table, int64_t slices, int nb, uint32_t* hist);
+__global__ void order_stable_scatter_kernel(const int32_t* count, int64_t n, int64_t s_max,
+                                            int shift, int nb, int64_t len, const uint32_t* table,
+                                            const uint32_t* off, int32_t* perm);
 
 }  // namespace dao

@@ -414,10 +414,20 @@ struct GradArgs {
   const float* dLdy1;
   float* dLdy0;
   float* scratch;          // per resident wavefront: [s_max][64]
-  float* partial;          // per wavefront: [NP] weight-gradient partial sums
+  float* partial;          // per chunk: [NP] weight-gradient partial sums
+  int64_t chunks;          // chunk c holds the groups c, c + chunks, c + 2 chunks, ...
   const int32_t* perm;
-  unsigned long long* groups;
+  unsigned long long* groups;  // chunk queue counter (zero at launch)
 };
+
+// Chunks of the shared-weight gradient: at most this many rows of partial
+// sums, so their number (and with it every rounding of the sum) depends on n
+// alone, not on the grid or on which wavefront claims which chunk.
+constexpr int64_t MAX_CHUNKS = 2048;
+inline int64_t grad_chunks(int64_t n) {
+  const int64_t ngroups = (n + SLOTS - 1) / SLOTS;
+  return ngroups < MAX_CHUNKS ? (ngroups > 0 ? ngroups : 1) : MAX_CHUNKS;
+}
 
 // Transpose through LDS: x holds unit 16T + 4g + r of slot j in x[T][r]; the
 // result holds, in xt[T][r], unit 16T + j of slot 4g + r (the operand
@@ -460,11 +470,26 @@ struct GradAcc {
 };
 
 // Reverse of one field evaluation at Y (state layout) with output cotangent
-// v: returns ybar = (df/dy)^T v and accumulates the weight cotangents.
+// v: returns ybar = (df/dy)^T v and accumulates the weight cotangents.  The
+// second hidden layer's activations come from h2c (what forward() returned
+// at this Y when the stage was recomputed, 16 values per lane at
+// h2c[(4 T + r) 64]); the first layer is evaluated again (4 products), with
+// the operations forward() uses, so both are the forward pass's bits.
 __device__ __forceinline__ float vjp(const Fwd& P, const Bwd& Q, const float* w2s, float* buf,
-                                     float Y, float v, GradAcc& G, int g, int j) {
+                                     const float* h2c, float Y, float v, GradAcc& G, int g,
+                                     int j) {
+  const W2Lds w2{w2s};
   f4 h1[4], h2[4];
-  (void)forward<W2Lds, false>(P, W2Lds{w2s}, g, j, Y, h1, h2);
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const f4 z = mma(P.w1[T], Y, w2.b1(T, g));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h1[T][r] = tanh_(z[r]);
+  }
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h2[T][r] = h2c[(4 * T + r) * WAVE];
   // dh2 = W3^T v, dz2 = dh2 (1 - h2^2)
   f4 dz2[4];
 #pragma unroll
@@ -557,25 +582,43 @@ __constant__ float TS_A_F32[6][5] = {
 // (st[0..5] = Y_i, st[6..11] = kbar_i, 64 lanes each) so that the six
 // stage VJPs run as one loop body.
 __device__ __forceinline__ void reverse(const Fwd& P, const Bwd& Q, const float* w2s, float* buf,
-                                        float* st, float y, float h, float& lam, GradAcc& G, int g,
-                                        int j) {
+                                        float* st, float* h2s, float y, float h, float& lam,
+                                        GradAcc& G, int g, int j) {
   const W2Lds w2{w2s};
   const int lane = 16 * g + j;
+  // h2s: the second hidden layer of each stage's evaluation, [6][16][64]
+  auto keep_h2 = [&](int i, const f4 (&h2)[4]) {
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h2s[(16 * i + 4 * T + r) * WAVE + lane] = h2[T][r];
+  };
   float k[7];
   float Yi = y;
   st[lane] = Yi;
-  k[0] = rhs(P, w2, g, j, y);
+  {
+    f4 h1[4], h2[4];
+    k[0] = forward(P, w2, g, j, y, h1, h2);
+    keep_h2(0, h2);
+  }
 #pragma unroll
   for (int i = 1; i < 6; ++i) {
     Yi = stage(i, y, h, k);
     st[i * WAVE + lane] = Yi;
-    k[i] = rhs(P, w2, g, j, Yi);
+    f4 h1[4], h2[4];
+    if (i < 5) {
+      k[i] = forward(P, w2, g, j, Yi, h1, h2);
+    } else {
+      (void)forward<W2Lds, false>(P, w2, g, j, Yi, h1, h2);  // f itself is not needed
+    }
+    keep_h2(i, h2);
   }
 #pragma unroll
   for (int i = 0; i < 6; ++i) st[(6 + i) * WAVE + lane] = (h * tsit5::a<float>(6, i)) * lam;
 #pragma unroll 1
   for (int i = 5; i >= 0; --i) {
-    const float yb = vjp(P, Q, w2s, buf, st[i * WAVE + lane], st[(6 + i) * WAVE + lane], G, g, j);
+    const float yb = vjp(P, Q, w2s, buf, h2s + 16 * i * WAVE + lane, st[i * WAVE + lane],
+                         st[(6 + i) * WAVE + lane], G, g, j);
     lam += yb;
     for (int jj = 0; jj < i; ++jj) {
       float& kb = st[(6 + jj) * WAVE + lane];
@@ -594,6 +637,7 @@ __device__ __forceinline__ float row_sum(float x) {
 __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   __shared__ float lds[4][4 * 272];
   __shared__ float stage_lds[4][12 * WAVE];
+  __shared__ float h2_lds[4][6 * 16 * WAVE];
   __shared__ __attribute__((aligned(16))) float w2s[NH * NH + 2 * NH];
   const int lane = laneId();
   const int g = lane >> 4, j = lane & 15;
@@ -615,105 +659,114 @@ __global__ void __launch_bounds__(256) grad_kernel(GradArgs a) {
   Bwd Q;
   Q.load(a.theta, g, j);
   GradAcc G;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) G.w2[i] = zero4();
-#pragma unroll
-  for (int T = 0; T < 4; ++T) {
-    G.w3t[T] = zero4();
-    G.w1t[T] = zero4();
-    G.b1[T] = 0.f;
-    G.b2[T] = 0.f;
-  }
-  G.b3 = 0.f;
   // A trajectory of the ensemble that failed, or holds more than s_max steps,
-  // has no gradient: its wavefront's partial sum becomes NaN, so the summed
+  // has no gradient: its chunk's partial sum becomes NaN, so the summed
   // shared-weight gradient is NaN rather than silently partial.
   bool failed = false;
-
+  auto fill = [&](float v) {
+    const f4 v4 = {v, v, v, v};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) G.w2[i] = v4;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      G.w3t[T] = v4;
+      G.w1t[T] = v4;
+      G.b1[T] = v;
+      G.b2[T] = v;
+    }
+    G.b3 = v;
+  };
   for (;;) {
-    unsigned long long grp = 0;
-    if (lane == 0) grp = atomicAdd(a.groups, 1ull);
-    grp = __shfl(grp, 0);
-    if (grp >= ngroups) break;
-    const int64_t idx = (int64_t)grp * SLOTS + j;
-    int64_t k = -1;
-    int cnt = 0;
-    bool ok = false;
-    if (idx < a.n) {
-      k = a.perm ? (int64_t)a.perm[idx] : idx;
-      if (k < 0 || k >= a.n) {
-        k = -1;  // an order that is not this record's: nothing is read or written
-      } else {
-        cnt = a.count[k];
-        ok = cnt >= 0 && cnt <= a.s_max && (a.status == nullptr || a.status[k] == TRAJ_OK);
-        if (!ok) cnt = 0;
-        failed = failed || !ok;
+    unsigned long long chunk = 0;
+    if (lane == 0) chunk = atomicAdd(a.groups, 1ull);
+    chunk = __shfl(chunk, 0);
+    if (chunk >= (unsigned long long)a.chunks) break;
+    fill(0.f);
+    failed = false;
+    for (unsigned long long grp = chunk; grp < ngroups; grp += (unsigned long long)a.chunks) {
+      const int64_t idx = (int64_t)grp * SLOTS + j;
+      int64_t k = -1;
+      int cnt = 0;
+      bool ok = false;
+      if (idx < a.n) {
+        k = a.perm ? (int64_t)a.perm[idx] : idx;
+        if (k < 0 || k >= a.n) {
+          k = -1;  // an order that is not this record's: nothing is read or written
+        } else {
+          cnt = a.count[k];
+          ok = cnt >= 0 && cnt <= a.s_max && (a.status == nullptr || a.status[k] == TRAJ_OK);
+          if (!ok) cnt = 0;
+          failed = failed || !ok;
+        }
       }
-    }
-    int mx = cnt;
+      int mx = cnt;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const int o = __shfl_xor(mx, off);
-      mx = (o > mx) ? o : mx;
+      for (int off = 1; off < 16; off <<= 1) {
+        const int o = __shfl_xor(mx, off);
+        mx = (o > mx) ? o : mx;
+      }
+      // A slot that is empty or failed carries a zero state and cotangent, so it
+      // contributes exactly nothing to the shared-weight gradient.
+      float y = 0.f, lam = 0.f;
+      const float* hrow = a.h_rec;
+      if (ok) {
+        y = a.y0[g * a.n + k];
+        lam = a.dLdy1[g * a.n + k];
+        hrow = a.h_rec + k * a.s_cap;
+      }
+      // Forward replay storing y_i (zero-size steps past a slot's count).
+      for (int i = 0; i < mx; ++i) {
+        const float hi = (i < cnt) ? hrow[i] : 0.f;
+        scr[(int64_t)i * WAVE] = y;
+        y = replay(P, w2s, g, j, y, hi);
+      }
+      for (int i = mx - 1; i >= 0; --i) {
+        const float yi = scr[(int64_t)i * WAVE];
+        const float hi = (i < cnt) ? hrow[i] : 0.f;
+        reverse(P, Q, w2s, buf, stage_lds[wv], h2_lds[wv], yi, hi, lam, G, g, j);
+      }
+      if (k >= 0 && a.dLdy0) a.dLdy0[g * a.n + k] = ok ? lam : nanR(0.f);
     }
-    // A slot that is empty or failed carries a zero state and cotangent, so it
-    // contributes exactly nothing to the shared-weight gradient.
-    float y = 0.f, lam = 0.f;
-    const float* hrow = a.h_rec;
-    if (ok) {
-      y = a.y0[g * a.n + k];
-      lam = a.dLdy1[g * a.n + k];
-      hrow = a.h_rec + k * a.s_cap;
-    }
-    // Forward replay storing y_i (zero-size steps past a slot's count).
-    for (int i = 0; i < mx; ++i) {
-      const float hi = (i < cnt) ? hrow[i] : 0.f;
-      scr[(int64_t)i * WAVE] = y;
-      y = replay(P, w2s, g, j, y, hi);
-    }
-    for (int i = mx - 1; i >= 0; --i) {
-      const float yi = scr[(int64_t)i * WAVE];
-      const float hi = (i < cnt) ? hrow[i] : 0.f;
-      reverse(P, Q, w2s, buf, stage_lds[wv], yi, hi, lam, G, g, j);
-    }
-    if (k >= 0 && a.dLdy0) a.dLdy0[g * a.n + k] = ok ? lam : nanR(0.f);
-  }
 
-  // Write this wavefront's partial weight gradient (packed like theta).
-  float* out = a.partial + slot * NP;
-  const bool poison = __ballot(failed) != 0ull;
-  auto pv = [&](float v) { return poison ? nanR(0.f) : v; };
+    // Write this chunk's partial weight gradient (packed like theta).
+    if (__ballot(failed) != 0ull) fill(nanR(0.f));
+    // Stores from one base per block of the row (it moves with the chunk)
+    // and constant offsets.
+    float* out = a.partial + (int64_t)chunk * NP;
+    float* o2 = out + OW2 + 4 * g * NH + j;
 #pragma unroll
-  for (int T2 = 0; T2 < 4; ++T2)
+    for (int T2 = 0; T2 < 4; ++T2)
 #pragma unroll
-    for (int T1 = 0; T1 < 4; ++T1)
+      for (int T1 = 0; T1 < 4; ++T1)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        out[OW2 + (16 * T2 + 4 * g + r) * NH + 16 * T1 + j] = pv(G.w2[T2 * 4 + T1][r]);
+        for (int r = 0; r < 4; ++r) o2[(16 * T2 + r) * NH + 16 * T1] = G.w2[T2 * 4 + T1][r];
+    float* o3 = out + OW3 + j * NH + 4 * g;
+    float* o1 = out + OW1 + 16 * g + j;
+    float* ob = out + OB1 + j;
 #pragma unroll
-  for (int T = 0; T < 4; ++T) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int u = 16 * T + 4 * g + r;
+    for (int T = 0; T < 4; ++T) {
       if (j < 4) {
-        out[OW3 + j * NH + u] = pv(G.w3t[T][r]);
-        out[OW1 + u * 4 + j] = pv(G.w1t[T][r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          o3[16 * T + r] = G.w3t[T][r];
+          o1[(16 * T + r) * 4] = G.w1t[T][r];
+        }
+      }
+      if (g == 0) {
+        ob[16 * T] = G.b1[T];
+        ob[OB2 - OB1 + 16 * T] = G.b2[T];
       }
     }
-    if (g == 0) {
-      out[OB1 + 16 * T + j] = pv(G.b1[T]);
-      out[OB2 + 16 * T + j] = pv(G.b2[T]);
-    }
+    const float s3 = row_sum(G.b3);
+    if (j == 0) out[OB3 + g] = s3;
   }
-  const float s3 = row_sum(G.b3);
-  if (j == 0) out[OB3 + g] = pv(s3);
 }
 
-// dL/dtheta[p] = sum over wavefronts w of partial[w][p], deterministically:
-// pass 1 sums each chunk of REDUCE_CHUNK consecutive rows into the chunk's
-// first row (block (x, c): columns 256x .. 256x + 255 of chunk c, so every
-// row read is coalesced and a column of a chunk belongs to one thread);
-// pass 2 sums those rows in chunk order.
+// dL/dtheta[p] = sum over the chunks' rows w of partial[w][p], in a fixed
+// order: pass 1 sums each run of REDUCE_CHUNK consecutive rows into the run's
+// first row (block (x, c): columns 256x .. 256x + 255 of run c, so every row
+// read is coalesced and a column of a run belongs to one thread); pass 2 sums
+// those rows in order.
 constexpr int REDUCE_CHUNK = 64;
 __global__ void __launch_bounds__(256) reduce_chunks_kernel(float* partial, int64_t nw) {
   const int p = blockIdx.x * blockDim.x + threadIdx.x;

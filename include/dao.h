@@ -194,6 +194,9 @@ size_t dao_grad_workspace_min(dao_system sys, dao_method method, dao_dtype dtype
  *            whose count exceeds s_max, gets NaN in its entries; for the
  *            shared weights of DAO_SYS_MLP one such trajectory makes the
  *            whole summed gradient NaN (a partial sum is never returned).
+ *            The MLP's sum runs in an order fixed by n alone: the same
+ *            inputs give the same bits whatever the workspace size, stream
+ *            or scheduling.
  *   dLdy0    real[d][n]; may be NULL
  * Errors: DAO_EINVAL, DAO_EUNSUPPORTED, DAO_EWORKSPACE, DAO_EDEVICE.
  */
@@ -228,11 +231,11 @@ dao_status dao_grad_ordered(dao_system sys, dao_method method, dao_dtype dtype, 
 /*
  * dao_grad_noalloc -- dao_grad for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
- * forbid hipMalloc): the same gradient, bit for bit for the per-trajectory
- * systems (the neural field's shared-weight sum to binary32 rounding), with
- * its scratch (queue counter, step-count histogram, trajectory order and
- * per-wavefront tiles) in a static device array of the library instead of a
- * workspace argument.  Arguments, results and errors as dao_grad.
+ * forbid hipMalloc): the same gradient, bit for bit, with its scratch (queue
+ * counter, step-count histogram, trajectory order, per-wavefront tiles and
+ * the neural field's partial sums) in a static device array of the library
+ * instead of a workspace argument.  Arguments, results and errors as
+ * dao_grad.
  *   Limit: the array is 64 MiB (67,108,864 bytes) per GPU, held from the
  *   library's first use on that GPU until the process ends.  A call whose
  *   dao_grad_workspace_min(sys, method, dtype, n, s_max) exceeds it returns
