@@ -37,14 +37,14 @@ def _stream(stream=None):
     return _tstream(stream).cuda_stream
 
 
-def _expect(device, *specs):
+def _expect(device, *specs, placed: bool = True):
     """Each (name, tensor, dtype, shape) of specs (None tensors skipped) must
     have that dtype and shape and be a contiguous device tensor on `device`
     (if given).  The kernels take plain pointers and trust the sizes they are
     told, so every array is checked before its pointer is passed: a cotangent
     of the wrong type would be read as the record's type, a short one read
     past its end.  Types and shapes of all arrays are checked first, then
-    where they live."""
+    where they live (skipped with placed=False)."""
     for name, t, dtype, shape in specs:
         if t is None:
             continue
@@ -53,7 +53,7 @@ def _expect(device, *specs):
         if tuple(t.shape) != tuple(shape):
             raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     for name, t, _, _ in specs:
-        if t is None:
+        if t is None or not placed:
             continue
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device (cuda) tensor")
@@ -103,10 +103,32 @@ class Record:
     def s_cap(self):
         return self.h.shape[1]
 
+    def check(self, placed: bool = True):
+        """The record's arrays agree with each other and with its system (the
+        kernels index them by n, s_cap and d alone); placed=False leaves out
+        where they live."""
+        if self.system not in _lib.SYSTEMS or self.method not in _lib.METHODS:
+            raise ValueError(f"unknown system or method: {self.system}, {self.method}")
+        if self.dtype not in _TORCH_DTYPE:
+            raise ValueError(f"unknown dtype {self.dtype}")
+        td = _TORCH_DTYPE[self.dtype]
+        d, p, shared = _lib.dao_system_dims(_lib.SYSTEMS[self.system])
+        if self.count.dim() != 1 or self.h.dim() != 2:
+            raise ValueError("count must be [n] and h [n, s_cap]")
+        n, s_cap = self.count.shape[0], self.h.shape[1]
+        _expect(self.count.device, ("h", self.h, td, (n, s_cap)), ("t", self.t, td, (n, s_cap)),
+                ("count", self.count, torch.int32, (n,)), ("nrej", self.nrej, torch.int32, (n,)),
+                ("status", self.status, torch.int32, (n,)), ("y0", self.y0, td, (d, n)),
+                ("theta", self.theta, td, (p,) if shared else (p, n)),
+                ("y", self.y, td, (n, s_cap, d)), placed=placed)
+
     def stats(self, out=None, stream=None) -> torch.Tensor:
         """Device int64[4] = (max count, total accepted steps, failed
         trajectories, total rejected attempts), written in stream order by
         dao_record_stats; nothing is synchronised."""
+        self.check(placed=False)
+        _expect(self.count.device, ("out", out, torch.int64, (4,)), placed=False)
+        self.check()
         _expect(self.count.device, ("out", out, torch.int64, (4,)))
         o = torch.empty(4, dtype=torch.int64, device=self.count.device) if out is None else out
         _lib.check(_lib.dao_record_stats(self.n, self.c_struct(), _ptr(o), _stream(stream)))
@@ -241,8 +263,10 @@ def sens(rec: Record, theta: torch.Tensor | None = None, with_theta: bool = True
          with_y0: bool = False, s_max: int | None = None, workspace=None, stream=None):
     """Forward sensitivities of y1 through the replay of rec's mesh:
     (S_theta [d][p][n] or None, S_y0 [d][d][n] or None)."""
+    rec.check(placed=False)
     th = rec.theta if theta is None else theta
     _expect(rec.count.device, ("theta", th, rec.y0.dtype, rec.theta.shape))
+    rec.check()
     n = rec.n
     d, p, _ = _lib.dao_system_dims(_lib.SYSTEMS[rec.system])
     s_max = rec.s_cap if s_max is None else min(int(s_max), rec.s_cap)
@@ -258,6 +282,7 @@ def sens(rec: Record, theta: torch.Tensor | None = None, with_theta: bool = True
 
 
 def _grad_setup(rec: Record, s_max, workspace, device, stream):
+    rec.check()
     n = rec.n
     s_max = rec.s_cap if s_max is None else min(int(s_max), rec.s_cap)
     ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
@@ -268,6 +293,7 @@ def _grad_setup(rec: Record, s_max, workspace, device, stream):
 
 def _check_grad_arrays(rec: Record, th, dLdy1, out_theta, out_y0):
     """theta and the outputs like the solve's theta and y0; dLdy1 [d][n]."""
+    rec.check(placed=False)
     td, shape = rec.y0.dtype, tuple(rec.y0.shape)
     _expect(rec.count.device, ("theta", th, td, rec.theta.shape), ("dLdy1", dLdy1, td, shape),
             ("out_theta", out_theta, td, rec.theta.shape), ("out_y0", out_y0, td, shape))
@@ -315,6 +341,7 @@ def states_at(rec: Record, tq: torch.Tensor, theta: torch.Tensor | None = None,
     """States at the requested times tq (device [m], ascending in [t0, t1]) on
     rec's mesh, by a shortened step from the start of the step that holds
     each time: [m][d][n]."""
+    rec.check(placed=False)
     th = rec.theta if theta is None else theta
     n, m = rec.n, int(tq.numel())
     d, _, _ = _lib.dao_system_dims(_lib.SYSTEMS[rec.system])
@@ -326,6 +353,7 @@ def states_at(rec: Record, tq: torch.Tensor, theta: torch.Tensor | None = None,
     _expect(dev, ("theta", th, rec.y0.dtype, rec.theta.shape),
             ("out", out, rec.y0.dtype, (m, d, n)))
     _check_dev(tq)
+    rec.check()
     s_max = rec.s_cap if s_max is None else min(int(s_max), rec.s_cap)
     ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
     dev = rec.count.device
@@ -347,6 +375,7 @@ def grad_at(rec: Record, tq: torch.Tensor, dLdyq: torch.Tensor, dLdy1: torch.Ten
     """dL/dtheta and dL/dy0 for L = sum_q <dLdyq[q], y(tq[q])> + <dLdy1, y(t1)>
     on rec's mesh, the states at tq taken as states_at() takes them.
     tq: device [m], ascending in [t0, t1]; dLdyq: [m][d][n]; dLdy1: [d][n] or None."""
+    rec.check(placed=False)
     th = rec.theta if theta is None else theta
     if tq.dim() != 1:
         raise ValueError("tq must be one-dimensional")
@@ -358,6 +387,7 @@ def grad_at(rec: Record, tq: torch.Tensor, dLdyq: torch.Tensor, dLdy1: torch.Ten
         raise ValueError(f"dLdyq must have shape {(m, d, n)}")
     _check_grad_arrays(rec, th, dLdy1, out_theta, out_y0)
     _check_dev(tq, dLdyq)
+    rec.check()
     s_max = rec.s_cap if s_max is None else min(int(s_max), rec.s_cap)
     ids = _lib.SYSTEMS[rec.system], _lib.METHODS[rec.method], _lib.DTYPES[rec.dtype]
     dev = rec.count.device

@@ -87,3 +87,31 @@ def test_cotangent_target_is_checked():
     y1 = torch.zeros((3, 8), dtype=torch.float64)
     with pytest.raises(ValueError, match="device"):
         dao.cotangent(y1, torch.zeros((3, 8), dtype=torch.float64))
+
+
+def test_an_inconsistent_record_is_refused():
+    # the kernels index a record's arrays by n, s_cap and d alone
+    rec = record()
+    g = torch.zeros((3, 8), dtype=torch.float64)
+    bad = [("count", torch.zeros(7, dtype=torch.int32), ValueError),  # n = 7: h, y0 disagree
+           ("status", torch.zeros(8, dtype=torch.int64), TypeError),
+           ("h", torch.zeros((8, 4), dtype=torch.float32), TypeError),
+           ("t", torch.zeros((8, 5), dtype=torch.float64), ValueError),
+           ("y0", torch.zeros((3, 9), dtype=torch.float64), ValueError),
+           ("y", torch.zeros((8, 4, 2), dtype=torch.float64), ValueError)]
+    for field, value, exc in bad:
+        r = record()
+        setattr(r, field, value)
+        name = "h" if field == "count" else field
+        with pytest.raises(exc, match=name):
+            dao.grad(r, g)
+        with pytest.raises(exc, match=name):
+            dao.states_at(r, torch.zeros(2, dtype=torch.float64))
+    with pytest.raises(ValueError, match="unknown"):
+        r = record()
+        r.method = "rk4"
+        dao.grad(r, g)
+    # consistent, but on the host: refused as such
+    with pytest.raises(ValueError, match="device"):
+        rec.check()
+    rec.check(placed=False)
