@@ -587,7 +587,10 @@ dao_status launch_grad(int mode, int64_t n, const void* theta, const void* y0, c
   const int64_t ngroups = (n + WAVE - 1) / WAVE;
   const int64_t waves_per_block = BLOCK / WAVE;
   int64_t blocks = (ngroups + waves_per_block - 1) / waves_per_block;
-  const int64_t res = resident_blocks(kern, (size_t)BLOCK_WAVES * 16 * WAVE * sizeof(R));
+  // the LDS ring through which the forward pass reads the record's h (and,
+  // for Rodas5P on large systems, the reverse step's stage solutions)
+  const size_t lds = (size_t)BLOCK_WAVES * grad_lds_reals<Sys, M>() * sizeof(R);
+  const int64_t res = resident_blocks(kern, lds);
   if (blocks > res) blocks = res;
   if (blocks > slots / waves_per_block) blocks = slots / waves_per_block;
   if (blocks < 1) return fail(DAO_EWORKSPACE, "dao_grad: workspace too small");
@@ -624,8 +627,6 @@ dao_status launch_grad(int mode, int64_t n, const void* theta, const void* y0, c
     a.t1 = R(at->t1);
     a.y_rec = nullptr;  // the forward replay assigns the times to steps
   }
-  // the LDS ring through which the forward pass reads the record's h
-  const size_t lds = (size_t)BLOCK_WAVES * 16 * WAVE * sizeof(R);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(BLOCK), lds, stream, a);
   return check_hip(hipGetLastError(), "grad kernel launch");
 }

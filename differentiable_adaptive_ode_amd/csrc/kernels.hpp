@@ -590,6 +590,19 @@ struct RowRing {
   }
 };
 
+// The gradient kernel's LDS per wavefront (reals): the forward replay's ring
+// of record h (16 x 64), and, for Rodas5P on systems whose reverse step does
+// not fit the registers, the reverse step's stage solutions (8 x D x 64; the
+// ring is dead by then, so the two share the area).
+template <class Sys, int METHOD>
+constexpr bool rodas_stages_in_lds() {
+  return METHOD == M_RODAS5P && Sys::D >= 8;
+}
+template <class Sys, int METHOD>
+constexpr int grad_lds_reals() {
+  return (rodas_stages_in_lds<Sys, METHOD>() && 8 * Sys::D > 16 ? 8 * Sys::D : 16) * WAVE;
+}
+
 // AT: the loss also holds cotangents of the states at requested times
 // (application paper arXiv 2609.28458 Sec. 2.3 fits residuals at observation
 // times; the states are those of states_kernel).  The forward pass assigns
@@ -752,7 +765,8 @@ grad_kernel(GradArgs<R> a) {
       if (rows8) {
         HIP_DYNAMIC_SHARED(unsigned char, gr_lds)
         RowRing<R> rr;
-        rr.init((R(*)[WAVE])((R*)gr_lds + (threadIdx.x / WAVE) * (16 * WAVE)), hrow, mx, lane);
+        rr.init((R(*)[WAVE])((R*)gr_lds + (threadIdx.x / WAVE) * grad_lds_reals<Sys, METHOD>()),
+                hrow, mx, lane);
         for (int i = 0; i < mx; ++i) fwd(i, rr.at(i));
       } else {
         for (int i = 0; i < mx; ++i) {
@@ -851,7 +865,14 @@ grad_kernel(GradArgs<R> a) {
         } else if constexpr (METHOD == M_RODAS5P) {
           rodas5p::Stages<R, D> S;
           rodas5p::stages<R, Sys>(sys, yj, hj, S);
-          rodas5p::sweep<R, Sys>(sys, S, hj, lam, pb);
+          if constexpr (rodas_stages_in_lds<Sys, METHOD>()) {
+            HIP_DYNAMIC_SHARED(unsigned char, rs_lds)
+            R* const us = (R*)rs_lds + (threadIdx.x / WAVE) * grad_lds_reals<Sys, METHOD>() + lane;
+            rodas5p::put_stages(S, us);
+            rodas5p::sweep_lds<R, Sys>(sys, S.w, yj, hj, us, lam, pb);
+          } else {
+            rodas5p::sweep<R, Sys>(sys, S, hj, lam, pb);
+          }
         } else {
           ros23::Stages<R, D> S;
           ros23::stages<R, Sys>(sys, yj, hj, S);

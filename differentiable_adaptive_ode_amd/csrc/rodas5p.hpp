@@ -221,5 +221,126 @@ __device__ __forceinline__ void sweep(const Sys& sys, const Stages<R, Sys::D>& S
   for (int j = 0; j < P; ++j) pb[j] += zero ? R(0) : pt[j];
 }
 
+// The same reverse step with the stage solutions in LDS, for systems whose
+// step does not fit the registers (d = 8: the factors, the stage solutions,
+// the stage states and the stage cotangents together are ~400 doubles).  us
+// points at this lane's element of the wavefront's area [8][D][64]: u_i,c at
+// us[(i D + c) 64].  The stage states are recomputed from y and the u_j with
+// the operations run() used, so every value is run()'s own.  Each stage's
+// loads are tied to that stage's incoming cotangent through an empty asm
+// statement: without it the compiler issues every stage's loads and
+// recomputed states at the top of the step and holds them all in registers.
+// Its transposed solves run their row exchanges as selects (SKIP = false):
+// the compiler barrier on the skip branches pins the loads around it, and
+// the reverse step then spilled 630 registers and ran 3.8x slower.  The Jacobian cotangent
+// rb u_i^T is pulled back stage by stage (the pull-back is linear), so only
+// the entries the pull-back reads are ever formed.
+template <class R, int D>
+__device__ __forceinline__ void put_stages(const Stages<R, D>& S, R* us) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int c = 0; c < D; ++c) us[(i * D + c) * WAVE] = S.u[i][c];
+}
+
+template <class R, class Sys>
+__device__ __forceinline__ void sweep_lds(const Sys& sys, const ros23::LU<R, Sys::D>& w,
+                                          const R (&y)[Sys::D], R h, const R* us_,
+                                          R (&lam)[Sys::D], R (&pb)[Sys::P]) {
+  constexpr int D = Sys::D, P = Sys::P;
+  const R* us = us_;
+  int dep = 0;  // always 0; the asm below makes it depend on the cotangent
+  auto u = [&](int i, int c) -> R { return us[(i * D + c) * WAVE + dep]; };
+  const bool zero = (h == R(0));
+  const R hinv = recipR(zero ? R(1) : h);
+  // stage state Y_i as run() forms it (Y_6 = Y_5 + u_5, Y_7 = Y_6 + u_6)
+  auto stage_y = [&](int i, R (&Yi)[D]) {
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      const int i5 = i < 5 ? i : 5;
+      R v = y[c];
+      if (i5 > 0) {
+        R acc = R(A[i5][0]) * u(0, c);
+#pragma unroll
+        for (int j = 1; j < 5; ++j)
+          if (j < i5) acc = fmaR(R(A[i5][j]), u(j, c), acc);
+        v = acc + y[c];
+      }
+      if (i >= 6) v = v + u(5, c);
+      if (i >= 7) v = v + u(6, c);
+      Yi[c] = v;
+    }
+  };
+  R ub[8][D], yb[D], Yb[D], pt[P];
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    ub[7][c] = lam[c];
+    Yb[c] = lam[c];
+    yb[c] = R(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 7; ++i)
+#pragma unroll
+    for (int c = 0; c < D; ++c) ub[i][c] = R(0);
+#pragma unroll
+  for (int j = 0; j < P; ++j) pt[j] = R(0);
+#pragma unroll
+  for (int i = 7; i >= 0; --i) {
+    // stage i's loads and recomputed state wait for ub_i to be complete
+    asm volatile("" : "+v"(dep) : "v"(ub[i][0]));
+    R Yi[D], rb[D], tmp[D];
+    stage_y(i, Yi);
+    ros23::solve_t<R, D, false>(w, ub[i], rb);
+    {
+      // W's cotangent -rb u_i^T is +rb u_i^T on J(y, theta), pulled back at
+      // once (the pull-back is linear; only the entries it reads are formed)
+      R ui[D], Jo[D][D];
+#pragma unroll
+      for (int b = 0; b < D; ++b) ui[b] = u(i, b);
+#pragma unroll
+      for (int a = 0; a < D; ++a)
+#pragma unroll
+        for (int b = 0; b < D; ++b) Jo[a][b] = rb[a] * ui[b];
+      sys.jac_vjp(y, Jo, yb, pt);
+    }
+    sys.vjp(Yi, rb, tmp, pt);
+    if (i == 0) {
+#pragma unroll
+      for (int c = 0; c < D; ++c) yb[c] += tmp[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < D; ++c) Yb[c] += tmp[c];
+#pragma unroll
+      for (int j = 0; j < 7; ++j) {
+        if (j < i) {
+          const R ch = R(C[i][j]) * hinv;
+#pragma unroll
+          for (int c = 0; c < D; ++c) ub[j][c] = fmaR(ch, rb[c], ub[j][c]);
+        }
+      }
+      if (i >= 6) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) ub[i - 1][c] += Yb[c];
+      } else {
+#pragma unroll
+        for (int c = 0; c < D; ++c) yb[c] += Yb[c];
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+          if (j < i) {
+#pragma unroll
+            for (int c = 0; c < D; ++c) ub[j][c] = fmaR(R(A[i][j]), Yb[c], ub[j][c]);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < D; ++c) Yb[c] = R(0);
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < D; ++c) lam[c] = zero ? lam[c] : yb[c];
+#pragma unroll
+  for (int j = 0; j < P; ++j) pb[j] += zero ? R(0) : pt[j];
+}
+
 }  // namespace rodas5p
 }  // namespace dao
