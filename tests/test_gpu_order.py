@@ -25,7 +25,10 @@ def expected(count, s_max):
 
 @pytest.mark.parametrize("n,s_max,hi", [(1, 8, 8), (1000, 70, 70), (1025, 6, 9),
                                         (64 * 1024 + 37, 1000, 1000),
-                                        (300_000, 20_000, 20_000), (200_000, 8191, 300)])
+                                        (300_000, 20_000, 20_000), (200_000, 8191, 300),
+                                        # one bin of real counts; exactly 4096 bins (12 bits);
+                                        # the first s_max that needs a shift
+                                        (5000, 0, 0), (70_000, 4094, 4094), (70_000, 4095, 4095)])
 def test_order_is_a_stable_sort_by_bin(n, s_max, hi):
     from differentiable_adaptive_ode_amd import _lib
 
