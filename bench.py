@@ -247,7 +247,7 @@ CPU_SAMPLES = {"lotka_volterra": (256, 256, 256), "lorenz63": (65536, 32768, 102
 
 def cpu_threads():
     """Host threads the oracle baseline runs on: the threads this process may
-    use, at most 16 (a one-GPU machine's CPU share)."""
+    use, at most 16 (the host CPU share of one GPU on an 8-GPU node)."""
     try:
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -540,7 +540,7 @@ def roofline_of(m):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; the ensemble would shard by "
+        print("bench.py: the benchmark runs on exactly one GPU; the ensemble would shard by "
               "trajectory index across GPUs, with no exchange for per-trajectory parameters "
               "and one all-reduce of the shared weights otherwise. Use --gpus 1.",
               file=sys.stderr)
