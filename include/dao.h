@@ -208,8 +208,9 @@ dao_status dao_grad(dao_system sys, dao_method method, dao_dtype dtype, int64_t 
 /*
  * dao_grad in two parts.  The gradient runs trajectories in groups of similar
  * step count; dao_grad_order sorts the record's trajectories by count[k] into
- * the workspace, and dao_grad_ordered runs the gradient with the order the
- * workspace holds.  dao_grad does both.  One order serves any number of
+ * the workspace (a stable sort: equal counts keep index order, so the order
+ * depends on the counts alone), and dao_grad_ordered runs the gradient with
+ * the order the workspace holds.  dao_grad does both.  One order serves any number of
  * dao_grad_ordered calls on the same record counts, n and s_max (Sec. 3.1
  * and 4.8 reuse one record while theta moves: theta, y0 and dLdy1 may change
  * between them), provided nothing else writes the workspace in between (a
