@@ -227,3 +227,30 @@ def test_grad_noalloc_rejects_before_touching_the_device(L):
     assert L.dao_grad_noalloc(*ids, 64, 1, 1, rec, -1, 1, None, None, None) == L.DAO_EINVAL
     assert L.dao_grad_noalloc(*ids, 64, None, 1, rec, 8, 1, None, None, None) == L.DAO_EINVAL
     assert L.dao_grad_noalloc(9, 0, 0, 64, 1, 1, rec, 8, 1, None, None, None) == L.DAO_EINVAL
+
+
+def test_gradient_workspace_sizes_are_consistent(L):
+    # For every supported (system, method, dtype): the minimum workspace fits
+    # in the recommended one, both grow with n and s_max, and the neural
+    # field's holds one row of 4,740 partial sums per chunk of 16-trajectory
+    # groups (a chunk per group up to 2,048 groups, then 2,048 chunks).
+    sizes = (0, 1, 65, 1000, 40_000, 1 << 20)
+    for sysname, sid in L.SYSTEMS.items():
+        for mname, mid in L.METHODS.items():
+            for did in L.DTYPES.values():
+                prev_min = prev_size = 0
+                for n in sizes:
+                    size = L.dao_grad_workspace_size(sid, mid, did, n, 64)
+                    if size == 0:
+                        break  # combination not provided
+                    smin = L.dao_grad_workspace_min(sid, mid, did, n, 64)
+                    assert 0 < smin <= size, (sysname, mname, did, n)
+                    assert smin >= prev_min and size >= prev_size, (sysname, mname, did, n)
+                    assert L.dao_grad_workspace_min(sid, mid, did, n, 256) >= smin
+                    prev_min, prev_size = smin, size
+    mlp = L.SYSTEMS["mlp"]
+    for n in (1, 16 * 2048, 16 * 2048 + 1, 1 << 20):
+        groups = (n + 15) // 16
+        chunks = min(groups, 2048)
+        rows = L.dao_grad_workspace_min(mlp, 0, 1, n, 64) - L.dao_grad_workspace_min(mlp, 0, 1, 0, 64)
+        assert rows >= (chunks - 1) * 4740 * 4, n
