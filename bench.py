@@ -318,19 +318,20 @@ def solve_bytes(w, steps_total, with_t):
     return th + w.n * (2 * w.d * r + 12) + steps_total * r * (2 if with_t else 1)
 
 
-def grad_bytes(w, steps_total, waves):
+def grad_bytes(w, steps_total, rows):
     """Algorithmic HBM bytes of one ordered gradient call: per trajectory the
     parameters, initial state, cotangent, count, status and order read and the
     two gradients written; per accepted step h read once and the stored state
     written and read back (with the step's h: d + 1 values each way); the
-    neural field keeps d values per step and adds each wavefront's partial
-    weight gradient, written and read by the reduction."""
+    neural field keeps d values per step and adds the rows of partial weight
+    gradients (one per chunk of 16-trajectory groups), written and read by the
+    reduction."""
     r = 8 if w.dtype == "f64" else 4
     p = w.theta.shape[0]
     if w.system == "mlp":
         per_traj = 3 * w.d * r + 12
         return (p * r + w.n * per_traj + steps_total * (r + 2 * w.d * r)
-                + waves * p * r * 2 + p * r)
+                + rows * p * r * 2 + p * r)
     per_traj = (2 * p + 3 * w.d) * r + 12
     return w.n * per_traj + steps_total * (r + 2 * (w.d + 1) * r)
 
@@ -465,9 +466,9 @@ def measure_gradient(w, args, steps, warmup, graph):
     # with recorded states the gradient does no forward replay
     fl_grad = steps_total * (cfg["grad"] - (cfg["replay"] if states else 0))
     peak = cfg["peak"]
-    waves = min(-(-w.n // 16), 1024)  # the neural gradient's wavefronts (one per SIMD)
+    rows = min(-(-w.n // 16), 2048)  # the neural gradient's partial-sum rows (chunks)
     by_solve = solve_bytes(w, steps_total, with_t)
-    by_grad = grad_bytes(w, steps_total, waves)
+    by_grad = grad_bytes(w, steps_total, rows)
 
     def part(fl, by, t):
         # graded against the attainable rate min(peak, AI x HBM bandwidth)
