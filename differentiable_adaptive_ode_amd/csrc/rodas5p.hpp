@@ -66,7 +66,7 @@ __device__ __forceinline__ void run(const Sys& sys, const R (&y)[Sys::D], R h,
   for (int i = 0; i < D; ++i)
 #pragma unroll
     for (int j = 0; j < D; ++j) S.w.m[i][j] = (i == j) ? ginv - J[i][j] : -J[i][j];
-  ros23::factor<R, D, SKIP>(S.w);
+  ros23::factor<R, D, SKIP, Sys>(S.w);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     R r[D];
@@ -100,7 +100,7 @@ __device__ __forceinline__ void run(const Sys& sys, const R (&y)[Sys::D], R h,
         r[c] = fmaR(acc, hinv, F[c]);
       }
     }
-    ros23::solve<R, D, SKIP>(S.w, r, S.u[i]);
+    ros23::solve<R, D, SKIP, Sys>(S.w, r, S.u[i]);
   }
 }
 
@@ -173,7 +173,7 @@ __device__ __forceinline__ void sweep(const Sys& sys, const Stages<R, Sys::D>& S
 #pragma unroll
   for (int i = 7; i >= 0; --i) {
     R rb[D], tmp[D];
-    ros23::solve_t<R, D>(S.w, ub[i], rb);
+    ros23::solve_t<R, D, true, Sys>(S.w, ub[i], rb);
 #pragma unroll
     for (int a = 0; a < D; ++a)
 #pragma unroll

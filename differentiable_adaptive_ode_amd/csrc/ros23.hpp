@@ -24,6 +24,8 @@
 // wavefront-uniform branch; they would leave every value as it is.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace dao {
@@ -44,54 +46,164 @@ struct LU {
   bool swaps;  // some lane of the wavefront exchanges rows (wavefront-uniform)
 };
 
+// Sparse systems.  A system may declare which entries of its Jacobian can be
+// nonzero (static constexpr bool jac_nz(i, j)).  W then has that pattern plus
+// the diagonal, and eliminating without row exchanges fills in only where
+// lu_nz says (computed at compile time).  While no lane of the wavefront has
+// exchanged rows, factor, solve and solve_t skip the entries outside it: the
+// dense code would only add exact zeros there (a structurally zero multiplier
+// or row entry), so every nonzero value is the dense code's own.  From the
+// first step at which some lane exchanges rows, the dense code runs.
+template <class Sys, class = void>
+struct HasJacPattern : std::false_type {};
+template <class Sys>
+struct HasJacPattern<Sys, std::void_t<decltype(Sys::jac_nz(0, 0))>> : std::true_type {};
+
+template <int D>
+struct Pattern {
+  bool nz[D][D];
+};
+template <class Sys>
+constexpr Pattern<Sys::D> fill_pattern() {
+  constexpr int D = Sys::D;
+  Pattern<D> p{};
+  for (int i = 0; i < D; ++i)
+    for (int j = 0; j < D; ++j) p.nz[i][j] = (i == j) || Sys::jac_nz(i, j);
+  for (int k = 0; k < D; ++k)
+    for (int i = k + 1; i < D; ++i)
+      if (p.nz[i][k])
+        for (int j = k + 1; j < D; ++j)
+          if (p.nz[k][j]) p.nz[i][j] = true;
+  return p;
+}
+template <class Sys>
+__device__ constexpr Pattern<Sys::D> lu_nz = fill_pattern<Sys>();
+
+// Whether factor/solve/solve_t take the sparse path for Sys (void: dense).
+template <class Sys, bool SKIP>
+constexpr bool sparse_lu() {
+  if constexpr (std::is_void<Sys>::value) {
+    return false;
+  } else {
+    return SKIP && HasJacPattern<Sys>::value;
+  }
+}
+
 // SKIP (here and below): test, once per elimination step and per solve,
 // whether any lane of the wavefront exchanges rows, and skip the exchange on
 // a real branch when none does.  Without it the exchanges are selects in
 // straight-line code, which suits kernels that run many independent solves
 // per step (the sensitivity tangents), where branches would keep the
 // compiler from interleaving them.
-template <class R, int D, bool SKIP = true>
-__device__ __forceinline__ void factor(LU<R, D>& f) {
+// One elimination step k of factor (a template parameter: the sparse and the
+// dense step together are too large for the compiler to unroll a loop over k,
+// and a loop left rolled would index the factors at run time, through
+// scratch memory).
+template <int K, class R, int D, bool SKIP, class Sys>
+__device__ __forceinline__ void factor_step(LU<R, D>& f, bool& dense) {
+  if constexpr (K < D) {
+    constexpr int k = K;
+    bool done = false;  // step k taken by the sparse code
+    if constexpr (sparse_lu<Sys, SKIP>()) {
+      if (!dense) {
+        // pivot among the rows that can be nonzero in column k (a structural
+        // zero never wins: 0 > best is false)
+        int p = k;
+        R best = absR(f.m[k][k]);
 #pragma unroll
-  for (int k = 0; k < D; ++k) {
-    int p = k;
-    R best = absR(f.m[k][k]);
+        for (int i = k + 1; i < D; ++i) {
+          if (lu_nz<Sys>.nz[i][k]) {
+            R v = absR(f.m[i][k]);
+            if (v > best) { best = v; p = i; }
+          }
+        }
+        if ((k + 1 < D) && __ballot(p != k) != 0ull) {
+          dense = true;  // some lane exchanges rows at step k: the dense code from here on
+        } else {
+          f.piv[k] = k;
+          f.rp[k] = recipR(f.m[k][k]);
 #pragma unroll
-    for (int i = k + 1; i < D; ++i) {
-      R v = absR(f.m[i][k]);
-      if (v > best) { best = v; p = i; }
-    }
-    f.piv[k] = p;
-    const bool any = !SKIP || ((k + 1 < D) && __ballot(p != k) != 0ull);
-    if (k == 0) f.swaps = any;
-    else f.swaps = f.swaps || any;
-    if (any) {
-      if (SKIP) skip_point();
+          for (int i = k + 1; i < D; ++i) {
+            if (lu_nz<Sys>.nz[i][k]) {
+              R l = f.m[i][k] * f.rp[k];
+              f.m[i][k] = l;
 #pragma unroll
-      for (int i = k + 1; i < D; ++i) {
-        const bool sw = (p == i);
-#pragma unroll
-        for (int j = 0; j < D; ++j) {
-          R rk = f.m[k][j], ri = f.m[i][j];
-          f.m[k][j] = sw ? ri : rk;
-          f.m[i][j] = sw ? rk : ri;
+              for (int j = k + 1; j < D; ++j)
+                if (lu_nz<Sys>.nz[k][j]) f.m[i][j] = fmaR(-l, f.m[k][j], f.m[i][j]);
+            }
+          }
+          done = true;
         }
       }
     }
-    f.rp[k] = recipR(f.m[k][k]);
+    if (!done) {
+      int p = k;
+      R best = absR(f.m[k][k]);
 #pragma unroll
-    for (int i = k + 1; i < D; ++i) {
-      R l = f.m[i][k] * f.rp[k];
-      f.m[i][k] = l;
+      for (int i = k + 1; i < D; ++i) {
+        R v = absR(f.m[i][k]);
+        if (v > best) { best = v; p = i; }
+      }
+      f.piv[k] = p;
+      const bool any = !SKIP || ((k + 1 < D) && __ballot(p != k) != 0ull);
+      f.swaps = f.swaps || any;
+      if (any) {
+        if (SKIP) skip_point();
 #pragma unroll
-      for (int j = k + 1; j < D; ++j) f.m[i][j] = fmaR(-l, f.m[k][j], f.m[i][j]);
+        for (int i = k + 1; i < D; ++i) {
+          const bool sw = (p == i);
+#pragma unroll
+          for (int j = 0; j < D; ++j) {
+            R rk = f.m[k][j], ri = f.m[i][j];
+            f.m[k][j] = sw ? ri : rk;
+            f.m[i][j] = sw ? rk : ri;
+          }
+        }
+      }
+      f.rp[k] = recipR(f.m[k][k]);
+#pragma unroll
+      for (int i = k + 1; i < D; ++i) {
+        R l = f.m[i][k] * f.rp[k];
+        f.m[i][k] = l;
+#pragma unroll
+        for (int j = k + 1; j < D; ++j) f.m[i][j] = fmaR(-l, f.m[k][j], f.m[i][j]);
+      }
     }
+    factor_step<K + 1, R, D, SKIP, Sys>(f, dense);
   }
 }
 
+template <class R, int D, bool SKIP = true, class Sys = void>
+__device__ __forceinline__ void factor(LU<R, D>& f) {
+  bool dense = !sparse_lu<Sys, SKIP>();  // (wavefront-uniform) the dense code runs
+  f.swaps = false;
+  factor_step<0, R, D, SKIP, Sys>(f, dense);
+}
+
 // x = W^-1 b
-template <class R, int D, bool SKIP = true>
+template <class R, int D, bool SKIP = true, class Sys = void>
 __device__ __forceinline__ void solve(const LU<R, D>& f, const R (&b)[D], R (&x)[D]) {
+  if constexpr (sparse_lu<Sys, SKIP>()) {
+    if (!f.swaps) {
+      R z[D];
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        z[i] = b[i];
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+          if (j < i && lu_nz<Sys>.nz[i][j]) z[i] = fmaR(-f.m[i][j], z[j], z[i]);
+      }
+#pragma unroll
+      for (int i = D - 1; i >= 0; --i) {
+        R acc = z[i];
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+          if (j > i && lu_nz<Sys>.nz[i][j]) acc = fmaR(-f.m[i][j], x[j], acc);
+        x[i] = acc * f.rp[i];
+      }
+      return;
+    }
+  }
   R z[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) z[i] = b[i];
@@ -124,8 +236,30 @@ __device__ __forceinline__ void solve(const LU<R, D>& f, const R (&b)[D], R (&x)
 }
 
 // x = W^-T b, with W = P^T L U:  U^T z = b,  L^T w = z,  x = P^T w.
-template <class R, int D, bool SKIP = true>
+template <class R, int D, bool SKIP = true, class Sys = void>
 __device__ __forceinline__ void solve_t(const LU<R, D>& f, const R (&b)[D], R (&x)[D]) {
+  if constexpr (sparse_lu<Sys, SKIP>()) {
+    if (!f.swaps) {
+      R z[D];
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        R acc = b[i];
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+          if (j < i && lu_nz<Sys>.nz[j][i]) acc = fmaR(-f.m[j][i], z[j], acc);
+        z[i] = acc * f.rp[i];
+      }
+#pragma unroll
+      for (int i = D - 1; i >= 0; --i) {
+        R acc = z[i];
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+          if (j > i && lu_nz<Sys>.nz[j][i]) acc = fmaR(-f.m[j][i], x[j], acc);
+        x[i] = acc;
+      }
+      return;
+    }
+  }
   R z[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
@@ -169,7 +303,7 @@ __device__ __forceinline__ void build_w(const Sys& sys, const R (&y)[Sys::D], R 
   for (int i = 0; i < D; ++i)
 #pragma unroll
     for (int j = 0; j < D; ++j) w.m[i][j] = fmaR(-hd, J[i][j], R(i == j ? 1 : 0));
-  factor<R, D, SKIP>(w);
+  factor<R, D, SKIP, Sys>(w);
 }
 
 // Trial step: F0 = f(y) on entry; returns ynew, F2 = f(ynew) and err.
@@ -181,14 +315,14 @@ __device__ __forceinline__ void trial(const Sys& sys, const R (&y)[Sys::D], R h,
   LU<R, D> w;
   build_w<R, Sys, SKIP>(sys, y, h, w);
   R k1[D], k2[D], Y1[D], F1[D], r[D], u[D], k3[D];
-  solve<R, D, SKIP>(w, F0, k1);
+  solve<R, D, SKIP, Sys>(w, F0, k1);
   R hh = R(0.5) * h;
 #pragma unroll
   for (int c = 0; c < D; ++c) Y1[c] = fmaR(hh, k1[c], y[c]);
   sys.f(Y1, F1);
 #pragma unroll
   for (int c = 0; c < D; ++c) r[c] = F1[c] - k1[c];
-  solve<R, D, SKIP>(w, r, u);
+  solve<R, D, SKIP, Sys>(w, r, u);
 #pragma unroll
   for (int c = 0; c < D; ++c) k2[c] = u[c] + k1[c];
 #pragma unroll
@@ -199,7 +333,7 @@ __device__ __forceinline__ void trial(const Sys& sys, const R (&y)[Sys::D], R h,
     R t2 = fmaR(R(-E32), k2[c] - F1[c], F2[c]);
     r[c] = fmaR(R(-2), k1[c] - F0[c], t2);
   }
-  solve<R, D, SKIP>(w, r, k3);
+  solve<R, D, SKIP, Sys>(w, r, k3);
   // the embedded error without its factor h/6 (in the error weights)
 #pragma unroll
   for (int c = 0; c < D; ++c) err[c] = fmaR(R(-2), k2[c], k1[c]) + k3[c];
@@ -213,14 +347,14 @@ __device__ __forceinline__ void replay(const Sys& sys, R (&y)[Sys::D], R h) {
   build_w(sys, y, h, w);
   R F0[D], k1[D], Y1[D], F1[D], r[D], u[D];
   sys.f(y, F0);
-  solve<R, D>(w, F0, k1);
+  solve<R, D, true, Sys>(w, F0, k1);
   R hh = R(0.5) * h;
 #pragma unroll
   for (int c = 0; c < D; ++c) Y1[c] = fmaR(hh, k1[c], y[c]);
   sys.f(Y1, F1);
 #pragma unroll
   for (int c = 0; c < D; ++c) r[c] = F1[c] - k1[c];
-  solve<R, D>(w, r, u);
+  solve<R, D, true, Sys>(w, r, u);
 #pragma unroll
   for (int c = 0; c < D; ++c) y[c] = fmaR(h, u[c] + k1[c], y[c]);
 }
@@ -246,14 +380,14 @@ __device__ __forceinline__ void stages(const Sys& sys, const R (&y)[Sys::D], R h
 #pragma unroll
   for (int c = 0; c < D; ++c) S.y[c] = y[c];
   sys.f(y, F0);
-  solve<R, D, SKIP>(S.w, F0, S.k1);
+  solve<R, D, SKIP, Sys>(S.w, F0, S.k1);
   R hh = R(0.5) * h;
 #pragma unroll
   for (int c = 0; c < D; ++c) S.Y1[c] = fmaR(hh, S.k1[c], y[c]);
   sys.f(S.Y1, F1);
 #pragma unroll
   for (int c = 0; c < D; ++c) r[c] = F1[c] - S.k1[c];
-  solve<R, D, SKIP>(S.w, r, S.u);
+  solve<R, D, SKIP, Sys>(S.w, r, S.u);
 }
 
 template <class R, class Sys>
@@ -269,7 +403,7 @@ __device__ __forceinline__ void sweep(const Sys& sys, const Stages<R, Sys::D>& S
     k1b[c] = ub[c];
   }
   // u = W^-1 r:  rb = W^-T ub,  Wb = -rb u^T
-  solve_t<R, D>(S.w, ub, rb);
+  solve_t<R, D, true, Sys>(S.w, ub, rb);
   // r = F1 - k1
 #pragma unroll
   for (int c = 0; c < D; ++c) k1b[c] -= rb[c];
@@ -281,7 +415,7 @@ __device__ __forceinline__ void sweep(const Sys& sys, const Stages<R, Sys::D>& S
     k1b[c] = fmaR(hh, tmp[c], k1b[c]);
   }
   // k1 = W^-1 F0:  F0b = W^-T k1b,  Wb -= F0b k1^T
-  solve_t<R, D>(S.w, k1b, F0b);
+  solve_t<R, D, true, Sys>(S.w, k1b, F0b);
   // F0 = f(y)
   sys.vjp(S.y, F0b, tmp, pb);
 #pragma unroll

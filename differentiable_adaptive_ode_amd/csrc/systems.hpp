@@ -234,6 +234,12 @@ struct Robertson {
 template <class R>
 struct Hires {
   static constexpr int D = 8, P = 12;
+  // entries of the Jacobian that can be nonzero (those jac() sets), row by
+  // row as bit masks over the columns: the linear solves skip the others
+  static constexpr bool jac_nz(int i, int j) {
+    constexpr unsigned rows[D] = {0x07, 0x03, 0x1C, 0x0E, 0x70, 0xF8, 0xE0, 0xE0};
+    return (rows[i] >> j) & 1u;
+  }
   R k[P];
   __device__ void load(const R* theta, int64_t n, int64_t kk) {
 #pragma unroll
