@@ -95,6 +95,7 @@ constexpr bool sparse_lu() {
 // straight-line code, which suits kernels that run many independent solves
 // per step (the sensitivity tangents), where branches would keep the
 // compiler from interleaving them.
+//
 // One elimination step k of factor (a template parameter: the sparse and the
 // dense step together are too large for the compiler to unroll a loop over k,
 // and a loop left rolled would index the factors at run time, through
