@@ -79,6 +79,17 @@ constexpr Pattern<Sys::D> fill_pattern() {
 template <class Sys>
 __device__ constexpr Pattern<Sys::D> lu_nz = fill_pattern<Sys>();
 
+// Whether J's entry (i, j) can be nonzero (every entry, for a system that
+// declares no pattern).
+template <class Sys>
+__device__ constexpr bool jac_entry(int i, int j) {
+  if constexpr (HasJacPattern<Sys>::value) {
+    return Sys::jac_nz(i, j);
+  } else {
+    return true;
+  }
+}
+
 // Whether factor/solve/solve_t take the sparse path for Sys (void: dense).
 template <class Sys, bool SKIP>
 constexpr bool sparse_lu() {
@@ -452,12 +463,14 @@ __device__ __forceinline__ void tangent(const Sys& sys, const Stages<R, Sys::D>&
     for (int c = 0; c < D; ++c) yd[c] = S[c][t];
     sys.jvp(St.y, yd, dir[t], F0d);
     sys.jac_jvp(St.y, yd, dir[t], Jd);
-    // F0d - Wd k1 = F0d + h d Jd k1
+    // F0d - Wd k1 = F0d + h d Jd k1 (Jd has J's pattern: the structural
+    // zeros would add exact zeros)
 #pragma unroll
     for (int i = 0; i < D; ++i) {
       R acc = R(0);
 #pragma unroll
-      for (int j = 0; j < D; ++j) acc = fmaR(Jd[i][j], St.k1[j], acc);
+      for (int j = 0; j < D; ++j)
+        if (jac_entry<Sys>(i, j)) acc = fmaR(Jd[i][j], St.k1[j], acc);
       r[i] = fmaR(hd, acc, F0d[i]);
     }
     solve<R, D, SKIP>(St.w, r, k1d);
@@ -469,7 +482,8 @@ __device__ __forceinline__ void tangent(const Sys& sys, const Stages<R, Sys::D>&
     for (int i = 0; i < D; ++i) {
       R acc = R(0);
 #pragma unroll
-      for (int j = 0; j < D; ++j) acc = fmaR(Jd[i][j], St.u[j], acc);
+      for (int j = 0; j < D; ++j)
+        if (jac_entry<Sys>(i, j)) acc = fmaR(Jd[i][j], St.u[j], acc);
       r[i] = fmaR(hd, acc, F1d[i] - k1d[i]);
     }
     solve<R, D, SKIP>(St.w, r, ud);
