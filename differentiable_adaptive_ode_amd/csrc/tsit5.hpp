@@ -205,30 +205,38 @@ template <class R, class Sys>
 __device__ __forceinline__ void stages(const Coef<R>& C, const Sys& sys, const R (&y)[Sys::D], R h,
                                        Stages<R, Sys::D>& S) {
   constexpr int D = Sys::D;
-  // Each stage's sum a_i0 k_0 + a_i1 k_1 + ... is built as the k_j appear, j
-  // ascending (the order stage_state uses, so the same bits), and each k_j
+  // Each stage's sum is built as the k_j appear, j ascending, and each k_j
   // dies as soon as it is added: the live set is the sums still open plus
-  // the stage states kept, not every k_j beside every stage state.
+  // the stage states kept, not every k_j beside every stage state.  From
+  // d = 3 on the sums are y + sum_j (h a_ij) k_j: one product h a_ij per
+  // coupling instead of a product per component, and Y_i is the sum itself,
+  // one multiply-add earlier.  The stage states then round differently from
+  // the solve's (y + h sum_j a_ij k_j); they only feed the stage VJPs, and the
+  // step's y_j and y_{j+1} stay the replay's.
+  constexpr bool HA = D >= 3;
   R acc[6][D];
   R k[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) S.Y[0][c] = y[c];
   sys.f(S.Y[0], k);
 #pragma unroll
-  for (int i = 1; i < 6; ++i)
+  for (int i = 1; i < 6; ++i) {
+    const R ha = h * C.a[i][0];
 #pragma unroll
-    for (int c = 0; c < D; ++c) acc[i][c] = C.a[i][0] * k[c];
+    for (int c = 0; c < D; ++c) acc[i][c] = HA ? fmaR(ha, k[c], y[c]) : C.a[i][0] * k[c];
+  }
 #pragma unroll
   for (int j = 1; j < 6; ++j) {
 #pragma unroll
-    for (int c = 0; c < D; ++c) S.Y[j][c] = fmaR(h, acc[j][c], y[c]);
+    for (int c = 0; c < D; ++c) S.Y[j][c] = HA ? acc[j][c] : fmaR(h, acc[j][c], y[c]);
     if (j < 5) {
       sys.f(S.Y[j], k);
 #pragma unroll
       for (int i = 2; i < 6; ++i)
         if (i > j) {
+          const R a = HA ? h * C.a[i][j] : C.a[i][j];
 #pragma unroll
-          for (int c = 0; c < D; ++c) acc[i][c] = fmaR(C.a[i][j], k[c], acc[i][c]);
+          for (int c = 0; c < D; ++c) acc[i][c] = fmaR(a, k[c], acc[i][c]);
         }
     }
   }
