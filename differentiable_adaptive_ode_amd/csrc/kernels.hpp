@@ -617,10 +617,14 @@ constexpr int grad_lds_reals() {
 // 128 registers, four wavefronts per SIMD; Verner 7 without requested times
 // to 256, two wavefronts per SIMD (one wavefront with its overflow in
 // accumulation registers was slower); with requested times the spills would
-// be many and one wavefront is faster.
+// be many and one wavefront is faster.  Tsit5 with requested times and
+// d <= 6 is held to 256 as well: the orbit's kernel needs two registers more
+// (two spilled; without the cap it ran one wavefront per SIMD, ~10 % slower).
 template <class R, class Sys, int METHOD, bool AT = false>
 __global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu((METHOD == M_ROS23 && Sys::D <= 3) ? 4 : (METHOD == M_VERN7 && !AT) ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu((METHOD == M_ROS23 && Sys::D <= 3) ? 4
+                                   : ((METHOD == M_VERN7 && !AT) ||
+                                      (METHOD == M_TSIT5 && AT && Sys::D <= 6)) ? 2 : 1)))
 grad_kernel(GradArgs<R> a) {
   constexpr int D = Sys::D, P = Sys::P;
   const int lane = laneId();
